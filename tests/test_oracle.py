@@ -1,0 +1,9 @@
+"""The fp64 oracle against its pins (CPU only)."""
+import pytest
+
+import pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin()
