@@ -1,0 +1,335 @@
+"""Benchmark of the SNACK COO layer's hot path on one MI355X.
+
+A step is one forward (Y = X W^T + b), one input gradient (dX = dY W) and one
+weight gradient (dW on the stored entries) of one sparse layer, inputs already
+resident in HBM.  Default workload: a 10000 x 10000 layer at 95 % sparsity
+(5,000,000 stored entries, uniform positions), batch 64, fp32.
+
+Prints one JSON line: the metric (microseconds per fwd+dX+dW step), the
+roofline of the dominant kernel (algorithmic HBM bytes per launch over its
+average duration, timed with HIP events that bracket exactly that kernel), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+WORKLOADS = {
+    # name: (layer, batch, dtype)
+    "target95_b64": ("target95", 64, "f32"),
+    "target95_b1": ("target95", 1, "f32"),
+    "llm90_b64": ("llm90", 64, "f32"),
+    "llm90_b16": ("llm90", 16, "f32"),
+    "llm90_b1": ("llm90", 1, "f32"),
+    "mid_b32": ("mid", 32, "f32"),
+    "xs99_b1": ("xs99", 1, "f32"),
+    "xs999_b1": ("xs999", 1, "f32"),
+    "xs99_zipf_b1": ("xs99_zipf", 1, "f32"),
+    "gpt2_fc_b1024": ("gpt2_fc", 1024, "f32"),
+    "gpt2_fc_b1024_bf16": ("gpt2_fc", 1024, "bf16"),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(op, nnz, O, I, B, s):
+    """Bytes the method itself must move per launch (HBM), s = activation bytes."""
+    if op == "fwd":
+        return 12 * nnz + s * B * I + s * B * O + 4 * O
+    if op == "dx":
+        return 12 * nnz + s * B * O + s * B * I
+    return 12 * nnz + s * B * I + s * B * O  # dw: rows, cols, write dW; read X and dY
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "coo_spmm_row_amd", "csrc", "snack_coo.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Layer:
+    def __init__(self, name, B, dtype, dev):
+        import torch
+        import coo_spmm_row_amd as snk
+        import synth
+        spec = synth.LAYERS[name]
+        t0 = time.time()
+        L = synth.make_layer(spec)
+        built = snk.snack_coo_build(L["out_features"], L["in_features"], L["rows"], L["cols"], L["vals"])
+        self.host_build_s = time.time() - t0
+        self.spec, self.L, self.built, self.B, self.dtype = spec, L, built, B, dtype
+        self.O, self.I, self.nnz = L["out_features"], L["in_features"], L["nnz"]
+        self.W = snk.SnackCOO.from_built(built, dev)
+        seeds = synth.seeds_for(spec.config_id, spec.variant)
+        self.x = synth.make_acts(seeds["X"](0), B, self.I)
+        self.dy = synth.make_acts(seeds["dY"](0), B, self.O)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.X = torch.from_numpy(self.x).to(dev).to(tdt)
+        self.dY = torch.from_numpy(self.dy).to(dev).to(tdt)
+        self.bias = torch.from_numpy(L["bias"]).to(dev)
+        self.Y = torch.empty((B, self.O), dtype=tdt, device=dev)
+        self.dX = torch.empty((B, self.I), dtype=tdt, device=dev)
+        self.dW = torch.empty(self.nnz, dtype=torch.float32, device=dev)
+        code = snk.SNACK_BF16 if dtype == "bf16" else snk.SNACK_F32
+        need = max(snk.snack_coo_workspace_bytes(op, self.W, B, code) for op in (0, 1, 2))
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self.s = 2 if dtype == "bf16" else 4
+
+    def op(self, name):
+        import coo_spmm_row_amd as snk
+        if name == "fwd":
+            snk.snack_coo_fwd(self.W, self.X, self.bias, out=self.Y, workspace=self.ws)
+        elif name == "dx":
+            snk.snack_coo_bwd_input(self.W, self.dY, out=self.dX, workspace=self.ws)
+        else:
+            snk.snack_coo_grad_weight(self.W, self.X, self.dY, out=self.dW, workspace=self.ws)
+
+    def step(self):
+        self.op("fwd")
+        self.op("dx")
+        self.op("dw")
+
+
+OPS = ("fwd", "dx", "dw")
+
+
+def make_events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()  # creates the underlying HIP event
+    return evs
+
+
+def timed_steps(layer, K):
+    """K back-to-back steps; the probe brackets each op's main kernel.  Returns
+    (total ms, {op: [kernel ms per launch]})."""
+    import torch
+    import coo_spmm_row_amd as snk
+    pairs = {op: [(a, b) for a, b in zip(make_events(K), make_events(K))] for op in OPS}
+    start, stop = make_events(2)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        for op in OPS:
+            a, b = pairs[op][i]
+            snk.snack_coo_set_probe(a, b)
+            layer.op(op)
+    snk.snack_coo_set_probe()
+    stop.record()
+    torch.cuda.synchronize()
+    total = start.elapsed_time(stop)
+    kern = {op: [a.elapsed_time(b) for a, b in pairs[op]] for op in OPS}
+    return total, kern
+
+
+def op_times(layer, K):
+    """Per-op wall time on the stream (all kernels of the op), back to back."""
+    import torch
+    out = {}
+    for op in OPS:
+        a, b = make_events(2)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(K):
+            layer.op(op)
+        b.record()
+        torch.cuda.synchronize()
+        out[op] = a.elapsed_time(b) / K * 1000.0
+    return out
+
+
+def cold_kernel_times(layer, K, flush_bytes=1 << 30):
+    """Main-kernel time per op with the 256 MB last-level cache flushed before each launch."""
+    import torch
+    import coo_spmm_row_amd as snk
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device=layer.X.device)
+    res = {}
+    for op in OPS:
+        evs = [(a, b) for a, b in zip(make_events(K), make_events(K))]
+        for i in range(K):
+            scratch.add_(1.0)  # streams 2 x flush_bytes through the caches
+            snk.snack_coo_set_probe(*evs[i])
+            layer.op(op)
+            snk.snack_coo_set_probe()
+        torch.cuda.synchronize()
+        res[op] = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1000.0
+    del scratch
+    return res
+
+
+def cpu_baseline(layer, budget_s=15.0):
+    """The fp64 oracle on the first Bs batch rows of the same inputs, scaled to the full batch."""
+    import oracle
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    b = layer.built
+    r, c, v = b["rows"], b["cols"], b["vals"]
+    O, I, B = layer.O, layer.I, layer.B
+    x = layer.x.astype(np.float64)
+    dy = layer.dy.astype(np.float64)
+
+    def run(bs):
+        t0 = time.perf_counter()
+        oracle.fwd(O, I, r, c, v, x[:bs], layer.L["bias"], nthreads=nthreads)
+        oracle.bwd_input(O, I, r, c, v, dy[:bs], nthreads=nthreads)
+        oracle.grad_weight(O, I, r, c, x[:bs], dy[:bs], nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    bs = 1
+    t = run(bs)
+    while bs < B and t * 2 < budget_s:
+        bs = min(B, bs * 2)
+        t = run(bs)
+    us_per_step = t * 1e6 * (B / bs)
+    return {"value": round(us_per_step, 1), "unit": "us/step (fwd+dX+dW)", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle on the first {bs} of {B} batch rows of the same layer "
+                      f"({t:.1f} s), scaled by {B}/{bs}"}
+
+
+def traffic_for(workload, kernel):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload, {})
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or rec.get("source_sha") != kernel_source_sha():
+        return None  # counters were taken on another kernel version
+    return rec.get("traffic_bytes")
+
+
+def batch1_sweep(dev, K):
+    """Batch-1 fwd+dX+dW latency at every sparsity level of the 10k x 10k layer."""
+    out = {}
+    for name, label in (("llm90", "90%"), ("target95", "95%"), ("xs99", "99%"), ("xs999", "99.9%")):
+        layer = Layer(name, 1, "f32", dev)
+        for _ in range(3):
+            layer.step()
+        total, kern = timed_steps(layer, K)
+        out[label] = {"us_per_step": round(total / K * 1000.0, 2),
+                      "kernel_us": {op: round(float(np.mean(kern[op])) * 1000.0, 2) for op in OPS}}
+        del layer
+    return out
+
+
+def calibrate_copy(dev, nbytes, reps):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="target95_b64", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip cold-cache and batch-1 sweeps")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import coo_spmm_row_amd as snk  # noqa: F401  (fails loudly if the library is missing)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(dev, args.calibrate_copy, max(1, args.steps))
+        return
+
+    name, B, dtype = WORKLOADS[args.workload]
+    log(f"workload {args.workload}: building layer")
+    layer = Layer(name, B, dtype, dev)
+    log(f"layer {layer.O}x{layer.I} nnz={layer.nnz} B={B} {dtype} (host build {layer.host_build_s:.1f} s)")
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    total_ms, kern = timed_steps(layer, args.steps)
+    ms_per_step = total_ms / args.steps
+    kernel_us = {op: float(np.mean(kern[op])) * 1000.0 for op in OPS}
+    dom = max(OPS, key=lambda o: kernel_us[o])
+    kname = {"fwd": "forward gather-reduce", "dx": "input-gradient gather-reduce",
+             "dw": "weight-gradient sampled product"}[dom]
+    nbytes = {op: algorithmic_bytes(op, layer.nnz, layer.O, layer.I, B, layer.s) for op in OPS}
+    achieved = nbytes[dom] / (kernel_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for(args.workload, dom),
+                "kernel": kname, "kernel_us": round(kernel_us[dom], 2),
+                "algorithmic_bytes": nbytes[dom]}
+    extras = {"kernel_us": {op: round(v, 2) for op, v in kernel_us.items()},
+              "kernel_frac_hbm": {op: round(nbytes[op] / (kernel_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                  for op in OPS}}
+    if not args.no_extras:
+        log("op-level and cold-cache timings")
+        extras["op_us"] = {op: round(v, 2) for op, v in op_times(layer, args.steps).items()}
+        cold = cold_kernel_times(layer, min(args.steps, 20))
+        extras["kernel_us_cold"] = {op: round(v, 2) for op, v in cold.items()}
+        extras["kernel_frac_hbm_cold"] = {op: round(nbytes[op] / (cold[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                          for op in OPS}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(layer)
+    if not args.no_extras and B != 1:
+        log("batch-1 sweep over sparsity")
+        del layer
+        torch.cuda.empty_cache()
+        extras["batch1_us_per_step"] = batch1_sweep(dev, max(10, args.steps // 2))
+    line = {
+        "metric": "COO SpMM fwd+dX+dW us/call (one layer step)",
+        "value": round(ms_per_step * 1000.0, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded uniform positions, N(0,1) activations)",
+        "config": {},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    import synth
+    spec = synth.LAYERS[name]
+    line["config"] = {"workload": f"{spec.out_features}x{spec.in_features} sparse layer, "
+                                  f"{100 * (1 - spec.density):.1f}% sparsity, batch {B}",
+                      "out_features": spec.out_features, "in_features": spec.in_features,
+                      "nnz": spec.nnz, "batch": B, "structure": spec.structure}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

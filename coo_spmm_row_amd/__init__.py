@@ -1,0 +1,277 @@
+"""SNACK truly-sparse linear layer on MI355X -- Python binding of libsnack_coo.
+
+Thin ctypes marshalling over the C ABI declared in ``include/snack_coo.h``:
+every step of the layer runs in the library (HIP kernels for gfx950, host C++
+for the builder and the topology update).  PyTorch supplies device memory and
+the current HIP stream only.  Importing this package fails if the library has
+not been built (``python -m coo_spmm_row_amd.build``).
+
+Source: "Beyond Masked Sparsity: SNACK Enables Truly Sparse Neural Networks on
+GPU" (arXiv:2610.04093): Algorithm 1 and Section 3.2 (forward SpMM), Section
+3.4 and Appendix F (input and weight gradients), Appendix B Table 7 (COO / CSR
+/ CSC), Algorithm 2 and Appendix G (prune-and-regrow).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsnack_coo.so")
+
+SNACK_F32, SNACK_BF16 = 0, 1
+OP_FWD, OP_BWD_INPUT, OP_GRAD_WEIGHT = 0, 1, 2
+STATUS = {0: "OK", 1: "NULL", 2: "SHAPE", 3: "INDEX", 4: "DUPLICATE", 5: "ALIGN", 6: "DTYPE",
+          7: "WORKSPACE", 8: "HIP", 9: "INTERNAL", 10: "NOMEM", 11: "UNSORTED"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m coo_spmm_row_amd.build` "
+                      "(hipcc --offload-arch=gfx950); there is no fallback path")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class SnackError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _lib.snack_last_error().decode(errors="replace")
+        super().__init__(f"{where}: SNACK_ERR_{STATUS.get(code, code)}: {msg}")
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("out_features", ctypes.c_int64), ("in_features", ctypes.c_int64),
+                ("nnz", ctypes.c_int64), ("rows", ctypes.c_void_p), ("cols", ctypes.c_void_p),
+                ("vals", ctypes.c_void_p), ("row_offsets", ctypes.c_void_p),
+                ("col_perm", ctypes.c_void_p), ("col_rows", ctypes.c_void_p),
+                ("col_cols", ctypes.c_void_p), ("col_offsets", ctypes.c_void_p)]
+
+
+_i64, _p, _u64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64
+_D = ctypes.POINTER(_Desc)
+_lib.snack_last_error.restype = ctypes.c_char_p
+_lib.snack_coo_abi_version.restype = ctypes.c_int
+_lib.snack_coo_build.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]
+_lib.snack_coo_workspace_bytes.argtypes = [ctypes.c_int, _D, _i64, ctypes.c_int]
+_lib.snack_coo_workspace_bytes.restype = ctypes.c_size_t
+_lib.snack_coo_fwd.argtypes = [_D, _p, _i64, ctypes.c_int, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.snack_coo_bwd_input.argtypes = [_D, _p, _i64, ctypes.c_int, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.snack_coo_grad_weight.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, ctypes.c_size_t, _p]
+_lib.snack_coo_topology_update.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i64, _u64, _p, _p, _p, _p, _p]
+_lib.snack_coo_set_probe.argtypes = [_p, _p]
+
+EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_bwd_input",
+            "snack_coo_grad_weight", "snack_coo_topology_update", "snack_last_error",
+            "snack_coo_abi_version", "snack_coo_set_probe")
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SnackError(status, where)
+
+
+# ------------------------------------------------------------------ host calls
+def snack_coo_build(out_features: int, in_features: int, rows, cols, vals=None, column_view: bool = True):
+    """Host builder: sort to (row, col), row offsets, optional column view (numpy in, numpy out)."""
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    nnz = int(rows.size)
+    if cols.size != nnz:
+        raise ValueError("rows and cols differ in length")
+    vals_in = None if vals is None else np.ascontiguousarray(vals, dtype=np.float32)
+    out = {"rows": np.empty(nnz, np.int32), "cols": np.empty(nnz, np.int32),
+           "vals": np.empty(nnz, np.float32) if vals_in is not None else None,
+           "perm": np.empty(nnz, np.int32), "row_offsets": np.empty(out_features + 1, np.int32)}
+    if column_view:
+        out.update(col_perm=np.empty(nnz, np.int32), col_rows=np.empty(nnz, np.int32),
+                   col_cols=np.empty(nnz, np.int32), col_offsets=np.empty(in_features + 1, np.int32))
+    st = _lib.snack_coo_build(out_features, in_features, nnz, _np_ptr(rows), _np_ptr(cols), _np_ptr(vals_in),
+                              _np_ptr(out["rows"]), _np_ptr(out["cols"]), _np_ptr(out["vals"]),
+                              _np_ptr(out["perm"]), _np_ptr(out["row_offsets"]),
+                              _np_ptr(out.get("col_perm")), _np_ptr(out.get("col_rows")),
+                              _np_ptr(out.get("col_cols")), _np_ptr(out.get("col_offsets")))
+    _check(st, "snack_coo_build")
+    out["out_features"], out["in_features"], out["nnz"] = out_features, in_features, nnz
+    return out
+
+
+def snack_coo_topology_update(out_features: int, in_features: int, rows, cols, vals, n_prune: int, seed: int):
+    """Host prune-and-regrow (Appendix G with Algorithm 2); returns the new sorted triple."""
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    vals = np.ascontiguousarray(vals, dtype=np.float32)
+    nnz = int(rows.size)
+    out = {"rows": np.empty(nnz, np.int32), "cols": np.empty(nnz, np.int32),
+           "vals": np.empty(nnz, np.float32), "row_offsets": np.empty(out_features + 1, np.int32)}
+    trials = ctypes.c_int64(0)
+    st = _lib.snack_coo_topology_update(out_features, in_features, nnz, _np_ptr(rows), _np_ptr(cols),
+                                        _np_ptr(vals), int(n_prune), ctypes.c_uint64(seed),
+                                        _np_ptr(out["rows"]), _np_ptr(out["cols"]), _np_ptr(out["vals"]),
+                                        _np_ptr(out["row_offsets"]), ctypes.byref(trials))
+    _check(st, "snack_coo_topology_update")
+    out["trials"] = int(trials.value)
+    return out
+
+
+# ------------------------------------------------------------------ device side
+class SnackCOO:
+    """A layer weight resident on one GPU: the sorted triple, row offsets and
+    (optionally) the column view, as torch tensors.  ``vals`` may be updated in
+    place (same length); the structure arrays must stay as built."""
+
+    def __init__(self, out_features, in_features, rows, cols, vals, row_offsets,
+                 col_perm=None, col_rows=None, col_cols=None, col_offsets=None):
+        self.out_features, self.in_features = int(out_features), int(in_features)
+        self.rows, self.cols, self.vals, self.row_offsets = rows, cols, vals, row_offsets
+        self.col_perm, self.col_rows, self.col_cols, self.col_offsets = col_perm, col_rows, col_cols, col_offsets
+        self.nnz = int(rows.numel())
+        self._desc = _Desc()
+        self._refresh()
+
+    @classmethod
+    def from_built(cls, built: dict, device, vals=None):
+        import torch
+        def t(a):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        v = built["vals"] if vals is None else vals
+        return cls(built["out_features"], built["in_features"], t(built["rows"]), t(built["cols"]),
+                   t(np.ascontiguousarray(v, dtype=np.float32)), t(built["row_offsets"]),
+                   t(built.get("col_perm")), t(built.get("col_rows")), t(built.get("col_cols")),
+                   t(built.get("col_offsets")))
+
+    def _refresh(self):
+        d = self._desc
+        d.out_features, d.in_features, d.nnz = self.out_features, self.in_features, self.nnz
+        ptr = lambda x: None if x is None else x.data_ptr()
+        d.rows, d.cols, d.vals, d.row_offsets = ptr(self.rows), ptr(self.cols), ptr(self.vals), ptr(self.row_offsets)
+        d.col_perm, d.col_rows = ptr(self.col_perm), ptr(self.col_rows)
+        d.col_cols, d.col_offsets = ptr(self.col_cols), ptr(self.col_offsets)
+
+    @property
+    def desc(self):
+        self._refresh()
+        return ctypes.byref(self._desc)
+
+    @property
+    def device(self):
+        return self.rows.device
+
+    def device_bytes(self) -> int:
+        return sum(int(x.numel() * x.element_size()) for x in
+                   (self.rows, self.cols, self.vals, self.row_offsets, self.col_perm, self.col_rows,
+                    self.col_cols, self.col_offsets) if x is not None)
+
+
+_ws_cache = {}
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SNACK_F32
+    if t.dtype == torch.bfloat16:
+        return SNACK_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream_handle(device, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(device, nbytes: int, workspace=None):
+    import torch
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    key = (str(device),)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return ctypes.c_void_p(buf.data_ptr()), buf.numel()
+
+
+def _check_act(t, rows_expected, cols_expected, name):
+    if t.dim() != 2 or t.shape[1] != cols_expected or (rows_expected is not None and t.shape[0] != rows_expected):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [batch, {cols_expected}]")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def snack_coo_workspace_bytes(op: int, W: SnackCOO, batch: int, act_dtype: int) -> int:
+    return int(_lib.snack_coo_workspace_bytes(op, W.desc, batch, act_dtype))
+
+
+def snack_coo_fwd(W: SnackCOO, X, bias=None, out=None, workspace=None, stream=None):
+    """Y = X W^T + bias (Y has X's dtype)."""
+    import torch
+    _check_act(X, None, W.in_features, "X")
+    B = X.shape[0]
+    dt = _dtype_code(X)
+    Y = out if out is not None else torch.empty((B, W.out_features), dtype=X.dtype, device=X.device)
+    _check_act(Y, B, W.out_features, "Y")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != W.out_features):
+        raise ValueError("bias must be float32 [out_features]")
+    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_FWD, W, B, dt), workspace)
+    st = _lib.snack_coo_fwd(W.desc, ctypes.c_void_p(X.data_ptr()), B, dt,
+                            None if bias is None else ctypes.c_void_p(bias.data_ptr()),
+                            ctypes.c_void_p(Y.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
+    _check(st, "snack_coo_fwd")
+    return Y
+
+
+def snack_coo_bwd_input(W: SnackCOO, dY, out=None, db=None, workspace=None, stream=None):
+    """dX = dY W (dX has dY's dtype); if ``db`` (float32 [O]) is given it receives sum_b dY[b]."""
+    import torch
+    _check_act(dY, None, W.out_features, "dY")
+    B = dY.shape[0]
+    dt = _dtype_code(dY)
+    dX = out if out is not None else torch.empty((B, W.in_features), dtype=dY.dtype, device=dY.device)
+    _check_act(dX, B, W.in_features, "dX")
+    ws, wsn = _workspace(dY.device, snack_coo_workspace_bytes(OP_BWD_INPUT, W, B, dt), workspace)
+    st = _lib.snack_coo_bwd_input(W.desc, ctypes.c_void_p(dY.data_ptr()), B, dt, ctypes.c_void_p(dX.data_ptr()),
+                                  None if db is None else ctypes.c_void_p(db.data_ptr()), ws, wsn,
+                                  _stream_handle(dY.device, stream))
+    _check(st, "snack_coo_bwd_input")
+    return dX
+
+
+def snack_coo_grad_weight(W: SnackCOO, X, dY, out=None, workspace=None, stream=None):
+    """dW[k] = sum_b dY[b, rows[k]] X[b, cols[k]] (float32 [nnz])."""
+    import torch
+    _check_act(X, None, W.in_features, "X")
+    B = X.shape[0]
+    _check_act(dY, B, W.out_features, "dY")
+    dt = _dtype_code(X)
+    if _dtype_code(dY) != dt:
+        raise TypeError("X and dY must have the same dtype")
+    dW = out if out is not None else torch.empty(W.nnz, dtype=torch.float32, device=X.device)
+    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_GRAD_WEIGHT, W, B, dt), workspace)
+    st = _lib.snack_coo_grad_weight(W.desc, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(dY.data_ptr()), B, dt,
+                                    ctypes.c_void_p(dW.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
+    _check(st, "snack_coo_grad_weight")
+    return dW
+
+
+def snack_coo_set_probe(start_event=None, stop_event=None):
+    """Arm (two torch.cuda.Event with timing, already recorded once) or disarm (no args) the
+    main-kernel timing probe for device calls made from this thread."""
+    a = None if start_event is None else ctypes.c_void_p(start_event.cuda_event)
+    b = None if stop_event is None else ctypes.c_void_p(stop_event.cuda_event)
+    _check(_lib.snack_coo_set_probe(a, b), "snack_coo_set_probe")
+
+
+def abi_version() -> int:
+    return int(_lib.snack_coo_abi_version())

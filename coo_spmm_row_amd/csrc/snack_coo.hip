@@ -1,0 +1,675 @@
+// snack_coo.hip -- device side of libsnack_coo for MI355X (gfx950, CDNA4, wave64).
+//
+// The SNACK layer (arXiv:2610.04093) keeps its weight W (O x I) as a COO triple
+// sorted by (row, col) and runs three sparse products on it:
+//   forward      Y[b,o]  = bias[o] + sum_{k: rows[k]=o} vals[k] X[b,cols[k]]   (Algorithm 1)
+//   input grad   dX[b,i] = sum_{k: cols[k]=i} vals[k] dY[b,rows[k]]            (Section 3.4)
+//   weight grad  dW[k]   = sum_b dY[b,rows[k]] X[b,cols[k]]                     (Section 3.4)
+// The paper's CUDA mapping (Section 3.2: one thread per non-zero and batch
+// column, atomics into C) is not used.  Here:
+//  * activations are first laid out feature-major (A^T[f][b], fp32) so that the
+//    operand row of one stored entry, A[:, f], is one contiguous vector;
+//  * forward and input gradient are the same gather-reduce over a sorted
+//    triple: the forward over the row order, the input gradient over the
+//    column view (W^T with swapped indices, as Section 3.4 states), reading
+//    vals through the column permutation.  Every output element is produced by
+//    exactly one lane or by a fixed-order fix-up, so results are deterministic
+//    and no atomics are used;
+//  * two mappings of the gather-reduce:
+//      segscan  - a wave owns a chunk of consecutive stored entries; lanes are
+//                 (entry group g, batch lane t); row segments inside a step are
+//                 combined by a segmented scan across entry groups; segments cut
+//                 by a chunk edge go to a small partials buffer and are finished
+//                 by fixup_kernel.  Balanced by nnz, so power-law rows are fine.
+//      rowgroup - for batches that are multiples of 4 and >= 16: a group of BT
+//                 lanes owns one output row, each lane holds 4 batch columns and
+//                 gathers float4s of the feature-major operand.
+//  * the weight gradient is a sampled dense-dense product over the stored
+//    entries: a group of BT lanes per entry, each lane a slice of the batch,
+//    reduced across the group by xor shuffles.
+// No MFMA: the work is an irregular gather, not a dense contraction.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/snack_coo.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;               // 4 waves per workgroup
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kXcds = 8;                  // MI355X: 8 accelerator dies, round-robin dispatch
+constexpr int64_t kMaxBatch = int64_t(1) << 22;  // keeps every grid.y within 65535
+
+typedef uint16_t bf16_t;
+
+// ---------------------------------------------------------------- element I/O
+__device__ __forceinline__ float load_act(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_act(const bf16_t *p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+__device__ __forceinline__ void store_act(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_act(bf16_t *p, int64_t i, float v) {
+    // round to nearest, ties to even; NaN stays a quiet NaN
+    uint32_t u = __float_as_uint(v);
+    uint16_t h;
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
+        h = static_cast<uint16_t>((u >> 16) | 0x0040u);
+    } else {
+        h = static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    }
+    p[i] = h;
+}
+
+// Logical workgroup index such that each XCD (blockIdx.x % 8 under round-robin
+// dispatch) works on one contiguous eighth of the logical range.  gridDim.x is
+// a multiple of 8; callers drop logical ids beyond their real count.
+__device__ __forceinline__ int64_t xcd_block() {
+    const int64_t per = gridDim.x / kXcds;
+    return (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+}
+
+// ---------------------------------------------------------------- layout
+// in [B][F] (batch-major, fp32 or bf16)  ->  out [F][B] fp32 (feature-major)
+template <typename InT>
+__global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__restrict__ in,
+                                                                  float *__restrict__ out,
+                                                                  int64_t B, int64_t F) {
+    __shared__ float tile[64][65];
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 64;
+    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int nb = static_cast<int>(min<int64_t>(64, B - b0));
+    const int nf = static_cast<int>(min<int64_t>(64, F - f0));
+    for (int bb = ty; bb < nb; bb += 4)
+        if (tx < nf) tile[bb][tx] = load_act(in, (b0 + bb) * F + f0 + tx);
+    __syncthreads();
+    for (int li = threadIdx.x; li < nf * nb; li += kBlock) {
+        const int ff = li / nb, bb = li % nb;
+        out[(f0 + ff) * B + b0 + bb] = tile[bb][ff];
+    }
+}
+
+// ---------------------------------------------------------------- segscan mapping
+// keys[k]  : output index of entry k (row for the forward, column for dX), sorted
+// gidx[k]  : operand row gathered by entry k (column for the forward, row for dX)
+// vals[perm ? perm[k] : k] : the entry's value
+// opnd     : feature-major operand [*][B]
+// out[b * out_ld + key] = bias[key] + sum over the key's entries
+// head/tail[chunk][B]   : partial sums of segments cut by a chunk edge
+template <int BT, typename OutT>
+__global__ __launch_bounds__(kBlock) void segscan_kernel(
+    int64_t nnz, int64_t chunk, int64_t nchunks, const int32_t *__restrict__ keys,
+    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm,
+    const float *__restrict__ opnd, int64_t B, const float *__restrict__ bias, OutT *__restrict__ out,
+    int64_t out_ld, float *__restrict__ head, float *__restrict__ tail) {
+    constexpr int G = kWave / BT;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane / BT, t = lane % BT;
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+    if (j >= nchunks) return;  // uniform per wave
+    const int64_t b = static_cast<int64_t>(blockIdx.y) * BT + t;
+    const bool bok = b < B;
+    const int64_t kbeg = j * chunk;
+    const int64_t kend = min(kbeg + chunk, nnz);
+    const int prev_key = kbeg > 0 ? keys[kbeg - 1] : -1;
+    const int next_key = kend < nnz ? keys[kend] : -1;
+    const int first_key = keys[kbeg];
+    float carry = 0.f;
+    int carry_key = -4;
+    for (int64_t base = kbeg; base < kend; base += G) {
+        const int64_t k = base + g;
+        const bool valid = k < kend;
+        int key = -2, nkey = -3;
+        float p = 0.f;
+        if (valid) {
+            key = keys[k];
+            nkey = (k + 1 < kend) ? keys[k + 1] : -3;
+            const float v = vals[perm ? static_cast<int64_t>(perm[k]) : k];
+            const int64_t c = gidx[k];
+            if (bok) p = v * opnd[c * B + b];
+        }
+        // segmented inclusive scan across the G entry groups (keys are sorted,
+        // so equal keys at distance d mean the whole span shares the key)
+#pragma unroll
+        for (int d = 1; d < G; d <<= 1) {
+            const float up = __shfl_up(p, d * BT, kWave);
+            const int upkey = __shfl_up(key, d * BT, kWave);
+            if (g >= d && upkey == key) p += up;
+        }
+        if (key == carry_key) p += carry;
+        carry = __shfl(p, (G - 1) * BT + t, kWave);
+        carry_key = __shfl(key, (G - 1) * BT + t, kWave);
+        if (valid && bok && nkey != key) {
+            const bool cut_left = key == prev_key;
+            const bool cut_right = (k == kend - 1) && key == next_key;
+            if (cut_left || cut_right) {
+                if (key == first_key)
+                    head[j * B + b] = p;
+                else
+                    tail[j * B + b] = p;
+            } else {
+                store_act(out, b * out_ld + key, p + (bias ? bias[key] : 0.f));
+            }
+        }
+    }
+}
+
+// Finishes keys with no entries (output = bias) and keys whose entries span
+// several chunks (sum of the chunk partials in chunk order, then the bias).
+template <typename OutT>
+__global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B, int64_t chunk,
+                                                       const int32_t *__restrict__ offs,
+                                                       const float *__restrict__ bias,
+                                                       const float *__restrict__ head,
+                                                       const float *__restrict__ tail,
+                                                       OutT *__restrict__ out, int64_t out_ld) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (r >= nkeys) return;
+    const float bv = bias ? bias[r] : 0.f;
+    const int64_t s = offs[r], e = offs[r + 1];
+    for (int64_t b = blockIdx.y; b < B; b += gridDim.y) {
+        if (s == e) {
+            store_act(out, b * out_ld + r, bv);
+            continue;
+        }
+        const int64_t cs = s / chunk, ce = (e - 1) / chunk;
+        if (cs == ce) continue;  // written by segscan_kernel
+        float v = (s == cs * chunk) ? head[cs * B + b] : tail[cs * B + b];
+        for (int64_t c = cs + 1; c <= ce; ++c) v += head[c * B + b];
+        store_act(out, b * out_ld + r, v + bv);
+    }
+}
+
+// ---------------------------------------------------------------- rowgroup mapping
+template <int BT, typename OutT>
+__global__ __launch_bounds__(kBlock) void rowgroup_kernel(
+    int64_t nkeys, const int32_t *__restrict__ offs, const int32_t *__restrict__ gidx,
+    const float *__restrict__ vals, const int32_t *__restrict__ perm, const float *__restrict__ opnd,
+    int64_t B, const float *__restrict__ bias, OutT *__restrict__ out, int64_t out_ld) {
+    constexpr int G = kWave / BT;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane / BT, t = lane % BT;
+    const int64_t r = (xcd_block() * kWavesPerBlock + threadIdx.x / kWave) * G + g;
+    if (r >= nkeys) return;
+    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * (4 * BT) + 4 * t;
+    if (b0 >= B) return;  // B % 4 == 0, so b0 < B means all four columns exist
+    const int64_t s = offs[r], e = offs[r + 1];
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int64_t k = s;
+    for (; k + 4 <= e; k += 4) {
+        float v[4];
+        int64_t c[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[u] = vals[perm ? static_cast<int64_t>(perm[k + u]) : k + u];
+            c[u] = gidx[k + u];
+        }
+        float4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4 *>(opnd + c[u] * B + b0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            a0 += v[u] * x[u].x;
+            a1 += v[u] * x[u].y;
+            a2 += v[u] * x[u].z;
+            a3 += v[u] * x[u].w;
+        }
+    }
+    for (; k < e; ++k) {
+        const float v = vals[perm ? static_cast<int64_t>(perm[k]) : k];
+        const float4 x = *reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(gidx[k]) * B + b0);
+        a0 += v * x.x;
+        a1 += v * x.y;
+        a2 += v * x.z;
+        a3 += v * x.w;
+    }
+    const float bv = bias ? bias[r] : 0.f;
+    store_act(out, (b0 + 0) * out_ld + r, a0 + bv);
+    store_act(out, (b0 + 1) * out_ld + r, a1 + bv);
+    store_act(out, (b0 + 2) * out_ld + r, a2 + bv);
+    store_act(out, (b0 + 3) * out_ld + r, a3 + bv);
+}
+
+// ---------------------------------------------------------------- weight gradient
+// xt [I][B], dyt [O][B] feature-major fp32.  A group of BT lanes per entry; lane
+// t covers batch columns t*VW + m*BT*VW (+0..VW-1).
+template <int BT, int VW>
+__global__ __launch_bounds__(kBlock) void sddmm_kernel(int64_t nnz, int64_t steps,
+                                                       const int32_t *__restrict__ rows,
+                                                       const int32_t *__restrict__ cols,
+                                                       const float *__restrict__ xt,
+                                                       const float *__restrict__ dyt, int64_t B,
+                                                       float *__restrict__ dW) {
+    constexpr int G = kWave / BT;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane / BT, t = lane % BT;
+    const int64_t w = xcd_block() * kWavesPerBlock + threadIdx.x / kWave;
+    const int64_t kbase = w * steps * G;
+    for (int64_t s = 0; s < steps; ++s) {
+        const int64_t k = kbase + s * G + g;
+        if (kbase + s * G >= nnz) break;  // uniform per wave
+        const bool valid = k < nnz;
+        float acc = 0.f;
+        if (valid) {
+            const float *xr = xt + static_cast<int64_t>(cols[k]) * B;
+            const float *yr = dyt + static_cast<int64_t>(rows[k]) * B;
+            if constexpr (VW == 4) {
+                for (int64_t bb = 4 * t; bb < B; bb += 4 * BT) {
+                    const float4 x = *reinterpret_cast<const float4 *>(xr + bb);
+                    const float4 y = *reinterpret_cast<const float4 *>(yr + bb);
+                    acc += x.x * y.x;
+                    acc += x.y * y.y;
+                    acc += x.z * y.z;
+                    acc += x.w * y.w;
+                }
+            } else {
+                for (int64_t bb = t; bb < B; bb += BT) acc += xr[bb] * yr[bb];
+            }
+        }
+#pragma unroll
+        for (int d = BT / 2; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, kWave);
+        if (valid && t == 0) dW[k] = acc;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void zero_kernel(float *__restrict__ p, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------- bias gradient
+template <typename InT>
+__global__ __launch_bounds__(kBlock) void bias_grad_kernel(int64_t O, int64_t B, const InT *__restrict__ dY,
+                                                           float *__restrict__ db) {
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (o >= O) return;
+    float s = 0.f;
+    for (int64_t b = 0; b < B; ++b) s += load_act(dY, b * O + o);
+    db[o] = s;
+}
+
+// ================================================================ host side
+using snack::fail;
+
+thread_local hipEvent_t g_probe_start = nullptr;
+thread_local hipEvent_t g_probe_stop = nullptr;
+
+// Records the armed probe's start event (before the main kernel) or stop event (after it).
+inline void probe(bool start, hipStream_t st) {
+    hipEvent_t e = start ? g_probe_start : g_probe_stop;
+    if (e) (void)hipEventRecord(e, st);
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up8(int64_t x) { return ceil_div(x, kXcds) * kXcds; }
+
+enum Mapping { kSegscan = 0, kRowgroup = 1 };
+
+// Device work plan of one gather-reduce (forward or input gradient).
+struct SpmmPlan {
+    Mapping mapping;
+    int bt;              // batch lanes per entry group (segscan) or lanes per row (rowgroup)
+    int64_t chunk;       // segscan: entries per wave
+    int64_t nchunks;
+    bool direct;         // operand used in place (fp32, batch 1) instead of a transposed copy
+    size_t off_opnd, off_head, off_tail, total;
+};
+
+inline int pow2_at_least(int64_t x) {
+    int p = 1;
+    while (p < x && p < kWave) p <<= 1;
+    return p;
+}
+
+SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t B, int dtype) {
+    SpmmPlan p{};
+    p.direct = (B == 1 && dtype == SNACK_F32);
+    if (B >= 16 && B % 4 == 0) {
+        p.mapping = kRowgroup;
+        p.bt = static_cast<int>(std::min<int64_t>(16, B / 4));
+    } else {
+        p.mapping = kSegscan;
+        p.bt = pow2_at_least(B);
+        const int64_t G = kWave / p.bt;
+        const int64_t target_waves = 8192;
+        int64_t steps = ceil_div(std::max<int64_t>(nnz, 1), G * target_waves);
+        steps = std::min<int64_t>(std::max<int64_t>(steps, 2), 32);
+        p.chunk = G * steps;
+        p.nchunks = ceil_div(nnz, p.chunk);
+    }
+    size_t at = 0;
+    p.off_opnd = at;
+    if (!p.direct) at = align_up(at + sizeof(float) * static_cast<size_t>(opnd_rows * B));
+    p.off_head = at;
+    if (p.mapping == kSegscan) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B));
+    p.off_tail = at;
+    if (p.mapping == kSegscan) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B));
+    p.total = at;
+    return p;
+}
+
+struct SddmmPlan {
+    int bt, vw;
+    int64_t steps, waves;
+    bool x_direct, dy_direct;
+    size_t off_x, off_dy, total;
+};
+
+SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
+    SddmmPlan p{};
+    p.vw = (B % 4 == 0) ? 4 : 1;
+    // about 16 batch columns per lane before the cross-lane reduction
+    int64_t bt = std::max<int64_t>(1, B / 16);
+    int b2 = 1;
+    while (b2 * 2 <= bt && b2 < 16) b2 <<= 1;
+    p.bt = b2;
+    const int64_t G = kWave / p.bt;
+    const int64_t target_waves = 8192;
+    p.steps = std::min<int64_t>(std::max<int64_t>(ceil_div(std::max<int64_t>(nnz, 1), G * target_waves), 1), 64);
+    p.waves = ceil_div(nnz, G * p.steps);
+    p.x_direct = p.dy_direct = (B == 1 && dtype == SNACK_F32);
+    size_t at = 0;
+    p.off_x = at;
+    if (!p.x_direct) at = align_up(at + sizeof(float) * static_cast<size_t>(I * B));
+    p.off_dy = at;
+    if (!p.dy_direct) at = align_up(at + sizeof(float) * static_cast<size_t>(O * B));
+    p.total = at;
+    return p;
+}
+
+int check_hip(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SNACK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return SNACK_OK;
+}
+
+int check_desc(const snack_coo_desc *W, bool need_colview, const char *who) {
+    if (!W) return fail(SNACK_ERR_NULL, "%s: descriptor is NULL", who);
+    const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+    if (O < 0 || I < 0 || nnz < 0 || O > 2147483647LL || I > 2147483647LL || nnz > 2147483647LL ||
+        nnz > O * I)
+        return fail(SNACK_ERR_SHAPE, "%s: bad sizes O=%lld I=%lld nnz=%lld", who, (long long)O,
+                    (long long)I, (long long)nnz);
+    if (nnz > 0 && (!W->rows || !W->cols || !W->vals))
+        return fail(SNACK_ERR_NULL, "%s: rows, cols and vals are required", who);
+    if (!W->row_offsets) return fail(SNACK_ERR_NULL, "%s: row_offsets is required", who);
+    if (need_colview && (!W->col_offsets || (nnz > 0 && (!W->col_perm || !W->col_rows || !W->col_cols))))
+        return fail(SNACK_ERR_NULL, "%s: the column view (col_perm, col_rows, col_cols, col_offsets) is required",
+                    who);
+    return SNACK_OK;
+}
+
+int check_act(const void *p, int dtype, const char *name, const char *who) {
+    if (!p) return fail(SNACK_ERR_NULL, "%s: %s is NULL", who, name);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (a % (dtype == SNACK_F32 ? 4 : 2))
+        return fail(SNACK_ERR_ALIGN, "%s: %s is not aligned to its element size", who, name);
+    return SNACK_OK;
+}
+
+int check_workspace(void *ws, size_t have, size_t need, const char *who) {
+    if (need == 0) return SNACK_OK;
+    if (!ws || have < need)
+        return fail(SNACK_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                    ws ? have : size_t(0));
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+        return fail(SNACK_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
+    return SNACK_OK;
+}
+
+// activation [B][F] -> feature-major fp32 [F][B] in `dst`
+int launch_to_feature_major(const void *src, int dtype, int64_t B, int64_t F, float *dst, hipStream_t st) {
+    if (B == 0 || F == 0) return SNACK_OK;
+    const dim3 grid(static_cast<unsigned>(ceil_div(F, 64)), static_cast<unsigned>(ceil_div(B, 64)));
+    if (dtype == SNACK_F32)
+        hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(kBlock), 0, st,
+                           static_cast<const float *>(src), dst, B, F);
+    else
+        hipLaunchKernelGGL(to_feature_major_kernel<bf16_t>, grid, dim3(kBlock), 0, st,
+                           static_cast<const bf16_t *>(src), dst, B, F);
+    return check_hip("to_feature_major");
+}
+
+template <typename OutT, int BT>
+void launch_segscan_bt(const SpmmPlan &p, int64_t nnz, const int32_t *keys, const int32_t *gidx,
+                       const float *vals, const int32_t *perm, const float *opnd, int64_t B,
+                       const float *bias, OutT *out, int64_t out_ld, float *head, float *tail,
+                       hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(p.nchunks, kWavesPerBlock)),
+                    static_cast<unsigned>(ceil_div(B, BT)));
+    hipLaunchKernelGGL((segscan_kernel<BT, OutT>), grid, dim3(kBlock), 0, st, nnz, p.chunk, p.nchunks,
+                       keys, gidx, vals, perm, opnd, B, bias, out, out_ld, head, tail);
+}
+
+template <typename OutT, int BT>
+void launch_rowgroup_bt(int64_t nkeys, const int32_t *offs, const int32_t *gidx, const float *vals,
+                        const int32_t *perm, const float *opnd, int64_t B, const float *bias, OutT *out,
+                        int64_t out_ld, hipStream_t st) {
+    constexpr int G = kWave / BT;
+    const int64_t blocks = round_up8(ceil_div(nkeys, G * kWavesPerBlock));
+    const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(ceil_div(B, 4 * BT)));
+    hipLaunchKernelGGL((rowgroup_kernel<BT, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
+                       perm, opnd, B, bias, out, out_ld);
+}
+
+// The gather-reduce shared by the forward (row order) and the input gradient
+// (column view).  nkeys = number of outputs per batch row; offs [nkeys+1].
+template <typename OutT>
+int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys, const int32_t *offs,
+             const int32_t *gidx, const float *vals, const int32_t *perm, const float *opnd, int64_t B,
+             const float *bias, OutT *out, char *ws, hipStream_t st) {
+    if (nkeys == 0 || B == 0) return SNACK_OK;
+    if (p.mapping == kRowgroup) {
+        probe(true, st);
+        switch (p.bt) {
+            case 4: launch_rowgroup_bt<OutT, 4>(nkeys, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
+            case 8: launch_rowgroup_bt<OutT, 8>(nkeys, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
+            case 16: launch_rowgroup_bt<OutT, 16>(nkeys, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
+            default: return fail(SNACK_ERR_INTERNAL, "rowgroup: unsupported lane count %d", p.bt);
+        }
+        probe(false, st);
+        return check_hip("rowgroup_kernel");
+    }
+    float *head = reinterpret_cast<float *>(ws + p.off_head);
+    float *tail = reinterpret_cast<float *>(ws + p.off_tail);
+    if (p.nchunks > 0) {
+        probe(true, st);
+        switch (p.bt) {
+#define SNACK_SEG(BTV) \
+    case BTV: launch_segscan_bt<OutT, BTV>(p, nnz, keys, gidx, vals, perm, opnd, B, bias, out, nkeys, head, tail, st); break;
+            SNACK_SEG(1) SNACK_SEG(2) SNACK_SEG(4) SNACK_SEG(8) SNACK_SEG(16) SNACK_SEG(32) SNACK_SEG(64)
+#undef SNACK_SEG
+            default: return fail(SNACK_ERR_INTERNAL, "segscan: unsupported lane count %d", p.bt);
+        }
+        probe(false, st);
+        if (int s = check_hip("segscan_kernel")) return s;
+    }
+    const dim3 grid(static_cast<unsigned>(ceil_div(nkeys, kBlock)),
+                    static_cast<unsigned>(std::min<int64_t>(B, 65535)));
+    hipLaunchKernelGGL(fixup_kernel<OutT>, grid, dim3(kBlock), 0, st, nkeys, B,
+                       p.chunk > 0 ? p.chunk : 1, offs, bias, head, tail, out, nkeys);
+    return check_hip("fixup_kernel");
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int64_t batch, int act_dtype) {
+    if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16) {
+        fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown dtype %d", act_dtype);
+        return 0;
+    }
+    if (check_desc(W, false, "workspace_bytes") || batch < 0) {
+        if (batch < 0) fail(SNACK_ERR_SHAPE, "workspace_bytes: negative batch");
+        return 0;
+    }
+    const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+    switch (op) {
+        case SNACK_OP_FWD: return plan_spmm(nnz, I, batch, act_dtype).total;
+        case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, batch, act_dtype).total;
+        case SNACK_OP_GRAD_WEIGHT: return plan_sddmm(nnz, O, I, batch, act_dtype).total;
+        default: fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown op %d", op); return 0;
+    }
+}
+
+extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t batch, int act_dtype,
+                             const float *bias, void *Y, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+    try {
+        const char *who = "snack_coo_fwd";
+        if (int s = check_desc(W, false, who)) return s;
+        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
+            return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
+        if (batch < 0 || batch > kMaxBatch)
+            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^22]", who, (long long)batch);
+        const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+        if (batch == 0 || O == 0) return snack::ok();
+        if (I > 0) { if (int s = check_act(X, act_dtype, "X", who)) return s; }
+        if (int s = check_act(Y, act_dtype, "Y", who)) return s;
+        const SpmmPlan p = plan_spmm(nnz, I, batch, act_dtype);
+        if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
+        hipStream_t st = static_cast<hipStream_t>(hip_stream);
+        char *ws = static_cast<char *>(workspace);
+        const float *xt = static_cast<const float *>(X);
+        if (!p.direct) {
+            float *dst = reinterpret_cast<float *>(ws + p.off_opnd);
+            if (int s = launch_to_feature_major(X, act_dtype, batch, I, dst, st)) return s;
+            xt = dst;
+        }
+        int s;
+        if (act_dtype == SNACK_F32)
+            s = run_spmm<float>(p, O, nnz, W->rows, W->row_offsets, W->cols, W->vals, nullptr, xt, batch, bias,
+                                static_cast<float *>(Y), ws, st);
+        else
+            s = run_spmm<bf16_t>(p, O, nnz, W->rows, W->row_offsets, W->cols, W->vals, nullptr, xt, batch, bias,
+                                 static_cast<bf16_t *>(Y), ws, st);
+        return s ? s : snack::ok();
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "snack_coo_fwd: unexpected exception");
+    }
+}
+
+extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int64_t batch, int act_dtype,
+                                   void *dX, float *db, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream) {
+    try {
+        const char *who = "snack_coo_bwd_input";
+        if (int s = check_desc(W, true, who)) return s;
+        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
+            return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
+        if (batch < 0 || batch > kMaxBatch)
+            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^22]", who, (long long)batch);
+        const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+        hipStream_t st = static_cast<hipStream_t>(hip_stream);
+        if (batch > 0 && O > 0) { if (int s = check_act(dY, act_dtype, "dY", who)) return s; }
+        if (batch > 0 && I > 0) { if (int s = check_act(dX, act_dtype, "dX", who)) return s; }
+        if (db && O > 0) {
+            if (reinterpret_cast<uintptr_t>(db) % 4) return fail(SNACK_ERR_ALIGN, "%s: db misaligned", who);
+            const dim3 grid(static_cast<unsigned>(ceil_div(O, kBlock)));
+            if (act_dtype == SNACK_F32)
+                hipLaunchKernelGGL(bias_grad_kernel<float>, grid, dim3(kBlock), 0, st, O, batch,
+                                   static_cast<const float *>(dY), db);
+            else
+                hipLaunchKernelGGL(bias_grad_kernel<bf16_t>, grid, dim3(kBlock), 0, st, O, batch,
+                                   static_cast<const bf16_t *>(dY), db);
+            if (int s = check_hip("bias_grad_kernel")) return s;
+        }
+        if (batch == 0 || I == 0) return snack::ok();
+        const SpmmPlan p = plan_spmm(nnz, O, batch, act_dtype);
+        if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
+        char *ws = static_cast<char *>(workspace);
+        const float *dyt = static_cast<const float *>(dY);
+        if (!p.direct) {
+            float *dst = reinterpret_cast<float *>(ws + p.off_opnd);
+            if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st)) return s;
+            dyt = dst;
+        }
+        int s;
+        if (act_dtype == SNACK_F32)
+            s = run_spmm<float>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt,
+                                batch, nullptr, static_cast<float *>(dX), ws, st);
+        else
+            s = run_spmm<bf16_t>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt,
+                                 batch, nullptr, static_cast<bf16_t *>(dX), ws, st);
+        return s ? s : snack::ok();
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "snack_coo_bwd_input: unexpected exception");
+    }
+}
+
+extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch,
+                                     int act_dtype, float *dW, void *workspace, size_t workspace_bytes,
+                                     void *hip_stream) {
+    try {
+        const char *who = "snack_coo_grad_weight";
+        if (int s = check_desc(W, false, who)) return s;
+        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
+            return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
+        if (batch < 0 || batch > kMaxBatch)
+            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^22]", who, (long long)batch);
+        const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+        if (nnz == 0) return snack::ok();
+        if (!dW) return fail(SNACK_ERR_NULL, "%s: dW is NULL", who);
+        if (reinterpret_cast<uintptr_t>(dW) % 4) return fail(SNACK_ERR_ALIGN, "%s: dW misaligned", who);
+        hipStream_t st = static_cast<hipStream_t>(hip_stream);
+        if (batch == 0) {
+            hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>(ceil_div(nnz, kBlock))), dim3(kBlock), 0,
+                               st, dW, nnz);
+            if (int s = check_hip("zero_kernel")) return s;
+            return snack::ok();
+        }
+        if (int s = check_act(X, act_dtype, "X", who)) return s;
+        if (int s = check_act(dY, act_dtype, "dY", who)) return s;
+        const SddmmPlan p = plan_sddmm(nnz, O, I, batch, act_dtype);
+        if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
+        char *ws = static_cast<char *>(workspace);
+        const float *xt = static_cast<const float *>(X);
+        const float *dyt = static_cast<const float *>(dY);
+        if (!p.x_direct) {
+            float *dst = reinterpret_cast<float *>(ws + p.off_x);
+            if (int s = launch_to_feature_major(X, act_dtype, batch, I, dst, st)) return s;
+            xt = dst;
+        }
+        if (!p.dy_direct) {
+            float *dst = reinterpret_cast<float *>(ws + p.off_dy);
+            if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st)) return s;
+            dyt = dst;
+        }
+        const int64_t blocks = round_up8(ceil_div(p.waves, kWavesPerBlock));
+        const dim3 grid(static_cast<unsigned>(blocks));
+        probe(true, st);
+        switch (p.bt * 8 + p.vw) {
+#define SNACK_SDDMM(BTV, VWV)                                                                          \
+    case BTV * 8 + VWV:                                                                                \
+        hipLaunchKernelGGL((sddmm_kernel<BTV, VWV>), grid, dim3(kBlock), 0, st, nnz, p.steps, W->rows, \
+                           W->cols, xt, dyt, batch, dW);                                               \
+        break;
+            SNACK_SDDMM(1, 1) SNACK_SDDMM(2, 1) SNACK_SDDMM(4, 1) SNACK_SDDMM(8, 1) SNACK_SDDMM(16, 1)
+            SNACK_SDDMM(1, 4) SNACK_SDDMM(2, 4) SNACK_SDDMM(4, 4) SNACK_SDDMM(8, 4) SNACK_SDDMM(16, 4)
+#undef SNACK_SDDMM
+            default: return fail(SNACK_ERR_INTERNAL, "%s: unsupported plan bt=%d vw=%d", who, p.bt, p.vw);
+        }
+        probe(false, st);
+        if (int s = check_hip("sddmm_kernel")) return s;
+        return snack::ok();
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "snack_coo_grad_weight: unexpected exception");
+    }
+}
+
+extern "C" int snack_coo_set_probe(void *start_event, void *stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(SNACK_ERR_NULL, "snack_coo_set_probe: give both events or neither");
+    g_probe_start = static_cast<hipEvent_t>(start_event);
+    g_probe_stop = static_cast<hipEvent_t>(stop_event);
+    return snack::ok();
+}

@@ -1,0 +1,194 @@
+/*
+ * snack_coo.h -- C ABI of the SNACK truly-sparse linear layer on MI355X (gfx950).
+ *
+ * Source: "Beyond Masked Sparsity: SNACK Enables Truly Sparse Neural Networks
+ * on GPU" (Badour, van Keulen, Mocanu; arXiv:2610.04093).
+ *
+ * The layer's weight W (out_features x in_features, O x I) exists only as its
+ * stored entries, a COO triple (rows[k], cols[k], vals[k]) for k < nnz
+ * (Section 3.1 and Figure 1; the triple is defined in Appendix B, Table 7).
+ * Three device operations make up the layer's hot path:
+ *
+ *   forward      Y  = X W^T + b        Y[b,o]  = bias[o] + sum_{k: rows[k]=o} vals[k] X[b,cols[k]]
+ *   input grad   dX = dY W             dX[b,i] = sum_{k: cols[k]=i} vals[k] dY[b,rows[k]]
+ *   weight grad  dW[k] = sum_b dY[b,rows[k]] X[b,cols[k]]   (only on the stored entries)
+ *
+ * (Algorithm 1 for the forward product; Section 3.4 and Appendix F,
+ * "Full gradient derivation", for both gradients.)  Two host operations sit
+ * beside them: the row-sorted COO builder (Table 7's COO, CSR index pointer
+ * and CSC view) and the magnitude prune-and-regrow topology update of
+ * Appendix G, which regrows with the uniform initializer of Algorithm 2.
+ *
+ * Conventions for every function below:
+ *  - Return value: SNACK_OK (0) or a positive snack_status; no exception
+ *    crosses the ABI.  snack_last_error() gives a message for the last
+ *    failure on the calling thread.
+ *  - Ownership: the caller allocates and frees every buffer.  The library
+ *    keeps no state between calls (apart from the optional per-thread timing
+ *    probe of snack_coo_set_probe) and never allocates device memory; device
+ *    scratch comes from the caller's workspace (see snack_coo_workspace_bytes).
+ *  - Sizes: O, I and nnz fit in int32; batch is at most 2^22.
+ *  - Streams: device calls only enqueue work on hip_stream (a hipStream_t;
+ *    NULL = the default stream) and never synchronise.  Device faults surface
+ *    at the caller's next synchronisation.  Calls on different streams that
+ *    share a workspace race.
+ *  - Layout: activations are row-major and batch-major (X[batch][I],
+ *    Y[batch][O], dY[batch][O], dX[batch][I]), contiguous.  Indices are int32,
+ *    0-based; vals, bias, dW and db are fp32.  Activations are fp32 or bf16
+ *    (SNACK_BF16: X, dY read as bf16; Y, dX written as bf16 rounded to nearest
+ *    even from fp32 accumulators).  All outputs are overwritten.
+ *  - Preconditions on a descriptor (established by snack_coo_build, checked
+ *    there, NOT re-checked by device calls): entries sorted by (row, col),
+ *    unique, in range; row_offsets and the column view consistent with them.
+ *    Device calls check only O(1) things (null pointers, sizes, dtype,
+ *    workspace size).
+ */
+#ifndef SNACK_COO_H
+#define SNACK_COO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum snack_status {
+    SNACK_OK = 0,
+    SNACK_ERR_NULL = 1,        /* a required pointer is NULL */
+    SNACK_ERR_SHAPE = 2,       /* negative or inconsistent sizes, nnz > O*I, sizes beyond int32 */
+    SNACK_ERR_INDEX = 3,       /* builder/topology: a row or column index out of range */
+    SNACK_ERR_DUPLICATE = 4,   /* builder: a (row, col) pair appears twice */
+    SNACK_ERR_ALIGN = 5,       /* a device pointer is not aligned to its element size */
+    SNACK_ERR_DTYPE = 6,       /* unknown activation dtype or op code */
+    SNACK_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than snack_coo_workspace_bytes */
+    SNACK_ERR_HIP = 8,         /* a HIP launch failed (message has hipGetErrorString) */
+    SNACK_ERR_INTERNAL = 9,    /* unexpected internal failure */
+    SNACK_ERR_NOMEM = 10,      /* host allocation failed (builder / topology) */
+    SNACK_ERR_UNSORTED = 11    /* topology: input triple not strictly sorted by (row, col) */
+} snack_status;
+
+enum { SNACK_F32 = 0, SNACK_BF16 = 1 };                                   /* activation dtype */
+enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2 };
+
+/* A layer's weight on the device.  Every pointer is a DEVICE pointer,
+ * borrowed for the duration of the call.
+ *   rows, cols, vals   [nnz]  the triple, sorted by (row, col)
+ *   row_offsets        [O+1]  row_offsets[r] = number of entries with row < r
+ *                             (Table 7's CSR index pointer); required
+ *   col_perm           [nnz]  column view: positions k of the triple listed in
+ *                             (col, row) order (Table 7's CSC order)
+ *   col_rows, col_cols [nnz]  rows[col_perm[j]], cols[col_perm[j]]
+ *   col_offsets        [I+1]  col_offsets[c] = number of entries with col < c
+ * The column view is needed by snack_coo_bwd_input only (NULL elsewhere). */
+typedef struct snack_coo_desc {
+    int64_t out_features;
+    int64_t in_features;
+    int64_t nnz;
+    const int32_t *rows;
+    const int32_t *cols;
+    const float *vals;
+    const int32_t *row_offsets;
+    const int32_t *col_perm;
+    const int32_t *col_rows;
+    const int32_t *col_cols;
+    const int32_t *col_offsets;
+} snack_coo_desc;
+
+/* Host-side COO builder (Appendix B, Table 7: COO triple, CSR index pointer,
+ * CSC view; Section 3.1: the COO and CSR forms are interchangeable).
+ * Inputs rows/cols/vals [nnz] are HOST arrays in any order.  Validates every
+ * index (SNACK_ERR_INDEX), rejects repeated (row, col) pairs
+ * (SNACK_ERR_DUPLICATE) and nnz > O*I or sizes beyond int32 (SNACK_ERR_SHAPE).
+ * Outputs (HOST, caller-allocated; each may be NULL except rows_out and
+ * cols_out when nnz > 0):
+ *   rows_out, cols_out, vals_out [nnz]  the triple sorted by (row, col);
+ *                                       vals are moved bit-exactly
+ *   perm_out        [nnz]  input position of each sorted entry
+ *   row_offsets_out [O+1]
+ *   col_perm_out, col_rows_out, col_cols_out [nnz], col_offsets_out [I+1]:
+ *                          the column view described at snack_coo_desc.
+ * vals may be NULL only if vals_out is NULL.  Pure host code: no GPU needed. */
+int snack_coo_build(int64_t out_features, int64_t in_features, int64_t nnz,
+                    const int32_t *rows, const int32_t *cols, const float *vals,
+                    int32_t *rows_out, int32_t *cols_out, float *vals_out,
+                    int32_t *perm_out, int32_t *row_offsets_out,
+                    int32_t *col_perm_out, int32_t *col_rows_out, int32_t *col_cols_out,
+                    int32_t *col_offsets_out);
+
+/* Bytes of device workspace that `op` (SNACK_OP_*) needs for this layer,
+ * batch size and activation dtype.  0 is a valid answer.  Returns 0 with
+ * snack_last_error() set if the arguments are invalid. */
+size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int64_t batch, int act_dtype);
+
+/* Forward SNACK layer (Algorithm 1 with the nn.Linear bias of Section 3.5):
+ * Y[b,o] = bias[o] + sum_{k: rows[k]=o} vals[k] X[b,cols[k]].
+ *   X     device [batch][I], fp32 or bf16 (act_dtype)
+ *   bias  device [O] fp32 or NULL (= 0); rows without entries output bias
+ *   Y     device [batch][O], same dtype as X, overwritten
+ *   workspace: device, >= snack_coo_workspace_bytes(SNACK_OP_FWD, ...) bytes,
+ *   256-byte aligned.  batch may be 0 (no-op). */
+int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t batch, int act_dtype,
+                  const float *bias, void *Y,
+                  void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Input gradient (Section 3.4 / Appendix F: dL/dX = W^T dL/dA, with W^T
+ * obtained by swapping the row and column index arrays):
+ * dX[b,i] = sum_{k: cols[k]=i} vals[k] dY[b,rows[k]].
+ *   dY  device [batch][O], fp32 or bf16; dX device [batch][I], same dtype
+ *   db  device [O] fp32 or NULL: if given, db[o] = sum_b dY[b,o] (the bias
+ *       gradient of the nn.Linear drop-in)
+ *   Requires the column view in W. */
+int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int64_t batch, int act_dtype,
+                        void *dX, float *db,
+                        void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Weight gradient on the support (Section 3.4 / Appendix F: sum of the batch's
+ * rank-1 outer products evaluated only at (i,j) in supp(W)):
+ * dW[k] = sum_b dY[b,rows[k]] X[b,cols[k]], written in the order of the
+ * triple (fp32, overwritten; entries with vals[k] == 0 are still computed).
+ *   X device [batch][I], dY device [batch][O], fp32 or bf16; dW device [nnz]. */
+int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY,
+                          int64_t batch, int act_dtype, float *dW,
+                          void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Host-side topology update (Appendix G: magnitude prune-and-regrow; regrowth
+ * with the uniform initializer of Algorithm 2).  Input: a HOST triple sorted
+ * strictly by (row, col) (SNACK_ERR_UNSORTED otherwise).
+ *  1. prune the n_prune entries of smallest |vals| (ties: lower position first);
+ *  2. regrow n_prune positions: draw row = getrand(O), then col = getrand(I),
+ *     reject the pair if it is live (survivors and positions already regrown),
+ *     where getrand(n) = floor(u * n / 2^64) of the next SplitMix64 output u
+ *     of a generator started at `seed`; regrown entries get the value +0.0f;
+ *  3. write the result sorted by (row, col) (rows_out, cols_out, vals_out
+ *     [nnz], row_offsets_out [O+1] or NULL) and the number of draws to
+ *     trials_out (or NULL).
+ * O*I is limited to 2^34 positions (a bitmap of live positions is used).
+ * Outputs must not alias the inputs. */
+int snack_coo_topology_update(int64_t out_features, int64_t in_features, int64_t nnz,
+                              const int32_t *rows, const int32_t *cols, const float *vals,
+                              int64_t n_prune, uint64_t seed,
+                              int32_t *rows_out, int32_t *cols_out, float *vals_out,
+                              int32_t *row_offsets_out, int64_t *trials_out);
+
+/* Timing probe for benchmarks and profilers (not part of the method).  While
+ * armed on the calling thread, each device call records `start_event` on its
+ * stream immediately before launching its main kernel (the gather-reduce of
+ * snack_coo_fwd / snack_coo_bwd_input, the sampled product of
+ * snack_coo_grad_weight) and `stop_event` immediately after it, so the pair
+ * brackets exactly that kernel.  Both are caller-owned hipEvent_t handles
+ * created with timing enabled; passing NULL for both disarms the probe.
+ * Returns SNACK_ERR_NULL if exactly one of them is NULL. */
+int snack_coo_set_probe(void *start_event, void *stop_event);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char *snack_last_error(void);
+
+/* ABI version of this header: 1. */
+int snack_coo_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNACK_COO_H */

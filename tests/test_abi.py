@@ -1,0 +1,58 @@
+"""The C-ABI library loads and exports every function include/snack_coo.h declares (CPU only)."""
+import ctypes
+import os
+import re
+
+import coo_spmm_row_amd as snk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "snack_coo.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(snack_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    lib = ctypes.CDLL(snk.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(snk.EXPORTED)
+
+
+def test_abi_version():
+    assert snk.abi_version() == 1
+
+
+def test_binding_loads_only_the_in_tree_library():
+    assert os.path.dirname(snk.LIB_PATH) == os.path.join(ROOT, "coo_spmm_row_amd")
+    assert os.path.exists(snk.LIB_PATH)
+
+
+def test_device_calls_reject_bad_arguments_before_any_launch():
+    """Host-forced failures: the status comes back without touching a GPU."""
+    lib = snk._lib
+    assert lib.snack_coo_fwd(None, None, 1, 0, None, None, None, 0, None) == 1  # NULL descriptor
+    d = snk._Desc()
+    d.out_features, d.in_features, d.nnz = 4, 4, 20  # nnz > O*I
+    assert lib.snack_coo_fwd(ctypes.byref(d), None, 1, 0, None, None, None, 0, None) == 2
+    assert b"nnz" in lib.snack_last_error()
+    d.nnz = 0
+    d.row_offsets = 0x1000
+    assert lib.snack_coo_fwd(ctypes.byref(d), None, 1, 7, None, None, None, 0, None) == 6  # dtype
+    assert lib.snack_coo_fwd(ctypes.byref(d), None, -1, 0, None, None, None, 0, None) == 2  # batch
+    assert lib.snack_coo_fwd(ctypes.byref(d), 0x1000, 1, 0, None, None, None, 0, None) == 1  # Y NULL
+    assert lib.snack_coo_fwd(ctypes.byref(d), 0x1001, 1, 0, None, 0x2000, None, 0, None) == 5  # misaligned X
+    # bwd_input needs the column view
+    d.nnz = 3
+    d.rows = d.cols = d.vals = 0x1000
+    assert lib.snack_coo_bwd_input(ctypes.byref(d), 0x1000, 1, 0, 0x1000, None, None, 0, None) == 1
+    # a too-small workspace
+    d.nnz = 3
+    need = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 8, 0)
+    assert need > 0
+    assert lib.snack_coo_fwd(ctypes.byref(d), 0x1000, 8, 0, None, 0x2000, 0x10000, need - 1, None) == 7
+    assert lib.snack_coo_workspace_bytes(9, ctypes.byref(d), 8, 0) == 0

@@ -1,0 +1,268 @@
+"""HIP path against the fp64 oracle, element by element, through the C ABI (needs a gfx950 GPU)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (NTHREADS, acts, check_close, device_layer, from_device, named_layer, oracle_dw_entries,
+                      oracle_dx_cols, oracle_fwd_rows, say, to_device)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import coo_spmm_row_amd as snk  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def run_all(L, B, seed, bf16=False, bias=True):
+    """fwd, dX, dW (+db) on the GPU and in the oracle; compare everything."""
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    built, W = device_layer(L, DEV)
+    x_in, x64 = acts(seed, B, I, bf16)
+    dy_in, dy64 = acts(seed + 1, B, O, bf16)
+    X, dY = to_device(x_in, DEV, bf16), to_device(dy_in, DEV, bf16)
+    b = torch.from_numpy(L["bias"]).to(DEV) if bias else None
+    Y = snk.snack_coo_fwd(W, X, b)
+    db = torch.empty(O, dtype=torch.float32, device=DEV)
+    dX = snk.snack_coo_bwd_input(W, dY, db=db)
+    dW = snk.snack_coo_grad_weight(W, X, dY)
+    torch.cuda.synchronize()
+    r, c, v = built["rows"], built["cols"], built["vals"]
+    Yr = oracle.fwd(O, I, r, c, v, x64, L["bias"] if bias else None, nthreads=NTHREADS)
+    dXr = oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS)
+    dWr = oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS)
+    check_close(from_device(Y), Yr, nnz / max(O, 1), "fwd", bf16)
+    check_close(from_device(dX), dXr, nnz / max(I, 1), "dX", bf16)
+    check_close(dW.cpu().numpy(), dWr, B, "dW")
+    check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, "db")
+    return built, W, X, dY, Y, dX, dW
+
+
+# ------------------------------------------------------------ small shapes: tiles + ragged tails
+SMALL = [  # seed, shape, O, I, nnz
+    (101, "uniform", 300, 257, 9000),
+    (102, "empty_rows", 129, 200, 3000),
+    (103, "one_row", 50, 3000, 3000),
+    (104, "one_col", 4000, 37, 4000),
+    (105, "diag", 333, 333, 333),
+    (106, "uniform", 1, 5000, 1500),
+    (107, "uniform", 5000, 1, 700),
+]
+BATCHES = [1, 2, 3, 4, 5, 8, 13, 16, 20, 32, 64, 68, 100, 130]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}")
+@pytest.mark.parametrize("B", BATCHES)
+def test_small_shapes_fp32(case, B):
+    seed, shape, O, I, nnz = case
+    say(f"small fp32 {shape} {O}x{I} nnz={nnz} B={B}")
+    L = synth.random_small_layer(seed, O, I, nnz, shape)
+    run_all(L, B, seed + B)
+
+
+@pytest.mark.parametrize("B", [1, 3, 4, 16, 64, 72])
+def test_small_shapes_bf16(B):
+    say(f"small bf16 B={B}")
+    L = synth.random_small_layer(111, 260, 310, 8000, "empty_rows")
+    run_all(L, B, 900 + B, bf16=True)
+
+
+def test_no_bias_and_zero_batch():
+    say("no bias, batch 0")
+    L = synth.random_small_layer(121, 64, 80, 900, "uniform")
+    run_all(L, 7, 5, bias=False)
+    built, W = device_layer(L, DEV)
+    X = torch.zeros((0, 80), device=DEV)
+    assert snk.snack_coo_fwd(W, X).shape == (0, 64)
+    dW = snk.snack_coo_grad_weight(W, X, torch.zeros((0, 64), device=DEV))
+    torch.cuda.synchronize()
+    assert not torch.any(dW)
+
+
+def test_empty_layer():
+    say("nnz = 0")
+    L = {"rows": np.zeros(0, np.int32), "cols": np.zeros(0, np.int32), "vals": np.zeros(0, np.float32),
+         "bias": np.linspace(-1, 1, 40).astype(np.float32), "out_features": 40, "in_features": 30, "nnz": 0}
+    built, W = device_layer(L, DEV)
+    for B in (1, 5, 64):
+        X = torch.randn(B, 30, device=DEV)
+        Y = snk.snack_coo_fwd(W, X, torch.from_numpy(L["bias"]).to(DEV))
+        dX = snk.snack_coo_bwd_input(W, torch.randn(B, 40, device=DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(Y, torch.from_numpy(L["bias"]).to(DEV).expand(B, 40))
+        assert not torch.any(dX)
+
+
+def test_long_rows_span_many_chunks():
+    """A row far longer than one wave's chunk (power-law heavy rows)."""
+    say("long rows")
+    O, I = 6, 30000
+    rng = np.random.Generator(np.random.PCG64(5))
+    parts = []
+    for r, n in ((1, 30000), (2, 1), (4, 17000)):
+        parts.append(r * I + np.sort(rng.choice(I, n, replace=False)))
+    pos = np.concatenate(parts)
+    L = {"rows": (pos // I).astype(np.int32), "cols": (pos % I).astype(np.int32),
+         "vals": rng.standard_normal(pos.size).astype(np.float32) * 0.01,
+         "bias": rng.standard_normal(O).astype(np.float32), "out_features": O, "in_features": I, "nnz": pos.size}
+    for B in (1, 2, 8, 16, 64):
+        run_all(L, B, 40 + B)
+
+
+# ------------------------------------------------------------ the workloads
+@pytest.mark.parametrize("B", [4])
+def test_tiny_layer(B):
+    say(f"tiny 512x512 90% B={B}")
+    spec, L = named_layer("tiny")
+    run_all(L, B, 1010)
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_mid_layer(B):
+    say(f"mid 4096x4096 95% B={B}")
+    spec, L = named_layer("mid")
+    run_all(L, B, 2010 + B)
+
+
+@pytest.mark.parametrize("name", ["xs99", "xs999", "xs99_zipf", "xs999_zipf"])
+def test_extreme_sparse_batch1(name):
+    say(f"{name} B=1")
+    spec, L = named_layer(name)
+    built, W, X, dY, Y, dX, dW = run_all(L, 1, 4010)
+    # rows without entries output the bias exactly
+    empty = np.flatnonzero(np.diff(built["row_offsets"]) == 0)
+    if empty.size:
+        assert np.array_equal(Y.cpu().numpy()[0, empty], L["bias"][empty])
+
+
+@pytest.mark.parametrize("name", ["gpt2_qkv", "gpt2_fc", "gpt2_proj"])
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+def test_gpt2_shapes(name, bf16):
+    say(f"{name} B=1024 bf16={bf16}")
+    spec, L = named_layer(name)
+    run_all(L, 1024, 5010, bf16=bf16)
+
+
+def _sampled(name, B, seed, n_rows=64, n_cols=64, n_entries=4096):
+    spec, L = named_layer(name)
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    built, W = device_layer(L, DEV)
+    x, _ = acts(seed, B, I)
+    dy, _ = acts(seed + 1, B, O)
+    X, dYt = to_device(x, DEV), to_device(dy, DEV)
+    b = torch.from_numpy(L["bias"]).to(DEV)
+    Y = snk.snack_coo_fwd(W, X, b).cpu().numpy()
+    dX = snk.snack_coo_bwd_input(W, dYt).cpu().numpy()
+    dW = snk.snack_coo_grad_weight(W, X, dYt).cpu().numpy()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rs = np.sort(rng.choice(O, n_rows, replace=False))
+    cs = np.sort(rng.choice(I, n_cols, replace=False))
+    ks = np.sort(rng.choice(nnz, n_entries, replace=False))
+    ks = np.unique(np.concatenate([ks, [0, nnz - 1]]))
+    check_close(Y[:, rs], oracle_fwd_rows(built, x, L["bias"], rs), nnz / O, f"{name} fwd sample")
+    check_close(dX[:, cs], oracle_dx_cols(built, dy, cs), nnz / I, f"{name} dX sample")
+    check_close(dW[ks], oracle_dw_entries(built, x, dy, ks), B, f"{name} dW sample")
+    # whole-output property at full size: the adjoint identity in fp64
+    Yb = Y.astype(np.float64) - L["bias"].astype(np.float64)
+    a = float(np.sum(dy.astype(np.float64) * Yb))
+    c = float(np.sum(dX.astype(np.float64) * x.astype(np.float64)))
+    d = float(np.dot(dW.astype(np.float64), built["vals"].astype(np.float64)))
+    scale = math.sqrt(B * O) * math.sqrt(nnz) * 1e-5 + 1e-3
+    assert abs(a - c) <= scale and abs(a - d) <= scale, (a, c, d)
+
+
+@pytest.mark.parametrize("B", [1, 16, 64])
+def test_llm_scale_sampled(B):
+    say(f"llm90 10k 90% B={B} sampled")
+    _sampled("llm90", B, 3010 + B)
+
+
+@pytest.mark.parametrize("B", [1, 64])
+def test_target_layer_sampled(B):
+    say(f"target95 10k 95% B={B} sampled")
+    _sampled("target95", B, 3510 + B)
+
+
+def test_target_layer_full_compare_b64():
+    say("target95 B=64 full compare")
+    spec, L = named_layer("target95")
+    run_all(L, 64, 3600)
+
+
+# ------------------------------------------------------------ invariants
+def test_invariants_bias_determinism_scaling_permutation():
+    say("invariants")
+    L = synth.random_small_layer(131, 700, 900, 40000, "empty_rows")
+    built, W = device_layer(L, DEV)
+    b = torch.from_numpy(L["bias"]).to(DEV)
+    for B in (1, 5, 64):
+        X = to_device(synth.make_acts(77 + B, B, 900), DEV)
+        dY = to_device(synth.make_acts(78 + B, B, 700), DEV)
+        # X = 0 gives the bias exactly; dY = 0 gives dX = 0; X = 0 gives dW = 0
+        assert torch.equal(snk.snack_coo_fwd(W, torch.zeros_like(X), b), b.expand(B, 700))
+        assert not torch.any(snk.snack_coo_bwd_input(W, torch.zeros_like(dY)))
+        assert not torch.any(snk.snack_coo_grad_weight(W, torch.zeros_like(X), dY))
+        # deterministic: bit-identical reruns
+        Y1, Y2 = snk.snack_coo_fwd(W, X, b), snk.snack_coo_fwd(W, X, b)
+        assert torch.equal(Y1, Y2)
+        assert torch.equal(snk.snack_coo_bwd_input(W, dY), snk.snack_coo_bwd_input(W, dY))
+        assert torch.equal(snk.snack_coo_grad_weight(W, X, dY), snk.snack_coo_grad_weight(W, X, dY))
+        # power-of-two scaling is exact
+        assert torch.equal(snk.snack_coo_fwd(W, 2 * X), 2 * snk.snack_coo_fwd(W, X))
+        # empty rows output the bias exactly
+        empty = torch.from_numpy(np.flatnonzero(np.diff(built["row_offsets"]) == 0)).to(DEV)
+        assert empty.numel() > 0
+        assert torch.equal(Y1[:, empty], b[empty].expand(B, -1))
+        # a permuted input order builds the same layer and the same outputs
+        p = np.random.Generator(np.random.PCG64(B)).permutation(L["nnz"])
+        built2 = snk.snack_coo_build(700, 900, L["rows"][p], L["cols"][p], L["vals"][p])
+        W2 = snk.SnackCOO.from_built(built2, DEV)
+        assert torch.equal(snk.snack_coo_fwd(W2, X, b), Y1)
+    # true sparsity: device bytes of the weight are 12 nnz + 4 (O+1) plus the column view
+    nnz, O, I = L["nnz"], 700, 900
+    assert W.device_bytes() == 12 * nnz + 4 * (O + 1) + 12 * nnz + 4 * (I + 1)
+
+
+def test_linearity_in_x():
+    say("linearity")
+    L = synth.random_small_layer(141, 300, 400, 12000, "uniform")
+    built, W = device_layer(L, DEV)
+    X1 = to_device(synth.make_acts(1, 16, 400), DEV)
+    X2 = to_device(synth.make_acts(2, 16, 400), DEV)
+    lhs = snk.snack_coo_fwd(W, 0.5 * X1 - 3.0 * X2).cpu().numpy().astype(np.float64)
+    rhs = 0.5 * snk.snack_coo_fwd(W, X1).cpu().numpy().astype(np.float64) - \
+        3.0 * snk.snack_coo_fwd(W, X2).cpu().numpy().astype(np.float64)
+    check_close(lhs, rhs, 40, "linearity")
+
+
+def test_single_entry_and_stored_zero():
+    say("single entry / stored zero")
+    L = {"rows": np.array([3], np.int32), "cols": np.array([5], np.int32), "vals": np.array([0.0], np.float32),
+         "bias": np.arange(8, dtype=np.float32), "out_features": 8, "in_features": 9, "nnz": 1}
+    built, W = device_layer(L, DEV)
+    X = to_device(synth.make_acts(3, 4, 9), DEV)
+    dY = to_device(synth.make_acts(4, 4, 8), DEV)
+    dW = snk.snack_coo_grad_weight(W, X, dY).cpu().numpy()
+    ref = float(np.dot(dY.cpu().numpy()[:, 3].astype(np.float64), X.cpu().numpy()[:, 5].astype(np.float64)))
+    assert dW.shape == (1,) and abs(dW[0] - ref) <= 1e-5 * (1 + abs(ref))  # a stored zero still gets its gradient
+
+
+def test_workspace_contract():
+    say("workspace")
+    L = synth.random_small_layer(151, 100, 120, 2000, "uniform")
+    built, W = device_layer(L, DEV)
+    X = to_device(synth.make_acts(5, 8, 120), DEV)
+    need = snk.snack_coo_workspace_bytes(snk.OP_FWD, W, 8, snk.SNACK_F32)
+    assert need > 0
+    small = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_coo_fwd(W, X, workspace=small)
+    assert e.value.status == "WORKSPACE"
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    assert torch.equal(snk.snack_coo_fwd(W, X, workspace=ws), snk.snack_coo_fwd(W, X))
