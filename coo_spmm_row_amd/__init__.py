@@ -31,7 +31,26 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m coo_spmm_row_amd.build` "
                       "(hipcc --offload-arch=gfx950); there is no fallback path")
 
+# torch ships its own HIP runtime with the same soname as /opt/rocm's.  Loading
+# torch first makes the library bind to that one runtime, so torch's streams
+# and events are valid handles for the library's launches.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln}
+    except OSError:
+        return set()
+    return {os.path.realpath(p) for p in paths}
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError("two HIP runtimes are mapped in this process "
+                      f"({sorted(_hip_runtimes_mapped())}); import torch before loading libsnack_coo")
 
 
 class SnackError(RuntimeError):

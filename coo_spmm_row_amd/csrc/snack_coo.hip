@@ -335,7 +335,8 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t B, int dtype) {
     p.direct = (B == 1 && dtype == SNACK_F32);
     if (B >= 16 && B % 4 == 0) {
         p.mapping = kRowgroup;
-        p.bt = static_cast<int>(std::min<int64_t>(16, B / 4));
+        p.bt = 4;  // lanes per row: the largest power of two <= min(16, B/4)
+        while (p.bt * 2 <= std::min<int64_t>(16, B / 4)) p.bt *= 2;
     } else {
         p.mapping = kSegscan;
         p.bt = pow2_at_least(B);

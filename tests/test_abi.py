@@ -56,3 +56,9 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert need > 0
     assert lib.snack_coo_fwd(ctypes.byref(d), 0x1000, 8, 0, None, 0x2000, 0x10000, need - 1, None) == 7
     assert lib.snack_coo_workspace_bytes(9, ctypes.byref(d), 8, 0) == 0
+
+
+def test_one_hip_runtime_in_process():
+    """The library binds to torch's HIP runtime (same soname), so torch streams and events are valid."""
+    runtimes = snk._hip_runtimes_mapped()
+    assert len(runtimes) == 1, runtimes
