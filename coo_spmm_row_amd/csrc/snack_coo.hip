@@ -21,9 +21,10 @@
 //                 combined by a segmented scan across entry groups; segments cut
 //                 by a chunk edge go to a small partials buffer and are finished
 //                 by fixup_kernel.  Balanced by nnz, so power-law rows are fine.
-//      rowgroup - for batches that are multiples of 4 and >= 16: a group of BT
-//                 lanes owns one output row, each lane holds 4 batch columns and
-//                 gathers float4s of the feature-major operand.
+//      rowwave  - for batches that are multiples of 4 and >= 16: a wave owns one
+//                 output row at a time; its entries are read 64 per coalesced
+//                 load and prefetched a chunk ahead; lane slots gather float4s
+//                 of the feature-major operand with several loads in flight.
 //  * the weight gradient is a sampled dense-dense product over the stored
 //    entries: a group of BT lanes per entry, each lane a slice of the batch,
 //    reduced across the group by xor shuffles.
@@ -44,7 +45,7 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;               // 4 waves per workgroup
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kXcds = 8;                  // MI355X: 8 accelerator dies, round-robin dispatch
-constexpr int64_t kMaxBatch = int64_t(1) << 22;  // keeps every grid.y within 65535
+constexpr int64_t kMaxBatch = int64_t(1) << 21;  // keeps every grid.y within 65535
 
 typedef uint16_t bf16_t;
 
@@ -67,6 +68,26 @@ __device__ __forceinline__ void store_act(bf16_t *p, int64_t i, float v) {
     p[i] = h;
 }
 
+// Cross-lane moves within a row of 16 lanes (DPP).  Controls: quad_perm
+// [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16); every lane of the
+// group receives the group's sum.  The pairings (xor 1, xor 2, mirror within 8,
+// mirror within 16) form a butterfly, so each step adds two disjoint partial sums.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp_move<0xB1>(v);
+    if constexpr (N >= 4) v += dpp_move<0x4E>(v);
+    if constexpr (N >= 8) v += dpp_move<0x141>(v);
+    if constexpr (N >= 16) v += dpp_move<0x140>(v);
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+    return v;
+}
+
 // Logical workgroup index such that each XCD (blockIdx.x % 8 under round-robin
 // dispatch) works on one contiguous eighth of the logical range.  gridDim.x is
 // a multiple of 8; callers drop logical ids beyond their real count.
@@ -76,19 +97,29 @@ __device__ __forceinline__ int64_t xcd_block() {
 }
 
 // ---------------------------------------------------------------- layout
-// in [B][F] (batch-major, fp32 or bf16)  ->  out [F][B] fp32 (feature-major)
+// in [B][F] (batch-major, fp32 or bf16)  ->  out [F][B] fp32 (feature-major).
+// A workgroup moves a tile of 16 features x 64 batch rows through LDS: every
+// thread issues its four loads (64-byte row segments) before its stores, and
+// the tile's output is one contiguous run when B <= 64.
+constexpr int kTf = 16, kTb = 64;
 template <typename InT>
 __global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__restrict__ in,
                                                                   float *__restrict__ out,
                                                                   int64_t B, int64_t F) {
-    __shared__ float tile[64][65];
-    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 64;
-    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    const int nb = static_cast<int>(min<int64_t>(64, B - b0));
-    const int nf = static_cast<int>(min<int64_t>(64, F - f0));
-    for (int bb = ty; bb < nb; bb += 4)
-        if (tx < nf) tile[bb][tx] = load_act(in, (b0 + bb) * F + f0 + tx);
+    __shared__ float tile[kTb][kTf + 1];
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kTf;
+    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTb;
+    const int tx = threadIdx.x % kTf, ty = threadIdx.x / kTf;  // 16 x 16
+    const int nb = static_cast<int>(min<int64_t>(kTb, B - b0));
+    const int nf = static_cast<int>(min<int64_t>(kTf, F - f0));
+    float v[kTb / 16];
+#pragma unroll
+    for (int i = 0; i < kTb / 16; ++i) {
+        const int bb = ty + 16 * i;
+        v[i] = (bb < nb && tx < nf) ? load_act(in, (b0 + bb) * F + f0 + tx) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kTb / 16; ++i) tile[ty + 16 * i][tx] = v[i];
     __syncthreads();
     for (int li = threadIdx.x; li < nf * nb; li += kBlock) {
         const int ff = li / nb, bb = li % nb;
@@ -110,6 +141,7 @@ __global__ __launch_bounds__(kBlock) void segscan_kernel(
     const float *__restrict__ opnd, int64_t B, const float *__restrict__ bias, OutT *__restrict__ out,
     int64_t out_ld, float *__restrict__ head, float *__restrict__ tail) {
     constexpr int G = kWave / BT;
+    constexpr int U = 4;  // steps whose loads are issued together
     const int lane = threadIdx.x & (kWave - 1);
     const int g = lane / BT, t = lane % BT;
     const int64_t j = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
@@ -123,39 +155,52 @@ __global__ __launch_bounds__(kBlock) void segscan_kernel(
     const int first_key = keys[kbeg];
     float carry = 0.f;
     int carry_key = -4;
-    for (int64_t base = kbeg; base < kend; base += G) {
-        const int64_t k = base + g;
-        const bool valid = k < kend;
-        int key = -2, nkey = -3;
-        float p = 0.f;
-        if (valid) {
-            key = keys[k];
-            nkey = (k + 1 < kend) ? keys[k + 1] : -3;
-            const float v = vals[perm ? static_cast<int64_t>(perm[k]) : k];
-            const int64_t c = gidx[k];
-            if (bok) p = v * opnd[c * B + b];
-        }
-        // segmented inclusive scan across the G entry groups (keys are sorted,
-        // so equal keys at distance d mean the whole span shares the key)
+    for (int64_t base = kbeg; base < kend; base += U * G) {
+        int key[U], nkey[U];
+        float p[U];
+        int64_t c[U];
+        float v[U];
 #pragma unroll
-        for (int d = 1; d < G; d <<= 1) {
-            const float up = __shfl_up(p, d * BT, kWave);
-            const int upkey = __shfl_up(key, d * BT, kWave);
-            if (g >= d && upkey == key) p += up;
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = base + u * G + g;
+            key[u] = -2;
+            nkey[u] = -3;
+            c[u] = 0;
+            v[u] = 0.f;
+            if (k < kend) {
+                key[u] = keys[k];
+                nkey[u] = (k + 1 < kend) ? keys[k + 1] : -3;
+                v[u] = vals[perm ? static_cast<int64_t>(perm[k]) : k];
+                c[u] = gidx[k];
+            }
         }
-        if (key == carry_key) p += carry;
-        carry = __shfl(p, (G - 1) * BT + t, kWave);
-        carry_key = __shfl(key, (G - 1) * BT + t, kWave);
-        if (valid && bok && nkey != key) {
-            const bool cut_left = key == prev_key;
-            const bool cut_right = (k == kend - 1) && key == next_key;
-            if (cut_left || cut_right) {
-                if (key == first_key)
-                    head[j * B + b] = p;
-                else
-                    tail[j * B + b] = p;
-            } else {
-                store_act(out, b * out_ld + key, p + (bias ? bias[key] : 0.f));
+#pragma unroll
+        for (int u = 0; u < U; ++u) p[u] = (key[u] != -2 && bok) ? v[u] * opnd[c[u] * B + b] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = base + u * G + g;
+            // segmented inclusive scan across the G entry groups (keys are sorted,
+            // so equal keys at distance d mean the whole span shares the key)
+#pragma unroll
+            for (int d = 1; d < G; d <<= 1) {
+                const float up = __shfl_up(p[u], d * BT, kWave);
+                const int upkey = __shfl_up(key[u], d * BT, kWave);
+                if (g >= d && upkey == key[u]) p[u] += up;
+            }
+            if (key[u] == carry_key) p[u] += carry;
+            carry = __shfl(p[u], (G - 1) * BT + t, kWave);
+            carry_key = __shfl(key[u], (G - 1) * BT + t, kWave);
+            if (key[u] != -2 && bok && nkey[u] != key[u]) {
+                const bool cut_left = key[u] == prev_key;
+                const bool cut_right = (k == kend - 1) && key[u] == next_key;
+                if (cut_left || cut_right) {
+                    if (key[u] == first_key)
+                        head[j * B + b] = p[u];
+                    else
+                        tail[j * B + b] = p[u];
+                } else {
+                    store_act(out, b * out_ld + key[u], p[u] + (bias ? bias[key[u]] : 0.f));
+                }
             }
         }
     }
@@ -187,59 +232,113 @@ __global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B,
     }
 }
 
-// ---------------------------------------------------------------- rowgroup mapping
-template <int BT, typename OutT>
-__global__ __launch_bounds__(kBlock) void rowgroup_kernel(
+// ---------------------------------------------------------------- rowwave mapping
+// For batches that are multiples of 4.  A workgroup of 4 waves owns 4/WPR
+// output keys (rows), each split over WPR waves.  Lanes are (slot e, lane t):
+// S = 64/BT slots each take one stored entry per step, lane t holds batch
+// columns b0+4t .. b0+4t+3 (one float4 of the feature-major operand row).  A
+// wave reads its key's entries 64 at a time (chunks c, c+WPR, ...) with one
+// coalesced load per lane, prefetches its next chunk while the current one is
+// consumed, and keeps U float4 gathers in flight.  Slot partial sums are
+// combined by xor shuffles, the WPR waves of a key through LDS.
+template <int BT, int WPR, typename OutT>
+__global__ __launch_bounds__(kBlock) void rowwave_kernel(
     int64_t nkeys, const int32_t *__restrict__ offs, const int32_t *__restrict__ gidx,
     const float *__restrict__ vals, const int32_t *__restrict__ perm, const float *__restrict__ opnd,
     int64_t B, const float *__restrict__ bias, OutT *__restrict__ out, int64_t out_ld) {
-    constexpr int G = kWave / BT;
+    constexpr int S = kWave / BT;
+    constexpr int U = (S * 4 <= kWave) ? 4 : kWave / S;  // S*U divides 64
+    constexpr int KPB = kWavesPerBlock / WPR;             // keys per workgroup
+    __shared__ float4 part[kWavesPerBlock][BT];
     const int lane = threadIdx.x & (kWave - 1);
-    const int g = lane / BT, t = lane % BT;
-    const int64_t r = (xcd_block() * kWavesPerBlock + threadIdx.x / kWave) * G + g;
-    if (r >= nkeys) return;
+    const int wave = threadIdx.x / kWave;
+    const int e = lane / BT, t = lane % BT;
+    const int64_t r = xcd_block() * KPB + wave / WPR;
+    const int wsub = wave % WPR;
+    const bool rok = r < nkeys;  // uniform per wave
     const int64_t b0 = static_cast<int64_t>(blockIdx.y) * (4 * BT) + 4 * t;
-    if (b0 >= B) return;  // B % 4 == 0, so b0 < B means all four columns exist
-    const int64_t s = offs[r], e = offs[r + 1];
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int64_t k = s;
-    for (; k + 4 <= e; k += 4) {
-        float v[4];
-        int64_t c[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            v[u] = vals[perm ? static_cast<int64_t>(perm[k + u]) : k + u];
-            c[u] = gidx[k + u];
+    const bool bok = b0 < B;     // B % 4 == 0: all four columns exist
+    const int64_t B4 = B / 4;
+    const float4 *__restrict__ op4 = reinterpret_cast<const float4 *>(opnd) + b0 / 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (rok) {
+        const int64_t s = offs[r], end = offs[r + 1];
+        int mc = 0;
+        float mv = 0.f;
+        int64_t first = s + static_cast<int64_t>(wsub) * kWave;
+        if (first + lane < end) {
+            mc = gidx[first + lane];
+            mv = vals[perm ? static_cast<int64_t>(perm[first + lane]) : first + lane];
         }
-        float4 x[4];
+        for (int64_t base = first; base < end; base += WPR * kWave) {
+            const int cc = mc;
+            const float cv = mv;
+            const int n = static_cast<int>(min<int64_t>(kWave, end - base));
+            const int64_t nb = base + WPR * kWave;
+            if (nb < end) {  // prefetch this wave's next chunk
+                mc = 0;
+                mv = 0.f;
+                if (nb + lane < end) {
+                    mc = gidx[nb + lane];
+                    mv = vals[perm ? static_cast<int64_t>(perm[nb + lane]) : nb + lane];
+                }
+            }
+            for (int h = 0; h < n; h += S * U) {
+                float4 x[U];
+                float v[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4 *>(opnd + c[u] * B + b0);
+                for (int u = 0; u < U; ++u) {
+                    const int src = h + u * S + e;  // < 64
+                    const int c = __shfl(cc, src, kWave);
+                    v[u] = __shfl(cv, src, kWave);
+                    const bool live = bok && src < n;
+                    x[u] = live ? op4[static_cast<int64_t>(c) * B4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (!live) v[u] = 0.f;
+                }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a0 += v[u] * x[u].x;
-            a1 += v[u] * x[u].y;
-            a2 += v[u] * x[u].z;
-            a3 += v[u] * x[u].w;
+                for (int u = 0; u < U; ++u) {
+                    acc.x += v[u] * x[u].x;
+                    acc.y += v[u] * x[u].y;
+                    acc.z += v[u] * x[u].z;
+                    acc.w += v[u] * x[u].w;
+                }
+            }
         }
     }
-    for (; k < e; ++k) {
-        const float v = vals[perm ? static_cast<int64_t>(perm[k]) : k];
-        const float4 x = *reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(gidx[k]) * B + b0);
-        a0 += v * x.x;
-        a1 += v * x.y;
-        a2 += v * x.z;
-        a3 += v * x.w;
+#pragma unroll
+    for (int d = BT; d < kWave; d <<= 1) {
+        acc.x += __shfl_xor(acc.x, d, kWave);
+        acc.y += __shfl_xor(acc.y, d, kWave);
+        acc.z += __shfl_xor(acc.z, d, kWave);
+        acc.w += __shfl_xor(acc.w, d, kWave);
     }
-    const float bv = bias ? bias[r] : 0.f;
-    store_act(out, (b0 + 0) * out_ld + r, a0 + bv);
-    store_act(out, (b0 + 1) * out_ld + r, a1 + bv);
-    store_act(out, (b0 + 2) * out_ld + r, a2 + bv);
-    store_act(out, (b0 + 3) * out_ld + r, a3 + bv);
+    if constexpr (WPR > 1) {
+        if (e == 0) part[wave][t] = acc;
+        __syncthreads();
+        if (wsub == 0 && e == 0) {
+#pragma unroll
+            for (int q = 1; q < WPR; ++q) {
+                const float4 o = part[wave + q][t];
+                acc.x += o.x;
+                acc.y += o.y;
+                acc.z += o.z;
+                acc.w += o.w;
+            }
+        }
+    }
+    if (rok && wsub == 0 && e == 0 && bok) {
+        const float bv = bias ? bias[r] : 0.f;
+        store_act(out, (b0 + 0) * out_ld + r, acc.x + bv);
+        store_act(out, (b0 + 1) * out_ld + r, acc.y + bv);
+        store_act(out, (b0 + 2) * out_ld + r, acc.z + bv);
+        store_act(out, (b0 + 3) * out_ld + r, acc.w + bv);
+    }
 }
 
 // ---------------------------------------------------------------- weight gradient
 // xt [I][B], dyt [O][B] feature-major fp32.  A group of BT lanes per entry; lane
-// t covers batch columns t*VW + m*BT*VW (+0..VW-1).
+// t covers batch columns t*VW + m*BT*VW (+0..VW-1).  Four steps of G entries are
+// loaded before any is reduced, so each lane has several gathers in flight.
 template <int BT, int VW>
 __global__ __launch_bounds__(kBlock) void sddmm_kernel(int64_t nnz, int64_t steps,
                                                        const int32_t *__restrict__ rows,
@@ -248,34 +347,254 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(int64_t nnz, int64_t step
                                                        const float *__restrict__ dyt, int64_t B,
                                                        float *__restrict__ dW) {
     constexpr int G = kWave / BT;
+    constexpr int U = 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int g = lane / BT, t = lane % BT;
     const int64_t w = xcd_block() * kWavesPerBlock + threadIdx.x / kWave;
     const int64_t kbase = w * steps * G;
-    for (int64_t s = 0; s < steps; ++s) {
-        const int64_t k = kbase + s * G + g;
+    for (int64_t s = 0; s < steps; s += U) {
         if (kbase + s * G >= nnz) break;  // uniform per wave
-        const bool valid = k < nnz;
-        float acc = 0.f;
-        if (valid) {
-            const float *xr = xt + static_cast<int64_t>(cols[k]) * B;
-            const float *yr = dyt + static_cast<int64_t>(rows[k]) * B;
-            if constexpr (VW == 4) {
-                for (int64_t bb = 4 * t; bb < B; bb += 4 * BT) {
-                    const float4 x = *reinterpret_cast<const float4 *>(xr + bb);
-                    const float4 y = *reinterpret_cast<const float4 *>(yr + bb);
-                    acc += x.x * y.x;
-                    acc += x.y * y.y;
-                    acc += x.z * y.z;
-                    acc += x.w * y.w;
+        int64_t k[U];
+        bool valid[U];
+        const float *xr[U];
+        const float *yr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            k[u] = kbase + (s + u) * G + g;
+            valid[u] = (s + u < steps) && k[u] < nnz;
+            xr[u] = xt + (valid[u] ? static_cast<int64_t>(cols[k[u]]) * B : 0);
+            yr[u] = dyt + (valid[u] ? static_cast<int64_t>(rows[k[u]]) * B : 0);
+        }
+        float acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = 0.f;
+        if constexpr (VW == 4) {
+            for (int64_t bb = 4 * t; bb < B; bb += 4 * BT) {
+                float4 x[U], y[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    x[u] = valid[u] ? *reinterpret_cast<const float4 *>(xr[u] + bb) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    y[u] = valid[u] ? *reinterpret_cast<const float4 *>(yr[u] + bb) : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
-            } else {
-                for (int64_t bb = t; bb < B; bb += BT) acc += xr[bb] * yr[bb];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    acc[u] += x[u].x * y[u].x;
+                    acc[u] += x[u].y * y[u].y;
+                    acc[u] += x[u].z * y[u].z;
+                    acc[u] += x[u].w * y[u].w;
+                }
+            }
+        } else {
+            for (int64_t bb = t; bb < B; bb += BT) {
+                float x[U], y[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    x[u] = valid[u] ? xr[u][bb] : 0.f;
+                    y[u] = valid[u] ? yr[u][bb] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[u] += x[u] * y[u];
             }
         }
 #pragma unroll
-        for (int d = BT / 2; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, kWave);
-        if (valid && t == 0) dW[k] = acc;
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int d = BT / 2; d >= 1; d >>= 1) acc[u] += __shfl_xor(acc[u], d, kWave);
+            if (valid[u] && t == 0) dW[k[u]] = acc[u];
+        }
+    }
+}
+
+// Weight gradient for batches that are multiples of 4 (and >= 16).  A wave owns
+// a range of stored entries, read 64 at a time with the next 64 prefetched;
+// lanes are (slot e, lane t) with S = 64/BT slots, one entry each per step;
+// lane t covers batch float4s t, t+BT, ... of the entry's feature-major X row
+// (gathered, U steps in flight) and of its dY row, which is kept in registers
+// while consecutive entries stay in the same row (Q = B/(4*BT) float4s per
+// lane; Q == 0 means "too many to cache": reload per entry).  Each slot's BT
+// lanes are summed by xor shuffles.  Row offsets are 32-bit (the
+// feature-major copies are < 8 GB).
+template <int BT, int Q>
+__global__ __launch_bounds__(kBlock) void sddmm_wide_kernel(int64_t nnz, int64_t per_wave,
+                                                            const int32_t *__restrict__ rows,
+                                                            const int32_t *__restrict__ cols,
+                                                            const float *__restrict__ xt,
+                                                            const float *__restrict__ dyt, int64_t B,
+                                                            float *__restrict__ dW) {
+    constexpr int S = kWave / BT;
+    constexpr int U = 4;
+    constexpr int QC = Q > 0 ? Q : 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int e = lane / BT, t = lane % BT;
+    const int64_t wv = xcd_block() * kWavesPerBlock + threadIdx.x / kWave;
+    const int64_t k0 = wv * per_wave;
+    if (k0 >= nnz) return;  // uniform per wave
+    const int64_t k1 = min(k0 + per_wave, nnz);
+    const int B4 = static_cast<int>(B / 4);
+    const float4 *__restrict__ x4 = reinterpret_cast<const float4 *>(xt);
+    const float4 *__restrict__ y4 = reinterpret_cast<const float4 *>(dyt);
+    int crow = -1;          // row whose dY slice is cached
+    float4 dyc[QC];
+    int mr = 0, mc = 0;
+    if (k0 + lane < k1) {
+        mr = rows[k0 + lane];
+        mc = cols[k0 + lane];
+    }
+    for (int64_t base = k0; base < k1; base += kWave) {
+        const int cr = mr, cc = mc;
+        const int n = static_cast<int>(min<int64_t>(kWave, k1 - base));
+        const int64_t nb = base + kWave;
+        if (nb < k1) {
+            mr = 0;
+            mc = 0;
+            if (nb + lane < k1) {
+                mr = rows[nb + lane];
+                mc = cols[nb + lane];
+            }
+        }
+        for (int h = 0; h < n; h += S * U) {
+            int ro[U];
+            float p[U];
+            if constexpr (Q > 0) {
+                float4 xv[U][QC];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int src = h + u * S + e;  // < 64 because S*U divides 64
+                    const int xo = __shfl(cc, src, kWave) * B4 + t;
+                    ro[u] = __shfl(cr, src, kWave);
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) xv[u][q] = x4[xo + q * BT];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (ro[u] != crow) {  // row changed: refresh the cached dY slice
+                        crow = ro[u];
+#pragma unroll
+                        for (int q = 0; q < Q; ++q) dyc[q] = y4[crow * B4 + t + q * BT];
+                    }
+                    p[u] = 0.f;
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) {
+                        p[u] += xv[u][q].x * dyc[q].x;
+                        p[u] += xv[u][q].y * dyc[q].y;
+                        p[u] += xv[u][q].z * dyc[q].z;
+                        p[u] += xv[u][q].w * dyc[q].w;
+                    }
+                }
+            } else {
+                int xo[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int src = h + u * S + e;
+                    xo[u] = __shfl(cc, src, kWave) * B4;
+                    ro[u] = __shfl(cr, src, kWave) * B4;
+                    p[u] = 0.f;
+                }
+                for (int q = t; q < B4; q += BT) {
+                    float4 xv[U], yv[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        xv[u] = x4[xo[u] + q];
+                        yv[u] = y4[ro[u] + q];
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        p[u] += xv[u].x * yv[u].x;
+                        p[u] += xv[u].y * yv[u].y;
+                        p[u] += xv[u].z * yv[u].z;
+                        p[u] += xv[u].w * yv[u].w;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                p[u] = group_sum<BT>(p[u]);
+                const int src = h + u * S + e;
+                if (t == 0 && src < n) dW[base + src] = p[u];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- small-batch input gradient
+// For small B*I: each workgroup owns a contiguous range of stored entries in
+// row order (coalesced reads of rows, cols, vals), scatters vals[k]*dY[b,rows[k]]
+// into a private LDS copy of dX ([B][I]) with LDS atomic adds, and writes the
+// copy to partial[w].  dx_reduce_kernel sums the partials in workgroup order.
+// Summation order inside a workgroup follows the LDS atomics, so results are
+// equal to rounding but not bit-reproducible run to run.
+constexpr int kScatterThreads = 1024;
+
+template <typename InT>
+__global__ __launch_bounds__(kScatterThreads) void dx_scatter_kernel(int64_t nnz, int64_t per_wg, int64_t O,
+                                                                     int64_t I, int64_t B,
+                                                                     const int32_t *__restrict__ rows,
+                                                                     const int32_t *__restrict__ cols,
+                                                                     const float *__restrict__ vals,
+                                                                     const InT *__restrict__ dY,
+                                                                     float *__restrict__ partial) {
+    extern __shared__ float dxs[];
+    const int64_t n = B * I;
+    for (int64_t i = threadIdx.x; i < n; i += kScatterThreads) dxs[i] = 0.f;
+    __syncthreads();
+    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * per_wg;
+    const int64_t k1 = min(k0 + per_wg, nnz);
+    constexpr int U = 4;
+    for (int64_t k = k0 + threadIdx.x; k < k1; k += U * kScatterThreads) {
+        int r[U], c[U];
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kk = k + u * kScatterThreads;
+            const bool ok = kk < k1;
+            r[u] = ok ? rows[kk] : 0;
+            c[u] = ok ? cols[kk] : 0;
+            v[u] = ok ? vals[kk] : 0.f;
+        }
+        for (int64_t b = 0; b < B; ++b) {
+            float d[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) d[u] = load_act(dY, b * O + r[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (k + u * kScatterThreads < k1) atomicAdd(&dxs[b * I + c[u]], v[u] * d[u]);
+        }
+    }
+    __syncthreads();
+    float *__restrict__ mine = partial + static_cast<int64_t>(blockIdx.x) * n;
+    for (int64_t i = threadIdx.x; i < n; i += kScatterThreads) mine[i] = dxs[i];
+}
+
+// out[i] = sum over w of partial[w][i], w ascending within each of 4 interleaved
+// slices, then the slices in order: a fixed summation order.  A workgroup covers
+// 64 outputs; its 4 waves take the slices and keep 8 loads in flight.
+template <typename OutT>
+__global__ __launch_bounds__(kBlock) void dx_reduce_kernel(int64_t n, int64_t nparts,
+                                                           const float *__restrict__ partial,
+                                                           OutT *__restrict__ out) {
+    __shared__ float slice_sum[kWavesPerBlock][kWave];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+    float s = 0.f;
+    if (i < n) {
+        constexpr int U = 8;
+        int64_t w = wave;
+        for (; w + (U - 1) * kWavesPerBlock < nparts; w += U * kWavesPerBlock) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = partial[(w + u * kWavesPerBlock) * n + i];
+#pragma unroll
+            for (int u = 0; u < U; ++u) s += v[u];
+        }
+        for (; w < nparts; w += kWavesPerBlock) s += partial[w * n + i];
+    }
+    slice_sum[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && i < n) {
+        float tot = slice_sum[0][lane];
+#pragma unroll
+        for (int q = 1; q < kWavesPerBlock; ++q) tot += slice_sum[q][lane];
+        store_act(out, i, tot);
     }
 }
 
@@ -312,14 +631,15 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up8(int64_t x) { return ceil_div(x, kXcds) * kXcds; }
 
-enum Mapping { kSegscan = 0, kRowgroup = 1 };
+enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2 };
+constexpr int64_t kScatterLdsFloats = 16384;  // 64 KB private dX copy per workgroup
 
 // Device work plan of one gather-reduce (forward or input gradient).
 struct SpmmPlan {
     Mapping mapping;
-    int bt;              // batch lanes per entry group (segscan) or lanes per row (rowgroup)
-    int64_t chunk;       // segscan: entries per wave
-    int64_t nchunks;
+    int bt;              // batch lanes per entry group (segscan) or lanes per slot (rowwave)
+    int64_t chunk;       // segscan: entries per wave; scatter: entries per workgroup
+    int64_t nchunks;     // segscan: waves; scatter: workgroups (partial copies)
     bool direct;         // operand used in place (fp32, batch 1) instead of a transposed copy
     size_t off_opnd, off_head, off_tail, total;
 };
@@ -330,12 +650,26 @@ inline int pow2_at_least(int64_t x) {
     return p;
 }
 
-SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t B, int dtype) {
+// nout = outputs per batch row; scatter_ok: the caller can run the scatter
+// mapping (input gradient: row-order entries, outputs indexed by column).
+SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok) {
     SpmmPlan p{};
     p.direct = (B == 1 && dtype == SNACK_F32);
+    if (scatter_ok && B <= 4 && B * nout <= kScatterLdsFloats && nnz > 0) {
+        p.mapping = kScatter;
+        p.direct = true;  // reads dY in its batch-major layout
+        p.nchunks = std::min<int64_t>(std::max<int64_t>(ceil_div(nnz, 4096), 1), 256);
+        p.chunk = ceil_div(nnz, p.nchunks);
+        size_t at = 0;
+        p.off_opnd = p.off_tail = 0;
+        p.off_head = at;
+        at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B * nout));
+        p.total = at;
+        return p;
+    }
     if (B >= 16 && B % 4 == 0) {
-        p.mapping = kRowgroup;
-        p.bt = 4;  // lanes per row: the largest power of two <= min(16, B/4)
+        p.mapping = kRowwave;
+        p.bt = 4;  // lanes per slot: the largest power of two <= min(16, B/4)
         while (p.bt * 2 <= std::min<int64_t>(16, B / 4)) p.bt *= 2;
     } else {
         p.mapping = kSegscan;
@@ -359,24 +693,34 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t B, int dtype) {
 }
 
 struct SddmmPlan {
+    bool wide;           // sddmm_wide_kernel (batch a multiple of 4, >= 16) or sddmm_kernel
     int bt, vw;
-    int64_t steps, waves;
+    int64_t steps, waves, per_wave;
     bool x_direct, dy_direct;
     size_t off_x, off_dy, total;
 };
 
 SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
     SddmmPlan p{};
-    p.vw = (B % 4 == 0) ? 4 : 1;
-    // about 16 batch columns per lane before the cross-lane reduction
-    int64_t bt = std::max<int64_t>(1, B / 16);
-    int b2 = 1;
-    while (b2 * 2 <= bt && b2 < 16) b2 <<= 1;
-    p.bt = b2;
-    const int64_t G = kWave / p.bt;
     const int64_t target_waves = 8192;
-    p.steps = std::min<int64_t>(std::max<int64_t>(ceil_div(std::max<int64_t>(nnz, 1), G * target_waves), 1), 64);
-    p.waves = ceil_div(nnz, G * p.steps);
+    if (B >= 16 && B % 4 == 0) {
+        p.wide = true;
+        p.bt = 4;  // lanes per entry: the largest power of two <= min(16, B/4)
+        while (p.bt * 2 <= std::min<int64_t>(16, B / 4)) p.bt *= 2;
+        p.per_wave = std::min<int64_t>(256, ceil_div(ceil_div(std::max<int64_t>(nnz, 1), target_waves), kWave) * kWave);
+        p.waves = ceil_div(nnz, p.per_wave);
+    } else {
+        p.wide = false;
+        p.vw = (B % 4 == 0) ? 4 : 1;
+        // about 16 batch columns per lane before the cross-lane reduction
+        int64_t bt = std::max<int64_t>(1, B / 16);
+        int b2 = 1;
+        while (b2 * 2 <= bt && b2 < 16) b2 <<= 1;
+        p.bt = b2;
+        const int64_t G = kWave / p.bt;
+        p.steps = std::min<int64_t>(std::max<int64_t>(ceil_div(std::max<int64_t>(nnz, 1), G * target_waves), 1), 64);
+        p.waves = ceil_div(nnz, G * p.steps);
+    }
     p.x_direct = p.dy_direct = (B == 1 && dtype == SNACK_F32);
     size_t at = 0;
     p.off_x = at;
@@ -430,7 +774,7 @@ int check_workspace(void *ws, size_t have, size_t need, const char *who) {
 // activation [B][F] -> feature-major fp32 [F][B] in `dst`
 int launch_to_feature_major(const void *src, int dtype, int64_t B, int64_t F, float *dst, hipStream_t st) {
     if (B == 0 || F == 0) return SNACK_OK;
-    const dim3 grid(static_cast<unsigned>(ceil_div(F, 64)), static_cast<unsigned>(ceil_div(B, 64)));
+    const dim3 grid(static_cast<unsigned>(ceil_div(F, kTf)), static_cast<unsigned>(ceil_div(B, kTb)));
     if (dtype == SNACK_F32)
         hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(kBlock), 0, st,
                            static_cast<const float *>(src), dst, B, F);
@@ -452,14 +796,20 @@ void launch_segscan_bt(const SpmmPlan &p, int64_t nnz, const int32_t *keys, cons
 }
 
 template <typename OutT, int BT>
-void launch_rowgroup_bt(int64_t nkeys, const int32_t *offs, const int32_t *gidx, const float *vals,
-                        const int32_t *perm, const float *opnd, int64_t B, const float *bias, OutT *out,
-                        int64_t out_ld, hipStream_t st) {
-    constexpr int G = kWave / BT;
-    const int64_t blocks = round_up8(ceil_div(nkeys, G * kWavesPerBlock));
+void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const int32_t *gidx, const float *vals,
+                       const int32_t *perm, const float *opnd, int64_t B, const float *bias, OutT *out,
+                       int64_t out_ld, hipStream_t st) {
+    // keys with >= 256 entries on average are split over the 4 waves of a workgroup
+    const bool split = nnz >= 256 * nkeys;
+    const int64_t keys_per_block = split ? 1 : kWavesPerBlock;
+    const int64_t blocks = round_up8(ceil_div(nkeys, keys_per_block));
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(ceil_div(B, 4 * BT)));
-    hipLaunchKernelGGL((rowgroup_kernel<BT, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
-                       perm, opnd, B, bias, out, out_ld);
+    if (split)
+        hipLaunchKernelGGL((rowwave_kernel<BT, 4, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
+                           perm, opnd, B, bias, out, out_ld);
+    else
+        hipLaunchKernelGGL((rowwave_kernel<BT, 1, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
+                           perm, opnd, B, bias, out, out_ld);
 }
 
 // The gather-reduce shared by the forward (row order) and the input gradient
@@ -469,16 +819,16 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
              const int32_t *gidx, const float *vals, const int32_t *perm, const float *opnd, int64_t B,
              const float *bias, OutT *out, char *ws, hipStream_t st) {
     if (nkeys == 0 || B == 0) return SNACK_OK;
-    if (p.mapping == kRowgroup) {
+    if (p.mapping == kRowwave) {
         probe(true, st);
         switch (p.bt) {
-            case 4: launch_rowgroup_bt<OutT, 4>(nkeys, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
-            case 8: launch_rowgroup_bt<OutT, 8>(nkeys, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
-            case 16: launch_rowgroup_bt<OutT, 16>(nkeys, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
-            default: return fail(SNACK_ERR_INTERNAL, "rowgroup: unsupported lane count %d", p.bt);
+            case 4: launch_rowwave_bt<OutT, 4>(nkeys, nnz, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
+            case 8: launch_rowwave_bt<OutT, 8>(nkeys, nnz, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
+            case 16: launch_rowwave_bt<OutT, 16>(nkeys, nnz, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
+            default: return fail(SNACK_ERR_INTERNAL, "rowwave: unsupported lane count %d", p.bt);
         }
         probe(false, st);
-        return check_hip("rowgroup_kernel");
+        return check_hip("rowwave_kernel");
     }
     float *head = reinterpret_cast<float *>(ws + p.off_head);
     float *tail = reinterpret_cast<float *>(ws + p.off_tail);
@@ -515,8 +865,8 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
     }
     const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
     switch (op) {
-        case SNACK_OP_FWD: return plan_spmm(nnz, I, batch, act_dtype).total;
-        case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, batch, act_dtype).total;
+        case SNACK_OP_FWD: return plan_spmm(nnz, I, O, batch, act_dtype, false).total;
+        case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, I, batch, act_dtype, true).total;
         case SNACK_OP_GRAD_WEIGHT: return plan_sddmm(nnz, O, I, batch, act_dtype).total;
         default: fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown op %d", op); return 0;
     }
@@ -531,12 +881,12 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
             return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
         if (batch < 0 || batch > kMaxBatch)
-            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^22]", who, (long long)batch);
+            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
         if (batch == 0 || O == 0) return snack::ok();
         if (I > 0) { if (int s = check_act(X, act_dtype, "X", who)) return s; }
         if (int s = check_act(Y, act_dtype, "Y", who)) return s;
-        const SpmmPlan p = plan_spmm(nnz, I, batch, act_dtype);
+        const SpmmPlan p = plan_spmm(nnz, I, O, batch, act_dtype, false);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
         char *ws = static_cast<char *>(workspace);
@@ -568,7 +918,7 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
             return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
         if (batch < 0 || batch > kMaxBatch)
-            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^22]", who, (long long)batch);
+            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
         if (batch > 0 && O > 0) { if (int s = check_act(dY, act_dtype, "dY", who)) return s; }
@@ -585,9 +935,34 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             if (int s = check_hip("bias_grad_kernel")) return s;
         }
         if (batch == 0 || I == 0) return snack::ok();
-        const SpmmPlan p = plan_spmm(nnz, O, batch, act_dtype);
+        const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
+        if (p.mapping == kScatter) {
+            float *partial = reinterpret_cast<float *>(ws + p.off_head);
+            const size_t lds = sizeof(float) * static_cast<size_t>(batch * I);
+            probe(true, st);
+            if (act_dtype == SNACK_F32)
+                hipLaunchKernelGGL(dx_scatter_kernel<float>, dim3(static_cast<unsigned>(p.nchunks)),
+                                   dim3(kScatterThreads), lds, st, nnz, p.chunk, O, I, batch, W->rows, W->cols,
+                                   W->vals, static_cast<const float *>(dY), partial);
+            else
+                hipLaunchKernelGGL(dx_scatter_kernel<bf16_t>, dim3(static_cast<unsigned>(p.nchunks)),
+                                   dim3(kScatterThreads), lds, st, nnz, p.chunk, O, I, batch, W->rows, W->cols,
+                                   W->vals, static_cast<const bf16_t *>(dY), partial);
+            probe(false, st);
+            if (int s = check_hip("dx_scatter_kernel")) return s;
+            const int64_t n = batch * I;
+            const dim3 grid(static_cast<unsigned>(ceil_div(n, kWave)));
+            if (act_dtype == SNACK_F32)
+                hipLaunchKernelGGL(dx_reduce_kernel<float>, grid, dim3(kBlock), 0, st, n, p.nchunks, partial,
+                                   static_cast<float *>(dX));
+            else
+                hipLaunchKernelGGL(dx_reduce_kernel<bf16_t>, grid, dim3(kBlock), 0, st, n, p.nchunks, partial,
+                                   static_cast<bf16_t *>(dX));
+            if (int s = check_hip("dx_reduce_kernel")) return s;
+            return snack::ok();
+        }
         const float *dyt = static_cast<const float *>(dY);
         if (!p.direct) {
             float *dst = reinterpret_cast<float *>(ws + p.off_opnd);
@@ -616,7 +991,7 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
         if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
             return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
         if (batch < 0 || batch > kMaxBatch)
-            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^22]", who, (long long)batch);
+            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
         if (nnz == 0) return snack::ok();
         if (!dW) return fail(SNACK_ERR_NULL, "%s: dW is NULL", who);
@@ -648,7 +1023,21 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
         const int64_t blocks = round_up8(ceil_div(p.waves, kWavesPerBlock));
         const dim3 grid(static_cast<unsigned>(blocks));
         probe(true, st);
-        switch (p.bt * 8 + p.vw) {
+        if (p.wide) {
+            const int64_t q = batch / (4 * p.bt);  // float4s per lane (exact when it is cached)
+            const bool exact = batch % (4 * p.bt) == 0;
+#define SNACK_WIDE(BTV, QV)                                                                            \
+    hipLaunchKernelGGL((sddmm_wide_kernel<BTV, QV>), grid, dim3(kBlock), 0, st, nnz, p.per_wave, W->rows, \
+                       W->cols, xt, dyt, batch, dW)
+            if (exact && q == 1 && p.bt == 16) SNACK_WIDE(16, 1);
+            else if (exact && q == 2 && p.bt == 16) SNACK_WIDE(16, 2);
+            else if (exact && q == 1 && p.bt == 8) SNACK_WIDE(8, 1);
+            else if (exact && q == 1 && p.bt == 4) SNACK_WIDE(4, 1);
+            else if (p.bt == 16) SNACK_WIDE(16, 0);
+            else if (p.bt == 8) SNACK_WIDE(8, 0);
+            else SNACK_WIDE(4, 0);
+#undef SNACK_WIDE
+        } else switch (p.bt * 8 + p.vw) {
 #define SNACK_SDDMM(BTV, VWV)                                                                          \
     case BTV * 8 + VWV:                                                                                \
         hipLaunchKernelGGL((sddmm_kernel<BTV, VWV>), grid, dim3(kBlock), 0, st, nnz, p.steps, W->rows, \

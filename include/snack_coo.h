@@ -27,7 +27,7 @@
  *    keeps no state between calls (apart from the optional per-thread timing
  *    probe of snack_coo_set_probe) and never allocates device memory; device
  *    scratch comes from the caller's workspace (see snack_coo_workspace_bytes).
- *  - Sizes: O, I and nnz fit in int32; batch is at most 2^22.
+ *  - Sizes: O, I and nnz fit in int32; batch is at most 2^21.
  *  - Streams: device calls only enqueue work on hip_stream (a hipStream_t;
  *    NULL = the default stream) and never synchronise.  Device faults surface
  *    at the caller's next synchronisation.  Calls on different streams that

@@ -54,7 +54,7 @@ SMALL = [  # seed, shape, O, I, nnz
     (106, "uniform", 1, 5000, 1500),
     (107, "uniform", 5000, 1, 700),
 ]
-BATCHES = [1, 2, 3, 4, 5, 8, 13, 16, 20, 32, 64, 68, 100, 130]
+BATCHES = [1, 2, 3, 4, 5, 8, 13, 16, 20, 32, 64, 68, 100, 128, 130]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}")
@@ -208,10 +208,16 @@ def test_invariants_bias_determinism_scaling_permutation():
         assert torch.equal(snk.snack_coo_fwd(W, torch.zeros_like(X), b), b.expand(B, 700))
         assert not torch.any(snk.snack_coo_bwd_input(W, torch.zeros_like(dY)))
         assert not torch.any(snk.snack_coo_grad_weight(W, torch.zeros_like(X), dY))
-        # deterministic: bit-identical reruns
+        # deterministic: bit-identical reruns (the small-batch input gradient, which
+        # scatters into a workgroup-private LDS copy with atomics -- batch <= 4 and
+        # batch * in_features <= 16384 -- is reproducible to rounding only)
         Y1, Y2 = snk.snack_coo_fwd(W, X, b), snk.snack_coo_fwd(W, X, b)
         assert torch.equal(Y1, Y2)
-        assert torch.equal(snk.snack_coo_bwd_input(W, dY), snk.snack_coo_bwd_input(W, dY))
+        dX1, dX2 = snk.snack_coo_bwd_input(W, dY), snk.snack_coo_bwd_input(W, dY)
+        if B <= 4 and B * 900 <= 16384:
+            check_close(dX2.cpu().numpy(), dX1.cpu().numpy().astype(np.float64), 60, "dX rerun")
+        else:
+            assert torch.equal(dX1, dX2)
         assert torch.equal(snk.snack_coo_grad_weight(W, X, dY), snk.snack_coo_grad_weight(W, X, dY))
         # power-of-two scaling is exact
         assert torch.equal(snk.snack_coo_fwd(W, 2 * X), 2 * snk.snack_coo_fwd(W, X))
