@@ -269,12 +269,13 @@ def batch1_sweep(dev, K):
 
 
 def calibrate_copy(dev, nbytes, reps):
-    """A plain device copy of known size, for scaling the HBM byte counters."""
+    """A plain elementwise kernel of known size (reads nbytes, writes nbytes), for
+    scaling the HBM byte counters."""
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(reps):
-        dst.copy_(src)
+        torch.mul(src, 2.0, out=dst)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
