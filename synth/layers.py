@@ -163,7 +163,9 @@ def make_acts(seed: int, batch: int, features: int) -> np.ndarray:
 
 
 def random_small_layer(seed: int, out_features: int, in_features: int, nnz: int, shape: str = "uniform"):
-    """Small hand-shaped layers for edge cases: 'uniform', 'one_row', 'one_col', 'diag', 'empty_rows'."""
+    """Small hand-shaped layers for edge cases: 'uniform', 'one_row', 'one_col', 'diag', 'empty_rows',
+    'dense_lines' (uniform, plus two full rows and two full columns; three other rows and three
+    other columns keep only their entries on those full lines)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     O, I = out_features, in_features
     if shape == "uniform":
@@ -181,6 +183,16 @@ def random_small_layer(seed: int, out_features: int, in_features: int, nnz: int,
         live = np.sort(rng.choice(O, size=max(1, O // 4), replace=False))
         cand = (live[:, None] * I + np.arange(I)[None, :]).ravel()
         pos = np.sort(rng.choice(cand, size=min(nnz, cand.size), replace=False))
+    elif shape == "dense_lines":
+        lines_r = rng.choice(O, size=5, replace=False)
+        lines_c = rng.choice(I, size=5, replace=False)
+        full = np.concatenate([r * I + np.arange(I, dtype=np.int64) for r in lines_r[:2]] +
+                              [np.arange(O, dtype=np.int64) * I + c for c in lines_c[:2]])
+        pos = np.union1d(_uniform_positions(rng, O * I, nnz), full)
+        r_of, c_of = pos // I, pos % I
+        drop = np.isin(r_of, lines_r[2:]) | np.isin(c_of, lines_c[2:])
+        keep_full = np.isin(r_of, lines_r[:2]) | np.isin(c_of, lines_c[:2])
+        pos = pos[~drop | keep_full]
     else:
         raise ValueError(shape)
     pos = np.asarray(pos, dtype=np.int64)

@@ -272,3 +272,32 @@ def test_workspace_contract():
     assert e.value.status == "WORKSPACE"
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     assert torch.equal(snk.snack_coo_fwd(W, X, workspace=ws), snk.snack_coo_fwd(W, X))
+
+
+# Larger layers at batches 64 / 128 / 192: ragged tiles, odd shapes, 600 to 20000 keys, full rows
+# and columns (keys with thousands of entries next to keys with a few), rows with no entries
+# (three in four), and the column permutation of the input gradient.
+WIDE = [  # seed, shape, O, I, density
+    (191, "uniform", 3000, 1300, 0.05),
+    (192, "dense_lines", 2600, 2100, 0.06),
+    (193, "uniform", 20000, 600, 0.05),
+    (194, "uniform", 600, 20000, 0.05),
+    (195, "uniform", 1100, 700, 0.10),
+    (197, "empty_rows", 4000, 1300, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}")
+@pytest.mark.parametrize("B", [64, 128])
+def test_wide_layer_shapes(case, B):
+    seed, shape, O, I, density = case
+    say(f"wide layer {shape} {O}x{I} B={B}")
+    L = synth.random_small_layer(seed, O, I, int(density * O * I), shape)
+    run_all(L, B, 77 + B)
+
+
+@pytest.mark.parametrize("B", [64, 192])
+def test_wide_layer_bf16(B):
+    say(f"wide layer bf16 B={B}")
+    L = synth.random_small_layer(196, 2600, 2100, int(0.06 * 2600 * 2100), "dense_lines")
+    run_all(L, B, 300 + B, bf16=True)
