@@ -598,6 +598,319 @@ __global__ __launch_bounds__(kBlock) void dx_reduce_kernel(int64_t n, int64_t np
     }
 }
 
+// ---------------------------------------------------------------- batch-1 CSR stream mapping
+// Batch 1: the activations are vectors, so an entry's work is one multiply
+// and the path is bound by streaming the triple.  A wave owns the entries
+// [e0, e1) of a fixed-size chunk of the row-sorted triple and reads only cols
+// and vals (8 bytes per entry): the row of each entry is recovered from
+// row_offsets, read 64 rows at a time into a window that also holds those
+// rows' bias (forward) or dY values (gradients).  Eight 64-entry steps of loads
+// are in flight.  A step lies inside one row unless a row ends in it; only
+// then are lanes told apart by row.
+
+// Largest r in [0, O) with offs[r] <= e, for 0 <= e < offs[O]: the row holding entry e.
+// Wave-parallel: each round samples the interval at 64 points.
+__device__ int csr_row_of(const int32_t *__restrict__ offs, int O, int e, int lane) {
+    int lo = 0, hi = O;  // offs[lo] <= e < offs[hi]
+    while (hi - lo > kWave) {
+        const int len = hi - lo;
+        const int q = lo + static_cast<int>((static_cast<int64_t>(lane) * len) >> 6);
+        const int c = __popcll(__ballot(offs[q] <= e));  // a prefix of the lanes, c >= 1
+        const int qa = lo + static_cast<int>((static_cast<int64_t>(c - 1) * len) >> 6);
+        hi = c == kWave ? hi : lo + static_cast<int>((static_cast<int64_t>(c) * len) >> 6);
+        lo = qa;
+    }
+    const int r = lo + lane;
+    const bool le = r < hi && offs[min(r, O)] <= e;
+    return lo + __popcll(__ballot(le)) - 1;
+}
+
+// As csr_row_of, trying first the 64 rows around the row that entry e would be in if
+// all rows had the average length (one round of loads for near-uniform layers).
+__device__ int csr_row_of_guess(const int32_t *__restrict__ offs, int O, int nnz, int e, int lane) {
+    const int g = static_cast<int>((static_cast<int64_t>(e) * O) / nnz);
+    const int lo = max(0, min(g - kWave / 2, O - 1));
+    const int v = offs[min(lo + lane, O)];  // offs[O] = nnz > e
+    const int c = __popcll(__ballot(v <= e));
+    if (c >= 1 && c < kWave) return lo + c - 1;  // offs[lo + c - 1] <= e < offs[lo + c]
+    return csr_row_of(offs, O, e, lane);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over the 64 lanes, the same value in every lane (fixed order).
+__device__ __forceinline__ float wave_sum(float v) {
+    v = group_sum<16>(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+// 64 rows from rb: lane l holds the end offset of row rb + l and that row's value from rv
+// (bias or dY; 0 when rv is null).  Rows past O read row O - 1 / offset nnz (never used).
+template <typename ValT>
+__device__ __forceinline__ void csr_window(const int32_t *__restrict__ offs, int O, int rb, int lane,
+                                           const ValT *__restrict__ rv, int &wend, float &wval) {
+    wend = offs[min(rb + 1 + lane, O)];
+    wval = rv ? load_act(rv, min(rb + lane, O - 1)) : 0.f;
+}
+
+// x staged in LDS by 1024-thread workgroups (I <= kStageMaxI): a 4-byte gather from L2
+// moves a whole 64-byte line, so reading x once per workgroup saves ~16x the L2 traffic.
+constexpr int kStageThreads = 1024;
+constexpr int64_t kStageMaxI = 16384;
+
+// Copies x (I <= kStageMaxI elements) into LDS as fp32; every thread of the workgroup
+// takes part, issuing all of its loads before its stores (one round of latency).
+template <int THREADS, typename ActT>
+__device__ __forceinline__ void stage_vector(const ActT *__restrict__ x, int I, float *xs) {
+    constexpr int K = static_cast<int>(kStageMaxI / THREADS);
+    float v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int i = threadIdx.x + k * THREADS;
+        v[k] = i < I ? load_act(x, i) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int i = threadIdx.x + k * THREADS;
+        if (i < I) xs[i] = v[k];
+    }
+    __syncthreads();
+}
+
+// Forward, batch 1: y[r] = bias[r] + sum of the row's vals * x[cols].  Rows cut by a
+// chunk edge leave their partial sum in head[w] (the chunk's first row) or tail[w] (its
+// last row); fixup_kernel finishes them and the empty rows, as for segscan_kernel.
+// THREADS == kStageThreads: x is read from an LDS copy (I elements).
+template <typename ActT, typename OutT, int THREADS>
+__global__ __launch_bounds__(THREADS) void csr1_fwd_kernel(int O, int I, int nnz, int chunk, int nchunks,
+                                                           const int32_t *__restrict__ offs,
+                                                           const int32_t *__restrict__ cols,
+                                                           const float *__restrict__ vals,
+                                                           const ActT *__restrict__ x,
+                                                           const float *__restrict__ bias, OutT *__restrict__ y,
+                                                           float *__restrict__ head, float *__restrict__ tail) {
+    constexpr int U = 8;
+    constexpr bool kStaged = THREADS == kStageThreads;
+    extern __shared__ float xs[];
+    if constexpr (kStaged) stage_vector<THREADS>(x, I, xs);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = static_cast<int>(xcd_block()) * (THREADS / kWave) +
+                  __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    if (w >= nchunks) return;  // uniform per wave, after the only barrier
+    const int e0 = w * chunk, e1 = min(e0 + chunk, nnz);
+    int r = csr_row_of_guess(offs, O, nnz, e0, lane);
+    const int rfirst = r;
+    int rs = __builtin_amdgcn_readfirstlane(offs[r]);  // start of row r
+    int rb = r, wend;
+    float wbias;
+    csr_window(offs, O, rb, lane, bias, wend, wbias);
+    int E = __builtin_amdgcn_readlane(wend, 0);  // end of row r
+    float acc = 0.f;
+    for (int s0 = e0; s0 < e1; s0 += U * kWave) {
+        float p[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = s0 + u * kWave + lane;
+            const int kk = min(k, e1 - 1);
+            const float v = vals[kk];
+            const int c = cols[kk];
+            const float xv = kStaged ? xs[c] : load_act(x, c);
+            p[u] = k < e1 ? v * xv : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * kWave;
+            if (s >= e1) break;
+            int from = 0;  // lanes below `from` belong to rows finished in this step
+            while (E < s + kWave && E < e1) {  // row r ends inside this step
+                const int cut = E - s;
+                const float tot = wave_sum(acc + ((lane >= from && lane < cut) ? p[u] : 0.f));
+                const float bv = readlane_f(wbias, r - rb);
+                acc = 0.f;
+                if (E > rs && lane == 0) {  // non-empty; empty rows are left to the fix-up
+                    if (rs >= e0)
+                        store_act(y, r, tot + bv);
+                    else
+                        head[w] = tot;
+                }
+                from = cut;
+                rs = E;
+                ++r;
+                if (r - rb >= kWave) {
+                    rb = r;
+                    csr_window(offs, O, rb, lane, bias, wend, wbias);
+                }
+                E = __builtin_amdgcn_readlane(wend, r - rb);
+            }
+            acc += lane >= from ? p[u] : 0.f;
+        }
+    }
+    // row r holds entry e1 - 1: complete if it started in this chunk and ends at e1
+    const float tot = wave_sum(acc);
+    const float bv = readlane_f(wbias, r - rb);
+    if (lane == 0) {
+        if (rs >= e0 && E == e1)
+            store_act(y, r, tot + bv);
+        else if (r == rfirst)
+            head[w] = tot;
+        else
+            tail[w] = tot;
+    }
+}
+
+// Walk of one 64-entry step for the gradients: every lane gets the dY value of its
+// entry's row.  Advances (r, E, window) past the rows that end inside the step.
+template <typename ActT>
+__device__ __forceinline__ float csr_step_rowval(int s, int e1, int lane, int O, const int32_t *__restrict__ offs,
+                                                 const ActT *__restrict__ dy, int &r, int &E, int &rb, int &wend,
+                                                 float &wdy) {
+    float dl = readlane_f(wdy, r - rb);
+    while (E < s + kWave && E < e1) {  // row r ends inside this step
+        const int cut = E - s;
+        ++r;
+        if (r - rb >= kWave) {
+            rb = r;
+            csr_window(offs, O, rb, lane, dy, wend, wdy);
+        }
+        E = __builtin_amdgcn_readlane(wend, r - rb);
+        const float d = readlane_f(wdy, r - rb);
+        dl = lane >= cut ? d : dl;
+    }
+    return dl;
+}
+
+// Weight gradient, batch 1: dW[k] = dY[row k] * X[cols[k]], streamed in row order.
+// THREADS == kStageThreads: x is read from an LDS copy (I elements).
+template <typename ActT, int THREADS>
+__global__ __launch_bounds__(THREADS) void csr1_dw_kernel(int O, int I, int nnz, int chunk, int nchunks,
+                                                          const int32_t *__restrict__ offs,
+                                                          const int32_t *__restrict__ cols,
+                                                          const ActT *__restrict__ x, const ActT *__restrict__ dy,
+                                                          float *__restrict__ dW) {
+    constexpr int U = 8;
+    constexpr bool kStaged = THREADS == kStageThreads;
+    extern __shared__ float xs[];
+    if constexpr (kStaged) stage_vector<THREADS>(x, I, xs);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = static_cast<int>(xcd_block()) * (THREADS / kWave) +
+                  __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    if (w >= nchunks) return;  // uniform per wave, after the only barrier
+    const int e0 = w * chunk, e1 = min(e0 + chunk, nnz);
+    int r = csr_row_of_guess(offs, O, nnz, e0, lane);
+    int rb = r, wend;
+    float wdy;
+    csr_window(offs, O, rb, lane, dy, wend, wdy);
+    int E = __builtin_amdgcn_readlane(wend, 0);
+    for (int s0 = e0; s0 < e1; s0 += U * kWave) {
+        float xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = cols[min(s0 + u * kWave + lane, e1 - 1)];
+            xv[u] = kStaged ? xs[c] : load_act(x, c);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * kWave;
+            if (s >= e1) break;
+            const float dl = csr_step_rowval(s, e1, lane, O, offs, dy, r, E, rb, wend, wdy);
+            if (s + lane < e1) dW[s + lane] = dl * xv[u];
+        }
+    }
+}
+
+// Input gradient, batch 1, I <= 10240, without atomics: each of a workgroup's
+// 4 waves owns a private LDS copy of dX and the rows whose first entry lies in
+// its chunk, and walks them in steps of 64 entries that never span two rows.
+// The columns of one row are distinct and a wave's LDS operations complete in
+// order, so each lane adds vals[k] * dY[row k] into its copy with a plain
+// read and write.  The copies are then added in wave order into
+// partial[blockIdx.x], and dx_reduce_kernel adds the workgroups in order:
+// the result is deterministic.
+constexpr int kPrivWaves = 4;
+constexpr int64_t kPrivMaxI = 10240;  // 4 copies of dX in 160 KB of LDS
+
+template <typename ActT>
+__global__ __launch_bounds__(kPrivWaves *kWave) void csr1_dxpriv_kernel(int O, int I, int nnz, int chunk, int nwaves,
+                                                                       const int32_t *__restrict__ offs,
+                                                                       const int32_t *__restrict__ cols,
+                                                                       const float *__restrict__ vals,
+                                                                       const ActT *__restrict__ dy,
+                                                                       float *__restrict__ partial) {
+    extern __shared__ float cp[];  // [kPrivWaves][I]
+    constexpr int kThreads = kPrivWaves * kWave;
+    for (int i = threadIdx.x; i < kPrivWaves * I; i += kThreads) cp[i] = 0.f;
+    __syncthreads();
+    constexpr int U = 8;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    float *my = cp + wave * I;
+    const int w = blockIdx.x * kPrivWaves + wave;
+    if (w < nwaves) {  // uniform per wave; every wave reaches the barrier below
+        // entries [E0, E1): from the first row start >= a to the first row start >= b
+        const int a = w * chunk, b = min(a + chunk, nnz);
+        const int ra = csr_row_of_guess(offs, O, nnz, a, lane);
+        const int oa = __builtin_amdgcn_readfirstlane(offs[ra]);
+        const int E0 = oa == a ? a : __builtin_amdgcn_readfirstlane(offs[ra + 1]);
+        int E1 = nnz;
+        if (b < nnz) {
+            const int rb1 = csr_row_of_guess(offs, O, nnz, b, lane);
+            const int ob = __builtin_amdgcn_readfirstlane(offs[rb1]);
+            E1 = ob == b ? b : __builtin_amdgcn_readfirstlane(offs[rb1 + 1]);
+        }
+        if (E0 < E1) {
+            int r = csr_row_of_guess(offs, O, nnz, E0, lane);
+            int rb = r, wend;
+            float wdy;
+            csr_window(offs, O, rb, lane, dy, wend, wdy);
+            int E = __builtin_amdgcn_readlane(wend, 0);
+            float d = readlane_f(wdy, 0);
+            for (int s0 = E0; s0 < E1; s0 += U * kWave) {
+                int c[U];
+                float v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int kk = min(s0 + u * kWave + lane, E1 - 1);
+                    c[u] = cols[kk];
+                    v[u] = vals[kk];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = s0 + u * kWave;
+                    if (s >= E1) break;
+                    const int k = s + lane;
+                    int from = 0;
+                    while (true) {
+                        // lanes [from, E - s) of this step are row r's
+                        if (k < E1 && lane >= from && k < E) {
+                            const float t = my[c[u]];
+                            my[c[u]] = t + v[u] * d;
+                        }
+                        if (E >= s + kWave || E >= E1) break;
+                        from = E - s;
+                        ++r;
+                        if (r - rb >= kWave) {
+                            rb = r;
+                            csr_window(offs, O, rb, lane, dy, wend, wdy);
+                        }
+                        E = __builtin_amdgcn_readlane(wend, r - rb);
+                        d = readlane_f(wdy, r - rb);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    float *__restrict__ mine = partial + static_cast<int64_t>(blockIdx.x) * I;
+    for (int i = threadIdx.x; i < I; i += kThreads) {
+        float t = cp[i];
+#pragma unroll
+        for (int q = 1; q < kPrivWaves; ++q) t += cp[q * I + i];
+        mine[i] = t;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void zero_kernel(float *__restrict__ p, int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
     if (i < n) p[i] = 0.f;
@@ -629,17 +942,19 @@ inline void probe(bool start, hipStream_t st) {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline int64_t round_up8(int64_t x) { return ceil_div(x, kXcds) * kXcds; }
 
-enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2 };
+enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2, kCsr1 = 3, kCsr1Priv = 4 };
 constexpr int64_t kScatterLdsFloats = 16384;  // 64 KB private dX copy per workgroup
 
 // Device work plan of one gather-reduce (forward or input gradient).
 struct SpmmPlan {
     Mapping mapping;
     int bt;              // batch lanes per entry group (segscan) or lanes per slot (rowwave)
-    int64_t chunk;       // segscan: entries per wave; scatter: entries per workgroup
-    int64_t nchunks;     // segscan: waves; scatter: workgroups (partial copies)
+    int64_t chunk;       // segscan, csr1: entries per wave; scatter: entries per workgroup
+    int64_t nchunks;     // segscan, csr1: waves; scatter: workgroups (partial copies)
+    int64_t nparts;      // csr1 private copies: workgroups (partial copies)
     bool direct;         // operand used in place (fp32, batch 1) instead of a transposed copy
     size_t off_opnd, off_head, off_tail, total;
 };
@@ -655,6 +970,39 @@ inline int pow2_at_least(int64_t x) {
 SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok) {
     SpmmPlan p{};
     p.direct = (B == 1 && dtype == SNACK_F32);
+    // batch 1, rows averaging >= 32 entries: stream cols and vals, rows from row_offsets,
+    // activations read in place (the segmented scan is faster for shorter rows)
+    if (B == 1 && !scatter_ok && nnz > 0 && nnz >= 32 * nout) {
+        p.direct = true;
+        p.mapping = kCsr1;
+        p.chunk = round_up(ceil_div(nnz, 8192), 256);  // about 8192 waves
+        p.nchunks = ceil_div(nnz, p.chunk);
+        size_t at = 0;
+        p.off_opnd = 0;
+        p.off_head = at;
+        at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks));
+        p.off_tail = at;
+        at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks));
+        p.total = at;
+        return p;
+    }
+    // batch-1 input gradient of a large layer: private per-wave copies of dX, no atomics
+    // (below ~2M entries the atomic scatter's fixed costs are lower)
+    if (B == 1 && scatter_ok && nnz >= (int64_t(1) << 21) && nout <= kPrivMaxI) {
+        p.direct = true;
+        p.mapping = kCsr1Priv;
+        // about 256 workgroups per 4 copies of dX that fit a CU's LDS, 4 waves each
+        const int64_t parts = 256 * std::min<int64_t>(4, std::max<int64_t>(1, kPrivMaxI / nout));
+        p.chunk = round_up(ceil_div(nnz, parts * kPrivWaves), kWave);
+        p.nchunks = ceil_div(nnz, p.chunk);
+        p.nparts = ceil_div(p.nchunks, kPrivWaves);
+        size_t at = 0;
+        p.off_opnd = 0;
+        p.off_head = p.off_tail = at;
+        at = align_up(at + sizeof(float) * static_cast<size_t>(p.nparts * nout));
+        p.total = at;
+        return p;
+    }
     if (scatter_ok && B <= 4 && B * nout <= kScatterLdsFloats && nnz > 0) {
         p.mapping = kScatter;
         p.direct = true;  // reads dY in its batch-major layout
@@ -693,6 +1041,7 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
 }
 
 struct SddmmPlan {
+    bool csr1;           // batch 1: csr1_dw_kernel, activations read in place
     bool wide;           // sddmm_wide_kernel (batch a multiple of 4, >= 16) or sddmm_kernel
     int bt, vw;
     int64_t steps, waves, per_wave;
@@ -722,6 +1071,12 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
         p.waves = ceil_div(nnz, G * p.steps);
     }
     p.x_direct = p.dy_direct = (B == 1 && dtype == SNACK_F32);
+    if (B == 1 && nnz >= 128 * O) {  // rows averaging >= 128 entries
+        p.csr1 = true;
+        p.x_direct = p.dy_direct = true;
+        p.steps = round_up(ceil_div(std::max<int64_t>(nnz, 1), 8192), 256);  // entries per wave
+        p.waves = ceil_div(nnz, p.steps);
+    }
     size_t at = 0;
     p.off_x = at;
     if (!p.x_direct) at = align_up(at + sizeof(float) * static_cast<size_t>(I * B));
@@ -890,6 +1245,39 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
         char *ws = static_cast<char *>(workspace);
+        if (p.mapping == kCsr1) {
+            float *head = reinterpret_cast<float *>(ws + p.off_head);
+            float *tail = reinterpret_cast<float *>(ws + p.off_tail);
+            const bool staged = I <= kStageMaxI;
+            const int threads = staged ? kStageThreads : kBlock;
+            const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(p.nchunks, threads / kWave))));
+            const size_t lds = staged ? sizeof(float) * static_cast<size_t>(I) : 0;
+            const int o = static_cast<int>(O), in = static_cast<int>(I), nz = static_cast<int>(nnz),
+                      ch = static_cast<int>(p.chunk), nc = static_cast<int>(p.nchunks);
+#define SNACK_CSR1_FWD(T, TH)                                                                                   \
+    hipLaunchKernelGGL((csr1_fwd_kernel<T, T, TH>), grid, dim3(TH), lds, st, o, in, nz, ch, nc, W->row_offsets,    \
+                       W->cols, W->vals, static_cast<const T *>(X), bias, static_cast<T *>(Y), head, tail)
+            probe(true, st);
+            if (act_dtype == SNACK_F32) {
+                if (staged) SNACK_CSR1_FWD(float, kStageThreads);
+                else SNACK_CSR1_FWD(float, kBlock);
+            } else {
+                if (staged) SNACK_CSR1_FWD(bf16_t, kStageThreads);
+                else SNACK_CSR1_FWD(bf16_t, kBlock);
+            }
+#undef SNACK_CSR1_FWD
+            probe(false, st);
+            if (int s = check_hip("csr1_fwd_kernel")) return s;
+            const dim3 fgrid(static_cast<unsigned>(ceil_div(O, kBlock)), 1);
+            if (act_dtype == SNACK_F32)
+                hipLaunchKernelGGL(fixup_kernel<float>, fgrid, dim3(kBlock), 0, st, O, int64_t(1), p.chunk,
+                                   W->row_offsets, bias, head, tail, static_cast<float *>(Y), O);
+            else
+                hipLaunchKernelGGL(fixup_kernel<bf16_t>, fgrid, dim3(kBlock), 0, st, O, int64_t(1), p.chunk,
+                                   W->row_offsets, bias, head, tail, static_cast<bf16_t *>(Y), O);
+            if (int s = check_hip("fixup_kernel")) return s;
+            return snack::ok();
+        }
         const float *xt = static_cast<const float *>(X);
         if (!p.direct) {
             float *dst = reinterpret_cast<float *>(ws + p.off_opnd);
@@ -938,6 +1326,41 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
+        if (p.mapping == kCsr1Priv) {
+            float *partial = reinterpret_cast<float *>(ws + p.off_head);
+            const size_t lds = sizeof(float) * static_cast<size_t>(kPrivWaves * I);
+            static const bool attr = [] {  // up to 160 KB of LDS
+                (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&csr1_dxpriv_kernel<float>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          static_cast<int>(sizeof(float) * kPrivWaves * kPrivMaxI));
+                (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&csr1_dxpriv_kernel<bf16_t>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          static_cast<int>(sizeof(float) * kPrivWaves * kPrivMaxI));
+                return true;
+            }();
+            (void)attr;
+            const int o = static_cast<int>(O), in = static_cast<int>(I), nz = static_cast<int>(nnz),
+                      ch = static_cast<int>(p.chunk), nc = static_cast<int>(p.nchunks);
+            const dim3 grid(static_cast<unsigned>(p.nparts));
+            probe(true, st);
+            if (act_dtype == SNACK_F32)
+                hipLaunchKernelGGL(csr1_dxpriv_kernel<float>, grid, dim3(kPrivWaves * kWave), lds, st, o, in, nz, ch,
+                                   nc, W->row_offsets, W->cols, W->vals, static_cast<const float *>(dY), partial);
+            else
+                hipLaunchKernelGGL(csr1_dxpriv_kernel<bf16_t>, grid, dim3(kPrivWaves * kWave), lds, st, o, in, nz, ch,
+                                   nc, W->row_offsets, W->cols, W->vals, static_cast<const bf16_t *>(dY), partial);
+            probe(false, st);
+            if (int s = check_hip("csr1_dxpriv_kernel")) return s;
+            const dim3 rgrid(static_cast<unsigned>(ceil_div(I, kWave)));
+            if (act_dtype == SNACK_F32)
+                hipLaunchKernelGGL(dx_reduce_kernel<float>, rgrid, dim3(kBlock), 0, st, I, p.nparts, partial,
+                                   static_cast<float *>(dX));
+            else
+                hipLaunchKernelGGL(dx_reduce_kernel<bf16_t>, rgrid, dim3(kBlock), 0, st, I, p.nparts, partial,
+                                   static_cast<bf16_t *>(dX));
+            if (int s = check_hip("dx_reduce_kernel")) return s;
+            return snack::ok();
+        }
         if (p.mapping == kScatter) {
             float *partial = reinterpret_cast<float *>(ws + p.off_head);
             const size_t lds = sizeof(float) * static_cast<size_t>(batch * I);
@@ -1008,6 +1431,29 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
         const SddmmPlan p = plan_sddmm(nnz, O, I, batch, act_dtype);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
+        if (p.csr1) {
+            const bool staged = I <= kStageMaxI;
+            const int threads = staged ? kStageThreads : kBlock;
+            const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(p.waves, threads / kWave))));
+            const size_t lds = staged ? sizeof(float) * static_cast<size_t>(I) : 0;
+            const int o = static_cast<int>(O), in = static_cast<int>(I), nz = static_cast<int>(nnz),
+                      ch = static_cast<int>(p.steps), nc = static_cast<int>(p.waves);
+#define SNACK_CSR1_DW(T, TH)                                                                                  \
+    hipLaunchKernelGGL((csr1_dw_kernel<T, TH>), grid, dim3(TH), lds, st, o, in, nz, ch, nc, W->row_offsets, W->cols, \
+                       static_cast<const T *>(X), static_cast<const T *>(dY), dW)
+            probe(true, st);
+            if (act_dtype == SNACK_F32) {
+                if (staged) SNACK_CSR1_DW(float, kStageThreads);
+                else SNACK_CSR1_DW(float, kBlock);
+            } else {
+                if (staged) SNACK_CSR1_DW(bf16_t, kStageThreads);
+                else SNACK_CSR1_DW(bf16_t, kBlock);
+            }
+#undef SNACK_CSR1_DW
+            probe(false, st);
+            if (int s = check_hip("csr1_dw_kernel")) return s;
+            return snack::ok();
+        }
         const float *xt = static_cast<const float *>(X);
         const float *dyt = static_cast<const float *>(dY);
         if (!p.x_direct) {

@@ -288,12 +288,32 @@ WIDE = [  # seed, shape, O, I, density
 
 
 @pytest.mark.parametrize("case", WIDE, ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}")
-@pytest.mark.parametrize("B", [64, 128])
+@pytest.mark.parametrize("B", [1, 64, 128])
 def test_wide_layer_shapes(case, B):
     seed, shape, O, I, density = case
     say(f"wide layer {shape} {O}x{I} B={B}")
     L = synth.random_small_layer(seed, O, I, int(density * O * I), shape)
     run_all(L, B, 77 + B)
+
+
+# Batch 1 on layers of more than 2M entries with up to 10240 columns and rows of hundreds to
+# thousands of entries: the streamed row-order kernels for all three products (the input
+# gradient with per-wave private copies), with full rows and columns, and three rows in four
+# empty.
+BATCH1_LARGE = [  # seed, shape, O, I, density
+    (198, "dense_lines", 2500, 10000, 0.09),
+    (199, "empty_rows", 4000, 9000, 0.06),
+]
+
+
+@pytest.mark.parametrize("case", BATCH1_LARGE, ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}")
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+def test_batch1_large_layers(case, bf16):
+    seed, shape, O, I, density = case
+    say(f"batch-1 large {shape} {O}x{I} bf16={bf16}")
+    L = synth.random_small_layer(seed, O, I, int(density * O * I), shape)
+    assert L["nnz"] >= 2 ** 21
+    run_all(L, 1, 500 + seed, bf16=bf16)
 
 
 @pytest.mark.parametrize("B", [64, 192])
