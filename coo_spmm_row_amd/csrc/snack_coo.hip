@@ -97,7 +97,8 @@ __device__ __forceinline__ int64_t xcd_block() {
 }
 
 // ---------------------------------------------------------------- layout
-// in [B][F] (batch-major, fp32 or bf16)  ->  out [F][B] fp32 (feature-major).
+// in [B][F] (batch-major, fp32 or bf16)  ->  out [F+1][B] fp32 (feature-major), row F
+// zero (gathers of a missing entry point there instead of being masked).
 // A workgroup moves a tile of 16 features x 64 batch rows through LDS: every
 // thread issues its four loads (64-byte row segments) before its stores, and
 // the tile's output is one contiguous run when B <= 64.
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__r
     const int tx = threadIdx.x % kTf, ty = threadIdx.x / kTf;  // 16 x 16
     const int nb = static_cast<int>(min<int64_t>(kTb, B - b0));
     const int nf = static_cast<int>(min<int64_t>(kTf, F - f0));
+    if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < nb) out[F * B + b0 + threadIdx.x] = 0.f;
     float v[kTb / 16];
 #pragma unroll
     for (int i = 0; i < kTb / 16; ++i) {
@@ -238,69 +240,73 @@ __global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B,
 // S = 64/BT slots each take one stored entry per step, lane t holds batch
 // columns b0+4t .. b0+4t+3 (one float4 of the feature-major operand row).  A
 // wave reads its key's entries 64 at a time (chunks c, c+WPR, ...) with one
-// coalesced load per lane, prefetches its next chunk while the current one is
-// consumed, and keeps U float4 gathers in flight.  Slot partial sums are
-// combined by xor shuffles, the WPR waves of a key through LDS.
+// coalesced load per lane -- keeping each entry's operand row as a 32-bit
+// float4 offset -- prefetches its next chunk while the current one is
+// consumed, and keeps U float4 gathers in flight.  Lanes of a chunk past the
+// key's end point at the operand's zero row with value 0, so no step needs a
+// mask.  Slot partial sums are combined by xor shuffles, the WPR waves of a
+// key through LDS.  The operand including its zero row is below 4 GB.
 template <int BT, int WPR, typename OutT>
 __global__ __launch_bounds__(kBlock) void rowwave_kernel(
     int64_t nkeys, const int32_t *__restrict__ offs, const int32_t *__restrict__ gidx,
-    const float *__restrict__ vals, const int32_t *__restrict__ perm, const float *__restrict__ opnd,
+    const float *__restrict__ vals, const int32_t *__restrict__ perm, const float *__restrict__ opnd, int zero_row,
     int64_t B, const float *__restrict__ bias, OutT *__restrict__ out, int64_t out_ld) {
     constexpr int S = kWave / BT;
-    constexpr int U = (S * 4 <= kWave) ? 4 : kWave / S;  // S*U divides 64
+    constexpr int U = (S * 8 <= kWave) ? 8 : kWave / S;  // S*U divides 64
     constexpr int KPB = kWavesPerBlock / WPR;             // keys per workgroup
     __shared__ float4 part[kWavesPerBlock][BT];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int e = lane / BT, t = lane % BT;
     const int64_t r = xcd_block() * KPB + wave / WPR;
     const int wsub = wave % WPR;
     const bool rok = r < nkeys;  // uniform per wave
     const int64_t b0 = static_cast<int64_t>(blockIdx.y) * (4 * BT) + 4 * t;
     const bool bok = b0 < B;     // B % 4 == 0: all four columns exist
-    const int64_t B4 = B / 4;
-    const float4 *__restrict__ op4 = reinterpret_cast<const float4 *>(opnd) + b0 / 4;
+    const int B4 = static_cast<int>(B / 4);
+    // uniform base of this batch tile; a lane adds its float4 column and the entry's row
+    const char *__restrict__ tile = reinterpret_cast<const char *>(opnd) + blockIdx.y * (16 * BT);
+    const uint32_t lane_off = 16u * static_cast<uint32_t>(bok ? t : 0);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (rok) {
-        const int64_t s = offs[r], end = offs[r + 1];
-        int mc = 0;
+        const int zoff = zero_row * B4;
+        const int s = offs[r], end = offs[r + 1];
+        int mo = zoff;
         float mv = 0.f;
-        int64_t first = s + static_cast<int64_t>(wsub) * kWave;
+        const int first = s + wsub * kWave;
         if (first + lane < end) {
-            mc = gidx[first + lane];
-            mv = vals[perm ? static_cast<int64_t>(perm[first + lane]) : first + lane];
+            mo = gidx[first + lane] * B4;
+            mv = vals[perm ? perm[first + lane] : first + lane];
         }
-        for (int64_t base = first; base < end; base += WPR * kWave) {
-            const int cc = mc;
+        for (int base = first; base < end; base += WPR * kWave) {
+            const int co = mo;
             const float cv = mv;
-            const int n = static_cast<int>(min<int64_t>(kWave, end - base));
-            const int64_t nb = base + WPR * kWave;
+            const int n = min(kWave, end - base);
+            const int nb = base + WPR * kWave;
             if (nb < end) {  // prefetch this wave's next chunk
-                mc = 0;
+                mo = zoff;
                 mv = 0.f;
                 if (nb + lane < end) {
-                    mc = gidx[nb + lane];
-                    mv = vals[perm ? static_cast<int64_t>(perm[nb + lane]) : nb + lane];
+                    mo = gidx[nb + lane] * B4;
+                    mv = vals[perm ? perm[nb + lane] : nb + lane];
                 }
             }
             for (int h = 0; h < n; h += S * U) {
+                const int sa = (h + e) << 2;  // ds_bpermute address of slot e's entry; +4S per step
                 float4 x[U];
                 float v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int src = h + u * S + e;  // < 64
-                    const int c = __shfl(cc, src, kWave);
-                    v[u] = __shfl(cv, src, kWave);
-                    const bool live = bok && src < n;
-                    x[u] = live ? op4[static_cast<int64_t>(c) * B4] : make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (!live) v[u] = 0.f;
+                    const int o = __builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co);
+                    v[u] = __int_as_float(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, __float_as_int(cv)));
+                    x[u] = *reinterpret_cast<const float4 *>(tile + (16u * static_cast<uint32_t>(o) + lane_off));
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    acc.x += v[u] * x[u].x;
-                    acc.y += v[u] * x[u].y;
-                    acc.z += v[u] * x[u].z;
-                    acc.w += v[u] * x[u].w;
+                    acc.x = fmaf(v[u], x[u].x, acc.x);
+                    acc.y = fmaf(v[u], x[u].y, acc.y);
+                    acc.z = fmaf(v[u], x[u].z, acc.z);
+                    acc.w = fmaf(v[u], x[u].w, acc.w);
                 }
             }
         }
@@ -401,6 +407,75 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(int64_t nnz, int64_t step
 #pragma unroll
             for (int d = BT / 2; d >= 1; d >>= 1) acc[u] += __shfl_xor(acc[u], d, kWave);
             if (valid[u] && t == 0) dW[k[u]] = acc[u];
+        }
+    }
+}
+
+// Weight gradient for batches 4*BT*Q with Q in {1, 2, 4}: the rowwave mapping
+// for sampled products.  A workgroup owns 4/WPR rows of W, each split over WPR
+// waves; a wave keeps the row's dY slice in registers (lane t: float4s t,
+// t+BT, .. of the feature-major dY row, Q of them) for the whole row, takes
+// the row's entries 64 at a time with their X rows as 32-bit float4 offsets
+// (the next 64 prefetched; lanes past the row's end point at X's zero row),
+// gathers U entries per slot in flight and sums each slot's BT lanes by DPP.
+template <int BT, int WPR, int Q>
+__global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32_t *__restrict__ offs,
+                                                          const int32_t *__restrict__ cols,
+                                                          const float *__restrict__ xt, int zero_row,
+                                                          const float *__restrict__ dyt, int64_t B,
+                                                          float *__restrict__ dW) {
+    constexpr int S = kWave / BT;
+    constexpr int U = (S * 8 <= kWave) ? 8 : kWave / S;  // S*U divides 64
+    constexpr int KPB = kWavesPerBlock / WPR;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int e = lane / BT, t = lane % BT;
+    const int64_t r = xcd_block() * KPB + wave / WPR;
+    const int wsub = wave % WPR;
+    if (r >= O) return;  // uniform per wave; no barrier follows
+    const int B4 = static_cast<int>(B / 4);
+    const char *__restrict__ xb = reinterpret_cast<const char *>(xt) + 16u * static_cast<uint32_t>(t);
+    const float4 *__restrict__ y4 = reinterpret_cast<const float4 *>(dyt) + r * B4 + t;
+    float4 dyv[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) dyv[q] = y4[q * BT];
+    const int zoff = zero_row * B4;
+    const int s = offs[r], end = offs[r + 1];
+    const int first = s + wsub * kWave;
+    int mo = zoff;
+    if (first + lane < end) mo = cols[first + lane] * B4;
+    for (int base = first; base < end; base += WPR * kWave) {
+        const int co = mo;
+        const int n = min(kWave, end - base);
+        const int nb = base + WPR * kWave;
+        if (nb < end) {  // prefetch this wave's next chunk
+            mo = zoff;
+            if (nb + lane < end) mo = cols[nb + lane] * B4;
+        }
+        for (int h = 0; h < n; h += S * U) {
+            const int sa = (h + e) << 2;
+            float4 x[U][Q];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t o = 16u * static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co));
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    x[u][q] = *reinterpret_cast<const float4 *>(xb + (o + 16u * static_cast<uint32_t>(q * BT)));
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float d = 0.f;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    d = fmaf(x[u][q].x, dyv[q].x, d);
+                    d = fmaf(x[u][q].y, dyv[q].y, d);
+                    d = fmaf(x[u][q].z, dyv[q].z, d);
+                    d = fmaf(x[u][q].w, dyv[q].w, d);
+                }
+                d = group_sum<BT>(d);
+                const int src = h + u * S + e;
+                if (t == 0 && src < n) dW[base + src] = d;
+            }
         }
     }
 }
@@ -1015,7 +1090,7 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
         p.total = at;
         return p;
     }
-    if (B >= 16 && B % 4 == 0) {
+    if (B >= 16 && B % 4 == 0 && (opnd_rows + 1) * B * 4 < (int64_t(1) << 32)) {
         p.mapping = kRowwave;
         p.bt = 4;  // lanes per slot: the largest power of two <= min(16, B/4)
         while (p.bt * 2 <= std::min<int64_t>(16, B / 4)) p.bt *= 2;
@@ -1031,7 +1106,7 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
     }
     size_t at = 0;
     p.off_opnd = at;
-    if (!p.direct) at = align_up(at + sizeof(float) * static_cast<size_t>(opnd_rows * B));
+    if (!p.direct) at = align_up(at + sizeof(float) * static_cast<size_t>((opnd_rows + 1) * B));
     p.off_head = at;
     if (p.mapping == kSegscan) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B));
     p.off_tail = at;
@@ -1043,6 +1118,7 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
 struct SddmmPlan {
     bool csr1;           // batch 1: csr1_dw_kernel, activations read in place
     bool wide;           // sddmm_wide_kernel (batch a multiple of 4, >= 16) or sddmm_kernel
+    int rowq;            // > 0: rowsddmm_kernel with this many float4s per lane (1, 2 or 4)
     int bt, vw;
     int64_t steps, waves, per_wave;
     bool x_direct, dy_direct;
@@ -1070,6 +1146,10 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
         p.steps = std::min<int64_t>(std::max<int64_t>(ceil_div(std::max<int64_t>(nnz, 1), G * target_waves), 1), 64);
         p.waves = ceil_div(nnz, G * p.steps);
     }
+    if (p.wide && B % (4 * p.bt) == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
+        const int64_t q = B / (4 * p.bt);
+        if (q == 1 || q == 2 || q == 4) p.rowq = static_cast<int>(q);
+    }
     p.x_direct = p.dy_direct = (B == 1 && dtype == SNACK_F32);
     if (B == 1 && nnz >= 128 * O) {  // rows averaging >= 128 entries
         p.csr1 = true;
@@ -1079,9 +1159,9 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
     }
     size_t at = 0;
     p.off_x = at;
-    if (!p.x_direct) at = align_up(at + sizeof(float) * static_cast<size_t>(I * B));
+    if (!p.x_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * B));
     p.off_dy = at;
-    if (!p.dy_direct) at = align_up(at + sizeof(float) * static_cast<size_t>(O * B));
+    if (!p.dy_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * B));
     p.total = at;
     return p;
 }
@@ -1152,8 +1232,9 @@ void launch_segscan_bt(const SpmmPlan &p, int64_t nnz, const int32_t *keys, cons
 
 template <typename OutT, int BT>
 void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const int32_t *gidx, const float *vals,
-                       const int32_t *perm, const float *opnd, int64_t B, const float *bias, OutT *out,
-                       int64_t out_ld, hipStream_t st) {
+                       const int32_t *perm, const float *opnd, int64_t opnd_rows, int64_t B, const float *bias,
+                       OutT *out, int64_t out_ld, hipStream_t st) {
+    const int zero_row = static_cast<int>(opnd_rows);  // the transposed operand's zero row
     // keys with >= 256 entries on average are split over the 4 waves of a workgroup
     const bool split = nnz >= 256 * nkeys;
     const int64_t keys_per_block = split ? 1 : kWavesPerBlock;
@@ -1161,25 +1242,25 @@ void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const in
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(ceil_div(B, 4 * BT)));
     if (split)
         hipLaunchKernelGGL((rowwave_kernel<BT, 4, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
-                           perm, opnd, B, bias, out, out_ld);
+                           perm, opnd, zero_row, B, bias, out, out_ld);
     else
         hipLaunchKernelGGL((rowwave_kernel<BT, 1, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
-                           perm, opnd, B, bias, out, out_ld);
+                           perm, opnd, zero_row, B, bias, out, out_ld);
 }
 
 // The gather-reduce shared by the forward (row order) and the input gradient
 // (column view).  nkeys = number of outputs per batch row; offs [nkeys+1].
 template <typename OutT>
 int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys, const int32_t *offs,
-             const int32_t *gidx, const float *vals, const int32_t *perm, const float *opnd, int64_t B,
-             const float *bias, OutT *out, char *ws, hipStream_t st) {
+             const int32_t *gidx, const float *vals, const int32_t *perm, const float *opnd, int64_t opnd_rows,
+             int64_t B, const float *bias, OutT *out, char *ws, hipStream_t st) {
     if (nkeys == 0 || B == 0) return SNACK_OK;
     if (p.mapping == kRowwave) {
         probe(true, st);
         switch (p.bt) {
-            case 4: launch_rowwave_bt<OutT, 4>(nkeys, nnz, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
-            case 8: launch_rowwave_bt<OutT, 8>(nkeys, nnz, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
-            case 16: launch_rowwave_bt<OutT, 16>(nkeys, nnz, offs, gidx, vals, perm, opnd, B, bias, out, nkeys, st); break;
+            case 4: launch_rowwave_bt<OutT, 4>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); break;
+            case 8: launch_rowwave_bt<OutT, 8>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); break;
+            case 16: launch_rowwave_bt<OutT, 16>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); break;
             default: return fail(SNACK_ERR_INTERNAL, "rowwave: unsupported lane count %d", p.bt);
         }
         probe(false, st);
@@ -1286,10 +1367,10 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         }
         int s;
         if (act_dtype == SNACK_F32)
-            s = run_spmm<float>(p, O, nnz, W->rows, W->row_offsets, W->cols, W->vals, nullptr, xt, batch, bias,
+            s = run_spmm<float>(p, O, nnz, W->rows, W->row_offsets, W->cols, W->vals, nullptr, xt, I, batch, bias,
                                 static_cast<float *>(Y), ws, st);
         else
-            s = run_spmm<bf16_t>(p, O, nnz, W->rows, W->row_offsets, W->cols, W->vals, nullptr, xt, batch, bias,
+            s = run_spmm<bf16_t>(p, O, nnz, W->rows, W->row_offsets, W->cols, W->vals, nullptr, xt, I, batch, bias,
                                  static_cast<bf16_t *>(Y), ws, st);
         return s ? s : snack::ok();
     } catch (...) {
@@ -1394,10 +1475,10 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         }
         int s;
         if (act_dtype == SNACK_F32)
-            s = run_spmm<float>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt,
+            s = run_spmm<float>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt, O,
                                 batch, nullptr, static_cast<float *>(dX), ws, st);
         else
-            s = run_spmm<bf16_t>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt,
+            s = run_spmm<bf16_t>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt, O,
                                  batch, nullptr, static_cast<bf16_t *>(dX), ws, st);
         return s ? s : snack::ok();
     } catch (...) {
@@ -1469,7 +1550,33 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
         const int64_t blocks = round_up8(ceil_div(p.waves, kWavesPerBlock));
         const dim3 grid(static_cast<unsigned>(blocks));
         probe(true, st);
-        if (p.wide) {
+        if (p.rowq > 0) {
+            // rows averaging >= 256 entries are split over the 4 waves of a workgroup
+            const bool split = nnz >= 256 * O;
+            const dim3 rgrid(static_cast<unsigned>(round_up8(ceil_div(O, split ? 1 : kWavesPerBlock))));
+            const int zero_row = static_cast<int>(I);
+#define SNACK_ROWSD(BTV, WPRV, QV)                                                                             \
+    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, W->cols, xt, \
+                       zero_row, dyt, batch, dW)
+#define SNACK_ROWSD_Q(BTV, WPRV)                         \
+    do {                                                 \
+        if (p.rowq == 1) SNACK_ROWSD(BTV, WPRV, 1);      \
+        else if (p.rowq == 2) SNACK_ROWSD(BTV, WPRV, 2); \
+        else SNACK_ROWSD(BTV, WPRV, 4);                  \
+    } while (0)
+            if (p.bt == 16) {
+                if (split) SNACK_ROWSD_Q(16, 4);
+                else SNACK_ROWSD_Q(16, 1);
+            } else if (p.bt == 8) {
+                if (split) SNACK_ROWSD_Q(8, 4);
+                else SNACK_ROWSD_Q(8, 1);
+            } else {
+                if (split) SNACK_ROWSD_Q(4, 4);
+                else SNACK_ROWSD_Q(4, 1);
+            }
+#undef SNACK_ROWSD_Q
+#undef SNACK_ROWSD
+        } else if (p.wide) {
             const int64_t q = batch / (4 * p.bt);  // float4s per lane (exact when it is cached)
             const bool exact = batch % (4 * p.bt) == 0;
 #define SNACK_WIDE(BTV, QV)                                                                            \
