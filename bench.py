@@ -53,7 +53,21 @@ def algorithmic_bytes(op, nnz, O, I, B, s):
         return 12 * nnz + s * B * I + s * B * O + 4 * O
     if op == "dx":
         return 12 * nnz + s * B * O + s * B * I
+    if op == "bwd":  # both gradients: the triple once, dW written; dY and X read, dX written
+        return 16 * nnz + s * B * O + 2 * s * B * I
     return 12 * nnz + s * B * I + s * B * O  # dw: rows, cols, write dW; read X and dY
+
+
+def bwd_fused(B):
+    """Whether snack_coo_bwd runs its single column-view pass at this batch (the library's
+    rule: B = 4*BT*Q with BT the largest power of two <= min(16, B/4) and Q in {1, 2, 4});
+    otherwise it runs the two gradients one after the other.  Used to label timings only."""
+    if B < 16 or B % 4:
+        return False
+    bt = 4
+    while bt * 2 <= min(16, B // 4):
+        bt *= 2
+    return B % (4 * bt) == 0 and B // (4 * bt) in (1, 2, 4)
 
 
 def kernel_source_sha():
@@ -87,7 +101,7 @@ class Layer:
         self.dX = torch.empty((B, self.I), dtype=tdt, device=dev)
         self.dW = torch.empty(self.nnz, dtype=torch.float32, device=dev)
         code = snk.SNACK_BF16 if dtype == "bf16" else snk.SNACK_F32
-        need = max(snk.snack_coo_workspace_bytes(op, self.W, B, code) for op in (0, 1, 2))
+        need = max(snk.snack_coo_workspace_bytes(op, self.W, B, code) for op in (0, 1, 2, 3))
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         self.s = 2 if dtype == "bf16" else 4
 
@@ -97,16 +111,19 @@ class Layer:
             snk.snack_coo_fwd(self.W, self.X, self.bias, out=self.Y, workspace=self.ws)
         elif name == "dx":
             snk.snack_coo_bwd_input(self.W, self.dY, out=self.dX, workspace=self.ws)
-        else:
+        elif name == "dw":
             snk.snack_coo_grad_weight(self.W, self.X, self.dY, out=self.dW, workspace=self.ws)
+        else:  # both gradients in one call
+            snk.snack_coo_bwd(self.W, self.X, self.dY, dx_out=self.dX, dw_out=self.dW, workspace=self.ws)
 
     def step(self):
+        """One layer step: the forward and both gradients (snack_coo_bwd)."""
         self.op("fwd")
-        self.op("dx")
-        self.op("dw")
+        self.op("bwd")
 
 
-OPS = ("fwd", "dx", "dw")
+STEP_OPS = ("fwd", "bwd")          # what a step runs
+SPLIT_OPS = ("fwd", "dx", "dw")    # the three products as separate calls (reported beside)
 
 
 def make_events(n):
@@ -117,17 +134,17 @@ def make_events(n):
     return evs
 
 
-def timed_steps(layer, K):
-    """K back-to-back steps; the probe brackets each op's main kernel.  Returns
-    (total ms, {op: [kernel ms per launch]})."""
+def timed_steps(layer, K, ops=STEP_OPS):
+    """K back-to-back passes over `ops`; the probe brackets each op's main kernel.
+    Returns (total ms, {op: [kernel ms per launch]})."""
     import torch
     import coo_spmm_row_amd as snk
-    pairs = {op: [(a, b) for a, b in zip(make_events(K), make_events(K))] for op in OPS}
+    pairs = {op: [(a, b) for a, b in zip(make_events(K), make_events(K))] for op in ops}
     start, stop = make_events(2)
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        for op in OPS:
+        for op in ops:
             a, b = pairs[op][i]
             snk.snack_coo_set_probe(a, b)
             layer.op(op)
@@ -135,7 +152,7 @@ def timed_steps(layer, K):
     stop.record()
     torch.cuda.synchronize()
     total = start.elapsed_time(stop)
-    kern = {op: [a.elapsed_time(b) for a, b in pairs[op]] for op in OPS}
+    kern = {op: [a.elapsed_time(b) for a, b in pairs[op]] for op in ops}
     return total, kern
 
 
@@ -170,11 +187,11 @@ def graph_steps(layer, K, reps=3):
     return float(np.median(times))
 
 
-def op_times(layer, K):
+def op_times(layer, K, ops=STEP_OPS + ("dx", "dw")):
     """Per-op wall time on the stream (all kernels of the op), back to back."""
     import torch
     out = {}
-    for op in OPS:
+    for op in ops:
         a, b = make_events(2)
         torch.cuda.synchronize()
         a.record()
@@ -186,13 +203,13 @@ def op_times(layer, K):
     return out
 
 
-def cold_kernel_times(layer, K, flush_bytes=1 << 30):
+def cold_kernel_times(layer, K, ops, flush_bytes=1 << 30):
     """Main-kernel time per op with the 256 MB last-level cache flushed before each launch."""
     import torch
     import coo_spmm_row_amd as snk
     scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device=layer.X.device)
     res = {}
-    for op in OPS:
+    for op in ops:
         evs = [(a, b) for a, b in zip(make_events(K), make_events(K))]
         for i in range(K):
             scratch.add_(1.0)  # streams 2 x flush_bytes through the caches
@@ -259,11 +276,12 @@ def batch1_sweep(dev, K):
         layer = Layer(name, 1, "f32", dev)
         for _ in range(3):
             layer.step()
-        total, kern = timed_steps(layer, K)
+        total, _ = timed_steps(layer, K)
         g = graph_steps(layer, K)
+        _, kern = timed_steps(layer, K, SPLIT_OPS)  # at batch 1 the gradients run as two kernels
         out[label] = {"us_per_step_eager": round(total / K * 1000.0, 2),
                       "us_per_step_graph": None if g is None else round(g, 2),
-                      "kernel_us": {op: round(float(np.mean(kern[op])) * 1000.0, 2) for op in OPS}}
+                      "kernel_us": {op: round(float(np.mean(kern[op])) * 1000.0, 2) for op in SPLIT_OPS}}
         del layer
     return out
 
@@ -317,11 +335,16 @@ def main():
     graph_us = graph_steps(layer, args.steps)
     step_us = graph_us if graph_us is not None else eager_us
     ms_per_step = step_us / 1000.0
-    kernel_us = {op: float(np.mean(kern[op])) * 1000.0 for op in OPS}
-    dom = max(OPS, key=lambda o: kernel_us[o])
+    _, kern_split = timed_steps(layer, args.steps, ("dx", "dw"))
+    kern.update(kern_split)
+    all_ops = STEP_OPS + ("dx", "dw")
+    kernel_us = {op: float(np.mean(kern[op])) * 1000.0 for op in all_ops}
+    # the dominant kernel of the step (the fused backward pass when the batch allows it)
+    cand = STEP_OPS if bwd_fused(B) else SPLIT_OPS
+    dom = max(cand, key=lambda o: kernel_us[o])
     kname = {"fwd": "forward gather-reduce", "dx": "input-gradient gather-reduce",
-             "dw": "weight-gradient sampled product"}[dom]
-    nbytes = {op: algorithmic_bytes(op, layer.nnz, layer.O, layer.I, B, layer.s) for op in OPS}
+             "dw": "weight-gradient sampled product", "bwd": "fused backward pass (dX and dW)"}[dom]
+    nbytes = {op: algorithmic_bytes(op, layer.nnz, layer.O, layer.I, B, layer.s) for op in all_ops}
     achieved = nbytes[dom] / (kernel_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -330,16 +353,17 @@ def main():
                 "algorithmic_bytes": nbytes[dom]}
     extras = {"us_per_step_eager": round(eager_us, 2),
               "us_per_step_graph": None if graph_us is None else round(graph_us, 2),
+              "backward_fused": bwd_fused(B),
               "kernel_us": {op: round(v, 2) for op, v in kernel_us.items()},
               "kernel_frac_hbm": {op: round(nbytes[op] / (kernel_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-                                  for op in OPS}}
+                                  for op in all_ops}}
     if not args.no_extras:
         log("op-level and cold-cache timings")
         extras["op_us"] = {op: round(v, 2) for op, v in op_times(layer, args.steps).items()}
-        cold = cold_kernel_times(layer, min(args.steps, 20))
+        cold = cold_kernel_times(layer, min(args.steps, 20), cand)
         extras["kernel_us_cold"] = {op: round(v, 2) for op, v in cold.items()}
         extras["kernel_frac_hbm_cold"] = {op: round(nbytes[op] / (cold[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-                                          for op in OPS}
+                                          for op in cand}
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsnack_coo.so")
 
 SNACK_F32, SNACK_BF16 = 0, 1
-OP_FWD, OP_BWD_INPUT, OP_GRAD_WEIGHT = 0, 1, 2
+OP_FWD, OP_BWD_INPUT, OP_GRAD_WEIGHT, OP_BWD = 0, 1, 2, 3
 STATUS = {0: "OK", 1: "NULL", 2: "SHAPE", 3: "INDEX", 4: "DUPLICATE", 5: "ALIGN", 6: "DTYPE",
           7: "WORKSPACE", 8: "HIP", 9: "INTERNAL", 10: "NOMEM", 11: "UNSORTED"}
 
@@ -79,11 +79,12 @@ _lib.snack_coo_workspace_bytes.restype = ctypes.c_size_t
 _lib.snack_coo_fwd.argtypes = [_D, _p, _i64, ctypes.c_int, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.snack_coo_bwd_input.argtypes = [_D, _p, _i64, ctypes.c_int, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.snack_coo_grad_weight.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, ctypes.c_size_t, _p]
+_lib.snack_coo_bwd.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.snack_coo_topology_update.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i64, _u64, _p, _p, _p, _p, _p]
 _lib.snack_coo_set_probe.argtypes = [_p, _p]
 
 EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_bwd_input",
-            "snack_coo_grad_weight", "snack_coo_topology_update", "snack_last_error",
+            "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_last_error",
             "snack_coo_abi_version", "snack_coo_set_probe")
 
 
@@ -282,6 +283,28 @@ def snack_coo_grad_weight(W: SnackCOO, X, dY, out=None, workspace=None, stream=N
                                     ctypes.c_void_p(dW.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
     _check(st, "snack_coo_grad_weight")
     return dW
+
+
+def snack_coo_bwd(W: SnackCOO, X, dY, dx_out=None, dw_out=None, db=None, workspace=None, stream=None):
+    """Both gradients in one call: returns (dX, dW) as snack_coo_bwd_input and
+    snack_coo_grad_weight would (dX has dY's dtype, dW float32 [nnz]); ``db`` as for
+    snack_coo_bwd_input."""
+    import torch
+    _check_act(X, None, W.in_features, "X")
+    B = X.shape[0]
+    _check_act(dY, B, W.out_features, "dY")
+    dt = _dtype_code(X)
+    if _dtype_code(dY) != dt:
+        raise TypeError("X and dY must have the same dtype")
+    dX = dx_out if dx_out is not None else torch.empty((B, W.in_features), dtype=dY.dtype, device=dY.device)
+    _check_act(dX, B, W.in_features, "dX")
+    dW = dw_out if dw_out is not None else torch.empty(W.nnz, dtype=torch.float32, device=X.device)
+    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_BWD, W, B, dt), workspace)
+    st = _lib.snack_coo_bwd(W.desc, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(dY.data_ptr()), B, dt,
+                            ctypes.c_void_p(dX.data_ptr()), None if db is None else ctypes.c_void_p(db.data_ptr()),
+                            ctypes.c_void_p(dW.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
+    _check(st, "snack_coo_bwd")
+    return dX, dW
 
 
 def snack_coo_set_probe(start_event=None, stop_event=None):

@@ -411,6 +411,141 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(int64_t nnz, int64_t step
     }
 }
 
+// Both gradients in one pass over the column view (batch 4*BT*Q, Q in {1, 2, 4}).
+// A workgroup owns 4/WPR input columns i, each split over WPR waves.  The
+// column's X slice is held in registers (lane t: float4s t, t+BT, .. of the
+// feature-major X row i); each stored entry k of the column gathers its dY row
+// once and uses it twice: dX[., i] += vals[k] * dY[., row k] (accumulated as in
+// rowwave_kernel) and dW[k] = <X[., i], dY[., row k]> (summed over the slot's
+// BT lanes by DPP, written at the entry's row-order position).  The window
+// holds, per entry, the dY row as a 32-bit float4 offset, the value and that
+// position; lanes past the column's end point at dY's zero row.
+template <int BT, int WPR, int Q, typename OutT>
+__global__ __launch_bounds__(kBlock) void colbwd_kernel(
+    int64_t I, const int32_t *__restrict__ coffs, const int32_t *__restrict__ crows,
+    const int32_t *__restrict__ cperm, const float *__restrict__ vals, const float *__restrict__ xt,
+    const float *__restrict__ dyt, int zero_row, int64_t B, OutT *__restrict__ dX, float *__restrict__ dW) {
+    constexpr int S = kWave / BT;
+    constexpr int UQ = 8 / Q;                                   // gathers in flight: U*Q float4s
+    constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;       // S*U divides 64
+    constexpr int KPB = kWavesPerBlock / WPR;
+    __shared__ float4 part[kWavesPerBlock][BT * Q];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int e = lane / BT, t = lane % BT;
+    const int64_t col = xcd_block() * KPB + wave / WPR;
+    const int wsub = wave % WPR;
+    const bool cok = col < I;  // uniform per wave
+    const int B4 = static_cast<int>(B / 4);
+    const char *__restrict__ yb = reinterpret_cast<const char *>(dyt) + 16u * static_cast<uint32_t>(t);
+    float4 acc[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (cok) {
+        float4 xv[Q];
+        const float4 *__restrict__ x4 = reinterpret_cast<const float4 *>(xt) + col * B4 + t;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) xv[q] = x4[q * BT];
+        const int zoff = zero_row * B4;
+        const int s = coffs[col], end = coffs[col + 1];
+        const int first = s + wsub * kWave;
+        int mo = zoff, mp = 0;
+        float mv = 0.f;
+        if (first + lane < end) {
+            mp = cperm[first + lane];
+            mo = crows[first + lane] * B4;
+            mv = vals[mp];
+        }
+        for (int base = first; base < end; base += WPR * kWave) {
+            const int co = mo, cp = mp;
+            const float cv = mv;
+            const int n = min(kWave, end - base);
+            const int nb = base + WPR * kWave;
+            if (nb < end) {  // prefetch this wave's next chunk
+                mo = zoff;
+                mp = 0;
+                mv = 0.f;
+                if (nb + lane < end) {
+                    mp = cperm[nb + lane];
+                    mo = crows[nb + lane] * B4;
+                    mv = vals[mp];
+                }
+            }
+            for (int h = 0; h < n; h += S * U) {
+                const int sa = (h + e) << 2;
+                float4 y[U][Q];
+                float v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t o = 16u * static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co));
+                    v[u] = __int_as_float(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, __float_as_int(cv)));
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+                        y[u][q] = *reinterpret_cast<const float4 *>(yb + (o + 16u * static_cast<uint32_t>(q * BT)));
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) {
+                        acc[q].x = fmaf(v[u], y[u][q].x, acc[q].x);
+                        acc[q].y = fmaf(v[u], y[u][q].y, acc[q].y);
+                        acc[q].z = fmaf(v[u], y[u][q].z, acc[q].z);
+                        acc[q].w = fmaf(v[u], y[u][q].w, acc[q].w);
+                        d = fmaf(xv[q].x, y[u][q].x, d);
+                        d = fmaf(xv[q].y, y[u][q].y, d);
+                        d = fmaf(xv[q].z, y[u][q].z, d);
+                        d = fmaf(xv[q].w, y[u][q].w, d);
+                    }
+                    d = group_sum<BT>(d);
+                    const int k = __builtin_amdgcn_ds_bpermute(sa + 4 * S * u, cp);
+                    if (t == 0 && h + u * S + e < n) dW[k] = d;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+#pragma unroll
+        for (int d = BT; d < kWave; d <<= 1) {
+            acc[q].x += __shfl_xor(acc[q].x, d, kWave);
+            acc[q].y += __shfl_xor(acc[q].y, d, kWave);
+            acc[q].z += __shfl_xor(acc[q].z, d, kWave);
+            acc[q].w += __shfl_xor(acc[q].w, d, kWave);
+        }
+    }
+    if constexpr (WPR > 1) {
+        if (e == 0) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) part[wave][t + q * BT] = acc[q];
+        }
+        __syncthreads();
+        if (wsub == 0 && e == 0) {
+#pragma unroll
+            for (int w2 = 1; w2 < WPR; ++w2) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const float4 o = part[wave + w2][t + q * BT];
+                    acc[q].x += o.x;
+                    acc[q].y += o.y;
+                    acc[q].z += o.z;
+                    acc[q].w += o.w;
+                }
+            }
+        }
+    }
+    if (cok && wsub == 0 && e == 0) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int64_t b0 = 4 * static_cast<int64_t>(t + q * BT);
+            store_act(dX, (b0 + 0) * I + col, acc[q].x);
+            store_act(dX, (b0 + 1) * I + col, acc[q].y);
+            store_act(dX, (b0 + 2) * I + col, acc[q].z);
+            store_act(dX, (b0 + 3) * I + col, acc[q].w);
+        }
+    }
+}
+
 // Weight gradient for batches 4*BT*Q with Q in {1, 2, 4}: the rowwave mapping
 // for sampled products.  A workgroup owns 4/WPR rows of W, each split over WPR
 // waves; a wave keeps the row's dY slice in registers (lane t: float4s t,
@@ -1166,6 +1301,40 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
     return p;
 }
 
+// Backward pass plan: the fused column-view kernel for batches 4*BT*Q (Q in {1, 2, 4})
+// whose feature-major copies (with their zero rows) stay below 4 GB; otherwise the input
+// gradient and the weight gradient one after the other, sharing the workspace.
+struct BwdPlan {
+    bool fused;
+    int bt, q;
+    size_t off_x, off_dy, total;
+};
+
+BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
+    BwdPlan p{};
+    if (nnz > 0 && B >= 16 && B % 4 == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
+        int bt = 4;  // lanes per slot: the largest power of two <= min(16, B/4)
+        while (bt * 2 <= std::min<int64_t>(16, B / 4)) bt *= 2;
+        const int64_t q = B / (4 * bt);
+        if (B % (4 * bt) == 0 && (q == 1 || q == 2 || q == 4)) {
+            p.fused = true;
+            p.bt = bt;
+            p.q = static_cast<int>(q);
+        }
+    }
+    if (p.fused) {
+        size_t at = 0;
+        p.off_x = at;
+        at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * B));
+        p.off_dy = at;
+        at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * B));
+        p.total = at;
+    } else {
+        p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true).total, plan_sddmm(nnz, O, I, B, dtype).total);
+    }
+    return p;
+}
+
 int check_hip(const char *what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SNACK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -1304,6 +1473,7 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
         case SNACK_OP_FWD: return plan_spmm(nnz, I, O, batch, act_dtype, false).total;
         case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, I, batch, act_dtype, true).total;
         case SNACK_OP_GRAD_WEIGHT: return plan_sddmm(nnz, O, I, batch, act_dtype).total;
+        case SNACK_OP_BWD: return plan_bwd(nnz, O, I, batch, act_dtype).total;
         default: fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown op %d", op); return 0;
     }
 }
@@ -1606,6 +1776,99 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
         return snack::ok();
     } catch (...) {
         return fail(SNACK_ERR_INTERNAL, "snack_coo_grad_weight: unexpected exception");
+    }
+}
+
+namespace {
+
+template <typename OutT, int BT, int WPR>
+void launch_colbwd_q(int q, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W, const float *xt,
+                     const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW) {
+    if (q == 1)
+        hipLaunchKernelGGL((colbwd_kernel<BT, WPR, 1, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
+                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW);
+    else if (q == 2)
+        hipLaunchKernelGGL((colbwd_kernel<BT, WPR, 2, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
+                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW);
+    else
+        hipLaunchKernelGGL((colbwd_kernel<BT, WPR, 4, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
+                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW);
+}
+
+template <typename OutT>
+void launch_colbwd(const BwdPlan &p, bool split, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W,
+                   const float *xt, const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW) {
+#define SNACK_COLBWD(BTV)                                                                             \
+    if (split)                                                                                        \
+        launch_colbwd_q<OutT, BTV, 4>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);              \
+    else                                                                                              \
+        launch_colbwd_q<OutT, BTV, 1>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);
+    if (p.bt == 16) {
+        SNACK_COLBWD(16)
+    } else if (p.bt == 8) {
+        SNACK_COLBWD(8)
+    } else {
+        SNACK_COLBWD(4)
+    }
+#undef SNACK_COLBWD
+}
+
+}  // namespace
+
+extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch, int act_dtype,
+                             void *dX, float *db, float *dW, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+    try {
+        const char *who = "snack_coo_bwd";
+        if (int s = check_desc(W, true, who)) return s;
+        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
+            return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
+        if (batch < 0 || batch > kMaxBatch)
+            return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
+        const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+        const BwdPlan p = plan_bwd(nnz, O, I, batch, act_dtype);
+        if (!p.fused) {
+            if (int s = snack_coo_bwd_input(W, dY, batch, act_dtype, dX, db, workspace, workspace_bytes, hip_stream))
+                return s;
+            return snack_coo_grad_weight(W, X, dY, batch, act_dtype, dW, workspace, workspace_bytes, hip_stream);
+        }
+        if (int s = check_act(X, act_dtype, "X", who)) return s;
+        if (int s = check_act(dY, act_dtype, "dY", who)) return s;
+        if (int s = check_act(dX, act_dtype, "dX", who)) return s;
+        if (!dW) return fail(SNACK_ERR_NULL, "%s: dW is NULL", who);
+        if (reinterpret_cast<uintptr_t>(dW) % 4) return fail(SNACK_ERR_ALIGN, "%s: dW misaligned", who);
+        if (db && reinterpret_cast<uintptr_t>(db) % 4) return fail(SNACK_ERR_ALIGN, "%s: db misaligned", who);
+        if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
+        hipStream_t st = static_cast<hipStream_t>(hip_stream);
+        char *ws = static_cast<char *>(workspace);
+        if (db) {
+            const dim3 grid(static_cast<unsigned>(ceil_div(O, kBlock)));
+            if (act_dtype == SNACK_F32)
+                hipLaunchKernelGGL(bias_grad_kernel<float>, grid, dim3(kBlock), 0, st, O, batch,
+                                   static_cast<const float *>(dY), db);
+            else
+                hipLaunchKernelGGL(bias_grad_kernel<bf16_t>, grid, dim3(kBlock), 0, st, O, batch,
+                                   static_cast<const bf16_t *>(dY), db);
+            if (int s = check_hip("bias_grad_kernel")) return s;
+        }
+        float *xt = reinterpret_cast<float *>(ws + p.off_x);
+        float *dyt = reinterpret_cast<float *>(ws + p.off_dy);
+        if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st)) return s;
+        if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dyt, st)) return s;
+        // columns averaging >= 256 entries are split over the 4 waves of a workgroup
+        const bool split = nnz >= 256 * I;
+        const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(I, split ? 1 : kWavesPerBlock))));
+        const int zero_row = static_cast<int>(O);
+        probe(true, st);
+        if (act_dtype == SNACK_F32)
+            launch_colbwd<float>(p, split, grid, st, I, W, xt, dyt, zero_row, batch, static_cast<float *>(dX), dW);
+        else
+            launch_colbwd<bf16_t>(p, split, grid, st, I, W, xt, dyt, zero_row, batch, static_cast<bf16_t *>(dX), dW);
+        probe(false, st);
+        if (int s = check_hip("colbwd_kernel")) return s;
+        return snack::ok();
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "snack_coo_bwd: unexpected exception");
     }
 }
 

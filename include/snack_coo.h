@@ -69,7 +69,7 @@ typedef enum snack_status {
 } snack_status;
 
 enum { SNACK_F32 = 0, SNACK_BF16 = 1 };                                   /* activation dtype */
-enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2 };
+enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2, SNACK_OP_BWD = 3 };
 
 /* A layer's weight on the device.  Every pointer is a DEVICE pointer,
  * borrowed for the duration of the call.
@@ -80,7 +80,8 @@ enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2 };
  *                             (col, row) order (Table 7's CSC order)
  *   col_rows, col_cols [nnz]  rows[col_perm[j]], cols[col_perm[j]]
  *   col_offsets        [I+1]  col_offsets[c] = number of entries with col < c
- * The column view is needed by snack_coo_bwd_input only (NULL elsewhere). */
+ * The column view is needed by snack_coo_bwd_input and snack_coo_bwd only
+ * (NULL elsewhere). */
 typedef struct snack_coo_desc {
     int64_t out_features;
     int64_t in_features;
@@ -152,6 +153,22 @@ int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY
                           int64_t batch, int act_dtype, float *dW,
                           void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Both gradients of the backward pass (Section 3.4 / Appendix F: dL/dX and the
+ * weight gradient on supp(W) are computed from the same upstream gradient):
+ * the results of snack_coo_bwd_input (dX, and db if not NULL) and of
+ * snack_coo_grad_weight (dW) in one call.  Where the batch allows it
+ * (B = 4*BT*Q with BT a power of two <= 16 and Q in {1, 2, 4}, i.e. every
+ * multiple of 16 up to 256 and more), one pass over the column view gathers
+ * each entry's dY row once for both products; otherwise the two operations
+ * run one after the other on the stream.  Arguments and layouts as for the
+ * two calls; requires the column view; workspace >=
+ * snack_coo_workspace_bytes(SNACK_OP_BWD, ...).  dX and dW are overwritten
+ * (dW in the order of the triple); results agree with the separate calls to
+ * rounding (the summation order of dX differs). */
+int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch, int act_dtype,
+                  void *dX, float *db, float *dW,
+                  void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Host-side topology update (Appendix G: magnitude prune-and-regrow; regrowth
  * with the uniform initializer of Algorithm 2).  Input: a HOST triple sorted
  * strictly by (row, col) (SNACK_ERR_UNSORTED otherwise).
@@ -175,7 +192,8 @@ int snack_coo_topology_update(int64_t out_features, int64_t in_features, int64_t
  * armed on the calling thread, each device call records `start_event` on its
  * stream immediately before launching its main kernel (the gather-reduce of
  * snack_coo_fwd / snack_coo_bwd_input, the sampled product of
- * snack_coo_grad_weight) and `stop_event` immediately after it, so the pair
+ * snack_coo_grad_weight, the fused pass of snack_coo_bwd) and `stop_event`
+ * immediately after it, so the pair
  * brackets exactly that kernel.  Both are caller-owned hipEvent_t handles
  * created with timing enabled; passing NULL for both disarms the probe.
  * Returns SNACK_ERR_NULL if exactly one of them is NULL. */
@@ -184,7 +202,7 @@ int snack_coo_set_probe(void *start_event, void *stop_event);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *snack_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int snack_coo_abi_version(void);
 
 #ifdef __cplusplus

@@ -16,7 +16,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     lib = ctypes.CDLL(snk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert snk.abi_version() == 1
+    assert snk.abi_version() == 2
 
 
 def test_binding_loads_only_the_in_tree_library():
@@ -56,6 +56,17 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert need > 0
     assert lib.snack_coo_fwd(ctypes.byref(d), 0x1000, 8, 0, None, 0x2000, 0x10000, need - 1, None) == 7
     assert lib.snack_coo_workspace_bytes(9, ctypes.byref(d), 8, 0) == 0
+    # the fused backward: NULL descriptor, no column view, bad dtype, too-small workspace
+    assert lib.snack_coo_bwd(None, None, None, 16, 0, None, None, None, None, 0, None) == 1
+    assert lib.snack_coo_bwd(ctypes.byref(d), 0x1000, 0x1000, 16, 0, 0x1000, None, 0x1000, None, 0, None) == 1
+    d.col_perm = d.col_rows = d.col_cols = d.col_offsets = 0x1000
+    assert lib.snack_coo_bwd(ctypes.byref(d), 0x1000, 0x1000, 16, 5, 0x1000, None, 0x1000, None, 0, None) == 6
+    need = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 16, 0)
+    assert need > 0
+    assert lib.snack_coo_bwd(ctypes.byref(d), 0x1000, 0x1000, 16, 0, 0x1000, None, 0x1000, 0x10000, need - 1,
+                             None) == 7
+    assert lib.snack_coo_bwd(ctypes.byref(d), 0x1000, 0x1000, 16, 0, 0x1000, None, None, 0x10000, need,
+                             None) == 1  # dW NULL
 
 
 def test_one_hip_runtime_in_process():

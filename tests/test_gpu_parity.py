@@ -41,6 +41,13 @@ def run_all(L, B, seed, bf16=False, bias=True):
     check_close(from_device(dX), dXr, nnz / max(I, 1), "dX", bf16)
     check_close(dW.cpu().numpy(), dWr, B, "dW")
     check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, "db")
+    # both gradients from one call (one pass over the column view where the batch allows it)
+    db2 = torch.empty(O, dtype=torch.float32, device=DEV)
+    dX2, dW2 = snk.snack_coo_bwd(W, X, dY, db=db2)
+    torch.cuda.synchronize()
+    check_close(from_device(dX2), dXr, nnz / max(I, 1), "bwd dX", bf16)
+    check_close(dW2.cpu().numpy(), dWr, B, "bwd dW")
+    check_close(db2.cpu().numpy(), oracle.grad_bias(dy64), B, "bwd db")
     return built, W, X, dY, Y, dX, dW
 
 
@@ -219,6 +226,9 @@ def test_invariants_bias_determinism_scaling_permutation():
         else:
             assert torch.equal(dX1, dX2)
         assert torch.equal(snk.snack_coo_grad_weight(W, X, dY), snk.snack_coo_grad_weight(W, X, dY))
+        if B >= 16:  # the fused backward pass has no atomics: bit-identical reruns
+            a, b2 = snk.snack_coo_bwd(W, X, dY), snk.snack_coo_bwd(W, X, dY)
+            assert torch.equal(a[0], b2[0]) and torch.equal(a[1], b2[1])
         # power-of-two scaling is exact
         assert torch.equal(snk.snack_coo_fwd(W, 2 * X), 2 * snk.snack_coo_fwd(W, X))
         # empty rows output the bias exactly
