@@ -1404,8 +1404,10 @@ void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const in
                        const int32_t *perm, const float *opnd, int64_t opnd_rows, int64_t B, const float *bias,
                        OutT *out, int64_t out_ld, hipStream_t st) {
     const int zero_row = static_cast<int>(opnd_rows);  // the transposed operand's zero row
-    // keys with >= 256 entries on average are split over the 4 waves of a workgroup
-    const bool split = nnz >= 256 * nkeys;
+    // keys with >= 256 entries on average are split over the 4 waves of a workgroup, unless
+    // values are read through the column permutation: one wave per key keeps co-resident
+    // waves walking rows in step, so those reads share L2 lines
+    const bool split = !perm && nnz >= 256 * nkeys;
     const int64_t keys_per_block = split ? 1 : kWavesPerBlock;
     const int64_t blocks = round_up8(ceil_div(nkeys, keys_per_block));
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(ceil_div(B, 4 * BT)));
@@ -1796,21 +1798,14 @@ void launch_colbwd_q(int q, dim3 grid, hipStream_t st, int64_t I, const snack_co
 }
 
 template <typename OutT>
-void launch_colbwd(const BwdPlan &p, bool split, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W,
+void launch_colbwd(const BwdPlan &p, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W,
                    const float *xt, const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW) {
-#define SNACK_COLBWD(BTV)                                                                             \
-    if (split)                                                                                        \
-        launch_colbwd_q<OutT, BTV, 4>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);              \
-    else                                                                                              \
-        launch_colbwd_q<OutT, BTV, 1>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);
-    if (p.bt == 16) {
-        SNACK_COLBWD(16)
-    } else if (p.bt == 8) {
-        SNACK_COLBWD(8)
-    } else {
-        SNACK_COLBWD(4)
-    }
-#undef SNACK_COLBWD
+    if (p.bt == 16)
+        launch_colbwd_q<OutT, 16, 1>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);
+    else if (p.bt == 8)
+        launch_colbwd_q<OutT, 8, 1>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);
+    else
+        launch_colbwd_q<OutT, 4, 1>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);
 }
 
 }  // namespace
@@ -1855,15 +1850,16 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
         float *dyt = reinterpret_cast<float *>(ws + p.off_dy);
         if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st)) return s;
         if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dyt, st)) return s;
-        // columns averaging >= 256 entries are split over the 4 waves of a workgroup
-        const bool split = nnz >= 256 * I;
-        const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(I, split ? 1 : kWavesPerBlock))));
+        // one wave per column: co-resident waves then walk their columns' rows in step, so the
+        // vals reads and dW writes through the column permutation share L2 lines (splitting
+        // long columns over 4 waves scatters them over the whole triple at once)
+        const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(I, kWavesPerBlock))));
         const int zero_row = static_cast<int>(O);
         probe(true, st);
         if (act_dtype == SNACK_F32)
-            launch_colbwd<float>(p, split, grid, st, I, W, xt, dyt, zero_row, batch, static_cast<float *>(dX), dW);
+            launch_colbwd<float>(p, grid, st, I, W, xt, dyt, zero_row, batch, static_cast<float *>(dX), dW);
         else
-            launch_colbwd<bf16_t>(p, split, grid, st, I, W, xt, dyt, zero_row, batch, static_cast<bf16_t *>(dX), dW);
+            launch_colbwd<bf16_t>(p, grid, st, I, W, xt, dyt, zero_row, batch, static_cast<bf16_t *>(dX), dW);
         probe(false, st);
         if (int s = check_hip("colbwd_kernel")) return s;
         return snack::ok();
