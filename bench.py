@@ -246,7 +246,7 @@ def cpu_baseline(layer, budget_s=15.0):
         bs = min(B, bs * 2)
         t = run(bs)
     reps, total = 1, t
-    while total < budget_s and reps < 64:
+    while total < budget_s and reps < 2000:
         total += run(bs)
         reps += 1
     us_per_step = total / reps * 1e6 * (B / bs)
