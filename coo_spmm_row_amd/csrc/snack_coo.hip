@@ -102,26 +102,37 @@ __device__ __forceinline__ int64_t xcd_block() {
 // A workgroup moves a tile of 16 features x 64 batch rows through LDS: every
 // thread issues its four loads (64-byte row segments) before its stores, and
 // the tile's output is one contiguous run when B <= 64.
-constexpr int kTf = 16, kTb = 64;
+constexpr int kTf = 32, kTb = 64;
+// Up to two tensors per launch (blockIdx.z; the backward pass transposes X and dY together).
+// A workgroup moves a tile of 32 features x 64 batch rows through LDS: each thread issues its
+// eight loads (128-byte row segments per 32 lanes) before its stores, and the tile's output is
+// one contiguous run per feature.
 template <typename InT>
-__global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__restrict__ in,
-                                                                  float *__restrict__ out,
-                                                                  int64_t B, int64_t F) {
+__global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__restrict__ in0,
+                                                                  float *__restrict__ out0, int64_t F0,
+                                                                  const InT *__restrict__ in1,
+                                                                  float *__restrict__ out1, int64_t F1,
+                                                                  int64_t B) {
     __shared__ float tile[kTb][kTf + 1];
+    const InT *__restrict__ in = blockIdx.z == 0 ? in0 : in1;
+    float *__restrict__ out = blockIdx.z == 0 ? out0 : out1;
+    const int64_t F = blockIdx.z == 0 ? F0 : F1;
     const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kTf;
+    if (f0 >= F && !(blockIdx.x == 0)) return;  // uniform per workgroup, before the barrier
     const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTb;
-    const int tx = threadIdx.x % kTf, ty = threadIdx.x / kTf;  // 16 x 16
+    const int tx = threadIdx.x % kTf, ty = threadIdx.x / kTf;  // 32 x 8
     const int nb = static_cast<int>(min<int64_t>(kTb, B - b0));
-    const int nf = static_cast<int>(min<int64_t>(kTf, F - f0));
+    const int nf = static_cast<int>(max<int64_t>(0, min<int64_t>(kTf, F - f0)));
     if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < nb) out[F * B + b0 + threadIdx.x] = 0.f;
-    float v[kTb / 16];
+    constexpr int K = kTb / (kBlock / kTf);  // 8 rows per thread
+    float v[K];
 #pragma unroll
-    for (int i = 0; i < kTb / 16; ++i) {
-        const int bb = ty + 16 * i;
+    for (int i = 0; i < K; ++i) {
+        const int bb = ty + (kBlock / kTf) * i;
         v[i] = (bb < nb && tx < nf) ? load_act(in, (b0 + bb) * F + f0 + tx) : 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < kTb / 16; ++i) tile[ty + 16 * i][tx] = v[i];
+    for (int i = 0; i < K; ++i) tile[ty + (kBlock / kTf) * i][tx] = v[i];
     __syncthreads();
     for (int li = threadIdx.x; li < nf * nb; li += kBlock) {
         const int ff = li / nb, bb = li % nb;
@@ -1375,16 +1386,20 @@ int check_workspace(void *ws, size_t have, size_t need, const char *who) {
     return SNACK_OK;
 }
 
-// activation [B][F] -> feature-major fp32 [F][B] in `dst`
-int launch_to_feature_major(const void *src, int dtype, int64_t B, int64_t F, float *dst, hipStream_t st) {
-    if (B == 0 || F == 0) return SNACK_OK;
-    const dim3 grid(static_cast<unsigned>(ceil_div(F, kTf)), static_cast<unsigned>(ceil_div(B, kTb)));
+// activation [B][F] -> feature-major fp32 [F+1][B] in `dst` (row F zero); with src1 != NULL
+// also [B][F1] -> [F1+1][B] in dst1, in the same launch
+int launch_to_feature_major(const void *src, int dtype, int64_t B, int64_t F, float *dst, hipStream_t st,
+                            const void *src1 = nullptr, int64_t F1 = 0, float *dst1 = nullptr) {
+    if (B == 0 || (F == 0 && F1 == 0 && !src1)) return SNACK_OK;
+    const int64_t fmax = std::max(F, src1 ? F1 : 0);
+    const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, ceil_div(fmax, kTf))),
+                    static_cast<unsigned>(ceil_div(B, kTb)), src1 ? 2u : 1u);
     if (dtype == SNACK_F32)
-        hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(kBlock), 0, st,
-                           static_cast<const float *>(src), dst, B, F);
+        hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(kBlock), 0, st, static_cast<const float *>(src),
+                           dst, F, static_cast<const float *>(src1), dst1, F1, B);
     else
         hipLaunchKernelGGL(to_feature_major_kernel<bf16_t>, grid, dim3(kBlock), 0, st,
-                           static_cast<const bf16_t *>(src), dst, B, F);
+                           static_cast<const bf16_t *>(src), dst, F, static_cast<const bf16_t *>(src1), dst1, F1, B);
     return check_hip("to_feature_major");
 }
 
@@ -1848,8 +1863,7 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
         }
         float *xt = reinterpret_cast<float *>(ws + p.off_x);
         float *dyt = reinterpret_cast<float *>(ws + p.off_dy);
-        if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st)) return s;
-        if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dyt, st)) return s;
+        if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st, dY, O, dyt)) return s;
         // one wave per column: co-resident waves then walk their columns' rows in step, so the
         // vals reads and dW writes through the column permutation share L2 lines (splitting
         // long columns over 4 waves scatters them over the whole triple at once)
