@@ -326,6 +326,29 @@ def test_batch1_large_layers(case, bf16):
     run_all(L, 1, 500 + seed, bf16=bf16)
 
 
+# snack_coo_bwd over batches that pick each variant of the one-pass backward (B = 4*BT*Q:
+# 16 -> BT 4, 32 -> BT 8, 64/128/256 -> BT 16 with Q 1/2/4) and batches that fall back to the
+# two separate calls (48, 192, 512); fp32 and bf16.
+@pytest.mark.parametrize("B", [16, 32, 48, 64, 128, 192, 256, 512])
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+def test_backward_batches(B, bf16):
+    say(f"backward B={B} bf16={bf16}")
+    L = synth.random_small_layer(181, 700, 900, 60000, "dense_lines")
+    O, I = L["out_features"], L["in_features"]
+    built, W = device_layer(L, DEV)
+    x_in, x64 = acts(40 + B, B, I, bf16)
+    dy_in, dy64 = acts(41 + B, B, O, bf16)
+    X, dY = to_device(x_in, DEV, bf16), to_device(dy_in, DEV, bf16)
+    db = torch.empty(O, dtype=torch.float32, device=DEV)
+    dX, dW = snk.snack_coo_bwd(W, X, dY, db=db)
+    torch.cuda.synchronize()
+    r, c, v = built["rows"], built["cols"], built["vals"]
+    nnz = L["nnz"]
+    check_close(from_device(dX), oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS), nnz / I, "dX", bf16)
+    check_close(dW.cpu().numpy(), oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS), B, "dW")
+    check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, "db")
+
+
 @pytest.mark.parametrize("B", [64, 192])
 def test_wide_layer_bf16(B):
     say(f"wide layer bf16 B={B}")
