@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 
@@ -422,33 +423,106 @@ __global__ __launch_bounds__(kBlock) void sddmm_kernel(int64_t nnz, int64_t step
     }
 }
 
+// Largest r in [0, O) with offs[r] <= e, for 0 <= e < offs[O]: the row holding entry e.
+// Wave-parallel: each round samples the interval at 64 points.
+__device__ int csr_row_of(const int32_t *__restrict__ offs, int O, int e, int lane) {
+    int lo = 0, hi = O;  // offs[lo] <= e < offs[hi]
+    while (hi - lo > kWave) {
+        const int len = hi - lo;
+        const int q = lo + static_cast<int>((static_cast<int64_t>(lane) * len) >> 6);
+        const int c = __popcll(__ballot(offs[q] <= e));  // a prefix of the lanes, c >= 1
+        const int qa = lo + static_cast<int>((static_cast<int64_t>(c - 1) * len) >> 6);
+        hi = c == kWave ? hi : lo + static_cast<int>((static_cast<int64_t>(c) * len) >> 6);
+        lo = qa;
+    }
+    const int r = lo + lane;
+    const bool le = r < hi && offs[min(r, O)] <= e;
+    return lo + __popcll(__ballot(le)) - 1;
+}
+
+// As csr_row_of, trying first the 64 rows around the row that entry e would be in if
+// all rows had the average length (one round of loads for near-uniform layers).
+__device__ int csr_row_of_guess(const int32_t *__restrict__ offs, int O, int nnz, int e, int lane) {
+    // a guess only: float arithmetic (a 64-bit integer division costs ~100 scalar instructions)
+    const int g = static_cast<int>(static_cast<float>(e) * (static_cast<float>(O) *
+                                                            __builtin_amdgcn_rcpf(static_cast<float>(nnz))));
+    const int lo = max(0, min(g - kWave / 2, O - 1));
+    const int v = offs[min(lo + lane, O)];  // offs[O] = nnz > e
+    const int c = __popcll(__ballot(v <= e));
+    if (c >= 1 && c < kWave) return lo + c - 1;  // offs[lo + c - 1] <= e < offs[lo + c]
+    return csr_row_of(offs, O, e, lane);
+}
+
+// First index j in [lo, hi) with a[j] >= target (a ascending on [lo, hi)), or hi.
+// The wave first tries the 64 entries around `guess`, then narrows the interval
+// 64-fold per round of loads.  Every argument is uniform across the wave.
+__device__ int wave_lower_bound(const int32_t *__restrict__ a, int lo, int hi, int target, int guess, int lane) {
+    // invariant: the answer lies in [lo, hi]
+    if (hi - lo > kWave) {
+        const int w = min(max(guess - kWave / 2, lo), hi - kWave);
+        const int c = __popcll(__ballot(a[w + lane] < target));  // a prefix of the lanes
+        if (c > 0 && c < kWave) return w + c;
+        if (c == 0)
+            hi = w;
+        else
+            lo = w + kWave;
+    }
+    while (hi - lo > kWave) {
+        const int stride = (hi - lo + kWave - 1) / kWave;
+        const int j = lo + lane * stride;
+        const int c = __popcll(__ballot(j < hi && a[min(j, hi - 1)] < target));
+        if (c == 0) return lo;
+        const int nlo = lo + (c - 1) * stride + 1;
+        hi = min(hi, lo + c * stride);
+        lo = nlo;
+    }
+    if (hi <= lo) return lo;
+    const int j = lo + lane;
+    return lo + __popcll(__ballot(j < hi && a[min(j, hi - 1)] < target));
+}
+
 // Both gradients in one pass over the column view (batch 4*BT*Q, Q in {1, 2, 4}).
-// A workgroup owns 4/WPR input columns i, each split over WPR waves.  The
-// column's X slice is held in registers (lane t: float4s t, t+BT, .. of the
-// feature-major X row i); each stored entry k of the column gathers its dY row
-// once and uses it twice: dX[., i] += vals[k] * dY[., row k] (accumulated as in
-// rowwave_kernel) and dW[k] = <X[., i], dY[., row k]> (summed over the slot's
-// BT lanes by DPP, written at the entry's row-order position).  The window
-// holds, per entry, the dY row as a 32-bit float4 offset, the value and that
-// position; lanes past the column's end point at dY's zero row.
-template <int BT, int WPR, int Q, typename OutT>
+// A wave owns one input column i (with NB > 1: the column's entries whose rows lie in one
+// band of rows).  The column's X slice is held in registers (lane t: float4s t, t+BT, ..
+// of the feature-major X row i); each stored entry k gathers its dY row once and uses it
+// twice: dX[., i] += vals[k] * dY[., row k] (accumulated as in rowwave_kernel) and
+// dW[k] = <X[., i], dY[., row k]> (summed over the slot's BT lanes by DPP, written at the
+// entry's row-order position).  The window holds, per entry, the dY row as a 32-bit
+// float4 offset, the value and that position; lanes past the range point at dY's zero row.
+//
+// NB == 1: a workgroup owns 4 consecutive columns and writes dX directly.
+// NB == kXcds: the rows are cut into 8 bands of about nnz/8 entries each, and workgroup g
+// takes band g % 8 of columns 4*(g/8) .. +3.  Under round-robin dispatch band b then runs
+// on XCD b alone, walking the columns in order: the dY rows, vals and dW positions that
+// XCD touches are one eighth of each, and the dW lines of a row fill within a short span
+// of columns, so they are completed in L2 instead of being written back piecemeal.  Each
+// wave writes its band's share of dX[., i] as a feature-major row of part[b]; a second
+// kernel adds the bands in order.
+template <int BT, int Q, int NB, typename OutT>
 __global__ __launch_bounds__(kBlock) void colbwd_kernel(
     int64_t I, const int32_t *__restrict__ coffs, const int32_t *__restrict__ crows,
     const int32_t *__restrict__ cperm, const float *__restrict__ vals, const float *__restrict__ xt,
-    const float *__restrict__ dyt, int zero_row, int64_t B, OutT *__restrict__ dX, float *__restrict__ dW) {
+    const float *__restrict__ dyt, int zero_row, int64_t B, OutT *__restrict__ dX, float *__restrict__ dW,
+    const int32_t *__restrict__ offs, int nnz, float *__restrict__ part) {
     constexpr int S = kWave / BT;
     constexpr int UQ = 8 / Q;                                   // gathers in flight: U*Q float4s
     constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;       // S*U divides 64
-    constexpr int KPB = kWavesPerBlock / WPR;
-    __shared__ float4 part[kWavesPerBlock][BT * Q];
+    static_assert(U <= BT, "one storing lane per entry of a slot");
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int e = lane / BT, t = lane % BT;
-    const int64_t col = xcd_block() * KPB + wave / WPR;
-    const int wsub = wave % WPR;
+    int64_t col;
+    int band = 0;
+    if constexpr (NB == 1) {
+        col = xcd_block() * kWavesPerBlock + wave;
+    } else {
+        band = blockIdx.x % NB;
+        col = static_cast<int64_t>(blockIdx.x / NB) * kWavesPerBlock + wave;
+    }
     const bool cok = col < I;  // uniform per wave
     const int B4 = static_cast<int>(B / 4);
-    const char *__restrict__ yb = reinterpret_cast<const char *>(dyt) + 16u * static_cast<uint32_t>(t);
+    const char *__restrict__ yb = reinterpret_cast<const char *>(dyt);  // uniform base, 32-bit offsets
+    const uint32_t toff = 16u * static_cast<uint32_t>(t);
     float4 acc[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -458,8 +532,45 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
 #pragma unroll
         for (int q = 0; q < Q; ++q) xv[q] = x4[q * BT];
         const int zoff = zero_row * B4;
-        const int s = coffs[col], end = coffs[col + 1];
-        const int first = s + wsub * kWave;
+        int first = coffs[col], end = coffs[col + 1];
+        if constexpr (NB > 1) {
+            // rows [r0, r1) of this band: r_b = the row holding entry b*nnz/NB (r_0 = 0, r_NB = O).
+            // Both boundaries, and then both ends of the column's range, are found with loads
+            // issued together; a window that misses falls back to the full search.
+            const int O = zero_row;
+            const int e0 = static_cast<int>(static_cast<int64_t>(band) * nnz / NB);
+            const int e1 = min(nnz - 1, static_cast<int>(static_cast<int64_t>(band + 1) * nnz / NB));
+            const float rows_per_entry = static_cast<float>(O) * __builtin_amdgcn_rcpf(static_cast<float>(nnz));
+            const int q0 = max(0, min(static_cast<int>(e0 * rows_per_entry) - kWave / 2, O - 1));
+            const int q1 = max(0, min(static_cast<int>(e1 * rows_per_entry) - kWave / 2, O - 1));
+            const int o0 = offs[min(q0 + lane, O)], o1 = offs[min(q1 + lane, O)];  // offs[O] = nnz
+            const int c0 = __popcll(__ballot(o0 <= e0)), c1 = __popcll(__ballot(o1 <= e1));
+            int r0 = c0 >= 1 && c0 < kWave ? q0 + c0 - 1 : csr_row_of(offs, O, e0, lane);
+            int r1 = c1 >= 1 && c1 < kWave ? q1 + c1 - 1 : csr_row_of(offs, O, e1, lane);
+            if (band == 0) r0 = 0;
+            if (band == NB - 1) r1 = O;
+            const int s0 = first, len = end - first;
+            if (len > 0 && len <= kWave) {
+                const bool in = s0 + lane < end;
+                const int v = crows[min(s0 + lane, end - 1)];
+                first = s0 + __popcll(__ballot(in && v < r0));
+                end = s0 + __popcll(__ballot(in && v < r1));
+            } else if (len > kWave) {
+                // guesses: where the band's rows would start and end if the column's rows were uniform
+                const float per_row = static_cast<float>(len) * __builtin_amdgcn_rcpf(static_cast<float>(O));
+                const int g0 = s0 + static_cast<int>(per_row * r0), g1 = s0 + static_cast<int>(per_row * r1);
+                const int w0 = min(max(g0 - kWave / 2, s0), end - kWave);
+                const int w1 = min(max(g1 - kWave / 2, s0), end - kWave);
+                const int v0 = crows[w0 + lane], v1 = crows[w1 + lane];
+                const int n0 = __popcll(__ballot(v0 < r0)), n1 = __popcll(__ballot(v1 < r1));
+                const bool ok0 = (n0 > 0 || w0 == s0) && (n0 < kWave || w0 + kWave == end);
+                const bool ok1 = (n1 > 0 || w1 == s0) && (n1 < kWave || w1 + kWave == end);
+                const int j0 = ok0 ? w0 + n0 : wave_lower_bound(crows, s0, end, r0, g0, lane);
+                const int j1 = ok1 ? w1 + n1 : wave_lower_bound(crows, s0, end, r1, g1, lane);
+                first = j0;
+                end = j1;
+            }
+        }
         int mo = zoff, mp = 0;
         float mv = 0.f;
         if (first + lane < end) {
@@ -467,11 +578,11 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
             mo = crows[first + lane] * B4;
             mv = vals[mp];
         }
-        for (int base = first; base < end; base += WPR * kWave) {
+        for (int base = first; base < end; base += kWave) {
             const int co = mo, cp = mp;
             const float cv = mv;
             const int n = min(kWave, end - base);
-            const int nb = base + WPR * kWave;
+            const int nb = base + kWave;
             if (nb < end) {  // prefetch this wave's next chunk
                 mo = zoff;
                 mp = 0;
@@ -488,12 +599,18 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
                 float v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const uint32_t o = 16u * static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co));
+                    const uint32_t o =
+                        16u * static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co)) + toff;
                     v[u] = __int_as_float(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, __float_as_int(cv)));
 #pragma unroll
                     for (int q = 0; q < Q; ++q)
                         y[u][q] = *reinterpret_cast<const float4 *>(yb + (o + 16u * static_cast<uint32_t>(q * BT)));
                 }
+                // Banded: the dW values of the U entries per slot are stored together after the last
+                // gather is used (loads and stores share one completion counter, so a store issued
+                // between the gathers makes each later wait also wait for that store).  Unbanded,
+                // storing each entry as it completes measured faster.
+                float dsel = 0.f;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     float d = 0.f;
@@ -508,9 +625,20 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
                         d = fmaf(xv[q].z, y[u][q].z, d);
                         d = fmaf(xv[q].w, y[u][q].w, d);
                     }
-                    d = group_sum<BT>(d);
-                    const int k = __builtin_amdgcn_ds_bpermute(sa + 4 * S * u, cp);
-                    if (t == 0 && h + u * S + e < n) dW[k] = d;
+                    d = group_sum<BT>(d);  // the slot's sum, in all BT lanes
+                    if constexpr (NB > 1) {
+                        dsel = t == u ? d : dsel;
+                    } else {
+                        const int k = __builtin_amdgcn_ds_bpermute(sa + 4 * S * u, cp);
+                        if (t == 0 && h + u * S + e < n) dW[k] = d;
+                    }
+                }
+                if constexpr (NB > 1) {
+                    // lane t < U of slot e stores entry h + e + S*t
+                    const int k = __builtin_amdgcn_ds_bpermute(sa + 4 * S * (t < U ? t : 0), cp);
+                    if (t < U && h + t * S + e < n)
+                        *reinterpret_cast<float *>(reinterpret_cast<char *>(dW) + 4u * static_cast<uint32_t>(k)) =
+                            dsel;
                 }
             }
         }
@@ -525,35 +653,63 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
             acc[q].w += __shfl_xor(acc[q].w, d, kWave);
         }
     }
-    if constexpr (WPR > 1) {
-        if (e == 0) {
+    if (cok && e == 0) {
+        if constexpr (NB == 1) {
 #pragma unroll
-            for (int q = 0; q < Q; ++q) part[wave][t + q * BT] = acc[q];
-        }
-        __syncthreads();
-        if (wsub == 0 && e == 0) {
-#pragma unroll
-            for (int w2 = 1; w2 < WPR; ++w2) {
-#pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    const float4 o = part[wave + w2][t + q * BT];
-                    acc[q].x += o.x;
-                    acc[q].y += o.y;
-                    acc[q].z += o.z;
-                    acc[q].w += o.w;
-                }
+            for (int q = 0; q < Q; ++q) {
+                const int64_t b0 = 4 * static_cast<int64_t>(t + q * BT);
+                store_act(dX, (b0 + 0) * I + col, acc[q].x);
+                store_act(dX, (b0 + 1) * I + col, acc[q].y);
+                store_act(dX, (b0 + 2) * I + col, acc[q].z);
+                store_act(dX, (b0 + 3) * I + col, acc[q].w);
             }
+        } else {
+            float4 *__restrict__ p4 = reinterpret_cast<float4 *>(part) + (band * I + col) * B4 + t;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) p4[q * BT] = acc[q];
         }
     }
-    if (cok && wsub == 0 && e == 0) {
+}
+
+// dX[b][i] = sum over the NB bands, in band order, of part[band][i][b] (feature-major
+// fp32 partial sums) -> batch-major OutT.  A workgroup adds and transposes a tile of 32
+// columns x 64 batch rows through LDS; its stores are runs of 32 consecutive columns.
+template <int NB, typename OutT>
+__global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restrict__ part, int64_t I, int64_t B,
+                                                          OutT *__restrict__ dX) {
+    __shared__ float tile[kTb][kTf + 1];
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTf, b0 = static_cast<int64_t>(blockIdx.y) * kTb;
+    const int tid = threadIdx.x;
+    const int bq = tid % 16, cr = tid / 16;  // float4 bq of the tile's batch range, column cr and cr + 16
+    const int64_t B4 = B / 4;
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int64_t b0 = 4 * static_cast<int64_t>(t + q * BT);
-            store_act(dX, (b0 + 0) * I + col, acc[q].x);
-            store_act(dX, (b0 + 1) * I + col, acc[q].y);
-            store_act(dX, (b0 + 2) * I + col, acc[q].z);
-            store_act(dX, (b0 + 3) * I + col, acc[q].w);
+    for (int rr = 0; rr < 2; ++rr) {
+        const int64_t c = c0 + cr + 16 * rr;
+        const int64_t b4 = b0 / 4 + bq;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < I && b4 < B4) {
+            float4 v[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) v[k] = reinterpret_cast<const float4 *>(part)[(k * I + c) * B4 + b4];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                s.x += v[k].x;
+                s.y += v[k].y;
+                s.z += v[k].z;
+                s.w += v[k].w;
+            }
         }
+        tile[4 * bq + 0][cr + 16 * rr] = s.x;
+        tile[4 * bq + 1][cr + 16 * rr] = s.y;
+        tile[4 * bq + 2][cr + 16 * rr] = s.z;
+        tile[4 * bq + 3][cr + 16 * rr] = s.w;
+    }
+    __syncthreads();
+    const int c = tid % kTf;
+#pragma unroll
+    for (int k = 0; k < kTb / (kBlock / kTf); ++k) {
+        const int bb = tid / kTf + (kBlock / kTf) * k;
+        if (c0 + c < I && b0 + bb < B) store_act(dX, (b0 + bb) * I + c0 + c, tile[bb][c]);
     }
 }
 
@@ -828,34 +984,6 @@ __global__ __launch_bounds__(kBlock) void dx_reduce_kernel(int64_t n, int64_t np
 // rows' bias (forward) or dY values (gradients).  Eight 64-entry steps of loads
 // are in flight.  A step lies inside one row unless a row ends in it; only
 // then are lanes told apart by row.
-
-// Largest r in [0, O) with offs[r] <= e, for 0 <= e < offs[O]: the row holding entry e.
-// Wave-parallel: each round samples the interval at 64 points.
-__device__ int csr_row_of(const int32_t *__restrict__ offs, int O, int e, int lane) {
-    int lo = 0, hi = O;  // offs[lo] <= e < offs[hi]
-    while (hi - lo > kWave) {
-        const int len = hi - lo;
-        const int q = lo + static_cast<int>((static_cast<int64_t>(lane) * len) >> 6);
-        const int c = __popcll(__ballot(offs[q] <= e));  // a prefix of the lanes, c >= 1
-        const int qa = lo + static_cast<int>((static_cast<int64_t>(c - 1) * len) >> 6);
-        hi = c == kWave ? hi : lo + static_cast<int>((static_cast<int64_t>(c) * len) >> 6);
-        lo = qa;
-    }
-    const int r = lo + lane;
-    const bool le = r < hi && offs[min(r, O)] <= e;
-    return lo + __popcll(__ballot(le)) - 1;
-}
-
-// As csr_row_of, trying first the 64 rows around the row that entry e would be in if
-// all rows had the average length (one round of loads for near-uniform layers).
-__device__ int csr_row_of_guess(const int32_t *__restrict__ offs, int O, int nnz, int e, int lane) {
-    const int g = static_cast<int>((static_cast<int64_t>(e) * O) / nnz);
-    const int lo = max(0, min(g - kWave / 2, O - 1));
-    const int v = offs[min(lo + lane, O)];  // offs[O] = nnz > e
-    const int c = __popcll(__ballot(v <= e));
-    if (c >= 1 && c < kWave) return lo + c - 1;  // offs[lo + c - 1] <= e < offs[lo + c]
-    return csr_row_of(offs, O, e, lane);
-}
 
 __device__ __forceinline__ float readlane_f(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
@@ -1317,9 +1445,24 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
 // gradient and the weight gradient one after the other, sharing the workspace.
 struct BwdPlan {
     bool fused;
-    int bt, q;
-    size_t off_x, off_dy, total;
+    int bt, q, nb;  // nb: row bands of the fused kernel (1 or kXcds)
+    size_t off_x, off_dy, off_part, total;
 };
+
+#ifndef SNACK_BAND_MIN_NNZ
+#define SNACK_BAND_MIN_NNZ (int64_t(1) << 20)
+#endif
+
+// Layers with at least this many entries take the row-banded form of the fused backward pass;
+// the environment variable SNACK_COO_BAND_MIN_NNZ (a decimal count) overrides the default.
+int64_t band_min_nnz() {
+    if (const char *env = std::getenv("SNACK_COO_BAND_MIN_NNZ")) {
+        char *end = nullptr;
+        const long long v = std::strtoll(env, &end, 10);
+        if (end != env && *end == '\0' && v >= 0) return v;
+    }
+    return SNACK_BAND_MIN_NNZ;
+}
 
 BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
     BwdPlan p{};
@@ -1331,6 +1474,8 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
             p.fused = true;
             p.bt = bt;
             p.q = static_cast<int>(q);
+            // row bands (one per XCD) once the triple is large enough to spill L2
+            p.nb = nnz >= band_min_nnz() ? kXcds : 1;
         }
     }
     if (p.fused) {
@@ -1339,6 +1484,8 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
         at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * B));
         p.off_dy = at;
         at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * B));
+        p.off_part = at;
+        if (p.nb > 1) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nb * I * B));
         p.total = at;
     } else {
         p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true).total, plan_sddmm(nnz, O, I, B, dtype).total);
@@ -1798,29 +1945,50 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
 
 namespace {
 
-template <typename OutT, int BT, int WPR>
+template <typename OutT, int BT, int NB>
 void launch_colbwd_q(int q, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W, const float *xt,
-                     const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW) {
+                     const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part) {
+    const int nnz = static_cast<int>(W->nnz);
     if (q == 1)
-        hipLaunchKernelGGL((colbwd_kernel<BT, WPR, 1, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
-                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW);
+        hipLaunchKernelGGL((colbwd_kernel<BT, 1, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
+                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
+                           part);
     else if (q == 2)
-        hipLaunchKernelGGL((colbwd_kernel<BT, WPR, 2, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
-                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW);
+        hipLaunchKernelGGL((colbwd_kernel<BT, 2, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
+                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
+                           part);
     else
-        hipLaunchKernelGGL((colbwd_kernel<BT, WPR, 4, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
-                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW);
+        hipLaunchKernelGGL((colbwd_kernel<BT, 4, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
+                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
+                           part);
+}
+
+template <typename OutT, int NB>
+void launch_colbwd_nb(const BwdPlan &p, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W,
+                      const float *xt, const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part) {
+    if (p.bt == 16)
+        launch_colbwd_q<OutT, 16, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+    else if (p.bt == 8)
+        launch_colbwd_q<OutT, 8, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+    else
+        launch_colbwd_q<OutT, 4, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
 }
 
 template <typename OutT>
-void launch_colbwd(const BwdPlan &p, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W,
-                   const float *xt, const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW) {
-    if (p.bt == 16)
-        launch_colbwd_q<OutT, 16, 1>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);
-    else if (p.bt == 8)
-        launch_colbwd_q<OutT, 8, 1>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);
-    else
-        launch_colbwd_q<OutT, 4, 1>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW);
+int launch_colbwd(const BwdPlan &p, hipStream_t st, int64_t I, const snack_coo_desc *W, const float *xt,
+                  const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part) {
+    if (p.nb == 1) {
+        // one wave per column, 4 consecutive columns per workgroup, each XCD an eighth of the columns
+        const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(I, kWavesPerBlock))));
+        launch_colbwd_nb<OutT, 1>(p, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        return check_hip("colbwd_kernel");
+    }
+    const dim3 grid(static_cast<unsigned>(kXcds * ceil_div(I, kWavesPerBlock)));
+    launch_colbwd_nb<OutT, kXcds>(p, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+    if (int s = check_hip("colbwd_kernel")) return s;
+    const dim3 sgrid(static_cast<unsigned>(ceil_div(I, kTf)), static_cast<unsigned>(ceil_div(B, kTb)));
+    hipLaunchKernelGGL((band_sum_kernel<kXcds, OutT>), sgrid, dim3(kBlock), 0, st, part, I, B, dX);
+    return check_hip("band_sum_kernel");
 }
 
 }  // namespace
@@ -1867,15 +2035,15 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
         // one wave per column: co-resident waves then walk their columns' rows in step, so the
         // vals reads and dW writes through the column permutation share L2 lines (splitting
         // long columns over 4 waves scatters them over the whole triple at once)
-        const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(I, kWavesPerBlock))));
         const int zero_row = static_cast<int>(O);
+        float *part = reinterpret_cast<float *>(ws + p.off_part);
         probe(true, st);
-        if (act_dtype == SNACK_F32)
-            launch_colbwd<float>(p, grid, st, I, W, xt, dyt, zero_row, batch, static_cast<float *>(dX), dW);
-        else
-            launch_colbwd<bf16_t>(p, grid, st, I, W, xt, dyt, zero_row, batch, static_cast<bf16_t *>(dX), dW);
+        int s = act_dtype == SNACK_F32
+                    ? launch_colbwd<float>(p, st, I, W, xt, dyt, zero_row, batch, static_cast<float *>(dX), dW, part)
+                    : launch_colbwd<bf16_t>(p, st, I, W, xt, dyt, zero_row, batch, static_cast<bf16_t *>(dX), dW,
+                                            part);
         probe(false, st);
-        if (int s = check_hip("colbwd_kernel")) return s;
+        if (s) return s;
         return snack::ok();
     } catch (...) {
         return fail(SNACK_ERR_INTERNAL, "snack_coo_bwd: unexpected exception");

@@ -164,7 +164,13 @@ int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY
  * two calls; requires the column view; workspace >=
  * snack_coo_workspace_bytes(SNACK_OP_BWD, ...).  dX and dW are overwritten
  * (dW in the order of the triple); results agree with the separate calls to
- * rounding (the summation order of dX differs). */
+ * rounding (the summation order of dX differs).  Layers of at least 2^20
+ * entries take a row-banded form of the one-pass kernel: the rows are cut into
+ * 8 bands of about nnz/8 entries, each band's part of every column is walked on
+ * its own, and the 8 partial dX are added in band order (deterministic; the
+ * workspace then also holds 8*I*B floats).  The environment variable
+ * SNACK_COO_BAND_MIN_NNZ (a decimal entry count, read at every call of this
+ * function and of snack_coo_workspace_bytes) overrides that threshold. */
 int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch, int act_dtype,
                   void *dX, float *db, float *dW,
                   void *workspace, size_t workspace_bytes, void *hip_stream);

@@ -165,7 +165,8 @@ def make_acts(seed: int, batch: int, features: int) -> np.ndarray:
 def random_small_layer(seed: int, out_features: int, in_features: int, nnz: int, shape: str = "uniform"):
     """Small hand-shaped layers for edge cases: 'uniform', 'one_row', 'one_col', 'diag', 'empty_rows',
     'dense_lines' (uniform, plus two full rows and two full columns; three other rows and three
-    other columns keep only their entries on those full lines)."""
+    other columns keep only their entries on those full lines), 'skewed_rows' (row = floor(O*u^3)
+    for uniform u, so the low rows are dense and the high rows sparse; columns uniform)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     O, I = out_features, in_features
     if shape == "uniform":
@@ -193,6 +194,12 @@ def random_small_layer(seed: int, out_features: int, in_features: int, nnz: int,
         drop = np.isin(r_of, lines_r[2:]) | np.isin(c_of, lines_c[2:])
         keep_full = np.isin(r_of, lines_r[:2]) | np.isin(c_of, lines_c[:2])
         pos = pos[~drop | keep_full]
+    elif shape == "skewed_rows":
+        m = 2 * nnz + 64
+        r = np.minimum((O * rng.random(m) ** 3).astype(np.int64), O - 1)
+        c = rng.integers(0, I, size=m, dtype=np.int64)
+        cand = np.unique(r * I + c)
+        pos = np.sort(rng.choice(cand, size=min(nnz, cand.size), replace=False))
     else:
         raise ValueError(shape)
     pos = np.asarray(pos, dtype=np.int64)

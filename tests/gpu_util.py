@@ -1,6 +1,7 @@
 """Helpers for the GPU parity tests: device layers, tolerance checks, oracle sampling."""
 from __future__ import annotations
 
+import contextlib
 import functools
 import math
 import os
@@ -17,6 +18,28 @@ NTHREADS = max(1, min(16, os.cpu_count() or 1))
 def say(msg: str):
     print(f"[case] {msg}", flush=True)
     sys.stdout.flush()
+
+
+@contextlib.contextmanager
+def band_threshold(nnz_min: int | None):
+    """Run with SNACK_COO_BAND_MIN_NNZ set (the entry count from which snack_coo_bwd takes its
+    row-banded form), or with the library default when nnz_min is None."""
+    old = os.environ.get("SNACK_COO_BAND_MIN_NNZ")
+    if nnz_min is None:
+        os.environ.pop("SNACK_COO_BAND_MIN_NNZ", None)
+    else:
+        os.environ["SNACK_COO_BAND_MIN_NNZ"] = str(int(nnz_min))
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("SNACK_COO_BAND_MIN_NNZ", None)
+        else:
+            os.environ["SNACK_COO_BAND_MIN_NNZ"] = old
+
+
+# banded for every layer / never banded
+BANDINGS = {"banded": 1, "unbanded": 1 << 62}
 
 
 # ---------------------------------------------------------------- tolerances

@@ -73,3 +73,23 @@ def test_one_hip_runtime_in_process():
     """The library binds to torch's HIP runtime (same soname), so torch streams and events are valid."""
     runtimes = snk._hip_runtimes_mapped()
     assert len(runtimes) == 1, runtimes
+
+
+def test_banded_backward_workspace_follows_threshold(monkeypatch):
+    """The row-banded backward needs 8*I*B more floats of workspace; SNACK_COO_BAND_MIN_NNZ moves the
+    entry count from which snack_coo_bwd (and its workspace size) takes that form."""
+    lib = snk._lib
+    d = snk._Desc()
+    d.out_features, d.in_features, d.nnz = 300, 200, 5000
+    d.row_offsets = d.rows = d.cols = d.vals = 0x1000  # host-side sizing only: never dereferenced
+    d.col_perm = d.col_rows = d.col_cols = d.col_offsets = 0x1000
+    monkeypatch.setenv("SNACK_COO_BAND_MIN_NNZ", "1")
+    banded = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
+    monkeypatch.setenv("SNACK_COO_BAND_MIN_NNZ", str(1 << 62))
+    plain = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
+    monkeypatch.delenv("SNACK_COO_BAND_MIN_NNZ")
+    default = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)  # 5000 < 2^20: not banded
+    assert plain == default > 0
+    assert banded - plain >= 8 * 200 * 64 * 4
+    monkeypatch.setenv("SNACK_COO_BAND_MIN_NNZ", "not a number")  # ignored
+    assert lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0) == default

@@ -6,8 +6,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import (NTHREADS, acts, check_close, device_layer, from_device, named_layer, oracle_dw_entries,
-                      oracle_dx_cols, oracle_fwd_rows, say, to_device)
+from gpu_util import (BANDINGS, NTHREADS, acts, band_threshold, check_close, device_layer, from_device, named_layer,
+                      oracle_dw_entries, oracle_dx_cols, oracle_fwd_rows, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -326,27 +326,67 @@ def test_batch1_large_layers(case, bf16):
     run_all(L, 1, 500 + seed, bf16=bf16)
 
 
-# snack_coo_bwd over batches that pick each variant of the one-pass backward (B = 4*BT*Q:
-# 16 -> BT 4, 32 -> BT 8, 64/128/256 -> BT 16 with Q 1/2/4) and batches that fall back to the
-# two separate calls (48, 192, 512); fp32 and bf16.
-@pytest.mark.parametrize("B", [16, 32, 48, 64, 128, 192, 256, 512])
-@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
-def test_backward_batches(B, bf16):
-    say(f"backward B={B} bf16={bf16}")
-    L = synth.random_small_layer(181, 700, 900, 60000, "dense_lines")
-    O, I = L["out_features"], L["in_features"]
+def _check_bwd(L, B, seed, bf16=False):
+    """snack_coo_bwd (dX, dW, db) against the oracle."""
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
     built, W = device_layer(L, DEV)
-    x_in, x64 = acts(40 + B, B, I, bf16)
-    dy_in, dy64 = acts(41 + B, B, O, bf16)
+    x_in, x64 = acts(seed, B, I, bf16)
+    dy_in, dy64 = acts(seed + 1, B, O, bf16)
     X, dY = to_device(x_in, DEV, bf16), to_device(dy_in, DEV, bf16)
     db = torch.empty(O, dtype=torch.float32, device=DEV)
     dX, dW = snk.snack_coo_bwd(W, X, dY, db=db)
     torch.cuda.synchronize()
     r, c, v = built["rows"], built["cols"], built["vals"]
-    nnz = L["nnz"]
-    check_close(from_device(dX), oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS), nnz / I, "dX", bf16)
+    check_close(from_device(dX), oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS), nnz / max(I, 1), "dX",
+                bf16)
     check_close(dW.cpu().numpy(), oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS), B, "dW")
     check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, "db")
+    # a second call gives the same bits (fixed summation order, band partials added in order)
+    dX2, dW2 = snk.snack_coo_bwd(W, X, dY)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dX2) and torch.equal(dW, dW2)
+
+
+# snack_coo_bwd over batches that pick each variant of the one-pass backward (B = 4*BT*Q:
+# 16 -> BT 4, 32 -> BT 8, 64/128/256 -> BT 16 with Q 1/2/4) and batches that fall back to the
+# two separate calls (48, 192, 512); fp32 and bf16; the one-pass kernel with and without row bands.
+@pytest.mark.parametrize("banding", list(BANDINGS))
+@pytest.mark.parametrize("B", [16, 32, 48, 64, 128, 192, 256, 512])
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+def test_backward_batches(B, bf16, banding):
+    say(f"backward B={B} bf16={bf16} {banding}")
+    L = synth.random_small_layer(181, 700, 900, 60000, "dense_lines")
+    with band_threshold(BANDINGS[banding]):
+        _check_bwd(L, B, 40 + B, bf16)
+
+
+# The row-banded backward on layers whose bands are uneven or empty: rows holding more than an
+# eighth of the entries (several band boundaries fall on one row), three rows in four empty, full
+# rows and columns, rows skewed so that neither the band rows nor the columns' band ranges are
+# where a uniform guess puts them (the full searches run), columns longer and shorter than a
+# wave, and layers of 1 row or 1 column.
+BANDED = [  # seed, shape, O, I, nnz
+    (211, "one_row", 40, 5000, 5000),
+    (212, "empty_rows", 3000, 900, 120000),
+    (213, "dense_lines", 2600, 2100, 300000),
+    (214, "uniform", 9000, 300, 400000),
+    (215, "uniform", 300, 9000, 200000),
+    (216, "uniform", 1, 5000, 1500),
+    (217, "uniform", 5000, 1, 700),
+    (218, "diag", 333, 333, 333),
+    (219, "dense_lines", 50, 20000, 50000),
+    (220, "skewed_rows", 4000, 1200, 400000),
+]
+
+
+@pytest.mark.parametrize("case", BANDED, ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}")
+@pytest.mark.parametrize("B", [16, 64, 128])
+def test_backward_row_bands(case, B):
+    seed, shape, O, I, nnz = case
+    say(f"banded backward {shape} {O}x{I} nnz={nnz} B={B}")
+    L = synth.random_small_layer(seed, O, I, nnz, shape)
+    with band_threshold(1):
+        _check_bwd(L, B, 900 + seed + B)
 
 
 @pytest.mark.parametrize("B", [64, 192])
