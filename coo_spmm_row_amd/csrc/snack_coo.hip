@@ -1171,14 +1171,61 @@ __global__ __launch_bounds__(THREADS) void csr1_dw_kernel(int O, int I, int nnz,
 
 // Input gradient, batch 1, I <= 10240, without atomics: each of a workgroup's
 // 4 waves owns a private LDS copy of dX and the rows whose first entry lies in
-// its chunk, and walks them in steps of 64 entries that never span two rows.
-// The columns of one row are distinct and a wave's LDS operations complete in
-// order, so each lane adds vals[k] * dY[row k] into its copy with a plain
-// read and write.  The copies are then added in wave order into
-// partial[blockIdx.x], and dx_reduce_kernel adds the workgroups in order:
-// the result is deterministic.
+// its chunk.  A lane takes 4 consecutive entries per step (16-byte loads of cols
+// and vals), so a step covers 256 entries; two batches of kDxSteps steps are in
+// flight (a CU holds only 4 of these waves, so bytes in flight per wave set the
+// rate).  A step inside one row adds vals[k] * dY[row] into the copy with plain
+// reads and writes: a row's columns are distinct and a wave's LDS operations
+// complete in order.  A step that crosses row ends is taken row by row.  The
+// copies are then added in wave order into partial[blockIdx.x], and
+// dx_reduce_kernel adds the workgroups in order: the result is deterministic.
+// cols and vals must be 16-byte aligned (the plan checks).
 constexpr int kPrivWaves = 4;
 constexpr int64_t kPrivMaxI = 10240;  // 4 copies of dX in 160 KB of LDS
+constexpr int kDxSteps = 8;           // steps of 256 entries per batch of loads
+
+// 4 entries per lane from entry s + 4*lane, clamped to the last whole 16-byte group below
+// nnz4 = nnz & ~3 (the same two loads on every path, so the compiler's completion counting
+// stays exact; the entries [nnz4, nnz) are taken separately).
+__device__ __forceinline__ void dxq_load(const int32_t *__restrict__ cols, const float *__restrict__ vals, int nnz4,
+                                         int s, int lane, int4 &c, float4 &v) {
+    const int k = min(s + 4 * lane, nnz4 - 4);
+    c = *reinterpret_cast<const int4 *>(cols + k);
+    v = *reinterpret_cast<const float4 *>(vals + k);
+}
+
+// Row r's entries in the step of 256 from s (lanes hold entries k0 .. k0 + 3), then the
+// following rows while they start inside the step, up to entry `lim`; the row state (r, its
+// start Es, end E and dY value d, and the 64-row window from rb) advances with them.
+template <typename ActT>
+__device__ __forceinline__ void dxq_rows(float *my, int s, int k0, const int4 &c, const float4 &v, int lim, int &r,
+                                         int &rb, int &Es, int &E, float &d, int &wend, float &wdy,
+                                         const int32_t *__restrict__ offs, int O, const ActT *__restrict__ dy,
+                                         int lane) {
+    while (true) {
+        const int lo = max(Es, s), hi = min(E, lim);
+        const bool p0 = k0 >= lo && k0 < hi, p1 = k0 + 1 >= lo && k0 + 1 < hi;
+        const bool p2 = k0 + 2 >= lo && k0 + 2 < hi, p3 = k0 + 3 >= lo && k0 + 3 < hi;
+        float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
+        if (p0) t0 = my[c.x];
+        if (p1) t1 = my[c.y];
+        if (p2) t2 = my[c.z];
+        if (p3) t3 = my[c.w];
+        if (p0) my[c.x] = fmaf(v.x, d, t0);
+        if (p1) my[c.y] = fmaf(v.y, d, t1);
+        if (p2) my[c.z] = fmaf(v.z, d, t2);
+        if (p3) my[c.w] = fmaf(v.w, d, t3);
+        if (E >= s + 4 * kWave || E >= lim) break;
+        Es = E;
+        ++r;
+        if (r - rb >= kWave) {
+            rb = r;
+            csr_window(offs, O, rb, lane, dy, wend, wdy);
+        }
+        E = __builtin_amdgcn_readlane(wend, r - rb);
+        d = readlane_f(wdy, r - rb);
+    }
+}
 
 template <typename ActT>
 __global__ __launch_bounds__(kPrivWaves *kWave) void csr1_dxpriv_kernel(int O, int I, int nnz, int chunk, int nwaves,
@@ -1189,9 +1236,9 @@ __global__ __launch_bounds__(kPrivWaves *kWave) void csr1_dxpriv_kernel(int O, i
                                                                        float *__restrict__ partial) {
     extern __shared__ float cp[];  // [kPrivWaves][I]
     constexpr int kThreads = kPrivWaves * kWave;
+    constexpr int kStep = 4 * kWave;
     for (int i = threadIdx.x; i < kPrivWaves * I; i += kThreads) cp[i] = 0.f;
     __syncthreads();
-    constexpr int U = 8;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     float *my = cp + wave * I;
@@ -1209,44 +1256,63 @@ __global__ __launch_bounds__(kPrivWaves *kWave) void csr1_dxpriv_kernel(int O, i
             E1 = ob == b ? b : __builtin_amdgcn_readfirstlane(offs[rb1 + 1]);
         }
         if (E0 < E1) {
-            int r = csr_row_of_guess(offs, O, nnz, E0, lane);
+            int r = csr_row_of_guess(offs, O, nnz, E0, lane);  // the row starting at E0
             int rb = r, wend;
             float wdy;
             csr_window(offs, O, rb, lane, dy, wend, wdy);
+            int Es = E0;  // start of row r
             int E = __builtin_amdgcn_readlane(wend, 0);
             float d = readlane_f(wdy, 0);
-            for (int s0 = E0; s0 < E1; s0 += U * kWave) {
-                int c[U];
-                float v[U];
+            const int nnz4 = nnz & ~3;
+            const int E1m = min(E1, nnz4);  // the 16-byte loads cover [.., nnz4)
+            const int s00 = E0 & ~3;        // steps start 16-byte aligned
+            // batch of kDxSteps steps from s0 in (c, v): the whole step in row r takes the fast path
+            auto run = [&](int s0, const int4 *c, const float4 *v) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int kk = min(s0 + u * kWave + lane, E1 - 1);
-                    c[u] = cols[kk];
-                    v[u] = vals[kk];
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int s = s0 + u * kWave;
-                    if (s >= E1) break;
-                    const int k = s + lane;
-                    int from = 0;
-                    while (true) {
-                        // lanes [from, E - s) of this step are row r's
-                        if (k < E1 && lane >= from && k < E) {
-                            const float t = my[c[u]];
-                            my[c[u]] = t + v[u] * d;
+                for (int u = 0; u < kDxSteps; ++u) {
+                    const int s = s0 + u * kStep;
+                    if (s < E1m) {
+                        if (s >= Es && E >= s + kStep && E1m >= s + kStep) {  // the whole step is row r's
+                            const float t0 = my[c[u].x], t1 = my[c[u].y], t2 = my[c[u].z], t3 = my[c[u].w];
+                            my[c[u].x] = fmaf(v[u].x, d, t0);
+                            my[c[u].y] = fmaf(v[u].y, d, t1);
+                            my[c[u].z] = fmaf(v[u].z, d, t2);
+                            my[c[u].w] = fmaf(v[u].w, d, t3);
+                        } else {
+                            dxq_rows(my, s, s + 4 * lane, c[u], v[u], E1m, r, rb, Es, E, d, wend, wdy, offs, O, dy,
+                                     lane);
                         }
-                        if (E >= s + kWave || E >= E1) break;
-                        from = E - s;
-                        ++r;
-                        if (r - rb >= kWave) {
-                            rb = r;
-                            csr_window(offs, O, rb, lane, dy, wend, wdy);
-                        }
-                        E = __builtin_amdgcn_readlane(wend, r - rb);
-                        d = readlane_f(wdy, r - rb);
                     }
                 }
+                // every load of the batch is complete here on every path (a skipped step included),
+                // so the next batch's loads into these registers never wait for them
+#pragma unroll
+                for (int u = 0; u < kDxSteps; ++u) asm volatile("" ::"v"(c[u].x), "v"(v[u].x));
+            };
+            constexpr int kBatch = kDxSteps * kStep;
+            // two register sets used in turn (no copies, so no wait for the batch in flight)
+            int4 ca[kDxSteps], cb[kDxSteps];
+            float4 va[kDxSteps], vb[kDxSteps];
+#pragma unroll
+            for (int u = 0; u < kDxSteps; ++u) dxq_load(cols, vals, nnz4, s00 + u * kStep, lane, ca[u], va[u]);
+            for (int s0 = s00; s0 < E1m; s0 += 2 * kBatch) {
+#pragma unroll
+                for (int u = 0; u < kDxSteps; ++u)  // the next batch, unconditionally (clamped)
+                    dxq_load(cols, vals, nnz4, s0 + kBatch + u * kStep, lane, cb[u], vb[u]);
+                run(s0, ca, va);
+                if (s0 + kBatch >= E1m) break;
+#pragma unroll
+                for (int u = 0; u < kDxSteps; ++u)
+                    dxq_load(cols, vals, nnz4, s0 + 2 * kBatch + u * kStep, lane, ca[u], va[u]);
+                run(s0 + kBatch, cb, vb);
+            }
+            if (E1 > E1m) {  // entries [max(E0, nnz4), E1) at the end of the arrays: at most 3
+                const int s = nnz4, k0 = s + 4 * lane, last = nnz - 1;
+                const int4 ct = make_int4(cols[min(k0, last)], cols[min(k0 + 1, last)], cols[min(k0 + 2, last)],
+                                          cols[min(k0 + 3, last)]);
+                const float4 vt = make_float4(vals[min(k0, last)], vals[min(k0 + 1, last)], vals[min(k0 + 2, last)],
+                                              vals[min(k0 + 3, last)]);
+                dxq_rows(my, s, k0, ct, vt, E1, r, rb, Es, E, d, wend, wdy, offs, O, dy, lane);
             }
         }
     }
@@ -1316,7 +1382,13 @@ inline int pow2_at_least(int64_t x) {
 
 // nout = outputs per batch row; scatter_ok: the caller can run the scatter
 // mapping (input gradient: row-order entries, outputs indexed by column).
-SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok) {
+bool vec16(const snack_coo_desc *W) {
+    return reinterpret_cast<uintptr_t>(W->cols) % 16 == 0 && reinterpret_cast<uintptr_t>(W->vals) % 16 == 0;
+}
+
+// aligned16: cols and vals are 16-byte aligned (the batch-1 private-copy kernel loads 4 entries at once)
+SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok,
+                   bool aligned16 = false) {
     SpmmPlan p{};
     p.direct = (B == 1 && dtype == SNACK_F32);
     // batch 1, rows averaging >= 32 entries: stream cols and vals, rows from row_offsets,
@@ -1337,7 +1409,7 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
     }
     // batch-1 input gradient of a large layer: private per-wave copies of dX, no atomics
     // (below ~2M entries the atomic scatter's fixed costs are lower)
-    if (B == 1 && scatter_ok && nnz >= (int64_t(1) << 21) && nout <= kPrivMaxI) {
+    if (B == 1 && scatter_ok && aligned16 && nnz >= (int64_t(1) << 21) && nout <= kPrivMaxI) {
         p.direct = true;
         p.mapping = kCsr1Priv;
         // about 256 workgroups per 4 copies of dX that fit a CU's LDS, 4 waves each
@@ -1464,7 +1536,7 @@ int64_t band_min_nnz() {
     return SNACK_BAND_MIN_NNZ;
 }
 
-BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
+BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool aligned16) {
     BwdPlan p{};
     if (nnz > 0 && B >= 16 && B % 4 == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
         int bt = 4;  // lanes per slot: the largest power of two <= min(16, B/4)
@@ -1488,7 +1560,7 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
         if (p.nb > 1) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nb * I * B));
         p.total = at;
     } else {
-        p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true).total, plan_sddmm(nnz, O, I, B, dtype).total);
+        p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true, aligned16).total, plan_sddmm(nnz, O, I, B, dtype).total);
     }
     return p;
 }
@@ -1635,9 +1707,9 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
     const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
     switch (op) {
         case SNACK_OP_FWD: return plan_spmm(nnz, I, O, batch, act_dtype, false).total;
-        case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, I, batch, act_dtype, true).total;
+        case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W)).total;
         case SNACK_OP_GRAD_WEIGHT: return plan_sddmm(nnz, O, I, batch, act_dtype).total;
-        case SNACK_OP_BWD: return plan_bwd(nnz, O, I, batch, act_dtype).total;
+        case SNACK_OP_BWD: return plan_bwd(nnz, O, I, batch, act_dtype, vec16(W)).total;
         default: fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown op %d", op); return 0;
     }
 }
@@ -1738,7 +1810,7 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             if (int s = check_hip("bias_grad_kernel")) return s;
         }
         if (batch == 0 || I == 0) return snack::ok();
-        const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true);
+        const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W));
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
         if (p.mapping == kCsr1Priv) {
@@ -2004,7 +2076,7 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
         if (batch < 0 || batch > kMaxBatch)
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
-        const BwdPlan p = plan_bwd(nnz, O, I, batch, act_dtype);
+        const BwdPlan p = plan_bwd(nnz, O, I, batch, act_dtype, vec16(W));
         if (!p.fused) {
             if (int s = snack_coo_bwd_input(W, dY, batch, act_dtype, dX, db, workspace, workspace_bytes, hip_stream))
                 return s;
