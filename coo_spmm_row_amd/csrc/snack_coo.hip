@@ -942,35 +942,37 @@ __global__ __launch_bounds__(kScatterThreads) void dx_scatter_kernel(int64_t nnz
     for (int64_t i = threadIdx.x; i < n; i += kScatterThreads) mine[i] = dxs[i];
 }
 
-// out[i] = sum over w of partial[w][i], w ascending within each of 4 interleaved
+// out[i] = sum over w of partial[w][i], w ascending within each of 16 interleaved
 // slices, then the slices in order: a fixed summation order.  A workgroup covers
-// 64 outputs; its 4 waves take the slices and keep 8 loads in flight.
+// 64 outputs; its 16 waves take the slices and keep 8 loads in flight each.
+constexpr int kReduceThreads = 1024;
 template <typename OutT>
-__global__ __launch_bounds__(kBlock) void dx_reduce_kernel(int64_t n, int64_t nparts,
-                                                           const float *__restrict__ partial,
-                                                           OutT *__restrict__ out) {
-    __shared__ float slice_sum[kWavesPerBlock][kWave];
+__global__ __launch_bounds__(kReduceThreads) void dx_reduce_kernel(int64_t n, int64_t nparts,
+                                                                   const float *__restrict__ partial,
+                                                                   OutT *__restrict__ out) {
+    constexpr int kW = kReduceThreads / kWave;  // waves per workgroup, each over every kW-th part
+    __shared__ float slice_sum[kW][kWave];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kWave + lane;
     float s = 0.f;
     if (i < n) {
         constexpr int U = 8;
         int64_t w = wave;
-        for (; w + (U - 1) * kWavesPerBlock < nparts; w += U * kWavesPerBlock) {
+        for (; w + (U - 1) * kW < nparts; w += U * kW) {
             float v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = partial[(w + u * kWavesPerBlock) * n + i];
+            for (int u = 0; u < U; ++u) v[u] = partial[(w + u * kW) * n + i];
 #pragma unroll
             for (int u = 0; u < U; ++u) s += v[u];
         }
-        for (; w < nparts; w += kWavesPerBlock) s += partial[w * n + i];
+        for (; w < nparts; w += kW) s += partial[w * n + i];
     }
     slice_sum[wave][lane] = s;
     __syncthreads();
     if (wave == 0 && i < n) {
         float tot = slice_sum[0][lane];
 #pragma unroll
-        for (int q = 1; q < kWavesPerBlock; ++q) tot += slice_sum[q][lane];
+        for (int q = 1; q < kW; ++q) tot += slice_sum[q][lane];
         store_act(out, i, tot);
     }
 }
@@ -1184,12 +1186,13 @@ constexpr int kPrivWaves = 4;
 constexpr int64_t kPrivMaxI = 10240;  // 4 copies of dX in 160 KB of LDS
 constexpr int kDxSteps = 8;           // steps of 256 entries per batch of loads
 
-// 4 entries per lane from entry s + 4*lane, clamped to the last whole 16-byte group below
-// nnz4 = nnz & ~3 (the same two loads on every path, so the compiler's completion counting
-// stays exact; the entries [nnz4, nnz) are taken separately).
-__device__ __forceinline__ void dxq_load(const int32_t *__restrict__ cols, const float *__restrict__ vals, int nnz4,
+// 4 entries per lane from entry s + 4*lane, clamped to the 16-byte group at kmax (the wave's
+// last group below nnz & ~3).  Every path issues the same two loads, so the compiler's
+// completion counting stays exact, and loads past the wave's entries hit that one cached group
+// instead of fetching the next wave's; the entries [nnz & ~3, nnz) are taken separately.
+__device__ __forceinline__ void dxq_load(const int32_t *__restrict__ cols, const float *__restrict__ vals, int kmax,
                                          int s, int lane, int4 &c, float4 &v) {
-    const int k = min(s + 4 * lane, nnz4 - 4);
+    const int k = min(s + 4 * lane, kmax);
     c = *reinterpret_cast<const int4 *>(cols + k);
     v = *reinterpret_cast<const float4 *>(vals + k);
 }
@@ -1237,35 +1240,65 @@ __global__ __launch_bounds__(kPrivWaves *kWave) void csr1_dxpriv_kernel(int O, i
     extern __shared__ float cp[];  // [kPrivWaves][I]
     constexpr int kThreads = kPrivWaves * kWave;
     constexpr int kStep = 4 * kWave;
-    for (int i = threadIdx.x; i < kPrivWaves * I; i += kThreads) cp[i] = 0.f;
-    __syncthreads();
+    constexpr int kBatch = kDxSteps * kStep;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    float *my = cp + wave * I;
     const int w = blockIdx.x * kPrivWaves + wave;
+    const int a = w * chunk, b = min(a + chunk, nnz);
+    const int nnz4 = nnz & ~3;
+    // The first batch is loaded from the chunk's start before anything else (the row-aligned
+    // start E0 >= a is found while it is in flight; entries before E0 are not used).
+    const int s00 = a & ~3;
+    int4 ca[kDxSteps], cb[kDxSteps];
+    float4 va[kDxSteps], vb[kDxSteps];
+#pragma unroll
+    for (int u = 0; u < kDxSteps; ++u) dxq_load(cols, vals, nnz4 - 4, s00 + u * kStep, lane, ca[u], va[u]);
+    for (int i = threadIdx.x; i < kPrivWaves * I / 4; i += kThreads)  // 4*I floats: whole float4s
+        reinterpret_cast<float4 *>(cp)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    float *my = cp + wave * I;
     if (w < nwaves) {  // uniform per wave; every wave reaches the barrier below
-        // entries [E0, E1): from the first row start >= a to the first row start >= b
-        const int a = w * chunk, b = min(a + chunk, nnz);
-        const int ra = csr_row_of_guess(offs, O, nnz, a, lane);
-        const int oa = __builtin_amdgcn_readfirstlane(offs[ra]);
-        const int E0 = oa == a ? a : __builtin_amdgcn_readfirstlane(offs[ra + 1]);
-        int E1 = nnz;
+        // entries [E0, E1): from the first row start >= a to the first row start >= b.  Both
+        // ends, and the row starting at E0, come from one 64-row window of row_offsets each
+        // (loaded together) when the rows near a and b are where uniform rows would put them.
+        const float rows_per_entry = static_cast<float>(O) * __builtin_amdgcn_rcpf(static_cast<float>(nnz));
+        const int la = max(0, min(static_cast<int>(a * rows_per_entry) - kWave / 2, O - 1));
+        const int lb = max(0, min(static_cast<int>(b * rows_per_entry) - kWave / 2, O - 1));
+        const int wa = offs[min(la + lane, O)], wb = offs[min(lb + lane, O)];  // offs[O] = nnz
+        const int na = __popcll(__ballot(wa <= a)), nb = __popcll(__ballot(wb <= b));
+        int E0, E1 = nnz;
+        const bool hit_a = na >= 1 && na < kWave;  // offs[la + na - 1] <= a < offs[la + na]
+        if (hit_a) {
+            const int oa = __builtin_amdgcn_readlane(wa, na - 1);
+            E0 = oa == a ? a : __builtin_amdgcn_readlane(wa, na);
+        } else {
+            const int ra = csr_row_of(offs, O, a, lane);
+            const int oa = __builtin_amdgcn_readfirstlane(offs[ra]);
+            E0 = oa == a ? a : __builtin_amdgcn_readfirstlane(offs[ra + 1]);
+        }
         if (b < nnz) {
-            const int rb1 = csr_row_of_guess(offs, O, nnz, b, lane);
-            const int ob = __builtin_amdgcn_readfirstlane(offs[rb1]);
-            E1 = ob == b ? b : __builtin_amdgcn_readfirstlane(offs[rb1 + 1]);
+            if (nb >= 1 && nb < kWave) {
+                const int ob = __builtin_amdgcn_readlane(wb, nb - 1);
+                E1 = ob == b ? b : __builtin_amdgcn_readlane(wb, nb);
+            } else {
+                const int rb1 = csr_row_of(offs, O, b, lane);
+                const int ob = __builtin_amdgcn_readfirstlane(offs[rb1]);
+                E1 = ob == b ? b : __builtin_amdgcn_readfirstlane(offs[rb1 + 1]);
+            }
         }
         if (E0 < E1) {
-            int r = csr_row_of_guess(offs, O, nnz, E0, lane);  // the row starting at E0
+            // r: the row starting at E0 (the last of several that start there), from the same
+            // window when it reaches past E0
+            const int cr = __popcll(__ballot(wa <= E0));
+            int r = hit_a && cr < kWave ? la + cr - 1 : csr_row_of(offs, O, E0, lane);
             int rb = r, wend;
             float wdy;
             csr_window(offs, O, rb, lane, dy, wend, wdy);
             int Es = E0;  // start of row r
             int E = __builtin_amdgcn_readlane(wend, 0);
             float d = readlane_f(wdy, 0);
-            const int nnz4 = nnz & ~3;
             const int E1m = min(E1, nnz4);  // the 16-byte loads cover [.., nnz4)
-            const int s00 = E0 & ~3;        // steps start 16-byte aligned
+            const int kmax = min(nnz4, (E1 + 3) & ~3) - 4;
             // batch of kDxSteps steps from s0 in (c, v): the whole step in row r takes the fast path
             auto run = [&](int s0, const int4 *c, const float4 *v) {
 #pragma unroll
@@ -1289,21 +1322,16 @@ __global__ __launch_bounds__(kPrivWaves *kWave) void csr1_dxpriv_kernel(int O, i
 #pragma unroll
                 for (int u = 0; u < kDxSteps; ++u) asm volatile("" ::"v"(c[u].x), "v"(v[u].x));
             };
-            constexpr int kBatch = kDxSteps * kStep;
             // two register sets used in turn (no copies, so no wait for the batch in flight)
-            int4 ca[kDxSteps], cb[kDxSteps];
-            float4 va[kDxSteps], vb[kDxSteps];
-#pragma unroll
-            for (int u = 0; u < kDxSteps; ++u) dxq_load(cols, vals, nnz4, s00 + u * kStep, lane, ca[u], va[u]);
             for (int s0 = s00; s0 < E1m; s0 += 2 * kBatch) {
 #pragma unroll
                 for (int u = 0; u < kDxSteps; ++u)  // the next batch, unconditionally (clamped)
-                    dxq_load(cols, vals, nnz4, s0 + kBatch + u * kStep, lane, cb[u], vb[u]);
+                    dxq_load(cols, vals, kmax, s0 + kBatch + u * kStep, lane, cb[u], vb[u]);
                 run(s0, ca, va);
                 if (s0 + kBatch >= E1m) break;
 #pragma unroll
                 for (int u = 0; u < kDxSteps; ++u)
-                    dxq_load(cols, vals, nnz4, s0 + 2 * kBatch + u * kStep, lane, ca[u], va[u]);
+                    dxq_load(cols, vals, kmax, s0 + 2 * kBatch + u * kStep, lane, ca[u], va[u]);
                 run(s0 + kBatch, cb, vb);
             }
             if (E1 > E1m) {  // entries [max(E0, nnz4), E1) at the end of the arrays: at most 3
@@ -1318,11 +1346,28 @@ __global__ __launch_bounds__(kPrivWaves *kWave) void csr1_dxpriv_kernel(int O, i
     }
     __syncthreads();
     float *__restrict__ mine = partial + static_cast<int64_t>(blockIdx.x) * I;
-    for (int i = threadIdx.x; i < I; i += kThreads) {
-        float t = cp[i];
+    if (I % 4 == 0) {  // the copies and this partial are float4-aligned
+        const float4 *c4 = reinterpret_cast<const float4 *>(cp);
+        const int I4 = I / 4;
+        for (int i = threadIdx.x; i < I4; i += kThreads) {
+            float4 t = c4[i];
 #pragma unroll
-        for (int q = 1; q < kPrivWaves; ++q) t += cp[q * I + i];
-        mine[i] = t;
+            for (int q = 1; q < kPrivWaves; ++q) {
+                const float4 o = c4[q * I4 + i];
+                t.x += o.x;
+                t.y += o.y;
+                t.z += o.z;
+                t.w += o.w;
+            }
+            reinterpret_cast<float4 *>(mine)[i] = t;
+        }
+    } else {
+        for (int i = threadIdx.x; i < I; i += kThreads) {
+            float t = cp[i];
+#pragma unroll
+            for (int q = 1; q < kPrivWaves; ++q) t += cp[q * I + i];
+            mine[i] = t;
+        }
     }
 }
 
@@ -1840,10 +1885,10 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             if (int s = check_hip("csr1_dxpriv_kernel")) return s;
             const dim3 rgrid(static_cast<unsigned>(ceil_div(I, kWave)));
             if (act_dtype == SNACK_F32)
-                hipLaunchKernelGGL(dx_reduce_kernel<float>, rgrid, dim3(kBlock), 0, st, I, p.nparts, partial,
+                hipLaunchKernelGGL(dx_reduce_kernel<float>, rgrid, dim3(kReduceThreads), 0, st, I, p.nparts, partial,
                                    static_cast<float *>(dX));
             else
-                hipLaunchKernelGGL(dx_reduce_kernel<bf16_t>, rgrid, dim3(kBlock), 0, st, I, p.nparts, partial,
+                hipLaunchKernelGGL(dx_reduce_kernel<bf16_t>, rgrid, dim3(kReduceThreads), 0, st, I, p.nparts, partial,
                                    static_cast<bf16_t *>(dX));
             if (int s = check_hip("dx_reduce_kernel")) return s;
             return snack::ok();
@@ -1865,10 +1910,10 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             const int64_t n = batch * I;
             const dim3 grid(static_cast<unsigned>(ceil_div(n, kWave)));
             if (act_dtype == SNACK_F32)
-                hipLaunchKernelGGL(dx_reduce_kernel<float>, grid, dim3(kBlock), 0, st, n, p.nchunks, partial,
+                hipLaunchKernelGGL(dx_reduce_kernel<float>, grid, dim3(kReduceThreads), 0, st, n, p.nchunks, partial,
                                    static_cast<float *>(dX));
             else
-                hipLaunchKernelGGL(dx_reduce_kernel<bf16_t>, grid, dim3(kBlock), 0, st, n, p.nchunks, partial,
+                hipLaunchKernelGGL(dx_reduce_kernel<bf16_t>, grid, dim3(kReduceThreads), 0, st, n, p.nchunks, partial,
                                    static_cast<bf16_t *>(dX));
             if (int s = check_hip("dx_reduce_kernel")) return s;
             return snack::ok();
