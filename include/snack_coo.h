@@ -119,7 +119,10 @@ int snack_coo_build(int64_t out_features, int64_t in_features, int64_t nnz,
 
 /* Bytes of device workspace that `op` (SNACK_OP_*) needs for this layer,
  * batch size and activation dtype.  0 is a valid answer.  Returns 0 with
- * snack_last_error() set if the arguments are invalid. */
+ * snack_last_error() set if the arguments are invalid.  The answer can depend
+ * on the descriptor's pointers (at batch 1 the input gradient of a large layer
+ * takes its fastest kernel only when cols and vals are 16-byte aligned), so
+ * ask again for a descriptor whose arrays moved. */
 size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int64_t batch, int act_dtype);
 
 /* Forward SNACK layer (Algorithm 1 with the nn.Linear bias of Section 3.5):
