@@ -81,11 +81,12 @@ _lib.snack_coo_bwd_input.argtypes = [_D, _p, _i64, ctypes.c_int, _p, _p, _p, cty
 _lib.snack_coo_grad_weight.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, ctypes.c_size_t, _p]
 _lib.snack_coo_bwd.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.snack_coo_topology_update.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i64, _u64, _p, _p, _p, _p, _p]
+_lib.snack_coo_init_uniform.argtypes = [_i64, _i64, _i64, _u64, _p, _p, _p, _p]
 _lib.snack_coo_set_probe.argtypes = [_p, _p]
 
 EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_bwd_input",
-            "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_last_error",
-            "snack_coo_abi_version", "snack_coo_set_probe")
+            "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_coo_init_uniform",
+            "snack_last_error", "snack_coo_abi_version", "snack_coo_set_probe")
 
 
 def _np_ptr(a: Optional[np.ndarray]):
@@ -136,6 +137,19 @@ def snack_coo_topology_update(out_features: int, in_features: int, rows, cols, v
                                         _np_ptr(out["rows"]), _np_ptr(out["cols"]), _np_ptr(out["vals"]),
                                         _np_ptr(out["row_offsets"]), ctypes.byref(trials))
     _check(st, "snack_coo_topology_update")
+    out["trials"] = int(trials.value)
+    return out
+
+
+def snack_coo_init_uniform(out_features: int, in_features: int, nnz: int, seed: int):
+    """Host uniform initializer (Algorithm 2): nnz distinct positions, sorted by (row, col), with
+    row offsets and the number of trials (numpy out)."""
+    out = {"rows": np.empty(nnz, np.int32), "cols": np.empty(nnz, np.int32),
+           "row_offsets": np.empty(out_features + 1, np.int32)}
+    trials = ctypes.c_int64(0)
+    st = _lib.snack_coo_init_uniform(out_features, in_features, nnz, ctypes.c_uint64(seed), _np_ptr(out["rows"]),
+                                     _np_ptr(out["cols"]), _np_ptr(out["row_offsets"]), ctypes.byref(trials))
+    _check(st, "snack_coo_init_uniform")
     out["trials"] = int(trials.value)
     return out
 

@@ -81,7 +81,7 @@ using namespace snack;
 
 extern "C" const char *snack_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int snack_coo_abi_version(void) { return 2; }
+extern "C" int snack_coo_abi_version(void) { return 3; }
 
 extern "C" int snack_coo_build(int64_t O, int64_t I, int64_t nnz,
                                const int32_t *rows, const int32_t *cols, const float *vals,
@@ -152,6 +152,57 @@ extern "C" int snack_coo_build(int64_t O, int64_t I, int64_t nnz,
         return fail(SNACK_ERR_NOMEM, "build: out of host memory");
     } catch (...) {
         return fail(SNACK_ERR_INTERNAL, "build: unexpected exception");
+    }
+}
+
+extern "C" int snack_coo_init_uniform(int64_t O, int64_t I, int64_t nnz, uint64_t seed, int32_t *rows_out,
+                                      int32_t *cols_out, int32_t *row_offsets_out, int64_t *trials_out) {
+    try {
+        if (O <= 0 || I <= 0 || nnz < 0 || O > kInt32Max || I > kInt32Max || nnz > kInt32Max || nnz > O * I)
+            return fail(SNACK_ERR_SHAPE, "init_uniform: bad sizes (O=%lld I=%lld nnz=%lld)", (long long)O,
+                        (long long)I, (long long)nnz);
+        const uint64_t cells = static_cast<uint64_t>(O) * static_cast<uint64_t>(I);
+        if (cells > (1ULL << 34))
+            return fail(SNACK_ERR_SHAPE, "init_uniform: O*I=%llu exceeds the 2^34 bitmap limit",
+                        (unsigned long long)cells);
+        if (nnz > 0 && (!rows_out || !cols_out)) return fail(SNACK_ERR_NULL, "init_uniform: null array");
+        // Algorithm 2 from an empty set: rejection against a bitmap of the drawn positions
+        std::vector<uint64_t> drawn(static_cast<size_t>((cells + 63) / 64), 0);
+        SplitMix64 rng{seed};
+        int64_t trials = 0, count = 0;
+        while (count < nnz) {
+            const int64_t i = rng.below(O);
+            const int64_t j = rng.below(I);
+            ++trials;
+            const uint64_t q = static_cast<uint64_t>(i) * I + j;
+            uint64_t &w = drawn[q >> 6];
+            const uint64_t bit = 1ULL << (q & 63);
+            if (w & bit) continue;
+            w |= bit;
+            ++count;
+        }
+        // the bitmap holds exactly the drawn set: reading it in order gives the (row, col) sort
+        int64_t at = 0;
+        for (size_t wi = 0; wi < drawn.size() && at < nnz; ++wi) {
+            for (uint64_t w = drawn[wi]; w; w &= w - 1) {
+                const uint64_t q = (static_cast<uint64_t>(wi) << 6) + static_cast<uint64_t>(__builtin_ctzll(w));
+                rows_out[at] = static_cast<int32_t>(q / I);
+                cols_out[at] = static_cast<int32_t>(q % I);
+                ++at;
+            }
+        }
+        if (at != nnz) return fail(SNACK_ERR_INTERNAL, "init_uniform: produced %lld entries", (long long)at);
+        if (row_offsets_out) {
+            std::fill(row_offsets_out, row_offsets_out + O + 1, 0);
+            for (int64_t k = 0; k < nnz; ++k) ++row_offsets_out[rows_out[k] + 1];
+            for (int64_t r = 0; r < O; ++r) row_offsets_out[r + 1] += row_offsets_out[r];
+        }
+        if (trials_out) *trials_out = trials;
+        return ok();
+    } catch (const std::bad_alloc &) {
+        return fail(SNACK_ERR_NOMEM, "init_uniform: out of host memory");
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "init_uniform: unexpected exception");
     }
 }
 

@@ -178,6 +178,20 @@ int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_
                   void *dX, float *db, float *dW,
                   void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Host-side uniform initializer (Algorithm 2; its expected cost of about
+ * -ln(eta)/(1-eta) trials per entry at sparsity eta is in Appendix F): nnz
+ * distinct positions of the O x I matrix drawn by rejection.  Each trial draws
+ * row = getrand(O), then col = getrand(I), with getrand(n) = floor(u * n / 2^64)
+ * of the next SplitMix64 output u of a generator started at `seed` (the same
+ * generator as the regrowth of snack_coo_topology_update), and keeps the pair
+ * unless it was drawn before.  Output (host, caller-owned): rows_out, cols_out
+ * [nnz] sorted by (row, col), row_offsets_out [O+1] or NULL, the number of
+ * trials in trials_out (or NULL).  O*I is limited to 2^34 positions.  Values
+ * are the caller's (the pages fix only the positions). */
+int snack_coo_init_uniform(int64_t out_features, int64_t in_features, int64_t nnz, uint64_t seed,
+                           int32_t *rows_out, int32_t *cols_out, int32_t *row_offsets_out,
+                           int64_t *trials_out);
+
 /* Host-side topology update (Appendix G: magnitude prune-and-regrow; regrowth
  * with the uniform initializer of Algorithm 2).  Input: a HOST triple sorted
  * strictly by (row, col) (SNACK_ERR_UNSORTED otherwise).
@@ -211,7 +225,7 @@ int snack_coo_set_probe(void *start_event, void *stop_event);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *snack_last_error(void);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3 (3 added snack_coo_init_uniform). */
 int snack_coo_abi_version(void);
 
 #ifdef __cplusplus

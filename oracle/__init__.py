@@ -68,6 +68,7 @@ def configure(lib):
     lib.oracle_grad_bias.argtypes = [i64, i64, p, p]
     lib.oracle_topology.argtypes = [i64, i64, i64, p, p, p, i64, ctypes.c_uint64,
                                     p, p, p, p, p, p]
+    lib.oracle_init_uniform.argtypes = [i64, i64, i64, ctypes.c_uint64, p, p, p, p]
     lib.oracle_splitmix64.argtypes = [ctypes.c_uint64, i64, p]
     lib.oracle_splitmix64.restype = None
     lib.oracle_getrand.argtypes = [ctypes.c_uint64, i64, i64, p]
@@ -181,6 +182,21 @@ def getrand(seed: int, n: int, count: int) -> np.ndarray:
     lib = _load()
     out = np.empty(count, np.int64)
     lib.oracle_getrand(ctypes.c_uint64(seed), n, count, _ptr(out))
+    return out
+
+
+def init_uniform(O, I, nnz, seed):
+    """Algorithm 2: nnz distinct positions drawn by rejection (row, then column, per trial) from
+    one SplitMix64 stream; returns the sorted rows, cols, row offsets and the trial count."""
+    lib = _load()
+    out = {"rows": np.empty(nnz, np.int32), "cols": np.empty(nnz, np.int32),
+           "row_offsets": np.empty(O + 1, np.int32)}
+    trials = ctypes.c_int64(0)
+    st = lib.oracle_init_uniform(O, I, nnz, ctypes.c_uint64(seed), _ptr(out["rows"]), _ptr(out["cols"]),
+                                 _ptr(out["row_offsets"]), ctypes.byref(trials))
+    if st:
+        raise OracleError(st, "init_uniform")
+    out["trials"] = int(trials.value)
     return out
 
 

@@ -262,6 +262,38 @@ static int cmp_mag(const void *a, const void *b) {
 /* Input: a sorted triple.  Output: the sorted triple after prune-and-regrow,
  * pruned_out[0..n_prune) = the pruned positions of the input in ascending
  * order (optional), trials_out = number of (row, col) draws (optional). */
+/* Uniform initializer (SNACK, Algorithm 2; cost analysis in Appendix F): draw
+ * nnz distinct positions of the O x I matrix by rejection.  Each trial draws the
+ * row with getrand(O) and then the column with getrand(I) from one SplitMix64
+ * stream started at `seed`, and keeps the pair unless it was drawn before.  The
+ * positions are returned sorted by (row, col) with their row offsets (or NULL)
+ * and the number of trials. */
+int oracle_init_uniform(int64_t O, int64_t I, int64_t nnz, uint64_t seed,
+                        int32_t *rows_out, int32_t *cols_out, int32_t *row_offsets_out, int64_t *trials_out)
+{
+    if (O <= 0 || I <= 0 || nnz < 0 || nnz > O * I) return OR_SHAPE;
+    if (nnz > 0 && (!rows_out || !cols_out)) return OR_NULL;
+    unsigned char *seen = (unsigned char *)calloc((size_t)(O * I), 1);
+    int32_t *r = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nnz > 0 ? nnz : 1));
+    int32_t *c = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nnz > 0 ? nnz : 1));
+    if (!seen || !r || !c) { free(seen); free(r); free(c); return OR_NOMEM; }
+    uint64_t state = seed;
+    int64_t trials = 0, n = 0;
+    while (n < nnz) {
+        const int64_t row = getrand(&state, O);   /* row first, then column */
+        const int64_t col = getrand(&state, I);
+        trials += 1;
+        if (seen[row * I + col]) continue;         /* drawn before: reject */
+        seen[row * I + col] = 1;
+        r[n] = (int32_t)row; c[n] = (int32_t)col; ++n;
+    }
+    if (trials_out) *trials_out = trials;
+    int st = oracle_build(O, I, nnz, r, c, NULL, rows_out, cols_out, NULL,
+                          NULL, row_offsets_out, NULL, NULL, NULL, NULL);
+    free(seen); free(r); free(c);
+    return st;
+}
+
 int oracle_topology(int64_t O, int64_t I, int64_t nnz,
                     const int32_t *rows, const int32_t *cols, const float *vals,
                     int64_t n_prune, uint64_t seed,

@@ -345,9 +345,64 @@ def pin_topology_uniformity():
         assert chi2 < dof + 6.0 * math.sqrt(2 * dof), (chi2, dof)
 
 
+# ---------------------------------------------------------------- uniform initializer
+def _init_bruteforce(O, I, nnz, seed):
+    """Algorithm 2 written out in Python over the pinned SplitMix64 outputs: each trial takes the
+    row from one output and the column from the next (floor(u*n/2^64)), keeps new pairs only."""
+    u = iter(int(x) for x in oracle.splitmix64(seed, 200000))
+    drawn, trials = set(), 0
+    while len(drawn) < nnz:
+        r = (next(u) * O) >> 64
+        c = (next(u) * I) >> 64
+        trials += 1
+        drawn.add((r, c))
+    pos = sorted(drawn)
+    return (np.array([p[0] for p in pos], np.int32), np.array([p[1] for p in pos], np.int32), trials)
+
+
+def pin_init_uniform_bruteforce():
+    for O, I, nnz, seed in ((7, 5, 35, 3), (7, 5, 12, 4), (1, 40, 25, 5), (30, 1, 30, 6), (23, 31, 300, 7)):
+        out = oracle.init_uniform(O, I, nnz, seed)
+        rows, cols, trials = _init_bruteforce(O, I, nnz, seed)
+        assert np.array_equal(out["rows"], rows) and np.array_equal(out["cols"], cols), (O, I, nnz)
+        assert out["trials"] == trials, (out["trials"], trials)
+        assert np.array_equal(out["row_offsets"], np.searchsorted(rows, np.arange(O + 1)))
+
+
+def pin_init_uniform_trials_expectation():
+    """Appendix F: step i of Algorithm 2 succeeds with probability (mk - i)/mk, so the trial count
+    is a sum of geometric variables with mean sum mk/(mk - i) (about -mk ln(eta) at sparsity eta)."""
+    O, I, nnz = 40, 30, 900
+    N = O * I
+    succ = (N - np.arange(nnz)) / N
+    mean = float(np.sum(1.0 / succ))
+    var = float(np.sum((1.0 - succ) / succ ** 2))
+    n_runs = 40
+    avg = sum(oracle.init_uniform(O, I, nnz, 300 + t)["trials"] for t in range(n_runs)) / n_runs
+    assert abs(avg - mean) <= 5.0 * math.sqrt(var / n_runs), (avg, mean)
+    eta = 1.0 - nnz / N
+    assert abs(mean / nnz - (-math.log(eta) / (1.0 - eta))) < 0.02 * mean / nnz  # the pages' closed form
+
+
+def pin_init_uniform_uniformity():
+    """Positions are uniform over the matrix: chi-square on row and column counts."""
+    O, I, nnz = 50, 70, 700
+    rows_c, cols_c = np.zeros(O), np.zeros(I)
+    for t in range(40):
+        out = oracle.init_uniform(O, I, nnz, 700 + t)
+        rows_c += np.bincount(out["rows"], minlength=O)
+        cols_c += np.bincount(out["cols"], minlength=I)
+    for counts in (rows_c, cols_c):
+        exp = counts.sum() / counts.size
+        chi2 = float(np.sum((counts - exp) ** 2 / exp))
+        dof = counts.size - 1
+        assert chi2 < dof + 6.0 * math.sqrt(2 * dof), (chi2, dof)
+
+
 ALL_PINS = [
     pin_table7, pin_bruteforce, pin_scipy, pin_finite_differences, pin_adjoint,
     pin_special_cases, pin_thread_count_invariance, pin_builder_numpy, pin_builder_errors,
     pin_splitmix64, pin_topology_invariants, pin_topology_trials_expectation,
-    pin_topology_uniformity,
+    pin_topology_uniformity, pin_init_uniform_bruteforce, pin_init_uniform_trials_expectation,
+    pin_init_uniform_uniformity,
 ]

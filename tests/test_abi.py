@@ -16,7 +16,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(snk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert snk.abi_version() == 2
+    assert snk.abi_version() == 3
 
 
 def test_binding_loads_only_the_in_tree_library():
@@ -93,3 +93,4 @@ def test_banded_backward_workspace_follows_threshold(monkeypatch):
     assert banded - plain >= 8 * 200 * 64 * 4
     monkeypatch.setenv("SNACK_COO_BAND_MIN_NNZ", "not a number")  # ignored
     assert lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0) == default
+

@@ -347,6 +347,31 @@ def _check_bwd(L, B, seed, bf16=False):
     assert torch.equal(dX, dX2) and torch.equal(dW, dW2)
 
 
+def test_batch1_input_gradient_misaligned_arrays():
+    """cols and vals 4 bytes off a 16-byte boundary: the batch-1 input gradient cannot take its
+    16-byte loads and runs another kernel; the result must still match the oracle."""
+    seed, shape, O, I, density = BATCH1_LARGE[1]
+    say(f"batch-1 input gradient, misaligned cols/vals, {shape} {O}x{I}")
+    L = synth.random_small_layer(seed, O, I, int(density * O * I), shape)
+    built, W = device_layer(L, DEV)
+    nnz = L["nnz"]
+    cols = torch.empty(nnz + 1, dtype=torch.int32, device=DEV)[1:]
+    vals = torch.empty(nnz + 1, dtype=torch.float32, device=DEV)[1:]
+    cols.copy_(W.cols)
+    vals.copy_(W.vals)
+    assert cols.data_ptr() % 16 and vals.data_ptr() % 16
+    Wm = snk.SnackCOO(O, I, W.rows, cols, vals, W.row_offsets, W.col_perm, W.col_rows, W.col_cols, W.col_offsets)
+    assert snk._lib.snack_coo_workspace_bytes(snk.OP_BWD_INPUT, Wm.desc, 1, 0) > 0
+    dy_in, dy64 = acts(1700, 1, O)
+    dY = to_device(dy_in, DEV)
+    dX = snk.snack_coo_bwd_input(Wm, dY)
+    dXa = snk.snack_coo_bwd_input(W, dY)
+    torch.cuda.synchronize()
+    ref = oracle.bwd_input(O, I, built["rows"], built["cols"], built["vals"], dy64, nthreads=NTHREADS)
+    check_close(from_device(dX), ref, nnz / I, "dX misaligned")
+    check_close(from_device(dXa), ref, nnz / I, "dX aligned")
+
+
 # snack_coo_bwd over batches that pick each variant of the one-pass backward (B = 4*BT*Q:
 # 16 -> BT 4, 32 -> BT 8, 64/128/256 -> BT 16 with Q 1/2/4) and batches that fall back to the
 # two separate calls (48, 192, 512); fp32 and bf16; the one-pass kernel with and without row bands.

@@ -39,6 +39,12 @@ MUTANTS = [
     ("regrow_trials_miscount", "++trials;\n        if (live[i * I + j]) continue;", "if (live[i * I + j]) continue;\n        ++trials;"),
     ("regrow_swapped_ranges", "int64_t i = getrand(&state, O);\n        int64_t j = getrand(&state, I);",
      "int64_t i = getrand(&state, I) % O;\n        int64_t j = getrand(&state, O) % I;"),
+    ("init_column_first", "const int64_t row = getrand(&state, O);   /* row first, then column */\n        const int64_t col = getrand(&state, I);",
+     "const int64_t col = getrand(&state, I);\n        const int64_t row = getrand(&state, O);"),
+    ("init_no_rejection", "if (seen[row * I + col]) continue;         /* drawn before: reject */", ""),
+    ("init_trials_counts_accepted_only", "trials += 1;\n        if (seen[row * I + col]) continue;",
+     "if (seen[row * I + col]) continue;\n        trials += 1;"),
+    ("init_no_set_insert", "seen[row * I + col] = 1;\n        r[n]", "r[n]"),
 ]
 
 RUNNER = r"""

@@ -63,3 +63,27 @@ def test_topology_errors():
     assert e.value.status == "SHAPE"
     out = snk.snack_coo_topology_update(4, 4, [0, 1], [1, 1], [1.0, 2.0], 0, 0)
     assert out["rows"].tolist() == [0, 1] and out["trials"] == 0
+
+
+# ---------------------------------------------------------------- uniform initializer (Algorithm 2)
+@pytest.mark.parametrize("O,I,nnz", [(60, 45, 900), (32, 32, 1024), (1, 500, 77), (500, 1, 500), (512, 512, 26214),
+                                     (768, 2304, 17695), (333, 777, 0)])
+def test_init_uniform_matches_oracle(O, I, nnz):
+    for s in (0, 11, 2**64 - 1):
+        a = snk.snack_coo_init_uniform(O, I, nnz, s)
+        b = oracle.init_uniform(O, I, nnz, s)
+        for k in ("rows", "cols", "row_offsets"):
+            assert np.array_equal(a[k], b[k]), k
+        assert a["trials"] == b["trials"]
+
+
+def test_init_uniform_errors():
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_coo_init_uniform(4, 4, 17, 0)  # more positions than cells
+    assert e.value.status == "SHAPE"
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_coo_init_uniform(0, 4, 0, 0)
+    assert e.value.status == "SHAPE"
+    with pytest.raises(snk.SnackError) as e:
+        snk.snack_coo_init_uniform(1 << 18, 1 << 17, 10, 0)  # beyond the 2^34-cell bitmap
+    assert e.value.status == "SHAPE"
