@@ -286,6 +286,29 @@ def batch1_sweep(dev, K):
     return out
 
 
+def module_step_us(layer, K):
+    """The same layer step through the PyTorch drop-in (SnackLinear: autograd forward and
+    backward, plus the bias gradient the raw step does not take), eager, us per step."""
+    import torch
+    from coo_spmm_row_amd.layer import SnackLinear
+    m = SnackLinear.from_triple(layer.O, layer.I, layer.built["rows"], layer.built["cols"], layer.built["vals"],
+                                layer.L["bias"], device=layer.X.device)
+    X = layer.X.detach().clone().requires_grad_(True)
+    G = layer.dY
+    for _ in range(3):
+        m(X).backward(G)
+    start, stop = make_events(2)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(K):
+        m.zero_grad(set_to_none=True)
+        X.grad = None
+        m(X).backward(G)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / K * 1000.0
+
+
 def calibrate_copy(dev, nbytes, reps):
     """A plain elementwise kernel of known size (reads nbytes, writes nbytes), for
     scaling the HBM byte counters."""
@@ -364,6 +387,8 @@ def main():
         extras["kernel_us_cold"] = {op: round(v, 2) for op, v in cold.items()}
         extras["kernel_frac_hbm_cold"] = {op: round(nbytes[op] / (cold[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                           for op in cand}
+        log("the step through the PyTorch drop-in layer")
+        extras["module_us_per_step_eager"] = round(module_step_us(layer, args.steps), 2)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

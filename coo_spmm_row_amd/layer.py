@@ -1,0 +1,178 @@
+"""PyTorch drop-in for ``nn.Linear`` over the SNACK C ABI.
+
+SNACK ("Beyond Masked Sparsity: SNACK Enables Truly Sparse Neural Networks on GPU"),
+Section 3.5 and Appendix F: the layer keeps its weight as the COO triple on the device
+for its whole life, wires forward and backward through a custom autograd function (the
+SpMM for the output and the input gradient, the sparse outer product for the weight
+gradient), and draws its initial support with the uniform initializer of Algorithm 2.
+Every product runs in the library's kernels; this module only marshals tensors.
+
+Readings where the pages leave a step open:
+  * stored values start as N(0, 1 / (density * in_features)) (the variance-preserving
+    scale for a fan-in of density * in_features), the bias as nn.Linear's
+    U(-1/sqrt(in_features), 1/sqrt(in_features));
+  * prune-and-regrow (Appendix G) keeps the number of stored entries; regrown entries
+    start at 0, and optimizer state kept per entry no longer lines up with the new
+    support (the caller resets it).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+from torch import nn
+
+from . import (SnackCOO, snack_coo_build, snack_coo_bwd, snack_coo_bwd_input, snack_coo_fwd,
+               snack_coo_grad_weight, snack_coo_init_uniform, snack_coo_topology_update)
+
+_STRUCT = ("rows", "cols", "row_offsets", "col_perm", "col_rows", "col_cols", "col_offsets")
+
+
+class SnackLinearFunction(torch.autograd.Function):
+    """Y = X W^T + b with W a SnackCOO whose ``vals`` is the ``vals`` argument.
+
+    Backward: dX = dY W (SpMM over the column view), dW[k] = sum_b dY[b, rows[k]] X[b, cols[k]]
+    on the support only, db = sum_b dY[b]; both products from one fused call when both are needed.
+    """
+
+    @staticmethod
+    def forward(ctx, X: torch.Tensor, vals: torch.Tensor, bias: Optional[torch.Tensor], weight: SnackCOO):
+        Y = snack_coo_fwd(weight, X, bias)
+        ctx.save_for_backward(X)
+        ctx.weight = weight
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY: torch.Tensor):
+        (X,) = ctx.saved_tensors
+        W = ctx.weight
+        need_x, need_v, need_b = ctx.needs_input_grad[:3]
+        dY = dY.to(X.dtype).contiguous()
+        db = torch.empty(W.out_features, dtype=torch.float32, device=dY.device) if need_b else None
+        dX = dW = None
+        if need_v and (need_x or need_b):
+            dX, dW = snack_coo_bwd(W, X, dY, db=db)
+        elif need_v:
+            dW = snack_coo_grad_weight(W, X, dY)
+        elif need_x or need_b:
+            dX = snack_coo_bwd_input(W, dY, db=db)
+        return (dX if need_x else None), dW, db, None
+
+
+class SnackLinear(nn.Module):
+    """Truly sparse linear layer: ``out_features x in_features`` weight held as a sorted COO
+    triple with its column view (never dense), ``vals`` the trainable stored values.
+
+    Give either ``sparsity`` (fraction of zero weights) or ``nnz``.  Inputs are ``[..., in_features]``
+    in float32 or bfloat16 on the layer's GPU (bfloat16 in, bfloat16 out, fp32 accumulation);
+    there is no CPU path.
+    """
+
+    def __init__(self, in_features: int, out_features: int, sparsity: float = 0.9, bias: bool = True,
+                 seed: int = 0, nnz: Optional[int] = None, device=None):
+        super().__init__()
+        self.in_features, self.out_features = int(in_features), int(out_features)
+        cells = self.in_features * self.out_features
+        if nnz is None:
+            if not 0.0 <= sparsity < 1.0:
+                raise ValueError("sparsity must be in [0, 1)")
+            nnz = int(round((1.0 - sparsity) * cells))
+        if not 0 <= nnz <= cells:
+            raise ValueError(f"nnz={nnz} outside [0, {cells}]")
+        topo = snack_coo_init_uniform(self.out_features, self.in_features, int(nnz), int(seed))
+        density = max(nnz, 1) / cells
+        g = np.random.Generator(np.random.PCG64(int(seed) + 1))
+        vals = (g.standard_normal(nnz) / math.sqrt(density * self.in_features)).astype(np.float32)
+        self._set_topology(topo["rows"], topo["cols"], vals, device)
+        if bias:
+            bound = 1.0 / math.sqrt(self.in_features)
+            b = g.uniform(-bound, bound, self.out_features).astype(np.float32)
+            self.bias = nn.Parameter(torch.from_numpy(b).to(device))
+        else:
+            self.register_parameter("bias", None)
+
+    @classmethod
+    def from_triple(cls, out_features: int, in_features: int, rows, cols, vals, bias=None,
+                    device=None) -> "SnackLinear":
+        """A layer over a given support and values (host arrays in any order; the builder sorts
+        them and rejects duplicates), with the given bias or none."""
+        layer = cls.__new__(cls)
+        nn.Module.__init__(layer)
+        layer.in_features, layer.out_features = int(in_features), int(out_features)
+        layer._set_topology(rows, cols, vals, device)
+        if bias is not None:
+            layer.bias = nn.Parameter(torch.from_numpy(np.array(bias, np.float32)).to(device))
+        else:
+            layer.register_parameter("bias", None)
+        return layer
+
+    # ---------------------------------------------------------------- structure
+    def _set_topology(self, rows, cols, vals, device=None):
+        built = snack_coo_build(self.out_features, self.in_features, rows, cols, vals, column_view=True)
+        if device is None:
+            device = self.vals.device if hasattr(self, "vals") else torch.device("cpu")
+        for name in _STRUCT:
+            t = torch.from_numpy(np.ascontiguousarray(built[name])).to(device)
+            if name in self._buffers:
+                self._buffers[name] = t
+            else:
+                self.register_buffer(name, t)
+        v = torch.from_numpy(np.ascontiguousarray(built["vals"])).to(device)
+        if "vals" in self._parameters:
+            self.vals.data = v
+        else:
+            self.vals = nn.Parameter(v)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.rows.numel())
+
+    def weight_view(self) -> SnackCOO:
+        """The library descriptor over the current tensors (cheap; built per call)."""
+        return SnackCOO(self.out_features, self.in_features, self.rows, self.cols, self.vals.detach(),
+                        self.row_offsets, self.col_perm, self.col_rows, self.col_cols, self.col_offsets)
+
+    # ---------------------------------------------------------------- compute
+    def forward(self, X: torch.Tensor) -> torch.Tensor:
+        if X.shape[-1] != self.in_features:
+            raise ValueError(f"input has {X.shape[-1]} features, expected {self.in_features}")
+        lead = X.shape[:-1]
+        X2 = X.reshape(-1, self.in_features).contiguous()
+        Y = SnackLinearFunction.apply(X2, self.vals, self.bias, self.weight_view())
+        return Y.reshape(*lead, self.out_features)
+
+    # ---------------------------------------------------------------- topology update (Appendix G)
+    @torch.no_grad()
+    def prune_and_regrow(self, fraction: float = 0.1, seed: int = 0) -> int:
+        """Prune the floor(fraction * nnz) smallest |vals| and regrow as many empty positions with
+        Algorithm 2 (host, the library's topology update); returns the number of trials."""
+        n_prune = int(math.floor(fraction * self.nnz))
+        out = snack_coo_topology_update(self.out_features, self.in_features, self.rows.cpu().numpy(),
+                                        self.cols.cpu().numpy(), self.vals.detach().cpu().numpy(), n_prune,
+                                        int(seed))
+        self._set_topology(out["rows"], out["cols"], out["vals"], self.vals.device)
+        return out["trials"]
+
+    # ---------------------------------------------------------------- persistence
+    def save_npz(self, path) -> None:
+        """The COO triple (and bias) as an .npz file (plain arrays, no pickles)."""
+        arrays = {"shape": np.array([self.out_features, self.in_features], np.int64),
+                  "rows": self.rows.cpu().numpy(), "cols": self.cols.cpu().numpy(),
+                  "vals": self.vals.detach().cpu().numpy()}
+        if self.bias is not None:
+            arrays["bias"] = self.bias.detach().cpu().numpy()
+        np.savez(path, **arrays)
+
+    @classmethod
+    def load_npz(cls, path, device=None) -> "SnackLinear":
+        with np.load(path, allow_pickle=False) as f:
+            O, I = (int(x) for x in f["shape"])
+            return cls.from_triple(O, I, f["rows"], f["cols"], f["vals"],
+                                   f["bias"] if "bias" in f.files else None, device)
+
+    def extra_repr(self) -> str:
+        cells = self.in_features * self.out_features
+        return (f"in_features={self.in_features}, out_features={self.out_features}, nnz={self.nnz} "
+                f"(sparsity {1.0 - self.nnz / max(cells, 1):.4f}), bias={self.bias is not None}")

@@ -1,0 +1,71 @@
+"""SnackLinear host side (CPU): Algorithm 2 support, build, persistence, no CPU compute path."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+torch = pytest.importorskip("torch")
+from coo_spmm_row_amd.layer import SnackLinear  # noqa: E402
+
+
+def test_support_is_algorithm_2_and_column_view_is_the_builders():
+    layer = SnackLinear(300, 200, sparsity=0.9, seed=5)
+    assert layer.nnz == 6000
+    ref = oracle.init_uniform(200, 300, 6000, 5)
+    assert np.array_equal(layer.rows.numpy(), ref["rows"]) and np.array_equal(layer.cols.numpy(), ref["cols"])
+    assert np.array_equal(layer.row_offsets.numpy(), ref["row_offsets"])
+    cv = oracle.build_coo(200, 300, ref["rows"], ref["cols"])
+    for k in ("col_perm", "col_rows", "col_cols", "col_offsets"):
+        assert np.array_equal(getattr(layer, k).numpy(), cv[k]), k
+    # stored values ~ N(0, 1/(density*I)): the sample variance is within a few standard errors
+    v = layer.vals.detach().numpy().astype(np.float64)
+    target = 1.0 / (0.1 * 300)
+    assert abs(v.var() / target - 1.0) < 6.0 * math.sqrt(2.0 / v.size)
+    b = layer.bias.detach().numpy()
+    assert np.all(np.abs(b) <= 1.0 / math.sqrt(300))
+
+
+def test_same_seed_same_layer_other_seed_other_support():
+    a, b, c = SnackLinear(64, 48, 0.8, seed=1), SnackLinear(64, 48, 0.8, seed=1), SnackLinear(64, 48, 0.8, seed=2)
+    assert torch.equal(a.rows, b.rows) and torch.equal(a.cols, b.cols) and torch.equal(a.vals, b.vals)
+    assert not (torch.equal(a.rows, c.rows) and torch.equal(a.cols, c.cols))
+
+
+def test_nnz_argument_and_bounds():
+    assert SnackLinear(10, 10, nnz=37).nnz == 37
+    assert SnackLinear(10, 10, nnz=0).nnz == 0
+    with pytest.raises(ValueError):
+        SnackLinear(10, 10, nnz=101)
+    with pytest.raises(ValueError):
+        SnackLinear(10, 10, sparsity=1.0)
+
+
+def test_save_load_roundtrip(tmp_path):
+    layer = SnackLinear(40, 30, 0.7, seed=9)
+    p = tmp_path / "w.npz"
+    layer.save_npz(p)
+    back = SnackLinear.load_npz(p)
+    for k in ("rows", "cols", "row_offsets", "col_perm", "col_rows", "col_cols", "col_offsets"):
+        assert torch.equal(getattr(layer, k), getattr(back, k)), k
+    assert torch.equal(layer.vals, back.vals) and torch.equal(layer.bias, back.bias)
+    nb = SnackLinear(40, 30, 0.7, seed=9, bias=False)
+    nb.save_npz(tmp_path / "nb.npz")
+    assert SnackLinear.load_npz(tmp_path / "nb.npz").bias is None
+
+
+def test_prune_and_regrow_on_host_matches_the_oracle():
+    layer = SnackLinear(50, 40, 0.8, seed=3)
+    r, c, v = layer.rows.numpy().copy(), layer.cols.numpy().copy(), layer.vals.detach().numpy().copy()
+    trials = layer.prune_and_regrow(0.1, seed=77)
+    ref = oracle.topology(40, 50, r, c, v, int(0.1 * r.size), 77)
+    assert trials == ref["trials"]
+    assert np.array_equal(layer.rows.numpy(), ref["rows"]) and np.array_equal(layer.cols.numpy(), ref["cols"])
+    assert np.array_equal(layer.vals.detach().numpy().view(np.uint32), ref["vals"].view(np.uint32))
+
+
+def test_no_cpu_compute_path():
+    layer = SnackLinear(20, 10, 0.5)
+    with pytest.raises(ValueError, match="device tensor"):
+        layer(torch.randn(3, 20))
