@@ -121,7 +121,7 @@ def test_layer_sgd_reduces_loss_and_save_load_is_exact(tmp_path):
         loss = ((layer(X) - target) ** 2).sum(dim=1).mean()
         loss.backward()
         opt.step()
-        losses.append(float(loss))
+        losses.append(float(loss.detach()))
     assert losses[-1] < 0.2 * losses[0], losses
     layer.save_npz(tmp_path / "l.npz")
     back = SnackLinear.load_npz(tmp_path / "l.npz", device=DEV)
