@@ -309,6 +309,30 @@ def module_step_us(layer, K):
     return start.elapsed_time(stop) / K * 1000.0
 
 
+def topology_times(layer, frac=0.1, reps=3):
+    """Prune-and-regrow of the layer (floor(frac * nnz) entries) with its column view: on the
+    device (snack_coo_topology_update_device, which synchronizes; wall clock) and on the host
+    (snack_coo_topology_update + snack_coo_build, host arrays; copies not included). ms, best of reps."""
+    import torch
+    import coo_spmm_row_amd as snk
+    p = int(frac * layer.nnz)
+    r, c, v = layer.built["rows"], layer.built["cols"], layer.built["vals"]
+    snk.snack_coo_topology_update_device(layer.W, p, 7)  # warm-up (first launch of the sort kernels)
+    dev_ms, host_ms = [], []
+    for i in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        Wn, trials = snk.snack_coo_topology_update_device(layer.W, p, 100 + i)
+        torch.cuda.synchronize()
+        dev_ms.append((time.perf_counter() - t0) * 1e3)
+        del Wn
+        t0 = time.perf_counter()
+        out = snk.snack_coo_topology_update(layer.O, layer.I, r, c, v, p, 100 + i)
+        snk.snack_coo_build(layer.O, layer.I, out["rows"], out["cols"], out["vals"])
+        host_ms.append((time.perf_counter() - t0) * 1e3)
+    return {"n_prune": p, "device_ms": round(min(dev_ms), 2), "host_ms": round(min(host_ms), 1)}
+
+
 def calibrate_copy(dev, nbytes, reps):
     """A plain elementwise kernel of known size (reads nbytes, writes nbytes), for
     scaling the HBM byte counters."""
@@ -389,6 +413,8 @@ def main():
                                           for op in cand}
         log("the step through the PyTorch drop-in layer")
         extras["module_us_per_step_eager"] = round(module_step_us(layer, args.steps), 2)
+        log("topology update (prune 10 %, regrow, column view): device and host")
+        extras["topology_update"] = topology_times(layer)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

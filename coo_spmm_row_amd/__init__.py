@@ -82,11 +82,16 @@ _lib.snack_coo_grad_weight.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, c
 _lib.snack_coo_bwd.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.snack_coo_topology_update.argtypes = [_i64, _i64, _i64, _p, _p, _p, _i64, _u64, _p, _p, _p, _p, _p]
 _lib.snack_coo_init_uniform.argtypes = [_i64, _i64, _i64, _u64, _p, _p, _p, _p]
+_lib.snack_coo_topology_update_device.argtypes = [_D, _i64, _u64, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                                  _p, ctypes.c_size_t, _p]
+_lib.snack_coo_topology_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+_lib.snack_coo_topology_workspace_bytes.restype = ctypes.c_size_t
 _lib.snack_coo_set_probe.argtypes = [_p, _p]
 
 EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_bwd_input",
             "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_coo_init_uniform",
-            "snack_last_error", "snack_coo_abi_version", "snack_coo_set_probe")
+            "snack_coo_topology_update_device", "snack_coo_topology_workspace_bytes", "snack_last_error",
+            "snack_coo_abi_version", "snack_coo_set_probe")
 
 
 def _np_ptr(a: Optional[np.ndarray]):
@@ -319,6 +324,31 @@ def snack_coo_bwd(W: SnackCOO, X, dY, dx_out=None, dw_out=None, db=None, workspa
                             ctypes.c_void_p(dW.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
     _check(st, "snack_coo_bwd")
     return dX, dW
+
+
+def snack_coo_topology_update_device(W: SnackCOO, n_prune: int, seed: int, workspace=None, stream=None):
+    """Prune-and-regrow on the GPU (Appendix G, regrowth by Algorithm 2): returns (the new
+    SnackCOO with its column view, the number of draws); equal to the host update + builder."""
+    import torch
+    dev = W.device
+    O, I, n = W.out_features, W.in_features, W.nnz
+    i32 = dict(dtype=torch.int32, device=dev)
+    rows, cols = torch.empty(n, **i32), torch.empty(n, **i32)
+    vals = torch.empty(n, dtype=torch.float32, device=dev)
+    row_offsets, col_offsets = torch.empty(O + 1, **i32), torch.empty(I + 1, **i32)
+    col_perm, col_rows, col_cols = torch.empty(n, **i32), torch.empty(n, **i32), torch.empty(n, **i32)
+    need = int(_lib.snack_coo_topology_workspace_bytes(O, I, n, int(n_prune)))
+    if need == 0:  # invalid sizes (the message says which)
+        _check(2, "snack_coo_topology_workspace_bytes")
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=dev)
+    trials = ctypes.c_int64(0)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = _lib.snack_coo_topology_update_device(W.desc, int(n_prune), ctypes.c_uint64(seed), p(rows), p(cols),
+                                               p(vals), p(row_offsets), p(col_perm), p(col_rows), p(col_cols),
+                                               p(col_offsets), ctypes.byref(trials), p(ws),
+                                               ws.numel() * ws.element_size(), _stream_handle(dev, stream))
+    _check(st, "snack_coo_topology_update_device")
+    return SnackCOO(O, I, rows, cols, vals, row_offsets, col_perm, col_rows, col_cols, col_offsets), int(trials.value)
 
 
 def snack_coo_set_probe(start_event=None, stop_event=None):

@@ -21,11 +21,13 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     host_o = os.path.join(BUILD, "host.o")
     dev_o = os.path.join(BUILD, "snack_coo.o")
+    topo_o = os.path.join(BUILD, "topology.o")
     cmds = [
         ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-c",
          os.path.join(CSRC, "host.cpp"), "-o", host_o],
         ["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "snack_coo.hip"), "-o", dev_o],
-        ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", dev_o, host_o, "-o", LIB + ".tmp"],
+        ["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "topology.hip"), "-o", topo_o],
+        ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", dev_o, topo_o, host_o, "-o", LIB + ".tmp"],
     ]
     for cmd in cmds:
         if verbose:

@@ -25,7 +25,8 @@ import torch
 from torch import nn
 
 from . import (SnackCOO, snack_coo_build, snack_coo_bwd, snack_coo_bwd_input, snack_coo_fwd,
-               snack_coo_grad_weight, snack_coo_init_uniform, snack_coo_topology_update)
+               snack_coo_grad_weight, snack_coo_init_uniform, snack_coo_topology_update,
+               snack_coo_topology_update_device)
 
 _STRUCT = ("rows", "cols", "row_offsets", "col_perm", "col_rows", "col_cols", "col_offsets")
 
@@ -145,10 +146,20 @@ class SnackLinear(nn.Module):
 
     # ---------------------------------------------------------------- topology update (Appendix G)
     @torch.no_grad()
-    def prune_and_regrow(self, fraction: float = 0.1, seed: int = 0) -> int:
+    def prune_and_regrow(self, fraction: float = 0.1, seed: int = 0, on_device: Optional[bool] = None) -> int:
         """Prune the floor(fraction * nnz) smallest |vals| and regrow as many empty positions with
-        Algorithm 2 (host, the library's topology update); returns the number of trials."""
+        Algorithm 2; returns the number of trials.  On a GPU layer the update runs on the device
+        (snack_coo_topology_update_device) unless on_device=False, which takes the host path; both
+        give the same support, values and trial count."""
         n_prune = int(math.floor(fraction * self.nnz))
+        if on_device is None:
+            on_device = self.vals.is_cuda
+        if on_device:
+            W, trials = snack_coo_topology_update_device(self.weight_view(), n_prune, int(seed))
+            for name in _STRUCT:
+                self._buffers[name] = getattr(W, name)
+            self.vals.data = W.vals
+            return trials
         out = snack_coo_topology_update(self.out_features, self.in_features, self.rows.cpu().numpy(),
                                         self.cols.cpu().numpy(), self.vals.detach().cpu().numpy(), n_prune,
                                         int(seed))

@@ -178,6 +178,32 @@ int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_
                   void *dX, float *db, float *dW,
                   void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Device-side topology update (Appendix G prune-and-regrow, regrowth by
+ * Algorithm 2): the same result as snack_coo_topology_update on the same
+ * triple, n_prune and seed followed by snack_coo_build's column view, bit for
+ * bit, computed on the GPU.  Input W: a device triple sorted strictly by
+ * (row, col) with its values (as the builder emits; not re-checked), row
+ * offsets and column view not needed.  Outputs (device, caller-owned, must not
+ * alias W's arrays): rows_out, cols_out, vals_out [nnz], row_offsets_out
+ * [O+1], col_perm_out, col_rows_out, col_cols_out [nnz], col_offsets_out
+ * [I+1]; trials_out (HOST int64, or NULL) receives Algorithm 2's number of
+ * draws.  The regrowth generates its draws in batches and reads back one count
+ * per batch, so this call synchronizes hip_stream (it cannot be captured in a
+ * graph).  workspace >= snack_coo_topology_workspace_bytes(O, I, nnz, n_prune),
+ * 256-byte aligned.  O*I is limited to 2^34 positions. */
+int snack_coo_topology_update_device(const snack_coo_desc *W, int64_t n_prune, uint64_t seed,
+                                     int32_t *rows_out, int32_t *cols_out, float *vals_out,
+                                     int32_t *row_offsets_out, int32_t *col_perm_out, int32_t *col_rows_out,
+                                     int32_t *col_cols_out, int32_t *col_offsets_out, int64_t *trials_out,
+                                     void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Bytes of device workspace snack_coo_topology_update_device needs (0 with
+ * snack_last_error() set for invalid sizes).  The environment variable
+ * SNACK_COO_TOPOLOGY_DRAW_BATCH (a positive count) fixes the number of draws per
+ * batch, which is otherwise sized from the expected number of draws. */
+size_t snack_coo_topology_workspace_bytes(int64_t out_features, int64_t in_features, int64_t nnz,
+                                          int64_t n_prune);
+
 /* Host-side uniform initializer (Algorithm 2; its expected cost of about
  * -ln(eta)/(1-eta) trials per entry at sparsity eta is in Appendix F): nnz
  * distinct positions of the O x I matrix drawn by rejection.  Each trial draws
@@ -225,7 +251,7 @@ int snack_coo_set_probe(void *start_event, void *stop_event);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *snack_last_error(void);
 
-/* ABI version of this header: 3 (3 added snack_coo_init_uniform). */
+/* ABI version of this header: 4 (3 added snack_coo_init_uniform, 4 the device topology update). */
 int snack_coo_abi_version(void);
 
 #ifdef __cplusplus

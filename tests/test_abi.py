@@ -16,7 +16,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(snk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert snk.abi_version() == 3
+    assert snk.abi_version() == 4
 
 
 def test_binding_loads_only_the_in_tree_library():

@@ -96,9 +96,14 @@ def test_layer_prune_and_regrow_then_train():
     say("SnackLinear prune-and-regrow, then forward/backward on the new support")
     layer = SnackLinear(400, 300, sparsity=0.95, seed=13).to(DEV)
     r, c, v, _ = _host(layer)
-    layer.prune_and_regrow(0.1, seed=99)
+    trials = layer.prune_and_regrow(0.1, seed=99)  # on the device
     ref = oracle.topology(300, 400, r, c, v, int(0.1 * r.size), 99)
+    assert trials == ref["trials"]
     assert np.array_equal(layer.rows.cpu().numpy(), ref["rows"])
+    assert np.array_equal(layer.vals.detach().cpu().numpy().view(np.uint32), ref["vals"].view(np.uint32))
+    cv = oracle.build_coo(300, 400, ref["rows"], ref["cols"])
+    for k in ("col_perm", "col_rows", "col_cols", "col_offsets"):
+        assert np.array_equal(getattr(layer, k).cpu().numpy(), cv[k]), k
     assert layer.vals.device == DEV and layer.col_perm.device == DEV
     X, Y, out = _run(layer, (32,), 700)
     check_close(from_device(Y.detach()), out["Y"], layer.nnz / 300, "regrown Y")
