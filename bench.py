@@ -40,6 +40,8 @@ WORKLOADS = {
     "xs99_zipf_b1": ("xs99_zipf", 1, "f32"),
     "gpt2_fc_b1024": ("gpt2_fc", 1024, "f32"),
     "gpt2_fc_b1024_bf16": ("gpt2_fc", 1024, "bf16"),
+    "gamlp90_b1": ("gamlp90", 1, "f32"),
+    "gamlp90_b4096": ("gamlp90", 4096, "f32"),
 }
 
 
@@ -156,19 +158,26 @@ def timed_steps(layer, K, ops=STEP_OPS):
     return total, kern
 
 
-def graph_steps(layer, K, reps=3):
-    """The step captured once as a HIP graph and replayed K times (no host launch cost).
-    Returns microseconds per step (median over reps), or None if capture fails."""
+def graph_steps(layer, K, reps=3, ops=None):
+    """The step (or just `ops`) captured once as a HIP graph and replayed K times (no host launch
+    cost).  Returns microseconds per replay (median over reps), or None if capture fails."""
     import torch
+
+    def run():
+        if ops is None:
+            layer.step()
+        else:
+            for op in ops:
+                layer.op(op)
     try:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            layer.step()
+            run()
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            layer.step()
+            run()
         graph.replay()
         torch.cuda.synchronize()
     except RuntimeError as exc:  # capture unsupported: report eager only
@@ -333,6 +342,20 @@ def topology_times(layer, frac=0.1, reps=3):
     return {"n_prune": p, "device_ms": round(min(dev_ms), 2), "host_ms": round(min(host_ms), 1)}
 
 
+def gamlp_inference(dev, K):
+    """Batch-1 forward of the 5000 x 5000 GAMLP-shaped projection at 90 / 95 / 99 % sparsity
+    (graph-replayed, us per call)."""
+    out = {}
+    for name, label in (("gamlp90", "90%"), ("gamlp95", "95%"), ("gamlp99", "99%")):
+        layer = Layer(name, 1, "f32", dev)
+        for _ in range(3):
+            layer.op("fwd")
+        g = graph_steps(layer, K, ops=("fwd",))
+        out[label] = None if g is None else round(g, 2)
+        del layer
+    return out
+
+
 def calibrate_copy(dev, nbytes, reps):
     """A plain elementwise kernel of known size (reads nbytes, writes nbytes), for
     scaling the HBM byte counters."""
@@ -424,6 +447,8 @@ def main():
         del layer
         torch.cuda.empty_cache()
         extras["batch1_us_per_step"] = batch1_sweep(dev, max(10, args.steps // 2))
+        log("GAMLP-shaped batch-1 inference")
+        extras["gamlp_5000_b1_fwd_us"] = gamlp_inference(dev, max(20, args.steps))
     line = {
         "metric": "COO SpMM fwd+dX+dW us/call (one layer step)",
         "value": round(step_us, 2),

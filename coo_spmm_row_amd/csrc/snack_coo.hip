@@ -720,11 +720,14 @@ __global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restric
 // the row's entries 64 at a time with their X rows as 32-bit float4 offsets
 // (the next 64 prefetched; lanes past the row's end point at X's zero row),
 // gathers U entries per slot in flight and sums each slot's BT lanes by DPP.
+// ld: row stride (floats) of the feature-major copies; a batch wider than 4*BT*Q is taken in
+// slices of 4*BT*Q columns (xt and dyt offset by the slice), each adding into dW (acc != 0)
+// after the first.
 template <int BT, int WPR, int Q>
 __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32_t *__restrict__ offs,
                                                           const int32_t *__restrict__ cols,
                                                           const float *__restrict__ xt, int zero_row,
-                                                          const float *__restrict__ dyt, int64_t B,
+                                                          const float *__restrict__ dyt, int64_t ld, int acc,
                                                           float *__restrict__ dW) {
     constexpr int S = kWave / BT;
     constexpr int U = (S * 8 <= kWave) ? 8 : kWave / S;  // S*U divides 64
@@ -735,7 +738,7 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
     const int64_t r = xcd_block() * KPB + wave / WPR;
     const int wsub = wave % WPR;
     if (r >= O) return;  // uniform per wave; no barrier follows
-    const int B4 = static_cast<int>(B / 4);
+    const int B4 = static_cast<int>(ld / 4);
     const char *__restrict__ xb = reinterpret_cast<const char *>(xt) + 16u * static_cast<uint32_t>(t);
     const float4 *__restrict__ y4 = reinterpret_cast<const float4 *>(dyt) + r * B4 + t;
     float4 dyv[Q];
@@ -776,7 +779,7 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
                 }
                 d = group_sum<BT>(d);
                 const int src = h + u * S + e;
-                if (t == 0 && src < n) dW[base + src] = d;
+                if (t == 0 && src < n) dW[base + src] = acc ? dW[base + src] + d : d;
             }
         }
     }
@@ -1409,14 +1412,19 @@ enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2, kCsr1 = 3, kCsr1Priv = 
 constexpr int64_t kScatterLdsFloats = 16384;  // 64 KB private dX copy per workgroup
 
 // Device work plan of one gather-reduce (forward or input gradient).
+// layers from which the wide-batch gradient paths (column-order values for the input gradient,
+// 256-column slices for the weight gradient) pay off over the plain ones
+constexpr int64_t kLargeBatchMinNnz = int64_t(1) << 18;
+
 struct SpmmPlan {
     Mapping mapping;
+    bool cvals;          // rowwave over the column view: vals gathered into column order first
     int bt;              // batch lanes per entry group (segscan) or lanes per slot (rowwave)
     int64_t chunk;       // segscan, csr1: entries per wave; scatter: entries per workgroup
     int64_t nchunks;     // segscan, csr1: waves; scatter: workgroups (partial copies)
     int64_t nparts;      // csr1 private copies: workgroups (partial copies)
     bool direct;         // operand used in place (fp32, batch 1) instead of a transposed copy
-    size_t off_opnd, off_head, off_tail, total;
+    size_t off_opnd, off_head, off_tail, off_cvals, total;
 };
 
 inline int pow2_at_least(int64_t x) {
@@ -1502,6 +1510,13 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
     if (p.mapping == kSegscan) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B));
     p.off_tail = at;
     if (p.mapping == kSegscan) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B));
+    // the input gradient over the column view reads vals through the permutation once per batch
+    // tile; with 4 or more tiles on a large layer they are gathered into column order once, so
+    // every tile reads them coalesced and long keys split over 4 waves (one tile: the gather costs
+    // more than it saves)
+    p.cvals = scatter_ok && p.mapping == kRowwave && ceil_div(B, 4 * p.bt) >= 4 && nnz >= kLargeBatchMinNnz;
+    p.off_cvals = at;
+    if (p.cvals) at = align_up(at + sizeof(float) * static_cast<size_t>(nnz));
     p.total = at;
     return p;
 }
@@ -1510,6 +1525,7 @@ struct SddmmPlan {
     bool csr1;           // batch 1: csr1_dw_kernel, activations read in place
     bool wide;           // sddmm_wide_kernel (batch a multiple of 4, >= 16) or sddmm_kernel
     int rowq;            // > 0: rowsddmm_kernel with this many float4s per lane (1, 2 or 4)
+    int64_t slices;      // rowsddmm over this many 256-column batch slices (1: the whole batch)
     int bt, vw;
     int64_t steps, waves, per_wave;
     bool x_direct, dy_direct;
@@ -1537,9 +1553,17 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
         p.steps = std::min<int64_t>(std::max<int64_t>(ceil_div(std::max<int64_t>(nnz, 1), G * target_waves), 1), 64);
         p.waves = ceil_div(nnz, G * p.steps);
     }
+    p.slices = 1;
     if (p.wide && B % (4 * p.bt) == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
         const int64_t q = B / (4 * p.bt);
-        if (q == 1 || q == 2 || q == 4) p.rowq = static_cast<int>(q);
+        if (q == 1 || q == 2 || q == 4) {
+            p.rowq = static_cast<int>(q);
+        } else if (p.bt == 16 && B % 256 == 0 && nnz >= kLargeBatchMinNnz) {  // wide batch, large layer:
+            // slices of 256 columns (each gathers its part of the X rows once per entry; the
+            // per-entry kernel below re-reads the whole dY row per entry)
+            p.rowq = 4;
+            p.slices = B / 256;
+        }
     }
     p.x_direct = p.dy_direct = (B == 1 && dtype == SNACK_F32);
     if (B == 1 && nnz >= 128 * O) {  // rows averaging >= 128 entries
@@ -1698,6 +1722,14 @@ void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const in
                            perm, opnd, zero_row, B, bias, out, out_ld);
 }
 
+// out[j] = vals[perm[j]]: the stored values in column-view order
+__global__ __launch_bounds__(kBlock) void gather_vals_kernel(const int32_t *__restrict__ perm,
+                                                             const float *__restrict__ vals, int64_t n,
+                                                             float *__restrict__ out) {
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (j < n) out[j] = vals[perm[j]];
+}
+
 // The gather-reduce shared by the forward (row order) and the input gradient
 // (column view).  nkeys = number of outputs per batch row; offs [nkeys+1].
 template <typename OutT>
@@ -1707,6 +1739,13 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
     if (nkeys == 0 || B == 0) return SNACK_OK;
     if (p.mapping == kRowwave) {
         probe(true, st);
+        if (p.cvals && perm) {
+            float *cv = reinterpret_cast<float *>(ws + p.off_cvals);
+            hipLaunchKernelGGL(gather_vals_kernel, dim3(static_cast<unsigned>(ceil_div(nnz, kBlock))), dim3(kBlock), 0,
+                               st, perm, vals, nnz, cv);
+            vals = cv;
+            perm = nullptr;
+        }
         switch (p.bt) {
             case 4: launch_rowwave_bt<OutT, 4>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); break;
             case 8: launch_rowwave_bt<OutT, 8>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); break;
@@ -2006,9 +2045,11 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             const bool split = nnz >= 256 * O;
             const dim3 rgrid(static_cast<unsigned>(round_up8(ceil_div(O, split ? 1 : kWavesPerBlock))));
             const int zero_row = static_cast<int>(I);
-#define SNACK_ROWSD(BTV, WPRV, QV)                                                                             \
-    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, W->cols, xt, \
-                       zero_row, dyt, batch, dW)
+            // slice k: columns [256k, 256k + 256) of the copies (one launch per slice, in order)
+#define SNACK_ROWSD(BTV, WPRV, QV)                                                                           \
+    for (int64_t k = 0; k < p.slices; ++k)                                                                   \
+    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets,      \
+                       W->cols, xt + 256 * k, zero_row, dyt + 256 * k, batch, static_cast<int>(k > 0), dW)
 #define SNACK_ROWSD_Q(BTV, WPRV)                         \
     do {                                                 \
         if (p.rowq == 1) SNACK_ROWSD(BTV, WPRV, 1);      \

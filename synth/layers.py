@@ -64,6 +64,11 @@ LAYERS = {
     "gpt2_qkv":    Layer("gpt2_qkv", 2304, 768, 1, 100, (1024,), val_std=0.02, config_id=5, variant=0),
     "gpt2_fc":     Layer("gpt2_fc", 3072, 768, 1, 100, (1024,), val_std=0.02, config_id=5, variant=1),
     "gpt2_proj":   Layer("gpt2_proj", 768, 3072, 1, 100, (1024,), val_std=0.02, config_id=5, variant=2),
+    # the 5000 x 5000 feature-head projection of the GAMLP-shaped workload (Table 6 and its appendix):
+    # batch-1 inference at 90 / 95 / 99 % sparsity, training at batch 4096
+    "gamlp90":     Layer("gamlp90", 5000, 5000, 1, 10, (1, 4096), config_id=7, variant=0),
+    "gamlp95":     Layer("gamlp95", 5000, 5000, 1, 20, (1,), config_id=7, variant=1),
+    "gamlp99":     Layer("gamlp99", 5000, 5000, 1, 100, (1,), config_id=7, variant=2),
 }
 
 

@@ -148,6 +148,14 @@ def test_extreme_sparse_batch1(name):
         assert np.array_equal(Y.cpu().numpy()[0, empty], L["bias"][empty])
 
 
+@pytest.mark.parametrize("name", ["gamlp90", "gamlp95", "gamlp99"])
+def test_gamlp_shaped_batch1(name):
+    """The 5000 x 5000 GAMLP-shaped projection at batch 1 (all four products, full compare)."""
+    say(f"{name} batch 1")
+    spec, L = named_layer(name)
+    run_all(L, 1, 7000 + spec.variant)
+
+
 @pytest.mark.parametrize("name", ["gpt2_qkv", "gpt2_fc", "gpt2_proj"])
 @pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
 def test_gpt2_shapes(name, bf16):
