@@ -422,6 +422,18 @@ def test_backward_row_bands(case, B):
         _check_bwd(L, B, 900 + seed + B)
 
 
+# Wide batches on a layer of more than 2^18 entries: the input gradient gathers the values into
+# column order first (4+ batch tiles) and the weight gradient runs in 256-column slices that add
+# into dW (B = 512: 2 slices, 1024: 4); full rows and columns included.
+@pytest.mark.parametrize("B,bf16", [(256, False), (512, False), (1024, False), (512, True)],
+                         ids=["B256", "B512", "B1024", "B512-bf16"])
+def test_wide_batch_large_layer(B, bf16):
+    say(f"wide batch B={B} bf16={bf16} on 1500x2000 10%")
+    L = synth.random_small_layer(230, 1500, 2000, 300000, "dense_lines")
+    assert L["nnz"] >= 2 ** 18
+    run_all(L, B, 800 + B, bf16=bf16)
+
+
 @pytest.mark.parametrize("B", [64, 192])
 def test_wide_layer_bf16(B):
     say(f"wide layer bf16 B={B}")
