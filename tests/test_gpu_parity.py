@@ -439,3 +439,35 @@ def test_wide_layer_bf16(B):
     say(f"wide layer bf16 B={B}")
     L = synth.random_small_layer(196, 2600, 2100, int(0.06 * 2600 * 2100), "dense_lines")
     run_all(L, B, 300 + B, bf16=True)
+
+
+# ------------------------------------------------------------ seeded random sweep
+def _random_cases(n=36, seed=4242):
+    """Random shapes, densities, structures and batches (including 1, odd sizes, 16..192 and a
+    few wide ones); each is checked in full by run_all (forward, both gradients separately and
+    in one call, bias gradient)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = ["uniform", "empty_rows", "dense_lines", "skewed_rows", "one_row", "one_col"]
+    batches = [1, 2, 3, 4, 5, 7, 8, 12, 16, 20, 24, 32, 36, 48, 64, 96, 128, 132, 192, 256, 320]
+    out = []
+    for i in range(n):
+        O = int(rng.integers(1, 2500))
+        I = int(rng.integers(1, 2500))
+        dens = float(10 ** rng.uniform(-3.0, -0.7))
+        nnz = max(1, min(O * I, int(dens * O * I)))
+        shape = shapes[int(rng.integers(0, len(shapes)))]
+        B = batches[int(rng.integers(0, len(batches)))]
+        bf16 = bool(rng.random() < 0.25)
+        out.append((5000 + i, shape, O, I, nnz, B, bf16))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-n{c[4]}-B{c[5]}"
+                         + ("-bf16" if c[6] else ""))
+def test_random_sweep(case):
+    seed, shape, O, I, nnz, B, bf16 = case
+    say(f"random {shape} {O}x{I} nnz={nnz} B={B} bf16={bf16}")
+    L = synth.random_small_layer(seed, O, I, nnz, shape)
+    if L["nnz"] == 0:
+        pytest.skip("the shape left no entries")
+    run_all(L, B, seed, bf16=bf16)
