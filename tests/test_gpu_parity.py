@@ -180,9 +180,13 @@ def _sampled(name, B, seed, n_rows=64, n_cols=64, n_entries=4096):
     cs = np.sort(rng.choice(I, n_cols, replace=False))
     ks = np.sort(rng.choice(nnz, n_entries, replace=False))
     ks = np.unique(np.concatenate([ks, [0, nnz - 1]]))
+    dX2, dW2 = (t.cpu().numpy() for t in snk.snack_coo_bwd(W, X, dYt))  # both from one call
     check_close(Y[:, rs], oracle_fwd_rows(built, x, L["bias"], rs), nnz / O, f"{name} fwd sample")
-    check_close(dX[:, cs], oracle_dx_cols(built, dy, cs), nnz / I, f"{name} dX sample")
-    check_close(dW[ks], oracle_dw_entries(built, x, dy, ks), B, f"{name} dW sample")
+    ref_dx, ref_dw = oracle_dx_cols(built, dy, cs), oracle_dw_entries(built, x, dy, ks)
+    check_close(dX[:, cs], ref_dx, nnz / I, f"{name} dX sample")
+    check_close(dW[ks], ref_dw, B, f"{name} dW sample")
+    check_close(dX2[:, cs], ref_dx, nnz / I, f"{name} bwd dX sample")
+    check_close(dW2[ks], ref_dw, B, f"{name} bwd dW sample")
     # whole-output property at full size: the adjoint identity in fp64
     Yb = Y.astype(np.float64) - L["bias"].astype(np.float64)
     a = float(np.sum(dy.astype(np.float64) * Yb))
