@@ -412,6 +412,8 @@ def main():
     kern.update(kern_split)
     all_ops = STEP_OPS + ("dx", "dw")
     kernel_us = {op: float(np.mean(kern[op])) * 1000.0 for op in all_ops}
+    kernel_pct = {op: {f"p{q}": round(float(np.percentile(kern[op], q)) * 1000.0, 2) for q in (10, 50, 90)}
+                  for op in all_ops}
     # the dominant kernel of the step (the fused backward pass when the batch allows it)
     cand = STEP_OPS if bwd_fused(B) else SPLIT_OPS
     dom = max(cand, key=lambda o: kernel_us[o])
@@ -428,6 +430,7 @@ def main():
               "us_per_step_graph": None if graph_us is None else round(graph_us, 2),
               "backward_fused": bwd_fused(B),
               "kernel_us": {op: round(v, 2) for op, v in kernel_us.items()},
+              "kernel_us_percentiles": kernel_pct,
               "kernel_frac_hbm": {op: round(nbytes[op] / (kernel_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                   for op in all_ops}}
     if not args.no_extras:
