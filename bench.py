@@ -62,14 +62,9 @@ def algorithmic_bytes(op, nnz, O, I, B, s):
 
 def bwd_fused(B):
     """Whether snack_coo_bwd runs its single column-view pass at this batch (the library's
-    rule: B = 4*BT*Q with BT the largest power of two <= min(16, B/4) and Q in {1, 2, 4});
-    otherwise it runs the two gradients one after the other.  Used to label timings only."""
-    if B < 16 or B % 4:
-        return False
-    bt = 4
-    while bt * 2 <= min(16, B // 4):
-        bt *= 2
-    return B % (4 * bt) == 0 and B // (4 * bt) in (1, 2, 4)
+    rule: B = 4*BT*Q with BT a power of two <= 16 and Q <= 4 float4s per lane); otherwise it
+    runs the two gradients one after the other.  Used to label timings only."""
+    return B > 0 and B % 4 == 0 and any(B % (4 * bt) == 0 and B // (4 * bt) <= 4 for bt in (16, 8, 4, 2, 1))
 
 
 def kernel_source_sha():

@@ -21,7 +21,7 @@
 //                 combined by a segmented scan across entry groups; segments cut
 //                 by a chunk edge go to a small partials buffer and are finished
 //                 by fixup_kernel.  Balanced by nnz, so power-law rows are fine.
-//      rowwave  - for batches that are multiples of 4 and >= 16: a wave owns one
+//      rowwave  - for batches that are multiples of 4: a wave owns one
 //                 output row at a time; its entries are read 64 per coalesced
 //                 load and prefetched a chunk ahead; lane slots gather float4s
 //                 of the feature-major operand with several loads in flight.
@@ -250,36 +250,40 @@ __global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B,
 // For batches that are multiples of 4.  A workgroup of 4 waves owns 4/WPR
 // output keys (rows), each split over WPR waves.  Lanes are (slot e, lane t):
 // S = 64/BT slots each take one stored entry per step, lane t holds batch
-// columns b0+4t .. b0+4t+3 (one float4 of the feature-major operand row).  A
-// wave reads its key's entries 64 at a time (chunks c, c+WPR, ...) with one
-// coalesced load per lane -- keeping each entry's operand row as a 32-bit
-// float4 offset -- prefetches its next chunk while the current one is
-// consumed, and keeps U float4 gathers in flight.  Lanes of a chunk past the
+// columns b0+4t .. b0+4t+3 and, with Q > 1, the float4s t+BT, .., t+(Q-1)BT
+// further on (the batch tile is 4*BT*Q columns; Q > 1 only when tiles are
+// exact).  A wave reads its key's entries 64 at a time (chunks c, c+WPR, ...)
+// with one coalesced load per lane -- keeping each entry's operand row as a
+// 32-bit float4 offset -- prefetches its next chunk while the current one is
+// consumed, and keeps U*Q float4 gathers in flight.  Lanes of a chunk past the
 // key's end point at the operand's zero row with value 0, so no step needs a
 // mask.  Slot partial sums are combined by xor shuffles, the WPR waves of a
 // key through LDS.  The operand including its zero row is below 4 GB.
-template <int BT, int WPR, typename OutT>
+template <int BT, int WPR, int Q, typename OutT>
 __global__ __launch_bounds__(kBlock) void rowwave_kernel(
     int64_t nkeys, const int32_t *__restrict__ offs, const int32_t *__restrict__ gidx,
     const float *__restrict__ vals, const int32_t *__restrict__ perm, const float *__restrict__ opnd, int zero_row,
     int64_t B, const float *__restrict__ bias, OutT *__restrict__ out, int64_t out_ld) {
     constexpr int S = kWave / BT;
-    constexpr int U = (S * 8 <= kWave) ? 8 : kWave / S;  // S*U divides 64
+    constexpr int UQ = 8 / Q;
+    constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;  // S*U divides 64
     constexpr int KPB = kWavesPerBlock / WPR;             // keys per workgroup
-    __shared__ float4 part[kWavesPerBlock][BT];
+    __shared__ float4 part[kWavesPerBlock][Q][BT];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int e = lane / BT, t = lane % BT;
     const int64_t r = xcd_block() * KPB + wave / WPR;
     const int wsub = wave % WPR;
     const bool rok = r < nkeys;  // uniform per wave
-    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * (4 * BT) + 4 * t;
-    const bool bok = b0 < B;     // B % 4 == 0: all four columns exist
+    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * (4 * BT * Q) + 4 * t;
+    const bool bok = b0 < B;     // B % 4 == 0: all four columns exist (Q > 1: every lane)
     const int B4 = static_cast<int>(B / 4);
     // uniform base of this batch tile; a lane adds its float4 column and the entry's row
-    const char *__restrict__ tile = reinterpret_cast<const char *>(opnd) + blockIdx.y * (16 * BT);
+    const char *__restrict__ tile = reinterpret_cast<const char *>(opnd) + blockIdx.y * (16 * BT * Q);
     const uint32_t lane_off = 16u * static_cast<uint32_t>(bok ? t : 0);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 acc[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (rok) {
         const int zoff = zero_row * B4;
         const int s = offs[r], end = offs[r + 1];
@@ -305,51 +309,70 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
             }
             for (int h = 0; h < n; h += S * U) {
                 const int sa = (h + e) << 2;  // ds_bpermute address of slot e's entry; +4S per step
-                float4 x[U];
+                float4 x[U][Q];
                 float v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int o = __builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co);
                     v[u] = __int_as_float(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, __float_as_int(cv)));
-                    x[u] = *reinterpret_cast<const float4 *>(tile + (16u * static_cast<uint32_t>(o) + lane_off));
+                    const uint32_t a = 16u * static_cast<uint32_t>(o) + lane_off;
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+                        x[u][q] = *reinterpret_cast<const float4 *>(tile + (a + 16u * static_cast<uint32_t>(q * BT)));
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    acc.x = fmaf(v[u], x[u].x, acc.x);
-                    acc.y = fmaf(v[u], x[u].y, acc.y);
-                    acc.z = fmaf(v[u], x[u].z, acc.z);
-                    acc.w = fmaf(v[u], x[u].w, acc.w);
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) {
+                        acc[q].x = fmaf(v[u], x[u][q].x, acc[q].x);
+                        acc[q].y = fmaf(v[u], x[u][q].y, acc[q].y);
+                        acc[q].z = fmaf(v[u], x[u][q].z, acc[q].z);
+                        acc[q].w = fmaf(v[u], x[u][q].w, acc[q].w);
+                    }
                 }
             }
         }
     }
 #pragma unroll
-    for (int d = BT; d < kWave; d <<= 1) {
-        acc.x += __shfl_xor(acc.x, d, kWave);
-        acc.y += __shfl_xor(acc.y, d, kWave);
-        acc.z += __shfl_xor(acc.z, d, kWave);
-        acc.w += __shfl_xor(acc.w, d, kWave);
+    for (int q = 0; q < Q; ++q) {
+#pragma unroll
+        for (int d = BT; d < kWave; d <<= 1) {
+            acc[q].x += __shfl_xor(acc[q].x, d, kWave);
+            acc[q].y += __shfl_xor(acc[q].y, d, kWave);
+            acc[q].z += __shfl_xor(acc[q].z, d, kWave);
+            acc[q].w += __shfl_xor(acc[q].w, d, kWave);
+        }
     }
     if constexpr (WPR > 1) {
-        if (e == 0) part[wave][t] = acc;
+        if (e == 0) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) part[wave][q][t] = acc[q];
+        }
         __syncthreads();
         if (wsub == 0 && e == 0) {
 #pragma unroll
-            for (int q = 1; q < WPR; ++q) {
-                const float4 o = part[wave + q][t];
-                acc.x += o.x;
-                acc.y += o.y;
-                acc.z += o.z;
-                acc.w += o.w;
+            for (int w = 1; w < WPR; ++w) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const float4 o = part[wave + w][q][t];
+                    acc[q].x += o.x;
+                    acc[q].y += o.y;
+                    acc[q].z += o.z;
+                    acc[q].w += o.w;
+                }
             }
         }
     }
     if (rok && wsub == 0 && e == 0 && bok) {
         const float bv = bias ? bias[r] : 0.f;
-        store_act(out, (b0 + 0) * out_ld + r, acc.x + bv);
-        store_act(out, (b0 + 1) * out_ld + r, acc.y + bv);
-        store_act(out, (b0 + 2) * out_ld + r, acc.z + bv);
-        store_act(out, (b0 + 3) * out_ld + r, acc.w + bv);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int64_t c = b0 + 4 * q * BT;
+            store_act(out, (c + 0) * out_ld + r, acc[q].x + bv);
+            store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
+            store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
+            store_act(out, (c + 3) * out_ld + r, acc[q].w + bv);
+        }
     }
 }
 
@@ -481,7 +504,7 @@ __device__ int wave_lower_bound(const int32_t *__restrict__ a, int lo, int hi, i
     return lo + __popcll(__ballot(j < hi && a[min(j, hi - 1)] < target));
 }
 
-// Both gradients in one pass over the column view (batch 4*BT*Q, Q in {1, 2, 4}).
+// Both gradients in one pass over the column view (batch 4*BT*Q, Q in 1..4).
 // A wave owns one input column i (with NB > 1: the column's entries whose rows lie in one
 // band of rows).  The column's X slice is held in registers (lane t: float4s t, t+BT, ..
 // of the feature-major X row i); each stored entry k gathers its dY row once and uses it
@@ -713,7 +736,7 @@ __global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restric
     }
 }
 
-// Weight gradient for batches 4*BT*Q with Q in {1, 2, 4}: the rowwave mapping
+// Weight gradient for batches 4*BT*Q with Q in 1..4: the rowwave mapping
 // for sampled products.  A workgroup owns 4/WPR rows of W, each split over WPR
 // waves; a wave keeps the row's dY slice in registers (lane t: float4s t,
 // t+BT, .. of the feature-major dY row, Q of them) for the whole row, takes
@@ -721,16 +744,20 @@ __global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restric
 // (the next 64 prefetched; lanes past the row's end point at X's zero row),
 // gathers U entries per slot in flight and sums each slot's BT lanes by DPP.
 // ld: row stride (floats) of the feature-major copies; a batch wider than 4*BT*Q is taken in
-// slices of 4*BT*Q columns (xt and dyt offset by the slice), each adding into dW (acc != 0)
-// after the first.
-template <int BT, int WPR, int Q>
+// slices of 4*BT*Q columns (xt and dyt offset by the slice), each adding into dW (ACC) after
+// the first.  ACC reads the U old dW values of a step before its gathers: loads and stores
+// complete in issue order on one counter, so a read issued after the gathers would make the
+// step wait for all of them before its first add.  UQ: entries per slot in flight (at most
+// 64/S); the slices measured fastest with 2 (5000 x 5000 at 90 %, batch 4096: 2.07 ms with 8,
+// 1.87 with 2), a single pass with 8.
+template <int BT, int WPR, int Q, int UQ, bool ACC>
 __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32_t *__restrict__ offs,
                                                           const int32_t *__restrict__ cols,
                                                           const float *__restrict__ xt, int zero_row,
-                                                          const float *__restrict__ dyt, int64_t ld, int acc,
+                                                          const float *__restrict__ dyt, int64_t ld,
                                                           float *__restrict__ dW) {
     constexpr int S = kWave / BT;
-    constexpr int U = (S * 8 <= kWave) ? 8 : kWave / S;  // S*U divides 64
+    constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;  // S*U divides 64
     constexpr int KPB = kWavesPerBlock / WPR;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -759,6 +786,11 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
         }
         for (int h = 0; h < n; h += S * U) {
             const int sa = (h + e) << 2;
+            float old[U];
+            if constexpr (ACC) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) old[u] = dW[base + min(h + u * S + e, n - 1)];
+            }
             float4 x[U][Q];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -779,7 +811,7 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
                 }
                 d = group_sum<BT>(d);
                 const int src = h + u * S + e;
-                if (t == 0 && src < n) dW[base + src] = acc ? dW[base + src] + d : d;
+                if (t == 0 && src < n) dW[base + src] = ACC ? old[u] + d : d;
             }
         }
     }
@@ -1412,6 +1444,23 @@ enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2, kCsr1 = 3, kCsr1Priv = 
 constexpr int64_t kScatterLdsFloats = 16384;  // 64 KB private dX copy per workgroup
 
 // Device work plan of one gather-reduce (forward or input gradient).
+// Batch limits of the gather-reduce mappings (compile-time tuning knobs): the input gradient
+// scatters into LDS copies up to SNACK_SCATTER_MAX_B batch rows, and batches that are multiples
+// of 4 from SNACK_ROWWAVE_MIN_B on take the rowwave mapping.
+#ifndef SNACK_SCATTER_MAX_B
+#define SNACK_SCATTER_MAX_B 3
+#endif
+
+// 0: rowwave tiles of 4*BT columns; 1: one tile of 4*BT*Q columns (Q <= 4) where 4*BT does not
+// divide the batch; 2: such a tile wherever one exists.
+#ifndef SNACK_ROWWAVE_Q_MODE
+#define SNACK_ROWWAVE_Q_MODE 1
+#endif
+
+#ifndef SNACK_ROWWAVE_MIN_B
+#define SNACK_ROWWAVE_MIN_B 4
+#endif
+
 // layers from which the wide-batch gradient paths (column-order values for the input gradient,
 // 256-column slices for the weight gradient) pay off over the plain ones
 constexpr int64_t kLargeBatchMinNnz = int64_t(1) << 18;
@@ -1420,6 +1469,7 @@ struct SpmmPlan {
     Mapping mapping;
     bool cvals;          // rowwave over the column view: vals gathered into column order first
     int bt;              // batch lanes per entry group (segscan) or lanes per slot (rowwave)
+    int q;               // rowwave: float4s per lane (batch tile 4*bt*q)
     int64_t chunk;       // segscan, csr1: entries per wave; scatter: entries per workgroup
     int64_t nchunks;     // segscan, csr1: waves; scatter: workgroups (partial copies)
     int64_t nparts;      // csr1 private copies: workgroups (partial copies)
@@ -1477,7 +1527,7 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
         p.total = at;
         return p;
     }
-    if (scatter_ok && B <= 4 && B * nout <= kScatterLdsFloats && nnz > 0) {
+    if (scatter_ok && B <= SNACK_SCATTER_MAX_B && B * nout <= kScatterLdsFloats && nnz > 0) {
         p.mapping = kScatter;
         p.direct = true;  // reads dY in its batch-major layout
         p.nchunks = std::min<int64_t>(std::max<int64_t>(ceil_div(nnz, 4096), 1), 256);
@@ -1489,10 +1539,21 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
         p.total = at;
         return p;
     }
-    if (B >= 16 && B % 4 == 0 && (opnd_rows + 1) * B * 4 < (int64_t(1) << 32)) {
+    if (B >= SNACK_ROWWAVE_MIN_B && B % 4 == 0 && (opnd_rows + 1) * B * 4 < (int64_t(1) << 32)) {
         p.mapping = kRowwave;
-        p.bt = 4;  // lanes per slot: the largest power of two <= min(16, B/4)
+        p.bt = 1;  // lanes per slot: the largest power of two <= min(16, B/4)
         while (p.bt * 2 <= std::min<int64_t>(16, B / 4)) p.bt *= 2;
+        p.q = 1;
+        if (SNACK_ROWWAVE_Q_MODE == 2 || (SNACK_ROWWAVE_Q_MODE == 1 && B % (4 * p.bt) != 0)) {
+            // one exact tile of 4*BT*Q columns, Q <= 4 float4s per lane, where one exists
+            for (int bt = 16; bt >= 1; bt /= 2) {
+                if (B % (4 * bt) == 0 && B / (4 * bt) <= 4) {
+                    p.bt = bt;
+                    p.q = static_cast<int>(B / (4 * bt));
+                    break;
+                }
+            }
+        }
     } else {
         p.mapping = kSegscan;
         p.bt = pow2_at_least(B);
@@ -1514,7 +1575,7 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
     // tile; with 4 or more tiles on a large layer they are gathered into column order once, so
     // every tile reads them coalesced and long keys split over 4 waves (one tile: the gather costs
     // more than it saves)
-    p.cvals = scatter_ok && p.mapping == kRowwave && ceil_div(B, 4 * p.bt) >= 4 && nnz >= kLargeBatchMinNnz;
+    p.cvals = scatter_ok && p.mapping == kRowwave && ceil_div(B, 4 * p.bt * p.q) >= 4 && nnz >= kLargeBatchMinNnz;
     p.off_cvals = at;
     if (p.cvals) at = align_up(at + sizeof(float) * static_cast<size_t>(nnz));
     p.total = at;
@@ -1524,7 +1585,7 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
 struct SddmmPlan {
     bool csr1;           // batch 1: csr1_dw_kernel, activations read in place
     bool wide;           // sddmm_wide_kernel (batch a multiple of 4, >= 16) or sddmm_kernel
-    int rowq;            // > 0: rowsddmm_kernel with this many float4s per lane (1, 2 or 4)
+    int rowq;            // > 0: rowsddmm_kernel with this many float4s per lane (1 to 4)
     int64_t slices;      // rowsddmm over this many 256-column batch slices (1: the whole batch)
     int bt, vw;
     int64_t steps, waves, per_wave;
@@ -1554,13 +1615,19 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
         p.waves = ceil_div(nnz, G * p.steps);
     }
     p.slices = 1;
-    if (p.wide && B % (4 * p.bt) == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
-        const int64_t q = B / (4 * p.bt);
-        if (q == 1 || q == 2 || q == 4) {
-            p.rowq = static_cast<int>(q);
-        } else if (p.bt == 16 && B % 256 == 0 && nnz >= kLargeBatchMinNnz) {  // wide batch, large layer:
+    if (B >= 4 && B % 4 == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
+        // rowsddmm over B = 4*BT*Q: BT the largest power of two <= 16 that leaves Q <= 4
+        for (int bt = 16; bt >= 1; bt /= 2) {
+            if (B % (4 * bt) == 0 && B / (4 * bt) <= 4) {
+                p.bt = bt;
+                p.rowq = static_cast<int>(B / (4 * bt));
+                break;
+            }
+        }
+        if (p.rowq == 0 && B % 256 == 0 && nnz >= kLargeBatchMinNnz) {  // wide batch, large layer:
             // slices of 256 columns (each gathers its part of the X rows once per entry; the
-            // per-entry kernel below re-reads the whole dY row per entry)
+            // per-entry kernel re-reads the whole dY row per entry)
+            p.bt = 16;
             p.rowq = 4;
             p.slices = B / 256;
         }
@@ -1590,6 +1657,11 @@ struct BwdPlan {
     size_t off_x, off_dy, off_part, total;
 };
 
+// Smallest lane count per slot of the one-pass backward (1: batches 4, 8, 12 take it too).
+#ifndef SNACK_FUSED_MIN_BT
+#define SNACK_FUSED_MIN_BT 1
+#endif
+
 #ifndef SNACK_BAND_MIN_NNZ
 #define SNACK_BAND_MIN_NNZ (int64_t(1) << 20)
 #endif
@@ -1607,16 +1679,18 @@ int64_t band_min_nnz() {
 
 BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool aligned16) {
     BwdPlan p{};
-    if (nnz > 0 && B >= 16 && B % 4 == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
-        int bt = 4;  // lanes per slot: the largest power of two <= min(16, B/4)
-        while (bt * 2 <= std::min<int64_t>(16, B / 4)) bt *= 2;
-        const int64_t q = B / (4 * bt);
-        if (B % (4 * bt) == 0 && (q == 1 || q == 2 || q == 4)) {
-            p.fused = true;
-            p.bt = bt;
-            p.q = static_cast<int>(q);
-            // row bands (one per XCD) once the triple is large enough to spill L2
-            p.nb = nnz >= band_min_nnz() ? kXcds : 1;
+    if (nnz > 0 && B >= 4 && B % 4 == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
+        // B = 4*BT*Q: BT lanes per slot (the largest power of two <= 16 that leaves Q <= 4
+        // float4s per lane)
+        for (int bt = 16; bt >= SNACK_FUSED_MIN_BT; bt /= 2) {
+            if (B % (4 * bt) == 0 && B / (4 * bt) <= 4) {
+                p.fused = true;
+                p.bt = bt;
+                p.q = static_cast<int>(B / (4 * bt));
+                // row bands (one per XCD) once the triple is large enough to spill L2
+                p.nb = nnz >= band_min_nnz() ? kXcds : 1;
+                break;
+            }
         }
     }
     if (p.fused) {
@@ -1702,7 +1776,7 @@ void launch_segscan_bt(const SpmmPlan &p, int64_t nnz, const int32_t *keys, cons
                        keys, gidx, vals, perm, opnd, B, bias, out, out_ld, head, tail);
 }
 
-template <typename OutT, int BT>
+template <typename OutT, int BT, int Q>
 void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const int32_t *gidx, const float *vals,
                        const int32_t *perm, const float *opnd, int64_t opnd_rows, int64_t B, const float *bias,
                        OutT *out, int64_t out_ld, hipStream_t st) {
@@ -1713,12 +1787,12 @@ void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const in
     const bool split = !perm && nnz >= 256 * nkeys;
     const int64_t keys_per_block = split ? 1 : kWavesPerBlock;
     const int64_t blocks = round_up8(ceil_div(nkeys, keys_per_block));
-    const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(ceil_div(B, 4 * BT)));
+    const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(ceil_div(B, 4 * BT * Q)));
     if (split)
-        hipLaunchKernelGGL((rowwave_kernel<BT, 4, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
+        hipLaunchKernelGGL((rowwave_kernel<BT, 4, Q, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
                            perm, opnd, zero_row, B, bias, out, out_ld);
     else
-        hipLaunchKernelGGL((rowwave_kernel<BT, 1, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
+        hipLaunchKernelGGL((rowwave_kernel<BT, 1, Q, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
                            perm, opnd, zero_row, B, bias, out, out_ld);
 }
 
@@ -1746,11 +1820,18 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
             vals = cv;
             perm = nullptr;
         }
-        switch (p.bt) {
-            case 4: launch_rowwave_bt<OutT, 4>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); break;
-            case 8: launch_rowwave_bt<OutT, 8>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); break;
-            case 16: launch_rowwave_bt<OutT, 16>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); break;
-            default: return fail(SNACK_ERR_INTERNAL, "rowwave: unsupported lane count %d", p.bt);
+        switch (p.bt * 8 + p.q) {
+#define SNACK_RW(BTV, QV)                                                                                           \
+    case BTV * 8 + QV:                                                                                               \
+        launch_rowwave_bt<OutT, BTV, QV>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); \
+        break;
+            SNACK_RW(1, 1) SNACK_RW(2, 1) SNACK_RW(4, 1) SNACK_RW(8, 1) SNACK_RW(16, 1)
+            SNACK_RW(1, 3) SNACK_RW(2, 3) SNACK_RW(4, 3) SNACK_RW(8, 3) SNACK_RW(16, 3)
+#if SNACK_ROWWAVE_Q_MODE == 2
+            SNACK_RW(16, 2) SNACK_RW(16, 4)
+#endif
+#undef SNACK_RW
+            default: return fail(SNACK_ERR_INTERNAL, "rowwave: unsupported plan bt=%d q=%d", p.bt, p.q);
         }
         probe(false, st);
         return check_hip("rowwave_kernel");
@@ -2045,27 +2126,46 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             const bool split = nnz >= 256 * O;
             const dim3 rgrid(static_cast<unsigned>(round_up8(ceil_div(O, split ? 1 : kWavesPerBlock))));
             const int zero_row = static_cast<int>(I);
-            // slice k: columns [256k, 256k + 256) of the copies (one launch per slice, in order)
 #define SNACK_ROWSD(BTV, WPRV, QV)                                                                           \
-    for (int64_t k = 0; k < p.slices; ++k)                                                                   \
-    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets,      \
-                       W->cols, xt + 256 * k, zero_row, dyt + 256 * k, batch, static_cast<int>(k > 0), dW)
+    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV, 8, false>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, \
+                       W->cols, xt, zero_row, dyt, batch, dW)
 #define SNACK_ROWSD_Q(BTV, WPRV)                         \
     do {                                                 \
         if (p.rowq == 1) SNACK_ROWSD(BTV, WPRV, 1);      \
         else if (p.rowq == 2) SNACK_ROWSD(BTV, WPRV, 2); \
+        else if (p.rowq == 3) SNACK_ROWSD(BTV, WPRV, 3); \
         else SNACK_ROWSD(BTV, WPRV, 4);                  \
     } while (0)
-            if (p.bt == 16) {
-                if (split) SNACK_ROWSD_Q(16, 4);
-                else SNACK_ROWSD_Q(16, 1);
+#define SNACK_ROWSD_BT(BTV)                 \
+    if (split) SNACK_ROWSD_Q(BTV, 4);       \
+    else SNACK_ROWSD_Q(BTV, 1);
+            if (p.slices > 1) {
+                // slice k: columns [256k, 256k + 256) of the copies (one launch per slice, in order)
+                for (int64_t k = 0; k < p.slices; ++k) {
+#define SNACK_ROWSD_SLICE(WPRV, ACCV)                                                                          \
+    hipLaunchKernelGGL((rowsddmm_kernel<16, WPRV, 4, 2, ACCV>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, W->cols, \
+                       xt + 256 * k, zero_row, dyt + 256 * k, batch, dW)
+                    if (split) {
+                        if (k > 0) SNACK_ROWSD_SLICE(4, true);
+                        else SNACK_ROWSD_SLICE(4, false);
+                    } else {
+                        if (k > 0) SNACK_ROWSD_SLICE(1, true);
+                        else SNACK_ROWSD_SLICE(1, false);
+                    }
+#undef SNACK_ROWSD_SLICE
+                }
+            } else if (p.bt == 16) {
+                SNACK_ROWSD_BT(16)
             } else if (p.bt == 8) {
-                if (split) SNACK_ROWSD_Q(8, 4);
-                else SNACK_ROWSD_Q(8, 1);
+                SNACK_ROWSD_BT(8)
+            } else if (p.bt == 4) {
+                SNACK_ROWSD_BT(4)
+            } else if (p.bt == 2) {
+                SNACK_ROWSD_BT(2)
             } else {
-                if (split) SNACK_ROWSD_Q(4, 4);
-                else SNACK_ROWSD_Q(4, 1);
+                SNACK_ROWSD_BT(1)
             }
+#undef SNACK_ROWSD_BT
 #undef SNACK_ROWSD_Q
 #undef SNACK_ROWSD
         } else if (p.wide) {
@@ -2115,6 +2215,10 @@ void launch_colbwd_q(int q, dim3 grid, hipStream_t st, int64_t I, const snack_co
         hipLaunchKernelGGL((colbwd_kernel<BT, 2, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
                            W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
                            part);
+    else if (q == 3)
+        hipLaunchKernelGGL((colbwd_kernel<BT, 3, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
+                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
+                           part);
     else
         hipLaunchKernelGGL((colbwd_kernel<BT, 4, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
                            W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
@@ -2128,8 +2232,14 @@ void launch_colbwd_nb(const BwdPlan &p, dim3 grid, hipStream_t st, int64_t I, co
         launch_colbwd_q<OutT, 16, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
     else if (p.bt == 8)
         launch_colbwd_q<OutT, 8, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
-    else
+    else if (p.bt == 4)
         launch_colbwd_q<OutT, 4, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+#if SNACK_FUSED_MIN_BT < 4
+    else if (p.bt == 2)
+        launch_colbwd_q<OutT, 2, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+    else
+        launch_colbwd_q<OutT, 1, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+#endif
 }
 
 template <typename OutT>
