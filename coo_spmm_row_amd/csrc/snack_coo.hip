@@ -73,7 +73,7 @@ __device__ __forceinline__ void store_act(bf16_t *p, int64_t i, float v) {
 // [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16); every lane of the
@@ -89,6 +89,50 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Reduce-scatter of U values over aligned groups of N lanes (U <= N, both powers of two):
+// lane t of a group returns the group's sum of v[t / (N / U)].  The stages pair lanes by
+// mirror within 16 (xor 15), mirror within 8 (xor 7), xor 2 and xor 1 -- the last log2(N) of
+// these, an independent set of lane masks, so every stage adds disjoint partial sums.  While
+// more than one value is left, a lane keeps the half its own bit selects (bit 3, 2, 1, 0 of
+// the lane in those stages), and sends the other half to its partner, which differs in that
+// bit; once one value is left the remaining stages are plain reductions.  That is log2(U)
+// halvings (3 instructions per kept value) plus one add per further stage, against U full
+// group sums of log2(N) adds each.
+// One stage of group_reduce_scatter: M values live in w[0, M); partner = the DPP source lane.
+template <int CTRL, int BIT, int M, int U>
+__device__ __forceinline__ void reduce_scatter_stage(float (&w)[U], int t) {
+    if constexpr (M > 1) {
+        constexpr int H = M / 2;
+        const bool hi = (t >> BIT) & 1;
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            const float send = hi ? w[j] : w[j + H];
+            const float keep = hi ? w[j + H] : w[j];
+            w[j] = keep + dpp_move<CTRL>(send);
+        }
+    } else {
+        w[0] += dpp_move<CTRL>(w[0]);
+    }
+}
+
+template <int N, int U>
+__device__ __forceinline__ float group_reduce_scatter(const float (&v)[U], int t) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+    static_assert(U >= 1 && U <= N && (U & (U - 1)) == 0, "U a power of two <= N");
+    float w[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) w[j] = v[j];
+    constexpr int M0 = U;
+    if constexpr (N >= 16) reduce_scatter_stage<0x140, 3, M0, U>(w, t);
+    constexpr int M1 = N >= 16 && M0 > 1 ? M0 / 2 : M0;
+    if constexpr (N >= 8) reduce_scatter_stage<0x141, 2, M1, U>(w, t);
+    constexpr int M2 = N >= 8 && M1 > 1 ? M1 / 2 : M1;
+    if constexpr (N >= 4) reduce_scatter_stage<0x4E, 1, M2, U>(w, t);
+    constexpr int M3 = N >= 4 && M2 > 1 ? M2 / 2 : M2;
+    if constexpr (N >= 2) reduce_scatter_stage<0xB1, 0, M3, U>(w, t);
+    return w[0];
+}
+
 // Logical workgroup index such that each XCD (blockIdx.x % 8 under round-robin
 // dispatch) works on one contiguous eighth of the logical range.  gridDim.x is
 // a multiple of 8; callers drop logical ids beyond their real count.
@@ -100,14 +144,12 @@ __device__ __forceinline__ int64_t xcd_block() {
 // ---------------------------------------------------------------- layout
 // in [B][F] (batch-major, fp32 or bf16)  ->  out [F+1][B] fp32 (feature-major), row F
 // zero (gathers of a missing entry point there instead of being masked).
-// A workgroup moves a tile of 16 features x 64 batch rows through LDS: every
-// thread issues its four loads (64-byte row segments) before its stores, and
-// the tile's output is one contiguous run when B <= 64.
-constexpr int kTf = 32, kTb = 64;
 // Up to two tensors per launch (blockIdx.z; the backward pass transposes X and dY together).
-// A workgroup moves a tile of 32 features x 64 batch rows through LDS: each thread issues its
-// eight loads (128-byte row segments per 32 lanes) before its stores, and the tile's output is
-// one contiguous run per feature.
+// A workgroup moves a tile of 32 features x 64 batch rows through LDS.
+constexpr int kTf = 32, kTb = 64;
+
+// Any F and B: each thread issues its eight scalar loads (128-byte row segments per 32 lanes)
+// before its stores; the tile's output is one contiguous run per feature.
 template <typename InT>
 __global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__restrict__ in0,
                                                                   float *__restrict__ out0, int64_t F0,
@@ -138,6 +180,62 @@ __global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__r
     for (int li = threadIdx.x; li < nf * nb; li += kBlock) {
         const int ff = li / nb, bb = li % nb;
         out[(f0 + ff) * B + b0 + bb] = tile[bb][ff];
+    }
+}
+
+__device__ __forceinline__ float4 load_act4(const float *p, int64_t i) {
+    return *reinterpret_cast<const float4 *>(p + i);
+}
+__device__ __forceinline__ float4 load_act4(const bf16_t *p, int64_t i) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                       __uint_as_float(u.y & 0xFFFF0000u));
+}
+
+// F and B multiples of 4 (16-byte aligned rows): each thread loads two 4-feature vectors of
+// two batch rows and stores two 4-row vectors of two features, with no divisions.  LDS rows
+// are padded to 33 floats: the 4 scalar writes and reads of a vector fall in distinct banks.
+template <typename InT>
+__global__ __launch_bounds__(kBlock) void to_feature_major4_kernel(const InT *__restrict__ in0,
+                                                                   float *__restrict__ out0, int64_t F0,
+                                                                   const InT *__restrict__ in1,
+                                                                   float *__restrict__ out1, int64_t F1,
+                                                                   int64_t B) {
+    __shared__ float tile[kTb][kTf + 1];
+    const InT *__restrict__ in = blockIdx.z == 0 ? in0 : in1;
+    float *__restrict__ out = blockIdx.z == 0 ? out0 : out1;
+    const int64_t F = blockIdx.z == 0 ? F0 : F1;
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kTf;
+    if (f0 >= F && !(blockIdx.x == 0)) return;  // uniform per workgroup, before the barrier
+    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTb;
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && b0 + tid < B && tid < kTb) out[F * B + b0 + tid] = 0.f;
+    // load: thread -> batch row r = tid / 8 (+32), features 4 * (tid % 8) .. +3
+    const int lc = 4 * (tid % (kTf / 4)), lr = tid / (kTf / 4);
+    float4 v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t b = b0 + lr + 32 * i, f = f0 + lc;
+        v[i] = (b < B && f < F) ? load_act4(in, b * F + f) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float *t = &tile[lr + 32 * i][lc];
+        t[0] = v[i].x;
+        t[1] = v[i].y;
+        t[2] = v[i].z;
+        t[3] = v[i].w;
+    }
+    __syncthreads();
+    // store: thread -> feature ff = tid / 16 (+16), batch rows 4 * (tid % 16) .. +3
+    const int sq = 4 * (tid % (kTb / 4)), sf = tid / (kTb / 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ff = sf + 16 * i;
+        const int64_t f = f0 + ff, b = b0 + sq;
+        if (f < F && b < B)
+            *reinterpret_cast<float4 *>(out + f * B + b) =
+                make_float4(tile[sq][ff], tile[sq + 1][ff], tile[sq + 2][ff], tile[sq + 3][ff]);
     }
 }
 
@@ -629,11 +727,12 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
                     for (int q = 0; q < Q; ++q)
                         y[u][q] = *reinterpret_cast<const float4 *>(yb + (o + 16u * static_cast<uint32_t>(q * BT)));
                 }
-                // Banded: the dW values of the U entries per slot are stored together after the last
-                // gather is used (loads and stores share one completion counter, so a store issued
-                // between the gathers makes each later wait also wait for that store).  Unbanded,
-                // storing each entry as it completes measured faster.
-                float dsel = 0.f;
+                // dW: the U dot products of a slot are reduce-scattered over its BT lanes; lane t
+                // with t % (BT/U) == 0 then holds entry h + e + S*(t / (BT/U)) and stores it.  The
+                // stores come after the step's last gather is used (loads and stores share one
+                // completion counter, so a store issued between the gathers would make each later
+                // wait also wait for that store).
+                float dv[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     float d = 0.f;
@@ -648,20 +747,16 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
                         d = fmaf(xv[q].z, y[u][q].z, d);
                         d = fmaf(xv[q].w, y[u][q].w, d);
                     }
-                    d = group_sum<BT>(d);  // the slot's sum, in all BT lanes
-                    if constexpr (NB > 1) {
-                        dsel = t == u ? d : dsel;
-                    } else {
-                        const int k = __builtin_amdgcn_ds_bpermute(sa + 4 * S * u, cp);
-                        if (t == 0 && h + u * S + e < n) dW[k] = d;
-                    }
+                    dv[u] = d;
                 }
-                if constexpr (NB > 1) {
-                    // lane t < U of slot e stores entry h + e + S*t
-                    const int k = __builtin_amdgcn_ds_bpermute(sa + 4 * S * (t < U ? t : 0), cp);
-                    if (t < U && h + t * S + e < n)
+                {
+                    constexpr int R = BT / U;
+                    const float dsum = group_reduce_scatter<BT, U>(dv, t);
+                    const int us = t / R;
+                    const int k = __builtin_amdgcn_ds_bpermute(sa + 4 * S * us, cp);
+                    if (t % R == 0 && h + us * S + e < n)
                         *reinterpret_cast<float *>(reinterpret_cast<char *>(dW) + 4u * static_cast<uint32_t>(k)) =
-                            dsel;
+                            dsum;
                 }
             }
         }
@@ -742,7 +837,8 @@ __global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restric
 // t+BT, .. of the feature-major dY row, Q of them) for the whole row, takes
 // the row's entries 64 at a time with their X rows as 32-bit float4 offsets
 // (the next 64 prefetched; lanes past the row's end point at X's zero row),
-// gathers U entries per slot in flight and sums each slot's BT lanes by DPP.
+// gathers U entries per slot in flight and reduce-scatters each slot's U dot products over its
+// BT lanes by DPP.
 // ld: row stride (floats) of the feature-major copies; a batch wider than 4*BT*Q is taken in
 // slices of 4*BT*Q columns (xt and dyt offset by the slice), each adding into dW (ACC) after
 // the first.  ACC reads the U old dW values of a step before its gathers: loads and stores
@@ -786,11 +882,12 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
         }
         for (int h = 0; h < n; h += S * U) {
             const int sa = (h + e) << 2;
-            float old[U];
-            if constexpr (ACC) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) old[u] = dW[base + min(h + u * S + e, n - 1)];
-            }
+            // the slot's U dot products are reduce-scattered over its BT lanes: lane t with
+            // t % R == 0 ends with entry h + e + S*(t / R), and the wave's stores are contiguous
+            constexpr int R = BT / U;
+            const int src = h + (t / R) * S + e;
+            float old = 0.f;
+            if constexpr (ACC) old = dW[base + min(src, n - 1)];
             float4 x[U][Q];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -799,6 +896,7 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
                 for (int q = 0; q < Q; ++q)
                     x[u][q] = *reinterpret_cast<const float4 *>(xb + (o + 16u * static_cast<uint32_t>(q * BT)));
             }
+            float dv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float d = 0.f;
@@ -809,10 +907,10 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
                     d = fmaf(x[u][q].z, dyv[q].z, d);
                     d = fmaf(x[u][q].w, dyv[q].w, d);
                 }
-                d = group_sum<BT>(d);
-                const int src = h + u * S + e;
-                if (t == 0 && src < n) dW[base + src] = ACC ? old[u] + d : d;
+                dv[u] = d;
             }
+            const float dsum = group_reduce_scatter<BT, U>(dv, t);
+            if (t % R == 0 && src < n) dW[base + src] = ACC ? old + dsum : dsum;
         }
     }
 }
@@ -1756,12 +1854,16 @@ int launch_to_feature_major(const void *src, int dtype, int64_t B, int64_t F, fl
     const int64_t fmax = std::max(F, src1 ? F1 : 0);
     const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, ceil_div(fmax, kTf))),
                     static_cast<unsigned>(ceil_div(B, kTb)), src1 ? 2u : 1u);
-    if (dtype == SNACK_F32)
-        hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(kBlock), 0, st, static_cast<const float *>(src),
-                           dst, F, static_cast<const float *>(src1), dst1, F1, B);
-    else
-        hipLaunchKernelGGL(to_feature_major_kernel<bf16_t>, grid, dim3(kBlock), 0, st,
-                           static_cast<const bf16_t *>(src), dst, F, static_cast<const bf16_t *>(src1), dst1, F1, B);
+    const bool vec = B % 4 == 0 && F % 4 == 0 && (!src1 || F1 % 4 == 0);
+    if (dtype == SNACK_F32) {
+        const float *a = static_cast<const float *>(src), *a1 = static_cast<const float *>(src1);
+        if (vec) hipLaunchKernelGGL(to_feature_major4_kernel<float>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B);
+        else hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B);
+    } else {
+        const bf16_t *a = static_cast<const bf16_t *>(src), *a1 = static_cast<const bf16_t *>(src1);
+        if (vec) hipLaunchKernelGGL(to_feature_major4_kernel<bf16_t>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B);
+        else hipLaunchKernelGGL(to_feature_major_kernel<bf16_t>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B);
+    }
     return check_hip("to_feature_major");
 }
 
