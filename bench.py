@@ -67,6 +67,28 @@ def bwd_fused(B):
     return B > 0 and B % 4 == 0 and any(B % (4 * bt) == 0 and B // (4 * bt) <= 4 for bt in (16, 8, 4, 2, 1))
 
 
+def column_order_step(layer, K):
+    """The same step on the same layer with its values kept in column-view order (the layer's
+    value_order="col"): graph-replayed step time and per-kernel times.  The layer is restored."""
+    import torch
+    import coo_spmm_row_amd as snk
+    W_row, ws_row = layer.W, layer.ws
+    layer.W = W_row.to_column_order()
+    code = snk.SNACK_BF16 if layer.dtype == "bf16" else snk.SNACK_F32
+    need = max(snk.snack_coo_workspace_bytes(op, layer.W, layer.B, code) for op in (0, 1, 2, 3))
+    layer.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=ws_row.device)
+    try:
+        for _ in range(3):
+            layer.step()
+        torch.cuda.synchronize()
+        g = graph_steps(layer, K)
+        _, kern = timed_steps(layer, K)
+        return {"us_per_step_graph": None if g is None else round(g, 2),
+                "kernel_us": {op: round(float(np.mean(v)) * 1000.0, 2) for op, v in kern.items()}}
+    finally:
+        layer.W, layer.ws = W_row, ws_row
+
+
 def kernel_source_sha():
     h = hashlib.sha256()
     with open(os.path.join(ROOT, "coo_spmm_row_amd", "csrc", "snack_coo.hip"), "rb") as f:
@@ -439,6 +461,8 @@ def main():
         extras["module_us_per_step_eager"] = round(module_step_us(layer, args.steps), 2)
         log("topology update (prune 10 %, regrow, column view): device and host")
         extras["topology_update"] = topology_times(layer)
+        log("the step with the values kept in column-view order")
+        extras["column_order_values"] = column_order_step(layer, args.steps)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

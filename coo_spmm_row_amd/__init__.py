@@ -66,7 +66,8 @@ class _Desc(ctypes.Structure):
                 ("nnz", ctypes.c_int64), ("rows", ctypes.c_void_p), ("cols", ctypes.c_void_p),
                 ("vals", ctypes.c_void_p), ("row_offsets", ctypes.c_void_p),
                 ("col_perm", ctypes.c_void_p), ("col_rows", ctypes.c_void_p),
-                ("col_cols", ctypes.c_void_p), ("col_offsets", ctypes.c_void_p)]
+                ("col_cols", ctypes.c_void_p), ("col_offsets", ctypes.c_void_p),
+                ("row_to_col", ctypes.c_void_p)]
 
 
 _i64, _p, _u64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64
@@ -87,11 +88,13 @@ _lib.snack_coo_topology_update_device.argtypes = [_D, _i64, _u64, _p, _p, _p, _p
 _lib.snack_coo_topology_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
 _lib.snack_coo_topology_workspace_bytes.restype = ctypes.c_size_t
 _lib.snack_coo_set_probe.argtypes = [_p, _p]
+_lib.snack_coo_invert_perm.argtypes = [_p, _i64, _p, _p]
+_lib.snack_coo_gather_f32.argtypes = [_p, _p, _i64, _p, _p]
 
 EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_bwd_input",
             "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_coo_init_uniform",
             "snack_coo_topology_update_device", "snack_coo_topology_workspace_bytes", "snack_last_error",
-            "snack_coo_abi_version", "snack_coo_set_probe")
+            "snack_coo_abi_version", "snack_coo_set_probe", "snack_coo_invert_perm", "snack_coo_gather_f32")
 
 
 def _np_ptr(a: Optional[np.ndarray]):
@@ -163,13 +166,18 @@ def snack_coo_init_uniform(out_features: int, in_features: int, nnz: int, seed: 
 class SnackCOO:
     """A layer weight resident on one GPU: the sorted triple, row offsets and
     (optionally) the column view, as torch tensors.  ``vals`` may be updated in
-    place (same length); the structure arrays must stay as built."""
+    place (same length); the structure arrays must stay as built.
+
+    With ``row_to_col`` (the inverse of ``col_perm``) the values are kept in column-view order:
+    ``vals[j]`` belongs to triple entry ``col_perm[j]``, and every dW the library returns for this
+    weight is in the same order (see ``to_column_order``)."""
 
     def __init__(self, out_features, in_features, rows, cols, vals, row_offsets,
-                 col_perm=None, col_rows=None, col_cols=None, col_offsets=None):
+                 col_perm=None, col_rows=None, col_cols=None, col_offsets=None, row_to_col=None):
         self.out_features, self.in_features = int(out_features), int(in_features)
         self.rows, self.cols, self.vals, self.row_offsets = rows, cols, vals, row_offsets
         self.col_perm, self.col_rows, self.col_cols, self.col_offsets = col_perm, col_rows, col_cols, col_offsets
+        self.row_to_col = row_to_col
         self.nnz = int(rows.numel())
         self._desc = _Desc()
         self._refresh()
@@ -192,6 +200,7 @@ class SnackCOO:
         d.rows, d.cols, d.vals, d.row_offsets = ptr(self.rows), ptr(self.cols), ptr(self.vals), ptr(self.row_offsets)
         d.col_perm, d.col_rows = ptr(self.col_perm), ptr(self.col_rows)
         d.col_cols, d.col_offsets = ptr(self.col_cols), ptr(self.col_offsets)
+        d.row_to_col = ptr(self.row_to_col)
 
     @property
     def desc(self):
@@ -202,10 +211,42 @@ class SnackCOO:
     def device(self):
         return self.rows.device
 
+    @property
+    def column_order(self) -> bool:
+        return self.row_to_col is not None
+
     def device_bytes(self) -> int:
         return sum(int(x.numel() * x.element_size()) for x in
                    (self.rows, self.cols, self.vals, self.row_offsets, self.col_perm, self.col_rows,
-                    self.col_cols, self.col_offsets) if x is not None)
+                    self.col_cols, self.col_offsets, self.row_to_col) if x is not None)
+
+    def with_vals(self, vals) -> "SnackCOO":
+        """The same structure (and value order) over other values."""
+        return SnackCOO(self.out_features, self.in_features, self.rows, self.cols, vals, self.row_offsets,
+                        self.col_perm, self.col_rows, self.col_cols, self.col_offsets, self.row_to_col)
+
+    def to_column_order(self, stream=None) -> "SnackCOO":
+        """This weight with its values in column-view order (new ``vals`` and ``row_to_col``
+        tensors; the structure arrays are shared).  dW outputs for it come in the same order."""
+        import torch
+        if self.column_order:
+            return self
+        if self.col_perm is None:
+            raise ValueError("the column view is required")
+        rtc = snack_coo_invert_perm(self.col_perm, stream=stream)
+        vals = snack_coo_gather_f32(self.vals, self.col_perm, stream=stream)
+        W = self.with_vals(vals)
+        W.row_to_col = rtc
+        return W
+
+    def to_row_order(self, stream=None) -> "SnackCOO":
+        """This weight with its values in row (triple) order."""
+        if not self.column_order:
+            return self
+        vals = snack_coo_gather_f32(self.vals, self.row_to_col, stream=stream)
+        W = self.with_vals(vals)
+        W.row_to_col = None
+        return W
 
 
 _ws_cache = {}
@@ -349,6 +390,32 @@ def snack_coo_topology_update_device(W: SnackCOO, n_prune: int, seed: int, works
                                                ws.numel() * ws.element_size(), _stream_handle(dev, stream))
     _check(st, "snack_coo_topology_update_device")
     return SnackCOO(O, I, rows, cols, vals, row_offsets, col_perm, col_rows, col_cols, col_offsets), int(trials.value)
+
+
+def snack_coo_invert_perm(perm, out=None, stream=None):
+    """inv[perm[j]] = j on the device (int32); perm must be a permutation of 0..n-1."""
+    import torch
+    if perm.dtype != torch.int32 or not perm.is_cuda or not perm.is_contiguous():
+        raise ValueError("perm must be a contiguous int32 device tensor")
+    inv = out if out is not None else torch.empty_like(perm)
+    st = _lib.snack_coo_invert_perm(ctypes.c_void_p(perm.data_ptr()), perm.numel(), ctypes.c_void_p(inv.data_ptr()),
+                                    _stream_handle(perm.device, stream))
+    _check(st, "snack_coo_invert_perm")
+    return inv
+
+
+def snack_coo_gather_f32(src, idx, out=None, stream=None):
+    """dst[j] = src[idx[j]] on the device (float32 values, int32 indices)."""
+    import torch
+    if src.dtype != torch.float32 or idx.dtype != torch.int32 or not src.is_cuda or not idx.is_cuda:
+        raise ValueError("src must be float32 and idx int32, both on the device")
+    if not src.is_contiguous() or not idx.is_contiguous():
+        raise ValueError("src and idx must be contiguous")
+    dst = out if out is not None else torch.empty(idx.numel(), dtype=torch.float32, device=src.device)
+    st = _lib.snack_coo_gather_f32(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(idx.data_ptr()), idx.numel(),
+                                   ctypes.c_void_p(dst.data_ptr()), _stream_handle(src.device, stream))
+    _check(st, "snack_coo_gather_f32")
+    return dst
 
 
 def snack_coo_set_probe(start_event=None, stop_event=None):

@@ -611,7 +611,9 @@ __device__ int wave_lower_bound(const int32_t *__restrict__ a, int lo, int hi, i
 // entry's row-order position).  The window holds, per entry, the dY row as a 32-bit
 // float4 offset, the value and that position; lanes past the range point at dY's zero row.
 //
-// NB == 1: a workgroup owns 4 consecutive columns and writes dX directly.
+// NB == 1: a workgroup owns 4 consecutive columns and writes dX directly.  COLV (values kept in
+// column-view order): the value and dW position of column-view entry j are j itself, so both
+// are read and written coalesced and col_perm is not read.
 // NB == kXcds: the rows are cut into 8 bands of about nnz/8 entries each, and workgroup g
 // takes band g % 8 of columns 4*(g/8) .. +3.  Under round-robin dispatch band b then runs
 // on XCD b alone, walking the columns in order: the dY rows, vals and dW positions that
@@ -619,7 +621,7 @@ __device__ int wave_lower_bound(const int32_t *__restrict__ a, int lo, int hi, i
 // of columns, so they are completed in L2 instead of being written back piecemeal.  Each
 // wave writes its band's share of dX[., i] as a feature-major row of part[b]; a second
 // kernel adds the bands in order.
-template <int BT, int Q, int NB, typename OutT>
+template <int BT, int Q, int NB, typename OutT, bool COLV = false>
 __global__ __launch_bounds__(kBlock) void colbwd_kernel(
     int64_t I, const int32_t *__restrict__ coffs, const int32_t *__restrict__ crows,
     const int32_t *__restrict__ cperm, const float *__restrict__ vals, const float *__restrict__ xt,
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
         int mo = zoff, mp = 0;
         float mv = 0.f;
         if (first + lane < end) {
-            mp = cperm[first + lane];
+            mp = COLV ? first + lane : cperm[first + lane];
             mo = crows[first + lane] * B4;
             mv = vals[mp];
         }
@@ -709,7 +711,7 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
                 mp = 0;
                 mv = 0.f;
                 if (nb + lane < end) {
-                    mp = cperm[nb + lane];
+                    mp = COLV ? nb + lane : cperm[nb + lane];
                     mo = crows[nb + lane] * B4;
                     mv = vals[mp];
                 }
@@ -1583,13 +1585,14 @@ inline int pow2_at_least(int64_t x) {
 
 // nout = outputs per batch row; scatter_ok: the caller can run the scatter
 // mapping (input gradient: row-order entries, outputs indexed by column).
+// (values in column order are read from a gathered copy in the workspace, which is aligned)
 bool vec16(const snack_coo_desc *W) {
-    return reinterpret_cast<uintptr_t>(W->cols) % 16 == 0 && reinterpret_cast<uintptr_t>(W->vals) % 16 == 0;
+    return reinterpret_cast<uintptr_t>(W->cols) % 16 == 0 &&
+           (W->row_to_col || reinterpret_cast<uintptr_t>(W->vals) % 16 == 0);
 }
 
-// aligned16: cols and vals are 16-byte aligned (the batch-1 private-copy kernel loads 4 entries at once)
-SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok,
-                   bool aligned16 = false) {
+SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok,
+                       bool aligned16) {
     SpmmPlan p{};
     p.direct = (B == 1 && dtype == SNACK_F32);
     // batch 1, rows averaging >= 32 entries: stream cols and vals, rows from row_offsets,
@@ -1669,14 +1672,33 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
     if (p.mapping == kSegscan) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B));
     p.off_tail = at;
     if (p.mapping == kSegscan) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B));
-    // the input gradient over the column view reads vals through the permutation once per batch
-    // tile; with 4 or more tiles on a large layer they are gathered into column order once, so
-    // every tile reads them coalesced and long keys split over 4 waves (one tile: the gather costs
-    // more than it saves)
-    p.cvals = scatter_ok && p.mapping == kRowwave && ceil_div(B, 4 * p.bt * p.q) >= 4 && nnz >= kLargeBatchMinNnz;
-    p.off_cvals = at;
-    if (p.cvals) at = align_up(at + sizeof(float) * static_cast<size_t>(nnz));
     p.total = at;
+    return p;
+}
+
+// Appends n floats of workspace for values gathered into the order of the walk (off_cvals).
+void add_cvals(SpmmPlan &p, int64_t n) {
+    p.cvals = true;
+    p.off_cvals = align_up(p.total);
+    p.total = align_up(p.off_cvals + sizeof(float) * static_cast<size_t>(n));
+}
+
+// aligned16: cols and vals are 16-byte aligned (the batch-1 private-copy kernel loads 4 entries at once).
+// colvals: the values are stored in column-view order (snack_coo_desc.row_to_col != NULL).
+SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok,
+                   bool aligned16 = false, bool colvals = false) {
+    SpmmPlan p = plan_spmm_map(nnz, opnd_rows, nout, B, dtype, scatter_ok, aligned16);
+    // mappings that walk the row order with the values read in place (batch 1 and the small-batch
+    // scatter) take column-order values gathered into row order first
+    if (colvals && nnz > 0 && (p.mapping == kCsr1 || p.mapping == kCsr1Priv || p.mapping == kScatter))
+        add_cvals(p, nnz);
+    // the rowwave walks read the values through a permutation -- the input gradient with values in
+    // row order, the forward with values in column order -- once per batch tile; with 4 or more
+    // tiles on a large layer they are gathered into the walk's order once, so every tile reads them
+    // coalesced (one tile: the gather costs more than it saves)
+    else if (scatter_ok != colvals && p.mapping == kRowwave && ceil_div(B, 4 * p.bt * p.q) >= 4 &&
+             nnz >= kLargeBatchMinNnz)
+        add_cvals(p, nnz);
     return p;
 }
 
@@ -1688,10 +1710,13 @@ struct SddmmPlan {
     int bt, vw;
     int64_t steps, waves, per_wave;
     bool x_direct, dy_direct;
+    size_t off_dw;       // row-order dW staging (values in column order)
     size_t off_x, off_dy, total;
 };
 
-SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
+// colvals: dW goes out in column-view order; the kernels write it in row order to the
+// workspace (off_dw) and a gather through col_perm reorders it.
+SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool colvals = false) {
     SddmmPlan p{};
     const int64_t target_waves = 8192;
     if (B >= 16 && B % 4 == 0) {
@@ -1742,6 +1767,8 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype) {
     if (!p.x_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * B));
     p.off_dy = at;
     if (!p.dy_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * B));
+    p.off_dw = at;
+    if (colvals && nnz > 0) at = align_up(at + sizeof(float) * static_cast<size_t>(nnz));
     p.total = at;
     return p;
 }
@@ -1775,7 +1802,7 @@ int64_t band_min_nnz() {
     return SNACK_BAND_MIN_NNZ;
 }
 
-BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool aligned16) {
+BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool aligned16, bool colvals = false) {
     BwdPlan p{};
     if (nnz > 0 && B >= 4 && B % 4 == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
         // B = 4*BT*Q: BT lanes per slot (the largest power of two <= 16 that leaves Q <= 4
@@ -1785,8 +1812,9 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
                 p.fused = true;
                 p.bt = bt;
                 p.q = static_cast<int>(B / (4 * bt));
-                // row bands (one per XCD) once the triple is large enough to spill L2
-                p.nb = nnz >= band_min_nnz() ? kXcds : 1;
+                // row bands (one per XCD) once the triple is large enough to spill L2; values in
+                // column order are read and written in walk order, and the bands only add waves
+                p.nb = !colvals && nnz >= band_min_nnz() ? kXcds : 1;
                 break;
             }
         }
@@ -1801,7 +1829,8 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
         if (p.nb > 1) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nb * I * B));
         p.total = at;
     } else {
-        p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true, aligned16).total, plan_sddmm(nnz, O, I, B, dtype).total);
+        p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals).total,
+                           plan_sddmm(nnz, O, I, B, dtype, colvals).total);
     }
     return p;
 }
@@ -1822,9 +1851,10 @@ int check_desc(const snack_coo_desc *W, bool need_colview, const char *who) {
     if (nnz > 0 && (!W->rows || !W->cols || !W->vals))
         return fail(SNACK_ERR_NULL, "%s: rows, cols and vals are required", who);
     if (!W->row_offsets) return fail(SNACK_ERR_NULL, "%s: row_offsets is required", who);
-    if (need_colview && (!W->col_offsets || (nnz > 0 && (!W->col_perm || !W->col_rows || !W->col_cols))))
-        return fail(SNACK_ERR_NULL, "%s: the column view (col_perm, col_rows, col_cols, col_offsets) is required",
-                    who);
+    if ((need_colview || W->row_to_col) &&
+        (!W->col_offsets || (nnz > 0 && (!W->col_perm || !W->col_rows || !W->col_cols))))
+        return fail(SNACK_ERR_NULL, "%s: the column view (col_perm, col_rows, col_cols, col_offsets) is required%s",
+                    who, W->row_to_col ? " with values in column order" : "");
     return SNACK_OK;
 }
 
@@ -1906,6 +1936,13 @@ __global__ __launch_bounds__(kBlock) void gather_vals_kernel(const int32_t *__re
     if (j < n) out[j] = vals[perm[j]];
 }
 
+int launch_gather(const int32_t *idx, const float *src, int64_t n, float *dst, hipStream_t st) {
+    if (n == 0) return SNACK_OK;
+    hipLaunchKernelGGL(gather_vals_kernel, dim3(static_cast<unsigned>(ceil_div(n, kBlock))), dim3(kBlock), 0, st,
+                       idx, src, n, dst);
+    return check_hip("gather_vals_kernel");
+}
+
 // The gather-reduce shared by the forward (row order) and the input gradient
 // (column view).  nkeys = number of outputs per batch row; offs [nkeys+1].
 template <typename OutT>
@@ -1972,11 +2009,12 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
         return 0;
     }
     const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+    const bool cv = W->row_to_col != nullptr;
     switch (op) {
-        case SNACK_OP_FWD: return plan_spmm(nnz, I, O, batch, act_dtype, false).total;
-        case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W)).total;
-        case SNACK_OP_GRAD_WEIGHT: return plan_sddmm(nnz, O, I, batch, act_dtype).total;
-        case SNACK_OP_BWD: return plan_bwd(nnz, O, I, batch, act_dtype, vec16(W)).total;
+        case SNACK_OP_FWD: return plan_spmm(nnz, I, O, batch, act_dtype, false, false, cv).total;
+        case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W), cv).total;
+        case SNACK_OP_GRAD_WEIGHT: return plan_sddmm(nnz, O, I, batch, act_dtype, cv).total;
+        case SNACK_OP_BWD: return plan_bwd(nnz, O, I, batch, act_dtype, vec16(W), cv).total;
         default: fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown op %d", op); return 0;
     }
 }
@@ -1995,11 +2033,19 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         if (batch == 0 || O == 0) return snack::ok();
         if (I > 0) { if (int s = check_act(X, act_dtype, "X", who)) return s; }
         if (int s = check_act(Y, act_dtype, "Y", who)) return s;
-        const SpmmPlan p = plan_spmm(nnz, I, O, batch, act_dtype, false);
+        const SpmmPlan p = plan_spmm(nnz, I, O, batch, act_dtype, false, false, W->row_to_col != nullptr);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
         char *ws = static_cast<char *>(workspace);
+        // the row walk reads values in column order through row_to_col
+        const float *vals = W->vals;
+        const int32_t *vperm = W->row_to_col;
         if (p.mapping == kCsr1) {
+            if (vperm) {
+                float *cv = reinterpret_cast<float *>(ws + p.off_cvals);
+                if (int s = launch_gather(vperm, vals, nnz, cv, st)) return s;
+                vals = cv;
+            }
             float *head = reinterpret_cast<float *>(ws + p.off_head);
             float *tail = reinterpret_cast<float *>(ws + p.off_tail);
             const bool staged = I <= kStageMaxI;
@@ -2010,7 +2056,7 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
                       ch = static_cast<int>(p.chunk), nc = static_cast<int>(p.nchunks);
 #define SNACK_CSR1_FWD(T, TH)                                                                                   \
     hipLaunchKernelGGL((csr1_fwd_kernel<T, T, TH>), grid, dim3(TH), lds, st, o, in, nz, ch, nc, W->row_offsets,    \
-                       W->cols, W->vals, static_cast<const T *>(X), bias, static_cast<T *>(Y), head, tail)
+                       W->cols, vals, static_cast<const T *>(X), bias, static_cast<T *>(Y), head, tail)
             probe(true, st);
             if (act_dtype == SNACK_F32) {
                 if (staged) SNACK_CSR1_FWD(float, kStageThreads);
@@ -2040,10 +2086,10 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         }
         int s;
         if (act_dtype == SNACK_F32)
-            s = run_spmm<float>(p, O, nnz, W->rows, W->row_offsets, W->cols, W->vals, nullptr, xt, I, batch, bias,
+            s = run_spmm<float>(p, O, nnz, W->rows, W->row_offsets, W->cols, vals, vperm, xt, I, batch, bias,
                                 static_cast<float *>(Y), ws, st);
         else
-            s = run_spmm<bf16_t>(p, O, nnz, W->rows, W->row_offsets, W->cols, W->vals, nullptr, xt, I, batch, bias,
+            s = run_spmm<bf16_t>(p, O, nnz, W->rows, W->row_offsets, W->cols, vals, vperm, xt, I, batch, bias,
                                  static_cast<bf16_t *>(Y), ws, st);
         return s ? s : snack::ok();
     } catch (...) {
@@ -2077,9 +2123,18 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             if (int s = check_hip("bias_grad_kernel")) return s;
         }
         if (batch == 0 || I == 0) return snack::ok();
-        const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W));
+        const bool colvals = W->row_to_col != nullptr;
+        const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W), colvals);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
+        // row walks (batch-1 private copies, small-batch scatter) read values in row order: values
+        // kept in column order are gathered into row order first
+        const float *rvals = W->vals;
+        if (colvals && (p.mapping == kCsr1Priv || p.mapping == kScatter)) {
+            float *cv = reinterpret_cast<float *>(ws + p.off_cvals);
+            if (int s = launch_gather(W->row_to_col, W->vals, nnz, cv, st)) return s;
+            rvals = cv;
+        }
         if (p.mapping == kCsr1Priv) {
             float *partial = reinterpret_cast<float *>(ws + p.off_head);
             const size_t lds = sizeof(float) * static_cast<size_t>(kPrivWaves * I);
@@ -2099,10 +2154,10 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             probe(true, st);
             if (act_dtype == SNACK_F32)
                 hipLaunchKernelGGL(csr1_dxpriv_kernel<float>, grid, dim3(kPrivWaves * kWave), lds, st, o, in, nz, ch,
-                                   nc, W->row_offsets, W->cols, W->vals, static_cast<const float *>(dY), partial);
+                                   nc, W->row_offsets, W->cols, rvals, static_cast<const float *>(dY), partial);
             else
                 hipLaunchKernelGGL(csr1_dxpriv_kernel<bf16_t>, grid, dim3(kPrivWaves * kWave), lds, st, o, in, nz, ch,
-                                   nc, W->row_offsets, W->cols, W->vals, static_cast<const bf16_t *>(dY), partial);
+                                   nc, W->row_offsets, W->cols, rvals, static_cast<const bf16_t *>(dY), partial);
             probe(false, st);
             if (int s = check_hip("csr1_dxpriv_kernel")) return s;
             const dim3 rgrid(static_cast<unsigned>(ceil_div(I, kWave)));
@@ -2122,11 +2177,11 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             if (act_dtype == SNACK_F32)
                 hipLaunchKernelGGL(dx_scatter_kernel<float>, dim3(static_cast<unsigned>(p.nchunks)),
                                    dim3(kScatterThreads), lds, st, nnz, p.chunk, O, I, batch, W->rows, W->cols,
-                                   W->vals, static_cast<const float *>(dY), partial);
+                                   rvals, static_cast<const float *>(dY), partial);
             else
                 hipLaunchKernelGGL(dx_scatter_kernel<bf16_t>, dim3(static_cast<unsigned>(p.nchunks)),
                                    dim3(kScatterThreads), lds, st, nnz, p.chunk, O, I, batch, W->rows, W->cols,
-                                   W->vals, static_cast<const bf16_t *>(dY), partial);
+                                   rvals, static_cast<const bf16_t *>(dY), partial);
             probe(false, st);
             if (int s = check_hip("dx_scatter_kernel")) return s;
             const int64_t n = batch * I;
@@ -2146,12 +2201,14 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st)) return s;
             dyt = dst;
         }
+        // the column walk reads values in row order through col_perm, values in column order in place
+        const int32_t *vperm = colvals ? nullptr : W->col_perm;
         int s;
         if (act_dtype == SNACK_F32)
-            s = run_spmm<float>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt, O,
+            s = run_spmm<float>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, vperm, dyt, O,
                                 batch, nullptr, static_cast<float *>(dX), ws, st);
         else
-            s = run_spmm<bf16_t>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt, O,
+            s = run_spmm<bf16_t>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, vperm, dyt, O,
                                  batch, nullptr, static_cast<bf16_t *>(dX), ws, st);
         return s ? s : snack::ok();
     } catch (...) {
@@ -2160,7 +2217,7 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
 }
 
 extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch,
-                                     int act_dtype, float *dW, void *workspace, size_t workspace_bytes,
+                                     int act_dtype, float *dW_out, void *workspace, size_t workspace_bytes,
                                      void *hip_stream) {
     try {
         const char *who = "snack_coo_grad_weight";
@@ -2171,20 +2228,30 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
         if (nnz == 0) return snack::ok();
-        if (!dW) return fail(SNACK_ERR_NULL, "%s: dW is NULL", who);
-        if (reinterpret_cast<uintptr_t>(dW) % 4) return fail(SNACK_ERR_ALIGN, "%s: dW misaligned", who);
+        if (!dW_out) return fail(SNACK_ERR_NULL, "%s: dW is NULL", who);
+        if (reinterpret_cast<uintptr_t>(dW_out) % 4) return fail(SNACK_ERR_ALIGN, "%s: dW misaligned", who);
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
         if (batch == 0) {
             hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>(ceil_div(nnz, kBlock))), dim3(kBlock), 0,
-                               st, dW, nnz);
+                               st, dW_out, nnz);
             if (int s = check_hip("zero_kernel")) return s;
             return snack::ok();
         }
         if (int s = check_act(X, act_dtype, "X", who)) return s;
         if (int s = check_act(dY, act_dtype, "dY", who)) return s;
-        const SddmmPlan p = plan_sddmm(nnz, O, I, batch, act_dtype);
+        const bool colvals = W->row_to_col != nullptr;
+        const SddmmPlan p = plan_sddmm(nnz, O, I, batch, act_dtype, colvals);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
+        // the kernels write dW in row order; with values in column order into the workspace, and
+        // finish() gathers it into column order through col_perm
+        float *dW = colvals ? reinterpret_cast<float *>(ws + p.off_dw) : dW_out;
+        auto finish = [&]() -> int {
+            if (colvals) {
+                if (int s = launch_gather(W->col_perm, dW, nnz, dW_out, st)) return s;
+            }
+            return snack::ok();
+        };
         if (p.csr1) {
             const bool staged = I <= kStageMaxI;
             const int threads = staged ? kStageThreads : kBlock;
@@ -2206,7 +2273,7 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
 #undef SNACK_CSR1_DW
             probe(false, st);
             if (int s = check_hip("csr1_dw_kernel")) return s;
-            return snack::ok();
+            return finish();
         }
         const float *xt = static_cast<const float *>(X);
         const float *dyt = static_cast<const float *>(dY);
@@ -2297,7 +2364,7 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
         }
         probe(false, st);
         if (int s = check_hip("sddmm_kernel")) return s;
-        return snack::ok();
+        return finish();
     } catch (...) {
         return fail(SNACK_ERR_INTERNAL, "snack_coo_grad_weight: unexpected exception");
     }
@@ -2305,42 +2372,34 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
 
 namespace {
 
-template <typename OutT, int BT, int NB>
+template <typename OutT, int BT, int NB, bool COLV>
 void launch_colbwd_q(int q, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W, const float *xt,
                      const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part) {
     const int nnz = static_cast<int>(W->nnz);
-    if (q == 1)
-        hipLaunchKernelGGL((colbwd_kernel<BT, 1, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
-                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
-                           part);
-    else if (q == 2)
-        hipLaunchKernelGGL((colbwd_kernel<BT, 2, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
-                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
-                           part);
-    else if (q == 3)
-        hipLaunchKernelGGL((colbwd_kernel<BT, 3, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
-                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
-                           part);
-    else
-        hipLaunchKernelGGL((colbwd_kernel<BT, 4, NB, OutT>), grid, dim3(kBlock), 0, st, I, W->col_offsets,
-                           W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz,
-                           part);
+#define SNACK_COLBWD(QV)                                                                                            \
+    hipLaunchKernelGGL((colbwd_kernel<BT, QV, NB, OutT, COLV>), grid, dim3(kBlock), 0, st, I, W->col_offsets,     \
+                       W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz, part)
+    if (q == 1) SNACK_COLBWD(1);
+    else if (q == 2) SNACK_COLBWD(2);
+    else if (q == 3) SNACK_COLBWD(3);
+    else SNACK_COLBWD(4);
+#undef SNACK_COLBWD
 }
 
-template <typename OutT, int NB>
+template <typename OutT, int NB, bool COLV = false>
 void launch_colbwd_nb(const BwdPlan &p, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W,
                       const float *xt, const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part) {
     if (p.bt == 16)
-        launch_colbwd_q<OutT, 16, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 16, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
     else if (p.bt == 8)
-        launch_colbwd_q<OutT, 8, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 8, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
     else if (p.bt == 4)
-        launch_colbwd_q<OutT, 4, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 4, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
 #if SNACK_FUSED_MIN_BT < 4
     else if (p.bt == 2)
-        launch_colbwd_q<OutT, 2, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 2, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
     else
-        launch_colbwd_q<OutT, 1, NB>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 1, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
 #endif
 }
 
@@ -2348,9 +2407,13 @@ template <typename OutT>
 int launch_colbwd(const BwdPlan &p, hipStream_t st, int64_t I, const snack_coo_desc *W, const float *xt,
                   const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part) {
     if (p.nb == 1) {
-        // one wave per column, 4 consecutive columns per workgroup, each XCD an eighth of the columns
+        // one wave per column, 4 consecutive columns per workgroup, each XCD an eighth of the columns;
+        // values in column order are read and dW written at the walk's own positions
         const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(I, kWavesPerBlock))));
-        launch_colbwd_nb<OutT, 1>(p, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        if (W->row_to_col)
+            launch_colbwd_nb<OutT, 1, true>(p, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        else
+            launch_colbwd_nb<OutT, 1>(p, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
         return check_hip("colbwd_kernel");
     }
     const dim3 grid(static_cast<unsigned>(kXcds * ceil_div(I, kWavesPerBlock)));
@@ -2374,7 +2437,7 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
         if (batch < 0 || batch > kMaxBatch)
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
-        const BwdPlan p = plan_bwd(nnz, O, I, batch, act_dtype, vec16(W));
+        const BwdPlan p = plan_bwd(nnz, O, I, batch, act_dtype, vec16(W), W->row_to_col != nullptr);
         if (!p.fused) {
             if (int s = snack_coo_bwd_input(W, dY, batch, act_dtype, dX, db, workspace, workspace_bytes, hip_stream))
                 return s;
@@ -2426,4 +2489,43 @@ extern "C" int snack_coo_set_probe(void *start_event, void *stop_event) {
     g_probe_start = static_cast<hipEvent_t>(start_event);
     g_probe_stop = static_cast<hipEvent_t>(stop_event);
     return snack::ok();
+}
+
+namespace {
+__global__ __launch_bounds__(kBlock) void invert_perm_kernel(const int32_t *__restrict__ perm, int64_t n,
+                                                             int32_t *__restrict__ inv) {
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (j < n) inv[perm[j]] = static_cast<int32_t>(j);
+}
+}  // namespace
+
+extern "C" int snack_coo_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, void *hip_stream) {
+    try {
+        if (n < 0 || n > 2147483647LL) return fail(SNACK_ERR_SHAPE, "snack_coo_invert_perm: bad length %lld", (long long)n);
+        if (n == 0) return snack::ok();
+        if (!perm || !inv) return fail(SNACK_ERR_NULL, "snack_coo_invert_perm: perm and inv are required");
+        if (reinterpret_cast<uintptr_t>(perm) % 4 || reinterpret_cast<uintptr_t>(inv) % 4)
+            return fail(SNACK_ERR_ALIGN, "snack_coo_invert_perm: misaligned array");
+        hipLaunchKernelGGL(invert_perm_kernel, dim3(static_cast<unsigned>(ceil_div(n, kBlock))), dim3(kBlock), 0,
+                           static_cast<hipStream_t>(hip_stream), perm, n, inv);
+        if (int s = check_hip("invert_perm_kernel")) return s;
+        return snack::ok();
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "snack_coo_invert_perm: unexpected exception");
+    }
+}
+
+extern "C" int snack_coo_gather_f32(const float *src, const int32_t *idx, int64_t n, float *dst, void *hip_stream) {
+    try {
+        if (n < 0 || n > 2147483647LL) return fail(SNACK_ERR_SHAPE, "snack_coo_gather_f32: bad length %lld", (long long)n);
+        if (n == 0) return snack::ok();
+        if (!src || !idx || !dst) return fail(SNACK_ERR_NULL, "snack_coo_gather_f32: src, idx and dst are required");
+        if (reinterpret_cast<uintptr_t>(src) % 4 || reinterpret_cast<uintptr_t>(idx) % 4 ||
+            reinterpret_cast<uintptr_t>(dst) % 4)
+            return fail(SNACK_ERR_ALIGN, "snack_coo_gather_f32: misaligned array");
+        if (int s = launch_gather(idx, src, n, dst, static_cast<hipStream_t>(hip_stream))) return s;
+        return snack::ok();
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "snack_coo_gather_f32: unexpected exception");
+    }
 }

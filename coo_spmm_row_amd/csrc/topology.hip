@@ -314,6 +314,9 @@ extern "C" int snack_coo_topology_update_device(const snack_coo_desc *W, int64_t
     try {
         const char *who = "topology_update_device";
         if (!W) return fail(SNACK_ERR_NULL, "%s: NULL descriptor", who);
+        if (W->row_to_col)
+            return fail(SNACK_ERR_UNSORTED, "%s: values in column order (row_to_col set); gather them into row "
+                        "order first (snack_coo_gather_f32 with row_to_col)", who);
         const int64_t O = W->out_features, I = W->in_features, n = W->nnz;
         if (O <= 0 || I <= 0 || n < 0 || n > O * I || n_prune < 0 || n_prune > n || n > 2147483647LL)
             return fail(SNACK_ERR_SHAPE, "%s: bad sizes (O=%lld I=%lld nnz=%lld n_prune=%lld)", who, (long long)O,

@@ -14,6 +14,11 @@ Readings where the pages leave a step open:
   * prune-and-regrow (Appendix G) keeps the number of stored entries; regrown entries
     start at 0, and optimizer state kept per entry no longer lines up with the new
     support (the caller resets it).
+
+value_order="col" keeps ``vals`` (and so its gradient and any per-entry optimizer state) in
+column-view order for the layer's whole life: the backward pass then reads the values and writes
+their gradient contiguously, and the forward pass reads the values through ``row_to_col`` instead.
+The products are the same; save_npz always writes row (triple) order.
 """
 from __future__ import annotations
 
@@ -25,10 +30,11 @@ import torch
 from torch import nn
 
 from . import (SnackCOO, snack_coo_build, snack_coo_bwd, snack_coo_bwd_input, snack_coo_fwd,
-               snack_coo_grad_weight, snack_coo_init_uniform, snack_coo_topology_update,
+               snack_coo_gather_f32, snack_coo_grad_weight, snack_coo_init_uniform, snack_coo_topology_update,
                snack_coo_topology_update_device)
 
 _STRUCT = ("rows", "cols", "row_offsets", "col_perm", "col_rows", "col_cols", "col_offsets")
+_ORDERS = ("row", "col")
 
 
 class SnackLinearFunction(torch.autograd.Function):
@@ -72,8 +78,11 @@ class SnackLinear(nn.Module):
     """
 
     def __init__(self, in_features: int, out_features: int, sparsity: float = 0.9, bias: bool = True,
-                 seed: int = 0, nnz: Optional[int] = None, device=None):
+                 seed: int = 0, nnz: Optional[int] = None, device=None, value_order: str = "row"):
         super().__init__()
+        if value_order not in _ORDERS:
+            raise ValueError(f"value_order must be one of {_ORDERS}")
+        self.value_order = value_order
         self.in_features, self.out_features = int(in_features), int(out_features)
         cells = self.in_features * self.out_features
         if nnz is None:
@@ -96,11 +105,14 @@ class SnackLinear(nn.Module):
 
     @classmethod
     def from_triple(cls, out_features: int, in_features: int, rows, cols, vals, bias=None,
-                    device=None) -> "SnackLinear":
+                    device=None, value_order: str = "row") -> "SnackLinear":
         """A layer over a given support and values (host arrays in any order; the builder sorts
         them and rejects duplicates), with the given bias or none."""
+        if value_order not in _ORDERS:
+            raise ValueError(f"value_order must be one of {_ORDERS}")
         layer = cls.__new__(cls)
         nn.Module.__init__(layer)
+        layer.value_order = value_order
         layer.in_features, layer.out_features = int(in_features), int(out_features)
         layer._set_topology(rows, cols, vals, device)
         if bias is not None:
@@ -111,16 +123,29 @@ class SnackLinear(nn.Module):
 
     # ---------------------------------------------------------------- structure
     def _set_topology(self, rows, cols, vals, device=None):
+        """Build the sorted triple and column view on the host and move them to `device`; with
+        value_order "col" the values are permuted into column order here (host, set-up only)."""
         built = snack_coo_build(self.out_features, self.in_features, rows, cols, vals, column_view=True)
         if device is None:
             device = self.vals.device if hasattr(self, "vals") else torch.device("cpu")
-        for name in _STRUCT:
-            t = torch.from_numpy(np.ascontiguousarray(built[name])).to(device)
-            if name in self._buffers:
-                self._buffers[name] = t
-            else:
-                self.register_buffer(name, t)
-        v = torch.from_numpy(np.ascontiguousarray(built["vals"])).to(device)
+        v = built["vals"]
+        if self.value_order == "col":
+            cp = built["col_perm"]
+            rtc = np.empty_like(cp)
+            rtc[cp] = np.arange(cp.size, dtype=np.int32)
+            built["row_to_col"] = rtc
+            v = v[cp]
+        for name in _STRUCT + (("row_to_col",) if self.value_order == "col" else ()):
+            self._set_buffer(name, torch.from_numpy(np.ascontiguousarray(built[name])).to(device))
+        self._set_vals(torch.from_numpy(np.ascontiguousarray(v)).to(device))
+
+    def _set_buffer(self, name, t):
+        if name in self._buffers:
+            self._buffers[name] = t
+        else:
+            self.register_buffer(name, t)
+
+    def _set_vals(self, v):
         if "vals" in self._parameters:
             self.vals.data = v
         else:
@@ -133,7 +158,17 @@ class SnackLinear(nn.Module):
     def weight_view(self) -> SnackCOO:
         """The library descriptor over the current tensors (cheap; built per call)."""
         return SnackCOO(self.out_features, self.in_features, self.rows, self.cols, self.vals.detach(),
-                        self.row_offsets, self.col_perm, self.col_rows, self.col_cols, self.col_offsets)
+                        self.row_offsets, self.col_perm, self.col_rows, self.col_cols, self.col_offsets,
+                        self._buffers.get("row_to_col") if self.value_order == "col" else None)
+
+    def row_order_vals(self) -> torch.Tensor:
+        """The values in row (triple) order, whatever the layer keeps."""
+        v = self.vals.detach()
+        if self.value_order != "col":
+            return v
+        if v.is_cuda:
+            return snack_coo_gather_f32(v, self.row_to_col)
+        return torch.from_numpy(v.numpy()[self.row_to_col.numpy()])
 
     # ---------------------------------------------------------------- compute
     def forward(self, X: torch.Tensor) -> torch.Tensor:
@@ -155,13 +190,16 @@ class SnackLinear(nn.Module):
         if on_device is None:
             on_device = self.vals.is_cuda
         if on_device:
-            W, trials = snack_coo_topology_update_device(self.weight_view(), n_prune, int(seed))
+            W, trials = snack_coo_topology_update_device(self.weight_view().to_row_order(), n_prune, int(seed))
+            if self.value_order == "col":
+                W = W.to_column_order()
+                self._set_buffer("row_to_col", W.row_to_col)
             for name in _STRUCT:
                 self._buffers[name] = getattr(W, name)
             self.vals.data = W.vals
             return trials
         out = snack_coo_topology_update(self.out_features, self.in_features, self.rows.cpu().numpy(),
-                                        self.cols.cpu().numpy(), self.vals.detach().cpu().numpy(), n_prune,
+                                        self.cols.cpu().numpy(), self.row_order_vals().cpu().numpy(), n_prune,
                                         int(seed))
         self._set_topology(out["rows"], out["cols"], out["vals"], self.vals.device)
         return out["trials"]
@@ -171,19 +209,20 @@ class SnackLinear(nn.Module):
         """The COO triple (and bias) as an .npz file (plain arrays, no pickles)."""
         arrays = {"shape": np.array([self.out_features, self.in_features], np.int64),
                   "rows": self.rows.cpu().numpy(), "cols": self.cols.cpu().numpy(),
-                  "vals": self.vals.detach().cpu().numpy()}
+                  "vals": self.row_order_vals().cpu().numpy()}
         if self.bias is not None:
             arrays["bias"] = self.bias.detach().cpu().numpy()
         np.savez(path, **arrays)
 
     @classmethod
-    def load_npz(cls, path, device=None) -> "SnackLinear":
+    def load_npz(cls, path, device=None, value_order: str = "row") -> "SnackLinear":
         with np.load(path, allow_pickle=False) as f:
             O, I = (int(x) for x in f["shape"])
             return cls.from_triple(O, I, f["rows"], f["cols"], f["vals"],
-                                   f["bias"] if "bias" in f.files else None, device)
+                                   f["bias"] if "bias" in f.files else None, device, value_order)
 
     def extra_repr(self) -> str:
         cells = self.in_features * self.out_features
         return (f"in_features={self.in_features}, out_features={self.out_features}, nnz={self.nnz} "
-                f"(sparsity {1.0 - self.nnz / max(cells, 1):.4f}), bias={self.bias is not None}")
+                f"(sparsity {1.0 - self.nnz / max(cells, 1):.4f}), bias={self.bias is not None}, "
+                f"value_order={self.value_order}")

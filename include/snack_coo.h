@@ -80,8 +80,17 @@ enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2, SNACK
  *                             (col, row) order (Table 7's CSC order)
  *   col_rows, col_cols [nnz]  rows[col_perm[j]], cols[col_perm[j]]
  *   col_offsets        [I+1]  col_offsets[c] = number of entries with col < c
- * The column view is needed by snack_coo_bwd_input and snack_coo_bwd only
- * (NULL elsewhere). */
+ *   row_to_col         [nnz]  NULL, or the inverse of col_perm (row_to_col[col_perm[j]] = j;
+ *                             see snack_coo_invert_perm).  Non-NULL selects VALUES IN
+ *                             COLUMN ORDER: vals[j] is the value of column-view entry j
+ *                             (of triple entry col_perm[j]), and every dW output is in the
+ *                             same order (dW[j] for that entry).  The products are the same;
+ *                             only the storage order of vals and dW changes.  It lets the
+ *                             backward pass (a walk over the column view) read vals and
+ *                             write dW contiguously, and moves one permuted read per entry
+ *                             to the forward pass instead.  Requires the column view.
+ * The column view is needed by snack_coo_bwd_input and snack_coo_bwd, and with
+ * row_to_col (NULL elsewhere). */
 typedef struct snack_coo_desc {
     int64_t out_features;
     int64_t in_features;
@@ -94,6 +103,7 @@ typedef struct snack_coo_desc {
     const int32_t *col_rows;
     const int32_t *col_cols;
     const int32_t *col_offsets;
+    const int32_t *row_to_col;
 } snack_coo_desc;
 
 /* Host-side COO builder (Appendix B, Table 7: COO triple, CSR index pointer,
@@ -182,8 +192,9 @@ int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_
  * Algorithm 2): the same result as snack_coo_topology_update on the same
  * triple, n_prune and seed followed by snack_coo_build's column view, bit for
  * bit, computed on the GPU.  Input W: a device triple sorted strictly by
- * (row, col) with its values (as the builder emits; not re-checked), row
- * offsets and column view not needed.  Outputs (device, caller-owned, must not
+ * (row, col) with its values in row order (row_to_col NULL, else
+ * SNACK_ERR_UNSORTED; as the builder emits; not re-checked), row offsets and
+ * column view not needed.  Outputs (device, caller-owned, must not
  * alias W's arrays): rows_out, cols_out, vals_out [nnz], row_offsets_out
  * [O+1], col_perm_out, col_rows_out, col_cols_out [nnz], col_offsets_out
  * [I+1]; trials_out (HOST int64, or NULL) receives Algorithm 2's number of
@@ -237,6 +248,18 @@ int snack_coo_topology_update(int64_t out_features, int64_t in_features, int64_t
                               int32_t *rows_out, int32_t *cols_out, float *vals_out,
                               int32_t *row_offsets_out, int64_t *trials_out);
 
+/* Device helpers for values kept in column order (snack_coo_desc.row_to_col).
+ * All pointers are DEVICE pointers; n < 2^31; the work is enqueued on hip_stream.
+ *   snack_coo_invert_perm: inv[perm[j]] = j for j < n.  perm must be a
+ *     permutation of 0..n-1 (not checked: a repeated or out-of-range index
+ *     writes out of bounds).  With perm = col_perm this gives row_to_col.
+ *   snack_coo_gather_f32: dst[j] = src[idx[j]] for j < n (0 <= idx[j] < length
+ *     of src, not checked).  Row-order values to column order:
+ *     idx = col_perm; back: idx = row_to_col.  dst must not alias src.
+ * Errors: SNACK_ERR_SHAPE (bad n), SNACK_ERR_NULL, SNACK_ERR_ALIGN (4 bytes). */
+int snack_coo_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, void *hip_stream);
+int snack_coo_gather_f32(const float *src, const int32_t *idx, int64_t n, float *dst, void *hip_stream);
+
 /* Timing probe for benchmarks and profilers (not part of the method).  While
  * armed on the calling thread, each device call records `start_event` on its
  * stream immediately before launching its main kernel (the gather-reduce of
@@ -251,7 +274,8 @@ int snack_coo_set_probe(void *start_event, void *stop_event);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *snack_last_error(void);
 
-/* ABI version of this header: 4 (3 added snack_coo_init_uniform, 4 the device topology update). */
+/* ABI version of this header: 5 (3 added snack_coo_init_uniform, 4 the device topology update,
+ * 5 values in column order: snack_coo_desc.row_to_col, snack_coo_invert_perm, snack_coo_gather_f32). */
 int snack_coo_abi_version(void);
 
 #ifdef __cplusplus

@@ -16,7 +16,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(snk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert snk.abi_version() == 4
+    assert snk.abi_version() == 5
 
 
 def test_binding_loads_only_the_in_tree_library():
@@ -94,3 +94,33 @@ def test_banded_backward_workspace_follows_threshold(monkeypatch):
     monkeypatch.setenv("SNACK_COO_BAND_MIN_NNZ", "not a number")  # ignored
     assert lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0) == default
 
+
+
+def test_column_order_values_host_checks_and_workspace():
+    """Values in column order (row_to_col set): every device call then needs the column view, the
+    weight gradient reserves nnz more floats of workspace for its row-order staging, the fused
+    backward drops the row bands, and the device topology update refuses the layout."""
+    lib = snk._lib
+    d = snk._Desc()
+    d.out_features, d.in_features, d.nnz = 300, 200, 5000
+    d.row_offsets = d.rows = d.cols = d.vals = 0x1000  # host-side sizing only: never dereferenced
+    row_dw = lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 64, 0)
+    d.row_to_col = 0x1000
+    assert lib.snack_coo_fwd(ctypes.byref(d), 0x1000, 8, 0, None, 0x2000, 0x10000, 1 << 30, None) == 1
+    assert b"column view" in lib.snack_last_error()
+    d.col_perm = d.col_rows = d.col_cols = d.col_offsets = 0x1000
+    assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 64, 0) >= row_dw + 4 * 5000
+    d.nnz = 1 << 21
+    d.out_features = d.in_features = 4096
+    col_bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
+    d.row_to_col = None
+    row_bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)  # 2^21 entries: banded
+    assert row_bwd - col_bwd >= 8 * 4096 * 64 * 4
+    d.row_to_col = 0x1000
+    ws = lib.snack_coo_topology_workspace_bytes(4096, 4096, 1 << 21, 10)
+    assert lib.snack_coo_topology_update_device(ctypes.byref(d), 10, 0, *([0x1000] * 8), None, 0x10000, ws,
+                                                None) == 11
+    assert lib.snack_coo_invert_perm(None, 4, None, None) == 1
+    assert lib.snack_coo_invert_perm(0x1000, -1, 0x1000, None) == 2
+    assert lib.snack_coo_gather_f32(0x1001, 0x1000, 4, 0x1000, None) == 5
+    assert lib.snack_coo_gather_f32(None, None, 0, None, None) == 0

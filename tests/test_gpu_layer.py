@@ -131,3 +131,36 @@ def test_layer_sgd_reduces_loss_and_save_load_is_exact(tmp_path):
     layer.save_npz(tmp_path / "l.npz")
     back = SnackLinear.load_npz(tmp_path / "l.npz", device=DEV)
     assert torch.equal(back(X), layer(X))
+
+
+@pytest.mark.parametrize("lead", [(16,), (5,), (64,)], ids=["B16", "B5", "B64"])
+def test_column_order_layer_matches_row_order_layer(lead):
+    """value_order="col" gives the same outputs and, permuted by col_perm, the same value gradients;
+    a few SGD steps and a device prune-and-regrow keep both layers equal bit for bit."""
+    say(f"SnackLinear column-order values lead={lead}")
+    row = SnackLinear(300, 200, sparsity=0.9, seed=31).to(DEV)
+    col = SnackLinear(300, 200, sparsity=0.9, seed=31, value_order="col").to(DEV)
+    cp = row.col_perm.long()
+    x_in, _ = acts(800, int(np.prod(lead)), 300)
+    g_in, _ = acts(801, int(np.prod(lead)), 200)
+    X = torch.from_numpy(x_in).to(DEV).reshape(*lead, 300)
+    G = torch.from_numpy(g_in).to(DEV).reshape(*lead, 200)
+    opt_r = torch.optim.SGD(row.parameters(), lr=0.01)
+    opt_c = torch.optim.SGD(col.parameters(), lr=0.01)
+    for step in range(3):
+        Xr, Xc = X.clone().requires_grad_(True), X.clone().requires_grad_(True)
+        Yr, Yc = row(Xr), col(Xc)
+        assert torch.equal(Yr, Yc), step
+        (Yr * G).sum().backward()
+        (Yc * G).sum().backward()
+        assert torch.equal(col.vals.grad, row.vals.grad[cp]), step
+        assert torch.equal(col.bias.grad, row.bias.grad), step
+        check_close(Xc.grad.cpu().numpy(), Xr.grad.cpu().numpy().astype(np.float64), row.nnz / 300, "col dX")
+        opt_r.step(); opt_c.step(); opt_r.zero_grad(); opt_c.zero_grad()
+    assert torch.equal(col.row_order_vals(), row.vals.detach())
+    assert row.prune_and_regrow(0.1, seed=5) == col.prune_and_regrow(0.1, seed=5)
+    assert torch.equal(col.rows, row.rows) and torch.equal(col.col_perm, row.col_perm)
+    assert torch.equal(col.vals.detach(), row.vals.detach()[row.col_perm.long()])
+    assert torch.equal(col.row_to_col[row.col_perm.long()],
+                       torch.arange(row.nnz, dtype=torch.int32, device=DEV))
+    assert torch.equal(row(X), col(X))

@@ -69,3 +69,27 @@ def test_no_cpu_compute_path():
     layer = SnackLinear(20, 10, 0.5)
     with pytest.raises(ValueError, match="device tensor"):
         layer(torch.randn(3, 20))
+
+
+def test_column_order_layer_host_side(tmp_path):
+    """value_order="col": the same support and values, kept in column-view order with row_to_col the
+    inverse of col_perm; host prune-and-regrow and save/load work on row order."""
+    row = SnackLinear(60, 45, 0.8, seed=21)
+    col = SnackLinear(60, 45, 0.8, seed=21, value_order="col")
+    cp = row.col_perm.numpy()
+    assert np.array_equal(col.vals.detach().numpy(), row.vals.detach().numpy()[cp])
+    assert np.array_equal(col.row_to_col.numpy()[cp], np.arange(cp.size))
+    assert torch.equal(col.row_order_vals(), row.vals.detach())
+    assert "value_order=col" in repr(col)
+    col.save_npz(tmp_path / "c.npz")
+    back = SnackLinear.load_npz(tmp_path / "c.npz")  # row order on disk
+    assert torch.equal(back.vals, row.vals)
+    back_c = SnackLinear.load_npz(tmp_path / "c.npz", value_order="col")
+    assert torch.equal(back_c.vals, col.vals) and torch.equal(back_c.row_to_col, col.row_to_col)
+    t_row, t_col = row.prune_and_regrow(0.2, seed=7), col.prune_and_regrow(0.2, seed=7)
+    assert t_row == t_col
+    assert torch.equal(col.rows, row.rows) and torch.equal(col.cols, row.cols)
+    assert torch.equal(col.row_order_vals(), row.vals.detach())
+    assert np.array_equal(col.vals.detach().numpy(), row.vals.detach().numpy()[row.col_perm.numpy()])
+    with pytest.raises(ValueError):
+        SnackLinear(10, 10, value_order="diagonal")
