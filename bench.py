@@ -62,9 +62,10 @@ def algorithmic_bytes(op, nnz, O, I, B, s):
 
 def bwd_fused(B):
     """Whether snack_coo_bwd runs its single column-view pass at this batch (the library's
-    rule: B = 4*BT*Q with BT a power of two <= 16 and Q <= 4 float4s per lane); otherwise it
-    runs the two gradients one after the other.  Used to label timings only."""
-    return B > 0 and B % 4 == 0 and any(B % (4 * bt) == 0 and B // (4 * bt) <= 4 for bt in (16, 8, 4, 2, 1))
+    rule: batches 2..256 are padded with zero columns to a tile of 4*BT*Q columns, BT a power of
+    two <= 16 and Q <= 4, and run fused; batch 1 and larger batches run the two gradients one
+    after the other).  Used to label timings only."""
+    return 2 <= B <= 256
 
 
 def column_order_step(layer, K):

@@ -142,8 +142,8 @@ __device__ __forceinline__ int64_t xcd_block() {
 }
 
 // ---------------------------------------------------------------- layout
-// in [B][F] (batch-major, fp32 or bf16)  ->  out [F+1][B] fp32 (feature-major), row F
-// zero (gathers of a missing entry point there instead of being masked).
+// in [B][F] (batch-major, fp32 or bf16)  ->  out [F+1][Bp] fp32 (feature-major, Bp >= B; columns
+// B..Bp-1 zero), row F zero (gathers of a missing entry point there instead of being masked).
 // Up to two tensors per launch (blockIdx.z; the backward pass transposes X and dY together).
 // A workgroup moves a tile of 32 features x 64 batch rows through LDS.
 constexpr int kTf = 32, kTb = 64;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__r
                                                                   float *__restrict__ out0, int64_t F0,
                                                                   const InT *__restrict__ in1,
                                                                   float *__restrict__ out1, int64_t F1,
-                                                                  int64_t B) {
+                                                                  int64_t B, int64_t Bp) {
     __shared__ float tile[kTb][kTf + 1];
     const InT *__restrict__ in = blockIdx.z == 0 ? in0 : in1;
     float *__restrict__ out = blockIdx.z == 0 ? out0 : out1;
@@ -164,9 +164,10 @@ __global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__r
     if (f0 >= F && !(blockIdx.x == 0)) return;  // uniform per workgroup, before the barrier
     const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTb;
     const int tx = threadIdx.x % kTf, ty = threadIdx.x / kTf;  // 32 x 8
-    const int nb = static_cast<int>(min<int64_t>(kTb, B - b0));
+    const int nb = static_cast<int>(max<int64_t>(0, min<int64_t>(kTb, B - b0)));
+    const int nbp = static_cast<int>(min<int64_t>(kTb, Bp - b0));  // with the zero columns
     const int nf = static_cast<int>(max<int64_t>(0, min<int64_t>(kTf, F - f0)));
-    if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < nb) out[F * B + b0 + threadIdx.x] = 0.f;
+    if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < nbp) out[F * Bp + b0 + threadIdx.x] = 0.f;
     constexpr int K = kTb / (kBlock / kTf);  // 8 rows per thread
     float v[K];
 #pragma unroll
@@ -177,9 +178,9 @@ __global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__r
 #pragma unroll
     for (int i = 0; i < K; ++i) tile[ty + (kBlock / kTf) * i][tx] = v[i];
     __syncthreads();
-    for (int li = threadIdx.x; li < nf * nb; li += kBlock) {
-        const int ff = li / nb, bb = li % nb;
-        out[(f0 + ff) * B + b0 + bb] = tile[bb][ff];
+    for (int li = threadIdx.x; li < nf * nbp; li += kBlock) {  // rows nb..nbp-1 of the tile are zero
+        const int ff = li / nbp, bb = li % nbp;
+        out[(f0 + ff) * Bp + b0 + bb] = tile[bb][ff];
     }
 }
 
@@ -192,15 +193,15 @@ __device__ __forceinline__ float4 load_act4(const bf16_t *p, int64_t i) {
                        __uint_as_float(u.y & 0xFFFF0000u));
 }
 
-// F and B multiples of 4 (16-byte aligned rows): each thread loads two 4-feature vectors of
-// two batch rows and stores two 4-row vectors of two features, with no divisions.  LDS rows
+// F and Bp multiples of 4 (16-byte aligned rows): each thread loads two 4-feature vectors of
+// two batch rows (zeros past B) and stores two 4-row vectors of two features, with no divisions.  LDS rows
 // are padded to 33 floats: the 4 scalar writes and reads of a vector fall in distinct banks.
 template <typename InT>
 __global__ __launch_bounds__(kBlock) void to_feature_major4_kernel(const InT *__restrict__ in0,
                                                                    float *__restrict__ out0, int64_t F0,
                                                                    const InT *__restrict__ in1,
                                                                    float *__restrict__ out1, int64_t F1,
-                                                                   int64_t B) {
+                                                                   int64_t B, int64_t Bp) {
     __shared__ float tile[kTb][kTf + 1];
     const InT *__restrict__ in = blockIdx.z == 0 ? in0 : in1;
     float *__restrict__ out = blockIdx.z == 0 ? out0 : out1;
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void to_feature_major4_kernel(const InT *__
     if (f0 >= F && !(blockIdx.x == 0)) return;  // uniform per workgroup, before the barrier
     const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTb;
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && b0 + tid < B && tid < kTb) out[F * B + b0 + tid] = 0.f;
+    if (blockIdx.x == 0 && b0 + tid < Bp && tid < kTb) out[F * Bp + b0 + tid] = 0.f;
     // load: thread -> batch row r = tid / 8 (+32), features 4 * (tid % 8) .. +3
     const int lc = 4 * (tid % (kTf / 4)), lr = tid / (kTf / 4);
     float4 v[2];
@@ -233,8 +234,8 @@ __global__ __launch_bounds__(kBlock) void to_feature_major4_kernel(const InT *__
     for (int i = 0; i < 2; ++i) {
         const int ff = sf + 16 * i;
         const int64_t f = f0 + ff, b = b0 + sq;
-        if (f < F && b < B)
-            *reinterpret_cast<float4 *>(out + f * B + b) =
+        if (f < F && b < Bp)
+            *reinterpret_cast<float4 *>(out + f * Bp + b) =
                 make_float4(tile[sq][ff], tile[sq + 1][ff], tile[sq + 2][ff], tile[sq + 3][ff]);
     }
 }
@@ -356,12 +357,13 @@ __global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B,
 // consumed, and keeps U*Q float4 gathers in flight.  Lanes of a chunk past the
 // key's end point at the operand's zero row with value 0, so no step needs a
 // mask.  Slot partial sums are combined by xor shuffles, the WPR waves of a
-// key through LDS.  The operand including its zero row is below 4 GB.
+// key through LDS.  The operand including its zero row is below 4 GB.  B is the operand's batch
+// columns (a multiple of 4; zero columns pad a batch of nbo columns), nbo the columns stored.
 template <int BT, int WPR, int Q, typename OutT>
 __global__ __launch_bounds__(kBlock) void rowwave_kernel(
     int64_t nkeys, const int32_t *__restrict__ offs, const int32_t *__restrict__ gidx,
     const float *__restrict__ vals, const int32_t *__restrict__ perm, const float *__restrict__ opnd, int zero_row,
-    int64_t B, const float *__restrict__ bias, OutT *__restrict__ out, int64_t out_ld) {
+    int64_t B, const float *__restrict__ bias, OutT *__restrict__ out, int64_t out_ld, int64_t nbo) {
     constexpr int S = kWave / BT;
     constexpr int UQ = 8 / Q;
     constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;  // S*U divides 64
@@ -466,10 +468,16 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int64_t c = b0 + 4 * q * BT;
-            store_act(out, (c + 0) * out_ld + r, acc[q].x + bv);
-            store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
-            store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
-            store_act(out, (c + 3) * out_ld + r, acc[q].w + bv);
+            if (c + 3 < nbo) {
+                store_act(out, (c + 0) * out_ld + r, acc[q].x + bv);
+                store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
+                store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
+                store_act(out, (c + 3) * out_ld + r, acc[q].w + bv);
+            } else {  // the last, padded float4 of the batch
+                if (c + 0 < nbo) store_act(out, (c + 0) * out_ld + r, acc[q].x + bv);
+                if (c + 1 < nbo) store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
+                if (c + 2 < nbo) store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
+            }
         }
     }
 }
@@ -626,7 +634,7 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
     int64_t I, const int32_t *__restrict__ coffs, const int32_t *__restrict__ crows,
     const int32_t *__restrict__ cperm, const float *__restrict__ vals, const float *__restrict__ xt,
     const float *__restrict__ dyt, int zero_row, int64_t B, OutT *__restrict__ dX, float *__restrict__ dW,
-    const int32_t *__restrict__ offs, int nnz, float *__restrict__ part) {
+    const int32_t *__restrict__ offs, int nnz, float *__restrict__ part, int64_t nbo) {
     constexpr int S = kWave / BT;
     constexpr int UQ = 8 / Q;                                   // gathers in flight: U*Q float4s
     constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;       // S*U divides 64
@@ -776,12 +784,12 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
     if (cok && e == 0) {
         if constexpr (NB == 1) {
 #pragma unroll
-            for (int q = 0; q < Q; ++q) {
+            for (int q = 0; q < Q; ++q) {  // nbo of the B (padded) batch columns are stored
                 const int64_t b0 = 4 * static_cast<int64_t>(t + q * BT);
-                store_act(dX, (b0 + 0) * I + col, acc[q].x);
-                store_act(dX, (b0 + 1) * I + col, acc[q].y);
-                store_act(dX, (b0 + 2) * I + col, acc[q].z);
-                store_act(dX, (b0 + 3) * I + col, acc[q].w);
+                if (b0 + 0 < nbo) store_act(dX, (b0 + 0) * I + col, acc[q].x);
+                if (b0 + 1 < nbo) store_act(dX, (b0 + 1) * I + col, acc[q].y);
+                if (b0 + 2 < nbo) store_act(dX, (b0 + 2) * I + col, acc[q].z);
+                if (b0 + 3 < nbo) store_act(dX, (b0 + 3) * I + col, acc[q].w);
             }
         } else {
             float4 *__restrict__ p4 = reinterpret_cast<float4 *>(part) + (band * I + col) * B4 + t;
@@ -792,16 +800,16 @@ __global__ __launch_bounds__(kBlock) void colbwd_kernel(
 }
 
 // dX[b][i] = sum over the NB bands, in band order, of part[band][i][b] (feature-major
-// fp32 partial sums) -> batch-major OutT.  A workgroup adds and transposes a tile of 32
+// fp32 partial sums, Bp columns per row) -> batch-major OutT for b < B.  A workgroup adds and transposes a tile of 32
 // columns x 64 batch rows through LDS; its stores are runs of 32 consecutive columns.
 template <int NB, typename OutT>
-__global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restrict__ part, int64_t I, int64_t B,
-                                                          OutT *__restrict__ dX) {
+__global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restrict__ part, int64_t I, int64_t Bp,
+                                                          int64_t B, OutT *__restrict__ dX) {
     __shared__ float tile[kTb][kTf + 1];
     const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTf, b0 = static_cast<int64_t>(blockIdx.y) * kTb;
     const int tid = threadIdx.x;
     const int bq = tid % 16, cr = tid / 16;  // float4 bq of the tile's batch range, column cr and cr + 16
-    const int64_t B4 = B / 4;
+    const int64_t B4 = Bp / 4;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         const int64_t c = c0 + cr + 16 * rr;
@@ -1169,11 +1177,12 @@ __device__ __forceinline__ void stage_vector(const ActT *__restrict__ x, int I, 
 // chunk edge leave their partial sum in head[w] (the chunk's first row) or tail[w] (its
 // last row); fixup_kernel finishes them and the empty rows, as for segscan_kernel.
 // THREADS == kStageThreads: x is read from an LDS copy (I elements).
-template <typename ActT, typename OutT, int THREADS>
+template <typename ActT, typename OutT, int THREADS, bool VPERM = false>
 __global__ __launch_bounds__(THREADS) void csr1_fwd_kernel(int O, int I, int nnz, int chunk, int nchunks,
                                                            const int32_t *__restrict__ offs,
                                                            const int32_t *__restrict__ cols,
                                                            const float *__restrict__ vals,
+                                                           const int32_t *__restrict__ vperm,
                                                            const ActT *__restrict__ x,
                                                            const float *__restrict__ bias, OutT *__restrict__ y,
                                                            float *__restrict__ head, float *__restrict__ tail) {
@@ -1200,7 +1209,7 @@ __global__ __launch_bounds__(THREADS) void csr1_fwd_kernel(int O, int I, int nnz
         for (int u = 0; u < U; ++u) {
             const int k = s0 + u * kWave + lane;
             const int kk = min(k, e1 - 1);
-            const float v = vals[kk];
+            const float v = vals[VPERM ? vperm[kk] : kk];
             const int c = cols[kk];
             const float xv = kStaged ? xs[c] : load_act(x, c);
             p[u] = k < e1 ? v * xv : 0.f;
@@ -1548,7 +1557,7 @@ constexpr int64_t kScatterLdsFloats = 16384;  // 64 KB private dX copy per workg
 // scatters into LDS copies up to SNACK_SCATTER_MAX_B batch rows, and batches that are multiples
 // of 4 from SNACK_ROWWAVE_MIN_B on take the rowwave mapping.
 #ifndef SNACK_SCATTER_MAX_B
-#define SNACK_SCATTER_MAX_B 3
+#define SNACK_SCATTER_MAX_B 1
 #endif
 
 // 0: rowwave tiles of 4*BT columns; 1: one tile of 4*BT*Q columns (Q <= 4) where 4*BT does not
@@ -1574,8 +1583,24 @@ struct SpmmPlan {
     int64_t nchunks;     // segscan, csr1: waves; scatter: workgroups (partial copies)
     int64_t nparts;      // csr1 private copies: workgroups (partial copies)
     bool direct;         // operand used in place (fp32, batch 1) instead of a transposed copy
+    int64_t bpad;        // batch columns of the feature-major operand (rowwave: B rounded up to 4)
     size_t off_opnd, off_head, off_tail, off_cvals, total;
 };
+
+// Batch columns of the feature-major copies.  The float4-lane kernels take batch tiles of
+// 4*BT*Q columns (BT a power of two <= 16, Q <= 4 float4s per lane); a batch up to 256 is padded
+// with zero columns to the smallest such size, so one tile covers it and the backward pass runs
+// fused, and a larger one to a multiple of 4.  The kernels store only the real columns; the
+// padded products are exact zeros.
+inline int64_t pad_batch(int64_t B) {
+    if (B <= 1) return B;
+    if (B <= 256) {
+        constexpr int64_t kTiles[] = {4, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256};
+        for (int64_t t : kTiles)
+            if (t >= B) return t;
+    }
+    return (B + 3) / 4 * 4;
+}
 
 inline int pow2_at_least(int64_t x) {
     int p = 1;
@@ -1594,6 +1619,7 @@ bool vec16(const snack_coo_desc *W) {
 SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok,
                        bool aligned16) {
     SpmmPlan p{};
+    p.bpad = B;
     p.direct = (B == 1 && dtype == SNACK_F32);
     // batch 1, rows averaging >= 32 entries: stream cols and vals, rows from row_offsets,
     // activations read in place (the segmented scan is faster for shorter rows)
@@ -1640,17 +1666,20 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
         p.total = at;
         return p;
     }
-    if (B >= SNACK_ROWWAVE_MIN_B && B % 4 == 0 && (opnd_rows + 1) * B * 4 < (int64_t(1) << 32)) {
+    const int64_t Bp = pad_batch(B);
+    p.bpad = B;
+    if (Bp >= SNACK_ROWWAVE_MIN_B && (opnd_rows + 1) * Bp * 4 < (int64_t(1) << 32)) {
         p.mapping = kRowwave;
-        p.bt = 1;  // lanes per slot: the largest power of two <= min(16, B/4)
-        while (p.bt * 2 <= std::min<int64_t>(16, B / 4)) p.bt *= 2;
+        p.bpad = Bp;
+        p.bt = 1;  // lanes per slot: the largest power of two <= min(16, Bp/4)
+        while (p.bt * 2 <= std::min<int64_t>(16, Bp / 4)) p.bt *= 2;
         p.q = 1;
-        if (SNACK_ROWWAVE_Q_MODE == 2 || (SNACK_ROWWAVE_Q_MODE == 1 && B % (4 * p.bt) != 0)) {
+        if (SNACK_ROWWAVE_Q_MODE == 2 || (SNACK_ROWWAVE_Q_MODE == 1 && Bp % (4 * p.bt) != 0)) {
             // one exact tile of 4*BT*Q columns, Q <= 4 float4s per lane, where one exists
             for (int bt = 16; bt >= 1; bt /= 2) {
-                if (B % (4 * bt) == 0 && B / (4 * bt) <= 4) {
+                if (Bp % (4 * bt) == 0 && Bp / (4 * bt) <= 4) {
                     p.bt = bt;
-                    p.q = static_cast<int>(B / (4 * bt));
+                    p.q = static_cast<int>(Bp / (4 * bt));
                     break;
                 }
             }
@@ -1667,7 +1696,7 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
     }
     size_t at = 0;
     p.off_opnd = at;
-    if (!p.direct) at = align_up(at + sizeof(float) * static_cast<size_t>((opnd_rows + 1) * B));
+    if (!p.direct) at = align_up(at + sizeof(float) * static_cast<size_t>((opnd_rows + 1) * p.bpad));
     p.off_head = at;
     if (p.mapping == kSegscan) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nchunks * B));
     p.off_tail = at;
@@ -1687,17 +1716,16 @@ void add_cvals(SpmmPlan &p, int64_t n) {
 // colvals: the values are stored in column-view order (snack_coo_desc.row_to_col != NULL).
 SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int dtype, bool scatter_ok,
                    bool aligned16 = false, bool colvals = false) {
-    SpmmPlan p = plan_spmm_map(nnz, opnd_rows, nout, B, dtype, scatter_ok, aligned16);
-    // mappings that walk the row order with the values read in place (batch 1 and the small-batch
-    // scatter) take column-order values gathered into row order first
-    if (colvals && nnz > 0 && (p.mapping == kCsr1 || p.mapping == kCsr1Priv || p.mapping == kScatter))
-        add_cvals(p, nnz);
+    // with values in column order the input gradient (scatter_ok) walks only the column view, where
+    // they are in place: the batch-1 CSR walk of the forward serves it there, and the row walks
+    // (private copies, scatter) are not used
+    SpmmPlan p = plan_spmm_map(nnz, opnd_rows, nout, B, dtype, scatter_ok && !colvals, aligned16);
     // the rowwave walks read the values through a permutation -- the input gradient with values in
     // row order, the forward with values in column order -- once per batch tile; with 4 or more
     // tiles on a large layer they are gathered into the walk's order once, so every tile reads them
     // coalesced (one tile: the gather costs more than it saves)
-    else if (scatter_ok != colvals && p.mapping == kRowwave && ceil_div(B, 4 * p.bt * p.q) >= 4 &&
-             nnz >= kLargeBatchMinNnz)
+    if (scatter_ok != colvals && p.mapping == kRowwave && ceil_div(p.bpad, 4 * p.bt * p.q) >= 4 &&
+        nnz >= kLargeBatchMinNnz)
         add_cvals(p, nnz);
     return p;
 }
@@ -1710,6 +1738,7 @@ struct SddmmPlan {
     int bt, vw;
     int64_t steps, waves, per_wave;
     bool x_direct, dy_direct;
+    int64_t bpad;        // batch columns of the feature-major copies (rowsddmm: B rounded up to 4)
     size_t off_dw;       // row-order dW staging (values in column order)
     size_t off_x, off_dy, total;
 };
@@ -1738,25 +1767,31 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
         p.waves = ceil_div(nnz, G * p.steps);
     }
     p.slices = 1;
-    if (B >= 4 && B % 4 == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
-        // rowsddmm over B = 4*BT*Q: BT the largest power of two <= 16 that leaves Q <= 4
+    p.bpad = B;
+    const int64_t Bp = pad_batch(B);
+    if (Bp >= 4 && (std::max(I, O) + 1) * Bp * 4 < (int64_t(1) << 32)) {
+        // rowsddmm over the padded batch Bp = 4*BT*Q: BT the largest power of two <= 16 that
+        // leaves Q <= 4
         for (int bt = 16; bt >= 1; bt /= 2) {
-            if (B % (4 * bt) == 0 && B / (4 * bt) <= 4) {
+            if (Bp % (4 * bt) == 0 && Bp / (4 * bt) <= 4) {
                 p.bt = bt;
-                p.rowq = static_cast<int>(B / (4 * bt));
+                p.rowq = static_cast<int>(Bp / (4 * bt));
                 break;
             }
         }
-        if (p.rowq == 0 && B % 256 == 0 && nnz >= kLargeBatchMinNnz) {  // wide batch, large layer:
+        if (p.rowq == 0 && Bp % 256 == 0 && nnz >= kLargeBatchMinNnz) {  // wide batch, large layer:
             // slices of 256 columns (each gathers its part of the X rows once per entry; the
             // per-entry kernel re-reads the whole dY row per entry)
             p.bt = 16;
             p.rowq = 4;
-            p.slices = B / 256;
+            p.slices = Bp / 256;
         }
+        if (p.rowq > 0) p.bpad = Bp;
     }
     p.x_direct = p.dy_direct = (B == 1 && dtype == SNACK_F32);
-    if (B == 1 && nnz >= 128 * O) {  // rows averaging >= 128 entries
+    // rows averaging >= 128 entries; with values in column order the walk is over the column view
+    // (columns averaging >= 128 entries), which writes dW in that order directly
+    if (B == 1 && nnz >= 128 * (colvals ? I : O)) {
         p.csr1 = true;
         p.x_direct = p.dy_direct = true;
         p.steps = round_up(ceil_div(std::max<int64_t>(nnz, 1), 8192), 256);  // entries per wave
@@ -1764,21 +1799,22 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
     }
     size_t at = 0;
     p.off_x = at;
-    if (!p.x_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * B));
+    if (!p.x_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * p.bpad));
     p.off_dy = at;
-    if (!p.dy_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * B));
+    if (!p.dy_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * p.bpad));
     p.off_dw = at;
-    if (colvals && nnz > 0) at = align_up(at + sizeof(float) * static_cast<size_t>(nnz));
+    if (colvals && nnz > 0 && !p.csr1) at = align_up(at + sizeof(float) * static_cast<size_t>(nnz));
     p.total = at;
     return p;
 }
 
-// Backward pass plan: the fused column-view kernel for batches 4*BT*Q (Q in {1, 2, 4})
+// Backward pass plan: the fused column-view kernel for (padded) batches 4*BT*Q (Q in 1..4)
 // whose feature-major copies (with their zero rows) stay below 4 GB; otherwise the input
 // gradient and the weight gradient one after the other, sharing the workspace.
 struct BwdPlan {
     bool fused;
     int bt, q, nb;  // nb: row bands of the fused kernel (1 or kXcds)
+    int64_t bpad;   // batch columns of the feature-major copies (B rounded up to 4)
     size_t off_x, off_dy, off_part, total;
 };
 
@@ -1804,14 +1840,16 @@ int64_t band_min_nnz() {
 
 BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool aligned16, bool colvals = false) {
     BwdPlan p{};
-    if (nnz > 0 && B >= 4 && B % 4 == 0 && (std::max(I, O) + 1) * B * 4 < (int64_t(1) << 32)) {
-        // B = 4*BT*Q: BT lanes per slot (the largest power of two <= 16 that leaves Q <= 4
-        // float4s per lane)
+    const int64_t Bp = pad_batch(B);
+    p.bpad = Bp;
+    if (nnz > 0 && Bp >= 4 && (std::max(I, O) + 1) * Bp * 4 < (int64_t(1) << 32)) {
+        // padded batch Bp = 4*BT*Q: BT lanes per slot (the largest power of two <= 16 that leaves
+        // Q <= 4 float4s per lane)
         for (int bt = 16; bt >= SNACK_FUSED_MIN_BT; bt /= 2) {
-            if (B % (4 * bt) == 0 && B / (4 * bt) <= 4) {
+            if (Bp % (4 * bt) == 0 && Bp / (4 * bt) <= 4) {
                 p.fused = true;
                 p.bt = bt;
-                p.q = static_cast<int>(B / (4 * bt));
+                p.q = static_cast<int>(Bp / (4 * bt));
                 // row bands (one per XCD) once the triple is large enough to spill L2; values in
                 // column order are read and written in walk order, and the bands only add waves
                 p.nb = !colvals && nnz >= band_min_nnz() ? kXcds : 1;
@@ -1822,11 +1860,11 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
     if (p.fused) {
         size_t at = 0;
         p.off_x = at;
-        at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * B));
+        at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * Bp));
         p.off_dy = at;
-        at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * B));
+        at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * Bp));
         p.off_part = at;
-        if (p.nb > 1) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nb * I * B));
+        if (p.nb > 1) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nb * I * Bp));
         p.total = at;
     } else {
         p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals).total,
@@ -1876,23 +1914,25 @@ int check_workspace(void *ws, size_t have, size_t need, const char *who) {
     return SNACK_OK;
 }
 
-// activation [B][F] -> feature-major fp32 [F+1][B] in `dst` (row F zero); with src1 != NULL
-// also [B][F1] -> [F1+1][B] in dst1, in the same launch
+// activation [B][F] -> feature-major fp32 [F+1][Bp] in `dst` (row F zero, columns B..Bp-1 zero;
+// Bp = 0 means B); with src1 != NULL also [B][F1] -> [F1+1][Bp] in dst1, in the same launch
 int launch_to_feature_major(const void *src, int dtype, int64_t B, int64_t F, float *dst, hipStream_t st,
-                            const void *src1 = nullptr, int64_t F1 = 0, float *dst1 = nullptr) {
+                            const void *src1 = nullptr, int64_t F1 = 0, float *dst1 = nullptr, int64_t Bp = 0) {
+    if (Bp < B) Bp = B;
     if (B == 0 || (F == 0 && F1 == 0 && !src1)) return SNACK_OK;
     const int64_t fmax = std::max(F, src1 ? F1 : 0);
     const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, ceil_div(fmax, kTf))),
-                    static_cast<unsigned>(ceil_div(B, kTb)), src1 ? 2u : 1u);
-    const bool vec = B % 4 == 0 && F % 4 == 0 && (!src1 || F1 % 4 == 0);
+                    static_cast<unsigned>(ceil_div(Bp, kTb)), src1 ? 2u : 1u);
+    // vector loads need rows of F a multiple of 4 (16-byte aligned), vector stores Bp
+    const bool vec = Bp % 4 == 0 && F % 4 == 0 && (!src1 || F1 % 4 == 0);
     if (dtype == SNACK_F32) {
         const float *a = static_cast<const float *>(src), *a1 = static_cast<const float *>(src1);
-        if (vec) hipLaunchKernelGGL(to_feature_major4_kernel<float>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B);
-        else hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B);
+        if (vec) hipLaunchKernelGGL(to_feature_major4_kernel<float>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B, Bp);
+        else hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B, Bp);
     } else {
         const bf16_t *a = static_cast<const bf16_t *>(src), *a1 = static_cast<const bf16_t *>(src1);
-        if (vec) hipLaunchKernelGGL(to_feature_major4_kernel<bf16_t>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B);
-        else hipLaunchKernelGGL(to_feature_major_kernel<bf16_t>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B);
+        if (vec) hipLaunchKernelGGL(to_feature_major4_kernel<bf16_t>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B, Bp);
+        else hipLaunchKernelGGL(to_feature_major_kernel<bf16_t>, grid, dim3(kBlock), 0, st, a, dst, F, a1, dst1, F1, B, Bp);
     }
     return check_hip("to_feature_major");
 }
@@ -1911,7 +1951,7 @@ void launch_segscan_bt(const SpmmPlan &p, int64_t nnz, const int32_t *keys, cons
 template <typename OutT, int BT, int Q>
 void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const int32_t *gidx, const float *vals,
                        const int32_t *perm, const float *opnd, int64_t opnd_rows, int64_t B, const float *bias,
-                       OutT *out, int64_t out_ld, hipStream_t st) {
+                       OutT *out, int64_t out_ld, int64_t nbo, hipStream_t st) {
     const int zero_row = static_cast<int>(opnd_rows);  // the transposed operand's zero row
     // keys with >= 256 entries on average are split over the 4 waves of a workgroup, unless
     // values are read through the column permutation: one wave per key keeps co-resident
@@ -1922,10 +1962,10 @@ void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const in
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(ceil_div(B, 4 * BT * Q)));
     if (split)
         hipLaunchKernelGGL((rowwave_kernel<BT, 4, Q, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
-                           perm, opnd, zero_row, B, bias, out, out_ld);
+                           perm, opnd, zero_row, B, bias, out, out_ld, nbo);
     else
         hipLaunchKernelGGL((rowwave_kernel<BT, 1, Q, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
-                           perm, opnd, zero_row, B, bias, out, out_ld);
+                           perm, opnd, zero_row, B, bias, out, out_ld, nbo);
 }
 
 // out[j] = vals[perm[j]]: the stored values in column-view order
@@ -1962,7 +2002,8 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
         switch (p.bt * 8 + p.q) {
 #define SNACK_RW(BTV, QV)                                                                                           \
     case BTV * 8 + QV:                                                                                               \
-        launch_rowwave_bt<OutT, BTV, QV>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, B, bias, out, nkeys, st); \
+        launch_rowwave_bt<OutT, BTV, QV>(nkeys, nnz, offs, gidx, vals, perm, opnd, opnd_rows, p.bpad, bias, out, nkeys, \
+                                         B, st);                                                                    \
         break;
             SNACK_RW(1, 1) SNACK_RW(2, 1) SNACK_RW(4, 1) SNACK_RW(8, 1) SNACK_RW(16, 1)
             SNACK_RW(1, 3) SNACK_RW(2, 3) SNACK_RW(4, 3) SNACK_RW(8, 3) SNACK_RW(16, 3)
@@ -2019,6 +2060,53 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
     }
 }
 
+namespace {
+
+// Batch 1 over a CSR structure (offs [nkeys+1], gidx/vals in walk order, vals through vperm when
+// non-NULL): y[key] = bias[key] + sum of vals * x[gidx], then the chunk-edge fix-up.  The forward
+// runs it over the row view; with values in column order the input gradient runs it over the
+// column view.
+int launch_csr1(const SpmmPlan &p, int act_dtype, int64_t nkeys, int64_t nx, int64_t nnz, const int32_t *offs,
+                const int32_t *gidx, const float *vals, const int32_t *vperm, const void *x, const float *bias,
+                void *y, char *ws, hipStream_t st) {
+    float *head = reinterpret_cast<float *>(ws + p.off_head);
+    float *tail = reinterpret_cast<float *>(ws + p.off_tail);
+    const bool staged = nx <= kStageMaxI;
+    const int threads = staged ? kStageThreads : kBlock;
+    const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(p.nchunks, threads / kWave))));
+    const size_t lds = staged ? sizeof(float) * static_cast<size_t>(nx) : 0;
+    const int o = static_cast<int>(nkeys), in = static_cast<int>(nx), nz = static_cast<int>(nnz),
+              ch = static_cast<int>(p.chunk), nc = static_cast<int>(p.nchunks);
+#define SNACK_CSR1_FWD(T, TH, VP)                                                                                 \
+    hipLaunchKernelGGL((csr1_fwd_kernel<T, T, TH, VP>), grid, dim3(TH), lds, st, o, in, nz, ch, nc, offs, gidx, vals, \
+                       vperm, static_cast<const T *>(x), bias, static_cast<T *>(y), head, tail)
+#define SNACK_CSR1_FWD_T(T)                                   \
+    if (staged && vperm) SNACK_CSR1_FWD(T, kStageThreads, true); \
+    else if (staged) SNACK_CSR1_FWD(T, kStageThreads, false);    \
+    else if (vperm) SNACK_CSR1_FWD(T, kBlock, true);             \
+    else SNACK_CSR1_FWD(T, kBlock, false);
+    probe(true, st);
+    if (act_dtype == SNACK_F32) {
+        SNACK_CSR1_FWD_T(float)
+    } else {
+        SNACK_CSR1_FWD_T(bf16_t)
+    }
+#undef SNACK_CSR1_FWD_T
+#undef SNACK_CSR1_FWD
+    probe(false, st);
+    if (int s = check_hip("csr1_fwd_kernel")) return s;
+    const dim3 fgrid(static_cast<unsigned>(ceil_div(nkeys, kBlock)), 1);
+    if (act_dtype == SNACK_F32)
+        hipLaunchKernelGGL(fixup_kernel<float>, fgrid, dim3(kBlock), 0, st, nkeys, int64_t(1), p.chunk, offs, bias,
+                           head, tail, static_cast<float *>(y), nkeys);
+    else
+        hipLaunchKernelGGL(fixup_kernel<bf16_t>, fgrid, dim3(kBlock), 0, st, nkeys, int64_t(1), p.chunk, offs, bias,
+                           head, tail, static_cast<bf16_t *>(y), nkeys);
+    return check_hip("fixup_kernel");
+}
+
+}  // namespace
+
 extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t batch, int act_dtype,
                              const float *bias, void *Y, void *workspace, size_t workspace_bytes,
                              void *hip_stream) {
@@ -2041,47 +2129,14 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         const float *vals = W->vals;
         const int32_t *vperm = W->row_to_col;
         if (p.mapping == kCsr1) {
-            if (vperm) {
-                float *cv = reinterpret_cast<float *>(ws + p.off_cvals);
-                if (int s = launch_gather(vperm, vals, nnz, cv, st)) return s;
-                vals = cv;
-            }
-            float *head = reinterpret_cast<float *>(ws + p.off_head);
-            float *tail = reinterpret_cast<float *>(ws + p.off_tail);
-            const bool staged = I <= kStageMaxI;
-            const int threads = staged ? kStageThreads : kBlock;
-            const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(p.nchunks, threads / kWave))));
-            const size_t lds = staged ? sizeof(float) * static_cast<size_t>(I) : 0;
-            const int o = static_cast<int>(O), in = static_cast<int>(I), nz = static_cast<int>(nnz),
-                      ch = static_cast<int>(p.chunk), nc = static_cast<int>(p.nchunks);
-#define SNACK_CSR1_FWD(T, TH)                                                                                   \
-    hipLaunchKernelGGL((csr1_fwd_kernel<T, T, TH>), grid, dim3(TH), lds, st, o, in, nz, ch, nc, W->row_offsets,    \
-                       W->cols, vals, static_cast<const T *>(X), bias, static_cast<T *>(Y), head, tail)
-            probe(true, st);
-            if (act_dtype == SNACK_F32) {
-                if (staged) SNACK_CSR1_FWD(float, kStageThreads);
-                else SNACK_CSR1_FWD(float, kBlock);
-            } else {
-                if (staged) SNACK_CSR1_FWD(bf16_t, kStageThreads);
-                else SNACK_CSR1_FWD(bf16_t, kBlock);
-            }
-#undef SNACK_CSR1_FWD
-            probe(false, st);
-            if (int s = check_hip("csr1_fwd_kernel")) return s;
-            const dim3 fgrid(static_cast<unsigned>(ceil_div(O, kBlock)), 1);
-            if (act_dtype == SNACK_F32)
-                hipLaunchKernelGGL(fixup_kernel<float>, fgrid, dim3(kBlock), 0, st, O, int64_t(1), p.chunk,
-                                   W->row_offsets, bias, head, tail, static_cast<float *>(Y), O);
-            else
-                hipLaunchKernelGGL(fixup_kernel<bf16_t>, fgrid, dim3(kBlock), 0, st, O, int64_t(1), p.chunk,
-                                   W->row_offsets, bias, head, tail, static_cast<bf16_t *>(Y), O);
-            if (int s = check_hip("fixup_kernel")) return s;
+            if (int s = launch_csr1(p, act_dtype, O, I, nnz, W->row_offsets, W->cols, vals, vperm, X, bias, Y, ws, st))
+                return s;
             return snack::ok();
         }
         const float *xt = static_cast<const float *>(X);
         if (!p.direct) {
             float *dst = reinterpret_cast<float *>(ws + p.off_opnd);
-            if (int s = launch_to_feature_major(X, act_dtype, batch, I, dst, st)) return s;
+            if (int s = launch_to_feature_major(X, act_dtype, batch, I, dst, st, nullptr, 0, nullptr, p.bpad)) return s;
             xt = dst;
         }
         int s;
@@ -2127,14 +2182,14 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W), colvals);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
-        // row walks (batch-1 private copies, small-batch scatter) read values in row order: values
-        // kept in column order are gathered into row order first
-        const float *rvals = W->vals;
-        if (colvals && (p.mapping == kCsr1Priv || p.mapping == kScatter)) {
-            float *cv = reinterpret_cast<float *>(ws + p.off_cvals);
-            if (int s = launch_gather(W->row_to_col, W->vals, nnz, cv, st)) return s;
-            rvals = cv;
+        // values in column order: batch 1 walks the column view as the forward walks the rows
+        if (p.mapping == kCsr1) {
+            if (int s = launch_csr1(p, act_dtype, I, O, nnz, W->col_offsets, W->col_rows, W->vals, nullptr, dY,
+                                    nullptr, dX, ws, st))
+                return s;
+            return snack::ok();
         }
+        const float *rvals = W->vals;  // the row walks below run with values in row order only
         if (p.mapping == kCsr1Priv) {
             float *partial = reinterpret_cast<float *>(ws + p.off_head);
             const size_t lds = sizeof(float) * static_cast<size_t>(kPrivWaves * I);
@@ -2198,7 +2253,8 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         const float *dyt = static_cast<const float *>(dY);
         if (!p.direct) {
             float *dst = reinterpret_cast<float *>(ws + p.off_opnd);
-            if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st)) return s;
+            if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st, nullptr, 0, nullptr, p.bpad))
+                return s;
             dyt = dst;
         }
         // the column walk reads values in row order through col_perm, values in column order in place
@@ -2253,15 +2309,22 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             return snack::ok();
         };
         if (p.csr1) {
-            const bool staged = I <= kStageMaxI;
+            // dW[k] = dY[row] * X[col] along the row view, or (values in column order) along the
+            // column view with the roles of X and dY swapped, straight into column order
+            const int64_t nk = colvals ? I : O, nx = colvals ? O : I;
+            const int32_t *woffs = colvals ? W->col_offsets : W->row_offsets;
+            const int32_t *widx = colvals ? W->col_rows : W->cols;
+            const void *wx = colvals ? dY : X, *wdy = colvals ? X : dY;
+            float *wdw = colvals ? dW_out : dW;
+            const bool staged = nx <= kStageMaxI;
             const int threads = staged ? kStageThreads : kBlock;
             const dim3 grid(static_cast<unsigned>(round_up8(ceil_div(p.waves, threads / kWave))));
-            const size_t lds = staged ? sizeof(float) * static_cast<size_t>(I) : 0;
-            const int o = static_cast<int>(O), in = static_cast<int>(I), nz = static_cast<int>(nnz),
+            const size_t lds = staged ? sizeof(float) * static_cast<size_t>(nx) : 0;
+            const int o = static_cast<int>(nk), in = static_cast<int>(nx), nz = static_cast<int>(nnz),
                       ch = static_cast<int>(p.steps), nc = static_cast<int>(p.waves);
 #define SNACK_CSR1_DW(T, TH)                                                                                  \
-    hipLaunchKernelGGL((csr1_dw_kernel<T, TH>), grid, dim3(TH), lds, st, o, in, nz, ch, nc, W->row_offsets, W->cols, \
-                       static_cast<const T *>(X), static_cast<const T *>(dY), dW)
+    hipLaunchKernelGGL((csr1_dw_kernel<T, TH>), grid, dim3(TH), lds, st, o, in, nz, ch, nc, woffs, widx,            \
+                       static_cast<const T *>(wx), static_cast<const T *>(wdy), wdw)
             probe(true, st);
             if (act_dtype == SNACK_F32) {
                 if (staged) SNACK_CSR1_DW(float, kStageThreads);
@@ -2273,18 +2336,19 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
 #undef SNACK_CSR1_DW
             probe(false, st);
             if (int s = check_hip("csr1_dw_kernel")) return s;
-            return finish();
+            return snack::ok();
         }
         const float *xt = static_cast<const float *>(X);
         const float *dyt = static_cast<const float *>(dY);
         if (!p.x_direct) {
             float *dst = reinterpret_cast<float *>(ws + p.off_x);
-            if (int s = launch_to_feature_major(X, act_dtype, batch, I, dst, st)) return s;
+            if (int s = launch_to_feature_major(X, act_dtype, batch, I, dst, st, nullptr, 0, nullptr, p.bpad)) return s;
             xt = dst;
         }
         if (!p.dy_direct) {
             float *dst = reinterpret_cast<float *>(ws + p.off_dy);
-            if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st)) return s;
+            if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st, nullptr, 0, nullptr, p.bpad))
+                return s;
             dyt = dst;
         }
         const int64_t blocks = round_up8(ceil_div(p.waves, kWavesPerBlock));
@@ -2297,7 +2361,7 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             const int zero_row = static_cast<int>(I);
 #define SNACK_ROWSD(BTV, WPRV, QV)                                                                           \
     hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV, 8, false>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, \
-                       W->cols, xt, zero_row, dyt, batch, dW)
+                       W->cols, xt, zero_row, dyt, p.bpad, dW)
 #define SNACK_ROWSD_Q(BTV, WPRV)                         \
     do {                                                 \
         if (p.rowq == 1) SNACK_ROWSD(BTV, WPRV, 1);      \
@@ -2313,7 +2377,7 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
                 for (int64_t k = 0; k < p.slices; ++k) {
 #define SNACK_ROWSD_SLICE(WPRV, ACCV)                                                                          \
     hipLaunchKernelGGL((rowsddmm_kernel<16, WPRV, 4, 2, ACCV>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, W->cols, \
-                       xt + 256 * k, zero_row, dyt + 256 * k, batch, dW)
+                       xt + 256 * k, zero_row, dyt + 256 * k, p.bpad, dW)
                     if (split) {
                         if (k > 0) SNACK_ROWSD_SLICE(4, true);
                         else SNACK_ROWSD_SLICE(4, false);
@@ -2374,11 +2438,12 @@ namespace {
 
 template <typename OutT, int BT, int NB, bool COLV>
 void launch_colbwd_q(int q, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W, const float *xt,
-                     const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part) {
+                     const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part, int64_t nbo) {
     const int nnz = static_cast<int>(W->nnz);
 #define SNACK_COLBWD(QV)                                                                                            \
     hipLaunchKernelGGL((colbwd_kernel<BT, QV, NB, OutT, COLV>), grid, dim3(kBlock), 0, st, I, W->col_offsets,     \
-                       W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz, part)
+                       W->col_rows, W->col_perm, W->vals, xt, dyt, zero_row, B, dX, dW, W->row_offsets, nnz, part, \
+                       nbo)
     if (q == 1) SNACK_COLBWD(1);
     else if (q == 2) SNACK_COLBWD(2);
     else if (q == 3) SNACK_COLBWD(3);
@@ -2389,17 +2454,18 @@ void launch_colbwd_q(int q, dim3 grid, hipStream_t st, int64_t I, const snack_co
 template <typename OutT, int NB, bool COLV = false>
 void launch_colbwd_nb(const BwdPlan &p, dim3 grid, hipStream_t st, int64_t I, const snack_coo_desc *W,
                       const float *xt, const float *dyt, int zero_row, int64_t B, OutT *dX, float *dW, float *part) {
+    const int64_t Bp = p.bpad;  // the copies' batch columns; B of them are real
     if (p.bt == 16)
-        launch_colbwd_q<OutT, 16, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 16, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
     else if (p.bt == 8)
-        launch_colbwd_q<OutT, 8, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 8, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
     else if (p.bt == 4)
-        launch_colbwd_q<OutT, 4, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 4, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
 #if SNACK_FUSED_MIN_BT < 4
     else if (p.bt == 2)
-        launch_colbwd_q<OutT, 2, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 2, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
     else
-        launch_colbwd_q<OutT, 1, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
+        launch_colbwd_q<OutT, 1, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
 #endif
 }
 
@@ -2420,7 +2486,7 @@ int launch_colbwd(const BwdPlan &p, hipStream_t st, int64_t I, const snack_coo_d
     launch_colbwd_nb<OutT, kXcds>(p, grid, st, I, W, xt, dyt, zero_row, B, dX, dW, part);
     if (int s = check_hip("colbwd_kernel")) return s;
     const dim3 sgrid(static_cast<unsigned>(ceil_div(I, kTf)), static_cast<unsigned>(ceil_div(B, kTb)));
-    hipLaunchKernelGGL((band_sum_kernel<kXcds, OutT>), sgrid, dim3(kBlock), 0, st, part, I, B, dX);
+    hipLaunchKernelGGL((band_sum_kernel<kXcds, OutT>), sgrid, dim3(kBlock), 0, st, part, I, p.bpad, B, dX);
     return check_hip("band_sum_kernel");
 }
 
@@ -2464,7 +2530,7 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
         }
         float *xt = reinterpret_cast<float *>(ws + p.off_x);
         float *dyt = reinterpret_cast<float *>(ws + p.off_dy);
-        if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st, dY, O, dyt)) return s;
+        if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st, dY, O, dyt, p.bpad)) return s;
         // one wave per column: co-resident waves then walk their columns' rows in step, so the
         // vals reads and dW writes through the column permutation share L2 lines (splitting
         // long columns over 4 waves scatters them over the whole triple at once)

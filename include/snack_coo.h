@@ -160,7 +160,8 @@ int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int64_t batch, 
 /* Weight gradient on the support (Section 3.4 / Appendix F: sum of the batch's
  * rank-1 outer products evaluated only at (i,j) in supp(W)):
  * dW[k] = sum_b dY[b,rows[k]] X[b,cols[k]], written in the order of the
- * triple (fp32, overwritten; entries with vals[k] == 0 are still computed).
+ * triple (in column-view order with row_to_col; fp32, overwritten; entries
+ * with vals[k] == 0 are still computed).
  *   X device [batch][I], dY device [batch][O], fp32 or bf16; dW device [nnz]. */
 int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY,
                           int64_t batch, int act_dtype, float *dW,
@@ -169,19 +170,21 @@ int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY
 /* Both gradients of the backward pass (Section 3.4 / Appendix F: dL/dX and the
  * weight gradient on supp(W) are computed from the same upstream gradient):
  * the results of snack_coo_bwd_input (dX, and db if not NULL) and of
- * snack_coo_grad_weight (dW) in one call.  Where the batch allows it
- * (B = 4*BT*Q with BT a power of two <= 16 and Q in {1, 2, 4}, i.e. every
- * multiple of 16 up to 256 and more), one pass over the column view gathers
- * each entry's dY row once for both products; otherwise the two operations
- * run one after the other on the stream.  Arguments and layouts as for the
+ * snack_coo_grad_weight (dW) in one call.  For batches 2..256 one pass over
+ * the column view gathers each entry's dY row once for both products (the
+ * feature-major copies are padded with zero columns to a batch tile of
+ * 4*BT*Q columns, BT a power of two <= 16 and Q <= 4); at batch 1 and above
+ * 256 the two operations run one after the other on the stream.  Arguments and layouts as for the
  * two calls; requires the column view; workspace >=
  * snack_coo_workspace_bytes(SNACK_OP_BWD, ...).  dX and dW are overwritten
- * (dW in the order of the triple); results agree with the separate calls to
- * rounding (the summation order of dX differs).  Layers of at least 2^20
+ * (dW in the order of the triple, or of the column view with row_to_col);
+ * results agree with the separate calls to rounding (the summation order of
+ * dX differs).  Layers of at least 2^20
  * entries take a row-banded form of the one-pass kernel: the rows are cut into
  * 8 bands of about nnz/8 entries, each band's part of every column is walked on
  * its own, and the 8 partial dX are added in band order (deterministic; the
- * workspace then also holds 8*I*B floats).  The environment variable
+ * workspace then also holds 8*I*Bp floats, Bp the padded batch; values in
+ * column order never take the banded form).  The environment variable
  * SNACK_COO_BAND_MIN_NNZ (a decimal entry count, read at every call of this
  * function and of snack_coo_workspace_bytes) overrides that threshold. */
 int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch, int act_dtype,

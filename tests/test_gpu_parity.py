@@ -227,18 +227,18 @@ def test_invariants_bias_determinism_scaling_permutation():
         assert torch.equal(snk.snack_coo_fwd(W, torch.zeros_like(X), b), b.expand(B, 700))
         assert not torch.any(snk.snack_coo_bwd_input(W, torch.zeros_like(dY)))
         assert not torch.any(snk.snack_coo_grad_weight(W, torch.zeros_like(X), dY))
-        # deterministic: bit-identical reruns (the small-batch input gradient, which
-        # scatters into a workgroup-private LDS copy with atomics -- batch <= 3 and
-        # batch * in_features <= 16384 -- is reproducible to rounding only)
+        # deterministic: bit-identical reruns (the batch-1 input gradient of a small layer, which
+        # scatters into a workgroup-private LDS copy with atomics -- in_features <= 16384 -- is
+        # reproducible to rounding only)
         Y1, Y2 = snk.snack_coo_fwd(W, X, b), snk.snack_coo_fwd(W, X, b)
         assert torch.equal(Y1, Y2)
         dX1, dX2 = snk.snack_coo_bwd_input(W, dY), snk.snack_coo_bwd_input(W, dY)
-        if B <= 3 and B * 900 <= 16384:
+        if B == 1 and B * 900 <= 16384:
             check_close(dX2.cpu().numpy(), dX1.cpu().numpy().astype(np.float64), 60, "dX rerun")
         else:
             assert torch.equal(dX1, dX2)
         assert torch.equal(snk.snack_coo_grad_weight(W, X, dY), snk.snack_coo_grad_weight(W, X, dY))
-        if B % 4 == 0:  # the fused backward pass has no atomics: bit-identical reruns
+        if 2 <= B <= 256:  # the fused backward pass has no atomics: bit-identical reruns
             a, b2 = snk.snack_coo_bwd(W, X, dY), snk.snack_coo_bwd(W, X, dY)
             assert torch.equal(a[0], b2[0]) and torch.equal(a[1], b2[1])
         # power-of-two scaling is exact
@@ -384,13 +384,14 @@ def test_batch1_input_gradient_misaligned_arrays():
     check_close(from_device(dXa), ref, nnz / I, "dX aligned")
 
 
-# snack_coo_bwd over batches that pick each variant of the one-pass backward (B = 4*BT*Q with
-# BT the largest power of two <= 16 leaving Q <= 4: 4 -> BT 1, 8 -> BT 2, 12 -> BT 1 Q 3,
-# 16 -> BT 4, 24 -> BT 2 Q 3, 32 -> BT 8, 48 -> BT 4 Q 3, 64/128/192/256 -> BT 16 with Q 1..4)
-# and batches that fall back to the two separate calls (40, 512); fp32 and bf16; the one-pass
-# kernel with and without row bands.
+# snack_coo_bwd over batches that pick each variant of the one-pass backward (the batch padded
+# with zero columns to Bp = 4*BT*Q, BT the largest power of two <= 16 leaving Q <= 4: 4 -> BT 1,
+# 8 -> BT 2, 12 -> BT 1 Q 3, 16 -> BT 4, 24 -> BT 2 Q 3, 32 -> BT 8, 48 -> BT 4 Q 3,
+# 64/128/192/256 -> BT 16 with Q 1..4; padded: 5 -> 8, 13 -> 16, 20 -> 24, 40 -> 48, 65 -> 96,
+# 130 -> 192, 200 -> 256) and a batch that runs the two separate calls (512); fp32 and bf16; the
+# one-pass kernel with and without row bands.
 @pytest.mark.parametrize("banding", list(BANDINGS))
-@pytest.mark.parametrize("B", [4, 8, 12, 16, 24, 32, 40, 48, 64, 96, 128, 192, 256, 512])
+@pytest.mark.parametrize("B", [4, 5, 8, 12, 13, 16, 20, 24, 32, 40, 48, 64, 65, 96, 128, 130, 192, 200, 256, 512])
 @pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
 def test_backward_batches(B, bf16, banding):
     say(f"backward B={B} bf16={bf16} {banding}")
@@ -419,7 +420,7 @@ BANDED = [  # seed, shape, O, I, nnz
 
 
 @pytest.mark.parametrize("case", BANDED, ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}")
-@pytest.mark.parametrize("B", [4, 8, 16, 48, 64, 128])
+@pytest.mark.parametrize("B", [3, 4, 8, 16, 48, 64, 65, 128])
 def test_backward_row_bands(case, B):
     seed, shape, O, I, nnz = case
     say(f"banded backward {shape} {O}x{I} nnz={nnz} B={B}")
