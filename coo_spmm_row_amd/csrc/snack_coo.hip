@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstdint>
 #include <cstring>
@@ -478,6 +479,297 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
                 if (c + 1 < nbo) store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
                 if (c + 2 < nbo) store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- LDS-tiled gather-reduce
+// The same gather-reduce as rowwave (out[key][:] = sum over the key's entries of
+// vals * opnd[gidx][:]), with the operand rows served from LDS instead of L2.  W is cut into
+// tiles of (a range of keys) x (a block of cw operand rows); a 1024-thread workgroup stages its
+// block of the feature-major operand (cw rows of 64 batch columns, 256 B each, plus one zero
+// row: up to 160 KB, gfx950's LDS) once, then walks its keys' segments inside the block.  The
+// segments are found in a per-(key, block) offset table (tile_bounds_kernel; the triple is
+// sorted by key, then by gather index, so each segment is a contiguous run of the key's
+// entries).  Each tile writes fp32 partial sums part[bt][cb][key][64]; tile_sum_kernel adds the
+// blocks in block order, adds the bias and transposes to the batch-major output.
+//
+// Lanes: SL slots of 64/SL lanes; slot s walks key 4*g + s of the wave's group g and each lane
+// holds SL batch columns (SL floats).  A group's entries are loaded 16 per chunk register (each
+// row of 16 lanes holds entries j = 0..15 of its slot's chunk), one group ahead of the compute.
+// Step t of a chunk hands entry t to every lane of its row with DPP row_newbcast:t, folded into
+// the address add and (inline asm) into the FMA, so one step costs one LDS read of SL floats
+// per lane, one address add and SL FMAs.  Entries past a segment's end point at the zero row
+// with value 0.
+constexpr int kTileThreads = 1024;
+constexpr int kTileWaves = kTileThreads / kWave;
+constexpr int kTileBatch = 64;                        // batch columns of a tile: one 256-byte LDS row
+constexpr int kTileLdsRows = 640;                     // 160 KB of LDS
+constexpr int kTileMaxCols = kTileLdsRows - 1;        // operand rows per block (one more is the zero row)
+constexpr int kTileStageIters = kTileLdsRows * 16 / kTileThreads;  // float4 loads per thread to stage
+
+// lane T of each row of 16 lanes, broadcast to the row (DPP row_newbcast)
+template <int T>
+__device__ __forceinline__ uint32_t bcast16(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x150 + T, 0xF, 0xF, true));
+}
+
+// acc += (lane T of this row's v) * x.  The compiler does not fold a DPP move into v_fmac, so it
+// is written out; NOP1 adds the two wait states a VALU write of v needs before a DPP read of it
+// (used on the first step of a chunk: v is not written again until the chunk is done).
+template <int T, bool NOP1>
+__device__ __forceinline__ void fmac_bcast16(float &acc, float v, float x) {
+    if constexpr (NOP1)
+        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(acc) : "v"(v), "v"(x), "n"(T));
+    else
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(acc) : "v"(v), "v"(x), "n"(T));
+}
+
+template <int SL>
+struct TileVec;
+template <>
+struct TileVec<1> { typedef float T; };
+template <>
+struct TileVec<2> { typedef float2 T; };
+template <>
+struct TileVec<4> { typedef float4 T; };
+
+__device__ __forceinline__ float vget(const float &v, int) { return v; }
+__device__ __forceinline__ float vget(const float2 &v, int i) { return i == 0 ? v.x : v.y; }
+__device__ __forceinline__ float vget(const float4 &v, int i) {
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Four steps T0..T0+3 of one chunk: the four LDS reads first, then the FMAs.
+template <int SL, int T0>
+__device__ __forceinline__ void tile_steps4(float (&acc)[SL], uint32_t off, float v, uint32_t lane_off,
+                                            const char *lds) {
+    typedef typename TileVec<SL>::T V;
+    V x[4];
+    x[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) + lane_off));
+    x[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
+    x[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
+    x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+        fmac_bcast16<T0 + 0, T0 == 0>(acc[i], v, vget(x[0], i));
+        fmac_bcast16<T0 + 1, false>(acc[i], v, vget(x[1], i));
+        fmac_bcast16<T0 + 2, false>(acc[i], v, vget(x[2], i));
+        fmac_bcast16<T0 + 3, false>(acc[i], v, vget(x[3], i));
+    }
+}
+
+// One chunk of 16 entries, nst (uniform, 1..16) of them real for the longest slot.
+template <int SL>
+__device__ __forceinline__ void tile_chunk(float (&acc)[SL], uint32_t off, float v, int nst, uint32_t lane_off,
+                                           const char *lds) {
+    tile_steps4<SL, 0>(acc, off, v, lane_off, lds);
+    if (nst > 4) tile_steps4<SL, 4>(acc, off, v, lane_off, lds);
+    if (nst > 8) tile_steps4<SL, 8>(acc, off, v, lane_off, lds);
+    if (nst > 12) tile_steps4<SL, 12>(acc, off, v, lane_off, lds);
+}
+
+// tab[key][j] = first entry of the key at or past gather index j*cw (j = 0..ncb): the segment of
+// block j is [tab[key][j], tab[key][j+1]).
+__global__ __launch_bounds__(kBlock) void tile_bounds_kernel(int nkeys, int ncb, int cw,
+                                                             const int32_t *__restrict__ offs,
+                                                             const int32_t *__restrict__ gidx,
+                                                             int32_t *__restrict__ tab) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i >= static_cast<int64_t>(nkeys) * (ncb + 1)) return;
+    const int key = static_cast<int>(i / (ncb + 1)), j = static_cast<int>(i % (ncb + 1));
+    int lo = offs[key], hi = offs[key + 1];
+    if (j > 0 && j < ncb) {
+        const int c = j * cw;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (gidx[mid] < c) lo = mid + 1;
+            else hi = mid;
+        }
+    } else if (j == ncb) {
+        lo = hi;
+    }
+    tab[i] = lo;
+}
+
+// opnd: feature-major [opnd_rows (+1)][ld] fp32, ld a multiple of 64; batch tile bt = blockIdx.y
+// covers columns [64 bt, 64 bt + 64).  Logical workgroup L = cb * nrb + rb (XCD-contiguous).
+template <int SL, int CH>
+__global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
+    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
+    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const float *__restrict__ opnd,
+    int opnd_rows, int ld, float *__restrict__ part) {
+    extern __shared__ float4 xs4[];
+    const int64_t L = xcd_block();
+    if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
+    const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
+    const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
+    const int bt = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int j = lane & 15;                    // entry of a chunk held by this lane
+    const int slot = (lane >> 4) * SL / 4;      // rows of 16 lanes per slot: 4 / SL
+    const int ls = lane % (kWave / SL);         // lane within the slot: batch columns [ls*SL, ls*SL + SL)
+    const uint32_t lane_off = static_cast<uint32_t>(ls * SL * 4);
+    const uint32_t zoff = static_cast<uint32_t>(cw) * 256u;
+    const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
+    // group g of this wave: keys k_lo + (wave + kTileWaves * g) * SL + slot; keys_per_rb <= 1024
+    // keeps a wave's keys within 64, so lane g*SL + s holds the segment of group g's slot s
+    const int ngroups = (k_hi - k_lo + SL - 1) / SL;
+    const int my_groups = wave < ngroups ? (ngroups - wave + kTileWaves - 1) / kTileWaves : 0;
+    const int key_l = k_lo + (wave + kTileWaves * (lane / SL)) * SL + lane % SL;
+    const bool key_l_ok = lane / SL < my_groups && key_l < k_hi;
+    int seg_a, seg_e;  // issued before the staging loads, used after them
+    {
+        const int64_t at = static_cast<int64_t>(key_l_ok ? key_l : k_lo) * (ncb + 1) + cb;
+        seg_a = tab[at];
+        seg_e = tab[at + 1];
+    }
+    {  // stage the block's operand rows; rows cn..cw are zero (row cw is the zero row)
+        const float4 *src = reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld + kTileBatch * bt);
+        const int ld4 = ld / 4, n4 = (cw + 1) * 16;
+        float4 tmp[kTileStageIters];
+#pragma unroll
+        for (int it = 0; it < kTileStageIters; ++it) {
+            const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
+            const int c = i >> 4, q = i & 15;
+            tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int it = 0; it < kTileStageIters; ++it) {
+            const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
+            if (i < n4) xs4[i] = tmp[it];
+        }
+    }
+    const int seg_len = key_l_ok ? seg_e - seg_a : 0;
+    __syncthreads();
+    const char *lds = reinterpret_cast<const char *>(xs4);
+    float *pout = part + (static_cast<int64_t>(bt) * ncb + cb) * static_cast<int64_t>(nkeys) * kTileBatch;
+    // Chunks are loaded two groups ahead of the compute (three buffers in rotation).  Loads are
+    // issued unconditionally (clamped indices) and masked where they are used.
+    auto load_chunks = [&](int g, int (&gi)[CH], float (&vv)[CH]) {
+        const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
+        const int a = __builtin_amdgcn_ds_bpermute(src, seg_a);
+        const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, seg_len) : 0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int idx = 16 * c + j < len ? a + 16 * c + j : 0;
+            gi[c] = gidx[idx];
+            vv[c] = vals[idx];
+        }
+    };
+    auto group_len = [&](int len) {
+        int m = __builtin_amdgcn_readlane(len, 0);
+        if constexpr (SL >= 2) m = max(m, __builtin_amdgcn_readlane(len, 32));
+        if constexpr (SL >= 4) m = max(m, max(__builtin_amdgcn_readlane(len, 16), __builtin_amdgcn_readlane(len, 48)));
+        return m;
+    };
+    auto compute = [&](int g, const int (&gi)[CH], const float (&vv)[CH]) {
+        const int src = (g * SL + slot) * 4;
+        const int a = __builtin_amdgcn_ds_bpermute(src, seg_a);
+        const int len = __builtin_amdgcn_ds_bpermute(src, seg_len);
+        const int m = group_len(len);
+        float acc[SL];
+#pragma unroll
+        for (int i = 0; i < SL; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (16 * c < m) {
+                const bool ok = 16 * c + j < len;
+                const uint32_t off = ok ? static_cast<uint32_t>(gi[c] - c0) * 256u : zoff;
+                const float v = ok ? vv[c] : 0.f;
+                tile_chunk<SL>(acc, off, v, m - 16 * c, lane_off, lds);
+            }
+        }
+        for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
+            const bool ok = 16 * c + j < len;
+            const int idx = ok ? a + 16 * c + j : 0;
+            const int gv = gidx[idx];
+            const float w = vals[idx];
+            tile_chunk<SL>(acc, ok ? static_cast<uint32_t>(gv - c0) * 256u : zoff, ok ? w : 0.f, m - 16 * c, lane_off,
+                           lds);
+        }
+        // every chunk register is consumed here, also those a short group skipped: without this
+        // use, refilling them would wait for loads issued after them
+#pragma unroll
+        for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]));
+        const int key = k_lo + (wave + kTileWaves * g) * SL + slot;
+        if (key < k_hi) {
+            typedef typename TileVec<SL>::T V;
+            V r;
+            if constexpr (SL == 1) r = acc[0];
+            else if constexpr (SL == 2) r = make_float2(acc[0], acc[1]);
+            else r = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * kTileBatch + ls * SL) = r;
+        }
+    };
+    int gi0[CH], gi1[CH], gi2[CH];
+    float vv0[CH], vv1[CH], vv2[CH];
+    load_chunks(0, gi0, vv0);
+    load_chunks(1, gi1, vv1);
+    for (int g = 0; g < my_groups; g += 3) {
+        load_chunks(g + 2, gi2, vv2);
+        compute(g, gi0, vv0);
+        if (g + 1 >= my_groups) break;
+        load_chunks(g + 3, gi0, vv0);
+        compute(g + 1, gi1, vv1);
+        if (g + 2 >= my_groups) break;
+        load_chunks(g + 4, gi1, vv1);
+        compute(g + 2, gi2, vv2);
+    }
+}
+
+// out[b][key] = bias[key] + sum over blocks cb (in order) of part[bt][cb][key][b - 64 bt], b < nbo.
+// A workgroup adds 32 keys x 64 batch columns of one batch tile and writes them transposed.
+template <typename OutT>
+__global__ __launch_bounds__(kBlock) void tile_sum_kernel(const float *__restrict__ part, int nkeys, int ncb,
+                                                          int64_t nbo, const float *__restrict__ bias,
+                                                          OutT *__restrict__ out, int64_t out_ld) {
+    constexpr int KB = 32;
+    __shared__ float tr[KB][kTileBatch + 1];
+    const int k0 = blockIdx.x * KB, bt = blockIdx.y;
+    const int t = threadIdx.x;
+    {
+        const int kk = t >> 3, qq = t & 7;  // key k0 + kk, batch columns [8 qq, 8 qq + 8)
+        float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+        if (k0 + kk < nkeys) {
+            const float4 *p = reinterpret_cast<const float4 *>(
+                part + ((static_cast<int64_t>(bt) * ncb) * nkeys + k0 + kk) * kTileBatch + 8 * qq);
+            const int64_t stride4 = static_cast<int64_t>(nkeys) * (kTileBatch / 4);
+            int cb = 0;
+            for (; cb + 4 <= ncb; cb += 4) {
+                float4 u[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    u[2 * i] = p[(cb + i) * stride4];
+                    u[2 * i + 1] = p[(cb + i) * stride4 + 1];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s0.x += u[2 * i].x; s0.y += u[2 * i].y; s0.z += u[2 * i].z; s0.w += u[2 * i].w;
+                    s1.x += u[2 * i + 1].x; s1.y += u[2 * i + 1].y; s1.z += u[2 * i + 1].z; s1.w += u[2 * i + 1].w;
+                }
+            }
+            for (; cb < ncb; ++cb) {
+                const float4 u0 = p[cb * stride4], u1 = p[cb * stride4 + 1];
+                s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
+                s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
+            }
+        }
+        float *row = &tr[kk][8 * qq];
+        row[0] = s0.x; row[1] = s0.y; row[2] = s0.z; row[3] = s0.w;
+        row[4] = s1.x; row[5] = s1.y; row[6] = s1.z; row[7] = s1.w;
+    }
+    __syncthreads();
+    const int b = t >> 2, kq = (t & 3) * (KB / 4);  // batch row 64 bt + b, keys [k0 + kq, +8)
+    const int64_t bb = static_cast<int64_t>(bt) * kTileBatch + b;
+    if (bb < nbo) {
+#pragma unroll
+        for (int i = 0; i < KB / 4; ++i) {
+            const int key = k0 + kq + i;
+            if (key < nkeys) store_act(out, bb * out_ld + key, tr[kq + i][b] + (bias ? bias[key] : 0.f));
         }
     }
 }
@@ -1549,7 +1841,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline int64_t round_up8(int64_t x) { return ceil_div(x, kXcds) * kXcds; }
 
-enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2, kCsr1 = 3, kCsr1Priv = 4 };
+enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2, kCsr1 = 3, kCsr1Priv = 4, kTile = 5 };
 constexpr int64_t kScatterLdsFloats = 16384;  // 64 KB private dX copy per workgroup
 
 // Device work plan of one gather-reduce (forward or input gradient).
@@ -1585,6 +1877,10 @@ struct SpmmPlan {
     bool direct;         // operand used in place (fp32, batch 1) instead of a transposed copy
     int64_t bpad;        // batch columns of the feature-major operand (rowwave: B rounded up to 4)
     size_t off_opnd, off_head, off_tail, off_cvals, total;
+    // kTile: slots per wave, prefetched chunks, column blocks, key blocks, block width, keys per
+    // key block, 64-column batch tiles; offset table and partial sums in the workspace
+    int tsl, tch, tncb, tnrb, tcw, tkpr, tnbt;
+    size_t off_tab, off_part;
 };
 
 // Batch columns of the feature-major copies.  The float4-lane kernels take batch tiles of
@@ -1705,6 +2001,54 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
     return p;
 }
 
+// The LDS-tiled gather-reduce (kTile) for batches padded to a multiple of 64 on layers of at
+// least kTileMinNnz entries whose segments per (key, block) average at least 8 entries, when the
+// walk reads the values in place.  SNACK_COO_TILE=0 in the environment turns it off; 1, 2 or 4
+// picks the slots per wave (batch columns per lane).
+constexpr int64_t kTileMinNnz = int64_t(1) << 20;
+
+int tile_env() {
+    const char *env = std::getenv("SNACK_COO_TILE");
+    if (!env) return -1;
+    if (!std::strcmp(env, "0")) return 0;
+    if (!std::strcmp(env, "1")) return 1;
+    if (!std::strcmp(env, "2")) return 2;
+    if (!std::strcmp(env, "4")) return 4;
+    return -1;
+}
+
+void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64_t B) {
+    const int env = tile_env();
+    if (env == 0) return;
+    const int64_t Bp = pad_batch(B);
+    if (Bp % kTileBatch != 0 || Bp / kTileBatch > 65535 || nnz < kTileMinNnz || opnd_rows < 1 || nkeys < 1) return;
+    const int64_t ncb = ceil_div(opnd_rows, kTileMaxCols);
+    const int64_t cw = ceil_div(opnd_rows, ncb);
+    const double mean = static_cast<double>(nnz) / static_cast<double>(nkeys * ncb);
+    if (mean < 8.0 || nkeys * (ncb + 1) >= (int64_t(1) << 31)) return;
+    p.mapping = kTile;
+    p.bpad = Bp;
+    p.tsl = env > 0 ? env : 4;
+    const double need = mean + 4.0 * std::sqrt(mean) + 1.0;
+    p.tch = need <= 32.0 ? 2 : (need <= 64.0 ? 4 : 8);
+    p.tncb = static_cast<int>(ncb);
+    p.tcw = static_cast<int>(cw);
+    const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256, ncb));
+    p.tkpr = static_cast<int>(std::min<int64_t>(ceil_div(nkeys, nrb0), kTileWaves * kWave));
+    p.tnrb = static_cast<int>(ceil_div(nkeys, p.tkpr));
+    p.tnbt = static_cast<int>(Bp / kTileBatch);
+    size_t at = 0;
+    p.off_opnd = at;
+    at = align_up(at + sizeof(float) * static_cast<size_t>((opnd_rows + 1) * Bp));
+    p.off_tab = at;
+    at = align_up(at + sizeof(int32_t) * static_cast<size_t>(nkeys * (ncb + 1)));
+    p.off_part = at;
+    at = align_up(at + sizeof(float) * static_cast<size_t>(p.tnbt) * static_cast<size_t>(ncb) *
+                           static_cast<size_t>(nkeys) * kTileBatch);
+    p.off_head = p.off_tail = at;
+    p.total = at;
+}
+
 // Appends n floats of workspace for values gathered into the order of the walk (off_cvals).
 void add_cvals(SpmmPlan &p, int64_t n) {
     p.cvals = true;
@@ -1720,6 +2064,9 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
     // they are in place: the batch-1 CSR walk of the forward serves it there, and the row walks
     // (private copies, scatter) are not used
     SpmmPlan p = plan_spmm_map(nnz, opnd_rows, nout, B, dtype, scatter_ok && !colvals, aligned16);
+    // values in the walk's order (the forward with values in row order, the input gradient with
+    // values in column order): the LDS-tiled walk where it applies
+    if (p.mapping == kRowwave && scatter_ok == colvals) plan_tile(p, nnz, opnd_rows, nout, B);
     // the rowwave walks read the values through a permutation -- the input gradient with values in
     // row order, the forward with values in column order -- once per batch tile; with 4 or more
     // tiles on a large layer they are gathered into the walk's order once, so every tile reads them
@@ -1983,6 +2330,64 @@ int launch_gather(const int32_t *idx, const float *src, int64_t n, float *dst, h
     return check_hip("gather_vals_kernel");
 }
 
+template <int SL, int CH>
+int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
+                       const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
+    const size_t lds = static_cast<size_t>(p.tcw + 1) * kTileBatch * sizeof(float);
+    static bool attr = false;  // the 160 KB of dynamic LDS, allowed once per instantiation
+    if (!attr) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_spmm_kernel<SL, CH>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess)
+            return fail(SNACK_ERR_HIP, "tile_spmm_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
+        attr = true;
+    }
+    const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)),
+                    static_cast<unsigned>(p.tnbt));
+    hipLaunchKernelGGL((tile_spmm_kernel<SL, CH>), grid, dim3(kTileThreads), lds, st, static_cast<int>(nkeys), p.tncb,
+                       p.tnrb, p.tcw, p.tkpr, tab, gidx, vals, opnd, static_cast<int>(opnd_rows),
+                       static_cast<int>(p.bpad), part);
+    return check_hip("tile_spmm_kernel");
+}
+
+template <int SL>
+int launch_tile_sl(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
+                   const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
+    switch (p.tch) {
+        case 2: return launch_tile_kernel<SL, 2>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st);
+        case 4: return launch_tile_kernel<SL, 4>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st);
+        case 8: return launch_tile_kernel<SL, 8>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st);
+        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported chunk count %d", p.tch);
+    }
+}
+
+// The LDS-tiled gather-reduce: segment table, tiles, block sums (bias, transpose).
+template <typename OutT>
+int launch_tile(const SpmmPlan &p, int64_t nkeys, const int32_t *offs, const int32_t *gidx, const float *vals,
+                const float *opnd, int64_t opnd_rows, int64_t B, const float *bias, OutT *out, char *ws,
+                hipStream_t st) {
+    int32_t *tab = reinterpret_cast<int32_t *>(ws + p.off_tab);
+    float *part = reinterpret_cast<float *>(ws + p.off_part);
+    probe(true, st);
+    const int64_t nt = nkeys * (p.tncb + 1);
+    hipLaunchKernelGGL(tile_bounds_kernel, dim3(static_cast<unsigned>(ceil_div(nt, kBlock))), dim3(kBlock), 0, st,
+                       static_cast<int>(nkeys), p.tncb, p.tcw, offs, gidx, tab);
+    if (int s = check_hip("tile_bounds_kernel")) return s;
+    int s;
+    switch (p.tsl) {
+        case 1: s = launch_tile_sl<1>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st); break;
+        case 2: s = launch_tile_sl<2>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st); break;
+        case 4: s = launch_tile_sl<4>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st); break;
+        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported slot count %d", p.tsl);
+    }
+    if (s) return s;
+    const dim3 sgrid(static_cast<unsigned>(ceil_div(nkeys, 32)), static_cast<unsigned>(p.tnbt));
+    hipLaunchKernelGGL(tile_sum_kernel<OutT>, sgrid, dim3(kBlock), 0, st, part, static_cast<int>(nkeys), p.tncb, B,
+                       bias, out, nkeys);
+    probe(false, st);
+    return check_hip("tile_sum_kernel");
+}
+
 // The gather-reduce shared by the forward (row order) and the input gradient
 // (column view).  nkeys = number of outputs per batch row; offs [nkeys+1].
 template <typename OutT>
@@ -1990,6 +2395,7 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
              const int32_t *gidx, const float *vals, const int32_t *perm, const float *opnd, int64_t opnd_rows,
              int64_t B, const float *bias, OutT *out, char *ws, hipStream_t st) {
     if (nkeys == 0 || B == 0) return SNACK_OK;
+    if (p.mapping == kTile) return launch_tile<OutT>(p, nkeys, offs, gidx, vals, opnd, opnd_rows, B, bias, out, ws, st);
     if (p.mapping == kRowwave) {
         probe(true, st);
         if (p.cvals && perm) {
