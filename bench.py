@@ -60,12 +60,13 @@ def algorithmic_bytes(op, nnz, O, I, B, s):
     return 12 * nnz + s * B * I + s * B * O  # dw: rows, cols, write dW; read X and dY
 
 
-def bwd_fused(B):
-    """Whether snack_coo_bwd runs its single column-view pass at this batch (the library's
-    rule: batches 2..256 are padded with zero columns to a tile of 4*BT*Q columns, BT a power of
-    two <= 16 and Q <= 4, and run fused; batch 1 and larger batches run the two gradients one
-    after the other).  Used to label timings only."""
-    return 2 <= B <= 256
+def bwd_fused(layer):
+    """Whether snack_coo_bwd runs its single column-view pass for this layer and batch (the
+    library's own choice, snack_coo_bwd_is_fused); otherwise it runs the two gradients as separate
+    passes and the step's dominant kernel is one of the three products.  Labels timings only."""
+    import coo_spmm_row_amd as snk
+    code = snk.SNACK_BF16 if layer.dtype == "bf16" else snk.SNACK_F32
+    return snk.snack_coo_bwd_is_fused(layer.W, layer.B, code)
 
 
 def column_order_step(layer, K):
@@ -433,7 +434,7 @@ def main():
     kernel_pct = {op: {f"p{q}": round(float(np.percentile(kern[op], q)) * 1000.0, 2) for q in (10, 50, 90)}
                   for op in all_ops}
     # the dominant kernel of the step (the fused backward pass when the batch allows it)
-    cand = STEP_OPS if bwd_fused(B) else SPLIT_OPS
+    cand = STEP_OPS if bwd_fused(layer) else SPLIT_OPS
     dom = max(cand, key=lambda o: kernel_us[o])
     kname = {"fwd": "forward gather-reduce", "dx": "input-gradient gather-reduce",
              "dw": "weight-gradient sampled product", "bwd": "fused backward pass (dX and dW)"}[dom]
@@ -446,7 +447,7 @@ def main():
                 "algorithmic_bytes": nbytes[dom]}
     extras = {"us_per_step_eager": round(eager_us, 2),
               "us_per_step_graph": None if graph_us is None else round(graph_us, 2),
-              "backward_fused": bwd_fused(B),
+              "backward_fused": bwd_fused(layer),
               "kernel_us": {op: round(v, 2) for op, v in kernel_us.items()},
               "kernel_us_percentiles": kernel_pct,
               "kernel_frac_hbm": {op: round(nbytes[op] / (kernel_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)

@@ -67,7 +67,8 @@ class _Desc(ctypes.Structure):
                 ("vals", ctypes.c_void_p), ("row_offsets", ctypes.c_void_p),
                 ("col_perm", ctypes.c_void_p), ("col_rows", ctypes.c_void_p),
                 ("col_cols", ctypes.c_void_p), ("col_offsets", ctypes.c_void_p),
-                ("row_to_col", ctypes.c_void_p)]
+                ("row_to_col", ctypes.c_void_p), ("row_blocks", ctypes.c_void_p),
+                ("col_blocks", ctypes.c_void_p)]
 
 
 _i64, _p, _u64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64
@@ -90,11 +91,17 @@ _lib.snack_coo_topology_workspace_bytes.restype = ctypes.c_size_t
 _lib.snack_coo_set_probe.argtypes = [_p, _p]
 _lib.snack_coo_invert_perm.argtypes = [_p, _i64, _p, _p]
 _lib.snack_coo_gather_f32.argtypes = [_p, _p, _i64, _p, _p]
+_lib.snack_coo_block_offsets_count.argtypes = [_D, ctypes.c_int]
+_lib.snack_coo_block_offsets_count.restype = ctypes.c_int64
+_lib.snack_coo_block_offsets.argtypes = [_D, ctypes.c_int, _p, _p]
+_lib.snack_coo_bwd_is_fused.argtypes = [_D, _i64, ctypes.c_int]
+SNACK_VIEW_ROWS, SNACK_VIEW_COLS = 0, 1
 
 EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_bwd_input",
             "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_coo_init_uniform",
             "snack_coo_topology_update_device", "snack_coo_topology_workspace_bytes", "snack_last_error",
-            "snack_coo_abi_version", "snack_coo_set_probe", "snack_coo_invert_perm", "snack_coo_gather_f32")
+            "snack_coo_abi_version", "snack_coo_set_probe", "snack_coo_invert_perm", "snack_coo_gather_f32",
+            "snack_coo_block_offsets_count", "snack_coo_block_offsets", "snack_coo_bwd_is_fused")
 
 
 def _np_ptr(a: Optional[np.ndarray]):
@@ -170,17 +177,30 @@ class SnackCOO:
 
     With ``row_to_col`` (the inverse of ``col_perm``) the values are kept in column-view order:
     ``vals[j]`` belongs to triple entry ``col_perm[j]``, and every dW the library returns for this
-    weight is in the same order (see ``to_column_order``)."""
+    weight is in the same order (see ``to_column_order``).
+
+    ``row_blocks`` / ``col_blocks`` are the segment tables of the tiled kernels (they depend on the
+    structure only).  ``blocks="build"`` (the default) builds them on the device when the weight
+    is on a GPU; pass tables built for the same structure (or ``blocks=None`` for none: each call
+    then builds its table in the workspace)."""
 
     def __init__(self, out_features, in_features, rows, cols, vals, row_offsets,
-                 col_perm=None, col_rows=None, col_cols=None, col_offsets=None, row_to_col=None):
+                 col_perm=None, col_rows=None, col_cols=None, col_offsets=None, row_to_col=None,
+                 row_blocks=None, col_blocks=None, blocks="build"):
         self.out_features, self.in_features = int(out_features), int(in_features)
         self.rows, self.cols, self.vals, self.row_offsets = rows, cols, vals, row_offsets
         self.col_perm, self.col_rows, self.col_cols, self.col_offsets = col_perm, col_rows, col_cols, col_offsets
         self.row_to_col = row_to_col
+        self.row_blocks, self.col_blocks = row_blocks, col_blocks
         self.nnz = int(rows.numel())
         self._desc = _Desc()
         self._refresh()
+        if blocks == "build" and rows.is_cuda:
+            if self.row_blocks is None:
+                self.row_blocks = snack_coo_block_offsets(self, SNACK_VIEW_ROWS)
+            if self.col_blocks is None and self.col_offsets is not None:
+                self.col_blocks = snack_coo_block_offsets(self, SNACK_VIEW_COLS)
+            self._refresh()
 
     @classmethod
     def from_built(cls, built: dict, device, vals=None):
@@ -201,6 +221,7 @@ class SnackCOO:
         d.col_perm, d.col_rows = ptr(self.col_perm), ptr(self.col_rows)
         d.col_cols, d.col_offsets = ptr(self.col_cols), ptr(self.col_offsets)
         d.row_to_col = ptr(self.row_to_col)
+        d.row_blocks, d.col_blocks = ptr(self.row_blocks), ptr(self.col_blocks)
 
     @property
     def desc(self):
@@ -215,15 +236,19 @@ class SnackCOO:
     def column_order(self) -> bool:
         return self.row_to_col is not None
 
-    def device_bytes(self) -> int:
+    def device_bytes(self, blocks: bool = True) -> int:
+        """Device bytes of the weight: the triple, row offsets, column view, value permutation and
+        (blocks=True) the segment tables."""
+        extra = (self.row_blocks, self.col_blocks) if blocks else ()
         return sum(int(x.numel() * x.element_size()) for x in
                    (self.rows, self.cols, self.vals, self.row_offsets, self.col_perm, self.col_rows,
-                    self.col_cols, self.col_offsets, self.row_to_col) if x is not None)
+                    self.col_cols, self.col_offsets, self.row_to_col) + extra if x is not None)
 
     def with_vals(self, vals) -> "SnackCOO":
         """The same structure (and value order) over other values."""
         return SnackCOO(self.out_features, self.in_features, self.rows, self.cols, vals, self.row_offsets,
-                        self.col_perm, self.col_rows, self.col_cols, self.col_offsets, self.row_to_col)
+                        self.col_perm, self.col_rows, self.col_cols, self.col_offsets, self.row_to_col,
+                        self.row_blocks, self.col_blocks, blocks=None)
 
     def to_column_order(self, stream=None) -> "SnackCOO":
         """This weight with its values in column-view order (new ``vals`` and ``row_to_col``
@@ -416,6 +441,28 @@ def snack_coo_gather_f32(src, idx, out=None, stream=None):
                                    ctypes.c_void_p(dst.data_ptr()), _stream_handle(src.device, stream))
     _check(st, "snack_coo_gather_f32")
     return dst
+
+
+def snack_coo_block_offsets(W: SnackCOO, view: int, out=None, stream=None):
+    """The segment table of one view (SNACK_VIEW_ROWS or SNACK_VIEW_COLS) on the device (int32)."""
+    import torch
+    n = int(_lib.snack_coo_block_offsets_count(W.desc, view))
+    if n < 0:
+        _check(6, "snack_coo_block_offsets_count")
+    t = out if out is not None else torch.empty(max(n, 1), dtype=torch.int32, device=W.device)
+    if t.numel() < n or t.dtype != torch.int32 or not t.is_cuda:
+        raise ValueError(f"out must be an int32 device tensor of at least {n} entries")
+    st = _lib.snack_coo_block_offsets(W.desc, view, ctypes.c_void_p(t.data_ptr()), _stream_handle(W.device, stream))
+    _check(st, "snack_coo_block_offsets")
+    return t
+
+
+def snack_coo_bwd_is_fused(W: SnackCOO, batch: int, act_dtype: int = 0) -> bool:
+    """Whether snack_coo_bwd runs its one-pass kernel (True) or two tiled passes (False)."""
+    r = int(_lib.snack_coo_bwd_is_fused(W.desc, int(batch), int(act_dtype)))
+    if r < 0:
+        _check(-r, "snack_coo_bwd_is_fused")
+    return r == 1
 
 
 def snack_coo_set_probe(start_event=None, stop_event=None):

@@ -81,7 +81,7 @@ using namespace snack;
 
 extern "C" const char *snack_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int snack_coo_abi_version(void) { return 5; }
+extern "C" int snack_coo_abi_version(void) { return 6; }
 
 extern "C" int snack_coo_build(int64_t O, int64_t I, int64_t nnz,
                                const int32_t *rows, const int32_t *cols, const float *vals,

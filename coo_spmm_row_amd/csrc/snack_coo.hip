@@ -596,11 +596,13 @@ __global__ __launch_bounds__(kBlock) void tile_bounds_kernel(int nkeys, int ncb,
 
 // opnd: feature-major [opnd_rows (+1)][ld] fp32, ld a multiple of 64; batch tile bt = blockIdx.y
 // covers columns [64 bt, 64 bt + 64).  Logical workgroup L = cb * nrb + rb (XCD-contiguous).
-template <int SL, int CH>
+// VP: the values are read through perm (vals[perm[k]]): the permutation is loaded with the gather
+// indices two groups ahead, the values it points at one group ahead.
+template <int SL, int CH, bool VP>
 __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
-    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const float *__restrict__ opnd,
-    int opnd_rows, int ld, float *__restrict__ part) {
+    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm,
+    const float *__restrict__ opnd, int opnd_rows, int ld, float *__restrict__ part) {
     extern __shared__ float4 xs4[];
     const int64_t L = xcd_block();
     if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
@@ -643,22 +645,28 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
             if (i < n4) xs4[i] = tmp[it];
         }
     }
-    const int seg_len = key_l_ok ? seg_e - seg_a : 0;
+    // lane l holds the segment and key of the wave's key l (group l / SL, slot l % SL)
+    const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : -1;
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(xs4);
     float *pout = part + (static_cast<int64_t>(bt) * ncb + cb) * static_cast<int64_t>(nkeys) * kTileBatch;
     // Chunks are loaded two groups ahead of the compute (three buffers in rotation).  Loads are
     // issued unconditionally (clamped indices) and masked where they are used.
-    auto load_chunks = [&](int g, int (&gi)[CH], float (&vv)[CH]) {
+    // vv: the values (VP: the permuted positions, turned into values by load_vals)
+    auto load_chunks = [&](int g, int (&gi)[CH], int (&vv)[CH]) {
         const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
-        const int a = __builtin_amdgcn_ds_bpermute(src, seg_a);
-        const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, seg_len) : 0;
+        const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
+        const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int idx = 16 * c + j < len ? a + 16 * c + j : 0;
             gi[c] = gidx[idx];
-            vv[c] = vals[idx];
+            vv[c] = VP ? perm[idx] : __float_as_int(vals[idx]);
         }
+    };
+    auto load_vals = [&](const int (&pm)[CH], int (&vv)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) vv[c] = __float_as_int(vals[pm[c]]);
     };
     auto group_len = [&](int len) {
         int m = __builtin_amdgcn_readlane(len, 0);
@@ -666,10 +674,11 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         if constexpr (SL >= 4) m = max(m, max(__builtin_amdgcn_readlane(len, 16), __builtin_amdgcn_readlane(len, 48)));
         return m;
     };
-    auto compute = [&](int g, const int (&gi)[CH], const float (&vv)[CH]) {
+    auto compute = [&](int g, const int (&gi)[CH], const int (&vv)[CH]) {
         const int src = (g * SL + slot) * 4;
-        const int a = __builtin_amdgcn_ds_bpermute(src, seg_a);
-        const int len = __builtin_amdgcn_ds_bpermute(src, seg_len);
+        const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
+        const int len = __builtin_amdgcn_ds_bpermute(src, s_len);
+        const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
         const int m = group_len(len);
         float acc[SL];
 #pragma unroll
@@ -679,7 +688,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
             if (16 * c < m) {
                 const bool ok = 16 * c + j < len;
                 const uint32_t off = ok ? static_cast<uint32_t>(gi[c] - c0) * 256u : zoff;
-                const float v = ok ? vv[c] : 0.f;
+                const float v = ok ? __int_as_float(vv[c]) : 0.f;
                 tile_chunk<SL>(acc, off, v, m - 16 * c, lane_off, lds);
             }
         }
@@ -687,7 +696,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
             const bool ok = 16 * c + j < len;
             const int idx = ok ? a + 16 * c + j : 0;
             const int gv = gidx[idx];
-            const float w = vals[idx];
+            const float w = vals[VP ? perm[idx] : idx];
             tile_chunk<SL>(acc, ok ? static_cast<uint32_t>(gv - c0) * 256u : zoff, ok ? w : 0.f, m - 16 * c, lane_off,
                            lds);
         }
@@ -695,8 +704,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         // use, refilling them would wait for loads issued after them
 #pragma unroll
         for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]));
-        const int key = k_lo + (wave + kTileWaves * g) * SL + slot;
-        if (key < k_hi) {
+        if (key >= 0) {
             typedef typename TileVec<SL>::T V;
             V r;
             if constexpr (SL == 1) r = acc[0];
@@ -706,68 +714,224 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         }
     };
     int gi0[CH], gi1[CH], gi2[CH];
-    float vv0[CH], vv1[CH], vv2[CH];
-    load_chunks(0, gi0, vv0);
-    load_chunks(1, gi1, vv1);
-    for (int g = 0; g < my_groups; g += 3) {
-        load_chunks(g + 2, gi2, vv2);
-        compute(g, gi0, vv0);
-        if (g + 1 >= my_groups) break;
-        load_chunks(g + 3, gi0, vv0);
-        compute(g + 1, gi1, vv1);
-        if (g + 2 >= my_groups) break;
-        load_chunks(g + 4, gi1, vv1);
-        compute(g + 2, gi2, vv2);
+    int vv0[CH], vv1[CH], vv2[CH];
+    if constexpr (!VP) {
+        load_chunks(0, gi0, vv0);
+        load_chunks(1, gi1, vv1);
+        for (int g = 0; g < my_groups; g += 3) {
+            load_chunks(g + 2, gi2, vv2);
+            compute(g, gi0, vv0);
+            if (g + 1 >= my_groups) break;
+            load_chunks(g + 3, gi0, vv0);
+            compute(g + 1, gi1, vv1);
+            if (g + 2 >= my_groups) break;
+            load_chunks(g + 4, gi1, vv1);
+            compute(g + 2, gi2, vv2);
+        }
+    } else {
+        int pm0[CH], pm1[CH], pm2[CH];
+        load_chunks(0, gi0, pm0);
+        load_chunks(1, gi1, pm1);
+        load_vals(pm0, vv0);
+        for (int g = 0; g < my_groups; g += 3) {
+            load_chunks(g + 2, gi2, pm2);
+            load_vals(pm1, vv1);
+            compute(g, gi0, vv0);
+            if (g + 1 >= my_groups) break;
+            load_chunks(g + 3, gi0, pm0);
+            load_vals(pm2, vv2);
+            compute(g + 1, gi1, vv1);
+            if (g + 2 >= my_groups) break;
+            load_chunks(g + 4, gi1, pm1);
+            load_vals(pm0, vv0);
+            compute(g + 2, gi2, vv2);
+        }
+    }
+}
+
+// Weight gradient on the same tiles: dW[k] = sum_b dY[b, row_k] X[b, col_k] for the entries of the
+// workgroup's (rows x column block) tile, with the block of X^T staged in LDS as above.  Slot s of
+// a group takes row 4g + s; each lane holds its 4 batch columns of that row's dY slice and, per
+// step, the dot product of its 4 columns with the entry's staged X row.  After a chunk of 16 steps
+// a reduce-scatter over the slot's 16 lanes leaves lane j with entry j's sum, stored in triple
+// order (16 consecutive entries per slot).  Batch tiles of 64 columns are taken in turn (the block
+// staged again), and tiles after the first add into dW; each entry belongs to one workgroup.
+template <int T0>
+__device__ __forceinline__ void tile_dot4(float (&p)[16], uint32_t off, uint32_t lane_off, const char *lds,
+                                          const float4 &dy) {
+    float4 x[4];
+    x[0] = *reinterpret_cast<const float4 *>(lds + (bcast16<T0 + 0>(off) + lane_off));
+    x[1] = *reinterpret_cast<const float4 *>(lds + (bcast16<T0 + 1>(off) + lane_off));
+    x[2] = *reinterpret_cast<const float4 *>(lds + (bcast16<T0 + 2>(off) + lane_off));
+    x[3] = *reinterpret_cast<const float4 *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        float d = x[u].x * dy.x;
+        d = fmaf(x[u].y, dy.y, d);
+        d = fmaf(x[u].z, dy.z, d);
+        p[T0 + u] = fmaf(x[u].w, dy.w, d);
+    }
+}
+
+template <int CH>
+__global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
+    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, int nbt, const int32_t *__restrict__ tab,
+    const int32_t *__restrict__ gidx, const float *__restrict__ opnd, int opnd_rows, const float *__restrict__ dyt,
+    int ld, float *__restrict__ dw) {
+    constexpr int SL = 4;
+    extern __shared__ float4 xs4[];
+    const int64_t L = xcd_block();
+    if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
+    const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
+    const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int j = lane & 15;
+    const int slot = lane >> 4;
+    const uint32_t lane_off = static_cast<uint32_t>(j * 16);
+    const uint32_t zoff = static_cast<uint32_t>(cw) * 256u;
+    const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
+    const int ngroups = (k_hi - k_lo + SL - 1) / SL;
+    const int my_groups = wave < ngroups ? (ngroups - wave + kTileWaves - 1) / kTileWaves : 0;
+    const int key_l = k_lo + (wave + kTileWaves * (lane / SL)) * SL + lane % SL;
+    const bool key_l_ok = lane / SL < my_groups && key_l < k_hi;
+    int seg_a, seg_e;
+    {
+        const int64_t at = static_cast<int64_t>(key_l_ok ? key_l : k_lo) * (ncb + 1) + cb;
+        seg_a = tab[at];
+        seg_e = tab[at + 1];
+    }
+    const char *lds = reinterpret_cast<const char *>(xs4);
+    for (int bt = 0; bt < nbt; ++bt) {
+        if (bt > 0) __syncthreads();  // the previous batch tile's reads of the block are done
+        {
+            const float4 *src =
+                reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld + kTileBatch * bt);
+            const int ld4 = ld / 4, n4 = (cw + 1) * 16;
+            float4 tmp[kTileStageIters];
+#pragma unroll
+            for (int it = 0; it < kTileStageIters; ++it) {
+                const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
+                const int c = i >> 4, q = i & 15;
+                tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int it = 0; it < kTileStageIters; ++it) {
+                const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
+                if (i < n4) xs4[i] = tmp[it];
+            }
+        }
+        const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : 0;
+        __syncthreads();
+        auto load_group = [&](int g, int (&gi)[CH], float4 &dy) {
+            const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
+            const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
+            const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+            const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
+#pragma unroll
+            for (int c = 0; c < CH; ++c) gi[c] = gidx[16 * c + j < len ? a + 16 * c + j : 0];
+            dy = *reinterpret_cast<const float4 *>(dyt + static_cast<int64_t>(key) * ld + kTileBatch * bt + 4 * j);
+        };
+        auto chunk = [&](int a, int len, int m, int c, uint32_t off, const float4 &dy) {
+            float p[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) p[t] = 0.f;
+            const int nst = m - 16 * c;
+            tile_dot4<0>(p, off, lane_off, lds, dy);
+            if (nst > 4) tile_dot4<4>(p, off, lane_off, lds, dy);
+            if (nst > 8) tile_dot4<8>(p, off, lane_off, lds, dy);
+            if (nst > 12) tile_dot4<12>(p, off, lane_off, lds, dy);
+            const float r = group_reduce_scatter<16, 16>(p, j);
+            if (16 * c + j < len) {
+                float *d = dw + a + 16 * c + j;
+                *d = bt == 0 ? r : *d + r;
+            }
+        };
+        auto compute = [&](int g, const int (&gi)[CH], const float4 &dy) {
+            const int src = (g * SL + slot) * 4;
+            const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
+            const int len = __builtin_amdgcn_ds_bpermute(src, s_len);
+            int m = max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
+                        max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                if (16 * c < m) {
+                    const bool ok = 16 * c + j < len;
+                    chunk(a, len, m, c, ok ? static_cast<uint32_t>(gi[c] - c0) * 256u : zoff, dy);
+                }
+            }
+            for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
+                const bool ok = 16 * c + j < len;
+                const int gv = gidx[ok ? a + 16 * c + j : 0];
+                chunk(a, len, m, c, ok ? static_cast<uint32_t>(gv - c0) * 256u : zoff, dy);
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]));
+            asm volatile("" ::"v"(dy.x), "v"(dy.y), "v"(dy.z), "v"(dy.w));
+        };
+        int gi0[CH], gi1[CH], gi2[CH];
+        float4 d0, d1, d2;
+        load_group(0, gi0, d0);
+        load_group(1, gi1, d1);
+        for (int g = 0; g < my_groups; g += 3) {
+            load_group(g + 2, gi2, d2);
+            compute(g, gi0, d0);
+            if (g + 1 >= my_groups) break;
+            load_group(g + 3, gi0, d0);
+            compute(g + 1, gi1, d1);
+            if (g + 2 >= my_groups) break;
+            load_group(g + 4, gi1, d1);
+            compute(g + 2, gi2, d2);
+        }
     }
 }
 
 // out[b][key] = bias[key] + sum over blocks cb (in order) of part[bt][cb][key][b - 64 bt], b < nbo.
-// A workgroup adds 32 keys x 64 batch columns of one batch tile and writes them transposed.
+// A workgroup adds 16 keys x 64 batch columns of one batch tile (one float4 per thread and block,
+// up to 16 blocks' loads in flight) and writes them transposed.
+constexpr int kSumKeys = 16;
 template <typename OutT>
 __global__ __launch_bounds__(kBlock) void tile_sum_kernel(const float *__restrict__ part, int nkeys, int ncb,
                                                           int64_t nbo, const float *__restrict__ bias,
                                                           OutT *__restrict__ out, int64_t out_ld) {
-    constexpr int KB = 32;
-    __shared__ float tr[KB][kTileBatch + 1];
-    const int k0 = blockIdx.x * KB, bt = blockIdx.y;
+    __shared__ float tr[kSumKeys][kTileBatch + 1];
+    const int k0 = blockIdx.x * kSumKeys, bt = blockIdx.y;
     const int t = threadIdx.x;
     {
-        const int kk = t >> 3, qq = t & 7;  // key k0 + kk, batch columns [8 qq, 8 qq + 8)
-        float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+        const int kk = t >> 4, qq = t & 15;  // key k0 + kk, batch columns [4 qq, 4 qq + 4)
+        float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f);
         if (k0 + kk < nkeys) {
             const float4 *p = reinterpret_cast<const float4 *>(
-                part + ((static_cast<int64_t>(bt) * ncb) * nkeys + k0 + kk) * kTileBatch + 8 * qq);
+                part + ((static_cast<int64_t>(bt) * ncb) * nkeys + k0 + kk) * kTileBatch + 4 * qq);
             const int64_t stride4 = static_cast<int64_t>(nkeys) * (kTileBatch / 4);
-            int cb = 0;
-            for (; cb + 4 <= ncb; cb += 4) {
-                float4 u[8];
+            for (int cb0 = 0; cb0 < ncb; cb0 += 16) {
+                float4 u[16];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    u[2 * i] = p[(cb + i) * stride4];
-                    u[2 * i + 1] = p[(cb + i) * stride4 + 1];
-                }
+                for (int i = 0; i < 16; ++i)
+                    u[i] = cb0 + i < ncb ? p[(cb0 + i) * stride4] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s0.x += u[2 * i].x; s0.y += u[2 * i].y; s0.z += u[2 * i].z; s0.w += u[2 * i].w;
-                    s1.x += u[2 * i + 1].x; s1.y += u[2 * i + 1].y; s1.z += u[2 * i + 1].z; s1.w += u[2 * i + 1].w;
+                for (int i = 0; i < 16; ++i) {
+                    if (cb0 + i < ncb) {
+                        s0.x += u[i].x;
+                        s0.y += u[i].y;
+                        s0.z += u[i].z;
+                        s0.w += u[i].w;
+                    }
                 }
-            }
-            for (; cb < ncb; ++cb) {
-                const float4 u0 = p[cb * stride4], u1 = p[cb * stride4 + 1];
-                s0.x += u0.x; s0.y += u0.y; s0.z += u0.z; s0.w += u0.w;
-                s1.x += u1.x; s1.y += u1.y; s1.z += u1.z; s1.w += u1.w;
             }
         }
-        float *row = &tr[kk][8 * qq];
-        row[0] = s0.x; row[1] = s0.y; row[2] = s0.z; row[3] = s0.w;
-        row[4] = s1.x; row[5] = s1.y; row[6] = s1.z; row[7] = s1.w;
+        float *row = &tr[kk][4 * qq];
+        row[0] = s0.x;
+        row[1] = s0.y;
+        row[2] = s0.z;
+        row[3] = s0.w;
     }
     __syncthreads();
-    const int b = t >> 2, kq = (t & 3) * (KB / 4);  // batch row 64 bt + b, keys [k0 + kq, +8)
+    const int b = t >> 2, kq = (t & 3) * (kSumKeys / 4);  // batch row 64 bt + b, keys [k0 + kq, +4)
     const int64_t bb = static_cast<int64_t>(bt) * kTileBatch + b;
     if (bb < nbo) {
 #pragma unroll
-        for (int i = 0; i < KB / 4; ++i) {
+        for (int i = 0; i < kSumKeys / 4; ++i) {
             const int key = k0 + kq + i;
             if (key < nkeys) store_act(out, bb * out_ld + key, tr[kq + i][b] + (bias ? bias[key] : 0.f));
         }
@@ -1828,9 +1992,11 @@ using snack::fail;
 
 thread_local hipEvent_t g_probe_start = nullptr;
 thread_local hipEvent_t g_probe_stop = nullptr;
+thread_local int g_probe_mute = 0;  // > 0: a caller brackets several launches itself
 
 // Records the armed probe's start event (before the main kernel) or stop event (after it).
 inline void probe(bool start, hipStream_t st) {
+    if (g_probe_mute > 0) return;
     hipEvent_t e = start ? g_probe_start : g_probe_stop;
     if (e) (void)hipEventRecord(e, st);
 }
@@ -2017,13 +2183,20 @@ int tile_env() {
     return -1;
 }
 
+// Column blocks over n operand rows: ncb = ceil(n / kTileMaxCols) blocks of cw = ceil(n / ncb)
+// (the layout of snack_coo_desc.row_blocks / col_blocks; one block for n = 0).
+void tile_blocks(int64_t n, int64_t &ncb, int64_t &cw) {
+    ncb = std::max<int64_t>(1, ceil_div(n, kTileMaxCols));
+    cw = std::max<int64_t>(1, ceil_div(n, ncb));
+}
+
 void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64_t B) {
     const int env = tile_env();
     if (env == 0) return;
     const int64_t Bp = pad_batch(B);
     if (Bp % kTileBatch != 0 || Bp / kTileBatch > 65535 || nnz < kTileMinNnz || opnd_rows < 1 || nkeys < 1) return;
-    const int64_t ncb = ceil_div(opnd_rows, kTileMaxCols);
-    const int64_t cw = ceil_div(opnd_rows, ncb);
+    int64_t ncb, cw;
+    tile_blocks(opnd_rows, ncb, cw);
     const double mean = static_cast<double>(nnz) / static_cast<double>(nkeys * ncb);
     if (mean < 8.0 || nkeys * (ncb + 1) >= (int64_t(1) << 31)) return;
     p.mapping = kTile;
@@ -2064,9 +2237,10 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
     // they are in place: the batch-1 CSR walk of the forward serves it there, and the row walks
     // (private copies, scatter) are not used
     SpmmPlan p = plan_spmm_map(nnz, opnd_rows, nout, B, dtype, scatter_ok && !colvals, aligned16);
-    // values in the walk's order (the forward with values in row order, the input gradient with
-    // values in column order): the LDS-tiled walk where it applies
-    if (p.mapping == kRowwave && scatter_ok == colvals) plan_tile(p, nnz, opnd_rows, nout, B);
+    // the LDS-tiled walk where it applies (values in the walk's order, or read through the
+    // permutation: the input gradient with values in row order, the forward in column order)
+    if (p.mapping == kRowwave) plan_tile(p, nnz, opnd_rows, nout, B);
+    if (p.mapping == kTile && scatter_ok != colvals && p.tnbt >= 4) add_cvals(p, nnz);
     // the rowwave walks read the values through a permutation -- the input gradient with values in
     // row order, the forward with values in column order -- once per batch tile; with 4 or more
     // tiles on a large layer they are gathered into the walk's order once, so every tile reads them
@@ -2088,6 +2262,11 @@ struct SddmmPlan {
     int64_t bpad;        // batch columns of the feature-major copies (rowsddmm: B rounded up to 4)
     size_t off_dw;       // row-order dW staging (values in column order)
     size_t off_x, off_dy, total;
+    // LDS-tiled weight gradient (tile_sddmm_kernel): chunks, column blocks, key blocks, block
+    // width, keys per key block, 64-column batch tiles; segment table in the workspace
+    bool tile;
+    int tch, tncb, tnrb, tcw, tkpr, tnbt;
+    size_t off_tab;
 };
 
 // colvals: dW goes out in column-view order; the kernels write it in row order to the
@@ -2144,6 +2323,28 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
         p.steps = round_up(ceil_div(std::max<int64_t>(nnz, 1), 8192), 256);  // entries per wave
         p.waves = ceil_div(nnz, p.steps);
     }
+    // the LDS-tiled walk: batches padded to a multiple of 64 on large layers whose (row, column
+    // block) segments average at least 8 entries
+    if (!p.csr1 && tile_env() != 0 && Bp % kTileBatch == 0 && nnz >= kTileMinNnz && I > 0 && O > 0) {
+        int64_t ncb, cw;
+        tile_blocks(I, ncb, cw);
+        const double mean = static_cast<double>(nnz) / static_cast<double>(O * ncb);
+        if (mean >= 8.0 && O * (ncb + 1) < (int64_t(1) << 31)) {
+            p.tile = true;
+            p.rowq = 0;
+            p.slices = 1;
+            p.bpad = Bp;
+            p.x_direct = p.dy_direct = false;
+            const double need = mean + 4.0 * std::sqrt(mean) + 1.0;
+            p.tch = need <= 32.0 ? 2 : (need <= 64.0 ? 4 : 8);
+            p.tncb = static_cast<int>(ncb);
+            p.tcw = static_cast<int>(cw);
+            const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256, ncb));
+            p.tkpr = static_cast<int>(std::min<int64_t>(ceil_div(O, nrb0), kTileWaves * kWave));
+            p.tnrb = static_cast<int>(ceil_div(O, p.tkpr));
+            p.tnbt = static_cast<int>(Bp / kTileBatch);
+        }
+    }
     size_t at = 0;
     p.off_x = at;
     if (!p.x_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * p.bpad));
@@ -2151,8 +2352,55 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
     if (!p.dy_direct) at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * p.bpad));
     p.off_dw = at;
     if (colvals && nnz > 0 && !p.csr1) at = align_up(at + sizeof(float) * static_cast<size_t>(nnz));
+    p.off_tab = at;
+    if (p.tile) at = align_up(at + sizeof(int32_t) * static_cast<size_t>(O * (p.tncb + 1)));
     p.total = at;
     return p;
+}
+
+int check_hip(const char *what);
+int launch_bounds(int64_t nkeys, int ncb, int cw, const int32_t *offs, const int32_t *gidx, int32_t *tab,
+                  hipStream_t st);
+
+template <int CH>
+int launch_tile_sddmm_kernel(const SddmmPlan &p, int64_t O, int64_t I, const int32_t *tab, const int32_t *cols,
+                             const float *xt, const float *dyt, float *dw, hipStream_t st) {
+    const size_t lds = static_cast<size_t>(p.tcw + 1) * kTileBatch * sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_sddmm_kernel<CH>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess)
+            return fail(SNACK_ERR_HIP, "tile_sddmm_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
+        attr = true;
+    }
+    const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)));
+    hipLaunchKernelGGL((tile_sddmm_kernel<CH>), grid, dim3(kTileThreads), lds, st, static_cast<int>(O), p.tncb,
+                       p.tnrb, p.tcw, p.tkpr, p.tnbt, tab, cols, xt, static_cast<int>(I), dyt,
+                       static_cast<int>(p.bpad), dw);
+    return check_hip("tile_sddmm_kernel");
+}
+
+// The tiled weight gradient (row view): segment table (unless the layer has one), then the tiles.
+int launch_tile_sddmm(const SddmmPlan &p, const snack_coo_desc *W, const float *xt, const float *dyt, float *dw,
+                      int32_t *tab_ws, hipStream_t st) {
+    const int64_t O = W->out_features, I = W->in_features;
+    const int32_t *tab = W->row_blocks;
+    probe(true, st);
+    if (!tab) {
+        int32_t *t = tab_ws;
+        if (int s = launch_bounds(O, p.tncb, p.tcw, W->row_offsets, W->cols, t, st)) return s;
+        tab = t;
+    }
+    int s;
+    switch (p.tch) {
+        case 2: s = launch_tile_sddmm_kernel<2>(p, O, I, tab, W->cols, xt, dyt, dw, st); break;
+        case 4: s = launch_tile_sddmm_kernel<4>(p, O, I, tab, W->cols, xt, dyt, dw, st); break;
+        case 8: s = launch_tile_sddmm_kernel<8>(p, O, I, tab, W->cols, xt, dyt, dw, st); break;
+        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported chunk count %d", p.tch);
+    }
+    probe(false, st);
+    return s;
 }
 
 // Backward pass plan: the fused column-view kernel for (padded) batches 4*BT*Q (Q in 1..4)
@@ -2163,6 +2411,12 @@ struct BwdPlan {
     int bt, q, nb;  // nb: row bands of the fused kernel (1 or kXcds)
     int64_t bpad;   // batch columns of the feature-major copies (B rounded up to 4)
     size_t off_x, off_dy, off_part, total;
+    // split: both gradients tiled, sharing the feature-major copies at off_x / off_dy; the input
+    // gradient's workspace starts at off_spmm, the weight gradient's segment table at off_sddmm
+    bool split;
+    SpmmPlan sp;
+    SddmmPlan sd;
+    size_t off_spmm, off_sddmm;
 };
 
 // Smallest lane count per slot of the one-pass backward (1: batches 4, 8, 12 take it too).
@@ -2204,6 +2458,31 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
             }
         }
     }
+    // both gradients tiled (the input gradient over the column view reading the values through
+    // col_perm, the weight gradient over the row view), one after the other, instead of the fused
+    // pass: values in row order and one 64-column batch tile (with more tiles, or values in column
+    // order, the fused pass measured faster)
+    if (p.fused && !colvals && Bp == kTileBatch) {
+        const SpmmPlan sp = plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals);
+        const SddmmPlan sd = plan_sddmm(nnz, O, I, B, dtype, colvals);
+        if (sp.mapping == kTile && sd.tile && sp.bpad == Bp && sd.bpad == Bp) {
+            p.fused = false;
+            p.split = true;
+            p.sp = sp;
+            p.sd = sd;
+            size_t at = 0;
+            p.off_x = at;
+            at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * Bp));
+            p.off_dy = at;
+            at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * Bp));
+            p.off_spmm = at;
+            at = align_up(at + sp.total);
+            p.off_sddmm = at;
+            at = align_up(at + sizeof(int32_t) * static_cast<size_t>(O * (sd.tncb + 1)));
+            p.total = at;
+            return p;
+        }
+    }
     if (p.fused) {
         size_t at = 0;
         p.off_x = at;
@@ -2240,6 +2519,8 @@ int check_desc(const snack_coo_desc *W, bool need_colview, const char *who) {
         (!W->col_offsets || (nnz > 0 && (!W->col_perm || !W->col_rows || !W->col_cols))))
         return fail(SNACK_ERR_NULL, "%s: the column view (col_perm, col_rows, col_cols, col_offsets) is required%s",
                     who, W->row_to_col ? " with values in column order" : "");
+    if (W->col_blocks && !W->col_offsets)
+        return fail(SNACK_ERR_NULL, "%s: col_blocks needs the column view", who);
     return SNACK_OK;
 }
 
@@ -2330,13 +2611,13 @@ int launch_gather(const int32_t *idx, const float *src, int64_t n, float *dst, h
     return check_hip("gather_vals_kernel");
 }
 
-template <int SL, int CH>
+template <int SL, int CH, bool VP>
 int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
-                       const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
+                       const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
     const size_t lds = static_cast<size_t>(p.tcw + 1) * kTileBatch * sizeof(float);
     static bool attr = false;  // the 160 KB of dynamic LDS, allowed once per instantiation
     if (!attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_spmm_kernel<SL, CH>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_spmm_kernel<SL, CH, VP>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess)
             return fail(SNACK_ERR_HIP, "tile_spmm_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
@@ -2344,44 +2625,63 @@ int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, con
     }
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)),
                     static_cast<unsigned>(p.tnbt));
-    hipLaunchKernelGGL((tile_spmm_kernel<SL, CH>), grid, dim3(kTileThreads), lds, st, static_cast<int>(nkeys), p.tncb,
-                       p.tnrb, p.tcw, p.tkpr, tab, gidx, vals, opnd, static_cast<int>(opnd_rows),
+    hipLaunchKernelGGL((tile_spmm_kernel<SL, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(nkeys),
+                       p.tncb, p.tnrb, p.tcw, p.tkpr, tab, gidx, vals, perm, opnd, static_cast<int>(opnd_rows),
                        static_cast<int>(p.bpad), part);
     return check_hip("tile_spmm_kernel");
 }
 
-template <int SL>
-int launch_tile_sl(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
-                   const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
+template <int SL, bool VP>
+int launch_tile_ch(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
+                   const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
     switch (p.tch) {
-        case 2: return launch_tile_kernel<SL, 2>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st);
-        case 4: return launch_tile_kernel<SL, 4>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st);
-        case 8: return launch_tile_kernel<SL, 8>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st);
+        case 2: return launch_tile_kernel<SL, 2, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
+        case 4: return launch_tile_kernel<SL, 4, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
+        case 8: return launch_tile_kernel<SL, 8, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
         default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported chunk count %d", p.tch);
     }
 }
 
+template <int SL>
+int launch_tile_sl(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
+                   const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
+    if (perm) return launch_tile_ch<SL, true>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
+    return launch_tile_ch<SL, false>(p, nkeys, tab, gidx, vals, nullptr, opnd, opnd_rows, part, st);
+}
+
 // The LDS-tiled gather-reduce: segment table, tiles, block sums (bias, transpose).
+int launch_bounds(int64_t nkeys, int ncb, int cw, const int32_t *offs, const int32_t *gidx, int32_t *tab,
+                  hipStream_t st) {
+    const int64_t nt = nkeys * (ncb + 1);
+    if (nt == 0) return SNACK_OK;
+    hipLaunchKernelGGL(tile_bounds_kernel, dim3(static_cast<unsigned>(ceil_div(nt, kBlock))), dim3(kBlock), 0, st,
+                       static_cast<int>(nkeys), ncb, cw, offs, gidx, tab);
+    return check_hip("tile_bounds_kernel");
+}
+
+// blocks: the layer's segment table for this walk (snack_coo_desc.row_blocks / col_blocks), or
+// NULL to build it in the workspace first.
 template <typename OutT>
 int launch_tile(const SpmmPlan &p, int64_t nkeys, const int32_t *offs, const int32_t *gidx, const float *vals,
-                const float *opnd, int64_t opnd_rows, int64_t B, const float *bias, OutT *out, char *ws,
-                hipStream_t st) {
-    int32_t *tab = reinterpret_cast<int32_t *>(ws + p.off_tab);
+                const int32_t *perm, const int32_t *blocks, const float *opnd, int64_t opnd_rows, int64_t B,
+                const float *bias, OutT *out, char *ws, hipStream_t st) {
+    const int32_t *tab = blocks;
     float *part = reinterpret_cast<float *>(ws + p.off_part);
     probe(true, st);
-    const int64_t nt = nkeys * (p.tncb + 1);
-    hipLaunchKernelGGL(tile_bounds_kernel, dim3(static_cast<unsigned>(ceil_div(nt, kBlock))), dim3(kBlock), 0, st,
-                       static_cast<int>(nkeys), p.tncb, p.tcw, offs, gidx, tab);
-    if (int s = check_hip("tile_bounds_kernel")) return s;
+    if (!tab) {
+        int32_t *t = reinterpret_cast<int32_t *>(ws + p.off_tab);
+        if (int s = launch_bounds(nkeys, p.tncb, p.tcw, offs, gidx, t, st)) return s;
+        tab = t;
+    }
     int s;
     switch (p.tsl) {
-        case 1: s = launch_tile_sl<1>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st); break;
-        case 2: s = launch_tile_sl<2>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st); break;
-        case 4: s = launch_tile_sl<4>(p, nkeys, tab, gidx, vals, opnd, opnd_rows, part, st); break;
+        case 1: s = launch_tile_sl<1>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
+        case 2: s = launch_tile_sl<2>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
+        case 4: s = launch_tile_sl<4>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
         default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported slot count %d", p.tsl);
     }
     if (s) return s;
-    const dim3 sgrid(static_cast<unsigned>(ceil_div(nkeys, 32)), static_cast<unsigned>(p.tnbt));
+    const dim3 sgrid(static_cast<unsigned>(ceil_div(nkeys, kSumKeys)), static_cast<unsigned>(p.tnbt));
     hipLaunchKernelGGL(tile_sum_kernel<OutT>, sgrid, dim3(kBlock), 0, st, part, static_cast<int>(nkeys), p.tncb, B,
                        bias, out, nkeys);
     probe(false, st);
@@ -2393,9 +2693,17 @@ int launch_tile(const SpmmPlan &p, int64_t nkeys, const int32_t *offs, const int
 template <typename OutT>
 int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys, const int32_t *offs,
              const int32_t *gidx, const float *vals, const int32_t *perm, const float *opnd, int64_t opnd_rows,
-             int64_t B, const float *bias, OutT *out, char *ws, hipStream_t st) {
+             int64_t B, const float *bias, OutT *out, char *ws, hipStream_t st, const int32_t *blocks) {
     if (nkeys == 0 || B == 0) return SNACK_OK;
-    if (p.mapping == kTile) return launch_tile<OutT>(p, nkeys, offs, gidx, vals, opnd, opnd_rows, B, bias, out, ws, st);
+    if (p.mapping == kTile) {
+        if (p.cvals && perm) {  // several batch tiles: the values gathered into walk order once
+            float *cv = reinterpret_cast<float *>(ws + p.off_cvals);
+            if (int s = launch_gather(perm, vals, nnz, cv, st)) return s;
+            vals = cv;
+            perm = nullptr;
+        }
+        return launch_tile<OutT>(p, nkeys, offs, gidx, vals, perm, blocks, opnd, opnd_rows, B, bias, out, ws, st);
+    }
     if (p.mapping == kRowwave) {
         probe(true, st);
         if (p.cvals && perm) {
@@ -2548,10 +2856,10 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         int s;
         if (act_dtype == SNACK_F32)
             s = run_spmm<float>(p, O, nnz, W->rows, W->row_offsets, W->cols, vals, vperm, xt, I, batch, bias,
-                                static_cast<float *>(Y), ws, st);
+                                static_cast<float *>(Y), ws, st, W->row_blocks);
         else
             s = run_spmm<bf16_t>(p, O, nnz, W->rows, W->row_offsets, W->cols, vals, vperm, xt, I, batch, bias,
-                                 static_cast<bf16_t *>(Y), ws, st);
+                                 static_cast<bf16_t *>(Y), ws, st, W->row_blocks);
         return s ? s : snack::ok();
     } catch (...) {
         return fail(SNACK_ERR_INTERNAL, "snack_coo_fwd: unexpected exception");
@@ -2668,10 +2976,10 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         int s;
         if (act_dtype == SNACK_F32)
             s = run_spmm<float>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, vperm, dyt, O,
-                                batch, nullptr, static_cast<float *>(dX), ws, st);
+                                batch, nullptr, static_cast<float *>(dX), ws, st, W->col_blocks);
         else
             s = run_spmm<bf16_t>(p, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, vperm, dyt, O,
-                                 batch, nullptr, static_cast<bf16_t *>(dX), ws, st);
+                                 batch, nullptr, static_cast<bf16_t *>(dX), ws, st, W->col_blocks);
         return s ? s : snack::ok();
     } catch (...) {
         return fail(SNACK_ERR_INTERNAL, "snack_coo_bwd_input: unexpected exception");
@@ -2756,6 +3064,11 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st, nullptr, 0, nullptr, p.bpad))
                 return s;
             dyt = dst;
+        }
+        if (p.tile) {
+            if (int s = launch_tile_sddmm(p, W, xt, dyt, dW, reinterpret_cast<int32_t *>(ws + p.off_tab), st))
+                return s;
+            return finish();
         }
         const int64_t blocks = round_up8(ceil_div(p.waves, kWavesPerBlock));
         const dim3 grid(static_cast<unsigned>(blocks));
@@ -2898,6 +3211,51 @@ int launch_colbwd(const BwdPlan &p, hipStream_t st, int64_t I, const snack_coo_d
 
 }  // namespace
 
+// Both gradients tiled (BwdPlan.split): db, one launch for the feature-major copies of X and dY,
+// the input gradient over the column view (values through col_perm), the weight gradient over
+// the row view.  The timing probe brackets both gradients' kernels.
+static int run_split_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *X, const void *dY, int64_t batch,
+                  int act_dtype, void *dX, float *db, float *dW, char *ws, hipStream_t st) {
+    const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+    if (db) {
+        const dim3 grid(static_cast<unsigned>(ceil_div(O, kBlock)));
+        if (act_dtype == SNACK_F32)
+            hipLaunchKernelGGL(bias_grad_kernel<float>, grid, dim3(kBlock), 0, st, O, batch,
+                               static_cast<const float *>(dY), db);
+        else
+            hipLaunchKernelGGL(bias_grad_kernel<bf16_t>, grid, dim3(kBlock), 0, st, O, batch,
+                               static_cast<const bf16_t *>(dY), db);
+        if (int s = check_hip("bias_grad_kernel")) return s;
+    }
+    float *xt = reinterpret_cast<float *>(ws + p.off_x);
+    float *dyt = reinterpret_cast<float *>(ws + p.off_dy);
+    if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st, dY, O, dyt, p.bpad)) return s;
+    probe(true, st);
+    ++g_probe_mute;
+    int s = act_dtype == SNACK_F32
+                ? run_spmm<float>(p.sp, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt,
+                                  O, batch, nullptr, static_cast<float *>(dX), ws + p.off_spmm, st, W->col_blocks)
+                : run_spmm<bf16_t>(p.sp, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm,
+                                   dyt, O, batch, nullptr, static_cast<bf16_t *>(dX), ws + p.off_spmm, st,
+                                   W->col_blocks);
+    if (!s) s = launch_tile_sddmm(p.sd, W, xt, dyt, dW, reinterpret_cast<int32_t *>(ws + p.off_sddmm), st);
+    --g_probe_mute;
+    if (s) return s;
+    probe(false, st);
+    return snack::ok();
+}
+
+extern "C" int snack_coo_bwd_is_fused(const snack_coo_desc *W, int64_t batch, int act_dtype) {
+    try {
+        if (int s = check_desc(W, true, "snack_coo_bwd_is_fused")) return -s;
+        const BwdPlan p = plan_bwd(W->nnz, W->out_features, W->in_features, batch, act_dtype, vec16(W),
+                                   W->row_to_col != nullptr);
+        return p.fused ? 1 : 0;
+    } catch (...) {
+        return -fail(SNACK_ERR_INTERNAL, "snack_coo_bwd_is_fused: unexpected exception");
+    }
+}
+
 extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch, int act_dtype,
                              void *dX, float *db, float *dW, void *workspace, size_t workspace_bytes,
                              void *hip_stream) {
@@ -2910,6 +3268,17 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
         const BwdPlan p = plan_bwd(nnz, O, I, batch, act_dtype, vec16(W), W->row_to_col != nullptr);
+        if (p.split) {
+            if (int s = check_act(X, act_dtype, "X", who)) return s;
+            if (int s = check_act(dY, act_dtype, "dY", who)) return s;
+            if (int s = check_act(dX, act_dtype, "dX", who)) return s;
+            if (!dW) return fail(SNACK_ERR_NULL, "%s: dW is NULL", who);
+            if (reinterpret_cast<uintptr_t>(dW) % 4) return fail(SNACK_ERR_ALIGN, "%s: dW misaligned", who);
+            if (db && reinterpret_cast<uintptr_t>(db) % 4) return fail(SNACK_ERR_ALIGN, "%s: db misaligned", who);
+            if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
+            return run_split_bwd(p, W, X, dY, batch, act_dtype, dX, db, dW, static_cast<char *>(workspace),
+                                 static_cast<hipStream_t>(hip_stream));
+        }
         if (!p.fused) {
             if (int s = snack_coo_bwd_input(W, dY, batch, act_dtype, dX, db, workspace, workspace_bytes, hip_stream))
                 return s;
@@ -2970,6 +3339,43 @@ __global__ __launch_bounds__(kBlock) void invert_perm_kernel(const int32_t *__re
     if (j < n) inv[perm[j]] = static_cast<int32_t>(j);
 }
 }  // namespace
+
+extern "C" int64_t snack_coo_block_offsets_count(const snack_coo_desc *W, int view) {
+    if (!W) {
+        fail(SNACK_ERR_NULL, "snack_coo_block_offsets_count: descriptor is NULL");
+        return -1;
+    }
+    if (view != SNACK_VIEW_ROWS && view != SNACK_VIEW_COLS) {
+        fail(SNACK_ERR_DTYPE, "snack_coo_block_offsets_count: unknown view %d", view);
+        return -1;
+    }
+    const int64_t keys = view == SNACK_VIEW_ROWS ? W->out_features : W->in_features;
+    int64_t ncb, cw;
+    tile_blocks(view == SNACK_VIEW_ROWS ? W->in_features : W->out_features, ncb, cw);
+    return keys * (ncb + 1);
+}
+
+extern "C" int snack_coo_block_offsets(const snack_coo_desc *W, int view, int32_t *out, void *hip_stream) {
+    try {
+        const char *who = "snack_coo_block_offsets";
+        if (view != SNACK_VIEW_ROWS && view != SNACK_VIEW_COLS)
+            return fail(SNACK_ERR_DTYPE, "%s: unknown view %d", who, view);
+        if (int s = check_desc(W, view == SNACK_VIEW_COLS, who)) return s;
+        const bool rows = view == SNACK_VIEW_ROWS;
+        const int64_t keys = rows ? W->out_features : W->in_features;
+        if (keys == 0) return snack::ok();
+        if (!out) return fail(SNACK_ERR_NULL, "%s: out is NULL", who);
+        int64_t ncb, cw;
+        tile_blocks(rows ? W->in_features : W->out_features, ncb, cw);
+        if (keys * (ncb + 1) >= (int64_t(1) << 31)) return fail(SNACK_ERR_SHAPE, "%s: table too large", who);
+        if (int s = launch_bounds(keys, static_cast<int>(ncb), static_cast<int>(cw), rows ? W->row_offsets : W->col_offsets,
+                                  rows ? W->cols : W->col_rows, out, static_cast<hipStream_t>(hip_stream)))
+            return s;
+        return snack::ok();
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "snack_coo_block_offsets: unexpected exception");
+    }
+}
 
 extern "C" int snack_coo_invert_perm(const int32_t *perm, int64_t n, int32_t *inv, void *hip_stream) {
     try {

@@ -140,6 +140,8 @@ class SnackLinear(nn.Module):
         self._set_vals(torch.from_numpy(np.ascontiguousarray(v)).to(device))
 
     def _set_buffer(self, name, t):
+        if name in _STRUCT:  # a new structure: the segment tables are rebuilt on next use
+            self._struct_version = getattr(self, "_struct_version", 0) + 1
         if name in self._buffers:
             self._buffers[name] = t
         else:
@@ -155,11 +157,25 @@ class SnackLinear(nn.Module):
     def nnz(self) -> int:
         return int(self.rows.numel())
 
+    def _blocks_key_now(self):
+        return (getattr(self, "_struct_version", 0), self.rows.data_ptr(), self.col_rows.data_ptr(), self.nnz,
+                str(self.rows.device))
+
     def weight_view(self) -> SnackCOO:
-        """The library descriptor over the current tensors (cheap; built per call)."""
+        """The library descriptor over the current tensors (cheap; built per call).  The segment
+        tables of the tiled kernels are built once per structure and device and kept."""
+        key = self._blocks_key_now()
+        if getattr(self, "_blocks_key", None) != key:
+            self._blocks = (None, None)
+            self._blocks_key = key
+            if self.rows.is_cuda:
+                W = SnackCOO(self.out_features, self.in_features, self.rows, self.cols, self.vals.detach(),
+                             self.row_offsets, self.col_perm, self.col_rows, self.col_cols, self.col_offsets)
+                self._blocks = (W.row_blocks, W.col_blocks)
         return SnackCOO(self.out_features, self.in_features, self.rows, self.cols, self.vals.detach(),
                         self.row_offsets, self.col_perm, self.col_rows, self.col_cols, self.col_offsets,
-                        self._buffers.get("row_to_col") if self.value_order == "col" else None)
+                        self._buffers.get("row_to_col") if self.value_order == "col" else None,
+                        self._blocks[0], self._blocks[1], blocks=None)
 
     def row_order_vals(self) -> torch.Tensor:
         """The values in row (triple) order, whatever the layer keeps."""
@@ -195,8 +211,10 @@ class SnackLinear(nn.Module):
                 W = W.to_column_order()
                 self._set_buffer("row_to_col", W.row_to_col)
             for name in _STRUCT:
-                self._buffers[name] = getattr(W, name)
+                self._set_buffer(name, getattr(W, name))
             self.vals.data = W.vals
+            self._blocks = (W.row_blocks, W.col_blocks)  # built for the new structure
+            self._blocks_key = self._blocks_key_now()
             return trials
         out = snack_coo_topology_update(self.out_features, self.in_features, self.rows.cpu().numpy(),
                                         self.cols.cpu().numpy(), self.row_order_vals().cpu().numpy(), n_prune,

@@ -89,6 +89,20 @@ enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2, SNACK
  *                             backward pass (a walk over the column view) read vals and
  *                             write dW contiguously, and moves one permuted read per entry
  *                             to the forward pass instead.  Requires the column view.
+ *   row_blocks  [O*(nb_r+1)] NULL, or the row order cut into column blocks: nb_r =
+ *                             ceil(I / 639) blocks of w_r = ceil(I / nb_r) columns, and
+ *                             row_blocks[r*(nb_r+1) + j] = the first triple position of row r
+ *                             whose column is >= j*w_r (j = nb_r: the row's end).  Each
+ *                             (row, block) segment is the run of the row's entries whose
+ *                             operand rows the tiled kernels stage together in LDS (Section
+ *                             3.1's row-sorted triple makes it contiguous).
+ *   col_blocks  [I*(nb_c+1)] NULL, or the same for the column view: nb_c = ceil(O / 639)
+ *                             blocks of w_c = ceil(O / nb_c) rows, positions in column-view
+ *                             order.  Requires the column view.
+ *                             Both tables depend on the structure only (not on the values or
+ *                             their order); fill them with snack_coo_block_offsets.  When NULL,
+ *                             a call that needs one builds it in its workspace (one extra
+ *                             kernel per call).
  * The column view is needed by snack_coo_bwd_input and snack_coo_bwd, and with
  * row_to_col (NULL elsewhere). */
 typedef struct snack_coo_desc {
@@ -104,6 +118,8 @@ typedef struct snack_coo_desc {
     const int32_t *col_cols;
     const int32_t *col_offsets;
     const int32_t *row_to_col;
+    const int32_t *row_blocks;
+    const int32_t *col_blocks;
 } snack_coo_desc;
 
 /* Host-side COO builder (Appendix B, Table 7: COO triple, CSR index pointer,
@@ -190,6 +206,12 @@ int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY
 int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch, int act_dtype,
                   void *dX, float *db, float *dW,
                   void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Whether snack_coo_bwd takes both gradients in its one pass over the column view (1), or in two
+ * tiled passes (0: the input gradient over the column view and the weight gradient over the row
+ * view, each operand row served from LDS) for this weight, batch and dtype -- the choice the call
+ * would make.  Negative: -(status) for an invalid descriptor.  For timing and diagnostics. */
+int snack_coo_bwd_is_fused(const snack_coo_desc *W, int64_t batch, int act_dtype);
 
 /* Device-side topology update (Appendix G prune-and-regrow, regrowth by
  * Algorithm 2): the same result as snack_coo_topology_update on the same
@@ -280,6 +302,23 @@ const char *snack_last_error(void);
 /* ABI version of this header: 5 (3 added snack_coo_init_uniform, 4 the device topology update,
  * 5 values in column order: snack_coo_desc.row_to_col, snack_coo_invert_perm, snack_coo_gather_f32). */
 int snack_coo_abi_version(void);
+
+/* Segment tables of snack_coo_desc.row_blocks (view = SNACK_VIEW_ROWS) and
+ * snack_coo_desc.col_blocks (view = SNACK_VIEW_COLS): the number of int32
+ * entries, keys * (nb + 1) with keys = O and nb = ceil(I / 639) for the rows
+ * (keys = I and nb = ceil(O / 639) for the column view; nb = 1 for an empty
+ * dimension), or -1 with snack_last_error() set for a NULL descriptor or an
+ * unknown view. */
+enum { SNACK_VIEW_ROWS = 0, SNACK_VIEW_COLS = 1 };
+int64_t snack_coo_block_offsets_count(const snack_coo_desc *W, int view);
+
+/* Fills `out` (DEVICE, snack_coo_block_offsets_count entries, caller-owned)
+ * with the segment table of one view, reading row_offsets and cols (rows) or
+ * col_offsets and col_rows (column view) of W; enqueued on hip_stream.  The
+ * table stays valid while the structure does: rebuild it after a topology
+ * update.  Errors: SNACK_ERR_NULL (W, out or a needed array NULL),
+ * SNACK_ERR_DTYPE (unknown view), SNACK_ERR_HIP. */
+int snack_coo_block_offsets(const snack_coo_desc *W, int view, int32_t *out, void *hip_stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     lib = ctypes.CDLL(snk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert snk.abi_version() == 5
+    assert snk.abi_version() == 6
 
 
 def test_binding_loads_only_the_in_tree_library():
@@ -124,3 +124,26 @@ def test_column_order_values_host_checks_and_workspace():
     assert lib.snack_coo_invert_perm(0x1000, -1, 0x1000, None) == 2
     assert lib.snack_coo_gather_f32(0x1001, 0x1000, 4, 0x1000, None) == 5
     assert lib.snack_coo_gather_f32(None, None, 0, None, None) == 0
+
+
+def test_block_offsets_count_and_errors():
+    """Segment-table sizes: keys * (ceil(n / 639) + 1); argument errors come back before any launch."""
+    lib = snk._lib
+    d = snk._Desc()
+    d.out_features, d.in_features, d.nnz = 10000, 10000, 0
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 10000 * 17
+    d.out_features, d.in_features = 700, 639
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 2
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_COLS) == 639 * 3
+    d.in_features = 640
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 3
+    d.in_features = 0
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 2
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), 5) == -1
+    assert lib.snack_coo_block_offsets_count(None, 0) == -1
+    d.in_features = 640
+    d.row_offsets = 0x1000
+    assert lib.snack_coo_block_offsets(ctypes.byref(d), 5, 0x1000, None) == 6      # unknown view
+    assert lib.snack_coo_block_offsets(ctypes.byref(d), 0, None, None) == 1        # out NULL
+    assert lib.snack_coo_block_offsets(ctypes.byref(d), 1, 0x1000, None) == 1      # no column view
+    assert lib.snack_coo_block_offsets(None, 0, 0x1000, None) == 1

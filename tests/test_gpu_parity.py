@@ -254,7 +254,10 @@ def test_invariants_bias_determinism_scaling_permutation():
         assert torch.equal(snk.snack_coo_fwd(W2, X, b), Y1)
     # true sparsity: device bytes of the weight are 12 nnz + 4 (O+1) plus the column view
     nnz, O, I = L["nnz"], 700, 900
-    assert W.device_bytes() == 12 * nnz + 4 * (O + 1) + 12 * nnz + 4 * (I + 1)
+    assert W.device_bytes(blocks=False) == 12 * nnz + 4 * (O + 1) + 12 * nnz + 4 * (I + 1)
+    # plus the segment tables of the tiled kernels: (nb + 1) offsets per row and per column
+    nb_r, nb_c = -(-I // 639), -(-O // 639)
+    assert W.device_bytes() == W.device_bytes(blocks=False) + 4 * (O * (nb_r + 1) + I * (nb_c + 1))
 
 
 def test_linearity_in_x():

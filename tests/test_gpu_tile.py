@@ -156,3 +156,114 @@ def test_tiled_in_graph(layers):
         torch.cuda.synchronize()
         assert torch.equal(Y, ref)
         _ = X.sum()
+
+
+def _ref_blocks(offs, gidx, n):
+    """table[key][j] = first position of the key's run at or past gather index j*w (numpy)."""
+    nb = max(1, -(-n // 639))
+    w = max(1, -(-n // nb))
+    keys = offs.size - 1
+    t = np.empty((keys, nb + 1), np.int64)
+    for key in range(keys):
+        a, e = int(offs[key]), int(offs[key + 1])
+        t[key] = a + np.searchsorted(gidx[a:e], np.arange(nb + 1) * w, side="left")
+        t[key, nb] = e
+    return t.ravel()
+
+
+@pytest.mark.parametrize("name", ["e1100x7777", "d2000x4000", "u4000x600"])
+def test_block_tables_exact(layers, name):
+    """snack_coo_block_offsets (both views) equals a per-key search, bit for bit."""
+    L = layers[name]
+    say(f"segment tables {name}")
+    built, W = device_layer(L, DEV)
+    O, I = L["out_features"], L["in_features"]
+    rb = W.row_blocks.cpu().numpy().astype(np.int64)
+    cb = W.col_blocks.cpu().numpy().astype(np.int64)
+    assert np.array_equal(rb, _ref_blocks(built["row_offsets"], built["cols"], I))
+    assert np.array_equal(cb, _ref_blocks(built["col_offsets"], built["col_rows"], O))
+
+
+def test_without_tables_same_bits(layers):
+    """A weight without segment tables (built per call in the workspace) gives the same bits."""
+    L = layers["u3000x5000"]
+    say("tiled with and without stored tables")
+    built, W = device_layer(L, DEV)
+    W0 = snk.SnackCOO(W.out_features, W.in_features, W.rows, W.cols, W.vals, W.row_offsets, W.col_perm,
+                      W.col_rows, W.col_cols, W.col_offsets, blocks=None)
+    assert W0.row_blocks is None and W.row_blocks is not None
+    x_in, _ = acts(7700, 64, L["in_features"])
+    X = to_device(x_in, DEV)
+    b = torch.from_numpy(L["bias"]).to(DEV)
+    assert torch.equal(snk.snack_coo_fwd(W, X, b), snk.snack_coo_fwd(W0, X, b))
+    dy_in, _ = acts(7701, 64, L["out_features"])
+    dY = to_device(dy_in, DEV)
+    Wc, W0c = W.to_column_order(), W0.to_column_order()
+    assert torch.equal(snk.snack_coo_bwd_input(Wc, dY), snk.snack_coo_bwd_input(W0c, dY))
+
+
+def _dw(L, B, seed, bf16, mode, colorder=False):
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    built, W = device_layer(L, DEV)
+    if colorder:
+        W = W.to_column_order()
+    x_in, x64 = acts(seed, B, I, bf16)
+    dy_in, dy64 = acts(seed + 1, B, O, bf16)
+    X, dY = to_device(x_in, DEV, bf16), to_device(dy_in, DEV, bf16)
+    with tile_mode(mode):
+        dW = snk.snack_coo_grad_weight(W, X, dY)
+    torch.cuda.synchronize()
+    ref = oracle.grad_weight(O, I, built["rows"], built["cols"], x64, dy64, nthreads=NTHREADS)
+    if colorder:
+        ref = ref[built["col_perm"].astype(np.int64)]
+    check_close(dW.cpu().numpy(), ref, B, f"dW mode={mode} col={colorder}")
+    return dW
+
+
+@pytest.mark.parametrize("name", ["u3000x5000", "e1100x7777", "d2000x4000", "u4000x600"])
+def test_tiled_dw_b64(layers, name):
+    say(f"tiled dW {name} B=64")
+    _dw(layers[name], 64, 7800, False, None)
+
+
+@pytest.mark.parametrize("B", [50, 128, 192])
+def test_tiled_dw_batches(layers, B):
+    say(f"tiled dW u3000x5000 B={B}")
+    _dw(layers["u3000x5000"], B, 7900 + B, False, None)
+
+
+def test_tiled_dw_bf16_and_column_order(layers):
+    say("tiled dW bf16 / column-order values")
+    _dw(layers["e1100x7777"], 64, 8000, True, None)
+    _dw(layers["d2000x4000"], 64, 8010, False, None, colorder=True)
+
+
+def test_tiled_dw_matches_untiled(layers):
+    L = layers["d2000x4000"]
+    say("tiled dW vs rowsddmm")
+    a = _dw(L, 64, 8100, False, None)
+    b = _dw(L, 64, 8100, False, "0")
+    check_close(a.cpu().numpy(), b.cpu().numpy(), 64, "tiled vs rowsddmm dW")
+
+
+@pytest.mark.parametrize("name,B,fused", [("u3000x5000", 64, False), ("e1100x7777", 50, False),
+                                          ("u3000x5000", 128, True)])
+def test_backward_forms(layers, name, B, fused):
+    """snack_coo_bwd: two tiled passes (values in row order, one 64-column batch tile) or the
+    one-pass kernel; dX, dW and db against the oracle either way."""
+    L = layers[name]
+    say(f"snack_coo_bwd {name} B={B} fused={fused}")
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    built, W = device_layer(L, DEV)
+    assert snk.snack_coo_bwd_is_fused(W, B) == fused
+    assert snk.snack_coo_bwd_is_fused(W.to_column_order(), B) is True
+    x_in, x64 = acts(8200 + B, B, I)
+    dy_in, dy64 = acts(8300 + B, B, O)
+    X, dY = to_device(x_in, DEV), to_device(dy_in, DEV)
+    db = torch.empty(O, dtype=torch.float32, device=DEV)
+    dX, dW = snk.snack_coo_bwd(W, X, dY, db=db)
+    torch.cuda.synchronize()
+    r, c, v = built["rows"], built["cols"], built["vals"]
+    check_close(dX.cpu().numpy(), oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS), nnz / I, "bwd dX")
+    check_close(dW.cpu().numpy(), oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS), B, "bwd dW")
+    check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, "bwd db")
