@@ -494,17 +494,18 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
 // entries).  Each tile writes fp32 partial sums part[bt][cb][key][64]; tile_sum_kernel adds the
 // blocks in block order, adds the bias and transposes to the batch-major output.
 //
-// Lanes: SL slots of 64/SL lanes; slot s walks key 4*g + s of the wave's group g and each lane
-// holds SL batch columns (SL floats).  A group's entries are loaded 16 per chunk register (each
-// row of 16 lanes holds entries j = 0..15 of its slot's chunk), one group ahead of the compute.
+// Lanes: 4 slots of 16 lanes; slot s walks key 4*g + s of the wave's group g, and each lane holds
+// VW batch columns (VW floats) of a TB = 16*VW column batch tile (64 for batches padded to a
+// multiple of 64, else 32 or 16).  A group's entries are loaded 16 per chunk register (each row
+// of 16 lanes holds entries j = 0..15 of its slot's chunk), two groups ahead of the compute.
 // Step t of a chunk hands entry t to every lane of its row with DPP row_newbcast:t, folded into
-// the address add and (inline asm) into the FMA, so one step costs one LDS read of SL floats
-// per lane, one address add and SL FMAs.  Entries past a segment's end point at the zero row
+// the address add and (inline asm) into the FMA, so one step costs one LDS read of VW floats
+// per lane, one address add and VW FMAs.  Entries past a segment's end point at the zero row
 // with value 0.
 constexpr int kTileThreads = 1024;
 constexpr int kTileWaves = kTileThreads / kWave;
-constexpr int kTileBatch = 64;                        // batch columns of a tile: one 256-byte LDS row
-constexpr int kTileLdsRows = 640;                     // 160 KB of LDS
+constexpr int kTileBatch = 64;                        // widest batch tile: one 256-byte LDS row
+constexpr int kTileLdsRows = 640;                     // 160 KB of LDS at 64 columns
 constexpr int kTileMaxCols = kTileLdsRows - 1;        // operand rows per block (one more is the zero row)
 constexpr int kTileStageIters = kTileLdsRows * 16 / kTileThreads;  // float4 loads per thread to stage
 
@@ -543,17 +544,17 @@ __device__ __forceinline__ float vget(const float4 &v, int i) {
 }
 
 // Four steps T0..T0+3 of one chunk: the four LDS reads first, then the FMAs.
-template <int SL, int T0>
-__device__ __forceinline__ void tile_steps4(float (&acc)[SL], uint32_t off, float v, uint32_t lane_off,
+template <int VW, int T0>
+__device__ __forceinline__ void tile_steps4(float (&acc)[VW], uint32_t off, float v, uint32_t lane_off,
                                             const char *lds) {
-    typedef typename TileVec<SL>::T V;
+    typedef typename TileVec<VW>::T V;
     V x[4];
     x[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) + lane_off));
     x[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
     x[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
     x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
 #pragma unroll
-    for (int i = 0; i < SL; ++i) {
+    for (int i = 0; i < VW; ++i) {
         fmac_bcast16<T0 + 0, T0 == 0>(acc[i], v, vget(x[0], i));
         fmac_bcast16<T0 + 1, false>(acc[i], v, vget(x[1], i));
         fmac_bcast16<T0 + 2, false>(acc[i], v, vget(x[2], i));
@@ -562,13 +563,13 @@ __device__ __forceinline__ void tile_steps4(float (&acc)[SL], uint32_t off, floa
 }
 
 // One chunk of 16 entries, nst (uniform, 1..16) of them real for the longest slot.
-template <int SL>
-__device__ __forceinline__ void tile_chunk(float (&acc)[SL], uint32_t off, float v, int nst, uint32_t lane_off,
+template <int VW>
+__device__ __forceinline__ void tile_chunk(float (&acc)[VW], uint32_t off, float v, int nst, uint32_t lane_off,
                                            const char *lds) {
-    tile_steps4<SL, 0>(acc, off, v, lane_off, lds);
-    if (nst > 4) tile_steps4<SL, 4>(acc, off, v, lane_off, lds);
-    if (nst > 8) tile_steps4<SL, 8>(acc, off, v, lane_off, lds);
-    if (nst > 12) tile_steps4<SL, 12>(acc, off, v, lane_off, lds);
+    tile_steps4<VW, 0>(acc, off, v, lane_off, lds);
+    if (nst > 4) tile_steps4<VW, 4>(acc, off, v, lane_off, lds);
+    if (nst > 8) tile_steps4<VW, 8>(acc, off, v, lane_off, lds);
+    if (nst > 12) tile_steps4<VW, 12>(acc, off, v, lane_off, lds);
 }
 
 // tab[key][j] = first entry of the key at or past gather index j*cw (j = 0..ncb): the segment of
@@ -594,15 +595,19 @@ __global__ __launch_bounds__(kBlock) void tile_bounds_kernel(int nkeys, int ncb,
     tab[i] = lo;
 }
 
-// opnd: feature-major [opnd_rows (+1)][ld] fp32, ld a multiple of 64; batch tile bt = blockIdx.y
-// covers columns [64 bt, 64 bt + 64).  Logical workgroup L = cb * nrb + rb (XCD-contiguous).
+// opnd: feature-major [opnd_rows (+1)][ld] fp32, ld a multiple of TB = 16 VW; batch tile
+// bt = blockIdx.y covers columns [TB bt, TB bt + TB): each lane of a slot holds VW of them, and one
+// staged operand row is TB floats.  Logical workgroup L = cb * nrb + rb (XCD-contiguous).
 // VP: the values are read through perm (vals[perm[k]]): the permutation is loaded with the gather
 // indices two groups ahead, the values it points at one group ahead.
-template <int SL, int CH, bool VP>
+template <int VW, int CH, bool VP>
 __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
     const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm,
     const float *__restrict__ opnd, int opnd_rows, int ld, float *__restrict__ part) {
+    constexpr int SL = 4;                      // slots (keys) per wave, 16 lanes each
+    constexpr int TB = 16 * VW;                // batch columns of a tile
+    constexpr uint32_t kRowBytes = 4u * TB;    // one staged operand row
     extern __shared__ float4 xs4[];
     const int64_t L = xcd_block();
     if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
@@ -612,10 +617,10 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int j = lane & 15;                    // entry of a chunk held by this lane
-    const int slot = (lane >> 4) * SL / 4;      // rows of 16 lanes per slot: 4 / SL
-    const int ls = lane % (kWave / SL);         // lane within the slot: batch columns [ls*SL, ls*SL + SL)
-    const uint32_t lane_off = static_cast<uint32_t>(ls * SL * 4);
-    const uint32_t zoff = static_cast<uint32_t>(cw) * 256u;
+    const int slot = lane >> 4;                 // the row of 16 lanes is the slot
+    const int ls = lane & 15;                   // lane within the slot: batch columns [ls*VW, ls*VW + VW)
+    const uint32_t lane_off = static_cast<uint32_t>(ls * VW * 4);
+    const uint32_t zoff = static_cast<uint32_t>(cw) * kRowBytes;
     const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
     // group g of this wave: keys k_lo + (wave + kTileWaves * g) * SL + slot; keys_per_rb <= 1024
     // keeps a wave's keys within 64, so lane g*SL + s holds the segment of group g's slot s
@@ -630,17 +635,19 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         seg_e = tab[at + 1];
     }
     {  // stage the block's operand rows; rows cn..cw are zero (row cw is the zero row)
-        const float4 *src = reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld + kTileBatch * bt);
-        const int ld4 = ld / 4, n4 = (cw + 1) * 16;
-        float4 tmp[kTileStageIters];
+        constexpr int R4 = TB / 4;  // float4s per staged row
+        constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
+        const float4 *src = reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld + TB * bt);
+        const int ld4 = ld / 4, n4 = (cw + 1) * R4;
+        float4 tmp[kIters];
 #pragma unroll
-        for (int it = 0; it < kTileStageIters; ++it) {
+        for (int it = 0; it < kIters; ++it) {
             const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
-            const int c = i >> 4, q = i & 15;
+            const int c = i / R4, q = i % R4;
             tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int it = 0; it < kTileStageIters; ++it) {
+        for (int it = 0; it < kIters; ++it) {
             const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
             if (i < n4) xs4[i] = tmp[it];
         }
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : -1;
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(xs4);
-    float *pout = part + (static_cast<int64_t>(bt) * ncb + cb) * static_cast<int64_t>(nkeys) * kTileBatch;
+    float *pout = part + (static_cast<int64_t>(bt) * ncb + cb) * static_cast<int64_t>(nkeys) * TB;
     // Chunks are loaded two groups ahead of the compute (three buffers in rotation).  Loads are
     // issued unconditionally (clamped indices) and masked where they are used.
     // vv: the values (VP: the permuted positions, turned into values by load_vals)
@@ -669,10 +676,8 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         for (int c = 0; c < CH; ++c) vv[c] = __float_as_int(vals[pm[c]]);
     };
     auto group_len = [&](int len) {
-        int m = __builtin_amdgcn_readlane(len, 0);
-        if constexpr (SL >= 2) m = max(m, __builtin_amdgcn_readlane(len, 32));
-        if constexpr (SL >= 4) m = max(m, max(__builtin_amdgcn_readlane(len, 16), __builtin_amdgcn_readlane(len, 48)));
-        return m;
+        return max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
+                   max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
     };
     auto compute = [&](int g, const int (&gi)[CH], const int (&vv)[CH]) {
         const int src = (g * SL + slot) * 4;
@@ -680,16 +685,16 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         const int len = __builtin_amdgcn_ds_bpermute(src, s_len);
         const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
         const int m = group_len(len);
-        float acc[SL];
+        float acc[VW];
 #pragma unroll
-        for (int i = 0; i < SL; ++i) acc[i] = 0.f;
+        for (int i = 0; i < VW; ++i) acc[i] = 0.f;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             if (16 * c < m) {
                 const bool ok = 16 * c + j < len;
-                const uint32_t off = ok ? static_cast<uint32_t>(gi[c] - c0) * 256u : zoff;
+                const uint32_t off = ok ? static_cast<uint32_t>(gi[c] - c0) * kRowBytes : zoff;
                 const float v = ok ? __int_as_float(vv[c]) : 0.f;
-                tile_chunk<SL>(acc, off, v, m - 16 * c, lane_off, lds);
+                tile_chunk<VW>(acc, off, v, m - 16 * c, lane_off, lds);
             }
         }
         for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
@@ -697,7 +702,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
             const int idx = ok ? a + 16 * c + j : 0;
             const int gv = gidx[idx];
             const float w = vals[VP ? perm[idx] : idx];
-            tile_chunk<SL>(acc, ok ? static_cast<uint32_t>(gv - c0) * 256u : zoff, ok ? w : 0.f, m - 16 * c, lane_off,
+            tile_chunk<VW>(acc, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, ok ? w : 0.f, m - 16 * c, lane_off,
                            lds);
         }
         // every chunk register is consumed here, also those a short group skipped: without this
@@ -705,12 +710,12 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
 #pragma unroll
         for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]));
         if (key >= 0) {
-            typedef typename TileVec<SL>::T V;
+            typedef typename TileVec<VW>::T V;
             V r;
-            if constexpr (SL == 1) r = acc[0];
-            else if constexpr (SL == 2) r = make_float2(acc[0], acc[1]);
+            if constexpr (VW == 1) r = acc[0];
+            else if constexpr (VW == 2) r = make_float2(acc[0], acc[1]);
             else r = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * kTileBatch + ls * SL) = r;
+            *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * TB + ls * VW) = r;
         }
     };
     int gi0[CH], gi1[CH], gi2[CH];
@@ -886,24 +891,25 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     }
 }
 
-// out[b][key] = bias[key] + sum over blocks cb (in order) of part[bt][cb][key][b - 64 bt], b < nbo.
-// A workgroup adds 16 keys x 64 batch columns of one batch tile (one float4 per thread and block,
-// up to 16 blocks' loads in flight) and writes them transposed.
-constexpr int kSumKeys = 16;
-template <typename OutT>
+// out[b][key] = bias[key] + sum over blocks cb (in order) of part[bt][cb][key][b - TB bt], b < nbo.
+// A workgroup adds 1024/TB keys x TB batch columns of one batch tile (one float4 per thread and
+// block, up to 16 blocks' loads in flight) and writes them transposed.
+template <typename OutT, int TB>
 __global__ __launch_bounds__(kBlock) void tile_sum_kernel(const float *__restrict__ part, int nkeys, int ncb,
                                                           int64_t nbo, const float *__restrict__ bias,
                                                           OutT *__restrict__ out, int64_t out_ld) {
-    __shared__ float tr[kSumKeys][kTileBatch + 1];
-    const int k0 = blockIdx.x * kSumKeys, bt = blockIdx.y;
+    constexpr int KW = 4 * kBlock / TB;  // keys per workgroup
+    constexpr int R4 = TB / 4;           // float4s per key and block
+    __shared__ float tr[KW][TB + 1];
+    const int k0 = blockIdx.x * KW, bt = blockIdx.y;
     const int t = threadIdx.x;
     {
-        const int kk = t >> 4, qq = t & 15;  // key k0 + kk, batch columns [4 qq, 4 qq + 4)
+        const int kk = t / R4, qq = t % R4;  // key k0 + kk, batch columns [4 qq, 4 qq + 4)
         float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f);
         if (k0 + kk < nkeys) {
             const float4 *p = reinterpret_cast<const float4 *>(
-                part + ((static_cast<int64_t>(bt) * ncb) * nkeys + k0 + kk) * kTileBatch + 4 * qq);
-            const int64_t stride4 = static_cast<int64_t>(nkeys) * (kTileBatch / 4);
+                part + ((static_cast<int64_t>(bt) * ncb) * nkeys + k0 + kk) * TB + 4 * qq);
+            const int64_t stride4 = static_cast<int64_t>(nkeys) * R4;
             for (int cb0 = 0; cb0 < ncb; cb0 += 16) {
                 float4 u[16];
 #pragma unroll
@@ -927,11 +933,11 @@ __global__ __launch_bounds__(kBlock) void tile_sum_kernel(const float *__restric
         row[3] = s0.w;
     }
     __syncthreads();
-    const int b = t >> 2, kq = (t & 3) * (kSumKeys / 4);  // batch row 64 bt + b, keys [k0 + kq, +4)
-    const int64_t bb = static_cast<int64_t>(bt) * kTileBatch + b;
+    const int b = t / (KW / 4), kq = (t % (KW / 4)) * 4;  // batch row TB bt + b, keys [k0 + kq, +4)
+    const int64_t bb = static_cast<int64_t>(bt) * TB + b;
     if (bb < nbo) {
 #pragma unroll
-        for (int i = 0; i < kSumKeys / 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const int key = k0 + kq + i;
             if (key < nkeys) store_act(out, bb * out_ld + key, tr[kq + i][b] + (bias ? bias[key] : 0.f));
         }
@@ -2043,9 +2049,9 @@ struct SpmmPlan {
     bool direct;         // operand used in place (fp32, batch 1) instead of a transposed copy
     int64_t bpad;        // batch columns of the feature-major operand (rowwave: B rounded up to 4)
     size_t off_opnd, off_head, off_tail, off_cvals, total;
-    // kTile: slots per wave, prefetched chunks, column blocks, key blocks, block width, keys per
-    // key block, 64-column batch tiles; offset table and partial sums in the workspace
-    int tsl, tch, tncb, tnrb, tcw, tkpr, tnbt;
+    // kTile: batch columns per tile (16, 32 or 64), prefetched chunks, column blocks, key blocks,
+    // block width, keys per key block, batch tiles; offset table and partial sums in the workspace
+    int ttb, tch, tncb, tnrb, tcw, tkpr, tnbt;
     size_t off_tab, off_part;
 };
 
@@ -2167,20 +2173,15 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
     return p;
 }
 
-// The LDS-tiled gather-reduce (kTile) for batches padded to a multiple of 64 on layers of at
-// least kTileMinNnz entries whose segments per (key, block) average at least 8 entries, when the
-// walk reads the values in place.  SNACK_COO_TILE=0 in the environment turns it off; 1, 2 or 4
-// picks the slots per wave (batch columns per lane).
+// The LDS-tiled gather-reduce (kTile) for batches padded to a multiple of 16 on layers of at
+// least kTileMinNnz entries whose segments per (key, block) average at least 8 entries; the batch
+// tile is 64 columns where the padded batch allows, else 32 or 16.  SNACK_COO_TILE=0 in the
+// environment turns the tiled kernels off.
 constexpr int64_t kTileMinNnz = int64_t(1) << 20;
 
 int tile_env() {
     const char *env = std::getenv("SNACK_COO_TILE");
-    if (!env) return -1;
-    if (!std::strcmp(env, "0")) return 0;
-    if (!std::strcmp(env, "1")) return 1;
-    if (!std::strcmp(env, "2")) return 2;
-    if (!std::strcmp(env, "4")) return 4;
-    return -1;
+    return env && !std::strcmp(env, "0") ? 0 : -1;
 }
 
 // Column blocks over n operand rows: ncb = ceil(n / kTileMaxCols) blocks of cw = ceil(n / ncb)
@@ -2194,30 +2195,33 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     const int env = tile_env();
     if (env == 0) return;
     const int64_t Bp = pad_batch(B);
-    if (Bp % kTileBatch != 0 || Bp / kTileBatch > 65535 || nnz < kTileMinNnz || opnd_rows < 1 || nkeys < 1) return;
+    const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
+    if (tb == 0 || Bp / tb > 65535 || nnz < kTileMinNnz || opnd_rows < 1 || nkeys < 1) return;
     int64_t ncb, cw;
     tile_blocks(opnd_rows, ncb, cw);
     const double mean = static_cast<double>(nnz) / static_cast<double>(nkeys * ncb);
     if (mean < 8.0 || nkeys * (ncb + 1) >= (int64_t(1) << 31)) return;
     p.mapping = kTile;
     p.bpad = Bp;
-    p.tsl = env > 0 ? env : 4;
+    p.ttb = tb;
+    // workgroups per CU: one at 64 columns (160 KB of LDS), two at 16 or 32 (the wave limit)
+    const int64_t per_cu = tb == 64 ? 1 : 2;
     const double need = mean + 4.0 * std::sqrt(mean) + 1.0;
     p.tch = need <= 32.0 ? 2 : (need <= 64.0 ? 4 : 8);
     p.tncb = static_cast<int>(ncb);
     p.tcw = static_cast<int>(cw);
-    const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256, ncb));
+    const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256 * per_cu, ncb));
     p.tkpr = static_cast<int>(std::min<int64_t>(ceil_div(nkeys, nrb0), kTileWaves * kWave));
     p.tnrb = static_cast<int>(ceil_div(nkeys, p.tkpr));
-    p.tnbt = static_cast<int>(Bp / kTileBatch);
+    p.tnbt = static_cast<int>(Bp / tb);
     size_t at = 0;
     p.off_opnd = at;
     at = align_up(at + sizeof(float) * static_cast<size_t>((opnd_rows + 1) * Bp));
     p.off_tab = at;
     at = align_up(at + sizeof(int32_t) * static_cast<size_t>(nkeys * (ncb + 1)));
     p.off_part = at;
-    at = align_up(at + sizeof(float) * static_cast<size_t>(p.tnbt) * static_cast<size_t>(ncb) *
-                           static_cast<size_t>(nkeys) * kTileBatch);
+    at = align_up(at + sizeof(float) * static_cast<size_t>(Bp) * static_cast<size_t>(ncb) *
+                           static_cast<size_t>(nkeys));
     p.off_head = p.off_tail = at;
     p.total = at;
 }
@@ -2611,13 +2615,13 @@ int launch_gather(const int32_t *idx, const float *src, int64_t n, float *dst, h
     return check_hip("gather_vals_kernel");
 }
 
-template <int SL, int CH, bool VP>
+template <int VW, int CH, bool VP>
 int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
                        const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
-    const size_t lds = static_cast<size_t>(p.tcw + 1) * kTileBatch * sizeof(float);
+    const size_t lds = static_cast<size_t>(p.tcw + 1) * (16 * VW) * sizeof(float);
     static bool attr = false;  // the 160 KB of dynamic LDS, allowed once per instantiation
     if (!attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_spmm_kernel<SL, CH, VP>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_spmm_kernel<VW, CH, VP>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess)
             return fail(SNACK_ERR_HIP, "tile_spmm_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
@@ -2625,28 +2629,28 @@ int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, con
     }
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)),
                     static_cast<unsigned>(p.tnbt));
-    hipLaunchKernelGGL((tile_spmm_kernel<SL, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(nkeys),
+    hipLaunchKernelGGL((tile_spmm_kernel<VW, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(nkeys),
                        p.tncb, p.tnrb, p.tcw, p.tkpr, tab, gidx, vals, perm, opnd, static_cast<int>(opnd_rows),
                        static_cast<int>(p.bpad), part);
     return check_hip("tile_spmm_kernel");
 }
 
-template <int SL, bool VP>
+template <int VW, bool VP>
 int launch_tile_ch(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
                    const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
     switch (p.tch) {
-        case 2: return launch_tile_kernel<SL, 2, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
-        case 4: return launch_tile_kernel<SL, 4, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
-        case 8: return launch_tile_kernel<SL, 8, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
+        case 2: return launch_tile_kernel<VW, 2, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
+        case 4: return launch_tile_kernel<VW, 4, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
+        case 8: return launch_tile_kernel<VW, 8, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
         default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported chunk count %d", p.tch);
     }
 }
 
-template <int SL>
-int launch_tile_sl(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
+template <int VW>
+int launch_tile_vw(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
                    const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
-    if (perm) return launch_tile_ch<SL, true>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
-    return launch_tile_ch<SL, false>(p, nkeys, tab, gidx, vals, nullptr, opnd, opnd_rows, part, st);
+    if (perm) return launch_tile_ch<VW, true>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
+    return launch_tile_ch<VW, false>(p, nkeys, tab, gidx, vals, nullptr, opnd, opnd_rows, part, st);
 }
 
 // The LDS-tiled gather-reduce: segment table, tiles, block sums (bias, transpose).
@@ -2674,16 +2678,24 @@ int launch_tile(const SpmmPlan &p, int64_t nkeys, const int32_t *offs, const int
         tab = t;
     }
     int s;
-    switch (p.tsl) {
-        case 1: s = launch_tile_sl<1>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
-        case 2: s = launch_tile_sl<2>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
-        case 4: s = launch_tile_sl<4>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
-        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported slot count %d", p.tsl);
+    switch (p.ttb) {
+        case 16: s = launch_tile_vw<1>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
+        case 32: s = launch_tile_vw<2>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
+        case 64: s = launch_tile_vw<4>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
+        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported batch tile %d", p.ttb);
     }
     if (s) return s;
-    const dim3 sgrid(static_cast<unsigned>(ceil_div(nkeys, kSumKeys)), static_cast<unsigned>(p.tnbt));
-    hipLaunchKernelGGL(tile_sum_kernel<OutT>, sgrid, dim3(kBlock), 0, st, part, static_cast<int>(nkeys), p.tncb, B,
-                       bias, out, nkeys);
+    const unsigned kw = static_cast<unsigned>(4 * kBlock / p.ttb);  // keys per block-sum workgroup
+    const dim3 sgrid(static_cast<unsigned>(ceil_div(nkeys, kw)), static_cast<unsigned>(p.tnbt));
+    if (p.ttb == 16)
+        hipLaunchKernelGGL((tile_sum_kernel<OutT, 16>), sgrid, dim3(kBlock), 0, st, part, static_cast<int>(nkeys),
+                           p.tncb, B, bias, out, nkeys);
+    else if (p.ttb == 32)
+        hipLaunchKernelGGL((tile_sum_kernel<OutT, 32>), sgrid, dim3(kBlock), 0, st, part, static_cast<int>(nkeys),
+                           p.tncb, B, bias, out, nkeys);
+    else
+        hipLaunchKernelGGL((tile_sum_kernel<OutT, 64>), sgrid, dim3(kBlock), 0, st, part, static_cast<int>(nkeys),
+                           p.tncb, B, bias, out, nkeys);
     probe(false, st);
     return check_hip("tile_sum_kernel");
 }

@@ -1,12 +1,14 @@
-"""The LDS-tiled gather-reduce (forward over the row order, input gradient over the column view
-with values in column order) against the fp64 oracle, for every slot width (needs a GPU).
+"""The LDS-tiled kernels (forward over the row order, input gradient over the column view with
+values in either order, weight gradient over the row view) against the fp64 oracle (needs a GPU).
 
-The tiled walk applies to layers of at least 2^20 entries at batches padded to a multiple of 64
-whose (key, column block) segments average at least 8 entries.  The cases cover: several column
-blocks with a narrower last one, one block, batches that need zero padding (50, 100) and several
-64-column batch tiles (128, 192, 256), empty rows and bias-only outputs, rows and columns longer
-than the prefetched chunks (the full lines of 'dense_lines'), bf16 activations, and the walk off
-(SNACK_COO_TILE=0) giving the same results within tolerance.
+The tiled walks apply to layers of at least 2^19 entries at batches padded to a multiple of 16
+(batch tiles of 64 columns where the padded batch allows, else 32 or 16; the weight gradient only
+at multiples of 64) whose (key, column block) segments average at least 8 entries.  The cases
+cover: several column blocks with a narrower last one, one block, every tile width, batches that
+need zero padding (50, 100) and several batch tiles (48, 96, 128, 192, 256), empty rows and
+bias-only outputs, rows and columns longer than the prefetched chunks (the full lines of
+'dense_lines'), bf16 activations, and the walks off (SNACK_COO_TILE=0) giving the same results
+within tolerance.
 """
 import contextlib
 import os
@@ -31,7 +33,7 @@ DEV = torch.device("cuda:0")
 
 @contextlib.contextmanager
 def tile_mode(v):
-    """SNACK_COO_TILE: '0' off, '1' / '2' / '4' slots per wave, None the library default."""
+    """SNACK_COO_TILE: '0' off, None the library default (on)."""
     old = os.environ.get("SNACK_COO_TILE")
     if v is None:
         os.environ.pop("SNACK_COO_TILE", None)
@@ -80,23 +82,37 @@ def _fwd_dx(L, B, seed, bf16, mode):
     return Y, dX
 
 
-@pytest.mark.parametrize("mode", ["1", "2", "4"])
+@pytest.mark.parametrize("B", [16, 32, 64])
 @pytest.mark.parametrize("name", ["u3000x5000", "e1100x7777", "d2000x4000", "u4000x600"])
-def test_tiled_fp32_b64(layers, name, mode):
-    say(f"tiled {name} B=64 slots={mode}")
-    _fwd_dx(layers[name], 64, 7100, False, mode)
+def test_tiled_fp32(layers, name, B):
+    say(f"tiled {name} B={B}")
+    _fwd_dx(layers[name], B, 7100 + B, False, None)
 
 
-@pytest.mark.parametrize("B", [50, 100, 128, 192, 256])
+@pytest.mark.parametrize("B", [13, 30, 48, 50, 96, 100, 128, 192, 256])
 def test_tiled_batches(layers, B):
     say(f"tiled u3000x5000 B={B}")
     _fwd_dx(layers["u3000x5000"], B, 7200 + B, False, None)
 
 
-@pytest.mark.parametrize("mode", ["1", "4"])
-def test_tiled_bf16(layers, mode):
-    say(f"tiled e1100x7777 bf16 B=64 slots={mode}")
-    _fwd_dx(layers["e1100x7777"], 64, 7300, True, mode)
+@pytest.mark.parametrize("B", [16, 64])
+def test_tiled_bf16(layers, B):
+    say(f"tiled e1100x7777 bf16 B={B}")
+    _fwd_dx(layers["e1100x7777"], B, 7300 + B, True, None)
+
+
+def test_tiled_row_order_input_gradient(layers):
+    """The input gradient with values in row order (read through col_perm), at every tile width."""
+    L = layers["e1100x7777"]
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    built, W = device_layer(L, DEV)
+    for B in (16, 32, 64, 128):
+        say(f"tiled row-order dX e1100x7777 B={B}")
+        dy_in, dy64 = acts(7350 + B, B, O)
+        dX = snk.snack_coo_bwd_input(W, to_device(dy_in, DEV))
+        torch.cuda.synchronize()
+        ref = oracle.bwd_input(O, I, built["rows"], built["cols"], built["vals"], dy64, nthreads=NTHREADS)
+        check_close(dX.cpu().numpy(), ref, nnz / I, f"row-order dX B={B}")
 
 
 def test_tiled_deterministic_and_bias_rows(layers):
