@@ -759,31 +759,36 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
 // a group takes row 4g + s; each lane holds its 4 batch columns of that row's dY slice and, per
 // step, the dot product of its 4 columns with the entry's staged X row.  After a chunk of 16 steps
 // a reduce-scatter over the slot's 16 lanes leaves lane j with entry j's sum, stored in triple
-// order (16 consecutive entries per slot).  Batch tiles of 64 columns are taken in turn (the block
-// staged again), and tiles after the first add into dW; each entry belongs to one workgroup.
-template <int T0>
+// order (16 consecutive entries per slot).  Each lane holds VW columns of a TB = 16 VW column batch
+// tile (float4 at 64 columns); batch tiles are taken in turn (the block staged again), and tiles
+// after the first add into dW; each entry belongs to one workgroup.
+template <int VW, int T0>
 __device__ __forceinline__ void tile_dot4(float (&p)[16], uint32_t off, uint32_t lane_off, const char *lds,
-                                          const float4 &dy) {
-    float4 x[4];
-    x[0] = *reinterpret_cast<const float4 *>(lds + (bcast16<T0 + 0>(off) + lane_off));
-    x[1] = *reinterpret_cast<const float4 *>(lds + (bcast16<T0 + 1>(off) + lane_off));
-    x[2] = *reinterpret_cast<const float4 *>(lds + (bcast16<T0 + 2>(off) + lane_off));
-    x[3] = *reinterpret_cast<const float4 *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+                                          const typename TileVec<VW>::T &dy) {
+    typedef typename TileVec<VW>::T V;
+    V x[4];
+    x[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) + lane_off));
+    x[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
+    x[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
+    x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        float d = x[u].x * dy.x;
-        d = fmaf(x[u].y, dy.y, d);
-        d = fmaf(x[u].z, dy.z, d);
-        p[T0 + u] = fmaf(x[u].w, dy.w, d);
+        float d = vget(x[u], 0) * vget(dy, 0);
+#pragma unroll
+        for (int i = 1; i < VW; ++i) d = fmaf(vget(x[u], i), vget(dy, i), d);
+        p[T0 + u] = d;
     }
 }
 
-template <int CH>
+template <int VW, int CH>
 __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, int nbt, const int32_t *__restrict__ tab,
     const int32_t *__restrict__ gidx, const float *__restrict__ opnd, int opnd_rows, const float *__restrict__ dyt,
     int ld, float *__restrict__ dw) {
     constexpr int SL = 4;
+    constexpr int TB = 16 * VW;
+    constexpr uint32_t kRowBytes = 4u * TB;
+    typedef typename TileVec<VW>::T V;
     extern __shared__ float4 xs4[];
     const int64_t L = xcd_block();
     if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
@@ -793,8 +798,8 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int j = lane & 15;
     const int slot = lane >> 4;
-    const uint32_t lane_off = static_cast<uint32_t>(j * 16);
-    const uint32_t zoff = static_cast<uint32_t>(cw) * 256u;
+    const uint32_t lane_off = static_cast<uint32_t>(j * VW * 4);
+    const uint32_t zoff = static_cast<uint32_t>(cw) * kRowBytes;
     const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
     const int ngroups = (k_hi - k_lo + SL - 1) / SL;
     const int my_groups = wave < ngroups ? (ngroups - wave + kTileWaves - 1) / kTileWaves : 0;
@@ -810,49 +815,54 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     for (int bt = 0; bt < nbt; ++bt) {
         if (bt > 0) __syncthreads();  // the previous batch tile's reads of the block are done
         {
-            const float4 *src =
-                reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld + kTileBatch * bt);
-            const int ld4 = ld / 4, n4 = (cw + 1) * 16;
-            float4 tmp[kTileStageIters];
+            constexpr int R4 = TB / 4;  // float4s per staged row
+            constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
+            const float4 *src = reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld + TB * bt);
+            const int ld4 = ld / 4, n4 = (cw + 1) * R4;
+            constexpr int kHalf = (kIters + 1) / 2;  // two rounds: fewer registers live
 #pragma unroll
-            for (int it = 0; it < kTileStageIters; ++it) {
-                const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
-                const int c = i >> 4, q = i & 15;
-                tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            for (int h = 0; h < 2; ++h) {
+                float4 tmp[kHalf];
 #pragma unroll
-            for (int it = 0; it < kTileStageIters; ++it) {
-                const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
-                if (i < n4) xs4[i] = tmp[it];
+                for (int it = 0; it < kHalf; ++it) {
+                    const int i = (h * kHalf + it) * kTileThreads + static_cast<int>(threadIdx.x);
+                    const int c = i / R4, q = i % R4;
+                    tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int it = 0; it < kHalf; ++it) {
+                    const int i = (h * kHalf + it) * kTileThreads + static_cast<int>(threadIdx.x);
+                    if (i < n4) xs4[i] = tmp[it];
+                }
             }
         }
         const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : 0;
         __syncthreads();
-        auto load_group = [&](int g, int (&gi)[CH], float4 &dy) {
+        auto load_group = [&](int g, int (&gi)[CH], V &dy) {
             const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
             const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
             const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
             const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
 #pragma unroll
             for (int c = 0; c < CH; ++c) gi[c] = gidx[16 * c + j < len ? a + 16 * c + j : 0];
-            dy = *reinterpret_cast<const float4 *>(dyt + static_cast<int64_t>(key) * ld + kTileBatch * bt + 4 * j);
+            dy = *reinterpret_cast<const V *>(dyt + static_cast<int64_t>(key) * ld + TB * bt + VW * j);
         };
-        auto chunk = [&](int a, int len, int m, int c, uint32_t off, const float4 &dy) {
+        auto chunk = [&](int a, int len, int m, int c, uint32_t off, const V &dy) {
             float p[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) p[t] = 0.f;
             const int nst = m - 16 * c;
-            tile_dot4<0>(p, off, lane_off, lds, dy);
-            if (nst > 4) tile_dot4<4>(p, off, lane_off, lds, dy);
-            if (nst > 8) tile_dot4<8>(p, off, lane_off, lds, dy);
-            if (nst > 12) tile_dot4<12>(p, off, lane_off, lds, dy);
+            tile_dot4<VW, 0>(p, off, lane_off, lds, dy);
+            if (nst > 4) tile_dot4<VW, 4>(p, off, lane_off, lds, dy);
+            if (nst > 8) tile_dot4<VW, 8>(p, off, lane_off, lds, dy);
+            if (nst > 12) tile_dot4<VW, 12>(p, off, lane_off, lds, dy);
             const float r = group_reduce_scatter<16, 16>(p, j);
             if (16 * c + j < len) {
                 float *d = dw + a + 16 * c + j;
                 *d = bt == 0 ? r : *d + r;
             }
         };
-        auto compute = [&](int g, const int (&gi)[CH], const float4 &dy) {
+        auto compute = [&](int g, const int (&gi)[CH], const V &dy) {
             const int src = (g * SL + slot) * 4;
             const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
             const int len = __builtin_amdgcn_ds_bpermute(src, s_len);
@@ -862,20 +872,21 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
             for (int c = 0; c < CH; ++c) {
                 if (16 * c < m) {
                     const bool ok = 16 * c + j < len;
-                    chunk(a, len, m, c, ok ? static_cast<uint32_t>(gi[c] - c0) * 256u : zoff, dy);
+                    chunk(a, len, m, c, ok ? static_cast<uint32_t>(gi[c] - c0) * kRowBytes : zoff, dy);
                 }
             }
             for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
                 const bool ok = 16 * c + j < len;
                 const int gv = gidx[ok ? a + 16 * c + j : 0];
-                chunk(a, len, m, c, ok ? static_cast<uint32_t>(gv - c0) * 256u : zoff, dy);
+                chunk(a, len, m, c, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, dy);
             }
 #pragma unroll
             for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]));
-            asm volatile("" ::"v"(dy.x), "v"(dy.y), "v"(dy.z), "v"(dy.w));
+#pragma unroll
+            for (int i = 0; i < VW; ++i) asm volatile("" ::"v"(vget(dy, i)));
         };
         int gi0[CH], gi1[CH], gi2[CH];
-        float4 d0, d1, d2;
+        V d0, d1, d2;
         load_group(0, gi0, d0);
         load_group(1, gi1, d1);
         for (int g = 0; g < my_groups; g += 3) {
@@ -2266,10 +2277,11 @@ struct SddmmPlan {
     int64_t bpad;        // batch columns of the feature-major copies (rowsddmm: B rounded up to 4)
     size_t off_dw;       // row-order dW staging (values in column order)
     size_t off_x, off_dy, total;
-    // LDS-tiled weight gradient (tile_sddmm_kernel): chunks, column blocks, key blocks, block
-    // width, keys per key block, 64-column batch tiles; segment table in the workspace
+    // LDS-tiled weight gradient (tile_sddmm_kernel): batch columns per tile (16, 32 or 64),
+    // chunks, column blocks, key blocks, block width, keys per key block, batch tiles; segment
+    // table in the workspace
     bool tile;
-    int tch, tncb, tnrb, tcw, tkpr, tnbt;
+    int ttb, tch, tncb, tnrb, tcw, tkpr, tnbt;
     size_t off_tab;
 };
 
@@ -2329,24 +2341,28 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
     }
     // the LDS-tiled walk: batches padded to a multiple of 64 on large layers whose (row, column
     // block) segments average at least 8 entries
-    if (!p.csr1 && tile_env() != 0 && Bp % kTileBatch == 0 && nnz >= kTileMinNnz && I > 0 && O > 0) {
+    const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
+    if (!p.csr1 && tile_env() != 0 && tb > 0 && nnz >= kTileMinNnz && I > 0 && O > 0) {
         int64_t ncb, cw;
         tile_blocks(I, ncb, cw);
         const double mean = static_cast<double>(nnz) / static_cast<double>(O * ncb);
         if (mean >= 8.0 && O * (ncb + 1) < (int64_t(1) << 31)) {
             p.tile = true;
+            p.ttb = tb;
             p.rowq = 0;
             p.slices = 1;
             p.bpad = Bp;
             p.x_direct = p.dy_direct = false;
             const double need = mean + 4.0 * std::sqrt(mean) + 1.0;
-            p.tch = need <= 32.0 ? 2 : (need <= 64.0 ? 4 : 8);
+            // 8 chunks at 64 columns would spill registers; longer segments take their further
+            // chunks unprefetched there
+            p.tch = need <= 32.0 ? 2 : (need <= 64.0 || tb == 64 ? 4 : 8);
             p.tncb = static_cast<int>(ncb);
             p.tcw = static_cast<int>(cw);
-            const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256, ncb));
+            const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256 * (tb == 64 ? 1 : 2), ncb));
             p.tkpr = static_cast<int>(std::min<int64_t>(ceil_div(O, nrb0), kTileWaves * kWave));
             p.tnrb = static_cast<int>(ceil_div(O, p.tkpr));
-            p.tnbt = static_cast<int>(Bp / kTileBatch);
+            p.tnbt = static_cast<int>(Bp / tb);
         }
     }
     size_t at = 0;
@@ -2366,20 +2382,20 @@ int check_hip(const char *what);
 int launch_bounds(int64_t nkeys, int ncb, int cw, const int32_t *offs, const int32_t *gidx, int32_t *tab,
                   hipStream_t st);
 
-template <int CH>
+template <int VW, int CH>
 int launch_tile_sddmm_kernel(const SddmmPlan &p, int64_t O, int64_t I, const int32_t *tab, const int32_t *cols,
                              const float *xt, const float *dyt, float *dw, hipStream_t st) {
-    const size_t lds = static_cast<size_t>(p.tcw + 1) * kTileBatch * sizeof(float);
+    const size_t lds = static_cast<size_t>(p.tcw + 1) * (16 * VW) * sizeof(float);
     static bool attr = false;
     if (!attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_sddmm_kernel<CH>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_sddmm_kernel<VW, CH>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess)
             return fail(SNACK_ERR_HIP, "tile_sddmm_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
         attr = true;
     }
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)));
-    hipLaunchKernelGGL((tile_sddmm_kernel<CH>), grid, dim3(kTileThreads), lds, st, static_cast<int>(O), p.tncb,
+    hipLaunchKernelGGL((tile_sddmm_kernel<VW, CH>), grid, dim3(kTileThreads), lds, st, static_cast<int>(O), p.tncb,
                        p.tnrb, p.tcw, p.tkpr, p.tnbt, tab, cols, xt, static_cast<int>(I), dyt,
                        static_cast<int>(p.bpad), dw);
     return check_hip("tile_sddmm_kernel");
@@ -2397,12 +2413,23 @@ int launch_tile_sddmm(const SddmmPlan &p, const snack_coo_desc *W, const float *
         tab = t;
     }
     int s;
-    switch (p.tch) {
-        case 2: s = launch_tile_sddmm_kernel<2>(p, O, I, tab, W->cols, xt, dyt, dw, st); break;
-        case 4: s = launch_tile_sddmm_kernel<4>(p, O, I, tab, W->cols, xt, dyt, dw, st); break;
-        case 8: s = launch_tile_sddmm_kernel<8>(p, O, I, tab, W->cols, xt, dyt, dw, st); break;
-        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported chunk count %d", p.tch);
+#define SNACK_TSD(VWV)                                                                              \
+    switch (p.tch) {                                                                                \
+        case 2: s = launch_tile_sddmm_kernel<VWV, 2>(p, O, I, tab, W->cols, xt, dyt, dw, st); break; \
+        case 4: s = launch_tile_sddmm_kernel<VWV, 4>(p, O, I, tab, W->cols, xt, dyt, dw, st); break; \
+        case 8: s = launch_tile_sddmm_kernel<VWV, 8>(p, O, I, tab, W->cols, xt, dyt, dw, st); break; \
+        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported chunk count %d", p.tch);        \
     }
+    if (p.ttb == 16) {
+        SNACK_TSD(1)
+    } else if (p.ttb == 32) {
+        SNACK_TSD(2)
+    } else if (p.tch == 2) {
+        s = launch_tile_sddmm_kernel<4, 2>(p, O, I, tab, W->cols, xt, dyt, dw, st);
+    } else {
+        s = launch_tile_sddmm_kernel<4, 4>(p, O, I, tab, W->cols, xt, dyt, dw, st);
+    }
+#undef SNACK_TSD
     probe(false, st);
     return s;
 }
@@ -2466,7 +2493,7 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
     // col_perm, the weight gradient over the row view), one after the other, instead of the fused
     // pass: values in row order and one 64-column batch tile (with more tiles, or values in column
     // order, the fused pass measured faster)
-    if (p.fused && !colvals && Bp == kTileBatch) {
+    if (p.fused && !colvals && (Bp == 16 || Bp == 32 || Bp == 64)) {
         const SpmmPlan sp = plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals);
         const SddmmPlan sd = plan_sddmm(nnz, O, I, B, dtype, colvals);
         if (sp.mapping == kTile && sd.tile && sp.bpad == Bp && sd.bpad == Bp) {
