@@ -297,6 +297,25 @@ def traffic_for(workload, kernel):
     return rec.get("traffic_bytes")
 
 
+def batch_sweep(dev, K, batches=(16, 32)):
+    """The step (graph-replayed, us) at small batches on the 10k x 10k layers at 90 and 95 %: the
+    metric's batch range below 64, with the backward's form and the per-op kernel times."""
+    out = {}
+    for name, label in (("llm90", "90%"), ("target95", "95%")):
+        for B in batches:
+            layer = Layer(name, B, "f32", dev)
+            for _ in range(3):
+                layer.step()
+            g = graph_steps(layer, K)
+            _, kern = timed_steps(layer, K)
+            out[f"{label} B={B}"] = {"us_per_step_graph": None if g is None else round(g, 2),
+                                     "backward_fused": bwd_fused(layer),
+                                     "kernel_us": {op: round(float(np.mean(kern[op])) * 1000.0, 2)
+                                                   for op in STEP_OPS}}
+            del layer
+    return out
+
+
 def batch1_sweep(dev, K):
     """Batch-1 fwd+dX+dW latency at every sparsity level of the 10k x 10k layer."""
     out = {}
@@ -474,6 +493,8 @@ def main():
         del layer
         torch.cuda.empty_cache()
         extras["batch1_us_per_step"] = batch1_sweep(dev, max(10, args.steps // 2))
+        log("batch 16 and 32 steps")
+        extras["small_batch_us_per_step"] = batch_sweep(dev, max(10, args.steps // 2))
         log("GAMLP-shaped batch-1 inference")
         extras["gamlp_5000_b1_fwd_us"] = gamlp_inference(dev, max(20, args.steps))
     line = {
