@@ -456,7 +456,7 @@ def main():
     cand = STEP_OPS if bwd_fused(layer) else SPLIT_OPS
     dom = max(cand, key=lambda o: kernel_us[o])
     kname = {"fwd": "forward gather-reduce", "dx": "input-gradient gather-reduce",
-             "dw": "weight-gradient sampled product", "bwd": "fused backward pass (dX and dW)"}[dom]
+             "dw": "weight-gradient sampled product", "bwd": "backward pass (dX and dW in one pass)"}[dom]
     nbytes = {op: algorithmic_bytes(op, layer.nnz, layer.O, layer.I, B, layer.s) for op in all_ops}
     achieved = nbytes[dom] / (kernel_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

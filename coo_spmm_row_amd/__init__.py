@@ -458,7 +458,7 @@ def snack_coo_block_offsets(W: SnackCOO, view: int, out=None, stream=None):
 
 
 def snack_coo_bwd_is_fused(W: SnackCOO, batch: int, act_dtype: int = 0) -> bool:
-    """Whether snack_coo_bwd runs its one-pass kernel (True) or two tiled passes (False)."""
+    """Whether snack_coo_bwd takes both gradients in one pass (True) or two tiled passes (False)."""
     r = int(_lib.snack_coo_bwd_is_fused(W.desc, int(batch), int(act_dtype)))
     if r < 0:
         _check(-r, "snack_coo_bwd_is_fused")

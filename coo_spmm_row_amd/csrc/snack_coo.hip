@@ -902,6 +902,203 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     }
 }
 
+// Both gradients in one tiled pass over the column view (one batch tile of TB = 16 VW columns).
+// The workgroup stages a block of cw rows of dY^T; slot s walks column 4g+s and holds its X^T slice
+// (VW floats per lane).  Each step reads an entry's staged dY row once and uses it twice: dX
+// partials += v * dY row (as tile_spmm_kernel), and the dot product with the X slice, which a
+// reduce-scatter over the slot's 16 lanes turns into dW of 16 entries per chunk.  dW goes to the
+// walk position, or (VP: values in row order) to perm of it, the same permuted position the
+// value was read from.  The block partials of dX are summed by tile_sum_kernel.
+template <int VW, int T0>
+__device__ __forceinline__ void tile_bwd_steps4(float (&acc)[VW], float (&p)[16], uint32_t off, float v,
+                                                uint32_t lane_off, const char *lds,
+                                                const typename TileVec<VW>::T &xs) {
+    typedef typename TileVec<VW>::T V;
+    V y[4];
+    y[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) + lane_off));
+    y[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
+    y[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
+    y[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+#pragma unroll
+    for (int i = 0; i < VW; ++i) {
+        fmac_bcast16<T0 + 0, T0 == 0>(acc[i], v, vget(y[0], i));
+        fmac_bcast16<T0 + 1, false>(acc[i], v, vget(y[1], i));
+        fmac_bcast16<T0 + 2, false>(acc[i], v, vget(y[2], i));
+        fmac_bcast16<T0 + 3, false>(acc[i], v, vget(y[3], i));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        float d = vget(y[u], 0) * vget(xs, 0);
+#pragma unroll
+        for (int i = 1; i < VW; ++i) d = fmaf(vget(y[u], i), vget(xs, i), d);
+        p[T0 + u] = d;
+    }
+}
+
+template <int VW, int CH, bool VP>
+__global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
+    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
+    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm,
+    const float *__restrict__ opnd, int opnd_rows, int ld, const float *__restrict__ xt,
+    float *__restrict__ part, float *__restrict__ dw) {
+    constexpr int SL = 4;
+    constexpr int TB = 16 * VW;
+    constexpr uint32_t kRowBytes = 4u * TB;
+    typedef typename TileVec<VW>::T V;
+    extern __shared__ float4 xs4[];
+    const int64_t L = xcd_block();
+    if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
+    const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
+    const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int j = lane & 15;
+    const int slot = lane >> 4;
+    const uint32_t lane_off = static_cast<uint32_t>(j * VW * 4);
+    const uint32_t zoff = static_cast<uint32_t>(cw) * kRowBytes;
+    const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
+    const int ngroups = (k_hi - k_lo + SL - 1) / SL;
+    const int my_groups = wave < ngroups ? (ngroups - wave + kTileWaves - 1) / kTileWaves : 0;
+    const int key_l = k_lo + (wave + kTileWaves * (lane / SL)) * SL + lane % SL;
+    const bool key_l_ok = lane / SL < my_groups && key_l < k_hi;
+    int seg_a, seg_e;
+    {
+        const int64_t at = static_cast<int64_t>(key_l_ok ? key_l : k_lo) * (ncb + 1) + cb;
+        seg_a = tab[at];
+        seg_e = tab[at + 1];
+    }
+    {  // stage the block's rows of dY^T; rows cn..cw are zero (row cw is the zero row)
+        constexpr int R4 = TB / 4;
+        constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
+        constexpr int kHalf = (kIters + 1) / 2;  // two rounds: fewer registers live
+        const float4 *src = reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld);
+        const int ld4 = ld / 4, n4 = (cw + 1) * R4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float4 tmp[kHalf];
+#pragma unroll
+            for (int it = 0; it < kHalf; ++it) {
+                const int i = (h * kHalf + it) * kTileThreads + static_cast<int>(threadIdx.x);
+                const int c = i / R4, q = i % R4;
+                tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int it = 0; it < kHalf; ++it) {
+                const int i = (h * kHalf + it) * kTileThreads + static_cast<int>(threadIdx.x);
+                if (i < n4) xs4[i] = tmp[it];
+            }
+        }
+    }
+    const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : -1;
+    __syncthreads();
+    const char *lds = reinterpret_cast<const char *>(xs4);
+    float *pout = part + static_cast<int64_t>(cb) * nkeys * TB;
+    // chunks two groups ahead (VP: permuted positions two ahead, values one ahead), the X^T slice
+    // of each slot's column with its group's chunks
+    auto load_chunks = [&](int g, int (&gi)[CH], int (&vv)[CH], V &xsl) {
+        const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
+        const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
+        const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+        const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int idx = 16 * c + j < len ? a + 16 * c + j : 0;
+            gi[c] = gidx[idx];
+            vv[c] = VP ? perm[idx] : __float_as_int(vals[idx]);
+        }
+        xsl = *reinterpret_cast<const V *>(xt + static_cast<int64_t>(key < 0 ? 0 : key) * ld + VW * j);
+    };
+    auto load_vals = [&](const int (&pm)[CH], int (&vv)[CH]) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) vv[c] = __float_as_int(vals[pm[c]]);
+    };
+    auto chunk = [&](float (&acc)[VW], int a, int len, int m, int c, uint32_t off, float v, int pos,
+                     const V &xsl) {
+        float p[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) p[t] = 0.f;
+        const int nst = m - 16 * c;
+        tile_bwd_steps4<VW, 0>(acc, p, off, v, lane_off, lds, xsl);
+        if (nst > 4) tile_bwd_steps4<VW, 4>(acc, p, off, v, lane_off, lds, xsl);
+        if (nst > 8) tile_bwd_steps4<VW, 8>(acc, p, off, v, lane_off, lds, xsl);
+        if (nst > 12) tile_bwd_steps4<VW, 12>(acc, p, off, v, lane_off, lds, xsl);
+        const float r = group_reduce_scatter<16, 16>(p, j);
+        if (16 * c + j < len) dw[pos] = r;
+    };
+    auto compute = [&](int g, const int (&gi)[CH], const int (&vv)[CH], const int (&pm)[CH], const V &xsl) {
+        const int src = (g * SL + slot) * 4;
+        const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
+        const int len = __builtin_amdgcn_ds_bpermute(src, s_len);
+        const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
+        const int m = max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
+                          max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
+        float acc[VW];
+#pragma unroll
+        for (int i = 0; i < VW; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (16 * c < m) {
+                const bool ok = 16 * c + j < len;
+                const uint32_t off = ok ? static_cast<uint32_t>(gi[c] - c0) * kRowBytes : zoff;
+                const float v = ok ? __int_as_float(vv[c]) : 0.f;
+                chunk(acc, a, len, m, c, off, v, VP ? pm[c] : a + 16 * c + j, xsl);
+            }
+        }
+        for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
+            const bool ok = 16 * c + j < len;
+            const int idx = ok ? a + 16 * c + j : 0;
+            const int gv = gidx[idx];
+            const int pv = VP ? perm[idx] : idx;
+            const float w = vals[pv];
+            chunk(acc, a, len, m, c, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, ok ? w : 0.f, pv, xsl);
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]), "v"(pm[c]));
+#pragma unroll
+        for (int i = 0; i < VW; ++i) asm volatile("" ::"v"(vget(xsl, i)));
+        if (key >= 0) {
+            V r;
+            if constexpr (VW == 1) r = acc[0];
+            else if constexpr (VW == 2) r = make_float2(acc[0], acc[1]);
+            else r = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * TB + j * VW) = r;
+        }
+    };
+    int gi0[CH], gi1[CH], gi2[CH], vv0[CH], vv1[CH], vv2[CH], pm0[CH], pm1[CH], pm2[CH];
+    V x0, x1, x2;
+    if constexpr (!VP) {
+        load_chunks(0, gi0, vv0, x0);
+        load_chunks(1, gi1, vv1, x1);
+        for (int g = 0; g < my_groups; g += 3) {
+            load_chunks(g + 2, gi2, vv2, x2);
+            compute(g, gi0, vv0, gi0, x0);
+            if (g + 1 >= my_groups) break;
+            load_chunks(g + 3, gi0, vv0, x0);
+            compute(g + 1, gi1, vv1, gi1, x1);
+            if (g + 2 >= my_groups) break;
+            load_chunks(g + 4, gi1, vv1, x1);
+            compute(g + 2, gi2, vv2, gi2, x2);
+        }
+    } else {
+        load_chunks(0, gi0, pm0, x0);
+        load_chunks(1, gi1, pm1, x1);
+        load_vals(pm0, vv0);
+        for (int g = 0; g < my_groups; g += 3) {
+            load_chunks(g + 2, gi2, pm2, x2);
+            load_vals(pm1, vv1);
+            compute(g, gi0, vv0, pm0, x0);
+            if (g + 1 >= my_groups) break;
+            load_chunks(g + 3, gi0, pm0, x0);
+            load_vals(pm2, vv2);
+            compute(g + 1, gi1, vv1, pm1, x1);
+            if (g + 2 >= my_groups) break;
+            load_chunks(g + 4, gi1, pm1, x1);
+            load_vals(pm0, vv0);
+            compute(g + 2, gi2, vv2, pm2, x2);
+        }
+    }
+}
+
 // out[b][key] = bias[key] + sum over blocks cb (in order) of part[bt][cb][key][b - TB bt], b < nbo.
 // A workgroup adds 1024/TB keys x TB batch columns of one batch tile (one float4 per thread and
 // block, up to 16 blocks' loads in flight) and writes them transposed.
@@ -2443,8 +2640,10 @@ struct BwdPlan {
     int64_t bpad;   // batch columns of the feature-major copies (B rounded up to 4)
     size_t off_x, off_dy, off_part, total;
     // split: both gradients tiled, sharing the feature-major copies at off_x / off_dy; the input
-    // gradient's workspace starts at off_spmm, the weight gradient's segment table at off_sddmm
-    bool split;
+    // gradient's workspace starts at off_spmm, the weight gradient's segment table at off_sddmm.
+    // tiled: both gradients in one tiled pass over the column view (tile_bwd_kernel), its segment
+    // table and dX partials in the workspace at off_spmm (laid out by sp)
+    bool split, tiled;
     SpmmPlan sp;
     SddmmPlan sd;
     size_t off_spmm, off_sddmm;
@@ -2461,6 +2660,18 @@ struct BwdPlan {
 
 // Layers with at least this many entries take the row-banded form of the fused backward pass;
 // the environment variable SNACK_COO_BAND_MIN_NNZ (a decimal count) overrides the default.
+// The backward's form where more than one applies: SNACK_COO_BWD_FORM = "fused" (the one-pass
+// kernel reading dY rows from L2), "split" (two tiled passes) or "tiled" (one tiled pass); unset:
+// the library's choice.
+int bwd_form_env() {
+    const char *env = std::getenv("SNACK_COO_BWD_FORM");
+    if (!env) return -1;
+    if (!std::strcmp(env, "fused")) return 0;
+    if (!std::strcmp(env, "split")) return 1;
+    if (!std::strcmp(env, "tiled")) return 2;
+    return -1;
+}
+
 int64_t band_min_nnz() {
     if (const char *env = std::getenv("SNACK_COO_BAND_MIN_NNZ")) {
         char *end = nullptr;
@@ -2493,7 +2704,29 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
     // col_perm, the weight gradient over the row view), one after the other, instead of the fused
     // pass: values in row order and one 64-column batch tile (with more tiles, or values in column
     // order, the fused pass measured faster)
-    if (p.fused && !colvals && (Bp == 16 || Bp == 32 || Bp == 64)) {
+    // default: values in column order take the one tiled pass at 64 columns; values in row order
+    // the two tiled passes (the one tiled pass writes dW through col_perm there, and the scattered
+    // stores cost more than the second pass: 10k/95 %/B = 64 118 against 92 us)
+    const int form = bwd_form_env();
+    const bool tiled_ok = form == 2 || (form < 0 && colvals && Bp == 64);
+    if (p.fused && tiled_ok && (Bp == 16 || Bp == 32 || Bp == 64)) {
+        const SpmmPlan sp = plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals);
+        if (sp.mapping == kTile && sp.bpad == Bp && sp.tnbt == 1 && !sp.cvals) {
+            p.fused = false;
+            p.tiled = true;
+            p.sp = sp;
+            size_t at = 0;
+            p.off_x = at;
+            at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * Bp));
+            p.off_dy = at;
+            at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * Bp));
+            p.off_spmm = at;
+            at = align_up(at + sp.total);
+            p.total = at;
+            return p;
+        }
+    }
+    if (p.fused && form != 0 && form != 2 && !colvals && (Bp == 16 || Bp == 32 || Bp == 64)) {
         const SpmmPlan sp = plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals);
         const SddmmPlan sd = plan_sddmm(nnz, O, I, B, dtype, colvals);
         if (sp.mapping == kTile && sd.tile && sp.bpad == Bp && sd.bpad == Bp) {
@@ -3284,12 +3517,95 @@ static int run_split_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *
     return snack::ok();
 }
 
+template <int VW, int CH, bool VP>
+int launch_tile_bwd_kernel(const SpmmPlan &sp, int64_t I, int64_t O, const int32_t *tab, const snack_coo_desc *W,
+                           const float *dyt, const float *xt, float *part, float *dW, hipStream_t st) {
+    const size_t lds = static_cast<size_t>(sp.tcw + 1) * (16 * VW) * sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_bwd_kernel<VW, CH, VP>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess)
+            return fail(SNACK_ERR_HIP, "tile_bwd_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
+        attr = true;
+    }
+    const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(sp.tncb) * sp.tnrb)));
+    hipLaunchKernelGGL((tile_bwd_kernel<VW, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(I),
+                       sp.tncb, sp.tnrb, sp.tcw, sp.tkpr, tab, W->col_rows, W->vals, VP ? W->col_perm : nullptr,
+                       dyt, static_cast<int>(O), static_cast<int>(sp.bpad), xt, part, dW);
+    return check_hip("tile_bwd_kernel");
+}
+
+template <int VW, bool VP>
+int launch_tile_bwd_ch(const SpmmPlan &sp, int64_t I, int64_t O, const int32_t *tab, const snack_coo_desc *W,
+                       const float *dyt, const float *xt, float *part, float *dW, hipStream_t st) {
+    if (sp.tch <= 2) return launch_tile_bwd_kernel<VW, 2, VP>(sp, I, O, tab, W, dyt, xt, part, dW, st);
+    return launch_tile_bwd_kernel<VW, 4, VP>(sp, I, O, tab, W, dyt, xt, part, dW, st);
+}
+
+// Both gradients in one tiled pass (BwdPlan.tiled): db, one launch for the feature-major copies of
+// X and dY, tile_bwd_kernel over the column view (dW written directly; values in row order read
+// and dW written through col_perm), then the block sums of dX.  The probe brackets the last two.
+template <typename OutT>
+int run_tiled_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *X, const void *dY, int64_t batch,
+                  int act_dtype, OutT *dX, float *db, float *dW, char *ws, hipStream_t st) {
+    const int64_t O = W->out_features, I = W->in_features;
+    const SpmmPlan &sp = p.sp;
+    if (db) {
+        const dim3 grid(static_cast<unsigned>(ceil_div(O, kBlock)));
+        if (act_dtype == SNACK_F32)
+            hipLaunchKernelGGL(bias_grad_kernel<float>, grid, dim3(kBlock), 0, st, O, batch,
+                               static_cast<const float *>(dY), db);
+        else
+            hipLaunchKernelGGL(bias_grad_kernel<bf16_t>, grid, dim3(kBlock), 0, st, O, batch,
+                               static_cast<const bf16_t *>(dY), db);
+        if (int s = check_hip("bias_grad_kernel")) return s;
+    }
+    float *xt = reinterpret_cast<float *>(ws + p.off_x);
+    float *dyt = reinterpret_cast<float *>(ws + p.off_dy);
+    if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st, dY, O, dyt, p.bpad)) return s;
+    char *sws = ws + p.off_spmm;
+    float *part = reinterpret_cast<float *>(sws + sp.off_part);
+    probe(true, st);
+    const int32_t *tab = W->col_blocks;
+    if (!tab) {
+        int32_t *t = reinterpret_cast<int32_t *>(sws + sp.off_tab);
+        if (int s = launch_bounds(I, sp.tncb, sp.tcw, W->col_offsets, W->col_rows, t, st)) return s;
+        tab = t;
+    }
+    const bool vp = W->row_to_col == nullptr;  // values in row order: read and write through col_perm
+    int s;
+    switch (sp.ttb * 2 + (vp ? 1 : 0)) {
+        case 33: s = launch_tile_bwd_ch<1, true>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
+        case 32: s = launch_tile_bwd_ch<1, false>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
+        case 65: s = launch_tile_bwd_ch<2, true>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
+        case 64: s = launch_tile_bwd_ch<2, false>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
+        case 129: s = launch_tile_bwd_ch<4, true>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
+        case 128: s = launch_tile_bwd_ch<4, false>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
+        default: return fail(SNACK_ERR_INTERNAL, "tiled backward: unsupported batch tile %d", sp.ttb);
+    }
+    if (s) return s;
+    const unsigned kw = static_cast<unsigned>(4 * kBlock / sp.ttb);
+    const dim3 sgrid(static_cast<unsigned>(ceil_div(I, kw)), 1);
+    if (sp.ttb == 16)
+        hipLaunchKernelGGL((tile_sum_kernel<OutT, 16>), sgrid, dim3(kBlock), 0, st, part, static_cast<int>(I), sp.tncb,
+                           batch, nullptr, dX, I);
+    else if (sp.ttb == 32)
+        hipLaunchKernelGGL((tile_sum_kernel<OutT, 32>), sgrid, dim3(kBlock), 0, st, part, static_cast<int>(I), sp.tncb,
+                           batch, nullptr, dX, I);
+    else
+        hipLaunchKernelGGL((tile_sum_kernel<OutT, 64>), sgrid, dim3(kBlock), 0, st, part, static_cast<int>(I), sp.tncb,
+                           batch, nullptr, dX, I);
+    probe(false, st);
+    return check_hip("tile_sum_kernel");
+}
+
 extern "C" int snack_coo_bwd_is_fused(const snack_coo_desc *W, int64_t batch, int act_dtype) {
     try {
         if (int s = check_desc(W, true, "snack_coo_bwd_is_fused")) return -s;
         const BwdPlan p = plan_bwd(W->nnz, W->out_features, W->in_features, batch, act_dtype, vec16(W),
                                    W->row_to_col != nullptr);
-        return p.fused ? 1 : 0;
+        return p.fused || p.tiled ? 1 : 0;
     } catch (...) {
         return -fail(SNACK_ERR_INTERNAL, "snack_coo_bwd_is_fused: unexpected exception");
     }
@@ -3307,6 +3623,23 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
         const BwdPlan p = plan_bwd(nnz, O, I, batch, act_dtype, vec16(W), W->row_to_col != nullptr);
+        if (p.tiled) {
+            if (int s = check_act(X, act_dtype, "X", who)) return s;
+            if (int s = check_act(dY, act_dtype, "dY", who)) return s;
+            if (int s = check_act(dX, act_dtype, "dX", who)) return s;
+            if (!dW) return fail(SNACK_ERR_NULL, "%s: dW is NULL", who);
+            if (reinterpret_cast<uintptr_t>(dW) % 4) return fail(SNACK_ERR_ALIGN, "%s: dW misaligned", who);
+            if (db && reinterpret_cast<uintptr_t>(db) % 4) return fail(SNACK_ERR_ALIGN, "%s: db misaligned", who);
+            if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
+            char *ws = static_cast<char *>(workspace);
+            hipStream_t st = static_cast<hipStream_t>(hip_stream);
+            const int s = act_dtype == SNACK_F32
+                              ? run_tiled_bwd<float>(p, W, X, dY, batch, act_dtype, static_cast<float *>(dX), db, dW,
+                                                     ws, st)
+                              : run_tiled_bwd<bf16_t>(p, W, X, dY, batch, act_dtype, static_cast<bf16_t *>(dX), db,
+                                                      dW, ws, st);
+            return s ? s : snack::ok();
+        }
         if (p.split) {
             if (int s = check_act(X, act_dtype, "X", who)) return s;
             if (int s = check_act(dY, act_dtype, "dY", who)) return s;

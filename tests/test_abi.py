@@ -112,9 +112,13 @@ def test_column_order_values_host_checks_and_workspace():
     assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 64, 0) >= row_dw + 4 * 5000
     d.nnz = 1 << 21
     d.out_features = d.in_features = 4096
-    col_bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
-    d.row_to_col = None
-    row_bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)  # 2^21 entries: banded
+    os.environ["SNACK_COO_BWD_FORM"] = "fused"  # the one-pass kernel that gathers dY from L2
+    try:
+        col_bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
+        d.row_to_col = None
+        row_bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)  # 2^21 entries: banded
+    finally:
+        os.environ.pop("SNACK_COO_BWD_FORM", None)
     assert row_bwd - col_bwd >= 8 * 4096 * 64 * 4
     d.row_to_col = 0x1000
     ws = lib.snack_coo_topology_workspace_bytes(4096, 4096, 1 << 21, 10)

@@ -50,13 +50,14 @@ def tile_mode(v):
 
 @pytest.fixture(scope="module")
 def layers():
+    # every layer holds at least 2^20 entries, the tiled kernels' threshold
     return {
         # I = 5000: 8 blocks of 625 columns; ~30 entries per segment
         "u3000x5000": synth.random_small_layer(701, 3000, 5000, 1_200_000, "uniform"),
         # I = 7777: 13 blocks of 599 columns (the last one 589); three in four rows empty
         "e1100x7777": synth.random_small_layer(702, 1100, 7777, 1_100_000, "empty_rows"),
         # two full rows and two full columns: segments of a whole block (> 128 entries)
-        "d2000x4000": synth.random_small_layer(703, 2000, 4000, 1_000_000, "dense_lines"),
+        "d2000x4000": synth.random_small_layer(703, 2000, 4000, 1_100_000, "dense_lines"),
         # I = 600 < one block: a single column block
         "u4000x600": synth.random_small_layer(704, 4000, 600, 1_050_000, "uniform"),
     }
@@ -262,24 +263,52 @@ def test_tiled_dw_matches_untiled(layers):
     check_close(a.cpu().numpy(), b.cpu().numpy(), 64, "tiled vs rowsddmm dW")
 
 
-@pytest.mark.parametrize("name,B,fused", [("u3000x5000", 64, False), ("e1100x7777", 50, False),
-                                          ("u3000x5000", 128, True)])
-def test_backward_forms(layers, name, B, fused):
-    """snack_coo_bwd: two tiled passes (values in row order, one 64-column batch tile) or the
-    one-pass kernel; dX, dW and db against the oracle either way."""
+@contextlib.contextmanager
+def bwd_form(v):
+    """SNACK_COO_BWD_FORM: 'fused', 'split', 'tiled', or None for the library's choice."""
+    old = os.environ.get("SNACK_COO_BWD_FORM")
+    if v is None:
+        os.environ.pop("SNACK_COO_BWD_FORM", None)
+    else:
+        os.environ["SNACK_COO_BWD_FORM"] = v
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("SNACK_COO_BWD_FORM", None)
+        else:
+            os.environ["SNACK_COO_BWD_FORM"] = old
+
+
+@pytest.mark.parametrize("form", [None, "fused", "split", "tiled"])
+@pytest.mark.parametrize("name,B", [("u3000x5000", 64), ("e1100x7777", 50), ("d2000x4000", 16),
+                                    ("u4000x600", 32), ("u3000x5000", 128)])
+def test_backward_forms(layers, name, B, form):
+    """snack_coo_bwd in each form (one pass gathering dY from L2, two tiled passes, one tiled pass;
+    a form that does not apply falls back to the library's choice), values in row and in column
+    order: dX, dW (in the values' order) and db against the oracle."""
     L = layers[name]
-    say(f"snack_coo_bwd {name} B={B} fused={fused}")
     O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    assert nnz >= 1 << 20
     built, W = device_layer(L, DEV)
-    assert snk.snack_coo_bwd_is_fused(W, B) == fused
-    assert snk.snack_coo_bwd_is_fused(W.to_column_order(), B) is True
     x_in, x64 = acts(8200 + B, B, I)
     dy_in, dy64 = acts(8300 + B, B, O)
     X, dY = to_device(x_in, DEV), to_device(dy_in, DEV)
-    db = torch.empty(O, dtype=torch.float32, device=DEV)
-    dX, dW = snk.snack_coo_bwd(W, X, dY, db=db)
-    torch.cuda.synchronize()
     r, c, v = built["rows"], built["cols"], built["vals"]
-    check_close(dX.cpu().numpy(), oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS), nnz / I, "bwd dX")
-    check_close(dW.cpu().numpy(), oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS), B, "bwd dW")
-    check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, "bwd db")
+    dXr = oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS)
+    dWr = oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS)
+    for order, w in (("row", W), ("col", W.to_column_order())):
+        say(f"snack_coo_bwd {name} B={B} form={form} values in {order} order")
+        db = torch.empty(O, dtype=torch.float32, device=DEV)
+        with bwd_form(form):
+            one_pass = snk.snack_coo_bwd_is_fused(w, B)
+            dX, dW = snk.snack_coo_bwd(w, X, dY, db=db)
+            torch.cuda.synchronize()
+        if form in (None, "split") and order == "row" and B <= 64:
+            assert not one_pass
+        if form in ("fused", "tiled") or order == "col" or B > 64:
+            assert one_pass
+        ref_w = dWr[built["col_perm"].astype(np.int64)] if order == "col" else dWr
+        check_close(dX.cpu().numpy(), dXr, nnz / I, f"bwd dX ({order})")
+        check_close(dW.cpu().numpy(), ref_w, B, f"bwd dW ({order})")
+        check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, f"bwd db ({order})")
