@@ -42,6 +42,15 @@
  *    unique, in range; row_offsets and the column view consistent with them.
  *    Device calls check only O(1) things (null pointers, sizes, dtype,
  *    workspace size).
+ *  - Kernel choice: each device call picks its kernels from the layer's size,
+ *    the batch and the value order; results agree to rounding whichever runs,
+ *    and every kernel is deterministic except the batch-1 input gradient's
+ *    LDS-atomic scatter.  Layers of at least 2^20 entries at batches padded to
+ *    a multiple of 16 take LDS-tiled kernels (operand rows staged in LDS per
+ *    column block, see row_blocks / col_blocks).  Environment overrides, read
+ *    at every call (also by snack_coo_workspace_bytes): SNACK_COO_TILE=0 turns
+ *    the tiled kernels off; SNACK_COO_BWD_FORM=fused|split|tiled picks the form
+ *    of snack_coo_bwd where it applies; SNACK_COO_BAND_MIN_NNZ (below).
  */
 #ifndef SNACK_COO_H
 #define SNACK_COO_H
@@ -195,8 +204,15 @@ int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY
  * snack_coo_workspace_bytes(SNACK_OP_BWD, ...).  dX and dW are overwritten
  * (dW in the order of the triple, or of the column view with row_to_col);
  * results agree with the separate calls to rounding (the summation order of
- * dX differs).  Layers of at least 2^20
- * entries take a row-banded form of the one-pass kernel: the rows are cut into
+ * dX differs).  Forms (snack_coo_bwd_is_fused tells which one a call takes):
+ * with the tiled kernels applicable (see the conventions above) and one batch
+ * tile, values in row order take two tiled passes (the input gradient over the
+ * column view, then the weight gradient over the row view, sharing one layout
+ * transpose), and values in column order at a padded batch of 64 one tiled
+ * pass that serves each staged dY row to both gradients; otherwise the
+ * one-pass kernel that gathers each entry's dY row from L2 once for both
+ * gradients.  Layers of at least 2^20
+ * entries take a row-banded form of that one-pass kernel: the rows are cut into
  * 8 bands of about nnz/8 entries, each band's part of every column is walked on
  * its own, and the 8 partial dX are added in band order (deterministic; the
  * workspace then also holds 8*I*Bp floats, Bp the padded batch; values in
