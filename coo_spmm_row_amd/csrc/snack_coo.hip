@@ -509,6 +509,17 @@ constexpr int kTileLdsRows = 640;                     // 160 KB of LDS at 64 col
 constexpr int kTileMaxCols = kTileLdsRows - 1;        // operand rows per block (one more is the zero row)
 constexpr int kTileStageIters = kTileLdsRows * 16 / kTileThreads;  // float4 loads per thread to stage
 
+// Raw buffer resource over n 4-byte elements: loads through it take a 32-bit byte offset (the
+// chunk offsets fold into the instruction's immediate), and loads past the end return 0 instead of
+// touching memory.  Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), n * 4, 0x00020000);
+}
+__device__ __forceinline__ int buf_ld(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+constexpr int kBufPast = static_cast<int>(0xFFFFFFF0u);  // a byte offset past any buffer: the load returns 0
+
 // lane T of each row of 16 lanes, broadcast to the row (DPP row_newbcast)
 template <int T>
 __device__ __forceinline__ uint32_t bcast16(uint32_t v) {
@@ -603,7 +614,7 @@ __global__ __launch_bounds__(kBlock) void tile_bounds_kernel(int nkeys, int ncb,
 template <int VW, int CH, bool VP>
 __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
-    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm, int nnz,
     const float *__restrict__ opnd, int opnd_rows, int ld, float *__restrict__ part) {
     constexpr int SL = 4;                      // slots (keys) per wave, 16 lanes each
     constexpr int TB = 16 * VW;                // batch columns of a tile
@@ -658,22 +669,26 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     const char *lds = reinterpret_cast<const char *>(xs4);
     float *pout = part + (static_cast<int64_t>(bt) * ncb + cb) * static_cast<int64_t>(nkeys) * TB;
     // Chunks are loaded two groups ahead of the compute (three buffers in rotation).  Loads are
-    // issued unconditionally (clamped indices) and masked where they are used.
+    // issued unconditionally through buffer resources (entries past a segment read its neighbours,
+    // or 0 past the arrays' end) and masked where they are used.
     // vv: the values (VP: the permuted positions, turned into values by load_vals)
-    auto load_chunks = [&](int g, int (&gi)[CH], int (&vv)[CH]) {
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
+    // Lanes past the segment (len) load from past the buffers' end: nothing is read for them.
+    auto load_chunks = [&](int g, int (&gi)[CH], int (&vv)[CH], int &len) {
         const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
         const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-        const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+        len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+        const int base = (a + j) * 4;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int idx = 16 * c + j < len ? a + 16 * c + j : 0;
-            gi[c] = gidx[idx];
-            vv[c] = VP ? perm[idx] : __float_as_int(vals[idx]);
+            const int off = 16 * c + j < len ? base + 64 * c : kBufPast;
+            gi[c] = buf_ld(rg, off);
+            vv[c] = buf_ld(VP ? rp : rv, off);
         }
     };
-    auto load_vals = [&](const int (&pm)[CH], int (&vv)[CH]) {
+    auto load_vals = [&](const int (&pm)[CH], int len, int (&vv)[CH]) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) vv[c] = __float_as_int(vals[pm[c]]);
+        for (int c = 0; c < CH; ++c) vv[c] = buf_ld(rv, 16 * c + j < len ? pm[c] * 4 : kBufPast);
     };
     auto group_len = [&](int len) {
         return max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
@@ -699,9 +714,9 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         }
         for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
             const bool ok = 16 * c + j < len;
-            const int idx = ok ? a + 16 * c + j : 0;
-            const int gv = gidx[idx];
-            const float w = vals[VP ? perm[idx] : idx];
+            const int pos = (a + 16 * c + j) * 4;
+            const int gv = buf_ld(rg, pos);
+            const float w = __int_as_float(buf_ld(rv, VP ? (ok ? buf_ld(rp, pos) * 4 : kBufPast) : pos));
             tile_chunk<VW>(acc, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, ok ? w : 0.f, m - 16 * c, lane_off,
                            lds);
         }
@@ -720,35 +735,36 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     };
     int gi0[CH], gi1[CH], gi2[CH];
     int vv0[CH], vv1[CH], vv2[CH];
+    int n0 = 0, n1 = 0, n2 = 0;
     if constexpr (!VP) {
-        load_chunks(0, gi0, vv0);
-        load_chunks(1, gi1, vv1);
+        load_chunks(0, gi0, vv0, n0);
+        load_chunks(1, gi1, vv1, n1);
         for (int g = 0; g < my_groups; g += 3) {
-            load_chunks(g + 2, gi2, vv2);
+            load_chunks(g + 2, gi2, vv2, n2);
             compute(g, gi0, vv0);
             if (g + 1 >= my_groups) break;
-            load_chunks(g + 3, gi0, vv0);
+            load_chunks(g + 3, gi0, vv0, n0);
             compute(g + 1, gi1, vv1);
             if (g + 2 >= my_groups) break;
-            load_chunks(g + 4, gi1, vv1);
+            load_chunks(g + 4, gi1, vv1, n1);
             compute(g + 2, gi2, vv2);
         }
     } else {
         int pm0[CH], pm1[CH], pm2[CH];
-        load_chunks(0, gi0, pm0);
-        load_chunks(1, gi1, pm1);
-        load_vals(pm0, vv0);
+        load_chunks(0, gi0, pm0, n0);
+        load_chunks(1, gi1, pm1, n1);
+        load_vals(pm0, n0, vv0);
         for (int g = 0; g < my_groups; g += 3) {
-            load_chunks(g + 2, gi2, pm2);
-            load_vals(pm1, vv1);
+            load_chunks(g + 2, gi2, pm2, n2);
+            load_vals(pm1, n1, vv1);
             compute(g, gi0, vv0);
             if (g + 1 >= my_groups) break;
-            load_chunks(g + 3, gi0, pm0);
-            load_vals(pm2, vv2);
+            load_chunks(g + 3, gi0, pm0, n0);
+            load_vals(pm2, n2, vv2);
             compute(g + 1, gi1, vv1);
             if (g + 2 >= my_groups) break;
-            load_chunks(g + 4, gi1, pm1);
-            load_vals(pm0, vv0);
+            load_chunks(g + 4, gi1, pm1, n1);
+            load_vals(pm0, n0, vv0);
             compute(g + 2, gi2, vv2);
         }
     }
@@ -783,8 +799,8 @@ __device__ __forceinline__ void tile_dot4(float (&p)[16], uint32_t off, uint32_t
 template <int VW, int CH>
 __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, int nbt, const int32_t *__restrict__ tab,
-    const int32_t *__restrict__ gidx, const float *__restrict__ opnd, int opnd_rows, const float *__restrict__ dyt,
-    int ld, float *__restrict__ dw) {
+    const int32_t *__restrict__ gidx, int nnz, const float *__restrict__ opnd, int opnd_rows,
+    const float *__restrict__ dyt, int ld, float *__restrict__ dw) {
     constexpr int SL = 4;
     constexpr int TB = 16 * VW;
     constexpr uint32_t kRowBytes = 4u * TB;
@@ -838,13 +854,15 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
         }
         const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : 0;
         __syncthreads();
+        const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz);
         auto load_group = [&](int g, int (&gi)[CH], V &dy) {
             const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
             const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-            const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
             const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
+            const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+            const int base = (a + j) * 4;
 #pragma unroll
-            for (int c = 0; c < CH; ++c) gi[c] = gidx[16 * c + j < len ? a + 16 * c + j : 0];
+            for (int c = 0; c < CH; ++c) gi[c] = buf_ld(rg, 16 * c + j < len ? base + 64 * c : kBufPast);
             dy = *reinterpret_cast<const V *>(dyt + static_cast<int64_t>(key) * ld + TB * bt + VW * j);
         };
         auto chunk = [&](int a, int len, int m, int c, uint32_t off, const V &dy) {
@@ -877,7 +895,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
             }
             for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
                 const bool ok = 16 * c + j < len;
-                const int gv = gidx[ok ? a + 16 * c + j : 0];
+                const int gv = buf_ld(rg, (a + 16 * c + j) * 4);
                 chunk(a, len, m, c, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, dy);
             }
 #pragma unroll
@@ -938,7 +956,7 @@ __device__ __forceinline__ void tile_bwd_steps4(float (&acc)[VW], float (&p)[16]
 template <int VW, int CH, bool VP>
 __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
-    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm, int nnz,
     const float *__restrict__ opnd, int opnd_rows, int ld, const float *__restrict__ xt,
     float *__restrict__ part, float *__restrict__ dw) {
     constexpr int SL = 4;
@@ -995,22 +1013,24 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
     float *pout = part + static_cast<int64_t>(cb) * nkeys * TB;
     // chunks two groups ahead (VP: permuted positions two ahead, values one ahead), the X^T slice
     // of each slot's column with its group's chunks
-    auto load_chunks = [&](int g, int (&gi)[CH], int (&vv)[CH], V &xsl) {
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
+    auto load_chunks = [&](int g, int (&gi)[CH], int (&vv)[CH], V &xsl, int &len) {
         const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
         const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-        const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
         const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
+        len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+        const int base = (a + j) * 4;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int idx = 16 * c + j < len ? a + 16 * c + j : 0;
-            gi[c] = gidx[idx];
-            vv[c] = VP ? perm[idx] : __float_as_int(vals[idx]);
+        for (int c = 0; c < CH; ++c) {  // lanes past the segment read nothing
+            const int off = 16 * c + j < len ? base + 64 * c : kBufPast;
+            gi[c] = buf_ld(rg, off);
+            vv[c] = buf_ld(VP ? rp : rv, off);
         }
         xsl = *reinterpret_cast<const V *>(xt + static_cast<int64_t>(key < 0 ? 0 : key) * ld + VW * j);
     };
-    auto load_vals = [&](const int (&pm)[CH], int (&vv)[CH]) {
+    auto load_vals = [&](const int (&pm)[CH], int len, int (&vv)[CH]) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) vv[c] = __float_as_int(vals[pm[c]]);
+        for (int c = 0; c < CH; ++c) vv[c] = buf_ld(rv, 16 * c + j < len ? pm[c] * 4 : kBufPast);
     };
     auto chunk = [&](float (&acc)[VW], int a, int len, int m, int c, uint32_t off, float v, int pos,
                      const V &xsl) {
@@ -1046,10 +1066,10 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
         }
         for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
             const bool ok = 16 * c + j < len;
-            const int idx = ok ? a + 16 * c + j : 0;
-            const int gv = gidx[idx];
-            const int pv = VP ? perm[idx] : idx;
-            const float w = vals[pv];
+            const int pos = (a + 16 * c + j) * 4;
+            const int gv = buf_ld(rg, pos);
+            const int pv = VP ? buf_ld(rp, pos) : a + 16 * c + j;
+            const float w = __int_as_float(buf_ld(rv, ok ? pv * 4 : kBufPast));
             chunk(acc, a, len, m, c, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, ok ? w : 0.f, pv, xsl);
         }
 #pragma unroll
@@ -1066,34 +1086,35 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
     };
     int gi0[CH], gi1[CH], gi2[CH], vv0[CH], vv1[CH], vv2[CH], pm0[CH], pm1[CH], pm2[CH];
     V x0, x1, x2;
+    int n0 = 0, n1 = 0, n2 = 0;
     if constexpr (!VP) {
-        load_chunks(0, gi0, vv0, x0);
-        load_chunks(1, gi1, vv1, x1);
+        load_chunks(0, gi0, vv0, x0, n0);
+        load_chunks(1, gi1, vv1, x1, n1);
         for (int g = 0; g < my_groups; g += 3) {
-            load_chunks(g + 2, gi2, vv2, x2);
+            load_chunks(g + 2, gi2, vv2, x2, n2);
             compute(g, gi0, vv0, gi0, x0);
             if (g + 1 >= my_groups) break;
-            load_chunks(g + 3, gi0, vv0, x0);
+            load_chunks(g + 3, gi0, vv0, x0, n0);
             compute(g + 1, gi1, vv1, gi1, x1);
             if (g + 2 >= my_groups) break;
-            load_chunks(g + 4, gi1, vv1, x1);
+            load_chunks(g + 4, gi1, vv1, x1, n1);
             compute(g + 2, gi2, vv2, gi2, x2);
         }
     } else {
-        load_chunks(0, gi0, pm0, x0);
-        load_chunks(1, gi1, pm1, x1);
-        load_vals(pm0, vv0);
+        load_chunks(0, gi0, pm0, x0, n0);
+        load_chunks(1, gi1, pm1, x1, n1);
+        load_vals(pm0, n0, vv0);
         for (int g = 0; g < my_groups; g += 3) {
-            load_chunks(g + 2, gi2, pm2, x2);
-            load_vals(pm1, vv1);
+            load_chunks(g + 2, gi2, pm2, x2, n2);
+            load_vals(pm1, n1, vv1);
             compute(g, gi0, vv0, pm0, x0);
             if (g + 1 >= my_groups) break;
-            load_chunks(g + 3, gi0, pm0, x0);
-            load_vals(pm2, vv2);
+            load_chunks(g + 3, gi0, pm0, x0, n0);
+            load_vals(pm2, n2, vv2);
             compute(g + 1, gi1, vv1, pm1, x1);
             if (g + 2 >= my_groups) break;
-            load_chunks(g + 4, gi1, pm1, x1);
-            load_vals(pm0, vv0);
+            load_chunks(g + 4, gi1, pm1, x1, n1);
+            load_vals(pm0, n0, vv0);
             compute(g + 2, gi2, vv2, pm2, x2);
         }
     }
@@ -2259,7 +2280,7 @@ struct SpmmPlan {
     size_t off_opnd, off_head, off_tail, off_cvals, total;
     // kTile: batch columns per tile (16, 32 or 64), prefetched chunks, column blocks, key blocks,
     // block width, keys per key block, batch tiles; offset table and partial sums in the workspace
-    int ttb, tch, tncb, tnrb, tcw, tkpr, tnbt;
+    int ttb, tch, tncb, tnrb, tcw, tkpr, tnbt, tnnz;
     size_t off_tab, off_part;
 };
 
@@ -2404,7 +2425,9 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     if (env == 0) return;
     const int64_t Bp = pad_batch(B);
     const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
-    if (tb == 0 || Bp / tb > 65535 || nnz < kTileMinNnz || opnd_rows < 1 || nkeys < 1) return;
+    // nnz < 2^30: the tiles read the per-entry arrays through 32-bit byte offsets
+    if (tb == 0 || Bp / tb > 65535 || nnz < kTileMinNnz || nnz >= (int64_t(1) << 30) || opnd_rows < 1 || nkeys < 1)
+        return;
     int64_t ncb, cw;
     tile_blocks(opnd_rows, ncb, cw);
     const double mean = static_cast<double>(nnz) / static_cast<double>(nkeys * ncb);
@@ -2412,6 +2435,7 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     p.mapping = kTile;
     p.bpad = Bp;
     p.ttb = tb;
+    p.tnnz = static_cast<int>(nnz);
     // workgroups per CU: one at 64 columns (160 KB of LDS), two at 16 or 32 (the wave limit)
     const int64_t per_cu = tb == 64 ? 1 : 2;
     const double need = mean + 4.0 * std::sqrt(mean) + 1.0;
@@ -2478,7 +2502,7 @@ struct SddmmPlan {
     // chunks, column blocks, key blocks, block width, keys per key block, batch tiles; segment
     // table in the workspace
     bool tile;
-    int ttb, tch, tncb, tnrb, tcw, tkpr, tnbt;
+    int ttb, tch, tncb, tnrb, tcw, tkpr, tnbt, tnnz;
     size_t off_tab;
 };
 
@@ -2539,13 +2563,14 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
     // the LDS-tiled walk: batches padded to a multiple of 64 on large layers whose (row, column
     // block) segments average at least 8 entries
     const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
-    if (!p.csr1 && tile_env() != 0 && tb > 0 && nnz >= kTileMinNnz && I > 0 && O > 0) {
+    if (!p.csr1 && tile_env() != 0 && tb > 0 && nnz >= kTileMinNnz && nnz < (int64_t(1) << 30) && I > 0 && O > 0) {
         int64_t ncb, cw;
         tile_blocks(I, ncb, cw);
         const double mean = static_cast<double>(nnz) / static_cast<double>(O * ncb);
         if (mean >= 8.0 && O * (ncb + 1) < (int64_t(1) << 31)) {
             p.tile = true;
             p.ttb = tb;
+            p.tnnz = static_cast<int>(nnz);
             p.rowq = 0;
             p.slices = 1;
             p.bpad = Bp;
@@ -2593,7 +2618,7 @@ int launch_tile_sddmm_kernel(const SddmmPlan &p, int64_t O, int64_t I, const int
     }
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)));
     hipLaunchKernelGGL((tile_sddmm_kernel<VW, CH>), grid, dim3(kTileThreads), lds, st, static_cast<int>(O), p.tncb,
-                       p.tnrb, p.tcw, p.tkpr, p.tnbt, tab, cols, xt, static_cast<int>(I), dyt,
+                       p.tnrb, p.tcw, p.tkpr, p.tnbt, tab, cols, p.tnnz, xt, static_cast<int>(I), dyt,
                        static_cast<int>(p.bpad), dw);
     return check_hip("tile_sddmm_kernel");
 }
@@ -2890,8 +2915,8 @@ int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, con
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)),
                     static_cast<unsigned>(p.tnbt));
     hipLaunchKernelGGL((tile_spmm_kernel<VW, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(nkeys),
-                       p.tncb, p.tnrb, p.tcw, p.tkpr, tab, gidx, vals, perm, opnd, static_cast<int>(opnd_rows),
-                       static_cast<int>(p.bpad), part);
+                       p.tncb, p.tnrb, p.tcw, p.tkpr, tab, gidx, vals, perm, p.tnnz, opnd,
+                       static_cast<int>(opnd_rows), static_cast<int>(p.bpad), part);
     return check_hip("tile_spmm_kernel");
 }
 
@@ -3532,7 +3557,7 @@ int launch_tile_bwd_kernel(const SpmmPlan &sp, int64_t I, int64_t O, const int32
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(sp.tncb) * sp.tnrb)));
     hipLaunchKernelGGL((tile_bwd_kernel<VW, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(I),
                        sp.tncb, sp.tnrb, sp.tcw, sp.tkpr, tab, W->col_rows, W->vals, VP ? W->col_perm : nullptr,
-                       dyt, static_cast<int>(O), static_cast<int>(sp.bpad), xt, part, dW);
+                       sp.tnnz, dyt, static_cast<int>(O), static_cast<int>(sp.bpad), xt, part, dW);
     return check_hip("tile_bwd_kernel");
 }
 
