@@ -2407,6 +2407,7 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
 // tile is 64 columns where the padded batch allows, else 32 or 16.  SNACK_COO_TILE=0 in the
 // environment turns the tiled kernels off.
 constexpr int64_t kTileMinNnz = int64_t(1) << 20;
+constexpr int64_t kTileMaxBatchTiles = 4;  // up to 256 batch columns
 
 int tile_env() {
     const char *env = std::getenv("SNACK_COO_TILE");
@@ -2425,8 +2426,11 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     if (env == 0) return;
     const int64_t Bp = pad_batch(B);
     const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
-    // nnz < 2^30: the tiles read the per-entry arrays through 32-bit byte offsets
-    if (tb == 0 || Bp / tb > 65535 || nnz < kTileMinNnz || nnz >= (int64_t(1) << 30) || opnd_rows < 1 || nkeys < 1)
+    // nnz < 2^30: the tiles read the per-entry arrays through 32-bit byte offsets.  At most
+    // kTileMaxBatchTiles batch tiles: the block partials grow with the batch, and wider batches keep
+    // the wide-batch gather paths.
+    if (tb == 0 || Bp / tb > kTileMaxBatchTiles || nnz < kTileMinNnz || nnz >= (int64_t(1) << 30) ||
+        opnd_rows < 1 || nkeys < 1)
         return;
     int64_t ncb, cw;
     tile_blocks(opnd_rows, ncb, cw);
@@ -2563,7 +2567,8 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
     // the LDS-tiled walk: batches padded to a multiple of 64 on large layers whose (row, column
     // block) segments average at least 8 entries
     const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
-    if (!p.csr1 && tile_env() != 0 && tb > 0 && nnz >= kTileMinNnz && nnz < (int64_t(1) << 30) && I > 0 && O > 0) {
+    if (!p.csr1 && tile_env() != 0 && tb > 0 && Bp / tb <= kTileMaxBatchTiles && nnz >= kTileMinNnz &&
+        nnz < (int64_t(1) << 30) && I > 0 && O > 0) {
         int64_t ncb, cw;
         tile_blocks(I, ncb, cw);
         const double mean = static_cast<double>(nnz) / static_cast<double>(O * ncb);
