@@ -28,6 +28,12 @@
 //  * the weight gradient is a sampled dense-dense product over the stored
 //    entries: a group of BT lanes per entry, each lane a slice of the batch,
 //    reduced across the group by xor shuffles.
+//  * LDS-tiled forms of all three (large layers, batches padded to a multiple
+//    of 16 up to 256): W is cut into tiles of a key range x a block of ~625
+//    operand rows; a 1024-thread workgroup stages its block of the operand in
+//    LDS once and serves every entry of the tile from there (tile_spmm_kernel,
+//    tile_sddmm_kernel, tile_bwd_kernel); the forward and input gradient write
+//    per-block partial sums that tile_sum_kernel adds in block order.
 // No MFMA: the work is an irregular gather, not a dense contraction.
 
 #include <hip/hip_runtime.h>
