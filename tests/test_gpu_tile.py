@@ -312,3 +312,73 @@ def test_backward_forms(layers, name, B, form):
         check_close(dX.cpu().numpy(), dXr, nnz / I, f"bwd dX ({order})")
         check_close(dW.cpu().numpy(), ref_w, B, f"bwd dW ({order})")
         check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, f"bwd db ({order})")
+
+
+@pytest.mark.parametrize("form", ["split", "tiled"])
+def test_backward_forms_bf16(layers, form):
+    """bf16 activations through the two-pass and one-pass tiled backward (dX rounded to bf16)."""
+    L = layers["e1100x7777"]
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    built, W = device_layer(L, DEV)
+    x_in, x64 = acts(8400, 64, I, True)
+    dy_in, dy64 = acts(8401, 64, O, True)
+    X, dY = to_device(x_in, DEV, True), to_device(dy_in, DEV, True)
+    r, c, v = built["rows"], built["cols"], built["vals"]
+    for order, w in (("row", W), ("col", W.to_column_order())):
+        say(f"snack_coo_bwd bf16 form={form} values in {order} order")
+        with bwd_form(form):
+            dX, dW = snk.snack_coo_bwd(w, X, dY)
+            torch.cuda.synchronize()
+        ref_w = oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS)
+        if order == "col":
+            ref_w = ref_w[built["col_perm"].astype(np.int64)]
+        check_close(from_device(dX), oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS), nnz / I,
+                    f"bf16 bwd dX ({order})", True)
+        check_close(dW.cpu().numpy(), ref_w, 64, f"bf16 bwd dW ({order})", True)
+
+
+@pytest.mark.parametrize("order", ["row", "col"])
+def test_tiled_backward_in_graph(layers, order):
+    """The step with the tiled backward (two passes for row order, one for column order) captured
+    in a HIP graph and replayed several times with eager work in between: every replay equals the
+    eager result bit for bit."""
+    L = layers["u3000x5000"]
+    say(f"tiled step in a HIP graph, values in {order} order")
+    built, W = device_layer(L, DEV)
+    if order == "col":
+        W = W.to_column_order()
+    B = 64
+    x_in, _ = acts(8500, B, L["in_features"])
+    dy_in, _ = acts(8501, B, L["out_features"])
+    X, dY = to_device(x_in, DEV), to_device(dy_in, DEV)
+    b = torch.from_numpy(L["bias"]).to(DEV)
+    need = max(snk.snack_coo_workspace_bytes(op, W, B, snk.SNACK_F32) for op in (0, 3))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
+    Y = torch.empty(B, L["out_features"], device=DEV)
+    dX = torch.empty(B, L["in_features"], device=DEV)
+    dW = torch.empty(L["nnz"], device=DEV)
+    db = torch.empty(L["out_features"], device=DEV)
+
+    def step():
+        snk.snack_coo_fwd(W, X, b, out=Y, workspace=ws)
+        snk.snack_coo_bwd(W, X, dY, dx_out=dX, dw_out=dW, db=db, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (Y, dX, dW, db)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        for t in (Y, dX, dW, db):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip((Y, dX, dW, db), ref):
+            assert torch.equal(t, r)
+        _ = X.sum()
