@@ -2386,6 +2386,11 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
                     break;
                 }
             }
+        } else if (Bp % 256 == 0 && nnz < 16 * nout) {
+            // keys averaging < 16 entries at wide batches: 256-column tiles (4 float4s per lane), so
+            // each key's index loads serve 4x the columns (a wave per key is latency-bound there)
+            p.bt = 16;
+            p.q = 4;
         }
     } else {
         p.mapping = kSegscan;
@@ -2552,7 +2557,8 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
                 break;
             }
         }
-        if (p.rowq == 0 && Bp % 256 == 0 && nnz >= kLargeBatchMinNnz) {  // wide batch, large layer:
+        // wide batch, large layer or rows averaging < 16 entries:
+        if (p.rowq == 0 && Bp % 256 == 0 && (nnz >= kLargeBatchMinNnz || nnz < 16 * O)) {
             // slices of 256 columns (each gathers its part of the X rows once per entry; the
             // per-entry kernel re-reads the whole dY row per entry)
             p.bt = 16;
@@ -3029,8 +3035,9 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
         break;
             SNACK_RW(1, 1) SNACK_RW(2, 1) SNACK_RW(4, 1) SNACK_RW(8, 1) SNACK_RW(16, 1)
             SNACK_RW(1, 3) SNACK_RW(2, 3) SNACK_RW(4, 3) SNACK_RW(8, 3) SNACK_RW(16, 3)
+            SNACK_RW(16, 4)
 #if SNACK_ROWWAVE_Q_MODE == 2
-            SNACK_RW(16, 2) SNACK_RW(16, 4)
+            SNACK_RW(16, 2)
 #endif
 #undef SNACK_RW
             default: return fail(SNACK_ERR_INTERNAL, "rowwave: unsupported plan bt=%d q=%d", p.bt, p.q);
