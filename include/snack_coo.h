@@ -224,10 +224,10 @@ int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_
                   void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Whether snack_coo_bwd takes both gradients in one pass over the column view (1: the kernel that
- * gathers dY rows from L2, or the tiled pass that serves them from LDS), or in two tiled passes (0:
- * the input gradient over the column view and the weight gradient over the row view) for this
- * weight, batch and dtype -- the choice the call would make.  Negative: -(status) for an invalid
- * descriptor.  For timing and diagnostics. */
+ * gathers dY rows from L2, or the tiled pass that serves them from LDS), or in two passes (0: the
+ * tiled input gradient over the column view and the tiled weight gradient over the row view, or at
+ * batch 1 the two gradients' own kernels) for this weight, batch and dtype -- the choice the call
+ * would make.  Negative: -(status) for an invalid descriptor.  For timing and diagnostics. */
 int snack_coo_bwd_is_fused(const snack_coo_desc *W, int64_t batch, int act_dtype);
 
 /* Device-side topology update (Appendix G prune-and-regrow, regrowth by

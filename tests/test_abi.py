@@ -167,3 +167,31 @@ def test_tiled_workspace_bounded_by_batch_tiles():
     fwd4096 = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 4096, 0)
     assert fwd4096 < 4 * 4096 * nb * 5000  # no partials: not tiled
     assert fwd4096 <= 4 * 5001 * 4096 + 4 * 2_500_000 + (1 << 20)  # operand copy and gathered values
+
+
+def test_backward_form_rules():
+    """The documented choice of snack_coo_bwd's form (host-side planning, no GPU): two tiled passes
+    for values in row order at one batch tile of 16, 32 or 64 columns on layers of >= 2^20 entries,
+    two untiled passes at batch 1, one pass otherwise (the tiled pass for column order at 64
+    columns, the L2-gather kernel else); SNACK_COO_TILE=0 and SNACK_COO_BWD_FORM override."""
+    lib = snk._lib
+    d = snk._Desc()
+    d.out_features, d.in_features, d.nnz = 10000, 10000, 5_000_000
+    d.row_offsets = d.rows = d.cols = d.vals = 0x1000
+    d.col_perm = d.col_rows = d.col_cols = d.col_offsets = 0x1000
+    fused = lambda B: lib.snack_coo_bwd_is_fused(ctypes.byref(d), B, 0)
+    # batch 1: the two gradients' own kernels one after the other (two passes, not tiled)
+    assert [fused(B) for B in (1, 16, 32, 50, 64, 96, 128)] == [0, 0, 0, 0, 0, 1, 1]
+    d.row_to_col = 0x1000  # values in column order: always one pass
+    assert [fused(B) for B in (16, 64, 128)] == [1, 1, 1]
+    d.row_to_col = None
+    d.nnz = 1_000_000  # below 2^20 entries: never tiled
+    assert fused(64) == 1
+    d.nnz = 5_000_000
+    for env, want in ((("SNACK_COO_TILE", "0"), 1), (("SNACK_COO_BWD_FORM", "fused"), 1),
+                      (("SNACK_COO_BWD_FORM", "tiled"), 1), (("SNACK_COO_BWD_FORM", "split"), 0)):
+        os.environ[env[0]] = env[1]
+        try:
+            assert fused(64) == want, env
+        finally:
+            os.environ.pop(env[0], None)
