@@ -510,10 +510,8 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
 // with value 0.
 constexpr int kTileThreads = 1024;
 constexpr int kTileWaves = kTileThreads / kWave;
-constexpr int kTileBatch = 64;                        // widest batch tile: one 256-byte LDS row
 constexpr int kTileLdsRows = 640;                     // 160 KB of LDS at 64 columns
 constexpr int kTileMaxCols = kTileLdsRows - 1;        // operand rows per block (one more is the zero row)
-constexpr int kTileStageIters = kTileLdsRows * 16 / kTileThreads;  // float4 loads per thread to stage
 
 // Raw buffer resource over n 4-byte elements: loads through it take a 32-bit byte offset (the
 // chunk offsets fold into the instruction's immediate), and loads past the end return 0 instead of
