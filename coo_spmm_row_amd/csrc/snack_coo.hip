@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstdint>
@@ -2619,18 +2620,30 @@ int check_hip(const char *what);
 int launch_bounds(int64_t nkeys, int ncb, int cw, const int32_t *offs, const int32_t *gidx, int32_t *tab,
                   hipStream_t st);
 
+// Allows kernel (name, f) lds bytes of dynamic LDS -- the most any of its launches asks for --
+// once per device: done holds a bit per device already set.
+int allow_lds(const void *f, size_t lds, std::atomic<uint64_t> &done, const char *name) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return check_hip(name);
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return SNACK_OK;
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return fail(SNACK_ERR_HIP, "%s: %zu bytes of LDS: %s", name, lds, hipGetErrorString(e));
+    done.fetch_or(bit, std::memory_order_release);
+    return SNACK_OK;
+}
+
+// The tiled kernels' largest dynamic LDS at VW floats per lane: kTileLdsRows staged rows of 16 VW.
+constexpr size_t tile_lds_max(int VW) { return static_cast<size_t>(kTileLdsRows) * 16 * VW * sizeof(float); }
+
 template <int VW, int CH>
 int launch_tile_sddmm_kernel(const SddmmPlan &p, int64_t O, int64_t I, const int32_t *tab, const int32_t *cols,
                              const float *xt, const float *dyt, float *dw, hipStream_t st) {
     const size_t lds = static_cast<size_t>(p.tcw + 1) * (16 * VW) * sizeof(float);
-    static bool attr = false;
-    if (!attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_sddmm_kernel<VW, CH>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess)
-            return fail(SNACK_ERR_HIP, "tile_sddmm_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
-        attr = true;
-    }
+    static std::atomic<uint64_t> lds_ok{0};
+    if (int s = allow_lds(reinterpret_cast<const void *>(&tile_sddmm_kernel<VW, CH>), tile_lds_max(VW), lds_ok,
+                          "tile_sddmm_kernel"))
+        return s;
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)));
     hipLaunchKernelGGL((tile_sddmm_kernel<VW, CH>), grid, dim3(kTileThreads), lds, st, static_cast<int>(O), p.tncb,
                        p.tnrb, p.tcw, p.tkpr, p.tnbt, tab, cols, p.tnnz, xt, static_cast<int>(I), dyt,
@@ -2919,14 +2932,10 @@ template <int VW, int CH, bool VP>
 int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
                        const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
     const size_t lds = static_cast<size_t>(p.tcw + 1) * (16 * VW) * sizeof(float);
-    static bool attr = false;  // the 160 KB of dynamic LDS, allowed once per instantiation
-    if (!attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_spmm_kernel<VW, CH, VP>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess)
-            return fail(SNACK_ERR_HIP, "tile_spmm_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
-        attr = true;
-    }
+    static std::atomic<uint64_t> lds_ok{0};  // up to 160 KB of dynamic LDS, allowed once per device
+    if (int s = allow_lds(reinterpret_cast<const void *>(&tile_spmm_kernel<VW, CH, VP>), tile_lds_max(VW), lds_ok,
+                          "tile_spmm_kernel"))
+        return s;
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)),
                     static_cast<unsigned>(p.tnbt));
     hipLaunchKernelGGL((tile_spmm_kernel<VW, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(nkeys),
@@ -3220,16 +3229,14 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         if (p.mapping == kCsr1Priv) {
             float *partial = reinterpret_cast<float *>(ws + p.off_head);
             const size_t lds = sizeof(float) * static_cast<size_t>(kPrivWaves * I);
-            static const bool attr = [] {  // up to 160 KB of LDS
-                (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&csr1_dxpriv_kernel<float>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          static_cast<int>(sizeof(float) * kPrivWaves * kPrivMaxI));
-                (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&csr1_dxpriv_kernel<bf16_t>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          static_cast<int>(sizeof(float) * kPrivWaves * kPrivMaxI));
-                return true;
-            }();
-            (void)attr;
+            static std::atomic<uint64_t> lds_f32{0}, lds_bf16{0};  // up to 160 KB of LDS
+            const size_t lds_max = sizeof(float) * kPrivWaves * kPrivMaxI;
+            if (int s = act_dtype == SNACK_F32
+                            ? allow_lds(reinterpret_cast<const void *>(&csr1_dxpriv_kernel<float>), lds_max, lds_f32,
+                                        "csr1_dxpriv_kernel")
+                            : allow_lds(reinterpret_cast<const void *>(&csr1_dxpriv_kernel<bf16_t>), lds_max,
+                                        lds_bf16, "csr1_dxpriv_kernel"))
+                return s;
             const int o = static_cast<int>(O), in = static_cast<int>(I), nz = static_cast<int>(nnz),
                       ch = static_cast<int>(p.chunk), nc = static_cast<int>(p.nchunks);
             const dim3 grid(static_cast<unsigned>(p.nparts));
@@ -3562,14 +3569,10 @@ template <int VW, int CH, bool VP>
 int launch_tile_bwd_kernel(const SpmmPlan &sp, int64_t I, int64_t O, const int32_t *tab, const snack_coo_desc *W,
                            const float *dyt, const float *xt, float *part, float *dW, hipStream_t st) {
     const size_t lds = static_cast<size_t>(sp.tcw + 1) * (16 * VW) * sizeof(float);
-    static bool attr = false;
-    if (!attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tile_bwd_kernel<VW, CH, VP>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess)
-            return fail(SNACK_ERR_HIP, "tile_bwd_kernel: %zu bytes of LDS: %s", lds, hipGetErrorString(e));
-        attr = true;
-    }
+    static std::atomic<uint64_t> lds_ok{0};
+    if (int s = allow_lds(reinterpret_cast<const void *>(&tile_bwd_kernel<VW, CH, VP>), tile_lds_max(VW), lds_ok,
+                          "tile_bwd_kernel"))
+        return s;
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(sp.tncb) * sp.tnrb)));
     hipLaunchKernelGGL((tile_bwd_kernel<VW, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(I),
                        sp.tncb, sp.tnrb, sp.tcw, sp.tkpr, tab, W->col_rows, W->vals, VP ? W->col_perm : nullptr,
