@@ -421,8 +421,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(each GPU would own a range of the weight's rows balanced by entries); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
