@@ -30,6 +30,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 WORKLOADS = {
     # name: (layer, batch, dtype)
     "target95_b64": ("target95", 64, "f32"),
+    "target95_b64_bf16": ("target95", 64, "bf16"),
     "target95_b1": ("target95", 1, "f32"),
     "llm90_b64": ("llm90", 64, "f32"),
     "llm90_b16": ("llm90", 16, "f32"),
