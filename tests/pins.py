@@ -345,6 +345,61 @@ def pin_topology_uniformity():
         assert chi2 < dof + 6.0 * math.sqrt(2 * dof), (chi2, dof)
 
 
+def _topology_bruteforce(O, I, rows, cols, vals, p, seed):
+    """Appendix G's prune step and Algorithm 2's regrowth written out in plain Python: drop the p
+    entries of smallest |w| (ties to the lower position in the sorted triple), then draw trials
+    from the pinned SplitMix64 stream -- the row from one output, the column from the next,
+    each as floor(u*n/2^64) -- and keep a pair only when it is not live; regrown values are +0.0.
+    Returns the sorted (row, col, value-bits) triple and the number of trials."""
+    nnz = len(rows)
+    mags = [abs(float(np.float32(v))) for v in vals]
+    order = sorted(range(nnz), key=lambda k: (mags[k], k))
+    gone = set(order[:p])
+    live = {}
+    for k in range(nnz):
+        if k not in gone:
+            live[(int(rows[k]), int(cols[k]))] = int(np.float32(vals[k]).view(np.uint32))
+    need = nnz - len(live)
+    u = iter(int(x) for x in oracle.splitmix64(seed, 2 * (50 * need + 1000)))
+    trials = 0
+    while len(live) < nnz:
+        r = (next(u) * O) >> 64
+        c = (next(u) * I) >> 64
+        trials += 1
+        if (r, c) in live:
+            continue
+        live[(r, c)] = 0
+    pos = sorted(live)
+    return ([q[0] for q in pos], [q[1] for q in pos], [live[q] for q in pos], trials)
+
+
+def pin_topology_bruteforce():
+    """The oracle's topology update equals the written-out prune-and-regrow exactly: rows, cols,
+    value bits and the trial count.  Cases: ties in |w| straddling the cut, a nearly full layer
+    (most draws rejected), one row, one column, zeros among the values, and nothing pruned."""
+    cases = []
+    L, v, p = _topology_case(71)
+    cases.append((L["out_features"], L["in_features"], L["rows"], L["cols"], v, p, 4321))
+    F = synth.random_small_layer(17, 12, 10, 115, "uniform")   # 115 of 120 cells live
+    cases.append((12, 10, F["rows"], F["cols"], F["vals"], 30, 99))
+    R = synth.random_small_layer(18, 1, 50, 30, "uniform")
+    cases.append((1, 50, R["rows"], R["cols"], R["vals"], 10, 7))
+    C = synth.random_small_layer(19, 40, 1, 25, "uniform")
+    cases.append((40, 1, C["rows"], C["cols"], C["vals"], 12, 8))
+    Z = synth.random_small_layer(20, 20, 20, 150, "uniform")
+    vz = Z["vals"].copy()
+    vz[::3] = np.float32(0.0)
+    vz[1::7] = np.float32(-0.0)
+    cases.append((20, 20, Z["rows"], Z["cols"], vz, 60, 31))
+    cases.append((20, 20, Z["rows"], Z["cols"], Z["vals"], 0, 32))
+    for O, I, rows, cols, vals, p, seed in cases:
+        out = oracle.topology(O, I, rows, cols, vals, p, seed=seed)
+        r, c, bits, trials = _topology_bruteforce(O, I, rows, cols, vals, p, seed)
+        assert out["rows"].tolist() == r and out["cols"].tolist() == c, (O, I, p, "positions")
+        assert out["vals"].view(np.uint32).tolist() == bits, (O, I, p, "value bits")
+        assert out["trials"] == trials, (O, I, p, out["trials"], trials)
+
+
 # ---------------------------------------------------------------- uniform initializer
 def _init_bruteforce(O, I, nnz, seed):
     """Algorithm 2 written out in Python over the pinned SplitMix64 outputs: each trial takes the
@@ -403,6 +458,6 @@ ALL_PINS = [
     pin_table7, pin_bruteforce, pin_scipy, pin_finite_differences, pin_adjoint,
     pin_special_cases, pin_thread_count_invariance, pin_builder_numpy, pin_builder_errors,
     pin_splitmix64, pin_topology_invariants, pin_topology_trials_expectation,
-    pin_topology_uniformity, pin_init_uniform_bruteforce, pin_init_uniform_trials_expectation,
+    pin_topology_uniformity, pin_topology_bruteforce, pin_init_uniform_bruteforce, pin_init_uniform_trials_expectation,
     pin_init_uniform_uniformity,
 ]

@@ -39,6 +39,8 @@ MUTANTS = [
     ("regrow_trials_miscount", "++trials;\n        if (live[i * I + j]) continue;", "if (live[i * I + j]) continue;\n        ++trials;"),
     ("regrow_swapped_ranges", "int64_t i = getrand(&state, O);\n        int64_t j = getrand(&state, I);",
      "int64_t i = getrand(&state, I) % O;\n        int64_t j = getrand(&state, O) % I;"),
+    ("regrow_column_first", "int64_t i = getrand(&state, O);\n        int64_t j = getrand(&state, I);",
+     "int64_t j = getrand(&state, I);\n        int64_t i = getrand(&state, O);"),
     ("init_column_first", "const int64_t row = getrand(&state, O);   /* row first, then column */\n        const int64_t col = getrand(&state, I);",
      "const int64_t col = getrand(&state, I);\n        const int64_t row = getrand(&state, O);"),
     ("init_no_rejection", "if (seen[row * I + col]) continue;         /* drawn before: reject */", ""),
