@@ -13,6 +13,7 @@ GPU" (arXiv:2610.04093): Algorithm 1 and Section 3.2 (forward SpMM), Section
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -95,13 +96,17 @@ _lib.snack_coo_block_offsets_count.argtypes = [_D, ctypes.c_int]
 _lib.snack_coo_block_offsets_count.restype = ctypes.c_int64
 _lib.snack_coo_block_offsets.argtypes = [_D, ctypes.c_int, _p, _p]
 _lib.snack_coo_bwd_is_fused.argtypes = [_D, _i64, ctypes.c_int]
+_lib.snack_coo_set_option.argtypes = [ctypes.c_int, _i64]
+_lib.snack_coo_get_option.argtypes = [ctypes.c_int]
+_lib.snack_coo_get_option.restype = _i64
 SNACK_VIEW_ROWS, SNACK_VIEW_COLS = 0, 1
 
 EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_bwd_input",
             "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_coo_init_uniform",
             "snack_coo_topology_update_device", "snack_coo_topology_workspace_bytes", "snack_last_error",
             "snack_coo_abi_version", "snack_coo_set_probe", "snack_coo_invert_perm", "snack_coo_gather_f32",
-            "snack_coo_block_offsets_count", "snack_coo_block_offsets", "snack_coo_bwd_is_fused")
+            "snack_coo_block_offsets_count", "snack_coo_block_offsets", "snack_coo_bwd_is_fused",
+            "snack_coo_set_option", "snack_coo_get_option")
 
 
 def _np_ptr(a: Optional[np.ndarray]):
@@ -475,3 +480,27 @@ def snack_coo_set_probe(start_event=None, stop_event=None):
 
 def abi_version() -> int:
     return int(_lib.snack_coo_abi_version())
+
+
+# Kernel-selection overrides (snack_coo_set_option): for tests and measurement only.
+OPT_TILE, OPT_BWD_FORM, OPT_BAND_MIN_NNZ, OPT_TOPOLOGY_DRAW_BATCH = 0, 1, 2, 3
+
+
+def set_option(opt: int, value: int) -> None:
+    """Process-wide override of a kernel choice (-1: the library's own)."""
+    _check(_lib.snack_coo_set_option(int(opt), int(value)), "snack_coo_set_option")
+
+
+def get_option(opt: int) -> int:
+    return int(_lib.snack_coo_get_option(int(opt)))
+
+
+@contextlib.contextmanager
+def option(opt: int, value: int):
+    """set_option for the duration of a with-block, then the previous value again."""
+    old = get_option(opt)
+    set_option(opt, value)
+    try:
+        yield
+    finally:
+        set_option(opt, old)

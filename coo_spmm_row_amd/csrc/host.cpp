@@ -12,6 +12,7 @@
 // (draw a row, draw a column, reject pairs already in the live set S).
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -81,7 +82,34 @@ using namespace snack;
 
 extern "C" const char *snack_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int snack_coo_abi_version(void) { return 6; }
+extern "C" int snack_coo_abi_version(void) { return 7; }
+
+namespace snack {
+namespace {
+constexpr int kNumOptions = 4;
+std::atomic<int64_t> g_options[kNumOptions] = {{-1}, {-1}, {-1}, {-1}};
+}  // namespace
+
+int64_t option(int which) {
+    return which >= 0 && which < kNumOptions ? g_options[which].load(std::memory_order_relaxed) : -1;
+}
+}  // namespace snack
+
+extern "C" int snack_coo_set_option(int opt, int64_t value) {
+    if (opt < 0 || opt >= kNumOptions) return fail(SNACK_ERR_DTYPE, "set_option: unknown option %d", opt);
+    bool okv = value == -1;
+    switch (opt) {
+        case SNACK_OPT_TILE: okv = okv || value == 0; break;
+        case SNACK_OPT_BWD_FORM: okv = okv || (value >= 0 && value <= 2); break;
+        case SNACK_OPT_BAND_MIN_NNZ: okv = okv || value >= 0; break;
+        case SNACK_OPT_TOPOLOGY_DRAW_BATCH: okv = okv || value >= 1; break;
+    }
+    if (!okv) return fail(SNACK_ERR_SHAPE, "set_option: value %lld out of range for option %d", (long long)value, opt);
+    g_options[opt].store(value, std::memory_order_relaxed);
+    return ok();
+}
+
+extern "C" int64_t snack_coo_get_option(int opt) { return option(opt); }
 
 extern "C" int snack_coo_build(int64_t O, int64_t I, int64_t nnz,
                                const int32_t *rows, const int32_t *cols, const float *vals,

@@ -11,4 +11,8 @@ int fail(int status, const char *fmt, ...);
 // Clears the calling thread's message and returns SNACK_OK.
 int ok();
 
+// Process-wide kernel-selection override set by snack_coo_set_option (SNACK_OPT_*); -1 means
+// the library's own choice.
+int64_t option(int which);
+
 }  // namespace snack

@@ -2229,6 +2229,7 @@ __global__ __launch_bounds__(kBlock) void bias_grad_kernel(int64_t O, int64_t B,
 
 // ================================================================ host side
 using snack::fail;
+using snack::option;
 
 thread_local hipEvent_t g_probe_start = nullptr;
 thread_local hipEvent_t g_probe_stop = nullptr;
@@ -2251,22 +2252,11 @@ enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2, kCsr1 = 3, kCsr1Priv = 
 constexpr int64_t kScatterLdsFloats = 16384;  // 64 KB private dX copy per workgroup
 
 // Device work plan of one gather-reduce (forward or input gradient).
-// Batch limits of the gather-reduce mappings (compile-time tuning knobs): the input gradient
-// scatters into LDS copies up to SNACK_SCATTER_MAX_B batch rows, and batches that are multiples
-// of 4 from SNACK_ROWWAVE_MIN_B on take the rowwave mapping.
-#ifndef SNACK_SCATTER_MAX_B
-#define SNACK_SCATTER_MAX_B 1
-#endif
-
-// 0: rowwave tiles of 4*BT columns; 1: one tile of 4*BT*Q columns (Q <= 4) where 4*BT does not
-// divide the batch; 2: such a tile wherever one exists.
-#ifndef SNACK_ROWWAVE_Q_MODE
-#define SNACK_ROWWAVE_Q_MODE 1
-#endif
-
-#ifndef SNACK_ROWWAVE_MIN_B
-#define SNACK_ROWWAVE_MIN_B 4
-#endif
+// Batch limits of the gather-reduce mappings: the input gradient scatters into LDS copies at
+// batch 1, and batches from 4 on take the rowwave mapping (tiles of 4*BT columns, or one tile of
+// 4*BT*Q columns, Q <= 4, where 4*BT does not divide the padded batch).
+constexpr int64_t kScatterMaxB = 1;
+constexpr int64_t kRowwaveMinB = 4;
 
 // layers from which the wide-batch gradient paths (column-order values for the input gradient,
 // 256-column slices for the weight gradient) pay off over the plain ones
@@ -2356,7 +2346,7 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
         p.total = at;
         return p;
     }
-    if (scatter_ok && B <= SNACK_SCATTER_MAX_B && B * nout <= kScatterLdsFloats && nnz > 0) {
+    if (scatter_ok && B <= kScatterMaxB && B * nout <= kScatterLdsFloats && nnz > 0) {
         p.mapping = kScatter;
         p.direct = true;  // reads dY in its batch-major layout
         p.nchunks = std::min<int64_t>(std::max<int64_t>(ceil_div(nnz, 4096), 1), 256);
@@ -2370,13 +2360,13 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
     }
     const int64_t Bp = pad_batch(B);
     p.bpad = B;
-    if (Bp >= SNACK_ROWWAVE_MIN_B && (opnd_rows + 1) * Bp * 4 < (int64_t(1) << 32)) {
+    if (Bp >= kRowwaveMinB && (opnd_rows + 1) * Bp * 4 < (int64_t(1) << 32)) {
         p.mapping = kRowwave;
         p.bpad = Bp;
         p.bt = 1;  // lanes per slot: the largest power of two <= min(16, Bp/4)
         while (p.bt * 2 <= std::min<int64_t>(16, Bp / 4)) p.bt *= 2;
         p.q = 1;
-        if (SNACK_ROWWAVE_Q_MODE == 2 || (SNACK_ROWWAVE_Q_MODE == 1 && Bp % (4 * p.bt) != 0)) {
+        if (Bp % (4 * p.bt) != 0) {
             // one exact tile of 4*BT*Q columns, Q <= 4 float4s per lane, where one exists
             for (int bt = 16; bt >= 1; bt /= 2) {
                 if (Bp % (4 * bt) == 0 && Bp / (4 * bt) <= 4) {
@@ -2419,16 +2409,21 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
 constexpr int64_t kTileMinNnz = int64_t(1) << 20;
 constexpr int64_t kTileMaxBatchTiles = 4;  // up to 256 batch columns
 
-int tile_env() {
-    const char *env = std::getenv("SNACK_COO_TILE");
-    return env && !std::strcmp(env, "0") ? 0 : -1;
-}
+int tile_env() { return option(SNACK_OPT_TILE) == 0 ? 0 : -1; }
 
 // Column blocks over n operand rows: ncb = ceil(n / kTileMaxCols) blocks of cw = ceil(n / ncb)
 // (the layout of snack_coo_desc.row_blocks / col_blocks; one block for n = 0).
 void tile_blocks(int64_t n, int64_t &ncb, int64_t &cw) {
     ncb = std::max<int64_t>(1, ceil_div(n, kTileMaxCols));
     cw = std::max<int64_t>(1, ceil_div(n, ncb));
+}
+
+// Keys per key range of the tiled walks: about 256 workgroups in all (one per CU at 64 columns,
+// two at 16 or 32), at most one key per thread of a 1024-thread workgroup.
+int tile_keys_per_range(int64_t nkeys, int64_t ncb, int tb) {
+    const int64_t per_cu = tb == 64 ? 1 : 2;
+    const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256 * per_cu, ncb));
+    return static_cast<int>(std::min<int64_t>(ceil_div(nkeys, nrb0), kTileWaves * kWave));
 }
 
 void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64_t B) {
@@ -2450,14 +2445,11 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     p.bpad = Bp;
     p.ttb = tb;
     p.tnnz = static_cast<int>(nnz);
-    // workgroups per CU: one at 64 columns (160 KB of LDS), two at 16 or 32 (the wave limit)
-    const int64_t per_cu = tb == 64 ? 1 : 2;
     const double need = mean + 4.0 * std::sqrt(mean) + 1.0;
     p.tch = need <= 32.0 ? 2 : (need <= 64.0 ? 4 : 8);
     p.tncb = static_cast<int>(ncb);
     p.tcw = static_cast<int>(cw);
-    const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256 * per_cu, ncb));
-    p.tkpr = static_cast<int>(std::min<int64_t>(ceil_div(nkeys, nrb0), kTileWaves * kWave));
+    p.tkpr = tile_keys_per_range(nkeys, ncb, tb);
     p.tnrb = static_cast<int>(ceil_div(nkeys, p.tkpr));
     p.tnbt = static_cast<int>(Bp / tb);
     size_t at = 0;
@@ -2597,8 +2589,7 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
             p.tch = need <= 32.0 ? 2 : (need <= 64.0 || tb == 64 ? 4 : 8);
             p.tncb = static_cast<int>(ncb);
             p.tcw = static_cast<int>(cw);
-            const int64_t nrb0 = std::max<int64_t>(1, ceil_div(256 * (tb == 64 ? 1 : 2), ncb));
-            p.tkpr = static_cast<int>(std::min<int64_t>(ceil_div(O, nrb0), kTileWaves * kWave));
+            p.tkpr = tile_keys_per_range(O, ncb, tb);
             p.tnrb = static_cast<int>(ceil_div(O, p.tkpr));
             p.tnbt = static_cast<int>(Bp / tb);
         }
@@ -2703,35 +2694,19 @@ struct BwdPlan {
 };
 
 // Smallest lane count per slot of the one-pass backward (1: batches 4, 8, 12 take it too).
-#ifndef SNACK_FUSED_MIN_BT
-#define SNACK_FUSED_MIN_BT 1
-#endif
+constexpr int kFusedMinBt = 1;
 
-#ifndef SNACK_BAND_MIN_NNZ
-#define SNACK_BAND_MIN_NNZ (int64_t(1) << 20)
-#endif
+// Layers with at least this many entries take the row-banded form of the fused backward pass
+// (SNACK_OPT_BAND_MIN_NNZ overrides it).  The backward's form where more than one applies is the
+// library's choice unless SNACK_OPT_BWD_FORM names one: 0 the one-pass kernel reading dY rows from
+// L2, 1 two tiled passes, 2 one tiled pass.
+constexpr int64_t kBandMinNnz = int64_t(1) << 20;
 
-// Layers with at least this many entries take the row-banded form of the fused backward pass;
-// the environment variable SNACK_COO_BAND_MIN_NNZ (a decimal count) overrides the default.
-// The backward's form where more than one applies: SNACK_COO_BWD_FORM = "fused" (the one-pass
-// kernel reading dY rows from L2), "split" (two tiled passes) or "tiled" (one tiled pass); unset:
-// the library's choice.
-int bwd_form_env() {
-    const char *env = std::getenv("SNACK_COO_BWD_FORM");
-    if (!env) return -1;
-    if (!std::strcmp(env, "fused")) return 0;
-    if (!std::strcmp(env, "split")) return 1;
-    if (!std::strcmp(env, "tiled")) return 2;
-    return -1;
-}
+int bwd_form_env() { return static_cast<int>(option(SNACK_OPT_BWD_FORM)); }
 
 int64_t band_min_nnz() {
-    if (const char *env = std::getenv("SNACK_COO_BAND_MIN_NNZ")) {
-        char *end = nullptr;
-        const long long v = std::strtoll(env, &end, 10);
-        if (end != env && *end == '\0' && v >= 0) return v;
-    }
-    return SNACK_BAND_MIN_NNZ;
+    const int64_t v = option(SNACK_OPT_BAND_MIN_NNZ);
+    return v >= 0 ? v : kBandMinNnz;
 }
 
 BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool aligned16, bool colvals = false) {
@@ -2741,7 +2716,7 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
     if (nnz > 0 && Bp >= 4 && (std::max(I, O) + 1) * Bp * 4 < (int64_t(1) << 32)) {
         // padded batch Bp = 4*BT*Q: BT lanes per slot (the largest power of two <= 16 that leaves
         // Q <= 4 float4s per lane)
-        for (int bt = 16; bt >= SNACK_FUSED_MIN_BT; bt /= 2) {
+        for (int bt = 16; bt >= kFusedMinBt; bt /= 2) {
             if (Bp % (4 * bt) == 0 && Bp / (4 * bt) <= 4) {
                 p.fused = true;
                 p.bt = bt;
@@ -3043,9 +3018,6 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
             SNACK_RW(1, 1) SNACK_RW(2, 1) SNACK_RW(4, 1) SNACK_RW(8, 1) SNACK_RW(16, 1)
             SNACK_RW(1, 3) SNACK_RW(2, 3) SNACK_RW(4, 3) SNACK_RW(8, 3) SNACK_RW(16, 3)
             SNACK_RW(16, 4)
-#if SNACK_ROWWAVE_Q_MODE == 2
-            SNACK_RW(16, 2)
-#endif
 #undef SNACK_RW
             default: return fail(SNACK_ERR_INTERNAL, "rowwave: unsupported plan bt=%d q=%d", p.bt, p.q);
         }
@@ -3500,12 +3472,10 @@ void launch_colbwd_nb(const BwdPlan &p, dim3 grid, hipStream_t st, int64_t I, co
         launch_colbwd_q<OutT, 8, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
     else if (p.bt == 4)
         launch_colbwd_q<OutT, 4, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
-#if SNACK_FUSED_MIN_BT < 4
     else if (p.bt == 2)
         launch_colbwd_q<OutT, 2, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
     else
         launch_colbwd_q<OutT, 1, NB, COLV>(p.q, grid, st, I, W, xt, dyt, zero_row, Bp, dX, dW, part, B);
-#endif
 }
 
 template <typename OutT>

@@ -218,10 +218,8 @@ double harmonic(double n) {
 // draws per batch: 1.25x the expected trial count (step i keeps a pair with probability
 // (C - S - i) / C for C cells and S survivors) plus slack, within the key's index bits
 int64_t draw_batch(int64_t O, int64_t I, int64_t nnz, int64_t n_prune) {
-    if (const char *env = std::getenv("SNACK_COO_TOPOLOGY_DRAW_BATCH")) {
-        const long long v = std::atoll(env);
-        if (v > 0) return std::min<int64_t>(v, (int64_t(1) << kDrawBits) - 1);
-    }
+    if (const int64_t v = option(SNACK_OPT_TOPOLOGY_DRAW_BATCH); v > 0)
+        return std::min<int64_t>(v, (int64_t(1) << kDrawBits) - 1);
     if (n_prune == 0) return 0;
     const double C = static_cast<double>(O) * static_cast<double>(I);
     const double free0 = C - static_cast<double>(nnz - n_prune);

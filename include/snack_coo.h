@@ -47,10 +47,8 @@
  *    and every kernel is deterministic except the batch-1 input gradient's
  *    LDS-atomic scatter.  Layers of at least 2^20 entries at batches padded to
  *    a multiple of 16 take LDS-tiled kernels (operand rows staged in LDS per
- *    column block, see row_blocks / col_blocks).  Environment overrides, read
- *    at every call (also by snack_coo_workspace_bytes): SNACK_COO_TILE=0 turns
- *    the tiled kernels off; SNACK_COO_BWD_FORM=fused|split|tiled picks the form
- *    of snack_coo_bwd where it applies; SNACK_COO_BAND_MIN_NNZ (below).
+ *    column block, see row_blocks / col_blocks).  For tests and measurement,
+ *    snack_coo_set_option overrides these choices process-wide (below).
  */
 #ifndef SNACK_COO_H
 #define SNACK_COO_H
@@ -216,9 +214,8 @@ int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY
  * 8 bands of about nnz/8 entries, each band's part of every column is walked on
  * its own, and the 8 partial dX are added in band order (deterministic; the
  * workspace then also holds 8*I*Bp floats, Bp the padded batch; values in
- * column order never take the banded form).  The environment variable
- * SNACK_COO_BAND_MIN_NNZ (a decimal entry count, read at every call of this
- * function and of snack_coo_workspace_bytes) overrides that threshold. */
+ * column order never take the banded form).  SNACK_OPT_BAND_MIN_NNZ
+ * (snack_coo_set_option) overrides that threshold. */
 int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch, int act_dtype,
                   void *dX, float *db, float *dW,
                   void *workspace, size_t workspace_bytes, void *hip_stream);
@@ -251,9 +248,9 @@ int snack_coo_topology_update_device(const snack_coo_desc *W, int64_t n_prune, u
                                      void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Bytes of device workspace snack_coo_topology_update_device needs (0 with
- * snack_last_error() set for invalid sizes).  The environment variable
- * SNACK_COO_TOPOLOGY_DRAW_BATCH (a positive count) fixes the number of draws per
- * batch, which is otherwise sized from the expected number of draws. */
+ * snack_last_error() set for invalid sizes).  SNACK_OPT_TOPOLOGY_DRAW_BATCH
+ * (snack_coo_set_option) fixes the number of draws per batch, which is
+ * otherwise sized from the expected number of draws. */
 size_t snack_coo_topology_workspace_bytes(int64_t out_features, int64_t in_features, int64_t nnz,
                                           int64_t n_prune);
 
@@ -316,9 +313,28 @@ int snack_coo_set_probe(void *start_event, void *stop_event);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *snack_last_error(void);
 
-/* ABI version of this header: 5 (3 added snack_coo_init_uniform, 4 the device topology update,
- * 5 values in column order: snack_coo_desc.row_to_col, snack_coo_invert_perm, snack_coo_gather_f32). */
+/* ABI version of this header: 7.  3 added snack_coo_init_uniform, 4 the device topology update,
+ * 5 values in column order (snack_coo_desc.row_to_col, snack_coo_invert_perm, snack_coo_gather_f32),
+ * 6 the segment tables (snack_coo_desc.row_blocks / col_blocks, snack_coo_block_offsets_count,
+ * snack_coo_block_offsets), 7 the kernel-selection options (snack_coo_set_option,
+ * snack_coo_get_option) in place of environment variables. */
 int snack_coo_abi_version(void);
+
+/* Kernel-selection overrides for tests and measurement (not part of the method).  Process-wide,
+ * read by every later call (snack_coo_workspace_bytes included); -1 restores the library's own
+ * choice.  They pick among kernels that compute the same products, so results agree to
+ * rounding whatever is set.
+ *   SNACK_OPT_TILE                 0: no LDS-tiled kernels
+ *   SNACK_OPT_BWD_FORM             form of snack_coo_bwd where more than one applies: 0 the one-pass
+ *                                  kernel reading dY rows from L2, 1 two tiled passes, 2 one tiled pass
+ *   SNACK_OPT_BAND_MIN_NNZ         entry count from which the one-pass backward runs in row bands
+ *                                  (default 2^20)
+ *   SNACK_OPT_TOPOLOGY_DRAW_BATCH  draws per batch of snack_coo_topology_update_device (>= 1)
+ * snack_coo_set_option returns SNACK_ERR_DTYPE for an unknown option and SNACK_ERR_SHAPE for a
+ * value out of range; snack_coo_get_option returns the current value (-1 for an unknown option). */
+enum { SNACK_OPT_TILE = 0, SNACK_OPT_BWD_FORM = 1, SNACK_OPT_BAND_MIN_NNZ = 2, SNACK_OPT_TOPOLOGY_DRAW_BATCH = 3 };
+int snack_coo_set_option(int option, int64_t value);
+int64_t snack_coo_get_option(int option);
 
 /* Segment tables of snack_coo_desc.row_blocks (view = SNACK_VIEW_ROWS) and
  * snack_coo_desc.col_blocks (view = SNACK_VIEW_COLS): the number of int32

@@ -16,7 +16,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     lib = ctypes.CDLL(snk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -24,7 +24,12 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert snk.abi_version() == 6
+    """The version the header documents is the one the library reports."""
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                            "snack_coo.h")).read()
+    m = re.search(r"ABI version of this header: (\d+)", hdr)
+    assert m, "header states no ABI version"
+    assert snk.abi_version() == int(m.group(1)) == 7
 
 
 def test_binding_loads_only_the_in_tree_library():
@@ -75,24 +80,37 @@ def test_one_hip_runtime_in_process():
     assert len(runtimes) == 1, runtimes
 
 
-def test_banded_backward_workspace_follows_threshold(monkeypatch):
-    """The row-banded backward needs 8*I*B more floats of workspace; SNACK_COO_BAND_MIN_NNZ moves the
+def test_banded_backward_workspace_follows_threshold():
+    """The row-banded backward needs 8*I*B more floats of workspace; SNACK_OPT_BAND_MIN_NNZ moves the
     entry count from which snack_coo_bwd (and its workspace size) takes that form."""
     lib = snk._lib
     d = snk._Desc()
     d.out_features, d.in_features, d.nnz = 300, 200, 5000
     d.row_offsets = d.rows = d.cols = d.vals = 0x1000  # host-side sizing only: never dereferenced
     d.col_perm = d.col_rows = d.col_cols = d.col_offsets = 0x1000
-    monkeypatch.setenv("SNACK_COO_BAND_MIN_NNZ", "1")
-    banded = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
-    monkeypatch.setenv("SNACK_COO_BAND_MIN_NNZ", str(1 << 62))
-    plain = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
-    monkeypatch.delenv("SNACK_COO_BAND_MIN_NNZ")
+    with snk.option(snk.OPT_BAND_MIN_NNZ, 1):
+        banded = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
+    with snk.option(snk.OPT_BAND_MIN_NNZ, 1 << 62):
+        plain = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
     default = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)  # 5000 < 2^20: not banded
     assert plain == default > 0
     assert banded - plain >= 8 * 200 * 64 * 4
-    monkeypatch.setenv("SNACK_COO_BAND_MIN_NNZ", "not a number")  # ignored
-    assert lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0) == default
+
+
+def test_options_validated_and_restored():
+    """snack_coo_set_option rejects unknown options and out-of-range values (the old value stays),
+    and -1 restores the library's own choice."""
+    lib = snk._lib
+    for opt in (snk.OPT_TILE, snk.OPT_BWD_FORM, snk.OPT_BAND_MIN_NNZ, snk.OPT_TOPOLOGY_DRAW_BATCH):
+        assert snk.get_option(opt) == -1
+    assert lib.snack_coo_set_option(9, 0) == 6 and lib.snack_coo_set_option(-1, 0) == 6  # SNACK_ERR_DTYPE
+    for opt, bad in ((snk.OPT_TILE, 1), (snk.OPT_BWD_FORM, 3), (snk.OPT_BAND_MIN_NNZ, -2),
+                     (snk.OPT_TOPOLOGY_DRAW_BATCH, 0)):
+        assert lib.snack_coo_set_option(opt, bad) == 2 and snk.get_option(opt) == -1  # SNACK_ERR_SHAPE
+    with snk.option(snk.OPT_BWD_FORM, 2):
+        assert snk.get_option(snk.OPT_BWD_FORM) == 2
+    assert snk.get_option(snk.OPT_BWD_FORM) == -1
+    assert lib.snack_coo_get_option(17) == -1
 
 
 
@@ -112,13 +130,10 @@ def test_column_order_values_host_checks_and_workspace():
     assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 64, 0) >= row_dw + 4 * 5000
     d.nnz = 1 << 21
     d.out_features = d.in_features = 4096
-    os.environ["SNACK_COO_BWD_FORM"] = "fused"  # the one-pass kernel that gathers dY from L2
-    try:
+    with snk.option(snk.OPT_BWD_FORM, 0):  # the one-pass kernel that gathers dY from L2
         col_bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)
         d.row_to_col = None
         row_bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, 0)  # 2^21 entries: banded
-    finally:
-        os.environ.pop("SNACK_COO_BWD_FORM", None)
     assert row_bwd - col_bwd >= 8 * 4096 * 64 * 4
     d.row_to_col = 0x1000
     ws = lib.snack_coo_topology_workspace_bytes(4096, 4096, 1 << 21, 10)
@@ -173,7 +188,7 @@ def test_backward_form_rules():
     """The documented choice of snack_coo_bwd's form (host-side planning, no GPU): two tiled passes
     for values in row order at one batch tile of 16, 32 or 64 columns on layers of >= 2^20 entries,
     two untiled passes at batch 1, one pass otherwise (the tiled pass for column order at 64
-    columns, the L2-gather kernel else); SNACK_COO_TILE=0 and SNACK_COO_BWD_FORM override."""
+    columns, the L2-gather kernel else); SNACK_OPT_TILE and SNACK_OPT_BWD_FORM override."""
     lib = snk._lib
     d = snk._Desc()
     d.out_features, d.in_features, d.nnz = 10000, 10000, 5_000_000
@@ -188,10 +203,7 @@ def test_backward_form_rules():
     d.nnz = 1_000_000  # below 2^20 entries: never tiled
     assert fused(64) == 1
     d.nnz = 5_000_000
-    for env, want in ((("SNACK_COO_TILE", "0"), 1), (("SNACK_COO_BWD_FORM", "fused"), 1),
-                      (("SNACK_COO_BWD_FORM", "tiled"), 1), (("SNACK_COO_BWD_FORM", "split"), 0)):
-        os.environ[env[0]] = env[1]
-        try:
-            assert fused(64) == want, env
-        finally:
-            os.environ.pop(env[0], None)
+    for (opt, val), want in (((snk.OPT_TILE, 0), 1), ((snk.OPT_BWD_FORM, 0), 1), ((snk.OPT_BWD_FORM, 2), 1),
+                             ((snk.OPT_BWD_FORM, 1), 0)):
+        with snk.option(opt, val):
+            assert fused(64) == want, (opt, val)

@@ -7,7 +7,7 @@ at multiples of 64) whose (key, column block) segments average at least 8 entrie
 cover: several column blocks with a narrower last one, one block, every tile width, batches that
 need zero padding (50, 100) and several batch tiles (48, 96, 128, 192, 256), empty rows and
 bias-only outputs, rows and columns longer than the prefetched chunks (the full lines of
-'dense_lines'), bf16 activations, and the walks off (SNACK_COO_TILE=0) giving the same results
+'dense_lines'), bf16 activations, and the walks off (SNACK_OPT_TILE = 0) giving the same results
 within tolerance.
 """
 import contextlib
@@ -31,21 +31,9 @@ import coo_spmm_row_amd as snk  # noqa: E402
 DEV = torch.device("cuda:0")
 
 
-@contextlib.contextmanager
 def tile_mode(v):
-    """SNACK_COO_TILE: '0' off, None the library default (on)."""
-    old = os.environ.get("SNACK_COO_TILE")
-    if v is None:
-        os.environ.pop("SNACK_COO_TILE", None)
-    else:
-        os.environ["SNACK_COO_TILE"] = v
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("SNACK_COO_TILE", None)
-        else:
-            os.environ["SNACK_COO_TILE"] = old
+    """The tiled kernels: '0' off (SNACK_OPT_TILE = 0), None the library default (on)."""
+    return snk.option(snk.OPT_TILE, -1 if v is None else int(v))
 
 
 @pytest.fixture(scope="module")
@@ -263,21 +251,9 @@ def test_tiled_dw_matches_untiled(layers):
     check_close(a.cpu().numpy(), b.cpu().numpy(), 64, "tiled vs rowsddmm dW")
 
 
-@contextlib.contextmanager
 def bwd_form(v):
-    """SNACK_COO_BWD_FORM: 'fused', 'split', 'tiled', or None for the library's choice."""
-    old = os.environ.get("SNACK_COO_BWD_FORM")
-    if v is None:
-        os.environ.pop("SNACK_COO_BWD_FORM", None)
-    else:
-        os.environ["SNACK_COO_BWD_FORM"] = v
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("SNACK_COO_BWD_FORM", None)
-        else:
-            os.environ["SNACK_COO_BWD_FORM"] = old
+    """snack_coo_bwd's form (SNACK_OPT_BWD_FORM): 'fused', 'split', 'tiled', or None for the library's choice."""
+    return snk.option(snk.OPT_BWD_FORM, {None: -1, "fused": 0, "split": 1, "tiled": 2}[v])
 
 
 @pytest.mark.parametrize("form", [None, "fused", "split", "tiled"])

@@ -57,14 +57,14 @@ def test_device_topology_matches_oracle(seed, O, I, nnz, frac):
         _check(O, I, L["rows"], L["cols"], v, p, s)
 
 
-def test_device_topology_many_draw_batches(monkeypatch):
+def test_device_topology_many_draw_batches():
     """Batches of 64 draws: the regrowth spans many batches, each marking its cells live."""
     say("device topology, 64 draws per batch")
-    monkeypatch.setenv("SNACK_COO_TOPOLOGY_DRAW_BATCH", "64")
-    L = synth.random_small_layer(21, 200, 150, 9000, "uniform")
-    _check(200, 150, L["rows"], L["cols"], L["vals"], 2000, 1234)
-    L = synth.random_small_layer(22, 32, 32, 1000, "uniform")  # nearly full: most draws rejected
-    _check(32, 32, L["rows"], L["cols"], L["vals"], 500, 99)
+    with snk.option(snk.OPT_TOPOLOGY_DRAW_BATCH, 64):
+        L = synth.random_small_layer(21, 200, 150, 9000, "uniform")
+        _check(200, 150, L["rows"], L["cols"], L["vals"], 2000, 1234)
+        L = synth.random_small_layer(22, 32, 32, 1000, "uniform")  # nearly full: most draws rejected
+        _check(32, 32, L["rows"], L["cols"], L["vals"], 500, 99)
 
 
 @pytest.mark.parametrize("name", ["gpt2_qkv", "gpt2_fc", "gpt2_proj"])
