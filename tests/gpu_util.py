@@ -20,22 +20,11 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-@contextlib.contextmanager
 def band_threshold(nnz_min: int | None):
-    """Run with SNACK_COO_BAND_MIN_NNZ set (the entry count from which snack_coo_bwd takes its
-    row-banded form), or with the library default when nnz_min is None."""
-    old = os.environ.get("SNACK_COO_BAND_MIN_NNZ")
-    if nnz_min is None:
-        os.environ.pop("SNACK_COO_BAND_MIN_NNZ", None)
-    else:
-        os.environ["SNACK_COO_BAND_MIN_NNZ"] = str(int(nnz_min))
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("SNACK_COO_BAND_MIN_NNZ", None)
-        else:
-            os.environ["SNACK_COO_BAND_MIN_NNZ"] = old
+    """Run with the entry count from which snack_coo_bwd takes its row-banded form set to nnz_min
+    (SNACK_OPT_BAND_MIN_NNZ), or the library default when nnz_min is None."""
+    import coo_spmm_row_amd as snk
+    return snk.option(snk.OPT_BAND_MIN_NNZ, -1 if nnz_min is None else int(nnz_min))
 
 
 # banded for every layer / never banded
@@ -75,10 +64,22 @@ def named_layer(name: str):
     return spec, L
 
 
+BUILD_KEYS = ("rows", "cols", "perm", "row_offsets", "col_perm", "col_rows", "col_cols", "col_offsets")
+
+
 def device_layer(L, device):
+    """The layer on the device through the library's builder, and the oracle's own build of the
+    same input (comparison sort, Appendix B / Table 7) for every reference computation.  The two
+    builds must agree bit for bit, so no reference value depends on the library's builder."""
     import coo_spmm_row_amd as snk
-    built = snk.snack_coo_build(L["out_features"], L["in_features"], L["rows"], L["cols"], L["vals"])
-    return built, snk.SnackCOO.from_built(built, device)
+    O, I = L["out_features"], L["in_features"]
+    built = snk.snack_coo_build(O, I, L["rows"], L["cols"], L["vals"])
+    ref = oracle.build_coo(O, I, L["rows"], L["cols"], L["vals"])
+    for k in BUILD_KEYS:
+        assert np.array_equal(built[k], ref[k]), f"library builder differs from the oracle's: {k}"
+    assert np.array_equal(built["vals"].view(np.uint32), ref["vals"].view(np.uint32)), "builder vals"
+    ref["out_features"], ref["in_features"], ref["nnz"] = O, I, int(ref["rows"].size)
+    return ref, snk.SnackCOO.from_built(built, device)
 
 
 def acts(seed, B, F, bf16=False):
@@ -102,32 +103,3 @@ def from_device(t):
         bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
         return synth.bf16_bits_to_f32(bits)
     return t.cpu().numpy()
-
-
-# ---------------------------------------------------------------- oracle on samples
-def oracle_fwd_rows(built, X, bias, rows_sel):
-    """Oracle forward restricted to the output rows rows_sel (all their entries)."""
-    off = built["row_offsets"]
-    ks = np.concatenate([np.arange(off[r], off[r + 1]) for r in rows_sel]) if len(rows_sel) else np.zeros(0, int)
-    remap = np.full(built["out_features"], -1, np.int64)
-    remap[rows_sel] = np.arange(len(rows_sel))
-    r = remap[built["rows"][ks]]
-    b = None if bias is None else bias[rows_sel]
-    return oracle.fwd(len(rows_sel), built["in_features"], r, built["cols"][ks], built["vals"][ks], X, b,
-                      nthreads=NTHREADS)
-
-
-def oracle_dx_cols(built, dY, cols_sel):
-    """Oracle input gradient restricted to the input columns cols_sel."""
-    mask = np.zeros(built["in_features"], bool)
-    mask[cols_sel] = True
-    ks = np.flatnonzero(mask[built["cols"]])
-    remap = np.full(built["in_features"], -1, np.int64)
-    remap[cols_sel] = np.arange(len(cols_sel))
-    return oracle.bwd_input(built["out_features"], len(cols_sel), built["rows"][ks], remap[built["cols"][ks]],
-                            built["vals"][ks], dY, nthreads=NTHREADS)
-
-
-def oracle_dw_entries(built, X, dY, ks):
-    return oracle.grad_weight(built["out_features"], built["in_features"], built["rows"][ks], built["cols"][ks],
-                              X, dY, nthreads=NTHREADS)

@@ -68,3 +68,13 @@ def test_builder_errors(args, status):
     # the oracle rejects the same inputs
     with pytest.raises(oracle.OracleError):
         oracle.build_coo(*args)
+
+
+@pytest.mark.parametrize("name", ["target95", "llm90"])
+def test_builder_matches_oracle_full_size_shuffled(name):
+    """The 10000 x 10000 layers at 95 % (5M entries) and 90 % (10M entries), fed in a shuffled
+    order: the library's counting sorts and the oracle's comparison sort agree bit for bit."""
+    L = synth.make_layer(synth.LAYERS[name])
+    rng = np.random.Generator(np.random.PCG64(17))
+    p = rng.permutation(L["nnz"])
+    _compare(L["out_features"], L["in_features"], L["rows"][p], L["cols"][p], L["vals"][p])

@@ -7,7 +7,7 @@ import pytest
 import oracle
 import synth
 from gpu_util import (BANDINGS, NTHREADS, acts, band_threshold, check_close, device_layer, from_device, named_layer,
-                      oracle_dw_entries, oracle_dx_cols, oracle_fwd_rows, say, to_device)
+                      say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,54 +164,32 @@ def test_gpt2_shapes(name, bf16):
     run_all(L, 1024, 5010, bf16=bf16)
 
 
-def _sampled(name, B, seed, n_rows=64, n_cols=64, n_entries=4096):
+def _full_with_adjoint(name, B, seed):
+    """Every output of the layer compared element by element with the oracle (run_all), then the
+    adjoint identity <dY, Y - b> = <dX, X> = <dW, vals> on the full outputs in fp64."""
     spec, L = named_layer(name)
     O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
-    built, W = device_layer(L, DEV)
+    built, W, X, dYt, Y, dX, dW = run_all(L, B, seed)
     x, _ = acts(seed, B, I)
     dy, _ = acts(seed + 1, B, O)
-    X, dYt = to_device(x, DEV), to_device(dy, DEV)
-    b = torch.from_numpy(L["bias"]).to(DEV)
-    Y = snk.snack_coo_fwd(W, X, b).cpu().numpy()
-    dX = snk.snack_coo_bwd_input(W, dYt).cpu().numpy()
-    dW = snk.snack_coo_grad_weight(W, X, dYt).cpu().numpy()
-    rng = np.random.Generator(np.random.PCG64(seed))
-    rs = np.sort(rng.choice(O, n_rows, replace=False))
-    cs = np.sort(rng.choice(I, n_cols, replace=False))
-    ks = np.sort(rng.choice(nnz, n_entries, replace=False))
-    ks = np.unique(np.concatenate([ks, [0, nnz - 1]]))
-    dX2, dW2 = (t.cpu().numpy() for t in snk.snack_coo_bwd(W, X, dYt))  # both from one call
-    check_close(Y[:, rs], oracle_fwd_rows(built, x, L["bias"], rs), nnz / O, f"{name} fwd sample")
-    ref_dx, ref_dw = oracle_dx_cols(built, dy, cs), oracle_dw_entries(built, x, dy, ks)
-    check_close(dX[:, cs], ref_dx, nnz / I, f"{name} dX sample")
-    check_close(dW[ks], ref_dw, B, f"{name} dW sample")
-    check_close(dX2[:, cs], ref_dx, nnz / I, f"{name} bwd dX sample")
-    check_close(dW2[ks], ref_dw, B, f"{name} bwd dW sample")
-    # whole-output property at full size: the adjoint identity in fp64
-    Yb = Y.astype(np.float64) - L["bias"].astype(np.float64)
+    Yb = Y.cpu().numpy().astype(np.float64) - L["bias"].astype(np.float64)
     a = float(np.sum(dy.astype(np.float64) * Yb))
-    c = float(np.sum(dX.astype(np.float64) * x.astype(np.float64)))
-    d = float(np.dot(dW.astype(np.float64), built["vals"].astype(np.float64)))
+    c = float(np.sum(dX.cpu().numpy().astype(np.float64) * x.astype(np.float64)))
+    d = float(np.dot(dW.cpu().numpy().astype(np.float64), built["vals"].astype(np.float64)))
     scale = math.sqrt(B * O) * math.sqrt(nnz) * 1e-5 + 1e-3
     assert abs(a - c) <= scale and abs(a - d) <= scale, (a, c, d)
 
 
 @pytest.mark.parametrize("B", [1, 16, 64])
-def test_llm_scale_sampled(B):
-    say(f"llm90 10k 90% B={B} sampled")
-    _sampled("llm90", B, 3010 + B)
+def test_llm_scale_full_compare(B):
+    say(f"llm90 10k 90% (10M entries) B={B} full compare")
+    _full_with_adjoint("llm90", B, 3010 + B)
 
 
 @pytest.mark.parametrize("B", [1, 64])
-def test_target_layer_sampled(B):
-    say(f"target95 10k 95% B={B} sampled")
-    _sampled("target95", B, 3510 + B)
-
-
-def test_target_layer_full_compare_b64():
-    say("target95 B=64 full compare")
-    spec, L = named_layer("target95")
-    run_all(L, 64, 3600)
+def test_target_layer_full_compare(B):
+    say(f"target95 10k 95% B={B} full compare")
+    _full_with_adjoint("target95", B, 3510 + B)
 
 
 # ------------------------------------------------------------ invariants
