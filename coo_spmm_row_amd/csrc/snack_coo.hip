@@ -511,12 +511,14 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
 // with value 0.
 constexpr int kTileThreads = 1024;
 constexpr int kTileWaves = kTileThreads / kWave;
-constexpr int kTileLdsRows = 640;                     // 160 KB of LDS at 64 columns
+constexpr int kTileLdsRows = 639;                     // staged rows: 159.75 KB of LDS at 64 columns
 constexpr int kTileMaxCols = kTileLdsRows - 1;        // operand rows per block (one more is the zero row)
+constexpr int kTileClaimBytes = 16;                   // after the staged rows: the workgroup's group counter
 
 // Raw buffer resource over n 4-byte elements: loads through it take a 32-bit byte offset (the
 // chunk offsets fold into the instruction's immediate), and loads past the end return 0 instead of
-// touching memory.  Word 3 is the gfx9 raw-buffer format.
+// touching memory.  Word 3 is the gfx9 raw-buffer format.  Callers keep n < 2^29, so byte offsets
+// of elements stay below 2^31 and below kBufPast.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int n) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), n * 4, 0x00020000);
 }
@@ -559,16 +561,20 @@ __device__ __forceinline__ float vget(const float4 &v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// Four steps T0..T0+3 of one chunk: the four LDS reads first, then the FMAs.
+// The LDS reads of steps T0..T0+3 of one chunk (entry T0+u's staged row, this lane's VW columns).
 template <int VW, int T0>
-__device__ __forceinline__ void tile_steps4(float (&acc)[VW], uint32_t off, float v, uint32_t lane_off,
+__device__ __forceinline__ void tile_reads4(typename TileVec<VW>::T (&x)[4], uint32_t off, uint32_t lane_off,
                                             const char *lds) {
     typedef typename TileVec<VW>::T V;
-    V x[4];
     x[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) + lane_off));
     x[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
     x[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
     x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+}
+
+// The FMAs of steps T0..T0+3: acc += (value of entry T0+u) * row.
+template <int VW, int T0>
+__device__ __forceinline__ void tile_fmas4(float (&acc)[VW], float v, const typename TileVec<VW>::T (&x)[4]) {
 #pragma unroll
     for (int i = 0; i < VW; ++i) {
         fmac_bcast16<T0 + 0, T0 == 0>(acc[i], v, vget(x[0], i));
@@ -578,14 +584,26 @@ __device__ __forceinline__ void tile_steps4(float (&acc)[VW], uint32_t off, floa
     }
 }
 
-// One chunk of 16 entries, nst (uniform, 1..16) of them real for the longest slot.
+// One chunk of 16 entries, nst (uniform, 1..16) of them real for the longest slot.  The reads of
+// each group of four steps are issued before the FMAs of the group before it, so a wave has a
+// group's LDS reads in flight while it computes.
 template <int VW>
 __device__ __forceinline__ void tile_chunk(float (&acc)[VW], uint32_t off, float v, int nst, uint32_t lane_off,
                                            const char *lds) {
-    tile_steps4<VW, 0>(acc, off, v, lane_off, lds);
-    if (nst > 4) tile_steps4<VW, 4>(acc, off, v, lane_off, lds);
-    if (nst > 8) tile_steps4<VW, 8>(acc, off, v, lane_off, lds);
-    if (nst > 12) tile_steps4<VW, 12>(acc, off, v, lane_off, lds);
+    typedef typename TileVec<VW>::T V;
+    V a[4], b[4];
+    tile_reads4<VW, 0>(a, off, lane_off, lds);
+    if (nst > 4) tile_reads4<VW, 4>(b, off, lane_off, lds);
+    tile_fmas4<VW, 0>(acc, v, a);
+    if (nst > 4) {
+        if (nst > 8) tile_reads4<VW, 8>(a, off, lane_off, lds);
+        tile_fmas4<VW, 4>(acc, v, b);
+        if (nst > 8) {
+            if (nst > 12) tile_reads4<VW, 12>(b, off, lane_off, lds);
+            tile_fmas4<VW, 8>(acc, v, a);
+            if (nst > 12) tile_fmas4<VW, 12>(acc, v, b);
+        }
+    }
 }
 
 // tab[key][j] = first entry of the key at or past gather index j*cw (j = 0..ncb): the segment of
@@ -631,25 +649,15 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
     const int bt = blockIdx.y;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int j = lane & 15;                    // entry of a chunk held by this lane
     const int slot = lane >> 4;                 // the row of 16 lanes is the slot
     const int ls = lane & 15;                   // lane within the slot: batch columns [ls*VW, ls*VW + VW)
     const uint32_t lane_off = static_cast<uint32_t>(ls * VW * 4);
     const uint32_t zoff = static_cast<uint32_t>(cw) * kRowBytes;
     const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
-    // group g of this wave: keys k_lo + (wave + kTileWaves * g) * SL + slot; keys_per_rb <= 1024
-    // keeps a wave's keys within 64, so lane g*SL + s holds the segment of group g's slot s
+    // group G = keys k_lo + SL*G .. +SL-1, slot s taking key k_lo + SL*G + s
     const int ngroups = (k_hi - k_lo + SL - 1) / SL;
-    const int my_groups = wave < ngroups ? (ngroups - wave + kTileWaves - 1) / kTileWaves : 0;
-    const int key_l = k_lo + (wave + kTileWaves * (lane / SL)) * SL + lane % SL;
-    const bool key_l_ok = lane / SL < my_groups && key_l < k_hi;
-    int seg_a, seg_e;  // issued before the staging loads, used after them
-    {
-        const int64_t at = static_cast<int64_t>(key_l_ok ? key_l : k_lo) * (ncb + 1) + cb;
-        seg_a = tab[at];
-        seg_e = tab[at + 1];
-    }
+    unsigned *claims = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(xs4) + (cw + 1) * kRowBytes);
     {  // stage the block's operand rows; rows cn..cw are zero (row cw is the zero row)
         constexpr int R4 = TB / 4;  // float4s per staged row
         constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
@@ -668,21 +676,30 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
             if (i < n4) xs4[i] = tmp[it];
         }
     }
-    // lane l holds the segment and key of the wave's key l (group l / SL, slot l % SL)
-    const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : -1;
+    if (threadIdx.x == 0) *claims = 0u;
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(xs4);
     float *pout = part + (static_cast<int64_t>(bt) * ncb + cb) * static_cast<int64_t>(nkeys) * TB;
-    // Chunks are loaded two groups ahead of the compute (three buffers in rotation).  Loads are
-    // issued unconditionally through buffer resources (entries past a segment read its neighbours,
-    // or 0 past the arrays' end) and masked where they are used.
-    // vv: the values (VP: the permuted positions, turned into values by load_vals)
+    // The waves take groups from the workgroup's counter as they go, so they all work until the
+    // tile is done.  A group's segments come from the table when it is claimed (D - 1 groups ahead
+    // of its compute), its chunks of gather indices and values one group later (VP: the permuted
+    // positions, then the values they point at one group before the compute).  Chunk loads go
+    // through buffer resources: lanes past a segment load from past the buffers' end, so nothing
+    // is read for them.
     const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
-    // Lanes past the segment (len) load from past the buffers' end: nothing is read for them.
-    auto load_chunks = [&](int g, int (&gi)[CH], int (&vv)[CH], int &len) {
-        const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
-        const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-        len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+    const __amdgpu_buffer_rsrc_t rt = buf_rsrc(tab, nkeys * (ncb + 1));
+    auto claim = [&]() {
+        unsigned g = 0;
+        if (lane == 0) g = atomicAdd(claims, 1u);
+        return static_cast<int>(__builtin_amdgcn_readfirstlane(g));
+    };
+    auto seg = [&](int G, int &a, int &len) {  // this slot's segment of group G (none past the tile)
+        const int key = k_lo + SL * G + slot;
+        const int off = G < ngroups && key < k_hi ? (key * (ncb + 1) + cb) * 4 : kBufPast;
+        a = buf_ld(rt, off);
+        len = buf_ld(rt, off == kBufPast ? kBufPast : off + 4) - a;
+    };
+    auto load_chunks = [&](int a, int len, int (&gi)[CH], int (&vv)[CH]) {
         const int base = (a + j) * 4;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
@@ -699,11 +716,8 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         return max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
                    max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
     };
-    auto compute = [&](int g, const int (&gi)[CH], const int (&vv)[CH]) {
-        const int src = (g * SL + slot) * 4;
-        const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-        const int len = __builtin_amdgcn_ds_bpermute(src, s_len);
-        const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
+    auto compute = [&](int G, int a, int len, const int (&gi)[CH], const int (&vv)[CH]) {
+        const int key = k_lo + SL * G + slot;
         const int m = group_len(len);
         float acc[VW];
 #pragma unroll
@@ -729,7 +743,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         // use, refilling them would wait for loads issued after them
 #pragma unroll
         for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]));
-        if (key >= 0) {
+        if (key < k_hi) {
             typedef typename TileVec<VW>::T V;
             V r;
             if constexpr (VW == 1) r = acc[0];
@@ -738,39 +752,48 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
             *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * TB + ls * VW) = r;
         }
     };
-    int gi0[CH], gi1[CH], gi2[CH];
-    int vv0[CH], vv1[CH], vv2[CH];
-    int n0 = 0, n1 = 0, n2 = 0;
-    if constexpr (!VP) {
-        load_chunks(0, gi0, vv0, n0);
-        load_chunks(1, gi1, vv1, n1);
-        for (int g = 0; g < my_groups; g += 3) {
-            load_chunks(g + 2, gi2, vv2, n2);
-            compute(g, gi0, vv0);
-            if (g + 1 >= my_groups) break;
-            load_chunks(g + 3, gi0, vv0, n0);
-            compute(g + 1, gi1, vv1);
-            if (g + 2 >= my_groups) break;
-            load_chunks(g + 4, gi1, vv1, n1);
-            compute(g + 2, gi2, vv2);
-        }
+    // ring of claimed groups: [0] computed now, [1] next, ..., [D-1] claimed this phase
+    constexpr int D = VP ? 4 : 3;
+    int Gs[D], As[D], Ls[D];
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) {
+        Gs[i] = claim();
+        seg(Gs[i], As[i], Ls[i]);
+    }
+    int gA[CH], gB[CH], gC[CH], pA[CH], pB[CH], pC[CH], vA[CH], vB[CH], vC[CH];
+    if constexpr (VP) {
+        load_chunks(As[0], Ls[0], gA, pA);
+        load_chunks(As[1], Ls[1], gB, pB);
+        load_vals(pA, Ls[0], vA);
     } else {
-        int pm0[CH], pm1[CH], pm2[CH];
-        load_chunks(0, gi0, pm0, n0);
-        load_chunks(1, gi1, pm1, n1);
-        load_vals(pm0, n0, vv0);
-        for (int g = 0; g < my_groups; g += 3) {
-            load_chunks(g + 2, gi2, pm2, n2);
-            load_vals(pm1, n1, vv1);
-            compute(g, gi0, vv0);
-            if (g + 1 >= my_groups) break;
-            load_chunks(g + 3, gi0, pm0, n0);
-            load_vals(pm2, n2, vv2);
-            compute(g + 1, gi1, vv1);
-            if (g + 2 >= my_groups) break;
-            load_chunks(g + 4, gi1, pm1, n1);
-            load_vals(pm0, n0, vv0);
-            compute(g + 2, gi2, vv2);
+        load_chunks(As[0], Ls[0], gA, vA);
+    }
+    // one phase: claim a group, issue the loads of the groups ahead, compute group [0]; buffers
+    // c (group [0]), n (group [1]), nn (group [2])
+    auto phase = [&](int (&gc)[CH], int (&vc)[CH], int (&gn)[CH], int (&pn)[CH], int (&vn)[CH],
+                     int (&gnn)[CH], int (&pnn)[CH]) {
+        Gs[D - 1] = claim();
+        seg(Gs[D - 1], As[D - 1], Ls[D - 1]);
+        if constexpr (VP) {
+            load_chunks(As[2], Ls[2], gnn, pnn);
+            load_vals(pn, Ls[1], vn);
+        } else {
+            load_chunks(As[1], Ls[1], gn, vn);
+        }
+        compute(Gs[0], As[0], Ls[0], gc, vc);
+#pragma unroll
+        for (int i = 0; i + 1 < D; ++i) {
+            Gs[i] = Gs[i + 1];
+            As[i] = As[i + 1];
+            Ls[i] = Ls[i + 1];
+        }
+        return Gs[0] < ngroups;
+    };
+    if (Gs[0] < ngroups) {
+        for (;;) {
+            if (!phase(gA, vA, gB, pB, vB, gC, pC)) break;
+            if (!phase(gB, vB, gC, pC, vC, gA, pA)) break;
+            if (!phase(gC, vC, gA, pA, vA, gB, pB)) break;
         }
     }
 }
@@ -783,21 +806,40 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
 // order (16 consecutive entries per slot).  Each lane holds VW columns of a TB = 16 VW column batch
 // tile (float4 at 64 columns); batch tiles are taken in turn (the block staged again), and tiles
 // after the first add into dW; each entry belongs to one workgroup.
+// Dot products of steps T0..T0+3: p[T0+u] = this lane's VW columns of entry T0+u's staged row
+// times its VW columns of the slot's dY row.
 template <int VW, int T0>
-__device__ __forceinline__ void tile_dot4(float (&p)[16], uint32_t off, uint32_t lane_off, const char *lds,
-                                          const typename TileVec<VW>::T &dy) {
-    typedef typename TileVec<VW>::T V;
-    V x[4];
-    x[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) + lane_off));
-    x[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
-    x[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
-    x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+__device__ __forceinline__ void tile_dots4(float (&p)[16], const typename TileVec<VW>::T (&x)[4],
+                                           const typename TileVec<VW>::T &dy) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         float d = vget(x[u], 0) * vget(dy, 0);
 #pragma unroll
         for (int i = 1; i < VW; ++i) d = fmaf(vget(x[u], i), vget(dy, i), d);
         p[T0 + u] = d;
+    }
+}
+
+// The 16 (or nst) dot products of one chunk, four steps at a time (its 16 products and the slot's
+// dY slice leave no room for a second group of reads in flight).
+template <int VW>
+__device__ __forceinline__ void tile_dot_chunk(float (&p)[16], uint32_t off, int nst, uint32_t lane_off,
+                                               const char *lds, const typename TileVec<VW>::T &dy) {
+    typedef typename TileVec<VW>::T V;
+    V a[4];
+    tile_reads4<VW, 0>(a, off, lane_off, lds);
+    tile_dots4<VW, 0>(p, a, dy);
+    if (nst > 4) {
+        tile_reads4<VW, 4>(a, off, lane_off, lds);
+        tile_dots4<VW, 4>(p, a, dy);
+    }
+    if (nst > 8) {
+        tile_reads4<VW, 8>(a, off, lane_off, lds);
+        tile_dots4<VW, 8>(p, a, dy);
+    }
+    if (nst > 12) {
+        tile_reads4<VW, 12>(a, off, lane_off, lds);
+        tile_dots4<VW, 12>(p, a, dy);
     }
 }
 
@@ -816,25 +858,30 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
     const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int j = lane & 15;
     const int slot = lane >> 4;
     const uint32_t lane_off = static_cast<uint32_t>(j * VW * 4);
     const uint32_t zoff = static_cast<uint32_t>(cw) * kRowBytes;
     const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
+    // group G = rows k_lo + SL*G .. +SL-1, taken from the workgroup's counter as in tile_spmm_kernel
     const int ngroups = (k_hi - k_lo + SL - 1) / SL;
-    const int my_groups = wave < ngroups ? (ngroups - wave + kTileWaves - 1) / kTileWaves : 0;
-    const int key_l = k_lo + (wave + kTileWaves * (lane / SL)) * SL + lane % SL;
-    const bool key_l_ok = lane / SL < my_groups && key_l < k_hi;
-    int seg_a, seg_e;
-    {
-        const int64_t at = static_cast<int64_t>(key_l_ok ? key_l : k_lo) * (ncb + 1) + cb;
-        seg_a = tab[at];
-        seg_e = tab[at + 1];
-    }
+    unsigned *claims = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(xs4) + (cw + 1) * kRowBytes);
     const char *lds = reinterpret_cast<const char *>(xs4);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz);
+    const __amdgpu_buffer_rsrc_t rt = buf_rsrc(tab, nkeys * (ncb + 1));
+    auto claim = [&]() {
+        unsigned g = 0;
+        if (lane == 0) g = atomicAdd(claims, 1u);
+        return static_cast<int>(__builtin_amdgcn_readfirstlane(g));
+    };
+    auto seg = [&](int G, int &a, int &len) {  // this slot's segment of group G (none past the tile)
+        const int key = k_lo + SL * G + slot;
+        const int off = G < ngroups && key < k_hi ? (key * (ncb + 1) + cb) * 4 : kBufPast;
+        a = buf_ld(rt, off);
+        len = buf_ld(rt, off == kBufPast ? kBufPast : off + 4) - a;
+    };
     for (int bt = 0; bt < nbt; ++bt) {
-        if (bt > 0) __syncthreads();  // the previous batch tile's reads of the block are done
+        if (bt > 0) __syncthreads();  // the previous batch tile's reads of the block (and claims) are done
         {
             constexpr int R4 = TB / 4;  // float4s per staged row
             constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
@@ -857,14 +904,11 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
                 }
             }
         }
-        const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : 0;
+        if (threadIdx.x == 0) *claims = 0u;
         __syncthreads();
-        const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz);
-        auto load_group = [&](int g, int (&gi)[CH], V &dy) {
-            const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
-            const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-            const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
-            const int len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+        // a group's chunks of gather indices and its rows' dY slices, one group after its claim
+        auto load_group = [&](int G, int a, int len, int (&gi)[CH], V &dy) {
+            const int key = min(k_lo + SL * G + slot, nkeys - 1);
             const int base = (a + j) * 4;
 #pragma unroll
             for (int c = 0; c < CH; ++c) gi[c] = buf_ld(rg, 16 * c + j < len ? base + 64 * c : kBufPast);
@@ -874,21 +918,14 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
             float p[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) p[t] = 0.f;
-            const int nst = m - 16 * c;
-            tile_dot4<VW, 0>(p, off, lane_off, lds, dy);
-            if (nst > 4) tile_dot4<VW, 4>(p, off, lane_off, lds, dy);
-            if (nst > 8) tile_dot4<VW, 8>(p, off, lane_off, lds, dy);
-            if (nst > 12) tile_dot4<VW, 12>(p, off, lane_off, lds, dy);
+            tile_dot_chunk<VW>(p, off, m - 16 * c, lane_off, lds, dy);
             const float r = group_reduce_scatter<16, 16>(p, j);
             if (16 * c + j < len) {
                 float *d = dw + a + 16 * c + j;
                 *d = bt == 0 ? r : *d + r;
             }
         };
-        auto compute = [&](int g, const int (&gi)[CH], const V &dy) {
-            const int src = (g * SL + slot) * 4;
-            const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-            const int len = __builtin_amdgcn_ds_bpermute(src, s_len);
+        auto compute = [&](int a, int len, const int (&gi)[CH], const V &dy) {
             int m = max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
                         max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
 #pragma unroll
@@ -908,19 +945,30 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
 #pragma unroll
             for (int i = 0; i < VW; ++i) asm volatile("" ::"v"(vget(dy, i)));
         };
-        int gi0[CH], gi1[CH], gi2[CH];
-        V d0, d1, d2;
-        load_group(0, gi0, d0);
-        load_group(1, gi1, d1);
-        for (int g = 0; g < my_groups; g += 3) {
-            load_group(g + 2, gi2, d2);
-            compute(g, gi0, d0);
-            if (g + 1 >= my_groups) break;
-            load_group(g + 3, gi0, d0);
-            compute(g + 1, gi1, d1);
-            if (g + 2 >= my_groups) break;
-            load_group(g + 4, gi1, d1);
-            compute(g + 2, gi2, d2);
+        // ring of claimed groups: [0] computed now, [1] its loads in flight, [2] claimed this phase
+        int Gs[3], As[3], Ls[3];
+        Gs[0] = claim();
+        seg(Gs[0], As[0], Ls[0]);
+        Gs[1] = claim();
+        seg(Gs[1], As[1], Ls[1]);
+        int gA[CH], gB[CH], gC[CH];
+        V dA, dB, dC;
+        load_group(Gs[0], As[0], Ls[0], gA, dA);
+        auto phase = [&](int (&gc)[CH], V &dc, int (&gn)[CH], V &dn) {
+            Gs[2] = claim();
+            seg(Gs[2], As[2], Ls[2]);
+            load_group(Gs[1], As[1], Ls[1], gn, dn);
+            compute(As[0], Ls[0], gc, dc);
+            Gs[0] = Gs[1], As[0] = As[1], Ls[0] = Ls[1];
+            Gs[1] = Gs[2], As[1] = As[2], Ls[1] = Ls[2];
+            return Gs[0] < ngroups;
+        };
+        if (Gs[0] < ngroups) {
+            for (;;) {
+                if (!phase(gA, dA, gB, dB)) break;
+                if (!phase(gB, dB, gC, dC)) break;
+                if (!phase(gC, dC, gA, dA)) break;
+            }
         }
     }
 }
@@ -2431,16 +2479,17 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     if (env == 0) return;
     const int64_t Bp = pad_batch(B);
     const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
-    // nnz < 2^30: the tiles read the per-entry arrays through 32-bit byte offsets.  At most
+    // nnz < 2^29: the tiles read the per-entry arrays (and the segment table) through 32-bit byte
+    // offsets, which stay below 2^31 and below the out-of-range offset kBufPast.  At most
     // kTileMaxBatchTiles batch tiles: the block partials grow with the batch, and wider batches keep
     // the wide-batch gather paths.
-    if (tb == 0 || Bp / tb > kTileMaxBatchTiles || nnz < kTileMinNnz || nnz >= (int64_t(1) << 30) ||
+    if (tb == 0 || Bp / tb > kTileMaxBatchTiles || nnz < kTileMinNnz || nnz >= (int64_t(1) << 29) ||
         opnd_rows < 1 || nkeys < 1)
         return;
     int64_t ncb, cw;
     tile_blocks(opnd_rows, ncb, cw);
     const double mean = static_cast<double>(nnz) / static_cast<double>(nkeys * ncb);
-    if (mean < 8.0 || nkeys * (ncb + 1) >= (int64_t(1) << 31)) return;
+    if (mean < 8.0 || nkeys * (ncb + 1) >= (int64_t(1) << 29)) return;
     p.mapping = kTile;
     p.bpad = Bp;
     p.ttb = tb;
@@ -2571,11 +2620,11 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
     // block) segments average at least 8 entries
     const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
     if (!p.csr1 && tile_env() != 0 && tb > 0 && Bp / tb <= kTileMaxBatchTiles && nnz >= kTileMinNnz &&
-        nnz < (int64_t(1) << 30) && I > 0 && O > 0) {
+        nnz < (int64_t(1) << 29) && I > 0 && O > 0) {
         int64_t ncb, cw;
         tile_blocks(I, ncb, cw);
         const double mean = static_cast<double>(nnz) / static_cast<double>(O * ncb);
-        if (mean >= 8.0 && O * (ncb + 1) < (int64_t(1) << 31)) {
+        if (mean >= 8.0 && O * (ncb + 1) < (int64_t(1) << 29)) {
             p.tile = true;
             p.ttb = tb;
             p.tnnz = static_cast<int>(nnz);
@@ -2591,7 +2640,7 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
             p.tcw = static_cast<int>(cw);
             p.tkpr = tile_keys_per_range(O, ncb, tb);
             p.tnrb = static_cast<int>(ceil_div(O, p.tkpr));
-            p.tnbt = static_cast<int>(Bp / tb);
+                    p.tnbt = static_cast<int>(Bp / tb);
         }
     }
     size_t at = 0;
@@ -2624,13 +2673,20 @@ int allow_lds(const void *f, size_t lds, std::atomic<uint64_t> &done, const char
     return SNACK_OK;
 }
 
-// The tiled kernels' largest dynamic LDS at VW floats per lane: kTileLdsRows staged rows of 16 VW.
-constexpr size_t tile_lds_max(int VW) { return static_cast<size_t>(kTileLdsRows) * 16 * VW * sizeof(float); }
+// The tiled kernels' largest dynamic LDS at VW floats per lane: kTileLdsRows staged rows of 16 VW
+// and the group counter.
+constexpr size_t tile_lds_max(int VW) {
+    return static_cast<size_t>(kTileLdsRows) * 16 * VW * sizeof(float) + kTileClaimBytes;
+}
+// Dynamic LDS of one launch: the staged block of cw rows, the zero row and the group counter.
+inline size_t tile_lds_bytes(int cw, int VW) {
+    return static_cast<size_t>(cw + 1) * (16 * VW) * sizeof(float) + kTileClaimBytes;
+}
 
 template <int VW, int CH>
 int launch_tile_sddmm_kernel(const SddmmPlan &p, int64_t O, int64_t I, const int32_t *tab, const int32_t *cols,
                              const float *xt, const float *dyt, float *dw, hipStream_t st) {
-    const size_t lds = static_cast<size_t>(p.tcw + 1) * (16 * VW) * sizeof(float);
+    const size_t lds = tile_lds_bytes(p.tcw, VW);
     static std::atomic<uint64_t> lds_ok{0};
     if (int s = allow_lds(reinterpret_cast<const void *>(&tile_sddmm_kernel<VW, CH>), tile_lds_max(VW), lds_ok,
                           "tile_sddmm_kernel"))
@@ -2906,7 +2962,7 @@ int launch_gather(const int32_t *idx, const float *src, int64_t n, float *dst, h
 template <int VW, int CH, bool VP>
 int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
                        const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
-    const size_t lds = static_cast<size_t>(p.tcw + 1) * (16 * VW) * sizeof(float);
+    const size_t lds = tile_lds_bytes(p.tcw, VW);
     static std::atomic<uint64_t> lds_ok{0};  // up to 160 KB of dynamic LDS, allowed once per device
     if (int s = allow_lds(reinterpret_cast<const void *>(&tile_spmm_kernel<VW, CH, VP>), tile_lds_max(VW), lds_ok,
                           "tile_spmm_kernel"))
@@ -3538,7 +3594,7 @@ static int run_split_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *
 template <int VW, int CH, bool VP>
 int launch_tile_bwd_kernel(const SpmmPlan &sp, int64_t I, int64_t O, const int32_t *tab, const snack_coo_desc *W,
                            const float *dyt, const float *xt, float *part, float *dW, hipStream_t st) {
-    const size_t lds = static_cast<size_t>(sp.tcw + 1) * (16 * VW) * sizeof(float);
+    const size_t lds = tile_lds_bytes(sp.tcw, VW);
     static std::atomic<uint64_t> lds_ok{0};
     if (int s = allow_lds(reinterpret_cast<const void *>(&tile_bwd_kernel<VW, CH, VP>), tile_lds_max(VW), lds_ok,
                           "tile_bwd_kernel"))

@@ -97,13 +97,13 @@ enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2, SNACK
  *                             write dW contiguously, and moves one permuted read per entry
  *                             to the forward pass instead.  Requires the column view.
  *   row_blocks  [O*(nb_r+1)] NULL, or the row order cut into column blocks: nb_r =
- *                             ceil(I / 639) blocks of w_r = ceil(I / nb_r) columns, and
+ *                             ceil(I / 638) blocks of w_r = ceil(I / nb_r) columns, and
  *                             row_blocks[r*(nb_r+1) + j] = the first triple position of row r
  *                             whose column is >= j*w_r (j = nb_r: the row's end).  Each
  *                             (row, block) segment is the run of the row's entries whose
  *                             operand rows the tiled kernels stage together in LDS (Section
  *                             3.1's row-sorted triple makes it contiguous).
- *   col_blocks  [I*(nb_c+1)] NULL, or the same for the column view: nb_c = ceil(O / 639)
+ *   col_blocks  [I*(nb_c+1)] NULL, or the same for the column view: nb_c = ceil(O / 638)
  *                             blocks of w_c = ceil(O / nb_c) rows, positions in column-view
  *                             order.  Requires the column view.
  *                             Both tables depend on the structure only (not on the values or
@@ -338,8 +338,8 @@ int64_t snack_coo_get_option(int option);
 
 /* Segment tables of snack_coo_desc.row_blocks (view = SNACK_VIEW_ROWS) and
  * snack_coo_desc.col_blocks (view = SNACK_VIEW_COLS): the number of int32
- * entries, keys * (nb + 1) with keys = O and nb = ceil(I / 639) for the rows
- * (keys = I and nb = ceil(O / 639) for the column view; nb = 1 for an empty
+ * entries, keys * (nb + 1) with keys = O and nb = ceil(I / 638) for the rows
+ * (keys = I and nb = ceil(O / 638) for the column view; nb = 1 for an empty
  * dimension), or -1 with snack_last_error() set for a NULL descriptor or an
  * unknown view. */
 enum { SNACK_VIEW_ROWS = 0, SNACK_VIEW_COLS = 1 };

@@ -146,15 +146,15 @@ def test_column_order_values_host_checks_and_workspace():
 
 
 def test_block_offsets_count_and_errors():
-    """Segment-table sizes: keys * (ceil(n / 639) + 1); argument errors come back before any launch."""
+    """Segment-table sizes: keys * (ceil(n / 638) + 1); argument errors come back before any launch."""
     lib = snk._lib
     d = snk._Desc()
     d.out_features, d.in_features, d.nnz = 10000, 10000, 0
     assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 10000 * 17
-    d.out_features, d.in_features = 700, 639
+    d.out_features, d.in_features = 700, 638
     assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 2
-    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_COLS) == 639 * 3
-    d.in_features = 640
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_COLS) == 638 * 3
+    d.in_features = 639
     assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 3
     d.in_features = 0
     assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 2
@@ -176,7 +176,7 @@ def test_tiled_workspace_bounded_by_batch_tiles():
     d = snk._Desc()
     d.out_features, d.in_features, d.nnz = 5000, 5000, 2_500_000
     d.row_offsets = d.rows = d.cols = d.vals = 0x1000
-    nb = -(-5000 // 639)  # column blocks of the tiled walk
+    nb = -(-5000 // 638)  # column blocks of the tiled walk
     fwd256 = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 256, 0)
     assert fwd256 >= 4 * 256 * nb * 5000  # block partials of the tiled forward
     fwd4096 = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 4096, 0)

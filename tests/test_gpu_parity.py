@@ -234,7 +234,7 @@ def test_invariants_bias_determinism_scaling_permutation():
     nnz, O, I = L["nnz"], 700, 900
     assert W.device_bytes(blocks=False) == 12 * nnz + 4 * (O + 1) + 12 * nnz + 4 * (I + 1)
     # plus the segment tables of the tiled kernels: (nb + 1) offsets per row and per column
-    nb_r, nb_c = -(-I // 639), -(-O // 639)
+    nb_r, nb_c = -(-I // 638), -(-O // 638)
     assert W.device_bytes() == W.device_bytes(blocks=False) + 4 * (O * (nb_r + 1) + I * (nb_c + 1))
 
 

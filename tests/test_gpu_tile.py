@@ -165,7 +165,7 @@ def test_tiled_in_graph(layers):
 
 def _ref_blocks(offs, gidx, n):
     """table[key][j] = first position of the key's run at or past gather index j*w (numpy)."""
-    nb = max(1, -(-n // 639))
+    nb = max(1, -(-n // 638))
     w = max(1, -(-n // nb))
     keys = offs.size - 1
     t = np.empty((keys, nb + 1), np.int64)
