@@ -561,15 +561,81 @@ __device__ __forceinline__ float vget(const float4 &v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// The LDS reads of steps T0..T0+3 of one chunk (entry T0+u's staged row, this lane's VW columns).
+// Staged rows of the tiled walks that read the activations in place (tile_spmm_kernel,
+// tile_sddmm_kernel): row r holds TB = 16 VW fp32 batch columns as NQ = TB / 4 chunks of 16 bytes,
+// chunk q (columns 4q .. 4q+3) at chunk position q ^ (r & (NQ - 1)).  Staging writes one chunk per
+// thread for consecutive rows, so the swizzle spreads a wave's writes over the banks; a slot reads
+// one whole row, so its reads stay conflict-free.  Lane byte offsets below 16 * NQ and row offsets
+// that are multiples of 16 * NQ combine as row_off(r) ^ lane_off, row_off(r) = r * 16 NQ +
+// 16 (r & (NQ - 1)): the XOR replaces the address add of an unswizzled row.
+template <int VW>
+__device__ __forceinline__ uint32_t tile_row_off(int r) {
+    constexpr int NQ = 4 * VW;
+    return static_cast<uint32_t>(r) * (16u * NQ) + 16u * static_cast<uint32_t>(r & (NQ - 1));
+}
+
+// Buffer resource over an activation of n elements (fp32 or bf16) and a load of one element,
+// widened to fp32: past the end, or at kBufPast, the load returns 0.  Callers keep n * the element
+// size below 2^31.
+template <typename InT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(const InT *p, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<InT *>(p), static_cast<short>(0),
+                                             n * static_cast<int>(sizeof(InT)), 0x00020000);
+}
+template <typename InT>
+__device__ __forceinline__ float act_ld(__amdgpu_buffer_rsrc_t r, int byte_off);
+template <>
+__device__ __forceinline__ float act_ld<float>(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+template <>
+__device__ __forceinline__ float act_ld<bf16_t>(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0)) << 16);
+}
+
+// Stages rows [r0, r0 + cn) (feature index) of batch tile bt of a batch-major activation [B][ld]
+// (fp32 or bf16, widened to fp32; ra = act_rsrc over its B * ld elements) into LDS rows 0 .. cn-1
+// in the swizzled layout above; rows cn .. cw (row cw is the zero row) and batch rows >= B are
+// zero (loaded past the buffer).  Item i is chunk q = i / 640 of row c = i % 640 (640 =
+// kTileLdsRows + 1 >= cw + 1, a constant divisor): consecutive threads take consecutive rows of
+// one chunk, so each of a chunk's four batch rows is read in runs of 64 features.
+template <int VW, typename InT>
+__device__ __forceinline__ void tile_stage_rows(float4 *xs4, __amdgpu_buffer_rsrc_t ra, int ld, int bt, int r0,
+                                                int cn, int cw) {
+    constexpr int NQ = 4 * VW, TB = 16 * VW, kStride = kTileLdsRows + 1;
+    constexpr int kEs = static_cast<int>(sizeof(InT));
+    constexpr int kIters = (kStride * NQ + kTileThreads - 1) / kTileThreads;
+    constexpr int kRound = kIters < 5 ? kIters : 5;  // items whose loads are in flight together
+#pragma unroll
+    for (int it0 = 0; it0 < kIters; it0 += kRound) {
+        float4 v[kRound];
+        int at[kRound];
+#pragma unroll
+        for (int u = 0; u < kRound && it0 + u < kIters; ++u) {
+            const int i = (it0 + u) * kTileThreads + static_cast<int>(threadIdx.x);
+            const int q = i / kStride, c = i - q * kStride;
+            at[u] = q < NQ && c <= cw ? c * NQ + (q ^ (c & (NQ - 1))) : -1;
+            const int off = q < NQ && c < cn ? ((TB * bt + 4 * q) * ld + r0 + c) * kEs : kBufPast;
+            const int step = off == kBufPast ? 0 : ld * kEs;
+            v[u] = make_float4(act_ld<InT>(ra, off), act_ld<InT>(ra, off + step), act_ld<InT>(ra, off + 2 * step),
+                               act_ld<InT>(ra, off + 3 * step));
+        }
+#pragma unroll
+        for (int u = 0; u < kRound && it0 + u < kIters; ++u)
+            if (at[u] >= 0) xs4[at[u]] = v[u];
+    }
+}
+
+// The LDS reads of steps T0..T0+3 of one chunk (entry T0+u's staged row, this lane's VW columns;
+// off is the entry's tile_row_off).
 template <int VW, int T0>
 __device__ __forceinline__ void tile_reads4(typename TileVec<VW>::T (&x)[4], uint32_t off, uint32_t lane_off,
                                             const char *lds) {
     typedef typename TileVec<VW>::T V;
-    x[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) + lane_off));
-    x[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
-    x[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
-    x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+    x[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) ^ lane_off));
+    x[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) ^ lane_off));
+    x[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) ^ lane_off));
+    x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) ^ lane_off));
 }
 
 // The FMAs of steps T0..T0+3: acc += (value of entry T0+u) * row.
@@ -629,20 +695,23 @@ __global__ __launch_bounds__(kBlock) void tile_bounds_kernel(int nkeys, int ncb,
     tab[i] = lo;
 }
 
-// opnd: feature-major [opnd_rows (+1)][ld] fp32, ld a multiple of TB = 16 VW; batch tile
-// bt = blockIdx.y covers columns [TB bt, TB bt + TB): each lane of a slot holds VW of them, and one
-// staged operand row is TB floats.  Logical workgroup L = cb * nrb + rb (XCD-contiguous).
+// act: the batch-major activation [B][opnd_rows] (fp32 or bf16, B * opnd_rows * its size < 2^31),
+// read in place; batch tile
+// bt = blockIdx.y covers columns [TB bt, TB bt + TB), TB = 16 VW: each lane of a slot holds VW of
+// them, and one staged operand row is TB floats (swizzled, tile_stage_rows).  Logical workgroup
+// L = cb * nrb + rb (XCD-contiguous).
 // VP: the values are read through perm (vals[perm[k]]): the permutation is loaded with the gather
 // indices two groups ahead, the values it points at one group ahead.
-template <int VW, int CH, bool VP>
+template <int VW, int CH, bool VP, typename InT>
 __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
     const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm, int nnz,
-    const float *__restrict__ opnd, int opnd_rows, int ld, float *__restrict__ part) {
+    const InT *__restrict__ act, int opnd_rows, int64_t B, float *__restrict__ part) {
     constexpr int SL = 4;                      // slots (keys) per wave, 16 lanes each
     constexpr int TB = 16 * VW;                // batch columns of a tile
     constexpr uint32_t kRowBytes = 4u * TB;    // one staged operand row
-    extern __shared__ float4 xs4[];
+    // static: its address is known when compiling, so a row chunk's address is one DPP XOR
+    __shared__ float4 xs4[kTileLdsRows * 4 * VW + kTileClaimBytes / 16];
     const int64_t L = xcd_block();
     if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
     const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
@@ -653,29 +722,13 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     const int slot = lane >> 4;                 // the row of 16 lanes is the slot
     const int ls = lane & 15;                   // lane within the slot: batch columns [ls*VW, ls*VW + VW)
     const uint32_t lane_off = static_cast<uint32_t>(ls * VW * 4);
-    const uint32_t zoff = static_cast<uint32_t>(cw) * kRowBytes;
+    const uint32_t zoff = tile_row_off<VW>(cw);
     const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
     // group G = keys k_lo + SL*G .. +SL-1, slot s taking key k_lo + SL*G + s
     const int ngroups = (k_hi - k_lo + SL - 1) / SL;
     unsigned *claims = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(xs4) + (cw + 1) * kRowBytes);
-    {  // stage the block's operand rows; rows cn..cw are zero (row cw is the zero row)
-        constexpr int R4 = TB / 4;  // float4s per staged row
-        constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
-        const float4 *src = reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld + TB * bt);
-        const int ld4 = ld / 4, n4 = (cw + 1) * R4;
-        float4 tmp[kIters];
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
-            const int c = i / R4, q = i % R4;
-            tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int i = it * kTileThreads + static_cast<int>(threadIdx.x);
-            if (i < n4) xs4[i] = tmp[it];
-        }
-    }
+    // the block's operand rows; rows cn..cw are zero (row cw is the zero row)
+    tile_stage_rows<VW, InT>(xs4, act_rsrc(act, static_cast<int>(B) * opnd_rows), opnd_rows, bt, c0, cn, cw);
     if (threadIdx.x == 0) *claims = 0u;
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(xs4);
@@ -726,7 +779,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         for (int c = 0; c < CH; ++c) {
             if (16 * c < m) {
                 const bool ok = 16 * c + j < len;
-                const uint32_t off = ok ? static_cast<uint32_t>(gi[c] - c0) * kRowBytes : zoff;
+                const uint32_t off = ok ? tile_row_off<VW>(gi[c] - c0) : zoff;
                 const float v = ok ? __int_as_float(vv[c]) : 0.f;
                 tile_chunk<VW>(acc, off, v, m - 16 * c, lane_off, lds);
             }
@@ -736,8 +789,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
             const int pos = (a + 16 * c + j) * 4;
             const int gv = buf_ld(rg, pos);
             const float w = __int_as_float(buf_ld(rv, VP ? (ok ? buf_ld(rp, pos) * 4 : kBufPast) : pos));
-            tile_chunk<VW>(acc, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, ok ? w : 0.f, m - 16 * c, lane_off,
-                           lds);
+            tile_chunk<VW>(acc, ok ? tile_row_off<VW>(gv - c0) : zoff, ok ? w : 0.f, m - 16 * c, lane_off, lds);
         }
         // every chunk register is consumed here, also those a short group skipped: without this
         // use, refilling them would wait for loads issued after them
@@ -843,16 +895,21 @@ __device__ __forceinline__ void tile_dot_chunk(float (&p)[16], uint32_t off, int
     }
 }
 
-template <int VW, int CH>
+// x: the batch-major X [B][opnd_rows], dy_act: the batch-major dY [B][nkeys] (fp32 or bf16), both
+// read in place: the X block is staged as in tile_spmm_kernel, and each lane loads its VW batch
+// columns of its slot's dY row (zero past the batch).  B * max(opnd_rows, nkeys) * the element
+// size < 2^31 (32-bit buffer offsets).
+template <int VW, int CH, typename InT>
 __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, int nbt, const int32_t *__restrict__ tab,
-    const int32_t *__restrict__ gidx, int nnz, const float *__restrict__ opnd, int opnd_rows,
-    const float *__restrict__ dyt, int ld, float *__restrict__ dw) {
+    const int32_t *__restrict__ gidx, int nnz, const InT *__restrict__ x, int opnd_rows,
+    const InT *__restrict__ dy_act, int64_t B, float *__restrict__ dw) {
     constexpr int SL = 4;
     constexpr int TB = 16 * VW;
     constexpr uint32_t kRowBytes = 4u * TB;
     typedef typename TileVec<VW>::T V;
-    extern __shared__ float4 xs4[];
+    // static: its address is known when compiling, so a row chunk's address is one DPP XOR
+    __shared__ float4 xs4[kTileLdsRows * 4 * VW + kTileClaimBytes / 16];
     const int64_t L = xcd_block();
     if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
     const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
@@ -861,7 +918,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     const int j = lane & 15;
     const int slot = lane >> 4;
     const uint32_t lane_off = static_cast<uint32_t>(j * VW * 4);
-    const uint32_t zoff = static_cast<uint32_t>(cw) * kRowBytes;
+    const uint32_t zoff = tile_row_off<VW>(cw);
     const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
     // group G = rows k_lo + SL*G .. +SL-1, taken from the workgroup's counter as in tile_spmm_kernel
     const int ngroups = (k_hi - k_lo + SL - 1) / SL;
@@ -869,6 +926,8 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     const char *lds = reinterpret_cast<const char *>(xs4);
     const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz);
     const __amdgpu_buffer_rsrc_t rt = buf_rsrc(tab, nkeys * (ncb + 1));
+    const __amdgpu_buffer_rsrc_t rx = act_rsrc(x, static_cast<int>(B) * opnd_rows);
+    const __amdgpu_buffer_rsrc_t rdy = act_rsrc(dy_act, static_cast<int>(B) * nkeys);
     auto claim = [&]() {
         unsigned g = 0;
         if (lane == 0) g = atomicAdd(claims, 1u);
@@ -882,28 +941,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     };
     for (int bt = 0; bt < nbt; ++bt) {
         if (bt > 0) __syncthreads();  // the previous batch tile's reads of the block (and claims) are done
-        {
-            constexpr int R4 = TB / 4;  // float4s per staged row
-            constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
-            const float4 *src = reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld + TB * bt);
-            const int ld4 = ld / 4, n4 = (cw + 1) * R4;
-            constexpr int kHalf = (kIters + 1) / 2;  // two rounds: fewer registers live
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float4 tmp[kHalf];
-#pragma unroll
-                for (int it = 0; it < kHalf; ++it) {
-                    const int i = (h * kHalf + it) * kTileThreads + static_cast<int>(threadIdx.x);
-                    const int c = i / R4, q = i % R4;
-                    tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int it = 0; it < kHalf; ++it) {
-                    const int i = (h * kHalf + it) * kTileThreads + static_cast<int>(threadIdx.x);
-                    if (i < n4) xs4[i] = tmp[it];
-                }
-            }
-        }
+        tile_stage_rows<VW, InT>(xs4, rx, opnd_rows, bt, c0, cn, cw);
         if (threadIdx.x == 0) *claims = 0u;
         __syncthreads();
         // a group's chunks of gather indices and its rows' dY slices, one group after its claim
@@ -912,7 +950,13 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
             const int base = (a + j) * 4;
 #pragma unroll
             for (int c = 0; c < CH; ++c) gi[c] = buf_ld(rg, 16 * c + j < len ? base + 64 * c : kBufPast);
-            dy = *reinterpret_cast<const V *>(dyt + static_cast<int64_t>(key) * ld + TB * bt + VW * j);
+            float d[VW];  // batch rows >= B: past the buffer, 0
+            const int off = ((TB * bt + VW * j) * nkeys + key) * static_cast<int>(sizeof(InT));
+#pragma unroll
+            for (int i = 0; i < VW; ++i) d[i] = act_ld<InT>(rdy, off + i * nkeys * static_cast<int>(sizeof(InT)));
+            if constexpr (VW == 1) dy = d[0];
+            else if constexpr (VW == 2) dy = make_float2(d[0], d[1]);
+            else dy = make_float4(d[0], d[1], d[2], d[3]);
         };
         auto chunk = [&](int a, int len, int m, int c, uint32_t off, const V &dy) {
             float p[16];
@@ -932,13 +976,13 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
             for (int c = 0; c < CH; ++c) {
                 if (16 * c < m) {
                     const bool ok = 16 * c + j < len;
-                    chunk(a, len, m, c, ok ? static_cast<uint32_t>(gi[c] - c0) * kRowBytes : zoff, dy);
+                    chunk(a, len, m, c, ok ? tile_row_off<VW>(gi[c] - c0) : zoff, dy);
                 }
             }
             for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
                 const bool ok = 16 * c + j < len;
                 const int gv = buf_ld(rg, (a + 16 * c + j) * 4);
-                chunk(a, len, m, c, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, dy);
+                chunk(a, len, m, c, ok ? tile_row_off<VW>(gv - c0) : zoff, dy);
             }
 #pragma unroll
             for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]));
@@ -2318,7 +2362,7 @@ struct SpmmPlan {
     int64_t chunk;       // segscan, csr1: entries per wave; scatter: entries per workgroup
     int64_t nchunks;     // segscan, csr1: waves; scatter: workgroups (partial copies)
     int64_t nparts;      // csr1 private copies: workgroups (partial copies)
-    bool direct;         // operand used in place (fp32, batch 1) instead of a transposed copy
+    bool direct;         // operand used in place (fp32 at batch 1; the tiled walk) instead of a transposed copy
     int64_t bpad;        // batch columns of the feature-major operand (rowwave: B rounded up to 4)
     size_t off_opnd, off_head, off_tail, off_cvals, total;
     // kTile: batch columns per tile (16, 32 or 64), prefetched chunks, column blocks, key blocks,
@@ -2483,8 +2527,9 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     // offsets, which stay below 2^31 and below the out-of-range offset kBufPast.  At most
     // kTileMaxBatchTiles batch tiles: the block partials grow with the batch, and wider batches keep
     // the wide-batch gather paths.
+    // The operand is read through 32-bit byte offsets too: Bp * opnd_rows floats below 2^31 bytes.
     if (tb == 0 || Bp / tb > kTileMaxBatchTiles || nnz < kTileMinNnz || nnz >= (int64_t(1) << 29) ||
-        opnd_rows < 1 || nkeys < 1)
+        opnd_rows < 1 || nkeys < 1 || Bp * opnd_rows >= (int64_t(1) << 29))
         return;
     int64_t ncb, cw;
     tile_blocks(opnd_rows, ncb, cw);
@@ -2501,9 +2546,9 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     p.tkpr = tile_keys_per_range(nkeys, ncb, tb);
     p.tnrb = static_cast<int>(ceil_div(nkeys, p.tkpr));
     p.tnbt = static_cast<int>(Bp / tb);
+    p.direct = true;  // the tiles stage their blocks from the batch-major activation
     size_t at = 0;
     p.off_opnd = at;
-    at = align_up(at + sizeof(float) * static_cast<size_t>((opnd_rows + 1) * Bp));
     p.off_tab = at;
     at = align_up(at + sizeof(int32_t) * static_cast<size_t>(nkeys * (ncb + 1)));
     p.off_part = at;
@@ -2620,7 +2665,7 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
     // block) segments average at least 8 entries
     const int tb = Bp % 64 == 0 ? 64 : (Bp % 32 == 0 ? 32 : (Bp % 16 == 0 ? 16 : 0));
     if (!p.csr1 && tile_env() != 0 && tb > 0 && Bp / tb <= kTileMaxBatchTiles && nnz >= kTileMinNnz &&
-        nnz < (int64_t(1) << 29) && I > 0 && O > 0) {
+        nnz < (int64_t(1) << 29) && I > 0 && O > 0 && Bp * std::max(I, O) < (int64_t(1) << 29)) {
         int64_t ncb, cw;
         tile_blocks(I, ncb, cw);
         const double mean = static_cast<double>(nnz) / static_cast<double>(O * ncb);
@@ -2631,7 +2676,7 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
             p.rowq = 0;
             p.slices = 1;
             p.bpad = Bp;
-            p.x_direct = p.dy_direct = false;
+            p.x_direct = p.dy_direct = true;  // X staged and dY read in their batch-major layout
             const double need = mean + 4.0 * std::sqrt(mean) + 1.0;
             // 8 chunks at 64 columns would spill registers; longer segments take their further
             // chunks unprefetched there
@@ -2640,7 +2685,7 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
             p.tcw = static_cast<int>(cw);
             p.tkpr = tile_keys_per_range(O, ncb, tb);
             p.tnrb = static_cast<int>(ceil_div(O, p.tkpr));
-                    p.tnbt = static_cast<int>(Bp / tb);
+            p.tnbt = static_cast<int>(Bp / tb);
         }
     }
     size_t at = 0;
@@ -2683,24 +2728,36 @@ inline size_t tile_lds_bytes(int cw, int VW) {
     return static_cast<size_t>(cw + 1) * (16 * VW) * sizeof(float) + kTileClaimBytes;
 }
 
-template <int VW, int CH>
-int launch_tile_sddmm_kernel(const SddmmPlan &p, int64_t O, int64_t I, const int32_t *tab, const int32_t *cols,
-                             const float *xt, const float *dyt, float *dw, hipStream_t st) {
-    const size_t lds = tile_lds_bytes(p.tcw, VW);
-    static std::atomic<uint64_t> lds_ok{0};
-    if (int s = allow_lds(reinterpret_cast<const void *>(&tile_sddmm_kernel<VW, CH>), tile_lds_max(VW), lds_ok,
-                          "tile_sddmm_kernel"))
-        return s;
+template <int VW, int CH, typename InT>
+int launch_tile_sddmm_kernel(const SddmmPlan &p, int64_t O, int64_t I, int64_t B, const int32_t *tab,
+                             const int32_t *cols, const InT *X, const InT *dY, float *dw, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)));
-    hipLaunchKernelGGL((tile_sddmm_kernel<VW, CH>), grid, dim3(kTileThreads), lds, st, static_cast<int>(O), p.tncb,
-                       p.tnrb, p.tcw, p.tkpr, p.tnbt, tab, cols, p.tnnz, xt, static_cast<int>(I), dyt,
-                       static_cast<int>(p.bpad), dw);
+    hipLaunchKernelGGL((tile_sddmm_kernel<VW, CH, InT>), grid, dim3(kTileThreads), 0, st, static_cast<int>(O),
+                       p.tncb, p.tnrb, p.tcw, p.tkpr, p.tnbt, tab, cols, p.tnnz, X, static_cast<int>(I), dY, B, dw);
     return check_hip("tile_sddmm_kernel");
 }
 
-// The tiled weight gradient (row view): segment table (unless the layer has one), then the tiles.
-int launch_tile_sddmm(const SddmmPlan &p, const snack_coo_desc *W, const float *xt, const float *dyt, float *dw,
-                      int32_t *tab_ws, hipStream_t st) {
+template <typename InT>
+int launch_tile_sddmm_t(const SddmmPlan &p, int64_t O, int64_t I, int64_t B, const int32_t *tab,
+                        const int32_t *cols, const InT *X, const InT *dY, float *dw, hipStream_t st) {
+    // 8 prefetched chunks only below 64 columns (at 64 they would spill registers)
+    switch (p.ttb * 16 + std::min(p.tch, p.ttb == 64 ? 4 : 8)) {
+        case 16 * 16 + 2: return launch_tile_sddmm_kernel<1, 2>(p, O, I, B, tab, cols, X, dY, dw, st);
+        case 16 * 16 + 4: return launch_tile_sddmm_kernel<1, 4>(p, O, I, B, tab, cols, X, dY, dw, st);
+        case 16 * 16 + 8: return launch_tile_sddmm_kernel<1, 8>(p, O, I, B, tab, cols, X, dY, dw, st);
+        case 32 * 16 + 2: return launch_tile_sddmm_kernel<2, 2>(p, O, I, B, tab, cols, X, dY, dw, st);
+        case 32 * 16 + 4: return launch_tile_sddmm_kernel<2, 4>(p, O, I, B, tab, cols, X, dY, dw, st);
+        case 32 * 16 + 8: return launch_tile_sddmm_kernel<2, 8>(p, O, I, B, tab, cols, X, dY, dw, st);
+        case 64 * 16 + 2: return launch_tile_sddmm_kernel<4, 2>(p, O, I, B, tab, cols, X, dY, dw, st);
+        case 64 * 16 + 4: return launch_tile_sddmm_kernel<4, 4>(p, O, I, B, tab, cols, X, dY, dw, st);
+        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported plan (batch tile %d, chunks %d)", p.ttb, p.tch);
+    }
+}
+
+// The tiled weight gradient (row view): segment table (unless the layer has one), then the tiles,
+// which read X and dY (act_dtype) in their batch-major layout.
+int launch_tile_sddmm(const SddmmPlan &p, const snack_coo_desc *W, const void *X, const void *dY, int64_t B,
+                      int act_dtype, float *dw, int32_t *tab_ws, hipStream_t st) {
     const int64_t O = W->out_features, I = W->in_features;
     const int32_t *tab = W->row_blocks;
     probe(true, st);
@@ -2709,24 +2766,11 @@ int launch_tile_sddmm(const SddmmPlan &p, const snack_coo_desc *W, const float *
         if (int s = launch_bounds(O, p.tncb, p.tcw, W->row_offsets, W->cols, t, st)) return s;
         tab = t;
     }
-    int s;
-#define SNACK_TSD(VWV)                                                                              \
-    switch (p.tch) {                                                                                \
-        case 2: s = launch_tile_sddmm_kernel<VWV, 2>(p, O, I, tab, W->cols, xt, dyt, dw, st); break; \
-        case 4: s = launch_tile_sddmm_kernel<VWV, 4>(p, O, I, tab, W->cols, xt, dyt, dw, st); break; \
-        case 8: s = launch_tile_sddmm_kernel<VWV, 8>(p, O, I, tab, W->cols, xt, dyt, dw, st); break; \
-        default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported chunk count %d", p.tch);        \
-    }
-    if (p.ttb == 16) {
-        SNACK_TSD(1)
-    } else if (p.ttb == 32) {
-        SNACK_TSD(2)
-    } else if (p.tch == 2) {
-        s = launch_tile_sddmm_kernel<4, 2>(p, O, I, tab, W->cols, xt, dyt, dw, st);
-    } else {
-        s = launch_tile_sddmm_kernel<4, 4>(p, O, I, tab, W->cols, xt, dyt, dw, st);
-    }
-#undef SNACK_TSD
+    const int s = act_dtype == SNACK_F32
+                      ? launch_tile_sddmm_t(p, O, I, B, tab, W->cols, static_cast<const float *>(X),
+                                            static_cast<const float *>(dY), dw, st)
+                      : launch_tile_sddmm_t(p, O, I, B, tab, W->cols, static_cast<const bf16_t *>(X),
+                                            static_cast<const bf16_t *>(dY), dw, st);
     probe(false, st);
     return s;
 }
@@ -2739,8 +2783,8 @@ struct BwdPlan {
     int bt, q, nb;  // nb: row bands of the fused kernel (1 or kXcds)
     int64_t bpad;   // batch columns of the feature-major copies (B rounded up to 4)
     size_t off_x, off_dy, off_part, total;
-    // split: both gradients tiled, sharing the feature-major copies at off_x / off_dy; the input
-    // gradient's workspace starts at off_spmm, the weight gradient's segment table at off_sddmm.
+    // split: both gradients tiled, reading X and dY in place; the input gradient's workspace
+    // starts at off_spmm, the weight gradient's segment table at off_sddmm.
     // tiled: both gradients in one tiled pass over the column view (tile_bwd_kernel), its segment
     // table and dX partials in the workspace at off_spmm (laid out by sp)
     bool split, tiled;
@@ -2818,11 +2862,8 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
             p.split = true;
             p.sp = sp;
             p.sd = sd;
-            size_t at = 0;
-            p.off_x = at;
-            at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * Bp));
-            p.off_dy = at;
-            at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * Bp));
+            size_t at = 0;  // both passes read X and dY in place
+            p.off_x = p.off_dy = at;
             p.off_spmm = at;
             at = align_up(at + sp.total);
             p.off_sddmm = at;
@@ -2959,38 +3000,34 @@ int launch_gather(const int32_t *idx, const float *src, int64_t n, float *dst, h
     return check_hip("gather_vals_kernel");
 }
 
-template <int VW, int CH, bool VP>
+template <int VW, int CH, bool VP, typename InT>
 int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
-                       const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
-    const size_t lds = tile_lds_bytes(p.tcw, VW);
-    static std::atomic<uint64_t> lds_ok{0};  // up to 160 KB of dynamic LDS, allowed once per device
-    if (int s = allow_lds(reinterpret_cast<const void *>(&tile_spmm_kernel<VW, CH, VP>), tile_lds_max(VW), lds_ok,
-                          "tile_spmm_kernel"))
-        return s;
+                       const int32_t *perm, const InT *act, int64_t opnd_rows, int64_t B, float *part,
+                       hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(p.tncb) * p.tnrb)),
                     static_cast<unsigned>(p.tnbt));
-    hipLaunchKernelGGL((tile_spmm_kernel<VW, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(nkeys),
-                       p.tncb, p.tnrb, p.tcw, p.tkpr, tab, gidx, vals, perm, p.tnnz, opnd,
-                       static_cast<int>(opnd_rows), static_cast<int>(p.bpad), part);
+    hipLaunchKernelGGL((tile_spmm_kernel<VW, CH, VP, InT>), grid, dim3(kTileThreads), 0, st,
+                       static_cast<int>(nkeys), p.tncb, p.tnrb, p.tcw, p.tkpr, tab, gidx, vals, perm, p.tnnz, act,
+                       static_cast<int>(opnd_rows), B, part);
     return check_hip("tile_spmm_kernel");
 }
 
-template <int VW, bool VP>
+template <int VW, bool VP, typename InT>
 int launch_tile_ch(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
-                   const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
+                   const int32_t *perm, const InT *act, int64_t opnd_rows, int64_t B, float *part, hipStream_t st) {
     switch (p.tch) {
-        case 2: return launch_tile_kernel<VW, 2, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
-        case 4: return launch_tile_kernel<VW, 4, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
-        case 8: return launch_tile_kernel<VW, 8, VP>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
+        case 2: return launch_tile_kernel<VW, 2, VP>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st);
+        case 4: return launch_tile_kernel<VW, 4, VP>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st);
+        case 8: return launch_tile_kernel<VW, 8, VP>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st);
         default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported chunk count %d", p.tch);
     }
 }
 
-template <int VW>
+template <int VW, typename InT>
 int launch_tile_vw(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
-                   const int32_t *perm, const float *opnd, int64_t opnd_rows, float *part, hipStream_t st) {
-    if (perm) return launch_tile_ch<VW, true>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st);
-    return launch_tile_ch<VW, false>(p, nkeys, tab, gidx, vals, nullptr, opnd, opnd_rows, part, st);
+                   const int32_t *perm, const InT *act, int64_t opnd_rows, int64_t B, float *part, hipStream_t st) {
+    if (perm) return launch_tile_ch<VW, true>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st);
+    return launch_tile_ch<VW, false>(p, nkeys, tab, gidx, vals, nullptr, act, opnd_rows, B, part, st);
 }
 
 // The LDS-tiled gather-reduce: segment table, tiles, block sums (bias, transpose).
@@ -3004,10 +3041,11 @@ int launch_bounds(int64_t nkeys, int ncb, int cw, const int32_t *offs, const int
 }
 
 // blocks: the layer's segment table for this walk (snack_coo_desc.row_blocks / col_blocks), or
-// NULL to build it in the workspace first.
+// NULL to build it in the workspace first.  act: the batch-major operand [B][opnd_rows], in the
+// output's type.
 template <typename OutT>
 int launch_tile(const SpmmPlan &p, int64_t nkeys, const int32_t *offs, const int32_t *gidx, const float *vals,
-                const int32_t *perm, const int32_t *blocks, const float *opnd, int64_t opnd_rows, int64_t B,
+                const int32_t *perm, const int32_t *blocks, const OutT *act, int64_t opnd_rows, int64_t B,
                 const float *bias, OutT *out, char *ws, hipStream_t st) {
     const int32_t *tab = blocks;
     float *part = reinterpret_cast<float *>(ws + p.off_part);
@@ -3019,9 +3057,9 @@ int launch_tile(const SpmmPlan &p, int64_t nkeys, const int32_t *offs, const int
     }
     int s;
     switch (p.ttb) {
-        case 16: s = launch_tile_vw<1>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
-        case 32: s = launch_tile_vw<2>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
-        case 64: s = launch_tile_vw<4>(p, nkeys, tab, gidx, vals, perm, opnd, opnd_rows, part, st); break;
+        case 16: s = launch_tile_vw<1>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st); break;
+        case 32: s = launch_tile_vw<2>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st); break;
+        case 64: s = launch_tile_vw<4>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st); break;
         default: return fail(SNACK_ERR_INTERNAL, "tile: unsupported batch tile %d", p.ttb);
     }
     if (s) return s;
@@ -3041,12 +3079,15 @@ int launch_tile(const SpmmPlan &p, int64_t nkeys, const int32_t *offs, const int
 }
 
 // The gather-reduce shared by the forward (row order) and the input gradient
-// (column view).  nkeys = number of outputs per batch row; offs [nkeys+1].
+// (column view).  nkeys = number of outputs per batch row; offs [nkeys+1].  opnd: the batch-major
+// activation (in the output's type) where the plan reads it in place (p.direct), else its fp32
+// feature-major copy.
 template <typename OutT>
 int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys, const int32_t *offs,
-             const int32_t *gidx, const float *vals, const int32_t *perm, const float *opnd, int64_t opnd_rows,
+             const int32_t *gidx, const float *vals, const int32_t *perm, const void *opnd_any, int64_t opnd_rows,
              int64_t B, const float *bias, OutT *out, char *ws, hipStream_t st, const int32_t *blocks) {
     if (nkeys == 0 || B == 0) return SNACK_OK;
+    const float *opnd = static_cast<const float *>(opnd_any);
     if (p.mapping == kTile) {
         if (p.cvals && perm) {  // several batch tiles: the values gathered into walk order once
             float *cv = reinterpret_cast<float *>(ws + p.off_cvals);
@@ -3054,7 +3095,8 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
             vals = cv;
             perm = nullptr;
         }
-        return launch_tile<OutT>(p, nkeys, offs, gidx, vals, perm, blocks, opnd, opnd_rows, B, bias, out, ws, st);
+        return launch_tile<OutT>(p, nkeys, offs, gidx, vals, perm, blocks, static_cast<const OutT *>(opnd_any),
+                                 opnd_rows, B, bias, out, ws, st);
     }
     if (p.mapping == kRowwave) {
         probe(true, st);
@@ -3197,7 +3239,7 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
                 return s;
             return snack::ok();
         }
-        const float *xt = static_cast<const float *>(X);
+        const void *xt = X;
         if (!p.direct) {
             float *dst = reinterpret_cast<float *>(ws + p.off_opnd);
             if (int s = launch_to_feature_major(X, act_dtype, batch, I, dst, st, nullptr, 0, nullptr, p.bpad)) return s;
@@ -3312,7 +3354,7 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
             if (int s = check_hip("dx_reduce_kernel")) return s;
             return snack::ok();
         }
-        const float *dyt = static_cast<const float *>(dY);
+        const void *dyt = dY;
         if (!p.direct) {
             float *dst = reinterpret_cast<float *>(ws + p.off_opnd);
             if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st, nullptr, 0, nullptr, p.bpad))
@@ -3400,6 +3442,12 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             if (int s = check_hip("csr1_dw_kernel")) return s;
             return snack::ok();
         }
+        if (p.tile) {
+            if (int s = launch_tile_sddmm(p, W, X, dY, batch, act_dtype, dW,
+                                          reinterpret_cast<int32_t *>(ws + p.off_tab), st))
+                return s;
+            return finish();
+        }
         const float *xt = static_cast<const float *>(X);
         const float *dyt = static_cast<const float *>(dY);
         if (!p.x_direct) {
@@ -3412,11 +3460,6 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             if (int s = launch_to_feature_major(dY, act_dtype, batch, O, dst, st, nullptr, 0, nullptr, p.bpad))
                 return s;
             dyt = dst;
-        }
-        if (p.tile) {
-            if (int s = launch_tile_sddmm(p, W, xt, dyt, dW, reinterpret_cast<int32_t *>(ws + p.off_tab), st))
-                return s;
-            return finish();
         }
         const int64_t blocks = round_up8(ceil_div(p.waves, kWavesPerBlock));
         const dim3 grid(static_cast<unsigned>(blocks));
@@ -3557,9 +3600,9 @@ int launch_colbwd(const BwdPlan &p, hipStream_t st, int64_t I, const snack_coo_d
 
 }  // namespace
 
-// Both gradients tiled (BwdPlan.split): db, one launch for the feature-major copies of X and dY,
-// the input gradient over the column view (values through col_perm), the weight gradient over
-// the row view.  The timing probe brackets both gradients' kernels.
+// Both gradients tiled (BwdPlan.split): db, the input gradient over the column view (values
+// through col_perm), the weight gradient over the row view; the tiles read X and dY in place.
+// The timing probe brackets both gradients' kernels.
 static int run_split_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *X, const void *dY, int64_t batch,
                   int act_dtype, void *dX, float *db, float *dW, char *ws, hipStream_t st) {
     const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
@@ -3573,18 +3616,17 @@ static int run_split_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *
                                static_cast<const bf16_t *>(dY), db);
         if (int s = check_hip("bias_grad_kernel")) return s;
     }
-    float *xt = reinterpret_cast<float *>(ws + p.off_x);
-    float *dyt = reinterpret_cast<float *>(ws + p.off_dy);
-    if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st, dY, O, dyt, p.bpad)) return s;
     probe(true, st);
     ++g_probe_mute;
     int s = act_dtype == SNACK_F32
-                ? run_spmm<float>(p.sp, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dyt,
+                ? run_spmm<float>(p.sp, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm, dY,
                                   O, batch, nullptr, static_cast<float *>(dX), ws + p.off_spmm, st, W->col_blocks)
                 : run_spmm<bf16_t>(p.sp, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, W->col_perm,
-                                   dyt, O, batch, nullptr, static_cast<bf16_t *>(dX), ws + p.off_spmm, st,
+                                   dY, O, batch, nullptr, static_cast<bf16_t *>(dX), ws + p.off_spmm, st,
                                    W->col_blocks);
-    if (!s) s = launch_tile_sddmm(p.sd, W, xt, dyt, dW, reinterpret_cast<int32_t *>(ws + p.off_sddmm), st);
+    if (!s)
+        s = launch_tile_sddmm(p.sd, W, X, dY, batch, act_dtype, dW, reinterpret_cast<int32_t *>(ws + p.off_sddmm),
+                              st);
     --g_probe_mute;
     if (s) return s;
     probe(false, st);
