@@ -279,7 +279,12 @@ class SnackCOO:
         return W
 
 
+# Workspace of the calls made without one: a buffer per (device, stream), grown as needed.  Each
+# buffer is recorded on its stream, so when a larger one replaces it the allocator reuses its memory
+# only after the work queued there.  Calls under HIP graph capture get a buffer of their own that
+# is never released: the graph's replays keep using its address.
 _ws_cache = {}
+_ws_captured = []
 
 
 def _dtype_code(t) -> int:
@@ -291,23 +296,36 @@ def _dtype_code(t) -> int:
     raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
 
 
-def _stream_handle(device, stream):
+def _stream(device, stream):
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return stream if stream is not None else torch.cuda.current_stream(device)
 
 
-def _workspace(device, nbytes: int, workspace=None):
+def _stream_handle(device, stream):
+    return ctypes.c_void_p(_stream(device, stream).cuda_stream)
+
+
+def _workspace(device, nbytes: int, workspace=None, stream=None):
+    """(pointer, bytes) of the call's workspace: the caller's `workspace`, else the cached buffer of
+    (device, stream) (see _ws_cache)."""
     import torch
     if nbytes == 0:
         return None, 0
     if workspace is not None:
         return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
-    key = (str(device),)
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
+    s = _stream(device, stream)
+    with torch.cuda.stream(s):
+        capturing = torch.cuda.is_current_stream_capturing()
+        if capturing:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            _ws_captured.append(buf)
+            return ctypes.c_void_p(buf.data_ptr()), buf.numel()
+        key = (torch.device(device).index, s.cuda_stream)
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            buf.record_stream(s)
+            _ws_cache[key] = buf
     return ctypes.c_void_p(buf.data_ptr()), buf.numel()
 
 
@@ -334,7 +352,7 @@ def snack_coo_fwd(W: SnackCOO, X, bias=None, out=None, workspace=None, stream=No
     _check_act(Y, B, W.out_features, "Y")
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != W.out_features):
         raise ValueError("bias must be float32 [out_features]")
-    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_FWD, W, B, dt), workspace)
+    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_FWD, W, B, dt), workspace, stream)
     st = _lib.snack_coo_fwd(W.desc, ctypes.c_void_p(X.data_ptr()), B, dt,
                             None if bias is None else ctypes.c_void_p(bias.data_ptr()),
                             ctypes.c_void_p(Y.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
@@ -350,7 +368,7 @@ def snack_coo_bwd_input(W: SnackCOO, dY, out=None, db=None, workspace=None, stre
     dt = _dtype_code(dY)
     dX = out if out is not None else torch.empty((B, W.in_features), dtype=dY.dtype, device=dY.device)
     _check_act(dX, B, W.in_features, "dX")
-    ws, wsn = _workspace(dY.device, snack_coo_workspace_bytes(OP_BWD_INPUT, W, B, dt), workspace)
+    ws, wsn = _workspace(dY.device, snack_coo_workspace_bytes(OP_BWD_INPUT, W, B, dt), workspace, stream)
     st = _lib.snack_coo_bwd_input(W.desc, ctypes.c_void_p(dY.data_ptr()), B, dt, ctypes.c_void_p(dX.data_ptr()),
                                   None if db is None else ctypes.c_void_p(db.data_ptr()), ws, wsn,
                                   _stream_handle(dY.device, stream))
@@ -368,7 +386,7 @@ def snack_coo_grad_weight(W: SnackCOO, X, dY, out=None, workspace=None, stream=N
     if _dtype_code(dY) != dt:
         raise TypeError("X and dY must have the same dtype")
     dW = out if out is not None else torch.empty(W.nnz, dtype=torch.float32, device=X.device)
-    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_GRAD_WEIGHT, W, B, dt), workspace)
+    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_GRAD_WEIGHT, W, B, dt), workspace, stream)
     st = _lib.snack_coo_grad_weight(W.desc, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(dY.data_ptr()), B, dt,
                                     ctypes.c_void_p(dW.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
     _check(st, "snack_coo_grad_weight")
@@ -389,7 +407,7 @@ def snack_coo_bwd(W: SnackCOO, X, dY, dx_out=None, dw_out=None, db=None, workspa
     dX = dx_out if dx_out is not None else torch.empty((B, W.in_features), dtype=dY.dtype, device=dY.device)
     _check_act(dX, B, W.in_features, "dX")
     dW = dw_out if dw_out is not None else torch.empty(W.nnz, dtype=torch.float32, device=X.device)
-    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_BWD, W, B, dt), workspace)
+    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_BWD, W, B, dt), workspace, stream)
     st = _lib.snack_coo_bwd(W.desc, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(dY.data_ptr()), B, dt,
                             ctypes.c_void_p(dX.data_ptr()), None if db is None else ctypes.c_void_p(db.data_ptr()),
                             ctypes.c_void_p(dW.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
