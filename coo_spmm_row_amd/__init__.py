@@ -80,6 +80,7 @@ _lib.snack_coo_build.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _
 _lib.snack_coo_workspace_bytes.argtypes = [ctypes.c_int, _D, _i64, ctypes.c_int]
 _lib.snack_coo_workspace_bytes.restype = ctypes.c_size_t
 _lib.snack_coo_fwd.argtypes = [_D, _p, _i64, ctypes.c_int, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.snack_coo_fwd_noalloc.argtypes = [_D, _p, _i64, ctypes.c_int, _p, _p, _p]
 _lib.snack_coo_bwd_input.argtypes = [_D, _p, _i64, ctypes.c_int, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.snack_coo_grad_weight.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, ctypes.c_size_t, _p]
 _lib.snack_coo_bwd.argtypes = [_D, _p, _p, _i64, ctypes.c_int, _p, _p, _p, _p, ctypes.c_size_t, _p]
@@ -101,8 +102,8 @@ _lib.snack_coo_get_option.argtypes = [ctypes.c_int]
 _lib.snack_coo_get_option.restype = _i64
 SNACK_VIEW_ROWS, SNACK_VIEW_COLS = 0, 1
 
-EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_bwd_input",
-            "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_coo_init_uniform",
+EXPORTED = ("snack_coo_build", "snack_coo_workspace_bytes", "snack_coo_fwd", "snack_coo_fwd_noalloc",
+            "snack_coo_bwd_input", "snack_coo_grad_weight", "snack_coo_bwd", "snack_coo_topology_update", "snack_coo_init_uniform",
             "snack_coo_topology_update_device", "snack_coo_topology_workspace_bytes", "snack_last_error",
             "snack_coo_abi_version", "snack_coo_set_probe", "snack_coo_invert_perm", "snack_coo_gather_f32",
             "snack_coo_block_offsets_count", "snack_coo_block_offsets", "snack_coo_bwd_is_fused",
@@ -358,6 +359,28 @@ def snack_coo_fwd(W: SnackCOO, X, bias=None, out=None, workspace=None, stream=No
                             ctypes.c_void_p(Y.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
     _check(st, "snack_coo_fwd")
     return Y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def snack_coo_fwd_noalloc(W: SnackCOO, X, out, bias=None, stream=None):
+    """snack_coo_fwd with its workspace in the library's static device scratch (nothing allocated:
+    ``out`` is required).  Calls on one device share the scratch and must not overlap."""
+    import torch
+    _check_act(X, None, W.in_features, "X")
+    B = X.shape[0]
+    dt = _dtype_code(X)
+    _check_act(out, B, W.out_features, "Y")
+    if out.dtype != X.dtype:
+        raise TypeError("Y must have X's dtype")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != W.out_features):
+        raise ValueError("bias must be float32 [out_features]")
+    st = _lib.snack_coo_fwd_noalloc(W.desc, ctypes.c_void_p(X.data_ptr()), B, dt,
+                                    None if bias is None else ctypes.c_void_p(bias.data_ptr()),
+                                    ctypes.c_void_p(out.data_ptr()), _stream_handle(X.device, stream))
+    _check(st, "snack_coo_fwd_noalloc")
+    return out
 
 
 def snack_coo_bwd_input(W: SnackCOO, dY, out=None, db=None, workspace=None, stream=None):

@@ -44,6 +44,7 @@
 #include <cstdlib>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/snack_coo.h"
 #include "internal.h"
@@ -3255,6 +3256,58 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         return s ? s : snack::ok();
     } catch (...) {
         return fail(SNACK_ERR_INTERNAL, "snack_coo_fwd: unexpected exception");
+    }
+}
+
+// Workspace of snack_coo_fwd_noalloc: every device the library runs on holds its own copy.  Host
+// code never passes the array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[SNACK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, looked up on its first use on that device.
+int scratch_address(void **out, const char *who) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return check_hip(who);
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(SNACK_ERR_INTERNAL, "%s: device %d beyond the %d the scratch table holds", who, dev,
+                    kScratchDevices);
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_acquire);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return fail(SNACK_ERR_HIP, "%s: address of the static scratch on device %d: %s", who, dev,
+                            hipGetErrorString(e));
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SNACK_OK;
+}
+}  // namespace
+
+extern "C" int snack_coo_fwd_noalloc(const snack_coo_desc *W, const void *X, int64_t batch, int act_dtype,
+                                     const float *bias, void *Y, void *hip_stream) {
+    try {
+        const char *who = "snack_coo_fwd_noalloc";
+        const size_t need = snack_coo_workspace_bytes(SNACK_OP_FWD, W, batch, act_dtype);
+        // need == 0: no workspace, or invalid arguments, which snack_coo_fwd reports
+        if (need == 0) return snack_coo_fwd(W, X, batch, act_dtype, bias, Y, nullptr, 0, hip_stream);
+        if (need > SNACK_NOALLOC_SCRATCH_BYTES)
+            return fail(SNACK_ERR_WORKSPACE, "%s: this call needs %zu bytes of workspace, more than the %zu of the static scratch",
+                        who, need, static_cast<size_t>(SNACK_NOALLOC_SCRATCH_BYTES));
+        void *ws = nullptr;
+        if (int s = scratch_address(&ws, who)) return s;
+        return snack_coo_fwd(W, X, batch, act_dtype, bias, Y, ws, SNACK_NOALLOC_SCRATCH_BYTES, hip_stream);
+    } catch (...) {
+        return fail(SNACK_ERR_INTERNAL, "snack_coo_fwd_noalloc: unexpected exception");
     }
 }
 

@@ -169,6 +169,19 @@ int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t batch, int act
                   const float *bias, void *Y,
                   void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* snack_coo_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels and results, with the
+ * workspace taken from a static device array of SNACK_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every device it runs on until the process ends.  The call allocates nothing; on its
+ * first call on a device (with that device current) it looks up that device's copy of the array.
+ * A call that needs more than SNACK_NOALLOC_SCRATCH_BYTES of workspace (snack_coo_workspace_bytes
+ * with SNACK_OP_FWD) returns SNACK_ERR_WORKSPACE and launches nothing.  Every call on one device
+ * shares the array: calls whose work overlaps on a device (other streams, other threads) race and
+ * must be ordered by the caller. */
+#define SNACK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int snack_coo_fwd_noalloc(const snack_coo_desc *W, const void *X, int64_t batch, int act_dtype,
+                          const float *bias, void *Y, void *hip_stream);
+
 /* Input gradient (Section 3.4 / Appendix F: dL/dX = W^T dL/dA, with W^T
  * obtained by swapping the row and column index arrays):
  * dX[b,i] = sum_{k: cols[k]=i} vals[k] dY[b,rows[k]].
@@ -313,11 +326,11 @@ int snack_coo_set_probe(void *start_event, void *stop_event);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *snack_last_error(void);
 
-/* ABI version of this header: 7.  3 added snack_coo_init_uniform, 4 the device topology update,
+/* ABI version of this header: 8.  3 added snack_coo_init_uniform, 4 the device topology update,
  * 5 values in column order (snack_coo_desc.row_to_col, snack_coo_invert_perm, snack_coo_gather_f32),
  * 6 the segment tables (snack_coo_desc.row_blocks / col_blocks, snack_coo_block_offsets_count,
  * snack_coo_block_offsets), 7 the kernel-selection options (snack_coo_set_option,
- * snack_coo_get_option) in place of environment variables. */
+ * snack_coo_get_option) in place of environment variables, 8 snack_coo_fwd_noalloc. */
 int snack_coo_abi_version(void);
 
 /* Kernel-selection overrides for tests and measurement (not part of the method).  Process-wide,

@@ -16,7 +16,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     lib = ctypes.CDLL(snk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -29,7 +29,7 @@ def test_abi_version():
                             "snack_coo.h")).read()
     m = re.search(r"ABI version of this header: (\d+)", hdr)
     assert m, "header states no ABI version"
-    assert snk.abi_version() == int(m.group(1)) == 7
+    assert snk.abi_version() == int(m.group(1)) == 8
 
 
 def test_binding_loads_only_the_in_tree_library():
@@ -72,6 +72,22 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
                              None) == 7
     assert lib.snack_coo_bwd(ctypes.byref(d), 0x1000, 0x1000, 16, 0, 0x1000, None, None, 0x10000, need,
                              None) == 1  # dW NULL
+
+
+def test_noalloc_forward_rejects_before_any_launch():
+    """snack_coo_fwd_noalloc: invalid arguments come back as from snack_coo_fwd, and a call whose
+    workspace would exceed the static scratch returns SNACK_ERR_WORKSPACE (no GPU touched)."""
+    lib = snk._lib
+    assert lib.snack_coo_fwd_noalloc(None, None, 1, 0, None, None, None) == 1  # NULL descriptor
+    d = snk._Desc()
+    d.out_features, d.in_features, d.nnz = 4, 4, 20  # nnz > O*I
+    assert lib.snack_coo_fwd_noalloc(ctypes.byref(d), None, 1, 0, None, None, None) == 2
+    d.out_features, d.in_features, d.nnz = 300, 100_000, 3
+    d.rows = d.cols = d.vals = d.row_offsets = 0x1000
+    need = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 256, 0)
+    assert need > snk.NOALLOC_SCRATCH_BYTES
+    assert lib.snack_coo_fwd_noalloc(ctypes.byref(d), 0x1000, 256, 0, None, 0x2000, None) == 7
+    assert b"static scratch" in lib.snack_last_error()
 
 
 def test_one_hip_runtime_in_process():
