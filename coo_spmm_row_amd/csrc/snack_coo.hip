@@ -497,10 +497,12 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
 // tiles of (a range of keys) x (a block of cw operand rows); a 1024-thread workgroup stages its
 // block of the feature-major operand (cw rows of 64 batch columns, 256 B each, plus one zero
 // row: up to 160 KB, gfx950's LDS) once, then walks its keys' segments inside the block.  The
-// segments are found in a per-(key, block) offset table (tile_bounds_kernel; the triple is
-// sorted by key, then by gather index, so each segment is a contiguous run of the key's
-// entries).  Each tile writes fp32 partial sums part[bt][cb][key][64]; tile_sum_kernel adds the
-// blocks in block order, adds the bias and transposes to the batch-major output.
+// segments come from a per-block segment list (tile_segments_kernel; the triple is sorted by key,
+// then by gather index, so each segment is a contiguous run of the key's entries), whose keys are
+// ordered by segment length within windows of kSegWindow keys: the four keys a wave walks together
+// have segments of about the same length, so little of the walk is padding.  Each tile writes fp32
+// partial sums part[bt][cb][key][64]; tile_sum_kernel adds the blocks in block order, adds the
+// bias and transposes to the batch-major output.
 //
 // Lanes: 4 slots of 16 lanes; slot s walks key 4*g + s of the wave's group g, and each lane holds
 // VW batch columns (VW floats) of a TB = 16*VW column batch tile (64 for batches padded to a
@@ -564,15 +566,20 @@ __device__ __forceinline__ float vget(const float4 &v, int i) {
 
 // Staged rows of the tiled walks that read the activations in place (tile_spmm_kernel,
 // tile_sddmm_kernel): row r holds TB = 16 VW fp32 batch columns as NQ = TB / 4 chunks of 16 bytes,
-// chunk q (columns 4q .. 4q+3) at chunk position q ^ (r & (NQ - 1)).  Staging writes one chunk per
-// thread for consecutive rows, so the swizzle spreads a wave's writes over the banks; a slot reads
-// one whole row, so its reads stay conflict-free.  Lane byte offsets below 16 * NQ and row offsets
-// that are multiples of 16 * NQ combine as row_off(r) ^ lane_off, row_off(r) = r * 16 NQ +
-// 16 (r & (NQ - 1)): the XOR replaces the address add of an unswizzled row.
+// chunk q (columns 4q .. 4q+3) at chunk position q ^ (r & kSwz).  Staging writes one chunk per
+// thread for consecutive rows; unswizzled, those writes would all hit the same four banks.  On
+// gfx950 a 128-bit LDS read by four slots of 16 lanes, each slot reading one row, runs at the full
+// rate only while the slots' chunk positions differ in their two low bits at most (measured: XOR of
+// the low two bits 232 B/clk/CU; XOR of all four bits by row 169; the writes reach 62 of at most
+// 72 B/clk/CU with the low two bits), hence kSwz = 3.  Lane byte offsets below 16 NQ and row
+// offsets that are multiples of 16 NQ combine as row_off(r) ^ lane_off, row_off(r) = r * 16 NQ +
+// 16 (r & kSwz): the XOR replaces the address add of an unswizzled row.
+constexpr int kSwz = 3;
+
 template <int VW>
 __device__ __forceinline__ uint32_t tile_row_off(int r) {
     constexpr int NQ = 4 * VW;
-    return static_cast<uint32_t>(r) * (16u * NQ) + 16u * static_cast<uint32_t>(r & (NQ - 1));
+    return static_cast<uint32_t>(r) * (16u * NQ) + 16u * static_cast<uint32_t>(r & kSwz);
 }
 
 // Buffer resource over an activation of n elements (fp32 or bf16) and a load of one element,
@@ -615,7 +622,7 @@ __device__ __forceinline__ void tile_stage_rows(float4 *xs4, __amdgpu_buffer_rsr
         for (int u = 0; u < kRound && it0 + u < kIters; ++u) {
             const int i = (it0 + u) * kTileThreads + static_cast<int>(threadIdx.x);
             const int q = i / kStride, c = i - q * kStride;
-            at[u] = q < NQ && c <= cw ? c * NQ + (q ^ (c & (NQ - 1))) : -1;
+            at[u] = q < NQ && c <= cw ? c * NQ + (q ^ (c & kSwz)) : -1;
             const int off = q < NQ && c < cn ? ((TB * bt + 4 * q) * ld + r0 + c) * kEs : kBufPast;
             const int step = off == kBufPast ? 0 : ld * kEs;
             v[u] = make_float4(act_ld<InT>(ra, off), act_ld<InT>(ra, off + step), act_ld<InT>(ra, off + 2 * step),
@@ -673,27 +680,58 @@ __device__ __forceinline__ void tile_chunk(float (&acc)[VW], uint32_t off, float
     }
 }
 
-// tab[key][j] = first entry of the key at or past gather index j*cw (j = 0..ncb): the segment of
-// block j is [tab[key][j], tab[key][j+1]).
-__global__ __launch_bounds__(kBlock) void tile_bounds_kernel(int nkeys, int ncb, int cw,
-                                                             const int32_t *__restrict__ offs,
-                                                             const int32_t *__restrict__ gidx,
-                                                             int32_t *__restrict__ tab) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (i >= static_cast<int64_t>(nkeys) * (ncb + 1)) return;
-    const int key = static_cast<int>(i / (ncb + 1)), j = static_cast<int>(i % (ncb + 1));
-    int lo = offs[key], hi = offs[key + 1];
-    if (j > 0 && j < ncb) {
-        const int c = j * cw;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (gidx[mid] < c) lo = mid + 1;
-            else hi = mid;
-        }
-    } else if (j == ncb) {
-        lo = hi;
+// Segment lists: seg[j][p] (int32 x 4) = {key, start, end, 0} for block j (gather indices
+// [j cw, j cw + cw)) and list position p: the key's entries in the block are [start, end).  Within
+// each window of kSegWindow positions [w kSegWindow, w kSegWindow + kSegWindow) the keys are those
+// of the same window, by decreasing end - start, equal lengths by increasing key.  One wave per
+// (block, window): lane l finds key w kSegWindow + l's segment by binary search and its rank by
+// comparing with every other lane's length.
+constexpr int kSegWindow = 32;  // 32 consecutive keys: one 128-byte line of a batch-major row
+
+__device__ __forceinline__ int first_at_or_past(const int32_t *__restrict__ gidx, int lo, int hi, int c) {
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (gidx[mid] < c) lo = mid + 1;
+        else hi = mid;
     }
-    tab[i] = lo;
+    return lo;
+}
+
+__global__ __launch_bounds__(kBlock) void tile_segments_kernel(int nkeys, int ncb, int cw,
+                                                               const int32_t *__restrict__ offs,
+                                                               const int32_t *__restrict__ gidx,
+                                                               int4 *__restrict__ seg) {
+    const int nwin = (nkeys + kSegWindow - 1) / kSegWindow;
+    const int64_t wv = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) / kWave;  // uniform per wave
+    if (wv >= static_cast<int64_t>(ncb) * nwin) return;
+    const int j = static_cast<int>(wv / nwin), w = static_cast<int>(wv % nwin);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int key = w * kSegWindow + lane;
+    const bool real = lane < kSegWindow && key < nkeys;
+    int a = 0, e = 0, len = -1;  // lanes without a key rank after every real one
+    if (real) {
+        const int lo = offs[key], hi = offs[key + 1];
+        a = j == 0 ? lo : first_at_or_past(gidx, lo, hi, j * cw);
+        e = j == ncb - 1 ? hi : first_at_or_past(gidx, a, hi, (j + 1) * cw);
+        len = e - a;
+    }
+    int rank = 0;
+    for (int m = 0; m < kSegWindow; ++m) {
+        const int lm = __builtin_amdgcn_readlane(len, m);
+        rank += (lm > len) || (lm == len && m < lane);
+    }
+    if (real) seg[static_cast<int64_t>(j) * nkeys + w * kSegWindow + rank] = make_int4(key, a, e, 0);
+}
+
+// Segment of list position pos of block cb (seg: the int4 records above as int32s, rs its buffer
+// resource; nothing past the tile: pos_ok false gives key 0 and an empty segment).
+__device__ __forceinline__ void seg_load(__amdgpu_buffer_rsrc_t rs, int cb, int nkeys, int pos, bool pos_ok,
+                                         int &key, int &a, int &len) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const v4i r = __builtin_amdgcn_raw_buffer_load_b128(rs, pos_ok ? (cb * nkeys + pos) * 16 : kBufPast, 0, 0);
+    key = r.x;
+    a = r.y;
+    len = r.z - r.y;
 }
 
 // act: the batch-major activation [B][opnd_rows] (fp32 or bf16, B * opnd_rows * its size < 2^31),
@@ -705,7 +743,7 @@ __global__ __launch_bounds__(kBlock) void tile_bounds_kernel(int nkeys, int ncb,
 // indices two groups ahead, the values it points at one group ahead.
 template <int VW, int CH, bool VP, typename InT>
 __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
-    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
+    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ segs,
     const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm, int nnz,
     const InT *__restrict__ act, int opnd_rows, int64_t B, float *__restrict__ part) {
     constexpr int SL = 4;                      // slots (keys) per wave, 16 lanes each
@@ -741,17 +779,15 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     // through buffer resources: lanes past a segment load from past the buffers' end, so nothing
     // is read for them.
     const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
-    const __amdgpu_buffer_rsrc_t rt = buf_rsrc(tab, nkeys * (ncb + 1));
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
     auto claim = [&]() {
         unsigned g = 0;
         if (lane == 0) g = atomicAdd(claims, 1u);
         return static_cast<int>(__builtin_amdgcn_readfirstlane(g));
     };
-    auto seg = [&](int G, int &a, int &len) {  // this slot's segment of group G (none past the tile)
-        const int key = k_lo + SL * G + slot;
-        const int off = G < ngroups && key < k_hi ? (key * (ncb + 1) + cb) * 4 : kBufPast;
-        a = buf_ld(rt, off);
-        len = buf_ld(rt, off == kBufPast ? kBufPast : off + 4) - a;
+    auto seg = [&](int G, int &key, int &a, int &len) {  // this slot's segment of group G (none past the tile)
+        const int pos = k_lo + SL * G + slot;
+        seg_load(rs, cb, nkeys, pos, G < ngroups && pos < k_hi, key, a, len);
     };
     auto load_chunks = [&](int a, int len, int (&gi)[CH], int (&vv)[CH]) {
         const int base = (a + j) * 4;
@@ -770,8 +806,8 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         return max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
                    max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
     };
-    auto compute = [&](int G, int a, int len, const int (&gi)[CH], const int (&vv)[CH]) {
-        const int key = k_lo + SL * G + slot;
+    auto compute = [&](int G, int key, int a, int len, const int (&gi)[CH], const int (&vv)[CH]) {
+        const int pos = k_lo + SL * G + slot;
         const int m = group_len(len);
         float acc[VW];
 #pragma unroll
@@ -796,7 +832,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         // use, refilling them would wait for loads issued after them
 #pragma unroll
         for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]));
-        if (key < k_hi) {
+        if (pos < k_hi) {
             typedef typename TileVec<VW>::T V;
             V r;
             if constexpr (VW == 1) r = acc[0];
@@ -807,11 +843,11 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     };
     // ring of claimed groups: [0] computed now, [1] next, ..., [D-1] claimed this phase
     constexpr int D = VP ? 4 : 3;
-    int Gs[D], As[D], Ls[D];
+    int Gs[D], Ks[D], As[D], Ls[D];
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) {
         Gs[i] = claim();
-        seg(Gs[i], As[i], Ls[i]);
+        seg(Gs[i], Ks[i], As[i], Ls[i]);
     }
     int gA[CH], gB[CH], gC[CH], pA[CH], pB[CH], pC[CH], vA[CH], vB[CH], vC[CH];
     if constexpr (VP) {
@@ -826,17 +862,18 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
     auto phase = [&](int (&gc)[CH], int (&vc)[CH], int (&gn)[CH], int (&pn)[CH], int (&vn)[CH],
                      int (&gnn)[CH], int (&pnn)[CH]) {
         Gs[D - 1] = claim();
-        seg(Gs[D - 1], As[D - 1], Ls[D - 1]);
+        seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
         if constexpr (VP) {
             load_chunks(As[2], Ls[2], gnn, pnn);
             load_vals(pn, Ls[1], vn);
         } else {
             load_chunks(As[1], Ls[1], gn, vn);
         }
-        compute(Gs[0], As[0], Ls[0], gc, vc);
+        compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc);
 #pragma unroll
         for (int i = 0; i + 1 < D; ++i) {
             Gs[i] = Gs[i + 1];
+            Ks[i] = Ks[i + 1];
             As[i] = As[i + 1];
             Ls[i] = Ls[i + 1];
         }
@@ -902,7 +939,7 @@ __device__ __forceinline__ void tile_dot_chunk(float (&p)[16], uint32_t off, int
 // size < 2^31 (32-bit buffer offsets).
 template <int VW, int CH, typename InT>
 __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
-    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, int nbt, const int32_t *__restrict__ tab,
+    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, int nbt, const int32_t *__restrict__ segs,
     const int32_t *__restrict__ gidx, int nnz, const InT *__restrict__ x, int opnd_rows,
     const InT *__restrict__ dy_act, int64_t B, float *__restrict__ dw) {
     constexpr int SL = 4;
@@ -926,7 +963,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
     unsigned *claims = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(xs4) + (cw + 1) * kRowBytes);
     const char *lds = reinterpret_cast<const char *>(xs4);
     const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz);
-    const __amdgpu_buffer_rsrc_t rt = buf_rsrc(tab, nkeys * (ncb + 1));
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
     const __amdgpu_buffer_rsrc_t rx = act_rsrc(x, static_cast<int>(B) * opnd_rows);
     const __amdgpu_buffer_rsrc_t rdy = act_rsrc(dy_act, static_cast<int>(B) * nkeys);
     auto claim = [&]() {
@@ -934,11 +971,9 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
         if (lane == 0) g = atomicAdd(claims, 1u);
         return static_cast<int>(__builtin_amdgcn_readfirstlane(g));
     };
-    auto seg = [&](int G, int &a, int &len) {  // this slot's segment of group G (none past the tile)
-        const int key = k_lo + SL * G + slot;
-        const int off = G < ngroups && key < k_hi ? (key * (ncb + 1) + cb) * 4 : kBufPast;
-        a = buf_ld(rt, off);
-        len = buf_ld(rt, off == kBufPast ? kBufPast : off + 4) - a;
+    auto seg = [&](int G, int &key, int &a, int &len) {  // this slot's segment of group G (none past the tile)
+        const int pos = k_lo + SL * G + slot;
+        seg_load(rs, cb, nkeys, pos, G < ngroups && pos < k_hi, key, a, len);
     };
     for (int bt = 0; bt < nbt; ++bt) {
         if (bt > 0) __syncthreads();  // the previous batch tile's reads of the block (and claims) are done
@@ -946,8 +981,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
         if (threadIdx.x == 0) *claims = 0u;
         __syncthreads();
         // a group's chunks of gather indices and its rows' dY slices, one group after its claim
-        auto load_group = [&](int G, int a, int len, int (&gi)[CH], V &dy) {
-            const int key = min(k_lo + SL * G + slot, nkeys - 1);
+        auto load_group = [&](int key, int a, int len, int (&gi)[CH], V &dy) {
             const int base = (a + j) * 4;
 #pragma unroll
             for (int c = 0; c < CH; ++c) gi[c] = buf_ld(rg, 16 * c + j < len ? base + 64 * c : kBufPast);
@@ -991,21 +1025,21 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
             for (int i = 0; i < VW; ++i) asm volatile("" ::"v"(vget(dy, i)));
         };
         // ring of claimed groups: [0] computed now, [1] its loads in flight, [2] claimed this phase
-        int Gs[3], As[3], Ls[3];
+        int Gs[3], Ks[3], As[3], Ls[3];
         Gs[0] = claim();
-        seg(Gs[0], As[0], Ls[0]);
+        seg(Gs[0], Ks[0], As[0], Ls[0]);
         Gs[1] = claim();
-        seg(Gs[1], As[1], Ls[1]);
+        seg(Gs[1], Ks[1], As[1], Ls[1]);
         int gA[CH], gB[CH], gC[CH];
         V dA, dB, dC;
-        load_group(Gs[0], As[0], Ls[0], gA, dA);
+        load_group(Ks[0], As[0], Ls[0], gA, dA);
         auto phase = [&](int (&gc)[CH], V &dc, int (&gn)[CH], V &dn) {
             Gs[2] = claim();
-            seg(Gs[2], As[2], Ls[2]);
-            load_group(Gs[1], As[1], Ls[1], gn, dn);
+            seg(Gs[2], Ks[2], As[2], Ls[2]);
+            load_group(Ks[1], As[1], Ls[1], gn, dn);
             compute(As[0], Ls[0], gc, dc);
-            Gs[0] = Gs[1], As[0] = As[1], Ls[0] = Ls[1];
-            Gs[1] = Gs[2], As[1] = As[2], Ls[1] = Ls[2];
+            Gs[0] = Gs[1], Ks[0] = Ks[1], As[0] = As[1], Ls[0] = Ls[1];
+            Gs[1] = Gs[2], Ks[1] = Ks[2], As[1] = As[2], Ls[1] = Ls[2];
             return Gs[0] < ngroups;
         };
         if (Gs[0] < ngroups) {
@@ -1053,7 +1087,7 @@ __device__ __forceinline__ void tile_bwd_steps4(float (&acc)[VW], float (&p)[16]
 
 template <int VW, int CH, bool VP>
 __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
-    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ tab,
+    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ segs,
     const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm, int nnz,
     const float *__restrict__ opnd, int opnd_rows, int ld, const float *__restrict__ xt,
     float *__restrict__ part, float *__restrict__ dw) {
@@ -1075,14 +1109,11 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
     const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
     const int ngroups = (k_hi - k_lo + SL - 1) / SL;
     const int my_groups = wave < ngroups ? (ngroups - wave + kTileWaves - 1) / kTileWaves : 0;
-    const int key_l = k_lo + (wave + kTileWaves * (lane / SL)) * SL + lane % SL;
-    const bool key_l_ok = lane / SL < my_groups && key_l < k_hi;
-    int seg_a, seg_e;
-    {
-        const int64_t at = static_cast<int64_t>(key_l_ok ? key_l : k_lo) * (ncb + 1) + cb;
-        seg_a = tab[at];
-        seg_e = tab[at + 1];
-    }
+    // lane l holds the segment of this wave's group l / SL, slot l % SL (list positions)
+    const int pos_l = k_lo + (wave + kTileWaves * (lane / SL)) * SL + lane % SL;
+    const bool key_l_ok = lane / SL < my_groups && pos_l < k_hi;
+    int key_l, seg_a, seg_len;
+    seg_load(buf_rsrc(segs, nkeys * ncb * 4), cb, nkeys, pos_l, key_l_ok, key_l, seg_a, seg_len);
     {  // stage the block's rows of dY^T; rows cn..cw are zero (row cw is the zero row)
         constexpr int R4 = TB / 4;
         constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
@@ -1105,7 +1136,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
             }
         }
     }
-    const int s_len = key_l_ok ? seg_e - seg_a : 0, s_a = seg_a, s_key = key_l_ok ? key_l : -1;
+    const int s_len = key_l_ok ? seg_len : 0, s_a = seg_a, s_key = key_l_ok ? key_l : -1;
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(xs4);
     float *pout = part + static_cast<int64_t>(cb) * nkeys * TB;
@@ -2535,7 +2566,7 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     int64_t ncb, cw;
     tile_blocks(opnd_rows, ncb, cw);
     const double mean = static_cast<double>(nnz) / static_cast<double>(nkeys * ncb);
-    if (mean < 8.0 || nkeys * (ncb + 1) >= (int64_t(1) << 29)) return;
+    if (mean < 8.0 || nkeys * ncb * 4 >= (int64_t(1) << 29)) return;
     p.mapping = kTile;
     p.bpad = Bp;
     p.ttb = tb;
@@ -2551,7 +2582,7 @@ void plan_tile(SpmmPlan &p, int64_t nnz, int64_t opnd_rows, int64_t nkeys, int64
     size_t at = 0;
     p.off_opnd = at;
     p.off_tab = at;
-    at = align_up(at + sizeof(int32_t) * static_cast<size_t>(nkeys * (ncb + 1)));
+    at = align_up(at + 4 * sizeof(int32_t) * static_cast<size_t>(nkeys * ncb));
     p.off_part = at;
     at = align_up(at + sizeof(float) * static_cast<size_t>(Bp) * static_cast<size_t>(ncb) *
                            static_cast<size_t>(nkeys));
@@ -2670,7 +2701,7 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
         int64_t ncb, cw;
         tile_blocks(I, ncb, cw);
         const double mean = static_cast<double>(nnz) / static_cast<double>(O * ncb);
-        if (mean >= 8.0 && O * (ncb + 1) < (int64_t(1) << 29)) {
+        if (mean >= 8.0 && O * ncb * 4 < (int64_t(1) << 29)) {
             p.tile = true;
             p.ttb = tb;
             p.tnnz = static_cast<int>(nnz);
@@ -2697,7 +2728,7 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
     p.off_dw = at;
     if (colvals && nnz > 0 && !p.csr1) at = align_up(at + sizeof(float) * static_cast<size_t>(nnz));
     p.off_tab = at;
-    if (p.tile) at = align_up(at + sizeof(int32_t) * static_cast<size_t>(O * (p.tncb + 1)));
+    if (p.tile) at = align_up(at + 4 * sizeof(int32_t) * static_cast<size_t>(O * p.tncb));
     p.total = at;
     return p;
 }
@@ -2868,7 +2899,7 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
             p.off_spmm = at;
             at = align_up(at + sp.total);
             p.off_sddmm = at;
-            at = align_up(at + sizeof(int32_t) * static_cast<size_t>(O * (sd.tncb + 1)));
+            at = align_up(at + 4 * sizeof(int32_t) * static_cast<size_t>(O * sd.tncb));
             p.total = at;
             return p;
         }
@@ -2911,6 +2942,8 @@ int check_desc(const snack_coo_desc *W, bool need_colview, const char *who) {
                     who, W->row_to_col ? " with values in column order" : "");
     if (W->col_blocks && !W->col_offsets)
         return fail(SNACK_ERR_NULL, "%s: col_blocks needs the column view", who);
+    if (reinterpret_cast<uintptr_t>(W->row_blocks) % 16 || reinterpret_cast<uintptr_t>(W->col_blocks) % 16)
+        return fail(SNACK_ERR_ALIGN, "%s: row_blocks and col_blocks must be 16-byte aligned", who);
     return SNACK_OK;
 }
 
@@ -3016,7 +3049,9 @@ int launch_tile_kernel(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, con
 template <int VW, bool VP, typename InT>
 int launch_tile_ch(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const int32_t *gidx, const float *vals,
                    const int32_t *perm, const InT *act, int64_t opnd_rows, int64_t B, float *part, hipStream_t st) {
-    switch (p.tch) {
+    // 8 prefetched chunks with permuted values at 64 columns would spill registers; longer
+    // segments take their further chunks unprefetched there
+    switch (VW == 4 && VP ? std::min(p.tch, 4) : p.tch) {
         case 2: return launch_tile_kernel<VW, 2, VP>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st);
         case 4: return launch_tile_kernel<VW, 4, VP>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st);
         case 8: return launch_tile_kernel<VW, 8, VP>(p, nkeys, tab, gidx, vals, perm, act, opnd_rows, B, part, st);
@@ -3034,14 +3069,14 @@ int launch_tile_vw(const SpmmPlan &p, int64_t nkeys, const int32_t *tab, const i
 // The LDS-tiled gather-reduce: segment table, tiles, block sums (bias, transpose).
 int launch_bounds(int64_t nkeys, int ncb, int cw, const int32_t *offs, const int32_t *gidx, int32_t *tab,
                   hipStream_t st) {
-    const int64_t nt = nkeys * (ncb + 1);
-    if (nt == 0) return SNACK_OK;
-    hipLaunchKernelGGL(tile_bounds_kernel, dim3(static_cast<unsigned>(ceil_div(nt, kBlock))), dim3(kBlock), 0, st,
-                       static_cast<int>(nkeys), ncb, cw, offs, gidx, tab);
-    return check_hip("tile_bounds_kernel");
+    const int64_t waves = ceil_div(nkeys, kSegWindow) * ncb;
+    if (waves == 0) return SNACK_OK;
+    hipLaunchKernelGGL(tile_segments_kernel, dim3(static_cast<unsigned>(ceil_div(waves, kBlock / kWave))), dim3(kBlock),
+                       0, st, static_cast<int>(nkeys), ncb, cw, offs, gidx, reinterpret_cast<int4 *>(tab));
+    return check_hip("tile_segments_kernel");
 }
 
-// blocks: the layer's segment table for this walk (snack_coo_desc.row_blocks / col_blocks), or
+// blocks: the layer's segment lists for this walk (snack_coo_desc.row_blocks / col_blocks), or
 // NULL to build it in the workspace first.  act: the batch-major operand [B][opnd_rows], in the
 // output's type.
 template <typename OutT>
@@ -3889,7 +3924,7 @@ extern "C" int64_t snack_coo_block_offsets_count(const snack_coo_desc *W, int vi
     const int64_t keys = view == SNACK_VIEW_ROWS ? W->out_features : W->in_features;
     int64_t ncb, cw;
     tile_blocks(view == SNACK_VIEW_ROWS ? W->in_features : W->out_features, ncb, cw);
-    return keys * (ncb + 1);
+    return keys * ncb * 4;
 }
 
 extern "C" int snack_coo_block_offsets(const snack_coo_desc *W, int view, int32_t *out, void *hip_stream) {
@@ -3902,9 +3937,10 @@ extern "C" int snack_coo_block_offsets(const snack_coo_desc *W, int view, int32_
         const int64_t keys = rows ? W->out_features : W->in_features;
         if (keys == 0) return snack::ok();
         if (!out) return fail(SNACK_ERR_NULL, "%s: out is NULL", who);
+        if (reinterpret_cast<uintptr_t>(out) % 16) return fail(SNACK_ERR_ALIGN, "%s: out must be 16-byte aligned", who);
         int64_t ncb, cw;
         tile_blocks(rows ? W->in_features : W->out_features, ncb, cw);
-        if (keys * (ncb + 1) >= (int64_t(1) << 31)) return fail(SNACK_ERR_SHAPE, "%s: table too large", who);
+        if (keys * ncb * 4 >= (int64_t(1) << 31)) return fail(SNACK_ERR_SHAPE, "%s: table too large", who);
         if (int s = launch_bounds(keys, static_cast<int>(ncb), static_cast<int>(cw), rows ? W->row_offsets : W->col_offsets,
                                   rows ? W->cols : W->col_rows, out, static_cast<hipStream_t>(hip_stream)))
             return s;

@@ -96,14 +96,18 @@ enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2, SNACK
  *                             backward pass (a walk over the column view) read vals and
  *                             write dW contiguously, and moves one permuted read per entry
  *                             to the forward pass instead.  Requires the column view.
- *   row_blocks  [O*(nb_r+1)] NULL, or the row order cut into column blocks: nb_r =
- *                             ceil(I / 638) blocks of w_r = ceil(I / nb_r) columns, and
- *                             row_blocks[r*(nb_r+1) + j] = the first triple position of row r
- *                             whose column is >= j*w_r (j = nb_r: the row's end).  Each
+ *   row_blocks  [nb_r*O*4] NULL, or the row order cut into column blocks: nb_r =
+ *                             ceil(I / 638) blocks of w_r = ceil(I / nb_r) columns.  For
+ *                             block j and list position p, the four int32s at (j*O + p)*4 are
+ *                             {r, start, end, 0}: row r's entries with a column in
+ *                             [j*w_r, (j+1)*w_r) are the triple positions [start, end).  Each
  *                             (row, block) segment is the run of the row's entries whose
  *                             operand rows the tiled kernels stage together in LDS (Section
- *                             3.1's row-sorted triple makes it contiguous).
- *   col_blocks  [I*(nb_c+1)] NULL, or the same for the column view: nb_c = ceil(O / 638)
+ *                             3.1's row-sorted triple makes it contiguous).  Within each
+ *                             window of 32 positions [32w, 32w + 32) the rows are rows
+ *                             32w .. 32w + 31, by decreasing end - start, equal lengths by
+ *                             increasing row.  16-byte aligned.
+ *   col_blocks  [nb_c*I*4] NULL, or the same for the column view: nb_c = ceil(O / 638)
  *                             blocks of w_c = ceil(O / nb_c) rows, positions in column-view
  *                             order.  Requires the column view.
  *                             Both tables depend on the structure only (not on the values or
@@ -326,11 +330,12 @@ int snack_coo_set_probe(void *start_event, void *stop_event);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *snack_last_error(void);
 
-/* ABI version of this header: 8.  3 added snack_coo_init_uniform, 4 the device topology update,
+/* ABI version of this header: 9.  3 added snack_coo_init_uniform, 4 the device topology update,
  * 5 values in column order (snack_coo_desc.row_to_col, snack_coo_invert_perm, snack_coo_gather_f32),
  * 6 the segment tables (snack_coo_desc.row_blocks / col_blocks, snack_coo_block_offsets_count,
  * snack_coo_block_offsets), 7 the kernel-selection options (snack_coo_set_option,
- * snack_coo_get_option) in place of environment variables, 8 snack_coo_fwd_noalloc. */
+ * snack_coo_get_option) in place of environment variables, 8 snack_coo_fwd_noalloc, 9 segment
+ * tables as per-block lists of {key, start, end} ordered by length within windows of 32 keys. */
 int snack_coo_abi_version(void);
 
 /* Kernel-selection overrides for tests and measurement (not part of the method).  Process-wide,
@@ -351,7 +356,7 @@ int64_t snack_coo_get_option(int option);
 
 /* Segment tables of snack_coo_desc.row_blocks (view = SNACK_VIEW_ROWS) and
  * snack_coo_desc.col_blocks (view = SNACK_VIEW_COLS): the number of int32
- * entries, keys * (nb + 1) with keys = O and nb = ceil(I / 638) for the rows
+ * entries, nb * keys * 4 with keys = O and nb = ceil(I / 638) for the rows
  * (keys = I and nb = ceil(O / 638) for the column view; nb = 1 for an empty
  * dimension), or -1 with snack_last_error() set for a NULL descriptor or an
  * unknown view. */
@@ -363,7 +368,7 @@ int64_t snack_coo_block_offsets_count(const snack_coo_desc *W, int view);
  * col_offsets and col_rows (column view) of W; enqueued on hip_stream.  The
  * table stays valid while the structure does: rebuild it after a topology
  * update.  Errors: SNACK_ERR_NULL (W, out or a needed array NULL),
- * SNACK_ERR_DTYPE (unknown view), SNACK_ERR_HIP. */
+ * SNACK_ERR_ALIGN (out not 16-byte aligned), SNACK_ERR_DTYPE (unknown view), SNACK_ERR_HIP. */
 int snack_coo_block_offsets(const snack_coo_desc *W, int view, int32_t *out, void *hip_stream);
 
 #ifdef __cplusplus

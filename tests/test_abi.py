@@ -29,7 +29,7 @@ def test_abi_version():
                             "snack_coo.h")).read()
     m = re.search(r"ABI version of this header: (\d+)", hdr)
     assert m, "header states no ABI version"
-    assert snk.abi_version() == int(m.group(1)) == 8
+    assert snk.abi_version() == int(m.group(1)) == 9
 
 
 def test_binding_loads_only_the_in_tree_library():
@@ -162,24 +162,26 @@ def test_column_order_values_host_checks_and_workspace():
 
 
 def test_block_offsets_count_and_errors():
-    """Segment-table sizes: keys * (ceil(n / 638) + 1); argument errors come back before any launch."""
+    """Segment-list sizes: ceil(n / 638) blocks * keys * 4 int32s; argument errors come back before any
+    launch."""
     lib = snk._lib
     d = snk._Desc()
     d.out_features, d.in_features, d.nnz = 10000, 10000, 0
-    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 10000 * 17
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 16 * 10000 * 4
     d.out_features, d.in_features = 700, 638
-    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 2
-    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_COLS) == 638 * 3
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 1 * 700 * 4
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_COLS) == 2 * 638 * 4
     d.in_features = 639
-    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 3
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 2 * 700 * 4
     d.in_features = 0
-    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 700 * 2
+    assert lib.snack_coo_block_offsets_count(ctypes.byref(d), snk.SNACK_VIEW_ROWS) == 1 * 700 * 4
     assert lib.snack_coo_block_offsets_count(ctypes.byref(d), 5) == -1
     assert lib.snack_coo_block_offsets_count(None, 0) == -1
     d.in_features = 640
     d.row_offsets = 0x1000
     assert lib.snack_coo_block_offsets(ctypes.byref(d), 5, 0x1000, None) == 6      # unknown view
     assert lib.snack_coo_block_offsets(ctypes.byref(d), 0, None, None) == 1        # out NULL
+    assert lib.snack_coo_block_offsets(ctypes.byref(d), 0, 0x1008, None) == 5      # out misaligned
     assert lib.snack_coo_block_offsets(ctypes.byref(d), 1, 0x1000, None) == 1      # no column view
     assert lib.snack_coo_block_offsets(None, 0, 0x1000, None) == 1
 

@@ -233,9 +233,10 @@ def test_invariants_bias_determinism_scaling_permutation():
     # true sparsity: device bytes of the weight are 12 nnz + 4 (O+1) plus the column view
     nnz, O, I = L["nnz"], 700, 900
     assert W.device_bytes(blocks=False) == 12 * nnz + 4 * (O + 1) + 12 * nnz + 4 * (I + 1)
-    # plus the segment tables of the tiled kernels: (nb + 1) offsets per row and per column
+    # plus the segment lists of the tiled kernels: a 16-byte record per (row, block) and per
+    # (column, block)
     nb_r, nb_c = -(-I // 638), -(-O // 638)
-    assert W.device_bytes() == W.device_bytes(blocks=False) + 4 * (O * (nb_r + 1) + I * (nb_c + 1))
+    assert W.device_bytes() == W.device_bytes(blocks=False) + 16 * (O * nb_r + I * nb_c)
 
 
 def test_linearity_in_x():

@@ -164,21 +164,32 @@ def test_tiled_in_graph(layers):
 
 
 def _ref_blocks(offs, gidx, n):
-    """table[key][j] = first position of the key's run at or past gather index j*w (numpy)."""
+    """Segment lists (numpy): for block j (gather indices [j w, j w + w)) and list position p the
+    record {key, start, end, 0}; within each window of 32 positions the window's keys by decreasing
+    segment length, equal lengths by increasing key."""
     nb = max(1, -(-n // 638))
     w = max(1, -(-n // nb))
     keys = offs.size - 1
-    t = np.empty((keys, nb + 1), np.int64)
+    bounds = np.empty((keys, nb + 1), np.int64)
     for key in range(keys):
         a, e = int(offs[key]), int(offs[key + 1])
-        t[key] = a + np.searchsorted(gidx[a:e], np.arange(nb + 1) * w, side="left")
-        t[key, nb] = e
-    return t.ravel()
+        bounds[key] = a + np.searchsorted(gidx[a:e], np.arange(nb + 1) * w, side="left")
+        bounds[key, nb] = e
+    rec = np.zeros((nb, keys, 4), np.int64)
+    for j in range(nb):
+        lens = bounds[:, j + 1] - bounds[:, j]
+        for w0 in range(0, keys, 32):
+            ks = np.arange(w0, min(keys, w0 + 32))
+            order = ks[np.lexsort((ks, -lens[ks]))]
+            rec[j, w0:w0 + ks.size, 0] = order
+            rec[j, w0:w0 + ks.size, 1] = bounds[order, j]
+            rec[j, w0:w0 + ks.size, 2] = bounds[order, j + 1]
+    return rec.ravel()
 
 
 @pytest.mark.parametrize("name", ["e1100x7777", "d2000x4000", "u4000x600"])
 def test_block_tables_exact(layers, name):
-    """snack_coo_block_offsets (both views) equals a per-key search, bit for bit."""
+    """snack_coo_block_offsets (both views) equals a per-key search and sort, bit for bit."""
     L = layers[name]
     say(f"segment tables {name}")
     built, W = device_layer(L, DEV)
