@@ -251,38 +251,62 @@ def cold_kernel_times(layer, K, ops, flush_bytes=1 << 30):
     return res
 
 
-def cpu_baseline(layer, budget_s=15.0):
-    """The fp64 oracle on the first Bs batch rows of the same inputs, scaled to the full batch."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(layer, budget_s=15.0, single_budget_s=10.0):
+    """The fp64 oracle on the first Bs batch rows of the same inputs, scaled to the full batch: on
+    the host threads this process may use (at most 16, the CPU share of one GPU), and on one."""
     import oracle
-    nthreads = max(1, min(16, os.cpu_count() or 1))
+    nthreads = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                          else (os.cpu_count() or 1)))
     b = layer.built
     r, c, v = b["rows"], b["cols"], b["vals"]
     O, I, B = layer.O, layer.I, layer.B
     x = layer.x.astype(np.float64)
     dy = layer.dy.astype(np.float64)
 
-    def run(bs):
+    def run(bs, nt):
         t0 = time.perf_counter()
-        oracle.fwd(O, I, r, c, v, x[:bs], layer.L["bias"], nthreads=nthreads)
-        oracle.bwd_input(O, I, r, c, v, dy[:bs], nthreads=nthreads)
-        oracle.grad_weight(O, I, r, c, x[:bs], dy[:bs], nthreads=nthreads)
+        oracle.fwd(O, I, r, c, v, x[:bs], layer.L["bias"], nthreads=nt)
+        oracle.bwd_input(O, I, r, c, v, dy[:bs], nthreads=nt)
+        oracle.grad_weight(O, I, r, c, x[:bs], dy[:bs], nthreads=nt)
         return time.perf_counter() - t0
 
-    # grow the batch sample until one pass costs >= budget/8, then repeat passes to ~budget
-    bs = 1
-    t = run(bs)
-    while bs < B and t * 8 < budget_s:
-        bs = min(B, bs * 2)
-        t = run(bs)
-    reps, total = 1, t
-    while total < budget_s and reps < 2000:
-        total += run(bs)
-        reps += 1
-    us_per_step = total / reps * 1e6 * (B / bs)
-    return {"value": round(us_per_step, 1), "unit": "us/step (fwd+dX+dW)", "cores": nthreads,
+    def measure(nt, budget):
+        # grow the batch sample until one pass costs >= budget/8, then repeat passes to ~budget
+        bs = 1
+        t = run(bs, nt)
+        while bs < B and t * 8 < budget:
+            bs = min(B, bs * 2)
+            t = run(bs, nt)
+        reps, total = 1, t
+        while total < budget and reps < 2000:
+            total += run(bs, nt)
+            reps += 1
+        return total / reps * 1e6 * (B / bs), bs, reps, total
+
+    us, bs, reps, total = measure(nthreads, budget_s)
+    us1, bs1, reps1, total1 = measure(1, single_budget_s)
+    model = cpu_model()
+    return {"value": round(us, 1), "unit": "us/step (fwd+dX+dW)", "cores": nthreads,
             "kind": "oracle",
             "sample": f"fp64 oracle fwd+dX+dW on the first {bs} of {B} batch rows of the same layer, "
-                      f"{reps} passes ({total:.1f} s of CPU time), scaled by {B}/{bs}"}
+                      f"{reps} passes ({total:.1f} s), scaled by {B}/{bs}; {nthreads} threads of a {model}",
+            "cpu_model": model,
+            "single_core": {"value": round(us1, 1), "cores": 1,
+                            "sample": f"the same on one thread: first {bs1} of {B} rows, {reps1} passes "
+                                      f"({total1:.1f} s), scaled by {B}/{bs1}"}}
 
 
 def traffic_for(workload, kernel):

@@ -841,7 +841,11 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
             *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * TB + ls * VW) = r;
         }
     };
-    // ring of claimed groups: [0] computed now, [1] next, ..., [D-1] claimed this phase
+    // ring of claimed groups: [0] computed now, [1] next, ..., [D-1] claimed this phase.  Without
+    // a permutation the chunks are loaded one group ahead; with one, the chunks (gather indices and
+    // permuted positions) two groups ahead and the values they point at one ahead.  (Loading the
+    // values two ahead measured slower: those scattered reads are bound by the address unit, not
+    // by their latency.)
     constexpr int D = VP ? 4 : 3;
     int Gs[D], Ks[D], As[D], Ls[D];
 #pragma unroll
@@ -849,27 +853,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         Gs[i] = claim();
         seg(Gs[i], Ks[i], As[i], Ls[i]);
     }
-    int gA[CH], gB[CH], gC[CH], pA[CH], pB[CH], pC[CH], vA[CH], vB[CH], vC[CH];
-    if constexpr (VP) {
-        load_chunks(As[0], Ls[0], gA, pA);
-        load_chunks(As[1], Ls[1], gB, pB);
-        load_vals(pA, Ls[0], vA);
-    } else {
-        load_chunks(As[0], Ls[0], gA, vA);
-    }
-    // one phase: claim a group, issue the loads of the groups ahead, compute group [0]; buffers
-    // c (group [0]), n (group [1]), nn (group [2])
-    auto phase = [&](int (&gc)[CH], int (&vc)[CH], int (&gn)[CH], int (&pn)[CH], int (&vn)[CH],
-                     int (&gnn)[CH], int (&pnn)[CH]) {
-        Gs[D - 1] = claim();
-        seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
-        if constexpr (VP) {
-            load_chunks(As[2], Ls[2], gnn, pnn);
-            load_vals(pn, Ls[1], vn);
-        } else {
-            load_chunks(As[1], Ls[1], gn, vn);
-        }
-        compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc);
+    auto advance = [&]() {
 #pragma unroll
         for (int i = 0; i + 1 < D; ++i) {
             Gs[i] = Gs[i + 1];
@@ -879,11 +863,45 @@ __global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
         }
         return Gs[0] < ngroups;
     };
-    if (Gs[0] < ngroups) {
-        for (;;) {
-            if (!phase(gA, vA, gB, pB, vB, gC, pC)) break;
-            if (!phase(gB, vB, gC, pC, vC, gA, pA)) break;
-            if (!phase(gC, vC, gA, pA, vA, gB, pB)) break;
+    if constexpr (VP) {
+        // buffer sets 0..2 rotate with the groups: set (t mod 3) holds group t's gather indices g,
+        // permuted positions p and values v
+        int g0[CH], g1[CH], g2[CH], p0[CH], p1[CH], p2[CH], v0[CH], v1[CH], v2[CH];
+        load_chunks(As[0], Ls[0], g0, p0);
+        load_chunks(As[1], Ls[1], g1, p1);
+        load_vals(p0, Ls[0], v0);
+        // one phase: claim group [3], load the chunks of [2] and the values of [1], compute [0]
+        auto phase = [&](int (&gc)[CH], int (&vc)[CH], int (&pv)[CH], int (&vv)[CH], int (&gl)[CH], int (&pl)[CH]) {
+            Gs[D - 1] = claim();
+            seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
+            load_chunks(As[2], Ls[2], gl, pl);
+            load_vals(pv, Ls[1], vv);
+            compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc);
+            return advance();
+        };
+        if (Gs[0] < ngroups) {
+            for (;;) {
+                if (!phase(g0, v0, p1, v1, g2, p2)) break;
+                if (!phase(g1, v1, p2, v2, g0, p0)) break;
+                if (!phase(g2, v2, p0, v0, g1, p1)) break;
+            }
+        }
+    } else {
+        int gA[CH], gB[CH], vA[CH], vB[CH];
+        load_chunks(As[0], Ls[0], gA, vA);
+        // one phase: claim group [2], load the chunks of [1], compute [0]
+        auto phase = [&](int (&gc)[CH], int (&vc)[CH], int (&gn)[CH], int (&vn)[CH]) {
+            Gs[D - 1] = claim();
+            seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
+            load_chunks(As[1], Ls[1], gn, vn);
+            compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc);
+            return advance();
+        };
+        if (Gs[0] < ngroups) {
+            for (;;) {
+                if (!phase(gA, vA, gB, vB)) break;
+                if (!phase(gB, vB, gA, vA)) break;
+            }
         }
     }
 }
