@@ -188,18 +188,19 @@ def test_block_offsets_count_and_errors():
 
 def test_tiled_workspace_bounded_by_batch_tiles():
     """The tiled kernels (and their block partials, batch x column blocks x keys floats) apply up to
-    256 batch columns; wider batches keep the wide-batch paths, whose workspace does not grow with
+    4096 batch columns; wider batches keep the wide-batch paths, whose workspace does not grow with
     the number of column blocks (host-side sizing only)."""
     lib = snk._lib
     d = snk._Desc()
     d.out_features, d.in_features, d.nnz = 5000, 5000, 2_500_000
     d.row_offsets = d.rows = d.cols = d.vals = 0x1000
     nb = -(-5000 // 638)  # column blocks of the tiled walk
-    fwd256 = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 256, 0)
-    assert fwd256 >= 4 * 256 * nb * 5000  # block partials of the tiled forward
-    fwd4096 = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 4096, 0)
-    assert fwd4096 < 4 * 4096 * nb * 5000  # no partials: not tiled
-    assert fwd4096 <= 4 * 5001 * 4096 + 4 * 2_500_000 + (1 << 20)  # operand copy and gathered values
+    for B in (256, 4096):
+        fwd = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), B, 0)
+        assert fwd >= 4 * B * nb * 5000  # block partials of the tiled forward
+    fwd8192 = lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 8192, 0)
+    assert fwd8192 < 4 * 8192 * nb * 5000  # no partials: not tiled
+    assert fwd8192 <= 4 * 5001 * 8192 + 4 * 2_500_000 + (1 << 20)  # operand copy and gathered values
 
 
 def test_backward_form_rules():

@@ -5,7 +5,8 @@ The tiled walks apply to layers of at least 2^19 entries at batches padded to a 
 (batch tiles of 64 columns where the padded batch allows, else 32 or 16; the weight gradient only
 at multiples of 64) whose (key, column block) segments average at least 8 entries.  The cases
 cover: several column blocks with a narrower last one, one block, every tile width, batches that
-need zero padding (50, 100) and several batch tiles (48, 96, 128, 192, 256), empty rows and
+need zero padding (50, 100) and several batch tiles (48, 96, 128, 192, 256, and 512 to 4096 on
+the 5000 x 5000 layer), empty rows and
 bias-only outputs, rows and columns longer than the prefetched chunks (the full lines of
 'dense_lines'), bf16 activations, and the walks off (SNACK_OPT_TILE = 0) giving the same results
 within tolerance.
@@ -18,7 +19,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import NTHREADS, acts, check_close, device_layer, from_device, say, to_device
+from gpu_util import NTHREADS, acts, check_close, device_layer, from_device, named_layer, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -299,6 +300,34 @@ def test_backward_forms(layers, name, B, form):
         check_close(dX.cpu().numpy(), dXr, nnz / I, f"bwd dX ({order})")
         check_close(dW.cpu().numpy(), ref_w, B, f"bwd dW ({order})")
         check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, f"bwd db ({order})")
+
+
+@pytest.mark.parametrize("B", [512, 1024, 4096])
+def test_tiled_large_batch(B):
+    """Up to 64 batch tiles of 64 columns on the 5000 x 5000 layer at 90 % (the GAMLP shape): the
+    forward, the input gradient (values through col_perm, gathered into walk order once), the
+    weight gradient (batch tiles added in turn) and snack_coo_bwd against the oracle, in full."""
+    spec, L = named_layer("gamlp90")
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    built, W = device_layer(L, DEV)
+    x_in, x64 = acts(8900 + B, B, I)
+    dy_in, dy64 = acts(8950 + B, B, O)
+    X, dY = to_device(x_in, DEV), to_device(dy_in, DEV)
+    b = torch.from_numpy(L["bias"]).to(DEV)
+    say(f"large batch B={B}")
+    Y = snk.snack_coo_fwd(W, X, b)
+    dX = snk.snack_coo_bwd_input(W, dY)
+    dW = snk.snack_coo_grad_weight(W, X, dY)
+    dX2, dW2 = snk.snack_coo_bwd(W, X, dY)
+    torch.cuda.synchronize()
+    r, c, v = built["rows"], built["cols"], built["vals"]
+    check_close(Y.cpu().numpy(), oracle.fwd(O, I, r, c, v, x64, L["bias"], nthreads=NTHREADS), nnz / O, f"fwd B={B}")
+    dXr = oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS)
+    dWr = oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS)
+    check_close(dX.cpu().numpy(), dXr, nnz / I, f"dX B={B}")
+    check_close(dW.cpu().numpy(), dWr, B, f"dW B={B}")
+    check_close(dX2.cpu().numpy(), dXr, nnz / I, f"bwd dX B={B}")
+    check_close(dW2.cpu().numpy(), dWr, B, f"bwd dW B={B}")
 
 
 @pytest.mark.parametrize("form", ["split", "tiled"])
