@@ -508,10 +508,10 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
 // VW batch columns (VW floats) of a TB = 16*VW column batch tile (64 for batches padded to a
 // multiple of 64, else 32 or 16).  A group's entries are loaded 16 per chunk register (each row
 // of 16 lanes holds entries j = 0..15 of its slot's chunk), two groups ahead of the compute.
-// Step t of a chunk hands entry t to every lane of its row with DPP row_newbcast:t, folded into
-// the address add and (inline asm) into the FMA, so one step costs one LDS read of VW floats
-// per lane, one address add and VW FMAs.  Entries past a segment's end point at the zero row
-// with value 0.
+// Step t of a chunk hands entry t to every lane of its row with DPP row_newbcast:t: folded into
+// the row address (an XOR), and moved once into a register for the value, so one step costs one
+// LDS read of VW floats per lane, an address XOR, a value move and VW plain FMAs.  Entries past a
+// segment's end point at the zero row with value 0.
 constexpr int kTileThreads = 1024;
 constexpr int kTileWaves = kTileThreads / kWave;
 constexpr int kTileLdsRows = 639;                     // staged rows: 159.75 KB of LDS at 64 columns
@@ -534,19 +534,6 @@ constexpr int kBufPast = static_cast<int>(0xFFFFFFF0u);  // a byte offset past a
 template <int T>
 __device__ __forceinline__ uint32_t bcast16(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x150 + T, 0xF, 0xF, true));
-}
-
-// acc += (lane T of this row's v) * x.  The compiler does not fold a DPP move into v_fmac, so it
-// is written out; NOP1 adds the two wait states a VALU write of v needs before a DPP read of it
-// (used on the first step of a chunk: v is not written again until the chunk is done).
-template <int T, bool NOP1>
-__device__ __forceinline__ void fmac_bcast16(float &acc, float v, float x) {
-    if constexpr (NOP1)
-        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-            : "+v"(acc) : "v"(v), "v"(x), "n"(T));
-    else
-        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-            : "+v"(acc) : "v"(v), "v"(x), "n"(T));
 }
 
 template <int SL>
@@ -646,15 +633,34 @@ __device__ __forceinline__ void tile_reads4(typename TileVec<VW>::T (&x)[4], uin
     x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) ^ lane_off));
 }
 
+// Lane T of each row of 16 lanes' v, broadcast to the row, in a register of its own (inline asm,
+// so the compiler does not fold the DPP move into the FMAs that use it: a DPP FMA issues at about
+// 0.77 per clock per CU, a plain one at the full rate).  NOP1: the two wait states a VALU write of
+// v needs before a DPP read, on the first step of a chunk; volatile keeps the moves of a chunk in
+// step order, so that one runs first (the compiler adds no wait states for inline asm).
+template <int T, bool NOP1>
+__device__ __forceinline__ float bcast16_reg(float v) {
+    float r;
+    if constexpr (NOP1)
+        asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                     : "=v"(r) : "v"(v), "n"(T));
+    else
+        asm volatile("v_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                     : "=v"(r) : "v"(v), "n"(T));
+    return r;
+}
+
 // The FMAs of steps T0..T0+3: acc += (value of entry T0+u) * row.
 template <int VW, int T0>
 __device__ __forceinline__ void tile_fmas4(float (&acc)[VW], float v, const typename TileVec<VW>::T (&x)[4]) {
+    const float v0 = bcast16_reg<T0 + 0, T0 == 0>(v), v1 = bcast16_reg<T0 + 1, false>(v);
+    const float v2 = bcast16_reg<T0 + 2, false>(v), v3 = bcast16_reg<T0 + 3, false>(v);
 #pragma unroll
     for (int i = 0; i < VW; ++i) {
-        fmac_bcast16<T0 + 0, T0 == 0>(acc[i], v, vget(x[0], i));
-        fmac_bcast16<T0 + 1, false>(acc[i], v, vget(x[1], i));
-        fmac_bcast16<T0 + 2, false>(acc[i], v, vget(x[2], i));
-        fmac_bcast16<T0 + 3, false>(acc[i], v, vget(x[3], i));
+        acc[i] = fmaf(v0, vget(x[0], i), acc[i]);
+        acc[i] = fmaf(v1, vget(x[1], i), acc[i]);
+        acc[i] = fmaf(v2, vget(x[2], i), acc[i]);
+        acc[i] = fmaf(v3, vget(x[3], i), acc[i]);
     }
 }
 
@@ -1087,12 +1093,14 @@ __device__ __forceinline__ void tile_bwd_steps4(float (&acc)[VW], float (&p)[16]
     y[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
     y[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
     y[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+    const float v0 = bcast16_reg<T0 + 0, T0 == 0>(v), v1 = bcast16_reg<T0 + 1, false>(v);
+    const float v2 = bcast16_reg<T0 + 2, false>(v), v3 = bcast16_reg<T0 + 3, false>(v);
 #pragma unroll
     for (int i = 0; i < VW; ++i) {
-        fmac_bcast16<T0 + 0, T0 == 0>(acc[i], v, vget(y[0], i));
-        fmac_bcast16<T0 + 1, false>(acc[i], v, vget(y[1], i));
-        fmac_bcast16<T0 + 2, false>(acc[i], v, vget(y[2], i));
-        fmac_bcast16<T0 + 3, false>(acc[i], v, vget(y[3], i));
+        acc[i] = fmaf(v0, vget(y[0], i), acc[i]);
+        acc[i] = fmaf(v1, vget(y[1], i), acc[i]);
+        acc[i] = fmaf(v2, vget(y[2], i), acc[i]);
+        acc[i] = fmaf(v3, vget(y[3], i), acc[i]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
