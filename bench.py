@@ -28,22 +28,25 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 COLD_CALLS = 50        # flushed launches behind each cold median
 
+# The values of a layer's weight are kept in the order that makes its step fastest: column-view
+# order ("col": the one-pass tiled backward reads them and writes dW in place, the forward reads
+# them through a permutation) at batches of one 64-column tile, triple order ("row") elsewhere.
 WORKLOADS = {
-    # name: (layer, batch, dtype)
-    "target95_b64": ("target95", 64, "f32"),
-    "target95_b64_bf16": ("target95", 64, "bf16"),
-    "target95_b1": ("target95", 1, "f32"),
-    "llm90_b64": ("llm90", 64, "f32"),
-    "llm90_b16": ("llm90", 16, "f32"),
-    "llm90_b1": ("llm90", 1, "f32"),
-    "mid_b32": ("mid", 32, "f32"),
-    "xs99_b1": ("xs99", 1, "f32"),
-    "xs999_b1": ("xs999", 1, "f32"),
-    "xs99_zipf_b1": ("xs99_zipf", 1, "f32"),
-    "gpt2_fc_b1024": ("gpt2_fc", 1024, "f32"),
-    "gpt2_fc_b1024_bf16": ("gpt2_fc", 1024, "bf16"),
-    "gamlp90_b1": ("gamlp90", 1, "f32"),
-    "gamlp90_b4096": ("gamlp90", 4096, "f32"),
+    # name: (layer, batch, dtype, value order)
+    "target95_b64": ("target95", 64, "f32", "col"),
+    "target95_b64_bf16": ("target95", 64, "bf16", "col"),
+    "target95_b1": ("target95", 1, "f32", "row"),
+    "llm90_b64": ("llm90", 64, "f32", "col"),
+    "llm90_b16": ("llm90", 16, "f32", "col"),
+    "llm90_b1": ("llm90", 1, "f32", "row"),
+    "mid_b32": ("mid", 32, "f32", "row"),
+    "xs99_b1": ("xs99", 1, "f32", "row"),
+    "xs999_b1": ("xs999", 1, "f32", "row"),
+    "xs99_zipf_b1": ("xs99_zipf", 1, "f32", "row"),
+    "gpt2_fc_b1024": ("gpt2_fc", 1024, "f32", "row"),
+    "gpt2_fc_b1024_bf16": ("gpt2_fc", 1024, "bf16", "row"),
+    "gamlp90_b1": ("gamlp90", 1, "f32", "row"),
+    "gamlp90_b4096": ("gamlp90", 4096, "f32", "row"),
 }
 
 
@@ -71,16 +74,17 @@ def bwd_fused(layer):
     return snk.snack_coo_bwd_is_fused(layer.W, layer.B, code)
 
 
-def column_order_step(layer, K):
-    """The same step on the same layer with its values kept in column-view order (the layer's
-    value_order="col"): graph-replayed step time and per-kernel times.  The layer is restored."""
+def other_order_step(layer, K):
+    """The same step on the same layer with its values kept in the other order (triple order for a
+    layer in column-view order, and the reverse): graph-replayed step time and per-kernel times.
+    The layer is restored."""
     import torch
     import coo_spmm_row_amd as snk
-    W_row, ws_row = layer.W, layer.ws
-    layer.W = W_row.to_column_order()
+    W0, ws0 = layer.W, layer.ws
+    layer.W = W0.to_row_order() if W0.column_order else W0.to_column_order()
     code = snk.SNACK_BF16 if layer.dtype == "bf16" else snk.SNACK_F32
     need = max(snk.snack_coo_workspace_bytes(op, layer.W, layer.B, code) for op in (0, 1, 2, 3))
-    layer.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=ws_row.device)
+    layer.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=ws0.device)
     try:
         for _ in range(3):
             layer.step()
@@ -90,7 +94,7 @@ def column_order_step(layer, K):
         return {"us_per_step_graph": None if g is None else round(g, 2),
                 "kernel_us": {op: round(float(np.mean(v)) * 1000.0, 2) for op, v in kern.items()}}
     finally:
-        layer.W, layer.ws = W_row, ws_row
+        layer.W, layer.ws = W0, ws0
 
 
 def kernel_source_sha():
@@ -101,7 +105,7 @@ def kernel_source_sha():
 
 
 class Layer:
-    def __init__(self, name, B, dtype, dev):
+    def __init__(self, name, B, dtype, dev, order="row"):
         import torch
         import coo_spmm_row_amd as snk
         import synth
@@ -113,6 +117,9 @@ class Layer:
         self.spec, self.L, self.built, self.B, self.dtype = spec, L, built, B, dtype
         self.O, self.I, self.nnz = L["out_features"], L["in_features"], L["nnz"]
         self.W = snk.SnackCOO.from_built(built, dev)
+        if order == "col":  # values (and dW) in column-view order
+            self.W = self.W.to_column_order()
+        self.order = order
         seeds = synth.seeds_for(spec.config_id, spec.variant)
         self.x = synth.make_acts(seeds["X"](0), B, self.I)
         self.dy = synth.make_acts(seeds["dY"](0), B, self.O)
@@ -390,12 +397,13 @@ def topology_times(layer, frac=0.1, reps=3):
     import coo_spmm_row_amd as snk
     p = int(frac * layer.nnz)
     r, c, v = layer.built["rows"], layer.built["cols"], layer.built["vals"]
-    snk.snack_coo_topology_update_device(layer.W, p, 7)  # warm-up (first launch of the sort kernels)
+    W = layer.W.to_row_order()  # the update works on the triple with its values in row order
+    snk.snack_coo_topology_update_device(W, p, 7)  # warm-up (first launch of the sort kernels)
     dev_ms, host_ms = [], []
     for i in range(reps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        Wn, trials = snk.snack_coo_topology_update_device(layer.W, p, 100 + i)
+        Wn, trials = snk.snack_coo_topology_update_device(W, p, 100 + i)
         torch.cuda.synchronize()
         dev_ms.append((time.perf_counter() - t0) * 1e3)
         del Wn
@@ -459,9 +467,9 @@ def main():
         calibrate_copy(dev, args.calibrate_copy, max(1, args.steps))
         return
 
-    name, B, dtype = WORKLOADS[args.workload]
+    name, B, dtype, order = WORKLOADS[args.workload]
     log(f"workload {args.workload}: building layer")
-    layer = Layer(name, B, dtype, dev)
+    layer = Layer(name, B, dtype, dev, order)
     log(f"layer {layer.O}x{layer.I} nnz={layer.nnz} B={B} {dtype} (host build {layer.host_build_s:.1f} s)")
     for _ in range(args.warmup):
         layer.step()
@@ -516,8 +524,9 @@ def main():
         extras["module_us_per_step_eager"] = round(module_step_us(layer, args.steps), 2)
         log("topology update (prune 10 %, regrow, column view): device and host")
         extras["topology_update"] = topology_times(layer)
-        log("the step with the values kept in column-view order")
-        extras["column_order_values"] = column_order_step(layer, args.steps)
+        other = "row_order_values" if order == "col" else "column_order_values"
+        log(f"the step with the values in the other order ({other})")
+        extras[other] = other_order_step(layer, args.steps)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -554,7 +563,8 @@ def main():
     line["config"] = {"workload": f"{spec.out_features}x{spec.in_features} sparse layer, "
                                   f"{100 * (1 - spec.density):.1f}% sparsity, batch {B}",
                       "out_features": spec.out_features, "in_features": spec.in_features,
-                      "nnz": spec.nnz, "batch": B, "structure": spec.structure}
+                      "nnz": spec.nnz, "batch": B, "structure": spec.structure,
+                      "value_order": {"col": "column view", "row": "triple (row)"}[order]}
     print(json.dumps(line), flush=True)
 
 
