@@ -89,9 +89,10 @@ def other_order_step(layer, K):
         for _ in range(3):
             layer.step()
         torch.cuda.synchronize()
+        e = plain_steps(layer, K)
         g = graph_steps(layer, K)
         _, kern = timed_steps(layer, K)
-        return {"us_per_step_graph": None if g is None else round(g, 2),
+        return {"us_per_step_eager": round(e, 2), "us_per_step_graph": None if g is None else round(g, 2),
                 "kernel_us": {op: round(float(np.mean(v)) * 1000.0, 2) for op, v in kern.items()}}
     finally:
         layer.W, layer.ws = W0, ws0
@@ -164,9 +165,24 @@ def make_events(n):
     return evs
 
 
+def plain_steps(layer, K):
+    """K back-to-back steps, eager, with events only around the whole region: us per step."""
+    import torch
+    start, stop = make_events(2)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(K):
+        layer.step()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / K * 1000.0
+
+
 def timed_steps(layer, K, ops=STEP_OPS):
     """K back-to-back passes over `ops`; the probe brackets each op's main kernel.
-    Returns (total ms, {op: [kernel ms per launch]})."""
+    Returns (total ms, {op: [kernel ms per launch]}).  The events between the kernels make each
+    step slower than plain_steps (each event write-back releases the caches): step times come
+    from plain_steps or graph_steps, kernel times from here."""
     import torch
     import coo_spmm_row_amd as snk
     pairs = {op: [(a, b) for a, b in zip(make_events(K), make_events(K))] for op in ops}
@@ -240,16 +256,22 @@ def op_times(layer, K, ops=STEP_OPS + ("dx", "dw")):
     return out
 
 
-def cold_kernel_times(layer, K, ops, flush_bytes=1 << 30):
-    """Main-kernel time per op with the 256 MB last-level cache flushed before each launch."""
+def cold_kernel_times(layer, K, ops, flush_bytes=1 << 30, write_flush=False):
+    """Main-kernel time per op with L2 and the 256 MB last-level cache flushed before each launch
+    by reading flush_bytes.  A read stream leaves clean lines behind; a write stream
+    (write_flush=True) leaves dirty ones, whose write-back the measured kernel then pays for as
+    it brings its own data in (about 14 us more on the 10k x 10k / 95 % / batch 64 backward)."""
     import torch
     import coo_spmm_row_amd as snk
-    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device=layer.X.device)
+    scratch = torch.zeros(flush_bytes // 4, dtype=torch.float32, device=layer.X.device)
     res = {}
     for op in ops:
         evs = [(a, b) for a, b in zip(make_events(K), make_events(K))]
         for i in range(K):
-            scratch.add_(1.0)  # streams 2 x flush_bytes through the caches
+            if write_flush:
+                scratch.add_(1.0)  # reads and writes flush_bytes
+            else:
+                scratch.sum()  # reads flush_bytes
             snk.snack_coo_set_probe(*evs[i])
             layer.op(op)
             snk.snack_coo_set_probe()
@@ -331,7 +353,7 @@ def traffic_for(workload, kernel):
 
 
 def batch_sweep(dev, K, batches=(16, 32)):
-    """The step (graph-replayed, us) at small batches on the 10k x 10k layers at 90 and 95 %: the
+    """The step (eager and graph-replayed, us) at small batches on the 10k x 10k layers at 90 and 95 %: the
     metric's batch range below 64, with the backward's form and the per-op kernel times."""
     out = {}
     for name, label in (("llm90", "90%"), ("target95", "95%")):
@@ -339,9 +361,11 @@ def batch_sweep(dev, K, batches=(16, 32)):
             layer = Layer(name, B, "f32", dev)
             for _ in range(3):
                 layer.step()
+            e = plain_steps(layer, K)
             g = graph_steps(layer, K)
             _, kern = timed_steps(layer, K)
-            out[f"{label} B={B}"] = {"us_per_step_graph": None if g is None else round(g, 2),
+            out[f"{label} B={B}"] = {"us_per_step_eager": round(e, 2),
+                                     "us_per_step_graph": None if g is None else round(g, 2),
                                      "backward_fused": bwd_fused(layer),
                                      "kernel_us": {op: round(float(np.mean(kern[op])) * 1000.0, 2)
                                                    for op in STEP_OPS}}
@@ -356,10 +380,10 @@ def batch1_sweep(dev, K):
         layer = Layer(name, 1, "f32", dev)
         for _ in range(3):
             layer.step()
-        total, _ = timed_steps(layer, K)
+        eager = plain_steps(layer, K)
         g = graph_steps(layer, K)
         _, kern = timed_steps(layer, K, SPLIT_OPS)  # at batch 1 the gradients run as two kernels
-        out[label] = {"us_per_step_eager": round(total / K * 1000.0, 2),
+        out[label] = {"us_per_step_eager": round(eager, 2),
                       "us_per_step_graph": None if g is None else round(g, 2),
                       "kernel_us": {op: round(float(np.mean(kern[op])) * 1000.0, 2) for op in SPLIT_OPS}}
         del layer
@@ -475,12 +499,15 @@ def main():
         layer.step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    total_ms, kern = timed_steps(layer, args.steps)
-    eager_us = total_ms / args.steps * 1000.0
+    eager_us = plain_steps(layer, args.steps)
     log("timing the step as a replayed HIP graph")
     graph_us = graph_steps(layer, args.steps)
-    step_us = graph_us if graph_us is not None else eager_us
+    # the step as launched eagerly or as one replayed graph, whichever is faster (both reported)
+    step_us = eager_us if graph_us is None else min(eager_us, graph_us)
+    step_timing = "eager" if step_us == eager_us else "graph"
     ms_per_step = step_us / 1000.0
+    log("kernel times (probe events around each op's main kernels)")
+    _, kern = timed_steps(layer, args.steps)
     _, kern_split = timed_steps(layer, args.steps, ("dx", "dw"))
     kern.update(kern_split)
     all_ops = STEP_OPS + ("dx", "dw")
@@ -493,8 +520,9 @@ def main():
     kname = {"fwd": "forward gather-reduce", "dx": "input-gradient gather-reduce",
              "dw": "weight-gradient sampled product", "bwd": "backward pass (dX and dW in one pass)"}[dom]
     nbytes = {op: algorithmic_bytes(op, layer.nnz, layer.O, layer.I, B, layer.s) for op in all_ops}
-    # the roofline of the dominant kernel from its cold median (the 256 MB last-level cache flushed
-    # before each of COLD_CALLS launches), the warm back-to-back mean beside it
+    # the roofline of the dominant kernel from its cold median (L2 and the 256 MB last-level cache
+    # flushed by a read stream before each of COLD_CALLS launches), the warm back-to-back mean
+    # beside it
     log(f"cold-cache timing of the dominant kernel ({COLD_CALLS} flushed calls)")
     cold_dom = cold_kernel_times(layer, COLD_CALLS, (dom,))[dom]
     achieved = nbytes[dom] / (cold_dom * 1e-6) / 1e9
@@ -502,12 +530,13 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_for(args.workload, dom),
-                "kernel": kname, "kernel_us": round(cold_dom, 2), "timing": f"cold median of {COLD_CALLS} calls",
+                "kernel": kname, "kernel_us": round(cold_dom, 2), "timing": f"cold median of {COLD_CALLS} calls (caches flushed by a 1 GiB read)",
                 "warm": {"achieved": round(achieved_warm, 1), "frac": round(achieved_warm / HBM_PEAK_GBS, 4),
                          "kernel_us": round(kernel_us[dom], 2), "timing": f"mean of {args.steps} back-to-back calls"},
                 "algorithmic_bytes": nbytes[dom]}
     extras = {"us_per_step_eager": round(eager_us, 2),
               "us_per_step_graph": None if graph_us is None else round(graph_us, 2),
+              "step_timing": step_timing,
               "backward_fused": bwd_fused(layer),
               "kernel_us": {op: round(v, 2) for op, v in kernel_us.items()},
               "kernel_us_percentiles": kernel_pct,
@@ -520,6 +549,8 @@ def main():
         extras["kernel_us_cold"] = {op: round(v, 2) for op, v in cold.items()}
         extras["kernel_frac_hbm_cold"] = {op: round(nbytes[op] / (cold[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                           for op in cand}
+        coldw = cold_kernel_times(layer, COLD_CALLS, (dom,), write_flush=True)
+        extras["kernel_us_cold_write_flush"] = {dom: round(coldw[dom], 2)}
         log("the step through the PyTorch drop-in layer")
         extras["module_us_per_step_eager"] = round(module_step_us(layer, args.steps), 2)
         log("topology update (prune 10 %, regrow, column view): device and host")

@@ -1077,22 +1077,21 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
 }
 
 // Both gradients in one tiled pass over the column view (one batch tile of TB = 16 VW columns).
-// The workgroup stages a block of cw rows of dY^T; slot s walks column 4g+s and holds its X^T slice
-// (VW floats per lane).  Each step reads an entry's staged dY row once and uses it twice: dX
-// partials += v * dY row (as tile_spmm_kernel), and the dot product with the X slice, which a
-// reduce-scatter over the slot's 16 lanes turns into dW of 16 entries per chunk.  dW goes to the
-// walk position, or (VP: values in row order) to perm of it, the same permuted position the
-// value was read from.  The block partials of dX are summed by tile_sum_kernel.
+// The workgroup stages a block of cw rows of dY (features of the output, read in place from the
+// batch-major dY and swizzled as in tile_spmm_kernel); slot s of a group walks the segment of one
+// column of W (the key) and holds that column's X slice: its VW batch columns of X, read in place.
+// Each step reads an entry's staged dY row once and uses it twice: dX partials += v * dY row (as
+// tile_spmm_kernel), and the dot product with the X slice, which a reduce-scatter over the slot's
+// 16 lanes turns into dW of 16 entries per chunk.  dW goes to the walk position, or (VP: values in
+// row order) to perm of it, the same permuted position the value was read from.  The block
+// partials of dX are summed by tile_sum_kernel.
 template <int VW, int T0>
 __device__ __forceinline__ void tile_bwd_steps4(float (&acc)[VW], float (&p)[16], uint32_t off, float v,
                                                 uint32_t lane_off, const char *lds,
                                                 const typename TileVec<VW>::T &xs) {
     typedef typename TileVec<VW>::T V;
     V y[4];
-    y[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) + lane_off));
-    y[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) + lane_off));
-    y[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) + lane_off));
-    y[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) + lane_off));
+    tile_reads4<VW, T0>(y, off, lane_off, lds);
     const float v0 = bcast16_reg<T0 + 0, T0 == 0>(v), v1 = bcast16_reg<T0 + 1, false>(v);
     const float v2 = bcast16_reg<T0 + 2, false>(v), v3 = bcast16_reg<T0 + 3, false>(v);
 #pragma unroll
@@ -1111,69 +1110,59 @@ __device__ __forceinline__ void tile_bwd_steps4(float (&acc)[VW], float (&p)[16]
     }
 }
 
-template <int VW, int CH, bool VP>
+// dy: the batch-major dY [B][opnd_rows], x: the batch-major X [B][nkeys] (fp32 or bf16; B times
+// max(opnd_rows, nkeys) times the element size < 2^31), B <= TB.  Groups are claimed from the
+// workgroup's counter as in tile_spmm_kernel; a group's X slices are loaded with its chunks.
+template <int VW, int CH, bool VP, typename InT>
 __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
     int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ segs,
     const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm, int nnz,
-    const float *__restrict__ opnd, int opnd_rows, int ld, const float *__restrict__ xt,
-    float *__restrict__ part, float *__restrict__ dw) {
+    const InT *__restrict__ dy, int opnd_rows, const InT *__restrict__ x, int64_t B, float *__restrict__ part,
+    float *__restrict__ dw) {
     constexpr int SL = 4;
     constexpr int TB = 16 * VW;
     constexpr uint32_t kRowBytes = 4u * TB;
+    constexpr int kEs = static_cast<int>(sizeof(InT));
     typedef typename TileVec<VW>::T V;
-    extern __shared__ float4 xs4[];
+    // static: its address is known when compiling, so a row chunk's address is one DPP XOR
+    __shared__ float4 xs4[kTileLdsRows * 4 * VW + kTileClaimBytes / 16];
     const int64_t L = xcd_block();
     if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
-    const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
+    // logical workgroup L = rb * ncb + cb: the column blocks of a key range sit together on one XCD,
+    // which reads that range's X slices into its L2 once (the forward's L = cb * nrb + rb stages
+    // each block on fewer XCDs instead).  Measured at 10k x 10k / 95 % / B = 64 with the caches
+    // flushed by a read stream: 69.0 against 70.7 us with the tile sums; warm, the same.
+    const int rb = static_cast<int>(L / ncb), cb = static_cast<int>(L % ncb);
     const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int j = lane & 15;
     const int slot = lane >> 4;
     const uint32_t lane_off = static_cast<uint32_t>(j * VW * 4);
-    const uint32_t zoff = static_cast<uint32_t>(cw) * kRowBytes;
+    const uint32_t zoff = tile_row_off<VW>(cw);
     const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
     const int ngroups = (k_hi - k_lo + SL - 1) / SL;
-    const int my_groups = wave < ngroups ? (ngroups - wave + kTileWaves - 1) / kTileWaves : 0;
-    // lane l holds the segment of this wave's group l / SL, slot l % SL (list positions)
-    const int pos_l = k_lo + (wave + kTileWaves * (lane / SL)) * SL + lane % SL;
-    const bool key_l_ok = lane / SL < my_groups && pos_l < k_hi;
-    int key_l, seg_a, seg_len;
-    seg_load(buf_rsrc(segs, nkeys * ncb * 4), cb, nkeys, pos_l, key_l_ok, key_l, seg_a, seg_len);
-    {  // stage the block's rows of dY^T; rows cn..cw are zero (row cw is the zero row)
-        constexpr int R4 = TB / 4;
-        constexpr int kIters = (kTileLdsRows * R4 + kTileThreads - 1) / kTileThreads;
-        constexpr int kHalf = (kIters + 1) / 2;  // two rounds: fewer registers live
-        const float4 *src = reinterpret_cast<const float4 *>(opnd + static_cast<int64_t>(c0) * ld);
-        const int ld4 = ld / 4, n4 = (cw + 1) * R4;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float4 tmp[kHalf];
-#pragma unroll
-            for (int it = 0; it < kHalf; ++it) {
-                const int i = (h * kHalf + it) * kTileThreads + static_cast<int>(threadIdx.x);
-                const int c = i / R4, q = i % R4;
-                tmp[it] = c < cn ? src[static_cast<int64_t>(c) * ld4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int it = 0; it < kHalf; ++it) {
-                const int i = (h * kHalf + it) * kTileThreads + static_cast<int>(threadIdx.x);
-                if (i < n4) xs4[i] = tmp[it];
-            }
-        }
-    }
-    const int s_len = key_l_ok ? seg_len : 0, s_a = seg_a, s_key = key_l_ok ? key_l : -1;
+    unsigned *claims = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(xs4) + (cw + 1) * kRowBytes);
+    // the block's rows of dY; rows cn..cw are zero (row cw is the zero row)
+    tile_stage_rows<VW, InT>(xs4, act_rsrc(dy, static_cast<int>(B) * opnd_rows), opnd_rows, 0, c0, cn, cw);
+    if (threadIdx.x == 0) *claims = 0u;
     __syncthreads();
     const char *lds = reinterpret_cast<const char *>(xs4);
     float *pout = part + static_cast<int64_t>(cb) * nkeys * TB;
-    // chunks two groups ahead (VP: permuted positions two ahead, values one ahead), the X^T slice
-    // of each slot's column with its group's chunks
     const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
-    auto load_chunks = [&](int g, int (&gi)[CH], int (&vv)[CH], V &xsl, int &len) {
-        const int src = ((g < my_groups ? g : 0) * SL + slot) * 4;
-        const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-        const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
-        len = g < my_groups ? __builtin_amdgcn_ds_bpermute(src, s_len) : 0;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
+    const __amdgpu_buffer_rsrc_t rx = act_rsrc(x, static_cast<int>(B) * nkeys);
+    auto claim = [&]() {
+        unsigned g = 0;
+        if (lane == 0) g = atomicAdd(claims, 1u);
+        return static_cast<int>(__builtin_amdgcn_readfirstlane(g));
+    };
+    auto seg = [&](int G, int &key, int &a, int &len) {  // this slot's segment of group G (none past the tile)
+        const int pos = k_lo + SL * G + slot;
+        seg_load(rs, cb, nkeys, pos, G < ngroups && pos < k_hi, key, a, len);
+    };
+    // a group's chunks (gather indices, and values or permuted positions) and the X slice of each
+    // slot's key (batch rows VW j .. VW j + VW - 1; none for an empty segment, rows >= B read as 0)
+    auto load_chunks = [&](int key, int a, int len, int (&gi)[CH], int (&vv)[CH], V &xsl) {
         const int base = (a + j) * 4;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {  // lanes past the segment read nothing
@@ -1181,14 +1170,24 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
             gi[c] = buf_ld(rg, off);
             vv[c] = buf_ld(VP ? rp : rv, off);
         }
-        xsl = *reinterpret_cast<const V *>(xt + static_cast<int64_t>(key < 0 ? 0 : key) * ld + VW * j);
+        const int xo = len > 0 ? (VW * j * nkeys + key) * kEs : kBufPast;
+        const int step = len > 0 ? nkeys * kEs : 0;
+        float d[VW];
+#pragma unroll
+        for (int i = 0; i < VW; ++i) d[i] = act_ld<InT>(rx, xo + i * step);
+        if constexpr (VW == 1) xsl = d[0];
+        else if constexpr (VW == 2) xsl = make_float2(d[0], d[1]);
+        else xsl = make_float4(d[0], d[1], d[2], d[3]);
     };
     auto load_vals = [&](const int (&pm)[CH], int len, int (&vv)[CH]) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) vv[c] = buf_ld(rv, 16 * c + j < len ? pm[c] * 4 : kBufPast);
     };
-    auto chunk = [&](float (&acc)[VW], int a, int len, int m, int c, uint32_t off, float v, int pos,
-                     const V &xsl) {
+    auto group_len = [&](int len) {
+        return max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
+                   max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
+    };
+    auto chunk = [&](float (&acc)[VW], int len, int m, int c, uint32_t off, float v, int wpos, const V &xsl) {
         float p[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) p[t] = 0.f;
@@ -1198,15 +1197,12 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
         if (nst > 8) tile_bwd_steps4<VW, 8>(acc, p, off, v, lane_off, lds, xsl);
         if (nst > 12) tile_bwd_steps4<VW, 12>(acc, p, off, v, lane_off, lds, xsl);
         const float r = group_reduce_scatter<16, 16>(p, j);
-        if (16 * c + j < len) dw[pos] = r;
+        if (16 * c + j < len) dw[wpos] = r;
     };
-    auto compute = [&](int g, const int (&gi)[CH], const int (&vv)[CH], const int (&pm)[CH], const V &xsl) {
-        const int src = (g * SL + slot) * 4;
-        const int a = __builtin_amdgcn_ds_bpermute(src, s_a);
-        const int len = __builtin_amdgcn_ds_bpermute(src, s_len);
-        const int key = __builtin_amdgcn_ds_bpermute(src, s_key);
-        const int m = max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
-                          max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
+    auto compute = [&](int G, int key, int a, int len, const int (&gi)[CH], const int (&vv)[CH],
+                       const int (&pm)[CH], const V &xsl) {
+        const int pos = k_lo + SL * G + slot;
+        const int m = group_len(len);
         float acc[VW];
 #pragma unroll
         for (int i = 0; i < VW; ++i) acc[i] = 0.f;
@@ -1214,24 +1210,26 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
         for (int c = 0; c < CH; ++c) {
             if (16 * c < m) {
                 const bool ok = 16 * c + j < len;
-                const uint32_t off = ok ? static_cast<uint32_t>(gi[c] - c0) * kRowBytes : zoff;
+                const uint32_t off = ok ? tile_row_off<VW>(gi[c] - c0) : zoff;
                 const float v = ok ? __int_as_float(vv[c]) : 0.f;
-                chunk(acc, a, len, m, c, off, v, VP ? pm[c] : a + 16 * c + j, xsl);
+                chunk(acc, len, m, c, off, v, VP ? pm[c] : a + 16 * c + j, xsl);
             }
         }
         for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
             const bool ok = 16 * c + j < len;
-            const int pos = (a + 16 * c + j) * 4;
-            const int gv = buf_ld(rg, pos);
-            const int pv = VP ? buf_ld(rp, pos) : a + 16 * c + j;
+            const int at = (a + 16 * c + j) * 4;
+            const int gv = buf_ld(rg, at);
+            const int pv = VP ? buf_ld(rp, at) : a + 16 * c + j;
             const float w = __int_as_float(buf_ld(rv, ok ? pv * 4 : kBufPast));
-            chunk(acc, a, len, m, c, ok ? static_cast<uint32_t>(gv - c0) * kRowBytes : zoff, ok ? w : 0.f, pv, xsl);
+            chunk(acc, len, m, c, ok ? tile_row_off<VW>(gv - c0) : zoff, ok ? w : 0.f, pv, xsl);
         }
+        // every chunk register is consumed here, also those a short group skipped: without this
+        // use, refilling them would wait for loads issued after them
 #pragma unroll
         for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]), "v"(pm[c]));
 #pragma unroll
         for (int i = 0; i < VW; ++i) asm volatile("" ::"v"(vget(xsl, i)));
-        if (key >= 0) {
+        if (pos < k_hi) {
             V r;
             if constexpr (VW == 1) r = acc[0];
             else if constexpr (VW == 2) r = make_float2(acc[0], acc[1]);
@@ -1239,38 +1237,67 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
             *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * TB + j * VW) = r;
         }
     };
-    int gi0[CH], gi1[CH], gi2[CH], vv0[CH], vv1[CH], vv2[CH], pm0[CH], pm1[CH], pm2[CH];
-    V x0, x1, x2;
-    int n0 = 0, n1 = 0, n2 = 0;
-    if constexpr (!VP) {
-        load_chunks(0, gi0, vv0, x0, n0);
-        load_chunks(1, gi1, vv1, x1, n1);
-        for (int g = 0; g < my_groups; g += 3) {
-            load_chunks(g + 2, gi2, vv2, x2, n2);
-            compute(g, gi0, vv0, gi0, x0);
-            if (g + 1 >= my_groups) break;
-            load_chunks(g + 3, gi0, vv0, x0, n0);
-            compute(g + 1, gi1, vv1, gi1, x1);
-            if (g + 2 >= my_groups) break;
-            load_chunks(g + 4, gi1, vv1, x1, n1);
-            compute(g + 2, gi2, vv2, gi2, x2);
+    // ring of claimed groups as in tile_spmm_kernel: without a permutation the chunks and X slices
+    // are loaded one group ahead; with one, two groups ahead, and the values one ahead
+    constexpr int D = VP ? 4 : 3;
+    int Gs[D], Ks[D], As[D], Ls[D];
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) {
+        Gs[i] = claim();
+        seg(Gs[i], Ks[i], As[i], Ls[i]);
+    }
+    auto advance = [&]() {
+#pragma unroll
+        for (int i = 0; i + 1 < D; ++i) {
+            Gs[i] = Gs[i + 1];
+            Ks[i] = Ks[i + 1];
+            As[i] = As[i + 1];
+            Ls[i] = Ls[i + 1];
+        }
+        return Gs[0] < ngroups;
+    };
+    if constexpr (VP) {
+        // buffer sets 0..2 rotate with the groups: set (t mod 3) holds group t's gather indices g,
+        // permuted positions p, values v and X slices x
+        int g0[CH], g1[CH], g2[CH], p0[CH], p1[CH], p2[CH], v0[CH], v1[CH], v2[CH];
+        V x0, x1, x2;
+        load_chunks(Ks[0], As[0], Ls[0], g0, p0, x0);
+        load_chunks(Ks[1], As[1], Ls[1], g1, p1, x1);
+        load_vals(p0, Ls[0], v0);
+        // one phase: claim group [3], load the chunks of [2] and the values of [1], compute [0]
+        auto phase = [&](int (&gc)[CH], int (&pc)[CH], int (&vc)[CH], const V &xc, int (&pv)[CH], int (&vv)[CH],
+                         int (&gl)[CH], int (&pl)[CH], V &xl) {
+            Gs[D - 1] = claim();
+            seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
+            load_chunks(Ks[2], As[2], Ls[2], gl, pl, xl);
+            load_vals(pv, Ls[1], vv);
+            compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc, pc, xc);
+            return advance();
+        };
+        if (Gs[0] < ngroups) {
+            for (;;) {
+                if (!phase(g0, p0, v0, x0, p1, v1, g2, p2, x2)) break;
+                if (!phase(g1, p1, v1, x1, p2, v2, g0, p0, x0)) break;
+                if (!phase(g2, p2, v2, x2, p0, v0, g1, p1, x1)) break;
+            }
         }
     } else {
-        load_chunks(0, gi0, pm0, x0, n0);
-        load_chunks(1, gi1, pm1, x1, n1);
-        load_vals(pm0, n0, vv0);
-        for (int g = 0; g < my_groups; g += 3) {
-            load_chunks(g + 2, gi2, pm2, x2, n2);
-            load_vals(pm1, n1, vv1);
-            compute(g, gi0, vv0, pm0, x0);
-            if (g + 1 >= my_groups) break;
-            load_chunks(g + 3, gi0, pm0, x0, n0);
-            load_vals(pm2, n2, vv2);
-            compute(g + 1, gi1, vv1, pm1, x1);
-            if (g + 2 >= my_groups) break;
-            load_chunks(g + 4, gi1, pm1, x1, n1);
-            load_vals(pm0, n0, vv0);
-            compute(g + 2, gi2, vv2, pm2, x2);
+        int gA[CH], gB[CH], vA[CH], vB[CH];
+        V xA, xB;
+        load_chunks(Ks[0], As[0], Ls[0], gA, vA, xA);
+        // one phase: claim group [2], load the chunks of [1], compute [0]
+        auto phase = [&](int (&gc)[CH], int (&vc)[CH], const V &xc, int (&gn)[CH], int (&vn)[CH], V &xn) {
+            Gs[D - 1] = claim();
+            seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
+            load_chunks(Ks[1], As[1], Ls[1], gn, vn, xn);
+            compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc, gc, xc);
+            return advance();
+        };
+        if (Gs[0] < ngroups) {
+            for (;;) {
+                if (!phase(gA, vA, xA, gB, vB, xB)) break;
+                if (!phase(gB, vB, xB, gA, vA, xA)) break;
+            }
         }
     }
 }
@@ -2779,16 +2806,6 @@ int allow_lds(const void *f, size_t lds, std::atomic<uint64_t> &done, const char
     return SNACK_OK;
 }
 
-// The tiled kernels' largest dynamic LDS at VW floats per lane: kTileLdsRows staged rows of 16 VW
-// and the group counter.
-constexpr size_t tile_lds_max(int VW) {
-    return static_cast<size_t>(kTileLdsRows) * 16 * VW * sizeof(float) + kTileClaimBytes;
-}
-// Dynamic LDS of one launch: the staged block of cw rows, the zero row and the group counter.
-inline size_t tile_lds_bytes(int cw, int VW) {
-    return static_cast<size_t>(cw + 1) * (16 * VW) * sizeof(float) + kTileClaimBytes;
-}
-
 template <int VW, int CH, typename InT>
 int launch_tile_sddmm_kernel(const SddmmPlan &p, int64_t O, int64_t I, int64_t B, const int32_t *tab,
                              const int32_t *cols, const InT *X, const InT *dY, float *dw, hipStream_t st) {
@@ -2898,20 +2915,15 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
     // stores cost more than the second pass: 10k/95 %/B = 64 118 against 92 us)
     const int form = bwd_form_env();
     const bool tiled_ok = form == 2 || (form < 0 && colvals && Bp == 64);
-    if (p.fused && tiled_ok && (Bp == 16 || Bp == 32 || Bp == 64)) {
+    if (p.fused && tiled_ok && (Bp == 16 || Bp == 32 || Bp == 64) && Bp * I < (int64_t(1) << 29)) {
+        // (the plan of the column-view walk bounds Bp O; X is read in place too)
         const SpmmPlan sp = plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals);
         if (sp.mapping == kTile && sp.bpad == Bp && sp.tnbt == 1 && !sp.cvals) {
             p.fused = false;
             p.tiled = true;
             p.sp = sp;
-            size_t at = 0;
-            p.off_x = at;
-            at = align_up(at + sizeof(float) * static_cast<size_t>((I + 1) * Bp));
-            p.off_dy = at;
-            at = align_up(at + sizeof(float) * static_cast<size_t>((O + 1) * Bp));
-            p.off_spmm = at;
-            at = align_up(at + sp.total);
-            p.total = at;
+            p.off_x = p.off_dy = p.off_spmm = 0;  // X and dY read in place
+            p.total = align_up(sp.total);
             return p;
         }
     }
@@ -3750,49 +3762,37 @@ static int run_split_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *
     return snack::ok();
 }
 
-template <int VW, int CH, bool VP>
-int launch_tile_bwd_kernel(const SpmmPlan &sp, int64_t I, int64_t O, const int32_t *tab, const snack_coo_desc *W,
-                           const float *dyt, const float *xt, float *part, float *dW, hipStream_t st) {
-    const size_t lds = tile_lds_bytes(sp.tcw, VW);
-    static std::atomic<uint64_t> lds_ok{0};
-    if (int s = allow_lds(reinterpret_cast<const void *>(&tile_bwd_kernel<VW, CH, VP>), tile_lds_max(VW), lds_ok,
-                          "tile_bwd_kernel"))
-        return s;
+template <int VW, int CH, bool VP, typename InT>
+int launch_tile_bwd_kernel(const SpmmPlan &sp, int64_t I, int64_t O, int64_t B, const int32_t *tab,
+                           const snack_coo_desc *W, const InT *dY, const InT *X, float *part, float *dW,
+                           hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(round_up8(static_cast<int64_t>(sp.tncb) * sp.tnrb)));
-    hipLaunchKernelGGL((tile_bwd_kernel<VW, CH, VP>), grid, dim3(kTileThreads), lds, st, static_cast<int>(I),
+    hipLaunchKernelGGL((tile_bwd_kernel<VW, CH, VP, InT>), grid, dim3(kTileThreads), 0, st, static_cast<int>(I),
                        sp.tncb, sp.tnrb, sp.tcw, sp.tkpr, tab, W->col_rows, W->vals, VP ? W->col_perm : nullptr,
-                       sp.tnnz, dyt, static_cast<int>(O), static_cast<int>(sp.bpad), xt, part, dW);
+                       sp.tnnz, dY, static_cast<int>(O), X, B, part, dW);
     return check_hip("tile_bwd_kernel");
 }
 
-template <int VW, bool VP>
-int launch_tile_bwd_ch(const SpmmPlan &sp, int64_t I, int64_t O, const int32_t *tab, const snack_coo_desc *W,
-                       const float *dyt, const float *xt, float *part, float *dW, hipStream_t st) {
-    if (sp.tch <= 2) return launch_tile_bwd_kernel<VW, 2, VP>(sp, I, O, tab, W, dyt, xt, part, dW, st);
-    return launch_tile_bwd_kernel<VW, 4, VP>(sp, I, O, tab, W, dyt, xt, part, dW, st);
+template <int VW, bool VP, typename InT>
+int launch_tile_bwd_ch(const SpmmPlan &sp, int64_t I, int64_t O, int64_t B, const int32_t *tab,
+                       const snack_coo_desc *W, const InT *dY, const InT *X, float *part, float *dW, hipStream_t st) {
+    if (sp.tch <= 2) return launch_tile_bwd_kernel<VW, 2, VP>(sp, I, O, B, tab, W, dY, X, part, dW, st);
+    return launch_tile_bwd_kernel<VW, 4, VP>(sp, I, O, B, tab, W, dY, X, part, dW, st);
 }
 
-// Both gradients in one tiled pass (BwdPlan.tiled): db, one launch for the feature-major copies of
-// X and dY, tile_bwd_kernel over the column view (dW written directly; values in row order read
-// and dW written through col_perm), then the block sums of dX.  The probe brackets the last two.
+// Both gradients in one tiled pass (BwdPlan.tiled): db, tile_bwd_kernel over the column view
+// reading X and dY in place (dW written directly; values in row order read and dW written through
+// col_perm), then the block sums of dX.  The probe brackets the last two.
 template <typename OutT>
-int run_tiled_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *X, const void *dY, int64_t batch,
-                  int act_dtype, OutT *dX, float *db, float *dW, char *ws, hipStream_t st) {
+int run_tiled_bwd(const BwdPlan &p, const snack_coo_desc *W, const OutT *X, const OutT *dY, int64_t batch,
+                  OutT *dX, float *db, float *dW, char *ws, hipStream_t st) {
     const int64_t O = W->out_features, I = W->in_features;
     const SpmmPlan &sp = p.sp;
     if (db) {
         const dim3 grid(static_cast<unsigned>(ceil_div(O, kBlock)));
-        if (act_dtype == SNACK_F32)
-            hipLaunchKernelGGL(bias_grad_kernel<float>, grid, dim3(kBlock), 0, st, O, batch,
-                               static_cast<const float *>(dY), db);
-        else
-            hipLaunchKernelGGL(bias_grad_kernel<bf16_t>, grid, dim3(kBlock), 0, st, O, batch,
-                               static_cast<const bf16_t *>(dY), db);
+        hipLaunchKernelGGL(bias_grad_kernel<OutT>, grid, dim3(kBlock), 0, st, O, batch, dY, db);
         if (int s = check_hip("bias_grad_kernel")) return s;
     }
-    float *xt = reinterpret_cast<float *>(ws + p.off_x);
-    float *dyt = reinterpret_cast<float *>(ws + p.off_dy);
-    if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st, dY, O, dyt, p.bpad)) return s;
     char *sws = ws + p.off_spmm;
     float *part = reinterpret_cast<float *>(sws + sp.off_part);
     probe(true, st);
@@ -3805,12 +3805,12 @@ int run_tiled_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *X, cons
     const bool vp = W->row_to_col == nullptr;  // values in row order: read and write through col_perm
     int s;
     switch (sp.ttb * 2 + (vp ? 1 : 0)) {
-        case 33: s = launch_tile_bwd_ch<1, true>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
-        case 32: s = launch_tile_bwd_ch<1, false>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
-        case 65: s = launch_tile_bwd_ch<2, true>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
-        case 64: s = launch_tile_bwd_ch<2, false>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
-        case 129: s = launch_tile_bwd_ch<4, true>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
-        case 128: s = launch_tile_bwd_ch<4, false>(sp, I, O, tab, W, dyt, xt, part, dW, st); break;
+        case 33: s = launch_tile_bwd_ch<1, true>(sp, I, O, batch, tab, W, dY, X, part, dW, st); break;
+        case 32: s = launch_tile_bwd_ch<1, false>(sp, I, O, batch, tab, W, dY, X, part, dW, st); break;
+        case 65: s = launch_tile_bwd_ch<2, true>(sp, I, O, batch, tab, W, dY, X, part, dW, st); break;
+        case 64: s = launch_tile_bwd_ch<2, false>(sp, I, O, batch, tab, W, dY, X, part, dW, st); break;
+        case 129: s = launch_tile_bwd_ch<4, true>(sp, I, O, batch, tab, W, dY, X, part, dW, st); break;
+        case 128: s = launch_tile_bwd_ch<4, false>(sp, I, O, batch, tab, W, dY, X, part, dW, st); break;
         default: return fail(SNACK_ERR_INTERNAL, "tiled backward: unsupported batch tile %d", sp.ttb);
     }
     if (s) return s;
@@ -3863,10 +3863,12 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
             char *ws = static_cast<char *>(workspace);
             hipStream_t st = static_cast<hipStream_t>(hip_stream);
             const int s = act_dtype == SNACK_F32
-                              ? run_tiled_bwd<float>(p, W, X, dY, batch, act_dtype, static_cast<float *>(dX), db, dW,
-                                                     ws, st)
-                              : run_tiled_bwd<bf16_t>(p, W, X, dY, batch, act_dtype, static_cast<bf16_t *>(dX), db,
-                                                      dW, ws, st);
+                              ? run_tiled_bwd<float>(p, W, static_cast<const float *>(X),
+                                                     static_cast<const float *>(dY), batch, static_cast<float *>(dX),
+                                                     db, dW, ws, st)
+                              : run_tiled_bwd<bf16_t>(p, W, static_cast<const bf16_t *>(X),
+                                                      static_cast<const bf16_t *>(dY), batch,
+                                                      static_cast<bf16_t *>(dX), db, dW, ws, st);
             return s ? s : snack::ok();
         }
         if (p.split) {
