@@ -2426,6 +2426,7 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline int64_t round_up8(int64_t x) { return ceil_div(x, kXcds) * kXcds; }
 
 enum Mapping { kSegscan = 0, kRowwave = 1, kScatter = 2, kCsr1 = 3, kCsr1Priv = 4, kTile = 5 };
+constexpr int64_t kPrivMinNnz = int64_t(1) << 21;  // batch-1 input gradient: private copies from here
 constexpr int64_t kScatterLdsFloats = 16384;  // 64 KB private dX copy per workgroup
 
 // Device work plan of one gather-reduce (forward or input gradient).
@@ -2507,8 +2508,7 @@ SpmmPlan plan_spmm_map(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, 
         return p;
     }
     // batch-1 input gradient of a large layer: private per-wave copies of dX, no atomics
-    // (below ~2M entries the atomic scatter's fixed costs are lower)
-    if (B == 1 && scatter_ok && aligned16 && nnz >= (int64_t(1) << 21) && nout <= kPrivMaxI) {
+    if (B == 1 && scatter_ok && aligned16 && nnz >= kPrivMinNnz && nout <= kPrivMaxI) {
         p.direct = true;
         p.mapping = kCsr1Priv;
         // about 256 workgroups per 4 copies of dX that fit a CU's LDS, 4 waves each
@@ -2660,7 +2660,13 @@ SpmmPlan plan_spmm(int64_t nnz, int64_t opnd_rows, int64_t nout, int64_t B, int 
     // with values in column order the input gradient (scatter_ok) walks only the column view, where
     // they are in place: the batch-1 CSR walk of the forward serves it there, and the row walks
     // (private copies, scatter) are not used
-    SpmmPlan p = plan_spmm_map(nnz, opnd_rows, nout, B, dtype, scatter_ok && !colvals, aligned16);
+    // Below kPrivMinNnz entries the batch-1 input gradient walks the column view whatever the value
+    // order (values in row order read through col_perm), as the forward walks the rows: measured on
+    // 10k x 10k layers, 11.2 against 18.9 us at 99 % and 6.9 against 11.1 us at 99.9 % for the LDS
+    // scatter and its reduce.  Above it the permuted reads cost more than the private copies of dX
+    // (38 against 23 us at 95 %).
+    const bool b1_col = B == 1 && nnz < kPrivMinNnz;
+    SpmmPlan p = plan_spmm_map(nnz, opnd_rows, nout, B, dtype, scatter_ok && !colvals && !b1_col, aligned16);
     // the LDS-tiled walk where it applies (values in the walk's order, or read through the
     // permutation: the input gradient with values in row order, the forward in column order)
     if (p.mapping == kRowwave) plan_tile(p, nnz, opnd_rows, nout, B);
@@ -3417,10 +3423,11 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W), colvals);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
-        // values in column order: batch 1 walks the column view as the forward walks the rows
+        // batch 1 walks the column view as the forward walks the rows (values in row order through
+        // col_perm)
         if (p.mapping == kCsr1) {
-            if (int s = launch_csr1(p, act_dtype, I, O, nnz, W->col_offsets, W->col_rows, W->vals, nullptr, dY,
-                                    nullptr, dX, ws, st))
+            if (int s = launch_csr1(p, act_dtype, I, O, nnz, W->col_offsets, W->col_rows, W->vals,
+                                    colvals ? nullptr : W->col_perm, dY, nullptr, dX, ws, st))
                 return s;
             return snack::ok();
         }

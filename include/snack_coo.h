@@ -45,7 +45,9 @@
  *  - Kernel choice: each device call picks its kernels from the layer's size,
  *    the batch and the value order; results agree to rounding whichever runs,
  *    and every kernel is deterministic except the batch-1 input gradient's
- *    LDS-atomic scatter.  Layers of at least 2^20 entries at batches padded to
+ *    LDS-atomic scatter (values in row order, at least 2^21 entries, and
+ *    in_features above 10240 or vals / cols not 16-byte aligned).  Layers of
+ *    at least 2^20 entries at batches padded to
  *    a multiple of 16 take LDS-tiled kernels (operand rows staged in LDS per
  *    column block, see row_blocks / col_blocks).  For tests and measurement,
  *    snack_coo_set_option overrides these choices process-wide (below).
