@@ -281,6 +281,25 @@ def cold_kernel_times(layer, K, ops, flush_bytes=1 << 30, write_flush=False):
     return res
 
 
+def profile_op(layer, op, K, W, flush):
+    """Counter runs (rocprofv3 --pmc): W warm-up steps, then K calls of one op (or of the step),
+    each after a 1 GiB read when flush == "read".  Prints one JSON line."""
+    import torch
+    scratch = torch.zeros((1 << 30) // 4, dtype=torch.float32, device=layer.X.device) if flush == "read" else None
+    for _ in range(W):
+        layer.step()
+    torch.cuda.synchronize()
+    for _ in range(K):
+        if scratch is not None:
+            scratch.sum()
+        if op == "step":
+            layer.step()
+        else:
+            layer.op(op)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_op": op, "calls": K, "warmup_steps": W, "flush": flush}), flush=True)
+
+
 def cpu_model() -> str:
     """The host CPU's model name (from /proc/cpuinfo)."""
     try:
@@ -476,6 +495,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip cold-cache and batch-1 sweeps")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--profile-op", choices=("fwd", "bwd", "dx", "dw", "step"),
+                    help="for counter runs: only --steps calls of this op after --warmup steps")
+    ap.add_argument("--flush", choices=("none", "read"), default="none",
+                    help="with --profile-op: a 1 GiB read before each call (the cold-cache runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -494,6 +517,9 @@ def main():
     name, B, dtype, order = WORKLOADS[args.workload]
     log(f"workload {args.workload}: building layer")
     layer = Layer(name, B, dtype, dev, order)
+    if args.profile_op:
+        profile_op(layer, args.profile_op, args.steps, args.warmup, args.flush)
+        return
     log(f"layer {layer.O}x{layer.I} nnz={layer.nnz} B={B} {dtype} (host build {layer.host_build_s:.1f} s)")
     for _ in range(args.warmup):
         layer.step()
