@@ -490,7 +490,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the default warm-up (about 0.1 s at the headline shape) lets the host and the GPU reach their
+    # steady clocks after the layer build: with 10 steps the eager step measured 109 us, with 1000
+    # steps 96.5 us, the kernels themselves unchanged
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="target95_b64", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip cold-cache and batch-1 sweeps")

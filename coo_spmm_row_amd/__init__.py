@@ -176,6 +176,9 @@ def snack_coo_init_uniform(out_features: int, in_features: int, nnz: int, seed: 
 
 
 # ------------------------------------------------------------------ device side
+_OPTIONAL_ARRAYS = ("col_perm", "col_rows", "col_cols", "col_offsets", "row_to_col", "row_blocks", "col_blocks")
+
+
 class SnackCOO:
     """A layer weight resident on one GPU: the sorted triple, row offsets and
     (optionally) the column view, as torch tensors.  ``vals`` may be updated in
@@ -222,15 +225,16 @@ class SnackCOO:
     def _refresh(self):
         d = self._desc
         d.out_features, d.in_features, d.nnz = self.out_features, self.in_features, self.nnz
-        ptr = lambda x: None if x is None else x.data_ptr()
-        d.rows, d.cols, d.vals, d.row_offsets = ptr(self.rows), ptr(self.cols), ptr(self.vals), ptr(self.row_offsets)
-        d.col_perm, d.col_rows = ptr(self.col_perm), ptr(self.col_rows)
-        d.col_cols, d.col_offsets = ptr(self.col_cols), ptr(self.col_offsets)
-        d.row_to_col = ptr(self.row_to_col)
-        d.row_blocks, d.col_blocks = ptr(self.row_blocks), ptr(self.col_blocks)
+        d.rows, d.cols, d.vals = self.rows.data_ptr(), self.cols.data_ptr(), self.vals.data_ptr()
+        d.row_offsets = self.row_offsets.data_ptr()
+        for name in _OPTIONAL_ARRAYS:
+            x = getattr(self, name)
+            setattr(d, name, None if x is None else x.data_ptr())
 
     @property
     def desc(self):
+        """The C descriptor over the tensors' current addresses (re-read on every access, so
+        tensors whose storage was replaced are never passed stale)."""
         self._refresh()
         return ctypes.byref(self._desc)
 
@@ -303,17 +307,23 @@ def _stream(device, stream):
 
 
 def _stream_handle(device, stream):
-    return ctypes.c_void_p(_stream(device, stream).cuda_stream)
-
-
-def _workspace(device, nbytes: int, workspace=None, stream=None):
-    """(pointer, bytes) of the call's workspace: the caller's `workspace`, else the cached buffer of
-    (device, stream) (see _ws_cache)."""
+    """The hipStream_t of `stream`, else of the current stream of `device` (a torch.device)."""
     import torch
-    if nbytes == 0:
-        return None, 0
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(idx))
+
+
+def _workspace(device, nbytes, workspace=None, stream=None):
+    """(pointer, bytes) of the call's workspace: the caller's `workspace` (the library checks its
+    size), else the cached buffer of (device, stream) (see _ws_cache) of at least nbytes() bytes."""
+    import torch
     if workspace is not None:
         return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    nbytes = nbytes()
+    if nbytes == 0:
+        return None, 0
     s = _stream(device, stream)
     with torch.cuda.stream(s):
         capturing = torch.cuda.is_current_stream_capturing()
@@ -339,8 +349,8 @@ def _check_act(t, rows_expected, cols_expected, name):
         raise ValueError(f"{name} must be a device tensor")
 
 
-def snack_coo_workspace_bytes(op: int, W: SnackCOO, batch: int, act_dtype: int) -> int:
-    return int(_lib.snack_coo_workspace_bytes(op, W.desc, batch, act_dtype))
+def snack_coo_workspace_bytes(op: int, W: SnackCOO, batch: int, act_dtype: int, desc=None) -> int:
+    return int(_lib.snack_coo_workspace_bytes(op, W.desc if desc is None else desc, batch, act_dtype))
 
 
 def snack_coo_fwd(W: SnackCOO, X, bias=None, out=None, workspace=None, stream=None):
@@ -353,8 +363,9 @@ def snack_coo_fwd(W: SnackCOO, X, bias=None, out=None, workspace=None, stream=No
     _check_act(Y, B, W.out_features, "Y")
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != W.out_features):
         raise ValueError("bias must be float32 [out_features]")
-    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_FWD, W, B, dt), workspace, stream)
-    st = _lib.snack_coo_fwd(W.desc, ctypes.c_void_p(X.data_ptr()), B, dt,
+    d = W.desc
+    ws, wsn = _workspace(X.device, lambda: snack_coo_workspace_bytes(OP_FWD, W, B, dt, d), workspace, stream)
+    st = _lib.snack_coo_fwd(d, ctypes.c_void_p(X.data_ptr()), B, dt,
                             None if bias is None else ctypes.c_void_p(bias.data_ptr()),
                             ctypes.c_void_p(Y.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
     _check(st, "snack_coo_fwd")
@@ -391,8 +402,9 @@ def snack_coo_bwd_input(W: SnackCOO, dY, out=None, db=None, workspace=None, stre
     dt = _dtype_code(dY)
     dX = out if out is not None else torch.empty((B, W.in_features), dtype=dY.dtype, device=dY.device)
     _check_act(dX, B, W.in_features, "dX")
-    ws, wsn = _workspace(dY.device, snack_coo_workspace_bytes(OP_BWD_INPUT, W, B, dt), workspace, stream)
-    st = _lib.snack_coo_bwd_input(W.desc, ctypes.c_void_p(dY.data_ptr()), B, dt, ctypes.c_void_p(dX.data_ptr()),
+    d = W.desc
+    ws, wsn = _workspace(dY.device, lambda: snack_coo_workspace_bytes(OP_BWD_INPUT, W, B, dt, d), workspace, stream)
+    st = _lib.snack_coo_bwd_input(d, ctypes.c_void_p(dY.data_ptr()), B, dt, ctypes.c_void_p(dX.data_ptr()),
                                   None if db is None else ctypes.c_void_p(db.data_ptr()), ws, wsn,
                                   _stream_handle(dY.device, stream))
     _check(st, "snack_coo_bwd_input")
@@ -409,8 +421,10 @@ def snack_coo_grad_weight(W: SnackCOO, X, dY, out=None, workspace=None, stream=N
     if _dtype_code(dY) != dt:
         raise TypeError("X and dY must have the same dtype")
     dW = out if out is not None else torch.empty(W.nnz, dtype=torch.float32, device=X.device)
-    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_GRAD_WEIGHT, W, B, dt), workspace, stream)
-    st = _lib.snack_coo_grad_weight(W.desc, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(dY.data_ptr()), B, dt,
+    d = W.desc
+    ws, wsn = _workspace(X.device, lambda: snack_coo_workspace_bytes(OP_GRAD_WEIGHT, W, B, dt, d), workspace,
+                         stream)
+    st = _lib.snack_coo_grad_weight(d, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(dY.data_ptr()), B, dt,
                                     ctypes.c_void_p(dW.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
     _check(st, "snack_coo_grad_weight")
     return dW
@@ -430,8 +444,9 @@ def snack_coo_bwd(W: SnackCOO, X, dY, dx_out=None, dw_out=None, db=None, workspa
     dX = dx_out if dx_out is not None else torch.empty((B, W.in_features), dtype=dY.dtype, device=dY.device)
     _check_act(dX, B, W.in_features, "dX")
     dW = dw_out if dw_out is not None else torch.empty(W.nnz, dtype=torch.float32, device=X.device)
-    ws, wsn = _workspace(X.device, snack_coo_workspace_bytes(OP_BWD, W, B, dt), workspace, stream)
-    st = _lib.snack_coo_bwd(W.desc, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(dY.data_ptr()), B, dt,
+    d = W.desc
+    ws, wsn = _workspace(X.device, lambda: snack_coo_workspace_bytes(OP_BWD, W, B, dt, d), workspace, stream)
+    st = _lib.snack_coo_bwd(d, ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(dY.data_ptr()), B, dt,
                             ctypes.c_void_p(dX.data_ptr()), None if db is None else ctypes.c_void_p(db.data_ptr()),
                             ctypes.c_void_p(dW.data_ptr()), ws, wsn, _stream_handle(X.device, stream))
     _check(st, "snack_coo_bwd")

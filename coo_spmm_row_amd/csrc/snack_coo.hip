@@ -2916,11 +2916,13 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
     // col_perm, the weight gradient over the row view), one after the other, instead of the fused
     // pass: values in row order and one 64-column batch tile (with more tiles, or values in column
     // order, the fused pass measured faster)
-    // default: values in column order take the one tiled pass at 64 columns; values in row order
-    // the two tiled passes (the one tiled pass writes dW through col_perm there, and the scattered
-    // stores cost more than the second pass: 10k/95 %/B = 64 118 against 92 us)
+    // default: values in column order take the one tiled pass (10k x 10k steps, us, against the
+    // one-pass kernel reading dY rows from L2: 90 % B = 16 109 / 121, B = 32 127 / 135, 95 %
+    // B = 16 68 / 69, B = 32 82 / 81, B = 64 97 / 107); values in row order the two tiled passes
+    // (the one tiled pass writes dW through col_perm there, and the scattered stores cost more
+    // than the second pass: 95 % B = 64 step 113 against 148 us)
     const int form = bwd_form_env();
-    const bool tiled_ok = form == 2 || (form < 0 && colvals && Bp == 64);
+    const bool tiled_ok = form == 2 || (form < 0 && colvals);
     if (p.fused && tiled_ok && (Bp == 16 || Bp == 32 || Bp == 64) && Bp * I < (int64_t(1) << 29)) {
         // (the plan of the column-view walk bounds Bp O; X is read in place too)
         const SpmmPlan sp = plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals);

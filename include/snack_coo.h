@@ -223,10 +223,10 @@ int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY
  * results agree with the separate calls to rounding (the summation order of
  * dX differs).  Forms (snack_coo_bwd_is_fused tells which one a call takes):
  * with the tiled kernels applicable (see the conventions above) and one batch
- * tile, values in row order take two tiled passes (the input gradient over the
- * column view, then the weight gradient over the row view, sharing one layout
- * transpose), and values in column order at a padded batch of 64 one tiled
- * pass that serves each staged dY row to both gradients; otherwise the
+ * tile (padded batch 16, 32 or 64), values in row order take two tiled passes
+ * (the input gradient over the column view, then the weight gradient over the
+ * row view, both reading X and dY in place), and values in column order one
+ * tiled pass that serves each staged dY row to both gradients; otherwise the
  * one-pass kernel that gathers each entry's dY row from L2 once for both
  * gradients.  Layers of at least 2^20
  * entries take a row-banded form of that one-pass kernel: the rows are cut into
