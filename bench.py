@@ -373,11 +373,12 @@ def traffic_for(workload, kernel):
 
 def batch_sweep(dev, K, batches=(16, 32)):
     """The step (eager and graph-replayed, us) at small batches on the 10k x 10k layers at 90 and 95 %: the
-    metric's batch range below 64, with the backward's form and the per-op kernel times."""
+    metric's batch range below 64, values in column order as in the headline workload, with the
+    backward's form and the per-op kernel times."""
     out = {}
     for name, label in (("llm90", "90%"), ("target95", "95%")):
         for B in batches:
-            layer = Layer(name, B, "f32", dev)
+            layer = Layer(name, B, "f32", dev, "col")
             for _ in range(3):
                 layer.step()
             e = plain_steps(layer, K)
