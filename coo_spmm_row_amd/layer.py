@@ -162,20 +162,26 @@ class SnackLinear(nn.Module):
                 str(self.rows.device))
 
     def weight_view(self) -> SnackCOO:
-        """The library descriptor over the current tensors (cheap; built per call).  The segment
-        tables of the tiled kernels are built once per structure and device and kept."""
+        """The library descriptor over the current tensors.  It is kept while the structure and the
+        storage of ``vals`` stay the same (in-place updates of the values keep it valid); the
+        segment tables of the tiled kernels are built once per structure and device."""
         key = self._blocks_key_now()
         if getattr(self, "_blocks_key", None) != key:
             self._blocks = (None, None)
             self._blocks_key = key
+            self._view = None
             if self.rows.is_cuda:
                 W = SnackCOO(self.out_features, self.in_features, self.rows, self.cols, self.vals.detach(),
                              self.row_offsets, self.col_perm, self.col_rows, self.col_cols, self.col_offsets)
                 self._blocks = (W.row_blocks, W.col_blocks)
-        return SnackCOO(self.out_features, self.in_features, self.rows, self.cols, self.vals.detach(),
-                        self.row_offsets, self.col_perm, self.col_rows, self.col_cols, self.col_offsets,
-                        self._buffers.get("row_to_col") if self.value_order == "col" else None,
-                        self._blocks[0], self._blocks[1], blocks=None)
+        view = getattr(self, "_view", None)
+        if view is None or view[0] != self.vals.data_ptr():
+            W = SnackCOO(self.out_features, self.in_features, self.rows, self.cols, self.vals.detach(),
+                         self.row_offsets, self.col_perm, self.col_rows, self.col_cols, self.col_offsets,
+                         self._buffers.get("row_to_col") if self.value_order == "col" else None,
+                         self._blocks[0], self._blocks[1], blocks=None)
+            self._view = view = (self.vals.data_ptr(), W)
+        return view[1]
 
     def row_order_vals(self) -> torch.Tensor:
         """The values in row (triple) order, whatever the layer keeps."""
@@ -185,6 +191,13 @@ class SnackLinear(nn.Module):
         if v.is_cuda:
             return snack_coo_gather_f32(v, self.row_to_col)
         return torch.from_numpy(v.numpy()[self.row_to_col.numpy()])
+
+    def __getstate__(self):
+        """Pickling and deepcopy leave out the cached descriptor view (it holds raw device
+        addresses); the copy builds its own on first use."""
+        state = self.__dict__.copy()
+        state.pop("_view", None)
+        return state
 
     # ---------------------------------------------------------------- compute
     def forward(self, X: torch.Tensor) -> torch.Tensor:
@@ -215,6 +228,7 @@ class SnackLinear(nn.Module):
             self.vals.data = W.vals
             self._blocks = (W.row_blocks, W.col_blocks)  # built for the new structure
             self._blocks_key = self._blocks_key_now()
+            self._view = None
             return trials
         out = snack_coo_topology_update(self.out_features, self.in_features, self.rows.cpu().numpy(),
                                         self.cols.cpu().numpy(), self.row_order_vals().cpu().numpy(), n_prune,

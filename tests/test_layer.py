@@ -93,3 +93,22 @@ def test_column_order_layer_host_side(tmp_path):
     assert np.array_equal(col.vals.detach().numpy(), row.vals.detach().numpy()[row.col_perm.numpy()])
     with pytest.raises(ValueError):
         SnackLinear(10, 10, value_order="diagonal")
+
+
+def test_deepcopy_and_pickle_after_a_descriptor_view():
+    """The layer's cached descriptor view holds raw addresses: deepcopy and pickling leave it out, and
+    the copies equal the original."""
+    import copy
+    import pickle
+    for order in ("row", "col"):
+        m = SnackLinear(60, 40, sparsity=0.8, seed=5, value_order=order)
+        W = m.weight_view()
+        assert m.weight_view() is W                      # kept while structure and values stay
+        c = copy.deepcopy(m)
+        p = pickle.loads(pickle.dumps(m))
+        for other in (c, p):
+            assert "_view" not in other.__dict__
+            assert torch.equal(other.vals, m.vals) and torch.equal(other.rows, m.rows)
+            assert other.weight_view().nnz == m.nnz
+        m.vals.data = m.vals.data.clone()                # new storage: a new view
+        assert m.weight_view() is not W
