@@ -475,6 +475,27 @@ def gamlp_inference(dev, K):
     return out
 
 
+def copy_peak_gbs(dev, nbytes=1 << 30, reps=20):
+    """A plain device copy of nbytes (read nbytes, write nbytes), median over reps: the box's own
+    streaming rate, GB/s of reads plus writes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = make_events(2)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / float(np.median(ts)) / 1e9
+
+
 def calibrate_copy(dev, nbytes, reps):
     """A plain elementwise kernel of known size (reads nbytes, writes nbytes), for
     scaling the HBM byte counters."""
@@ -564,6 +585,10 @@ def main():
                 "warm": {"achieved": round(achieved_warm, 1), "frac": round(achieved_warm / HBM_PEAK_GBS, 4),
                          "kernel_us": round(kernel_us[dom], 2), "timing": f"mean of {args.steps} back-to-back calls"},
                 "algorithmic_bytes": nbytes[dom]}
+    log("stream-copy rate of the box (1 GiB device copy)")
+    cp = copy_peak_gbs(dev)
+    roofline["copy_peak"] = {"achieved_gbs": round(cp, 1), "frac": round(achieved / cp, 4),
+                             "note": "cold achieved GB/s against a plain 1 GiB device copy on this box"}
     extras = {"us_per_step_eager": round(eager_us, 2),
               "us_per_step_graph": None if graph_us is None else round(graph_us, 2),
               "step_timing": step_timing,
