@@ -203,11 +203,28 @@ def test_tiled_workspace_bounded_by_batch_tiles():
     assert fwd8192 <= 4 * 5001 * 8192 + 4 * 2_500_000 + (1 << 20)  # operand copy and gathered values
 
 
+def test_tiled_planner_entry_bound():
+    """The tiled walks take 32-bit byte offsets into the per-entry arrays: a layer of 2^29 - 1
+    entries takes them (block partials in the forward's workspace), one of 2^29 does not (host-side
+    sizing only)."""
+    lib = snk._lib
+    d = snk._Desc()
+    n = 1 << 16
+    d.out_features, d.in_features = n, n
+    d.row_offsets = d.rows = d.cols = d.vals = 0x1000
+    nb = -(-n // 638)
+    partials = 4 * 64 * nb * n
+    d.nnz = (1 << 29) - 1
+    assert lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 64, 0) >= partials
+    d.nnz = 1 << 29
+    assert 0 < lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 64, 0) < partials
+
+
 def test_backward_form_rules():
     """The documented choice of snack_coo_bwd's form (host-side planning, no GPU): two tiled passes
     for values in row order at one batch tile of 16, 32 or 64 columns on layers of >= 2^20 entries,
-    two untiled passes at batch 1, one pass otherwise (the tiled pass for column order at 64
-    columns, the L2-gather kernel else); SNACK_OPT_TILE and SNACK_OPT_BWD_FORM override."""
+    two untiled passes at batch 1, one pass otherwise (the tiled pass for column order at one batch
+    tile, the L2-gather kernel else); SNACK_OPT_TILE and SNACK_OPT_BWD_FORM override."""
     lib = snk._lib
     d = snk._Desc()
     d.out_features, d.in_features, d.nnz = 10000, 10000, 5_000_000
