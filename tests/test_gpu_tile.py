@@ -330,18 +330,20 @@ def test_tiled_large_batch(B):
     check_close(dW2.cpu().numpy(), dWr, B, f"bwd dW B={B}")
 
 
+@pytest.mark.parametrize("B", [16, 32, 64])
 @pytest.mark.parametrize("form", ["split", "tiled"])
-def test_backward_forms_bf16(layers, form):
-    """bf16 activations through the two-pass and one-pass tiled backward (dX rounded to bf16)."""
+def test_backward_forms_bf16(layers, form, B):
+    """bf16 activations through the two-pass and one-pass tiled backward at one batch tile of 16,
+    32 or 64 columns (dX rounded to bf16)."""
     L = layers["e1100x7777"]
     O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
     built, W = device_layer(L, DEV)
-    x_in, x64 = acts(8400, 64, I, True)
-    dy_in, dy64 = acts(8401, 64, O, True)
+    x_in, x64 = acts(8400 + B, B, I, True)
+    dy_in, dy64 = acts(8401 + B, B, O, True)
     X, dY = to_device(x_in, DEV, True), to_device(dy_in, DEV, True)
     r, c, v = built["rows"], built["cols"], built["vals"]
     for order, w in (("row", W), ("col", W.to_column_order())):
-        say(f"snack_coo_bwd bf16 form={form} values in {order} order")
+        say(f"snack_coo_bwd bf16 form={form} B={B} values in {order} order")
         with bwd_form(form):
             dX, dW = snk.snack_coo_bwd(w, X, dY)
             torch.cuda.synchronize()
@@ -350,7 +352,7 @@ def test_backward_forms_bf16(layers, form):
             ref_w = ref_w[built["col_perm"].astype(np.int64)]
         check_close(from_device(dX), oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS), nnz / I,
                     f"bf16 bwd dX ({order})", True)
-        check_close(dW.cpu().numpy(), ref_w, 64, f"bf16 bwd dW ({order})", True)
+        check_close(dW.cpu().numpy(), ref_w, B, f"bf16 bwd dW ({order}) B={B}", True)
 
 
 @pytest.mark.parametrize("order", ["row", "col"])
