@@ -45,6 +45,9 @@ WORKLOADS = {
     "xs99_zipf_b1": ("xs99_zipf", 1, "f32", "row"),
     "gpt2_fc_b1024": ("gpt2_fc", 1024, "f32", "row"),
     "gpt2_fc_b1024_bf16": ("gpt2_fc", 1024, "bf16", "row"),
+    # bf16 activations and bf16 weights on the matrix cores (SNACK_BF16_HW)
+    "target95_b64_bf16hw": ("target95", 64, "bf16hw", "col"),
+    "gpt2_fc_b1024_bf16hw": ("gpt2_fc", 1024, "bf16hw", "row"),
     "gamlp90_b1": ("gamlp90", 1, "f32", "row"),
     "gamlp90_b4096": ("gamlp90", 4096, "f32", "row"),
 }
@@ -65,13 +68,17 @@ def algorithmic_bytes(op, nnz, O, I, B, s):
     return 12 * nnz + s * B * I + s * B * O  # dw: rows, cols, write dW; read X and dY
 
 
+def dtype_code(dtype):
+    import coo_spmm_row_amd as snk
+    return {"f32": snk.SNACK_F32, "bf16": snk.SNACK_BF16, "bf16hw": snk.SNACK_BF16_HW}[dtype]
+
+
 def bwd_fused(layer):
     """Whether snack_coo_bwd runs its single column-view pass for this layer and batch (the
     library's own choice, snack_coo_bwd_is_fused); otherwise it runs the two gradients as separate
     passes and the step's dominant kernel is one of the three products.  Labels timings only."""
     import coo_spmm_row_amd as snk
-    code = snk.SNACK_BF16 if layer.dtype == "bf16" else snk.SNACK_F32
-    return snk.snack_coo_bwd_is_fused(layer.W, layer.B, code)
+    return snk.snack_coo_bwd_is_fused(layer.W, layer.B, dtype_code(layer.dtype))
 
 
 def other_order_step(layer, K):
@@ -82,7 +89,7 @@ def other_order_step(layer, K):
     import coo_spmm_row_amd as snk
     W0, ws0 = layer.W, layer.ws
     layer.W = W0.to_row_order() if W0.column_order else W0.to_column_order()
-    code = snk.SNACK_BF16 if layer.dtype == "bf16" else snk.SNACK_F32
+    code = dtype_code(layer.dtype)
     need = max(snk.snack_coo_workspace_bytes(op, layer.W, layer.B, code) for op in (0, 1, 2, 3))
     layer.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=ws0.device)
     try:
@@ -96,6 +103,28 @@ def other_order_step(layer, K):
                 "kernel_us": {op: round(float(np.mean(v)) * 1000.0, 2) for op, v in kern.items()}}
     finally:
         layer.W, layer.ws = W0, ws0
+
+
+def half_weights_step(dev, K):
+    """The headline layer (10k x 10k, 95 %, batch 64, values in column order) with bf16
+    activations, once through the bf16 kernels (fp32 weights) and once through the half-precision
+    path (weights rounded to bf16, forward and input gradient on the matrix cores): eager step and
+    kernel times of the forward, the input gradient and the weight gradient."""
+    import torch
+    out = {}
+    for dt in ("bf16", "bf16hw"):
+        lay = Layer("target95", 64, dt, dev, "col")
+        for _ in range(20):
+            lay.step()
+        torch.cuda.synchronize()
+        e = plain_steps(lay, K)
+        _, kern = timed_steps(lay, K, ("fwd", "dx", "dw"))
+        out["half_weights" if dt == "bf16hw" else "bf16_weights_fp32"] = {
+            "us_per_step_eager": round(e, 2),
+            "kernel_us": {op: round(float(np.mean(v)) * 1000.0, 2) for op, v in kern.items()}}
+        del lay
+        torch.cuda.empty_cache()
+    return out
 
 
 def kernel_source_sha():
@@ -124,28 +153,31 @@ class Layer:
         seeds = synth.seeds_for(spec.config_id, spec.variant)
         self.x = synth.make_acts(seeds["X"](0), B, self.I)
         self.dy = synth.make_acts(seeds["dY"](0), B, self.O)
-        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
         self.X = torch.from_numpy(self.x).to(dev).to(tdt)
         self.dY = torch.from_numpy(self.dy).to(dev).to(tdt)
         self.bias = torch.from_numpy(L["bias"]).to(dev)
         self.Y = torch.empty((B, self.O), dtype=tdt, device=dev)
         self.dX = torch.empty((B, self.I), dtype=tdt, device=dev)
         self.dW = torch.empty(self.nnz, dtype=torch.float32, device=dev)
-        code = snk.SNACK_BF16 if dtype == "bf16" else snk.SNACK_F32
+        code = dtype_code(dtype)
         need = max(snk.snack_coo_workspace_bytes(op, self.W, B, code) for op in (0, 1, 2, 3))
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        self.s = 2 if dtype == "bf16" else 4
+        self.s = 4 if dtype == "f32" else 2
+        self.hw = dtype == "bf16hw"  # weights rounded to bf16, products on the matrix cores
 
     def op(self, name):
         import coo_spmm_row_amd as snk
+        hw = self.hw
         if name == "fwd":
-            snk.snack_coo_fwd(self.W, self.X, self.bias, out=self.Y, workspace=self.ws)
+            snk.snack_coo_fwd(self.W, self.X, self.bias, out=self.Y, workspace=self.ws, half_weights=hw)
         elif name == "dx":
-            snk.snack_coo_bwd_input(self.W, self.dY, out=self.dX, workspace=self.ws)
+            snk.snack_coo_bwd_input(self.W, self.dY, out=self.dX, workspace=self.ws, half_weights=hw)
         elif name == "dw":
-            snk.snack_coo_grad_weight(self.W, self.X, self.dY, out=self.dW, workspace=self.ws)
+            snk.snack_coo_grad_weight(self.W, self.X, self.dY, out=self.dW, workspace=self.ws, half_weights=hw)
         else:  # both gradients in one call
-            snk.snack_coo_bwd(self.W, self.X, self.dY, dx_out=self.dX, dw_out=self.dW, workspace=self.ws)
+            snk.snack_coo_bwd(self.W, self.X, self.dY, dx_out=self.dX, dw_out=self.dW, workspace=self.ws,
+                              half_weights=hw)
 
     def step(self):
         """One layer step: the forward and both gradients (snack_coo_bwd)."""
@@ -626,6 +658,8 @@ def main():
         extras["small_batch_us_per_step"] = batch_sweep(dev, max(10, args.steps // 2))
         log("GAMLP-shaped batch-1 inference")
         extras["gamlp_5000_b1_fwd_us"] = gamlp_inference(dev, max(20, args.steps))
+        log("bf16 activations with fp32 and with half-precision weights")
+        extras["bf16_step_weights"] = half_weights_step(dev, max(10, args.steps // 2))
     line = {
         "metric": "COO SpMM fwd+dX+dW us/call (one layer step)",
         "value": round(step_us, 2),
@@ -637,7 +671,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": "bf16" if dtype == "bf16hw" else dtype,
         "data": "synthetic (seeded uniform positions, N(0,1) activations)",
         "config": {},
         "roofline": roofline,

@@ -23,7 +23,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsnack_coo.so")
 
-SNACK_F32, SNACK_BF16 = 0, 1
+SNACK_F32, SNACK_BF16, SNACK_BF16_HW = 0, 1, 2
 OP_FWD, OP_BWD_INPUT, OP_GRAD_WEIGHT, OP_BWD = 0, 1, 2, 3
 STATUS = {0: "OK", 1: "NULL", 2: "SHAPE", 3: "INDEX", 4: "DUPLICATE", 5: "ALIGN", 6: "DTYPE",
           7: "WORKSPACE", 8: "HIP", 9: "INTERNAL", 10: "NOMEM", 11: "UNSORTED"}
@@ -292,8 +292,14 @@ _ws_cache = {}
 _ws_captured = []
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(t, half_weights: bool = False) -> int:
+    """The activation dtype code of tensor t; half_weights selects SNACK_BF16_HW (bf16 weights on
+    the matrix cores), which takes bf16 activations."""
     import torch
+    if half_weights:
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"half_weights takes bfloat16 activations, got {t.dtype}")
+        return SNACK_BF16_HW
     if t.dtype == torch.float32:
         return SNACK_F32
     if t.dtype == torch.bfloat16:
@@ -353,12 +359,13 @@ def snack_coo_workspace_bytes(op: int, W: SnackCOO, batch: int, act_dtype: int, 
     return int(_lib.snack_coo_workspace_bytes(op, W.desc if desc is None else desc, batch, act_dtype))
 
 
-def snack_coo_fwd(W: SnackCOO, X, bias=None, out=None, workspace=None, stream=None):
-    """Y = X W^T + bias (Y has X's dtype)."""
+def snack_coo_fwd(W: SnackCOO, X, bias=None, out=None, workspace=None, stream=None, half_weights=False):
+    """Y = X W^T + bias (Y has X's dtype); half_weights: the weights rounded to bf16 and the
+    products on the matrix cores (SNACK_BF16_HW, bf16 X)."""
     import torch
     _check_act(X, None, W.in_features, "X")
     B = X.shape[0]
-    dt = _dtype_code(X)
+    dt = _dtype_code(X, half_weights)
     Y = out if out is not None else torch.empty((B, W.out_features), dtype=X.dtype, device=X.device)
     _check_act(Y, B, W.out_features, "Y")
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != W.out_features):
@@ -375,13 +382,13 @@ def snack_coo_fwd(W: SnackCOO, X, bias=None, out=None, workspace=None, stream=No
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
-def snack_coo_fwd_noalloc(W: SnackCOO, X, out, bias=None, stream=None):
+def snack_coo_fwd_noalloc(W: SnackCOO, X, out, bias=None, stream=None, half_weights=False):
     """snack_coo_fwd with its workspace in the library's static device scratch (nothing allocated:
     ``out`` is required).  Calls on one device share the scratch and must not overlap."""
     import torch
     _check_act(X, None, W.in_features, "X")
     B = X.shape[0]
-    dt = _dtype_code(X)
+    dt = _dtype_code(X, half_weights)
     _check_act(out, B, W.out_features, "Y")
     if out.dtype != X.dtype:
         raise TypeError("Y must have X's dtype")
@@ -394,12 +401,13 @@ def snack_coo_fwd_noalloc(W: SnackCOO, X, out, bias=None, stream=None):
     return out
 
 
-def snack_coo_bwd_input(W: SnackCOO, dY, out=None, db=None, workspace=None, stream=None):
-    """dX = dY W (dX has dY's dtype); if ``db`` (float32 [O]) is given it receives sum_b dY[b]."""
+def snack_coo_bwd_input(W: SnackCOO, dY, out=None, db=None, workspace=None, stream=None, half_weights=False):
+    """dX = dY W (dX has dY's dtype); if ``db`` (float32 [O]) is given it receives sum_b dY[b];
+    half_weights as for snack_coo_fwd."""
     import torch
     _check_act(dY, None, W.out_features, "dY")
     B = dY.shape[0]
-    dt = _dtype_code(dY)
+    dt = _dtype_code(dY, half_weights)
     dX = out if out is not None else torch.empty((B, W.in_features), dtype=dY.dtype, device=dY.device)
     _check_act(dX, B, W.in_features, "dX")
     d = W.desc
@@ -411,14 +419,14 @@ def snack_coo_bwd_input(W: SnackCOO, dY, out=None, db=None, workspace=None, stre
     return dX
 
 
-def snack_coo_grad_weight(W: SnackCOO, X, dY, out=None, workspace=None, stream=None):
+def snack_coo_grad_weight(W: SnackCOO, X, dY, out=None, workspace=None, stream=None, half_weights=False):
     """dW[k] = sum_b dY[b, rows[k]] X[b, cols[k]] (float32 [nnz])."""
     import torch
     _check_act(X, None, W.in_features, "X")
     B = X.shape[0]
     _check_act(dY, B, W.out_features, "dY")
-    dt = _dtype_code(X)
-    if _dtype_code(dY) != dt:
+    dt = _dtype_code(X, half_weights)
+    if _dtype_code(dY, half_weights) != dt:
         raise TypeError("X and dY must have the same dtype")
     dW = out if out is not None else torch.empty(W.nnz, dtype=torch.float32, device=X.device)
     d = W.desc
@@ -430,7 +438,8 @@ def snack_coo_grad_weight(W: SnackCOO, X, dY, out=None, workspace=None, stream=N
     return dW
 
 
-def snack_coo_bwd(W: SnackCOO, X, dY, dx_out=None, dw_out=None, db=None, workspace=None, stream=None):
+def snack_coo_bwd(W: SnackCOO, X, dY, dx_out=None, dw_out=None, db=None, workspace=None, stream=None,
+                  half_weights=False):
     """Both gradients in one call: returns (dX, dW) as snack_coo_bwd_input and
     snack_coo_grad_weight would (dX has dY's dtype, dW float32 [nnz]); ``db`` as for
     snack_coo_bwd_input."""
@@ -438,8 +447,8 @@ def snack_coo_bwd(W: SnackCOO, X, dY, dx_out=None, dw_out=None, db=None, workspa
     _check_act(X, None, W.in_features, "X")
     B = X.shape[0]
     _check_act(dY, B, W.out_features, "dY")
-    dt = _dtype_code(X)
-    if _dtype_code(dY) != dt:
+    dt = _dtype_code(X, half_weights)
+    if _dtype_code(dY, half_weights) != dt:
         raise TypeError("X and dY must have the same dtype")
     dX = dx_out if dx_out is not None else torch.empty((B, W.in_features), dtype=dY.dtype, device=dY.device)
     _check_act(dX, B, W.in_features, "dX")

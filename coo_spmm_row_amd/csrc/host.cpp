@@ -82,7 +82,7 @@ using namespace snack;
 
 extern "C" const char *snack_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int snack_coo_abi_version(void) { return 9; }
+extern "C" int snack_coo_abi_version(void) { return 10; }
 
 namespace snack {
 namespace {

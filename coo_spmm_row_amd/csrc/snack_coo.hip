@@ -1355,6 +1355,214 @@ __global__ __launch_bounds__(kBlock) void tile_sum_kernel(const float *__restric
     }
 }
 
+// ---------------------------------------------------------------- half-precision weights on MFMA
+// The stored fp32 values are rounded to bf16 (nearest even) as they are read, and the products run
+// on gfx950's v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation) over tiles of W made
+// dense in LDS from the stored entries; W is never dense in HBM.  The pages name Tensor-Core
+// SNACK-COO for fp16/bf16 as future work (Conclusion, Limitations, and Future Work).
+//
+// Gather-reduce over a view (the forward over the row order, the input gradient over the column
+// view): out[b][key] = bias[key] + sum over the key's entries e of bf16(v_e) * act[b][gidx_e], as a
+// product of the dense tile W_view[keys][gather indices] (MFMA operand A, rows = keys) with the
+// activations (operand B, columns = batch).  A workgroup owns 64 keys x 64 batch columns (2 x 2
+// MFMA blocks of 32 x 32) and a run of the segment lists' blocks (a K group); it walks each block
+// in two halves of 336 gather indices (from the block's 8-aligned start): it writes the half's
+// entries of its keys into a zeroed LDS slab [64 keys][336] as bf16, its 4 waves take the half's
+// 16-index MFMA steps in contiguous runs (wave w steps 6w .. 6w + 5), and the written cells are
+// zeroed again.  Each wave reads its steps' activation operands (8 consecutive bf16 of one batch
+// row per lane) straight from the batch-major activations before the half's entries are written;
+// contiguous steps make each wave read whole 128-byte lines of a batch row (interleaved steps had
+// four waves fetch every line, each using a quarter, and the L1 fill rate bound the kernel).  The
+// 44 KB slab lets three workgroups share a CU.  At the end the waves' partial tiles are added in
+// wave order through LDS: with one K group the sum plus the bias is the output, else it goes to
+// part[bt][group][key][64] and tile_sum_kernel adds the groups in order.  The result does not
+// depend on timing.
+// A zero of the slab times a non-finite activation gives NaN: a NaN or infinite activation
+// reaches every key of its tile, as in a dense product with a masked weight.
+typedef __bf16 hw_bf8 __attribute__((ext_vector_type(8)));
+typedef float hw_f16 __attribute__((ext_vector_type(16)));
+
+constexpr int kHwThreads = 256;
+constexpr int kHwKeys = 64;                          // keys per workgroup: two MFMA row blocks of 32
+constexpr int kHwTb = 64;                            // batch columns per workgroup: two MFMA column blocks
+constexpr int kHwCols = 336;                         // slab columns: half of a block's <= 645 from an 8-aligned start
+constexpr int kHwSteps = kHwCols / 16;               // MFMA steps of 16 gather indices per half
+constexpr int kHwWaveSteps = (kHwSteps + 3) / 4;     // steps per wave and half
+constexpr int kHwRowBytes = 2 * kHwCols + 16;        // padded: consecutive slab rows start 4 banks apart
+constexpr int kHwCombineLd = kHwKeys + 1;            // floats per row of the combine buffer (bank spread)
+constexpr int kHwWgTarget = 768;                     // K groups make about this many workgroups (3 per CU)
+static_assert(2 * kHwCols >= 638 + 7, "two halves cover a block from its 8-aligned start");
+static_assert(kHwKeys * kHwRowBytes >= 4 * 32 * kHwCombineLd * 4, "combine buffer (one column block) fits the slab");
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN
+__device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// segs: the view's segment lists ({key, start, end, 0} per block and list position, keys of a
+// 32-key window together); act: bf16 [B][ngather], B * ngather * 2 + 2048 < 2^31, ngather a
+// multiple of 8 and act 16-byte aligned (each operand load is 16 aligned bytes).  Blocks
+// [bpg * z, bpg * z + bpg) for blockIdx.z = z; part: NULL (one K group: out written here) or the
+// fp32 partials [gridDim.y][gridDim.z][nkeys][64].
+template <bool VP, typename OutT>
+__global__ __launch_bounds__(kHwThreads, 3) void hw_spmm_kernel(int nkeys, int ngather, int ncb, int cw, int bpg,
+                                                               const int32_t *__restrict__ segs,
+                                                               const int32_t *__restrict__ gidx,
+                                                               const float *__restrict__ vals,
+                                                               const int32_t *__restrict__ perm, int nnz,
+                                                               const bf16_t *__restrict__ act, int64_t B,
+                                                               const float *__restrict__ bias, OutT *__restrict__ out,
+                                                               float *__restrict__ part) {
+    __shared__ __attribute__((aligned(16))) unsigned char slab[kHwKeys * kHwRowBytes];
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const int k0 = blockIdx.x * kHwKeys;
+    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kHwTb;
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    for (int i = t; i < kHwKeys * kHwRowBytes / 16; i += kHwThreads)
+        reinterpret_cast<uint4 *>(slab)[i] = make_uint4(0u, 0u, 0u, 0u);
+    // entry writers: 4 threads per list position of the tile
+    const int pos = k0 + t / 4, sub = t % 4;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
+    // activation operands: lane (n = lane % 32, half = lane / 32) reads batch row b0 + 32 nb + n,
+    // gather indices [base + 8 half, base + 8 half + 8) of each of its steps
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(act), static_cast<short>(0), static_cast<int>(B * ngather * 2), 0x00020000);
+    const int half = lane / 32, n = lane % 32;
+    int arow[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t b = b0 + 32 * nb + n;
+        arow[nb] = b < B ? static_cast<int>(b * ngather * 2) : kBufPast;  // rows past the batch read 0
+    }
+    hw_f16 acc[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+    __syncthreads();
+    const int cb_lo = static_cast<int>(blockIdx.z) * bpg, cb_hi = min(ncb, cb_lo + bpg);
+    for (int cb = cb_lo; cb < cb_hi; ++cb) {
+        const int g_lo = cb * cw, g0 = g_lo & ~7;
+        const int g_hi = min(g_lo + cw, ngather);
+        const v4i rec = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, pos < nkeys ? (cb * nkeys + pos) * 16 : kBufPast, 0, 0);
+        const int e_end = pos < nkeys ? rec.z : 0;
+        int ecur = rec.y + sub;  // this thread's next entry of the block (every 4th of its key's run)
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+            const int hs = g0 + kHwCols * h;  // the half's first gather index
+            if (hs >= g_hi) break;            // uniform: depends on the block only
+            const int he = min(hs + kHwCols, g_hi);
+            const int nsteps = (he - hs + 15) / 16;
+            const int row_off = (rec.x - k0) * kHwRowBytes - 2 * hs;
+            // this wave's activation operands for the half (issued first, used after the writes)
+            hw_bf8 bq[kHwWaveSteps][2];
+#pragma unroll
+            for (int q = 0; q < kHwWaveSteps; ++q) {
+                const int s = kHwWaveSteps * w + q;
+                const int col = (hs + 16 * s + 8 * half) * 2;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const int off = s < nsteps && arow[nb] != kBufPast ? arow[nb] + col : kBufPast;
+                    bq[q][nb] = __builtin_bit_cast(hw_bf8, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+                }
+            }
+            // the half's entries of this thread: a prefix of the rest of its run (sorted by index)
+            const int e_first = ecur;
+            for (;;) {
+                int g[4], v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = ecur + 4 * u;
+                    const int off = e < e_end ? e * 4 : kBufPast;
+                    g[u] = e < e_end ? buf_ld(rg, off) : 0x7FFFFFFF;
+                    v[u] = buf_ld(rv, VP ? (e < e_end ? buf_ld(rp, off) * 4 : kBufPast) : off);
+                }
+                int n_in = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (g[u] < he) {
+                        *reinterpret_cast<uint16_t *>(slab + row_off + 2 * g[u]) = bf16_bits_rne(__int_as_float(v[u]));
+                        ++n_in;
+                    }
+                }
+                ecur += 4 * n_in;
+                if (n_in < 4) break;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kHwWaveSteps; ++q) {
+                const int s = kHwWaveSteps * w + q;
+                if (s < nsteps) {
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb) {
+                        const hw_bf8 a = *reinterpret_cast<const hw_bf8 *>(
+                            slab + (32 * mb + n) * kHwRowBytes + 2 * (16 * s + 8 * half));
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb)
+                            acc[mb][nb] =
+                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[q][nb], acc[mb][nb], 0, 0, 0);
+                    }
+                }
+            }
+            __syncthreads();
+            // zero the cells written above (their gather indices read again)
+            for (int e0 = e_first; e0 < ecur; e0 += 16) {
+                int g[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) g[u] = buf_ld(rg, e0 + 4 * u < ecur ? (e0 + 4 * u) * 4 : kBufPast);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (e0 + 4 * u < ecur) *reinterpret_cast<uint16_t *>(slab + row_off + 2 * g[u]) = 0;
+            }
+            __syncthreads();
+        }
+    }
+    // the waves' partial tiles, added in wave order, one column block (32 batch columns) at a
+    // time: accumulator r of lane (n, half) in block (mb, nb) is key 32 mb + 8 (r / 4) + 4 half +
+    // r % 4, batch column 32 nb + n
+    float *cbuf = reinterpret_cast<float *>(slab);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                cbuf[(w * 32 + n) * kHwCombineLd + 32 * mb + 8 * (r / 4) + 4 * half + r % 4] = acc[mb][nb][r];
+        __syncthreads();
+        if (!part) {
+            const int key = t % kHwKeys;
+            const float bv = bias && k0 + key < nkeys ? bias[k0 + key] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int bc = t / kHwKeys + 4 * j;
+                float s = cbuf[bc * kHwCombineLd + key];
+#pragma unroll
+                for (int ww = 1; ww < 4; ++ww) s += cbuf[(ww * 32 + bc) * kHwCombineLd + key];
+                const int64_t b = b0 + 32 * nb + bc;
+                if (k0 + key < nkeys && b < B) store_act(out, b * nkeys + k0 + key, s + bv);
+            }
+        } else {
+            const int bc = t % 32;
+            float *pp = part + (static_cast<int64_t>(blockIdx.y) * gridDim.z + blockIdx.z) * nkeys * kHwTb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int key = t / 32 + 8 * j;
+                float s = cbuf[bc * kHwCombineLd + key];
+#pragma unroll
+                for (int ww = 1; ww < 4; ++ww) s += cbuf[(ww * 32 + bc) * kHwCombineLd + key];
+                if (k0 + key < nkeys) pp[static_cast<int64_t>(k0 + key) * kHwTb + 32 * nb + bc] = s;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- weight gradient
 // xt [I][B], dyt [O][B] feature-major fp32.  A group of BT lanes per entry; lane
 // t covers batch columns t*VW + m*BT*VW (+0..VW-1).  Four steps of G entries are
@@ -3230,9 +3438,99 @@ int run_spmm(const SpmmPlan &p, int64_t nkeys, int64_t nnz, const int32_t *keys,
 
 }  // namespace
 
+namespace {
+
+// Half-precision weights (SNACK_BF16_HW): the MFMA gather-reduce over one view.  K groups: runs
+// of the view's blocks split over workgroups so that about kHwWgTarget run (three per CU), their
+// partial tiles summed in group order by tile_sum_kernel.  Workspace: the partials (more than
+// one group), then the view's segment lists when the descriptor has none.
+struct HwPlan {
+    int64_t ncb, cw, nkt, nbt, nkg, bpg;
+    size_t off_part, off_tab, total;
+};
+
+HwPlan plan_hw(int64_t nkeys, int64_t ngather, int64_t B, const int32_t *blocks) {
+    HwPlan p{};
+    tile_blocks(ngather, p.ncb, p.cw);
+    p.nkt = ceil_div(nkeys, kHwKeys);
+    p.nbt = ceil_div(B, kHwTb);
+    const int64_t tiles = std::max<int64_t>(1, p.nkt * p.nbt);
+    p.nkg = std::min<int64_t>(p.ncb, std::max<int64_t>(1, ceil_div(kHwWgTarget, tiles)));
+    p.bpg = ceil_div(p.ncb, p.nkg);
+    p.nkg = ceil_div(p.ncb, p.bpg);
+    size_t at = 0;
+    p.off_part = at;
+    if (p.nkg > 1 && nkeys > 0) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nbt * p.nkg * nkeys * kHwTb));
+    p.off_tab = at;
+    if (!blocks && nkeys > 0) at = align_up(at + static_cast<size_t>(nkeys * p.ncb) * 16);
+    p.total = at;
+    return p;
+}
+
+size_t hw_spmm_bytes(int64_t nkeys, int64_t ngather, int64_t B, const int32_t *blocks) {
+    if (nkeys == 0 || B == 0) return 0;
+    return plan_hw(nkeys, ngather, B, blocks).total;
+}
+
+// What hw_spmm_kernel assumes of a call: 16-byte operand loads from 16-byte aligned rows, 32-bit
+// byte offsets into the activations, the entry arrays and the segment lists.
+int hw_spmm_check(int64_t nkeys, int64_t ngather, int64_t nnz, int64_t B, const void *act, const char *name,
+                  const char *who) {
+    if (ngather % 8)
+        return fail(SNACK_ERR_SHAPE, "%s: half-precision weights need %s's feature count to be a multiple of 8 (%lld)",
+                    who, name, (long long)ngather);
+    if (ngather > 0 && reinterpret_cast<uintptr_t>(act) % 16)
+        return fail(SNACK_ERR_ALIGN, "%s: half-precision weights need %s 16-byte aligned", who, name);
+    if ((B * ngather + 1024) * 2 >= (int64_t(1) << 31))
+        return fail(SNACK_ERR_SHAPE, "%s: %s of %lld x %lld elements is beyond the half-precision path's 2^30", who,
+                    name, (long long)B, (long long)ngather);
+    int64_t ncb, cw;
+    tile_blocks(ngather, ncb, cw);
+    if (nnz >= (int64_t(1) << 29) || nkeys * ncb * 4 >= (int64_t(1) << 29))
+        return fail(SNACK_ERR_SHAPE, "%s: layer beyond the half-precision path's 2^29 entries", who);
+    return SNACK_OK;
+}
+
+int launch_hw_spmm(int64_t nkeys, int64_t ngather, int64_t nnz, const int32_t *offs, const int32_t *gidx,
+                   const float *vals, const int32_t *perm, const int32_t *blocks, const void *act, int64_t B,
+                   const float *bias, void *out, char *ws, hipStream_t st) {
+    if (nkeys == 0 || B == 0) return SNACK_OK;
+    const HwPlan p = plan_hw(nkeys, ngather, B, blocks);
+    const int32_t *tab = blocks;
+    if (!tab) {
+        int32_t *t = reinterpret_cast<int32_t *>(ws + p.off_tab);
+        if (int s = launch_bounds(nkeys, static_cast<int>(p.ncb), static_cast<int>(p.cw), offs, gidx, t, st)) return s;
+        tab = t;
+    }
+    float *part = p.nkg > 1 ? reinterpret_cast<float *>(ws + p.off_part) : nullptr;
+    const dim3 grid(static_cast<unsigned>(p.nkt), static_cast<unsigned>(p.nbt), static_cast<unsigned>(p.nkg));
+    const int nk = static_cast<int>(nkeys), ng = static_cast<int>(ngather), nc = static_cast<int>(p.ncb),
+              w = static_cast<int>(p.cw), bpg = static_cast<int>(p.bpg), nz = static_cast<int>(nnz);
+    const bf16_t *a = static_cast<const bf16_t *>(act);
+    bf16_t *o = static_cast<bf16_t *>(out);
+    probe(true, st);
+    if (perm)
+        hipLaunchKernelGGL((hw_spmm_kernel<true, bf16_t>), grid, dim3(kHwThreads), 0, st, nk, ng, nc, w, bpg, tab,
+                           gidx, vals, perm, nz, a, B, bias, o, part);
+    else
+        hipLaunchKernelGGL((hw_spmm_kernel<false, bf16_t>), grid, dim3(kHwThreads), 0, st, nk, ng, nc, w, bpg, tab,
+                           gidx, vals, nullptr, nz, a, B, bias, o, part);
+    if (int s = check_hip("hw_spmm_kernel")) return s;
+    if (part) {
+        constexpr int kw = 4 * kBlock / kHwTb;
+        const dim3 sgrid(static_cast<unsigned>(ceil_div(nkeys, kw)), static_cast<unsigned>(p.nbt));
+        hipLaunchKernelGGL((tile_sum_kernel<bf16_t, kHwTb>), sgrid, dim3(kBlock), 0, st, part, nk,
+                           static_cast<int>(p.nkg), B, bias, o, nkeys);
+        if (int s = check_hip("tile_sum_kernel")) return s;
+    }
+    probe(false, st);
+    return SNACK_OK;
+}
+}  // namespace
+
 // ================================================================ C ABI
 extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int64_t batch, int act_dtype) {
-    if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16) {
+    if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16 && act_dtype != SNACK_BF16_HW) {
         fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown dtype %d", act_dtype);
         return 0;
     }
@@ -3242,6 +3540,17 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
     }
     const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
     const bool cv = W->row_to_col != nullptr;
+    if (act_dtype == SNACK_BF16_HW) {
+        const size_t dx = hw_spmm_bytes(I, O, batch, W->col_blocks);
+        const size_t dw = plan_sddmm(nnz, O, I, batch, SNACK_BF16, cv).total;
+        switch (op) {
+            case SNACK_OP_FWD: return hw_spmm_bytes(O, I, batch, W->row_blocks);
+            case SNACK_OP_BWD_INPUT: return dx;
+            case SNACK_OP_GRAD_WEIGHT: return dw;
+            case SNACK_OP_BWD: return std::max(dx, dw);
+            default: fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown op %d", op); return 0;
+        }
+    }
     switch (op) {
         case SNACK_OP_FWD: return plan_spmm(nnz, I, O, batch, act_dtype, false, false, cv).total;
         case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W), cv).total;
@@ -3304,7 +3613,7 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
     try {
         const char *who = "snack_coo_fwd";
         if (int s = check_desc(W, false, who)) return s;
-        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
+        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16 && act_dtype != SNACK_BF16_HW)
             return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
         if (batch < 0 || batch > kMaxBatch)
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
@@ -3312,6 +3621,15 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         if (batch == 0 || O == 0) return snack::ok();
         if (I > 0) { if (int s = check_act(X, act_dtype, "X", who)) return s; }
         if (int s = check_act(Y, act_dtype, "Y", who)) return s;
+        if (act_dtype == SNACK_BF16_HW) {
+            if (int s = hw_spmm_check(O, I, nnz, batch, X, "X", who)) return s;
+            if (int s = check_workspace(workspace, workspace_bytes, hw_spmm_bytes(O, I, batch, W->row_blocks), who)) return s;
+            // the row walk reads values in column order through row_to_col
+            if (int s = launch_hw_spmm(O, I, nnz, W->row_offsets, W->cols, W->vals, W->row_to_col, W->row_blocks, X,
+                                       batch, bias, Y, static_cast<char *>(workspace), static_cast<hipStream_t>(hip_stream)))
+                return s;
+            return snack::ok();
+        }
         const SpmmPlan p = plan_spmm(nnz, I, O, batch, act_dtype, false, false, W->row_to_col != nullptr);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -3401,7 +3719,7 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
     try {
         const char *who = "snack_coo_bwd_input";
         if (int s = check_desc(W, true, who)) return s;
-        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
+        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16 && act_dtype != SNACK_BF16_HW)
             return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
         if (batch < 0 || batch > kMaxBatch)
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
@@ -3409,6 +3727,9 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
         if (batch > 0 && O > 0) { if (int s = check_act(dY, act_dtype, "dY", who)) return s; }
         if (batch > 0 && I > 0) { if (int s = check_act(dX, act_dtype, "dX", who)) return s; }
+        if (act_dtype == SNACK_BF16_HW && batch > 0 && I > 0) {
+            if (int s = hw_spmm_check(I, O, nnz, batch, dY, "dY", who)) return s;
+        }
         if (db && O > 0) {
             if (reinterpret_cast<uintptr_t>(db) % 4) return fail(SNACK_ERR_ALIGN, "%s: db misaligned", who);
             const dim3 grid(static_cast<unsigned>(ceil_div(O, kBlock)));
@@ -3422,6 +3743,14 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         }
         if (batch == 0 || I == 0) return snack::ok();
         const bool colvals = W->row_to_col != nullptr;
+        if (act_dtype == SNACK_BF16_HW) {
+            if (int s = check_workspace(workspace, workspace_bytes, hw_spmm_bytes(I, O, batch, W->col_blocks), who)) return s;
+            // the column walk reads values in row order through col_perm, values in column order in place
+            if (int s = launch_hw_spmm(I, O, nnz, W->col_offsets, W->col_rows, W->vals, colvals ? nullptr : W->col_perm,
+                                       W->col_blocks, dY, batch, nullptr, dX, static_cast<char *>(workspace), st))
+                return s;
+            return snack::ok();
+        }
         const SpmmPlan p = plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W), colvals);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);
@@ -3520,8 +3849,9 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
     try {
         const char *who = "snack_coo_grad_weight";
         if (int s = check_desc(W, false, who)) return s;
-        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
+        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16 && act_dtype != SNACK_BF16_HW)
             return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
+        if (act_dtype == SNACK_BF16_HW) act_dtype = SNACK_BF16;  // dW does not read the weights
         if (batch < 0 || batch > kMaxBatch)
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
@@ -3841,6 +4171,7 @@ int run_tiled_bwd(const BwdPlan &p, const snack_coo_desc *W, const OutT *X, cons
 extern "C" int snack_coo_bwd_is_fused(const snack_coo_desc *W, int64_t batch, int act_dtype) {
     try {
         if (int s = check_desc(W, true, "snack_coo_bwd_is_fused")) return -s;
+        if (act_dtype == SNACK_BF16_HW) return 0;
         const BwdPlan p = plan_bwd(W->nnz, W->out_features, W->in_features, batch, act_dtype, vec16(W),
                                    W->row_to_col != nullptr);
         return p.fused || p.tiled ? 1 : 0;
@@ -3855,10 +4186,16 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
     try {
         const char *who = "snack_coo_bwd";
         if (int s = check_desc(W, true, who)) return s;
-        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16)
+        if (act_dtype != SNACK_F32 && act_dtype != SNACK_BF16 && act_dtype != SNACK_BF16_HW)
             return fail(SNACK_ERR_DTYPE, "%s: unknown dtype %d", who, act_dtype);
         if (batch < 0 || batch > kMaxBatch)
             return fail(SNACK_ERR_SHAPE, "%s: batch %lld outside [0, 2^21]", who, (long long)batch);
+        if (act_dtype == SNACK_BF16_HW) {
+            // the input gradient on MFMA, then the weight gradient (which does not read the weights)
+            if (int s = snack_coo_bwd_input(W, dY, batch, act_dtype, dX, db, workspace, workspace_bytes, hip_stream))
+                return s;
+            return snack_coo_grad_weight(W, X, dY, batch, act_dtype, dW, workspace, workspace_bytes, hip_stream);
+        }
         const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
         const BwdPlan p = plan_bwd(nnz, O, I, batch, act_dtype, vec16(W), W->row_to_col != nullptr);
         if (p.tiled) {

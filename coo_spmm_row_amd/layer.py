@@ -45,27 +45,30 @@ class SnackLinearFunction(torch.autograd.Function):
     """
 
     @staticmethod
-    def forward(ctx, X: torch.Tensor, vals: torch.Tensor, bias: Optional[torch.Tensor], weight: SnackCOO):
-        Y = snack_coo_fwd(weight, X, bias)
+    def forward(ctx, X: torch.Tensor, vals: torch.Tensor, bias: Optional[torch.Tensor], weight: SnackCOO,
+                half_weights: bool = False):
+        hw = bool(half_weights) and X.dtype == torch.bfloat16
+        Y = snack_coo_fwd(weight, X, bias, half_weights=hw)
         ctx.save_for_backward(X)
         ctx.weight = weight
+        ctx.hw = hw
         return Y
 
     @staticmethod
     def backward(ctx, dY: torch.Tensor):
         (X,) = ctx.saved_tensors
-        W = ctx.weight
+        W, hw = ctx.weight, ctx.hw
         need_x, need_v, need_b = ctx.needs_input_grad[:3]
         dY = dY.to(X.dtype).contiguous()
         db = torch.empty(W.out_features, dtype=torch.float32, device=dY.device) if need_b else None
         dX = dW = None
         if need_v and (need_x or need_b):
-            dX, dW = snack_coo_bwd(W, X, dY, db=db)
+            dX, dW = snack_coo_bwd(W, X, dY, db=db, half_weights=hw)
         elif need_v:
-            dW = snack_coo_grad_weight(W, X, dY)
+            dW = snack_coo_grad_weight(W, X, dY, half_weights=hw)
         elif need_x or need_b:
-            dX = snack_coo_bwd_input(W, dY, db=db)
-        return (dX if need_x else None), dW, db, None
+            dX = snack_coo_bwd_input(W, dY, db=db, half_weights=hw)
+        return (dX if need_x else None), dW, db, None, None
 
 
 class SnackLinear(nn.Module):
@@ -74,15 +77,19 @@ class SnackLinear(nn.Module):
 
     Give either ``sparsity`` (fraction of zero weights) or ``nnz``.  Inputs are ``[..., in_features]``
     in float32 or bfloat16 on the layer's GPU (bfloat16 in, bfloat16 out, fp32 accumulation);
-    there is no CPU path.
+    there is no CPU path.  ``half_weights`` (bfloat16 inputs only): the stored values are rounded
+    to bfloat16 as the kernels read them and the forward and input-gradient products run on the
+    matrix cores (SNACK_BF16_HW); the trainable values stay fp32.
     """
 
     def __init__(self, in_features: int, out_features: int, sparsity: float = 0.9, bias: bool = True,
-                 seed: int = 0, nnz: Optional[int] = None, device=None, value_order: str = "row"):
+                 seed: int = 0, nnz: Optional[int] = None, device=None, value_order: str = "row",
+                 half_weights: bool = False):
         super().__init__()
         if value_order not in _ORDERS:
             raise ValueError(f"value_order must be one of {_ORDERS}")
         self.value_order = value_order
+        self.half_weights = bool(half_weights)
         self.in_features, self.out_features = int(in_features), int(out_features)
         cells = self.in_features * self.out_features
         if nnz is None:
@@ -205,7 +212,7 @@ class SnackLinear(nn.Module):
             raise ValueError(f"input has {X.shape[-1]} features, expected {self.in_features}")
         lead = X.shape[:-1]
         X2 = X.reshape(-1, self.in_features).contiguous()
-        Y = SnackLinearFunction.apply(X2, self.vals, self.bias, self.weight_view())
+        Y = SnackLinearFunction.apply(X2, self.vals, self.bias, self.weight_view(), getattr(self, "half_weights", False))
         return Y.reshape(*lead, self.out_features)
 
     # ---------------------------------------------------------------- topology update (Appendix G)

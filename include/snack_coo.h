@@ -36,7 +36,22 @@
  *    Y[batch][O], dY[batch][O], dX[batch][I]), contiguous.  Indices are int32,
  *    0-based; vals, bias, dW and db are fp32.  Activations are fp32 or bf16
  *    (SNACK_BF16: X, dY read as bf16; Y, dX written as bf16 rounded to nearest
- *    even from fp32 accumulators).  All outputs are overwritten.
+ *    even from fp32 accumulators).  SNACK_BF16_HW, the half-precision path
+ *    (the Tensor-Core SNACK-COO for fp16/bf16 that the SNACK paper names as
+ *    future work, Conclusion, Limitations, and Future Work): activations as for
+ *    SNACK_BF16, and the weights in bf16 too -- each stored fp32 value is
+ *    rounded to bf16 (nearest even) as it is read -- with the products of the
+ *    forward and the input gradient run on gfx950's bf16 matrix cores (MFMA)
+ *    over tiles of W made dense in LDS (never in device memory); fp32
+ *    accumulation; deterministic.  The weight gradient does not read the
+ *    weights and is the same as with SNACK_BF16.  It needs the gathered
+ *    activation's feature count (I for the forward, O for the input gradient)
+ *    to be a multiple of 8 and that activation 16-byte aligned
+ *    (SNACK_ERR_SHAPE / SNACK_ERR_ALIGN otherwise), and it is meant for
+ *    batches of 32 and more (the matrix-core tiles are 32 batch rows wide).
+ *    Every product of a dense tile includes the zeros of W: a NaN or infinite
+ *    activation turns every output of its 64-key tile into NaN, as a dense
+ *    product with a masked weight would.  All outputs are overwritten.
  *  - Preconditions on a descriptor (established by snack_coo_build, checked
  *    there, NOT re-checked by device calls): entries sorted by (row, col),
  *    unique, in range; row_offsets and the column view consistent with them.
@@ -77,7 +92,7 @@ typedef enum snack_status {
     SNACK_ERR_UNSORTED = 11    /* topology: input triple not strictly sorted by (row, col) */
 } snack_status;
 
-enum { SNACK_F32 = 0, SNACK_BF16 = 1 };                                   /* activation dtype */
+enum { SNACK_F32 = 0, SNACK_BF16 = 1, SNACK_BF16_HW = 2 };               /* activation dtype */
 enum { SNACK_OP_FWD = 0, SNACK_OP_BWD_INPUT = 1, SNACK_OP_GRAD_WEIGHT = 2, SNACK_OP_BWD = 3 };
 
 /* A layer's weight on the device.  Every pointer is a DEVICE pointer,
@@ -332,12 +347,13 @@ int snack_coo_set_probe(void *start_event, void *stop_event);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *snack_last_error(void);
 
-/* ABI version of this header: 9.  3 added snack_coo_init_uniform, 4 the device topology update,
+/* ABI version of this header: 10.  3 added snack_coo_init_uniform, 4 the device topology update,
  * 5 values in column order (snack_coo_desc.row_to_col, snack_coo_invert_perm, snack_coo_gather_f32),
  * 6 the segment tables (snack_coo_desc.row_blocks / col_blocks, snack_coo_block_offsets_count,
  * snack_coo_block_offsets), 7 the kernel-selection options (snack_coo_set_option,
  * snack_coo_get_option) in place of environment variables, 8 snack_coo_fwd_noalloc, 9 segment
- * tables as per-block lists of {key, start, end} ordered by length within windows of 32 keys. */
+ * tables as per-block lists of {key, start, end} ordered by length within windows of 32 keys,
+ * 10 the half-precision path (act_dtype SNACK_BF16_HW). */
 int snack_coo_abi_version(void);
 
 /* Kernel-selection overrides for tests and measurement (not part of the method).  Process-wide,

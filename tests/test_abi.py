@@ -29,7 +29,7 @@ def test_abi_version():
                             "snack_coo.h")).read()
     m = re.search(r"ABI version of this header: (\d+)", hdr)
     assert m, "header states no ABI version"
-    assert snk.abi_version() == int(m.group(1)) == 9
+    assert snk.abi_version() == int(m.group(1)) == 10
 
 
 def test_binding_loads_only_the_in_tree_library():
@@ -243,3 +243,36 @@ def test_backward_form_rules():
                              ((snk.OPT_BWD_FORM, 1), 0)):
         with snk.option(opt, val):
             assert fused(64) == want, (opt, val)
+
+
+def test_half_precision_host_checks_and_workspace():
+    """SNACK_BF16_HW (2): accepted by every device call and the workspace query, checked before any
+    launch (gathered feature count a multiple of 8, activations 16-byte aligned), never the fused
+    backward; its workspace holds the K groups' partial tiles (10k x 10k at batch 64: 4 groups of
+    10000 x 64 fp32) and, without the descriptor's tables, the segment lists."""
+    lib = snk._lib
+    HW = snk.SNACK_BF16_HW
+    assert HW == 2
+    d = snk._Desc()
+    d.out_features, d.in_features, d.nnz = 10000, 10000, 5_000_000
+    d.row_offsets = d.rows = d.cols = d.vals = 0x1000  # host-side sizing and checks only
+    d.col_perm = d.col_rows = d.col_cols = d.col_offsets = 0x1000
+    tables = 10000 * 16 * 16  # keys x blocks x 16 bytes
+    part = 4 * 10000 * 64 * 4
+    assert lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 64, HW) == part + tables
+    d.row_blocks = d.col_blocks = 0x1000
+    assert lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 64, HW) == part
+    assert lib.snack_coo_workspace_bytes(1, ctypes.byref(d), 64, HW) == part
+    assert lib.snack_coo_workspace_bytes(3, ctypes.byref(d), 64, HW) >= part
+    assert lib.snack_coo_workspace_bytes(0, ctypes.byref(d), 64, 3) == 0  # unknown dtype
+    assert lib.snack_coo_bwd_is_fused(ctypes.byref(d), 64, HW) == 0
+    # I = 10000 is a multiple of 8; X 8- but not 16-byte aligned
+    assert lib.snack_coo_fwd(ctypes.byref(d), 0x1008, 64, HW, None, 0x2000, 0x10000, 1 << 30, None) == 5
+    assert b"16-byte" in lib.snack_last_error()
+    d.in_features = 9996  # not a multiple of 8
+    assert lib.snack_coo_fwd(ctypes.byref(d), 0x1000, 64, HW, None, 0x2000, 0x10000, 1 << 30, None) == 2
+    assert b"multiple of 8" in lib.snack_last_error()
+    d.in_features, d.out_features = 10000, 9996  # the input gradient gathers over O
+    assert lib.snack_coo_bwd_input(ctypes.byref(d), 0x1000, 64, HW, 0x2000, None, 0x10000, 1 << 30, None) == 2
+    assert lib.snack_coo_bwd(ctypes.byref(d), 0x1000, 0x1000, 64, HW, 0x2000, None, 0x3000, 0x10000, 1 << 30,
+                             None) == 2
