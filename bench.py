@@ -48,6 +48,8 @@ WORKLOADS = {
     # bf16 activations and bf16 weights on the matrix cores (SNACK_BF16_HW)
     "target95_b64_bf16hw": ("target95", 64, "bf16hw", "col"),
     "gpt2_fc_b1024_bf16hw": ("gpt2_fc", 1024, "bf16hw", "row"),
+    "gamlp90_b4096_bf16": ("gamlp90", 4096, "bf16", "row"),
+    "gamlp90_b4096_bf16hw": ("gamlp90", 4096, "bf16hw", "row"),
     "gamlp90_b1": ("gamlp90", 1, "f32", "row"),
     "gamlp90_b4096": ("gamlp90", 4096, "f32", "row"),
 }

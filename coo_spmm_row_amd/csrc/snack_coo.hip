@@ -1563,6 +1563,167 @@ __global__ __launch_bounds__(kHwThreads, 3) void hw_spmm_kernel(int nkeys, int n
     }
 }
 
+// Wide batches: the same gather-reduce with the densified slab shared by kHwWaves batch tiles.
+// A workgroup owns 64 keys x 256 batch columns; the slab of a half block is written once by all
+// threads, and wave w multiplies it by batch tile w (columns b0 + 64 w ..) over all of the half's
+// steps, so the entry loads and slab writes are shared by four batch tiles and each wave keeps
+// its own 64 x 64 output tile (no combine across waves).  Operand B loads run six steps ahead.
+constexpr int kHwWideTb = 4 * kHwTb;                 // batch columns per workgroup
+constexpr int kHwAhead = 10;                         // activation operand steps in flight per wave
+constexpr int64_t kHwWideMinPerKey = 64;             // entries per key from which the wide kernel runs
+
+template <bool VP, typename OutT>
+__global__ __launch_bounds__(kHwThreads, 2) void hw_spmm_wide_kernel(int nkeys, int ngather, int ncb, int cw,
+                                                                    int bpg, const int32_t *__restrict__ segs,
+                                                                    const int32_t *__restrict__ gidx,
+                                                                    const float *__restrict__ vals,
+                                                                    const int32_t *__restrict__ perm, int nnz,
+                                                                    const bf16_t *__restrict__ act, int64_t B,
+                                                                    const float *__restrict__ bias,
+                                                                    OutT *__restrict__ out, float *__restrict__ part) {
+    __shared__ __attribute__((aligned(16))) unsigned char slab[kHwKeys * kHwRowBytes];
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const int k0 = blockIdx.x * kHwKeys;
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kHwWideTb + kHwTb * w;  // this wave's batch tile
+    const bool active = b0 < B;                                                     // uniform per wave
+    for (int i = t; i < kHwKeys * kHwRowBytes / 16; i += kHwThreads)
+        reinterpret_cast<uint4 *>(slab)[i] = make_uint4(0u, 0u, 0u, 0u);
+    const int pos = k0 + t / 4, sub = t % 4;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(act), static_cast<short>(0), static_cast<int>(B * ngather * 2), 0x00020000);
+    const int half = lane / 32, n = lane % 32;
+    int arow[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int64_t b = b0 + 32 * nb + n;
+        arow[nb] = b < B ? static_cast<int>(b * ngather * 2) : kBufPast;
+    }
+    hw_f16 acc[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+    __syncthreads();
+    const int cb_lo = static_cast<int>(blockIdx.z) * bpg, cb_hi = min(ncb, cb_lo + bpg);
+    for (int cb = cb_lo; cb < cb_hi; ++cb) {
+        const int g_lo = cb * cw, g0 = g_lo & ~7;
+        const int g_hi = min(g_lo + cw, ngather);
+        const v4i rec = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, pos < nkeys ? (cb * nkeys + pos) * 16 : kBufPast, 0, 0);
+        const int e_end = pos < nkeys ? rec.z : 0;
+        int ecur = rec.y + sub;
+#pragma unroll 1
+        for (int h = 0; h < 2; ++h) {
+            const int hs = g0 + kHwCols * h;
+            if (hs >= g_hi) break;  // uniform: depends on the block only
+            const int he = min(hs + kHwCols, g_hi);
+            const int nsteps = (he - hs + 15) / 16;
+            const int row_off = (rec.x - k0) * kHwRowBytes - 2 * hs;
+            auto bload = [&](int s, int nb) {
+                const int off = active && s < nsteps && arow[nb] != kBufPast ? arow[nb] + (hs + 16 * s + 8 * half) * 2
+                                                                              : kBufPast;
+                return __builtin_bit_cast(hw_bf8, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+            };
+            hw_bf8 bq[kHwSteps][2];
+#pragma unroll
+            for (int s = 0; s < kHwAhead; ++s)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) bq[s][nb] = bload(s, nb);
+            const int e_first = ecur;
+            for (;;) {
+                int g[4], v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = ecur + 4 * u;
+                    const int off = e < e_end ? e * 4 : kBufPast;
+                    g[u] = e < e_end ? buf_ld(rg, off) : 0x7FFFFFFF;
+                    v[u] = buf_ld(rv, VP ? (e < e_end ? buf_ld(rp, off) * 4 : kBufPast) : off);
+                }
+                int n_in = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (g[u] < he) {
+                        *reinterpret_cast<uint16_t *>(slab + row_off + 2 * g[u]) = bf16_bits_rne(__int_as_float(v[u]));
+                        ++n_in;
+                    }
+                }
+                ecur += 4 * n_in;
+                if (n_in < 4) break;
+            }
+            __syncthreads();
+            if (active) {
+#pragma unroll
+                for (int s = 0; s < kHwSteps; ++s) {
+                    if (s + kHwAhead < kHwSteps) {
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb) bq[s + kHwAhead][nb] = bload(s + kHwAhead, nb);
+                    }
+                    if (s < nsteps) {
+#pragma unroll
+                        for (int mb = 0; mb < 2; ++mb) {
+                            const hw_bf8 a = *reinterpret_cast<const hw_bf8 *>(
+                                slab + (32 * mb + n) * kHwRowBytes + 2 * (16 * s + 8 * half));
+#pragma unroll
+                            for (int nb = 0; nb < 2; ++nb)
+                                acc[mb][nb] =
+                                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s][nb], acc[mb][nb], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            for (int e0 = e_first; e0 < ecur; e0 += 16) {
+                int g[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) g[u] = buf_ld(rg, e0 + 4 * u < ecur ? (e0 + 4 * u) * 4 : kBufPast);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (e0 + 4 * u < ecur) *reinterpret_cast<uint16_t *>(slab + row_off + 2 * g[u]) = 0;
+            }
+            __syncthreads();
+        }
+    }
+    // each wave's 64 x 64 tile through its quarter of the slab as fp32 [64 batch columns][65]:
+    // accumulator r of lane (n, half) in block (mb, nb) is key 32 mb + 8 (r / 4) + 4 half + r % 4,
+    // batch column 32 nb + n
+    static_assert(kHwKeys * kHwRowBytes >= kHwThreads / kWave * kHwTb * kHwCombineLd * 4 / 2,
+                  "two waves' tiles fit the slab at a time");
+    float *cbuf = reinterpret_cast<float *>(slab) + (w % 2) * kHwTb * kHwCombineLd;
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {  // waves 0 and 1, then 2 and 3
+        if (w / 2 == pass && active) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        cbuf[(32 * nb + n) * kHwCombineLd + 32 * mb + 8 * (r / 4) + 4 * half + r % 4] = acc[mb][nb][r];
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (!part) {
+                const int key = k0 + lane;  // lane = key within the tile (64 keys)
+                const float bv = bias && key < nkeys ? bias[key] : 0.f;
+                for (int bc = 0; bc < kHwTb; ++bc) {
+                    const int64_t b = b0 + bc;
+                    if (key < nkeys && b < B) store_act(out, b * nkeys + key, cbuf[bc * kHwCombineLd + lane] + bv);
+                }
+            } else {
+                const int bt = static_cast<int>(b0 / kHwTb);
+                float *pp = part + (static_cast<int64_t>(bt) * gridDim.z + blockIdx.z) * nkeys * kHwTb;
+                for (int r = 0; r < kHwKeys; ++r)
+                    if (k0 + r < nkeys) pp[static_cast<int64_t>(k0 + r) * kHwTb + lane] = cbuf[lane * kHwCombineLd + r];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- weight gradient
 // xt [I][B], dyt [O][B] feature-major fp32.  A group of BT lanes per entry; lane
 // t covers batch columns t*VW + m*BT*VW (+0..VW-1).  Four steps of G entries are
@@ -3445,17 +3606,24 @@ namespace {
 // partial tiles summed in group order by tile_sum_kernel.  Workspace: the partials (more than
 // one group), then the view's segment lists when the descriptor has none.
 struct HwPlan {
-    int64_t ncb, cw, nkt, nbt, nkg, bpg;
+    int64_t ncb, cw, nkt, nbt, ngy, nkg, bpg;
+    bool wide;  // hw_spmm_wide_kernel: batches beyond one tile share each densified slab
     size_t off_part, off_tab, total;
 };
 
-HwPlan plan_hw(int64_t nkeys, int64_t ngather, int64_t B, const int32_t *blocks) {
+HwPlan plan_hw(int64_t nkeys, int64_t ngather, int64_t nnz, int64_t B, const int32_t *blocks) {
     HwPlan p{};
     tile_blocks(ngather, p.ncb, p.cw);
     p.nkt = ceil_div(nkeys, kHwKeys);
     p.nbt = ceil_div(B, kHwTb);
-    const int64_t tiles = std::max<int64_t>(1, p.nkt * p.nbt);
-    p.nkg = std::min<int64_t>(p.ncb, std::max<int64_t>(1, ceil_div(kHwWgTarget, tiles)));
+    // keys averaging 64 entries or more: the slab writes cost enough to share them over four
+    // batch tiles; with fewer, one batch tile per workgroup keeps more MFMA work in flight
+    p.wide = p.nbt > 1 && nnz >= kHwWideMinPerKey * nkeys;
+    p.ngy = p.wide ? ceil_div(B, kHwWideTb) : p.nbt;
+    // K groups: about kHwWgTarget workgroups (three per CU), or two per CU for the wide kernel
+    const int64_t target = p.wide ? 512 : kHwWgTarget;
+    const int64_t tiles = std::max<int64_t>(1, p.nkt * p.ngy);
+    p.nkg = std::min<int64_t>(p.ncb, std::max<int64_t>(1, ceil_div(target, tiles)));
     p.bpg = ceil_div(p.ncb, p.nkg);
     p.nkg = ceil_div(p.ncb, p.bpg);
     size_t at = 0;
@@ -3467,9 +3635,9 @@ HwPlan plan_hw(int64_t nkeys, int64_t ngather, int64_t B, const int32_t *blocks)
     return p;
 }
 
-size_t hw_spmm_bytes(int64_t nkeys, int64_t ngather, int64_t B, const int32_t *blocks) {
+size_t hw_spmm_bytes(int64_t nkeys, int64_t ngather, int64_t nnz, int64_t B, const int32_t *blocks) {
     if (nkeys == 0 || B == 0) return 0;
-    return plan_hw(nkeys, ngather, B, blocks).total;
+    return plan_hw(nkeys, ngather, nnz, B, blocks).total;
 }
 
 // What hw_spmm_kernel assumes of a call: 16-byte operand loads from 16-byte aligned rows, 32-bit
@@ -3495,7 +3663,7 @@ int launch_hw_spmm(int64_t nkeys, int64_t ngather, int64_t nnz, const int32_t *o
                    const float *vals, const int32_t *perm, const int32_t *blocks, const void *act, int64_t B,
                    const float *bias, void *out, char *ws, hipStream_t st) {
     if (nkeys == 0 || B == 0) return SNACK_OK;
-    const HwPlan p = plan_hw(nkeys, ngather, B, blocks);
+    const HwPlan p = plan_hw(nkeys, ngather, nnz, B, blocks);
     const int32_t *tab = blocks;
     if (!tab) {
         int32_t *t = reinterpret_cast<int32_t *>(ws + p.off_tab);
@@ -3503,19 +3671,25 @@ int launch_hw_spmm(int64_t nkeys, int64_t ngather, int64_t nnz, const int32_t *o
         tab = t;
     }
     float *part = p.nkg > 1 ? reinterpret_cast<float *>(ws + p.off_part) : nullptr;
-    const dim3 grid(static_cast<unsigned>(p.nkt), static_cast<unsigned>(p.nbt), static_cast<unsigned>(p.nkg));
+    const dim3 grid(static_cast<unsigned>(p.nkt), static_cast<unsigned>(p.ngy), static_cast<unsigned>(p.nkg));
     const int nk = static_cast<int>(nkeys), ng = static_cast<int>(ngather), nc = static_cast<int>(p.ncb),
               w = static_cast<int>(p.cw), bpg = static_cast<int>(p.bpg), nz = static_cast<int>(nnz);
     const bf16_t *a = static_cast<const bf16_t *>(act);
     bf16_t *o = static_cast<bf16_t *>(out);
     probe(true, st);
-    if (perm)
+    if (p.wide && perm)
+        hipLaunchKernelGGL((hw_spmm_wide_kernel<true, bf16_t>), grid, dim3(kHwThreads), 0, st, nk, ng, nc, w, bpg,
+                           tab, gidx, vals, perm, nz, a, B, bias, o, part);
+    else if (p.wide)
+        hipLaunchKernelGGL((hw_spmm_wide_kernel<false, bf16_t>), grid, dim3(kHwThreads), 0, st, nk, ng, nc, w, bpg,
+                           tab, gidx, vals, nullptr, nz, a, B, bias, o, part);
+    else if (perm)
         hipLaunchKernelGGL((hw_spmm_kernel<true, bf16_t>), grid, dim3(kHwThreads), 0, st, nk, ng, nc, w, bpg, tab,
                            gidx, vals, perm, nz, a, B, bias, o, part);
     else
         hipLaunchKernelGGL((hw_spmm_kernel<false, bf16_t>), grid, dim3(kHwThreads), 0, st, nk, ng, nc, w, bpg, tab,
                            gidx, vals, nullptr, nz, a, B, bias, o, part);
-    if (int s = check_hip("hw_spmm_kernel")) return s;
+    if (int s = check_hip(p.wide ? "hw_spmm_wide_kernel" : "hw_spmm_kernel")) return s;
     if (part) {
         constexpr int kw = 4 * kBlock / kHwTb;
         const dim3 sgrid(static_cast<unsigned>(ceil_div(nkeys, kw)), static_cast<unsigned>(p.nbt));
@@ -3541,10 +3715,10 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
     const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
     const bool cv = W->row_to_col != nullptr;
     if (act_dtype == SNACK_BF16_HW) {
-        const size_t dx = hw_spmm_bytes(I, O, batch, W->col_blocks);
+        const size_t dx = hw_spmm_bytes(I, O, nnz, batch, W->col_blocks);
         const size_t dw = plan_sddmm(nnz, O, I, batch, SNACK_BF16, cv).total;
         switch (op) {
-            case SNACK_OP_FWD: return hw_spmm_bytes(O, I, batch, W->row_blocks);
+            case SNACK_OP_FWD: return hw_spmm_bytes(O, I, nnz, batch, W->row_blocks);
             case SNACK_OP_BWD_INPUT: return dx;
             case SNACK_OP_GRAD_WEIGHT: return dw;
             case SNACK_OP_BWD: return std::max(dx, dw);
@@ -3623,7 +3797,7 @@ extern "C" int snack_coo_fwd(const snack_coo_desc *W, const void *X, int64_t bat
         if (int s = check_act(Y, act_dtype, "Y", who)) return s;
         if (act_dtype == SNACK_BF16_HW) {
             if (int s = hw_spmm_check(O, I, nnz, batch, X, "X", who)) return s;
-            if (int s = check_workspace(workspace, workspace_bytes, hw_spmm_bytes(O, I, batch, W->row_blocks), who)) return s;
+            if (int s = check_workspace(workspace, workspace_bytes, hw_spmm_bytes(O, I, nnz, batch, W->row_blocks), who)) return s;
             // the row walk reads values in column order through row_to_col
             if (int s = launch_hw_spmm(O, I, nnz, W->row_offsets, W->cols, W->vals, W->row_to_col, W->row_blocks, X,
                                        batch, bias, Y, static_cast<char *>(workspace), static_cast<hipStream_t>(hip_stream)))
@@ -3744,7 +3918,7 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
         if (batch == 0 || I == 0) return snack::ok();
         const bool colvals = W->row_to_col != nullptr;
         if (act_dtype == SNACK_BF16_HW) {
-            if (int s = check_workspace(workspace, workspace_bytes, hw_spmm_bytes(I, O, batch, W->col_blocks), who)) return s;
+            if (int s = check_workspace(workspace, workspace_bytes, hw_spmm_bytes(I, O, nnz, batch, W->col_blocks), who)) return s;
             // the column walk reads values in row order through col_perm, values in column order in place
             if (int s = launch_hw_spmm(I, O, nnz, W->col_offsets, W->col_rows, W->vals, colvals ? nullptr : W->col_perm,
                                        W->col_blocks, dY, batch, nullptr, dX, static_cast<char *>(workspace), st))

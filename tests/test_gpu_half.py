@@ -12,7 +12,8 @@ is held to the bf16 tolerance as for SNACK_BF16.
 
 Cases: several column blocks with a narrower last one, a single block (I = 600 < 638), full rows
 and columns (segments of a whole block), empty rows, key counts that leave a partial last tile of
-64 keys, batches of 1, 32, 64, 100 and 130 (partial and several batch tiles), values in row order
+64 keys, batches of 1, 32, 64, 100, 130, 256, 300 and 512 (partial and several batch tiles, the
+wide kernel's groups of four tiles with a partial last group), values in row order
 and in column order (each kernel both with and without the value permutation), the 10000 x 10000
 layer at 95 % and batch 64 in full, reruns equal bit for bit, the allocation-free forward equal to
 the forward, and the shape and alignment errors of the path.
@@ -222,3 +223,24 @@ def test_half_weights_layer(order):
         dWr = dWr[layer.col_perm.cpu().numpy().astype(np.int64)]
     check_close(layer.vals.grad.cpu().numpy(), dWr, n, f"layer half dW ({order})", True)
     check_close(layer.bias.grad.cpu().numpy(), oracle.grad_bias(g64), n, "layer half db")
+
+
+@pytest.mark.parametrize("order", ["row", "col"])
+@pytest.mark.parametrize("B", [256, 300, 512])
+def test_half_wide_batches(layers, B, order):
+    """Batches beyond one 64-column tile take the wide kernel (four batch tiles share each
+    densified slab): one full group of four tiles, a second group with one partial tile (300), two
+    groups (512)."""
+    say(f"half-precision wide batches u3000x5000 B={B} values in {order} order")
+    _run(layers["u3000x5000"], B, 9800 + B, order)
+
+
+@pytest.mark.parametrize("B", [130, 300])
+def test_half_short_keys_wide_batches(B):
+    """Keys averaging under 64 entries stay on one batch tile per workgroup at any batch: the
+    forward of this layer (39 entries per row) runs the per-tile kernel at B > 64, its input
+    gradient (78 per column) the wide one."""
+    L = synth.random_small_layer(709, 1536, 768, 60_000, "uniform")
+    say(f"half-precision short keys s1536x768 B={B}")
+    for order in ("row", "col"):
+        _run(L, B, 9900 + B, order)
