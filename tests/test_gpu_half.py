@@ -244,3 +244,13 @@ def test_half_short_keys_wide_batches(B):
     say(f"half-precision short keys s1536x768 B={B}")
     for order in ("row", "col"):
         _run(L, B, 9900 + B, order)
+
+
+@pytest.mark.parametrize("order", ["row", "col"])
+def test_half_wide_many_tiles(order):
+    """The wide kernel over many tiles without K groups: an 8192 x 1024 layer at 10 % density and
+    batch 1000 (forward: 128 key tiles x 4 batch groups, the last group partial, one K group; input
+    gradient: 16 key tiles x 4 batch groups over 7 K groups, summed by the block sum)."""
+    L = synth.random_small_layer(710, 8192, 1024, 838_861, "uniform")
+    say(f"half-precision wide kernel s8192x1024 B=1000 values in {order} order")
+    _run(L, 1000, 9950, order)
