@@ -254,3 +254,51 @@ def test_half_wide_many_tiles(order):
     L = synth.random_small_layer(710, 8192, 1024, 838_861, "uniform")
     say(f"half-precision wide kernel s8192x1024 B=1000 values in {order} order")
     _run(L, 1000, 9950, order)
+
+
+@pytest.mark.parametrize("B", [64, 300])
+def test_half_graph_replays_match_eager(layers, B):
+    """The half-precision forward, input gradient and backward (K groups with their block sum at
+    batch 64, the wide kernel at 300) captured in a HIP graph and replayed four times with eager
+    work in between: every replay equals the eager result bit for bit."""
+    L = layers["u3000x5000"]
+    say(f"half-precision graph replay B={B}")
+    built, W = device_layer(L, DEV)
+    W = W.to_column_order()
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    X = to_device(acts(9960, B, I, True)[0], DEV, True)
+    dY = to_device(acts(9961, B, O, True)[0], DEV, True)
+    bias = torch.from_numpy(L["bias"]).to(DEV)
+    need = max(snk.snack_coo_workspace_bytes(op, W, B, snk.SNACK_BF16_HW) for op in (0, 1, 3))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
+    Y = torch.empty(B, O, dtype=torch.bfloat16, device=DEV)
+    dX = torch.empty(B, I, dtype=torch.bfloat16, device=DEV)
+    dX2 = torch.empty(B, I, dtype=torch.bfloat16, device=DEV)
+    dW2 = torch.empty(nnz, device=DEV)
+    db2 = torch.empty(O, device=DEV)
+    outs = (Y, dX, dX2, dW2, db2)
+
+    def step():
+        snk.snack_coo_fwd(W, X, bias, out=Y, workspace=ws, half_weights=True)
+        snk.snack_coo_bwd_input(W, dY, out=dX, workspace=ws, half_weights=True)
+        snk.snack_coo_bwd(W, X, dY, dx_out=dX2, dw_out=dW2, db=db2, workspace=ws, half_weights=True)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (got, want) in enumerate(zip(outs, ref)):
+            assert torch.equal(got, want), (rep, i)
