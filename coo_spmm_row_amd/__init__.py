@@ -548,7 +548,7 @@ def abi_version() -> int:
 
 
 # Kernel-selection overrides (snack_coo_set_option): for tests and measurement only.
-OPT_TILE, OPT_BWD_FORM, OPT_BAND_MIN_NNZ, OPT_TOPOLOGY_DRAW_BATCH = 0, 1, 2, 3
+OPT_TILE, OPT_BWD_FORM, OPT_BAND_MIN_NNZ, OPT_TOPOLOGY_DRAW_BATCH, OPT_BF16_DW_MFMA = 0, 1, 2, 3, 4
 
 
 def set_option(opt: int, value: int) -> None:

@@ -86,8 +86,8 @@ extern "C" int snack_coo_abi_version(void) { return 10; }
 
 namespace snack {
 namespace {
-constexpr int kNumOptions = 4;
-std::atomic<int64_t> g_options[kNumOptions] = {{-1}, {-1}, {-1}, {-1}};
+constexpr int kNumOptions = 5;
+std::atomic<int64_t> g_options[kNumOptions] = {{-1}, {-1}, {-1}, {-1}, {-1}};
 }  // namespace
 
 int64_t option(int which) {
@@ -103,6 +103,7 @@ extern "C" int snack_coo_set_option(int opt, int64_t value) {
         case SNACK_OPT_BWD_FORM: okv = okv || (value >= 0 && value <= 2); break;
         case SNACK_OPT_BAND_MIN_NNZ: okv = okv || value >= 0; break;
         case SNACK_OPT_TOPOLOGY_DRAW_BATCH: okv = okv || value >= 1; break;
+        case SNACK_OPT_BF16_DW_MFMA: okv = okv || value == 0 || value == 1; break;
     }
     if (!okv) return fail(SNACK_ERR_SHAPE, "set_option: value %lld out of range for option %d", (long long)value, opt);
     g_options[opt].store(value, std::memory_order_relaxed);

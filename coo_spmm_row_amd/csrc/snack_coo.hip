@@ -1724,6 +1724,133 @@ __global__ __launch_bounds__(kHwThreads, 2) void hw_spmm_wide_kernel(int nkeys, 
     }
 }
 
+// Weight gradient with bf16 activations on the matrix cores (batches of 256 and more).  Each
+// product of two bf16 values is exact in fp32, so this is the bf16 weight gradient (fp32
+// accumulation, in another order) whether or not the weights are half precision.  X and dY are
+// first copied feature-major as bf16 ([features][Bp], Bp the batch rounded up to 16, zero beyond
+// the batch), so that the batch, the product's reduction, is contiguous per lane.  Over the view
+// whose order the values are stored in (the row order: keys = rows, gather = columns; the column
+// view the reverse), a workgroup owns 64 keys (two MFMA row blocks of 32) x 256 gather indices
+// (a third of a segment-list block from its 8-aligned start; wave w takes column blocks 2w and
+// 2w + 1) and computes the dense 64 x 256 product over the batch with
+// v_mfma_f32_32x32x16_bf16, stages it in LDS as fp32, and writes dW for the stored entries of its
+// keys in those 256 indices (each entry belongs to one workgroup: no partial sums).
+constexpr int kHwDwKeys = 64;
+constexpr int kHwDwCols = 256;                      // a third of a block's <= 645 from an 8-aligned start
+constexpr int kHwDwLd = kHwDwCols + 1;              // floats per row of the staged product
+constexpr int kHwDwUnroll = 4;                      // MFMA steps whose operand loads are issued together
+static_assert(3 * kHwDwCols >= 638 + 7, "three thirds cover a block from its 8-aligned start");
+
+// in [B][F] bf16 -> out [F][Bp] bf16, zero for batch rows >= B; tiles of 64 features x 64 rows.
+__global__ __launch_bounds__(kBlock) void bf16_feature_major_kernel(const bf16_t *__restrict__ in, int64_t B,
+                                                                    int64_t F, int64_t Bp, bf16_t *__restrict__ out) {
+    __shared__ uint16_t tile[64][65];
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 64, b0 = static_cast<int64_t>(blockIdx.y) * 64;
+    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t b = b0 + ty + 4 * i, f = f0 + tx;
+        tile[ty + 4 * i][tx] = (b < B && f < F) ? in[b * F + f] : static_cast<uint16_t>(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t f = f0 + ty + 4 * i, b = b0 + tx;
+        if (f < F && b < Bp) out[f * Bp + b] = tile[tx][ty + 4 * i];
+    }
+}
+
+// segs: the view's segment lists; actK [nkeys][Bp], actG [ngather][Bp] (feature-major bf16,
+// (max(nkeys, ngather) + 320) * Bp * 2 < 2^31, Bp a multiple of 16); dW[e] for the view's entry e.
+__global__ __launch_bounds__(kHwThreads) void hw_sddmm_kernel(int nkeys, int ngather, int ncb, int cw, int Bp,
+                                                             const int32_t *__restrict__ segs,
+                                                             const int32_t *__restrict__ gidx, int nnz,
+                                                             const bf16_t *__restrict__ actK,
+                                                             const bf16_t *__restrict__ actG, float *__restrict__ dW) {
+    __shared__ float cbuf[kHwDwKeys * kHwDwLd];
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const int cb = static_cast<int>(blockIdx.y) / 3, third = static_cast<int>(blockIdx.y) % 3;
+    const int g_lo = cb * cw, g0 = g_lo & ~7, g_hi = min(g_lo + cw, ngather);
+    const int ts = g0 + kHwDwCols * third;
+    if (ts >= g_hi) return;  // whole workgroup, before any barrier
+    const int te = min(ts + kHwDwCols, g_hi);
+    const int k0 = blockIdx.x * kHwDwKeys;
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+    const int half = lane / 32, n = lane % 32;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(actK), static_cast<short>(0), static_cast<int>(static_cast<int64_t>(nkeys) * Bp * 2),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rgt = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(actG), static_cast<short>(0), static_cast<int>(static_cast<int64_t>(ngather) * Bp * 2),
+        0x00020000);
+    // operand rows: keys k0 + 32 mb + n (A), gather indices ts + 64 w + 32 nb + n (B); rows past the
+    // copies' ends read 0, rows of the next third or block give products that are never read
+    int ka[2], gb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        ka[i] = (k0 + 32 * i + n) * Bp * 2;
+        gb[i] = (ts + 64 * w + 32 * i + n) * Bp * 2;
+    }
+    hw_f16 acc[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+    const int nsteps = Bp / 16;
+    for (int s0 = 0; s0 < nsteps; s0 += kHwDwUnroll) {
+        hw_bf8 a[kHwDwUnroll][2], b[kHwDwUnroll][2];
+#pragma unroll
+        for (int u = 0; u < kHwDwUnroll; ++u) {
+            const int col = (16 * (s0 + u) + 8 * half) * 2;
+            const bool ok = s0 + u < nsteps;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                a[u][i] = __builtin_bit_cast(hw_bf8, __builtin_amdgcn_raw_buffer_load_b128(rk, ok ? ka[i] + col : kBufPast, 0, 0));
+                b[u][i] = __builtin_bit_cast(hw_bf8, __builtin_amdgcn_raw_buffer_load_b128(rgt, ok ? gb[i] + col : kBufPast, 0, 0));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kHwDwUnroll; ++u)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][mb], b[u][nb], acc[mb][nb], 0, 0, 0);
+    }
+    // the product through LDS: accumulator r of lane (n, half) in block (mb, nb) is key
+    // 32 mb + 8 (r / 4) + 4 half + r % 4, gather index ts + 64 w + 32 nb + n
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                cbuf[(32 * mb + 8 * (r / 4) + 4 * half + r % 4) * kHwDwLd + 64 * w + 32 * nb + n] = acc[mb][nb][r];
+    __syncthreads();
+    // the tile's entries: 4 threads per list position, every 4th entry of its run with a gather
+    // index in [ts, te) (a contiguous part of the run, which is sorted by index)
+    const int pos = k0 + t / 4, sub = t % 4;
+    if (pos >= nkeys) return;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz);
+    const v4i rec = __builtin_amdgcn_raw_buffer_load_b128(rs, (cb * nkeys + pos) * 16, 0, 0);
+    const float *crow = cbuf + (rec.x - k0) * kHwDwLd - ts;
+    for (int e0 = rec.y + sub; e0 < rec.z; e0 += 16) {
+        int g[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) g[u] = e0 + 4 * u < rec.z ? buf_ld(rg, (e0 + 4 * u) * 4) : 0x7FFFFFFF;
+        bool past = false;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (g[u] >= ts && g[u] < te) dW[e0 + 4 * u] = crow[g[u]];
+            past = past || g[u] >= te;
+        }
+        if (past) break;
+    }
+}
+
 // ---------------------------------------------------------------- weight gradient
 // xt [I][B], dyt [O][B] feature-major fp32.  A group of BT lanes per entry; lane
 // t covers batch columns t*VW + m*BT*VW (+0..VW-1).  Four steps of G entries are
@@ -3231,6 +3358,45 @@ int launch_tile_sddmm(const SddmmPlan &p, const snack_coo_desc *W, const void *X
 // Backward pass plan: the fused column-view kernel for (padded) batches 4*BT*Q (Q in 1..4)
 // whose feature-major copies (with their zero rows) stay below 4 GB; otherwise the input
 // gradient and the weight gradient one after the other, sharing the workspace.
+// The weight gradient on the matrix cores (bf16 activations, batches of kHwDwMinB and more):
+// workspace = the feature-major bf16 copies of X and dY, then the view's segment lists when the
+// descriptor has none.
+constexpr int64_t kHwDwMinB = 256;
+
+struct HwDwPlan {
+    bool use;
+    int64_t Bp, ncb, cw;
+    size_t off_x, off_dy, off_tab, total;
+};
+
+HwDwPlan plan_hw_dw(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool colvals, const int32_t *blocks) {
+    HwDwPlan p{};
+    p.Bp = round_up(B, int64_t(16));
+    // the dense products cost O*I*B against the stored products' nnz*B: measured on the matrix cores
+    // they win from about 1/12 density (5000 x 5000 at 10 %, B = 4096: 950 against 1235 us; 10k x
+    // 10k at 5 %, B = 512: 483 against 302 us)
+    const int64_t forced = option(SNACK_OPT_BF16_DW_MFMA);
+    const bool dense_enough = forced == 1 || (forced < 0 && 12 * nnz >= O * I);
+    p.use = (dtype == SNACK_BF16 || dtype == SNACK_BF16_HW) && B >= kHwDwMinB && nnz > 0 && dense_enough &&
+            nnz < (int64_t(1) << 29) && (std::max(O, I) + 320) * p.Bp * 2 < (int64_t(1) << 31);
+    if (!p.use) return p;
+    const int64_t nkeys = colvals ? I : O, ngather = colvals ? O : I;
+    tile_blocks(ngather, p.ncb, p.cw);
+    if (nkeys * p.ncb * 4 >= (int64_t(1) << 29)) {
+        p.use = false;
+        return p;
+    }
+    size_t at = 0;
+    p.off_x = at;
+    at = align_up(at + static_cast<size_t>(I * p.Bp) * 2);
+    p.off_dy = at;
+    at = align_up(at + static_cast<size_t>(O * p.Bp) * 2);
+    p.off_tab = at;
+    if (!blocks) at = align_up(at + static_cast<size_t>(nkeys * p.ncb) * 16);
+    p.total = at;
+    return p;
+}
+
 struct BwdPlan {
     bool fused;
     int bt, q, nb;  // nb: row bands of the fused kernel (1 or kXcds)
@@ -3332,8 +3498,10 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
         if (p.nb > 1) at = align_up(at + sizeof(float) * static_cast<size_t>(p.nb * I * Bp));
         p.total = at;
     } else {
+        // the separate calls; the weight gradient's segment lists counted as if the descriptor had none
+        const HwDwPlan hp = plan_hw_dw(nnz, O, I, B, dtype, colvals, nullptr);
         p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals).total,
-                           plan_sddmm(nnz, O, I, B, dtype, colvals).total);
+                           hp.use ? hp.total : plan_sddmm(nnz, O, I, B, dtype, colvals).total);
     }
     return p;
 }
@@ -3700,6 +3868,41 @@ int launch_hw_spmm(int64_t nkeys, int64_t ngather, int64_t nnz, const int32_t *o
     probe(false, st);
     return SNACK_OK;
 }
+
+// dW over the view the values are stored in (row order, or the column view with values in column
+// order), written in that order.
+int launch_hw_dw(const HwDwPlan &p, const snack_coo_desc *W, const void *X, const void *dY, int64_t B, float *dW,
+                 char *ws, hipStream_t st) {
+    const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+    const bool colvals = W->row_to_col != nullptr;
+    bf16_t *xt = reinterpret_cast<bf16_t *>(ws + p.off_x), *dyt = reinterpret_cast<bf16_t *>(ws + p.off_dy);
+    const dim3 gx(static_cast<unsigned>(ceil_div(I, 64)), static_cast<unsigned>(ceil_div(p.Bp, 64)));
+    const dim3 gy(static_cast<unsigned>(ceil_div(O, 64)), static_cast<unsigned>(ceil_div(p.Bp, 64)));
+    if (I > 0)
+        hipLaunchKernelGGL(bf16_feature_major_kernel, gx, dim3(kBlock), 0, st, static_cast<const bf16_t *>(X), B, I,
+                           p.Bp, xt);
+    if (O > 0)
+        hipLaunchKernelGGL(bf16_feature_major_kernel, gy, dim3(kBlock), 0, st, static_cast<const bf16_t *>(dY), B, O,
+                           p.Bp, dyt);
+    if (int s = check_hip("bf16_feature_major_kernel")) return s;
+    const int64_t nkeys = colvals ? I : O, ngather = colvals ? O : I;
+    const int32_t *offs = colvals ? W->col_offsets : W->row_offsets;
+    const int32_t *gidx = colvals ? W->col_rows : W->cols;
+    const int32_t *tab = colvals ? W->col_blocks : W->row_blocks;
+    if (!tab) {
+        int32_t *t = reinterpret_cast<int32_t *>(ws + p.off_tab);
+        if (int s = launch_bounds(nkeys, static_cast<int>(p.ncb), static_cast<int>(p.cw), offs, gidx, t, st)) return s;
+        tab = t;
+    }
+    const dim3 grid(static_cast<unsigned>(ceil_div(nkeys, kHwDwKeys)), static_cast<unsigned>(3 * p.ncb));
+    probe(true, st);
+    hipLaunchKernelGGL(hw_sddmm_kernel, grid, dim3(kHwThreads), 0, st, static_cast<int>(nkeys),
+                       static_cast<int>(ngather), static_cast<int>(p.ncb), static_cast<int>(p.cw),
+                       static_cast<int>(p.Bp), tab, gidx, static_cast<int>(nnz), colvals ? xt : dyt,
+                       colvals ? dyt : xt, dW);
+    probe(false, st);
+    return check_hip("hw_sddmm_kernel");
+}
 }  // namespace
 
 // ================================================================ C ABI
@@ -3716,7 +3919,8 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
     const bool cv = W->row_to_col != nullptr;
     if (act_dtype == SNACK_BF16_HW) {
         const size_t dx = hw_spmm_bytes(I, O, nnz, batch, W->col_blocks);
-        const size_t dw = plan_sddmm(nnz, O, I, batch, SNACK_BF16, cv).total;
+        const HwDwPlan hp = plan_hw_dw(nnz, O, I, batch, SNACK_BF16, cv, cv ? W->col_blocks : W->row_blocks);
+        const size_t dw = hp.use ? hp.total : plan_sddmm(nnz, O, I, batch, SNACK_BF16, cv).total;
         switch (op) {
             case SNACK_OP_FWD: return hw_spmm_bytes(O, I, nnz, batch, W->row_blocks);
             case SNACK_OP_BWD_INPUT: return dx;
@@ -3728,7 +3932,10 @@ extern "C" size_t snack_coo_workspace_bytes(int op, const snack_coo_desc *W, int
     switch (op) {
         case SNACK_OP_FWD: return plan_spmm(nnz, I, O, batch, act_dtype, false, false, cv).total;
         case SNACK_OP_BWD_INPUT: return plan_spmm(nnz, O, I, batch, act_dtype, true, vec16(W), cv).total;
-        case SNACK_OP_GRAD_WEIGHT: return plan_sddmm(nnz, O, I, batch, act_dtype, cv).total;
+        case SNACK_OP_GRAD_WEIGHT: {
+            const HwDwPlan hp = plan_hw_dw(nnz, O, I, batch, act_dtype, cv, cv ? W->col_blocks : W->row_blocks);
+            return hp.use ? hp.total : plan_sddmm(nnz, O, I, batch, act_dtype, cv).total;
+        }
         case SNACK_OP_BWD: return plan_bwd(nnz, O, I, batch, act_dtype, vec16(W), cv).total;
         default: fail(SNACK_ERR_DTYPE, "workspace_bytes: unknown op %d", op); return 0;
     }
@@ -4042,6 +4249,12 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
         if (int s = check_act(X, act_dtype, "X", who)) return s;
         if (int s = check_act(dY, act_dtype, "dY", who)) return s;
         const bool colvals = W->row_to_col != nullptr;
+        const HwDwPlan hp = plan_hw_dw(nnz, O, I, batch, act_dtype, colvals, colvals ? W->col_blocks : W->row_blocks);
+        if (hp.use) {
+            if (int s = check_workspace(workspace, workspace_bytes, hp.total, who)) return s;
+            if (int s = launch_hw_dw(hp, W, X, dY, batch, dW_out, static_cast<char *>(workspace), st)) return s;
+            return snack::ok();
+        }
         const SddmmPlan p = plan_sddmm(nnz, O, I, batch, act_dtype, colvals);
         if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
         char *ws = static_cast<char *>(workspace);

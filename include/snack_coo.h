@@ -353,7 +353,7 @@ const char *snack_last_error(void);
  * snack_coo_block_offsets), 7 the kernel-selection options (snack_coo_set_option,
  * snack_coo_get_option) in place of environment variables, 8 snack_coo_fwd_noalloc, 9 segment
  * tables as per-block lists of {key, start, end} ordered by length within windows of 32 keys,
- * 10 the half-precision path (act_dtype SNACK_BF16_HW). */
+ * 10 the half-precision path (act_dtype SNACK_BF16_HW) and SNACK_OPT_BF16_DW_MFMA. */
 int snack_coo_abi_version(void);
 
 /* Kernel-selection overrides for tests and measurement (not part of the method).  Process-wide,
@@ -366,9 +366,19 @@ int snack_coo_abi_version(void);
  *   SNACK_OPT_BAND_MIN_NNZ         entry count from which the one-pass backward runs in row bands
  *                                  (default 2^20)
  *   SNACK_OPT_TOPOLOGY_DRAW_BATCH  draws per batch of snack_coo_topology_update_device (>= 1)
+ *   SNACK_OPT_BF16_DW_MFMA         the weight gradient with bf16 activations at batches of 256 and
+ *                                  more on the matrix cores (dense products over the batch sampled
+ *                                  at the stored entries): 1 wherever it applies, 0 never (default:
+ *                                  layers at least 1/12 dense)
  * snack_coo_set_option returns SNACK_ERR_DTYPE for an unknown option and SNACK_ERR_SHAPE for a
  * value out of range; snack_coo_get_option returns the current value (-1 for an unknown option). */
-enum { SNACK_OPT_TILE = 0, SNACK_OPT_BWD_FORM = 1, SNACK_OPT_BAND_MIN_NNZ = 2, SNACK_OPT_TOPOLOGY_DRAW_BATCH = 3 };
+enum {
+    SNACK_OPT_TILE = 0,
+    SNACK_OPT_BWD_FORM = 1,
+    SNACK_OPT_BAND_MIN_NNZ = 2,
+    SNACK_OPT_TOPOLOGY_DRAW_BATCH = 3,
+    SNACK_OPT_BF16_DW_MFMA = 4
+};
 int snack_coo_set_option(int option, int64_t value);
 int64_t snack_coo_get_option(int option);
 

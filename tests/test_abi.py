@@ -117,11 +117,12 @@ def test_options_validated_and_restored():
     """snack_coo_set_option rejects unknown options and out-of-range values (the old value stays),
     and -1 restores the library's own choice."""
     lib = snk._lib
-    for opt in (snk.OPT_TILE, snk.OPT_BWD_FORM, snk.OPT_BAND_MIN_NNZ, snk.OPT_TOPOLOGY_DRAW_BATCH):
+    for opt in (snk.OPT_TILE, snk.OPT_BWD_FORM, snk.OPT_BAND_MIN_NNZ, snk.OPT_TOPOLOGY_DRAW_BATCH,
+                snk.OPT_BF16_DW_MFMA):
         assert snk.get_option(opt) == -1
     assert lib.snack_coo_set_option(9, 0) == 6 and lib.snack_coo_set_option(-1, 0) == 6  # SNACK_ERR_DTYPE
     for opt, bad in ((snk.OPT_TILE, 1), (snk.OPT_BWD_FORM, 3), (snk.OPT_BAND_MIN_NNZ, -2),
-                     (snk.OPT_TOPOLOGY_DRAW_BATCH, 0)):
+                     (snk.OPT_TOPOLOGY_DRAW_BATCH, 0), (snk.OPT_BF16_DW_MFMA, 2)):
         assert lib.snack_coo_set_option(opt, bad) == 2 and snk.get_option(opt) == -1  # SNACK_ERR_SHAPE
     with snk.option(snk.OPT_BWD_FORM, 2):
         assert snk.get_option(snk.OPT_BWD_FORM) == 2
@@ -276,3 +277,29 @@ def test_half_precision_host_checks_and_workspace():
     assert lib.snack_coo_bwd_input(ctypes.byref(d), 0x1000, 64, HW, 0x2000, None, 0x10000, 1 << 30, None) == 2
     assert lib.snack_coo_bwd(ctypes.byref(d), 0x1000, 0x1000, 64, HW, 0x2000, None, 0x3000, 0x10000, 1 << 30,
                              None) == 2
+
+
+def test_bf16_weight_gradient_mfma_workspace_follows_rule():
+    """The bf16 weight gradient on the matrix cores is planned for batches of 256 and more on
+    layers at least 1/12 dense (or wherever SNACK_OPT_BF16_DW_MFMA = 1), its workspace then the two
+    feature-major bf16 copies (plus the segment lists when the descriptor has none)."""
+    lib = snk._lib
+    d = snk._Desc()
+    d.out_features, d.in_features = 5000, 5000
+    d.row_offsets = d.rows = d.cols = d.vals = 0x1000  # host-side sizing only
+    d.col_perm = d.col_rows = d.col_cols = d.col_offsets = 0x1000
+    d.row_blocks = d.col_blocks = 0x1000
+    copies = (5000 * 4096 * 2) * 2
+    for code in (snk.SNACK_BF16, snk.SNACK_BF16_HW):
+        d.nnz = 2_500_000  # 10 %: on the matrix cores
+        assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 4096, code) == copies
+        d.nnz = 1_250_000  # 5 %: the VALU kernels
+        assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 4096, code) != copies
+        with snk.option(snk.OPT_BF16_DW_MFMA, 1):
+            assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 4096, code) == copies
+            assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 255, code) != (5000 * 256 * 2) * 2
+        d.nnz = 2_500_000
+        with snk.option(snk.OPT_BF16_DW_MFMA, 0):
+            assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 4096, code) != copies
+    d.nnz = 2_500_000
+    assert lib.snack_coo_workspace_bytes(2, ctypes.byref(d), 4096, snk.SNACK_F32) != copies  # fp32: never

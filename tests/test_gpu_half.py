@@ -302,3 +302,34 @@ def test_half_graph_replays_match_eager(layers, B):
         torch.cuda.synchronize()
         for i, (got, want) in enumerate(zip(outs, ref)):
             assert torch.equal(got, want), (rep, i)
+
+
+@pytest.mark.parametrize("half_weights", [False, True], ids=["bf16", "bf16hw"])
+@pytest.mark.parametrize("order", ["row", "col"])
+@pytest.mark.parametrize("name,B", [("u3000x5000", 300), ("u3000x5000", 512), ("d2000x4000", 257),
+                                    ("u4000x600", 384), ("e1104x2048", 1000)])
+def test_bf16_weight_gradient_on_matrix_cores(layers, name, B, order, half_weights):
+    """The weight gradient with bf16 activations at batches of 256 and more on the matrix cores
+    (feature-major bf16 copies, dense 64 x 256 products over the batch sampled at the stored
+    entries; forced by SNACK_OPT_BF16_DW_MFMA, which by default takes layers at least 1/12 dense),
+    with fp32 or half weights alike: the products of bf16 values are exact in fp32, so it
+    is held to the fp32 tolerance against the oracle on the same bf16 inputs, through
+    snack_coo_grad_weight and snack_coo_bwd, in the values' order."""
+    L = layers[name]
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    say(f"bf16 dW on the matrix cores {name} B={B} values in {order} order half_weights={half_weights}")
+    built, W = device_layer(L, DEV)
+    if order == "col":
+        W = W.to_column_order()
+    x_in, x64 = acts(9970 + B, B, I, True)
+    dy_in, dy64 = acts(9971 + B, B, O, True)
+    X, dY = to_device(x_in, DEV, True), to_device(dy_in, DEV, True)
+    with snk.option(snk.OPT_BF16_DW_MFMA, 1):  # every layer here, dense enough or not
+        dW = snk.snack_coo_grad_weight(W, X, dY, half_weights=half_weights)
+        dX2, dW2 = snk.snack_coo_bwd(W, X, dY, half_weights=half_weights)
+        torch.cuda.synchronize()
+    ref = oracle.grad_weight(O, I, built["rows"], built["cols"], x64, dy64, nthreads=NTHREADS)
+    if order == "col":
+        ref = ref[built["col_perm"].astype(np.int64)]
+    check_close(dW.cpu().numpy(), ref, B, f"bf16 dW {name} B={B} ({order})")
+    check_close(dW2.cpu().numpy(), ref, B, f"bf16 bwd dW {name} B={B} ({order})")
