@@ -130,9 +130,14 @@ def half_weights_step(dev, K):
 
 
 def kernel_source_sha():
+    """sha256[:16] over the library's device sources (csrc/*.hip and csrc/*.h, by name)."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "coo_spmm_row_amd", "csrc", "snack_coo.hip"), "rb") as f:
-        h.update(f.read())
+    csrc = os.path.join(ROOT, "coo_spmm_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode() + b"\0")
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -1,40 +1,36 @@
-// snack_coo.hip -- device side of libsnack_coo for MI355X (gfx950, CDNA4, wave64).
+// snack_coo.hip -- libsnack_coo for MI355X (gfx950, CDNA4, wave64): the host-side planners and
+// launchers and the C ABI; the kernels are in the headers included below, one per family.
 //
-// The SNACK layer (arXiv:2610.04093) keeps its weight W (O x I) as a COO triple
-// sorted by (row, col) and runs three sparse products on it:
+// The SNACK layer keeps its weight W (O x I) as a COO triple sorted by (row, col) and runs three
+// sparse products on it:
 //   forward      Y[b,o]  = bias[o] + sum_{k: rows[k]=o} vals[k] X[b,cols[k]]   (Algorithm 1)
 //   input grad   dX[b,i] = sum_{k: cols[k]=i} vals[k] dY[b,rows[k]]            (Section 3.4)
 //   weight grad  dW[k]   = sum_b dY[b,rows[k]] X[b,cols[k]]                     (Section 3.4)
-// The paper's CUDA mapping (Section 3.2: one thread per non-zero and batch
-// column, atomics into C) is not used.  Here:
-//  * activations are first laid out feature-major (A^T[f][b], fp32) so that the
-//    operand row of one stored entry, A[:, f], is one contiguous vector;
-//  * forward and input gradient are the same gather-reduce over a sorted
-//    triple: the forward over the row order, the input gradient over the
-//    column view (W^T with swapped indices, as Section 3.4 states), reading
-//    vals through the column permutation.  Every output element is produced by
-//    exactly one lane or by a fixed-order fix-up, so results are deterministic
-//    and no atomics are used;
-//  * two mappings of the gather-reduce:
-//      segscan  - a wave owns a chunk of consecutive stored entries; lanes are
-//                 (entry group g, batch lane t); row segments inside a step are
-//                 combined by a segmented scan across entry groups; segments cut
-//                 by a chunk edge go to a small partials buffer and are finished
-//                 by fixup_kernel.  Balanced by nnz, so power-law rows are fine.
-//      rowwave  - for batches that are multiples of 4: a wave owns one
-//                 output row at a time; its entries are read 64 per coalesced
-//                 load and prefetched a chunk ahead; lane slots gather float4s
-//                 of the feature-major operand with several loads in flight.
-//  * the weight gradient is a sampled dense-dense product over the stored
-//    entries: a group of BT lanes per entry, each lane a slice of the batch,
-//    reduced across the group by xor shuffles.
-//  * LDS-tiled forms of all three (large layers, batches padded to a multiple
-//    of 16 up to 256): W is cut into tiles of a key range x a block of ~625
-//    operand rows; a 1024-thread workgroup stages its block of the operand in
-//    LDS once and serves every entry of the tile from there (tile_spmm_kernel,
-//    tile_sddmm_kernel, tile_bwd_kernel); the forward and input gradient write
-//    per-block partial sums that tile_sum_kernel adds in block order.
-// No MFMA: the work is an irregular gather, not a dense contraction.
+// The paper's CUDA mapping (Section 3.2: one thread per non-zero and batch column, atomics into
+// C) is not used.  The forward and the input gradient are the same gather-reduce over a sorted
+// view: the forward over the row order, the input gradient over the column view (W^T with the
+// indices swapped, as Section 3.4 states).  Every output element is produced by one lane or by a
+// fixed-order sum of partials, so results are deterministic and no float atomics are used.
+//
+//   dev_common.h      launch constants, bf16 element I/O, DPP sums and reduce-scatters, the
+//                     XCD-aware workgroup order
+//   layout_kernels.h  batch-major to feature-major copies for the untiled gathers, clears, db
+//   rowmap_kernels.h  untiled gather-reduce: segmented scan over chunks of entries with its
+//                     fix-up (balanced by nnz: power-law rows are fine), one wave per key
+//   tile_kernels.h    LDS-tiled walks for large layers: a 1024-thread workgroup stages a block
+//                     of about 625 operand rows of one batch tile (up to 160 KB) read in place
+//                     from the batch-major activations and walks its keys' segments there;
+//                     forward and input gradient write per-block partials that tile_sum_kernel
+//                     adds in block order; the weight gradient and the one-pass backward (both
+//                     gradients from one staged dY block)
+//   half_kernels.h    the opt-in half-precision path: bf16 weights and activations on the bf16
+//                     matrix cores over tiles of W made dense in LDS, and the bf16 weight
+//                     gradient as dense products sampled at the stored entries
+//   sddmm_kernels.h   untiled weight gradients and the fused column backward
+//   batch1_kernels.h  batch-1 and small-batch kernels: CSR streams over the rows or the column
+//                     view, private LDS copies of dX
+// The planners below choose one of them per call from the layer's shape, the batch and the
+// activation type; the choice never depends on the values.
 
 #include <hip/hip_runtime.h>
 
@@ -49,2856 +45,15 @@
 #include "../../include/snack_coo.h"
 #include "internal.h"
 
+#include "dev_common.h"
+#include "layout_kernels.h"
+#include "rowmap_kernels.h"
+#include "tile_kernels.h"
+#include "half_kernels.h"
+#include "sddmm_kernels.h"
+#include "batch1_kernels.h"
+
 namespace {
-
-constexpr int kWave = 64;
-constexpr int kBlock = 256;               // 4 waves per workgroup
-constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kXcds = 8;                  // MI355X: 8 accelerator dies, round-robin dispatch
-constexpr int64_t kMaxBatch = int64_t(1) << 21;  // keeps every grid.y within 65535
-
-typedef uint16_t bf16_t;
-
-// ---------------------------------------------------------------- element I/O
-__device__ __forceinline__ float load_act(const float *p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float load_act(const bf16_t *p, int64_t i) {
-    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
-}
-
-__device__ __forceinline__ void store_act(float *p, int64_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void store_act(bf16_t *p, int64_t i, float v) {
-    // round to nearest, ties to even; NaN stays a quiet NaN
-    uint32_t u = __float_as_uint(v);
-    uint16_t h;
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
-        h = static_cast<uint16_t>((u >> 16) | 0x0040u);
-    } else {
-        h = static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-    }
-    p[i] = h;
-}
-
-// Cross-lane moves within a row of 16 lanes (DPP).  Controls: quad_perm
-// [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16); every lane of the
-// group receives the group's sum.  The pairings (xor 1, xor 2, mirror within 8,
-// mirror within 16) form a butterfly, so each step adds two disjoint partial sums.
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-    if constexpr (N >= 2) v += dpp_move<0xB1>(v);
-    if constexpr (N >= 4) v += dpp_move<0x4E>(v);
-    if constexpr (N >= 8) v += dpp_move<0x141>(v);
-    if constexpr (N >= 16) v += dpp_move<0x140>(v);
-    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
-    return v;
-}
-
-// Reduce-scatter of U values over aligned groups of N lanes (U <= N, both powers of two):
-// lane t of a group returns the group's sum of v[t / (N / U)].  The stages pair lanes by
-// mirror within 16 (xor 15), mirror within 8 (xor 7), xor 2 and xor 1 -- the last log2(N) of
-// these, an independent set of lane masks, so every stage adds disjoint partial sums.  While
-// more than one value is left, a lane keeps the half its own bit selects (bit 3, 2, 1, 0 of
-// the lane in those stages), and sends the other half to its partner, which differs in that
-// bit; once one value is left the remaining stages are plain reductions.  That is log2(U)
-// halvings (3 instructions per kept value) plus one add per further stage, against U full
-// group sums of log2(N) adds each.
-// One stage of group_reduce_scatter: M values live in w[0, M); partner = the DPP source lane.
-template <int CTRL, int BIT, int M, int U>
-__device__ __forceinline__ void reduce_scatter_stage(float (&w)[U], int t) {
-    if constexpr (M > 1) {
-        constexpr int H = M / 2;
-        const bool hi = (t >> BIT) & 1;
-#pragma unroll
-        for (int j = 0; j < H; ++j) {
-            const float send = hi ? w[j] : w[j + H];
-            const float keep = hi ? w[j + H] : w[j];
-            w[j] = keep + dpp_move<CTRL>(send);
-        }
-    } else {
-        w[0] += dpp_move<CTRL>(w[0]);
-    }
-}
-
-template <int N, int U>
-__device__ __forceinline__ float group_reduce_scatter(const float (&v)[U], int t) {
-    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
-    static_assert(U >= 1 && U <= N && (U & (U - 1)) == 0, "U a power of two <= N");
-    float w[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) w[j] = v[j];
-    constexpr int M0 = U;
-    if constexpr (N >= 16) reduce_scatter_stage<0x140, 3, M0, U>(w, t);
-    constexpr int M1 = N >= 16 && M0 > 1 ? M0 / 2 : M0;
-    if constexpr (N >= 8) reduce_scatter_stage<0x141, 2, M1, U>(w, t);
-    constexpr int M2 = N >= 8 && M1 > 1 ? M1 / 2 : M1;
-    if constexpr (N >= 4) reduce_scatter_stage<0x4E, 1, M2, U>(w, t);
-    constexpr int M3 = N >= 4 && M2 > 1 ? M2 / 2 : M2;
-    if constexpr (N >= 2) reduce_scatter_stage<0xB1, 0, M3, U>(w, t);
-    return w[0];
-}
-
-// Logical workgroup index such that each XCD (blockIdx.x % 8 under round-robin
-// dispatch) works on one contiguous eighth of the logical range.  gridDim.x is
-// a multiple of 8; callers drop logical ids beyond their real count.
-__device__ __forceinline__ int64_t xcd_block() {
-    const int64_t per = gridDim.x / kXcds;
-    return (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-}
-
-// ---------------------------------------------------------------- layout
-// in [B][F] (batch-major, fp32 or bf16)  ->  out [F+1][Bp] fp32 (feature-major, Bp >= B; columns
-// B..Bp-1 zero), row F zero (gathers of a missing entry point there instead of being masked).
-// Up to two tensors per launch (blockIdx.z; the backward pass transposes X and dY together).
-// A workgroup moves a tile of 32 features x 64 batch rows through LDS.
-constexpr int kTf = 32, kTb = 64;
-
-// Any F and B: each thread issues its eight scalar loads (128-byte row segments per 32 lanes)
-// before its stores; the tile's output is one contiguous run per feature.
-template <typename InT>
-__global__ __launch_bounds__(kBlock) void to_feature_major_kernel(const InT *__restrict__ in0,
-                                                                  float *__restrict__ out0, int64_t F0,
-                                                                  const InT *__restrict__ in1,
-                                                                  float *__restrict__ out1, int64_t F1,
-                                                                  int64_t B, int64_t Bp) {
-    __shared__ float tile[kTb][kTf + 1];
-    const InT *__restrict__ in = blockIdx.z == 0 ? in0 : in1;
-    float *__restrict__ out = blockIdx.z == 0 ? out0 : out1;
-    const int64_t F = blockIdx.z == 0 ? F0 : F1;
-    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kTf;
-    if (f0 >= F && !(blockIdx.x == 0)) return;  // uniform per workgroup, before the barrier
-    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTb;
-    const int tx = threadIdx.x % kTf, ty = threadIdx.x / kTf;  // 32 x 8
-    const int nb = static_cast<int>(max<int64_t>(0, min<int64_t>(kTb, B - b0)));
-    const int nbp = static_cast<int>(min<int64_t>(kTb, Bp - b0));  // with the zero columns
-    const int nf = static_cast<int>(max<int64_t>(0, min<int64_t>(kTf, F - f0)));
-    if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < nbp) out[F * Bp + b0 + threadIdx.x] = 0.f;
-    constexpr int K = kTb / (kBlock / kTf);  // 8 rows per thread
-    float v[K];
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-        const int bb = ty + (kBlock / kTf) * i;
-        v[i] = (bb < nb && tx < nf) ? load_act(in, (b0 + bb) * F + f0 + tx) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < K; ++i) tile[ty + (kBlock / kTf) * i][tx] = v[i];
-    __syncthreads();
-    for (int li = threadIdx.x; li < nf * nbp; li += kBlock) {  // rows nb..nbp-1 of the tile are zero
-        const int ff = li / nbp, bb = li % nbp;
-        out[(f0 + ff) * Bp + b0 + bb] = tile[bb][ff];
-    }
-}
-
-__device__ __forceinline__ float4 load_act4(const float *p, int64_t i) {
-    return *reinterpret_cast<const float4 *>(p + i);
-}
-__device__ __forceinline__ float4 load_act4(const bf16_t *p, int64_t i) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p + i);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
-                       __uint_as_float(u.y & 0xFFFF0000u));
-}
-
-// F and Bp multiples of 4 (16-byte aligned rows): each thread loads two 4-feature vectors of
-// two batch rows (zeros past B) and stores two 4-row vectors of two features, with no divisions.  LDS rows
-// are padded to 33 floats: the 4 scalar writes and reads of a vector fall in distinct banks.
-template <typename InT>
-__global__ __launch_bounds__(kBlock) void to_feature_major4_kernel(const InT *__restrict__ in0,
-                                                                   float *__restrict__ out0, int64_t F0,
-                                                                   const InT *__restrict__ in1,
-                                                                   float *__restrict__ out1, int64_t F1,
-                                                                   int64_t B, int64_t Bp) {
-    __shared__ float tile[kTb][kTf + 1];
-    const InT *__restrict__ in = blockIdx.z == 0 ? in0 : in1;
-    float *__restrict__ out = blockIdx.z == 0 ? out0 : out1;
-    const int64_t F = blockIdx.z == 0 ? F0 : F1;
-    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kTf;
-    if (f0 >= F && !(blockIdx.x == 0)) return;  // uniform per workgroup, before the barrier
-    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kTb;
-    const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && b0 + tid < Bp && tid < kTb) out[F * Bp + b0 + tid] = 0.f;
-    // load: thread -> batch row r = tid / 8 (+32), features 4 * (tid % 8) .. +3
-    const int lc = 4 * (tid % (kTf / 4)), lr = tid / (kTf / 4);
-    float4 v[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t b = b0 + lr + 32 * i, f = f0 + lc;
-        v[i] = (b < B && f < F) ? load_act4(in, b * F + f) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        float *t = &tile[lr + 32 * i][lc];
-        t[0] = v[i].x;
-        t[1] = v[i].y;
-        t[2] = v[i].z;
-        t[3] = v[i].w;
-    }
-    __syncthreads();
-    // store: thread -> feature ff = tid / 16 (+16), batch rows 4 * (tid % 16) .. +3
-    const int sq = 4 * (tid % (kTb / 4)), sf = tid / (kTb / 4);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int ff = sf + 16 * i;
-        const int64_t f = f0 + ff, b = b0 + sq;
-        if (f < F && b < Bp)
-            *reinterpret_cast<float4 *>(out + f * Bp + b) =
-                make_float4(tile[sq][ff], tile[sq + 1][ff], tile[sq + 2][ff], tile[sq + 3][ff]);
-    }
-}
-
-// ---------------------------------------------------------------- segscan mapping
-// keys[k]  : output index of entry k (row for the forward, column for dX), sorted
-// gidx[k]  : operand row gathered by entry k (column for the forward, row for dX)
-// vals[perm ? perm[k] : k] : the entry's value
-// opnd     : feature-major operand [*][B]
-// out[b * out_ld + key] = bias[key] + sum over the key's entries
-// head/tail[chunk][B]   : partial sums of segments cut by a chunk edge
-template <int BT, typename OutT>
-__global__ __launch_bounds__(kBlock) void segscan_kernel(
-    int64_t nnz, int64_t chunk, int64_t nchunks, const int32_t *__restrict__ keys,
-    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm,
-    const float *__restrict__ opnd, int64_t B, const float *__restrict__ bias, OutT *__restrict__ out,
-    int64_t out_ld, float *__restrict__ head, float *__restrict__ tail) {
-    constexpr int G = kWave / BT;
-    constexpr int U = 4;  // steps whose loads are issued together
-    const int lane = threadIdx.x & (kWave - 1);
-    const int g = lane / BT, t = lane % BT;
-    const int64_t j = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
-    if (j >= nchunks) return;  // uniform per wave
-    const int64_t b = static_cast<int64_t>(blockIdx.y) * BT + t;
-    const bool bok = b < B;
-    const int64_t kbeg = j * chunk;
-    const int64_t kend = min(kbeg + chunk, nnz);
-    const int prev_key = kbeg > 0 ? keys[kbeg - 1] : -1;
-    const int next_key = kend < nnz ? keys[kend] : -1;
-    const int first_key = keys[kbeg];
-    float carry = 0.f;
-    int carry_key = -4;
-    for (int64_t base = kbeg; base < kend; base += U * G) {
-        int key[U], nkey[U];
-        float p[U];
-        int64_t c[U];
-        float v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = base + u * G + g;
-            key[u] = -2;
-            nkey[u] = -3;
-            c[u] = 0;
-            v[u] = 0.f;
-            if (k < kend) {
-                key[u] = keys[k];
-                nkey[u] = (k + 1 < kend) ? keys[k + 1] : -3;
-                v[u] = vals[perm ? static_cast<int64_t>(perm[k]) : k];
-                c[u] = gidx[k];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) p[u] = (key[u] != -2 && bok) ? v[u] * opnd[c[u] * B + b] : 0.f;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = base + u * G + g;
-            // segmented inclusive scan across the G entry groups (keys are sorted,
-            // so equal keys at distance d mean the whole span shares the key)
-#pragma unroll
-            for (int d = 1; d < G; d <<= 1) {
-                const float up = __shfl_up(p[u], d * BT, kWave);
-                const int upkey = __shfl_up(key[u], d * BT, kWave);
-                if (g >= d && upkey == key[u]) p[u] += up;
-            }
-            if (key[u] == carry_key) p[u] += carry;
-            carry = __shfl(p[u], (G - 1) * BT + t, kWave);
-            carry_key = __shfl(key[u], (G - 1) * BT + t, kWave);
-            if (key[u] != -2 && bok && nkey[u] != key[u]) {
-                const bool cut_left = key[u] == prev_key;
-                const bool cut_right = (k == kend - 1) && key[u] == next_key;
-                if (cut_left || cut_right) {
-                    if (key[u] == first_key)
-                        head[j * B + b] = p[u];
-                    else
-                        tail[j * B + b] = p[u];
-                } else {
-                    store_act(out, b * out_ld + key[u], p[u] + (bias ? bias[key[u]] : 0.f));
-                }
-            }
-        }
-    }
-}
-
-// Finishes keys with no entries (output = bias) and keys whose entries span
-// several chunks (sum of the chunk partials in chunk order, then the bias).
-template <typename OutT>
-__global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B, int64_t chunk,
-                                                       const int32_t *__restrict__ offs,
-                                                       const float *__restrict__ bias,
-                                                       const float *__restrict__ head,
-                                                       const float *__restrict__ tail,
-                                                       OutT *__restrict__ out, int64_t out_ld) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (r >= nkeys) return;
-    const float bv = bias ? bias[r] : 0.f;
-    const int64_t s = offs[r], e = offs[r + 1];
-    for (int64_t b = blockIdx.y; b < B; b += gridDim.y) {
-        if (s == e) {
-            store_act(out, b * out_ld + r, bv);
-            continue;
-        }
-        const int64_t cs = s / chunk, ce = (e - 1) / chunk;
-        if (cs == ce) continue;  // written by segscan_kernel
-        float v = (s == cs * chunk) ? head[cs * B + b] : tail[cs * B + b];
-        for (int64_t c = cs + 1; c <= ce; ++c) v += head[c * B + b];
-        store_act(out, b * out_ld + r, v + bv);
-    }
-}
-
-// ---------------------------------------------------------------- rowwave mapping
-// For batches that are multiples of 4.  A workgroup of 4 waves owns 4/WPR
-// output keys (rows), each split over WPR waves.  Lanes are (slot e, lane t):
-// S = 64/BT slots each take one stored entry per step, lane t holds batch
-// columns b0+4t .. b0+4t+3 and, with Q > 1, the float4s t+BT, .., t+(Q-1)BT
-// further on (the batch tile is 4*BT*Q columns; Q > 1 only when tiles are
-// exact).  A wave reads its key's entries 64 at a time (chunks c, c+WPR, ...)
-// with one coalesced load per lane -- keeping each entry's operand row as a
-// 32-bit float4 offset -- prefetches its next chunk while the current one is
-// consumed, and keeps U*Q float4 gathers in flight.  Lanes of a chunk past the
-// key's end point at the operand's zero row with value 0, so no step needs a
-// mask.  Slot partial sums are combined by xor shuffles, the WPR waves of a
-// key through LDS.  The operand including its zero row is below 4 GB.  B is the operand's batch
-// columns (a multiple of 4; zero columns pad a batch of nbo columns), nbo the columns stored.
-template <int BT, int WPR, int Q, typename OutT>
-__global__ __launch_bounds__(kBlock) void rowwave_kernel(
-    int64_t nkeys, const int32_t *__restrict__ offs, const int32_t *__restrict__ gidx,
-    const float *__restrict__ vals, const int32_t *__restrict__ perm, const float *__restrict__ opnd, int zero_row,
-    int64_t B, const float *__restrict__ bias, OutT *__restrict__ out, int64_t out_ld, int64_t nbo) {
-    constexpr int S = kWave / BT;
-    constexpr int UQ = 8 / Q;
-    constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;  // S*U divides 64
-    constexpr int KPB = kWavesPerBlock / WPR;             // keys per workgroup
-    __shared__ float4 part[kWavesPerBlock][Q][BT];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    const int e = lane / BT, t = lane % BT;
-    const int64_t r = xcd_block() * KPB + wave / WPR;
-    const int wsub = wave % WPR;
-    const bool rok = r < nkeys;  // uniform per wave
-    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * (4 * BT * Q) + 4 * t;
-    const bool bok = b0 < B;     // B % 4 == 0: all four columns exist (Q > 1: every lane)
-    const int B4 = static_cast<int>(B / 4);
-    // uniform base of this batch tile; a lane adds its float4 column and the entry's row
-    const char *__restrict__ tile = reinterpret_cast<const char *>(opnd) + blockIdx.y * (16 * BT * Q);
-    const uint32_t lane_off = 16u * static_cast<uint32_t>(bok ? t : 0);
-    float4 acc[Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (rok) {
-        const int zoff = zero_row * B4;
-        const int s = offs[r], end = offs[r + 1];
-        int mo = zoff;
-        float mv = 0.f;
-        const int first = s + wsub * kWave;
-        if (first + lane < end) {
-            mo = gidx[first + lane] * B4;
-            mv = vals[perm ? perm[first + lane] : first + lane];
-        }
-        for (int base = first; base < end; base += WPR * kWave) {
-            const int co = mo;
-            const float cv = mv;
-            const int n = min(kWave, end - base);
-            const int nb = base + WPR * kWave;
-            if (nb < end) {  // prefetch this wave's next chunk
-                mo = zoff;
-                mv = 0.f;
-                if (nb + lane < end) {
-                    mo = gidx[nb + lane] * B4;
-                    mv = vals[perm ? perm[nb + lane] : nb + lane];
-                }
-            }
-            for (int h = 0; h < n; h += S * U) {
-                const int sa = (h + e) << 2;  // ds_bpermute address of slot e's entry; +4S per step
-                float4 x[U][Q];
-                float v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int o = __builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co);
-                    v[u] = __int_as_float(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, __float_as_int(cv)));
-                    const uint32_t a = 16u * static_cast<uint32_t>(o) + lane_off;
-#pragma unroll
-                    for (int q = 0; q < Q; ++q)
-                        x[u][q] = *reinterpret_cast<const float4 *>(tile + (a + 16u * static_cast<uint32_t>(q * BT)));
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-#pragma unroll
-                    for (int q = 0; q < Q; ++q) {
-                        acc[q].x = fmaf(v[u], x[u][q].x, acc[q].x);
-                        acc[q].y = fmaf(v[u], x[u][q].y, acc[q].y);
-                        acc[q].z = fmaf(v[u], x[u][q].z, acc[q].z);
-                        acc[q].w = fmaf(v[u], x[u][q].w, acc[q].w);
-                    }
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-#pragma unroll
-        for (int d = BT; d < kWave; d <<= 1) {
-            acc[q].x += __shfl_xor(acc[q].x, d, kWave);
-            acc[q].y += __shfl_xor(acc[q].y, d, kWave);
-            acc[q].z += __shfl_xor(acc[q].z, d, kWave);
-            acc[q].w += __shfl_xor(acc[q].w, d, kWave);
-        }
-    }
-    if constexpr (WPR > 1) {
-        if (e == 0) {
-#pragma unroll
-            for (int q = 0; q < Q; ++q) part[wave][q][t] = acc[q];
-        }
-        __syncthreads();
-        if (wsub == 0 && e == 0) {
-#pragma unroll
-            for (int w = 1; w < WPR; ++w) {
-#pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    const float4 o = part[wave + w][q][t];
-                    acc[q].x += o.x;
-                    acc[q].y += o.y;
-                    acc[q].z += o.z;
-                    acc[q].w += o.w;
-                }
-            }
-        }
-    }
-    if (rok && wsub == 0 && e == 0 && bok) {
-        const float bv = bias ? bias[r] : 0.f;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int64_t c = b0 + 4 * q * BT;
-            if (c + 3 < nbo) {
-                store_act(out, (c + 0) * out_ld + r, acc[q].x + bv);
-                store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
-                store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
-                store_act(out, (c + 3) * out_ld + r, acc[q].w + bv);
-            } else {  // the last, padded float4 of the batch
-                if (c + 0 < nbo) store_act(out, (c + 0) * out_ld + r, acc[q].x + bv);
-                if (c + 1 < nbo) store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
-                if (c + 2 < nbo) store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------- LDS-tiled gather-reduce
-// The same gather-reduce as rowwave (out[key][:] = sum over the key's entries of
-// vals * opnd[gidx][:]), with the operand rows served from LDS instead of L2.  W is cut into
-// tiles of (a range of keys) x (a block of cw operand rows); a 1024-thread workgroup stages its
-// block of the feature-major operand (cw rows of 64 batch columns, 256 B each, plus one zero
-// row: up to 160 KB, gfx950's LDS) once, then walks its keys' segments inside the block.  The
-// segments come from a per-block segment list (tile_segments_kernel; the triple is sorted by key,
-// then by gather index, so each segment is a contiguous run of the key's entries), whose keys are
-// ordered by segment length within windows of kSegWindow keys: the four keys a wave walks together
-// have segments of about the same length, so little of the walk is padding.  Each tile writes fp32
-// partial sums part[bt][cb][key][64]; tile_sum_kernel adds the blocks in block order, adds the
-// bias and transposes to the batch-major output.
-//
-// Lanes: 4 slots of 16 lanes; slot s walks key 4*g + s of the wave's group g, and each lane holds
-// VW batch columns (VW floats) of a TB = 16*VW column batch tile (64 for batches padded to a
-// multiple of 64, else 32 or 16).  A group's entries are loaded 16 per chunk register (each row
-// of 16 lanes holds entries j = 0..15 of its slot's chunk), two groups ahead of the compute.
-// Step t of a chunk hands entry t to every lane of its row with DPP row_newbcast:t: folded into
-// the row address (an XOR), and moved once into a register for the value, so one step costs one
-// LDS read of VW floats per lane, an address XOR, a value move and VW plain FMAs.  Entries past a
-// segment's end point at the zero row with value 0.
-constexpr int kTileThreads = 1024;
-constexpr int kTileWaves = kTileThreads / kWave;
-constexpr int kTileLdsRows = 639;                     // staged rows: 159.75 KB of LDS at 64 columns
-constexpr int kTileMaxCols = kTileLdsRows - 1;        // operand rows per block (one more is the zero row)
-constexpr int kTileClaimBytes = 16;                   // after the staged rows: the workgroup's group counter
-
-// Raw buffer resource over n 4-byte elements: loads through it take a 32-bit byte offset (the
-// chunk offsets fold into the instruction's immediate), and loads past the end return 0 instead of
-// touching memory.  Word 3 is the gfx9 raw-buffer format.  Callers keep n < 2^29, so byte offsets
-// of elements stay below 2^31 and below kBufPast.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int n) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0), n * 4, 0x00020000);
-}
-__device__ __forceinline__ int buf_ld(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
-}
-constexpr int kBufPast = static_cast<int>(0xFFFFFFF0u);  // a byte offset past any buffer: the load returns 0
-
-// lane T of each row of 16 lanes, broadcast to the row (DPP row_newbcast)
-template <int T>
-__device__ __forceinline__ uint32_t bcast16(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x150 + T, 0xF, 0xF, true));
-}
-
-template <int SL>
-struct TileVec;
-template <>
-struct TileVec<1> { typedef float T; };
-template <>
-struct TileVec<2> { typedef float2 T; };
-template <>
-struct TileVec<4> { typedef float4 T; };
-
-__device__ __forceinline__ float vget(const float &v, int) { return v; }
-__device__ __forceinline__ float vget(const float2 &v, int i) { return i == 0 ? v.x : v.y; }
-__device__ __forceinline__ float vget(const float4 &v, int i) {
-    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// Staged rows of the tiled walks that read the activations in place (tile_spmm_kernel,
-// tile_sddmm_kernel): row r holds TB = 16 VW fp32 batch columns as NQ = TB / 4 chunks of 16 bytes,
-// chunk q (columns 4q .. 4q+3) at chunk position q ^ (r & kSwz).  Staging writes one chunk per
-// thread for consecutive rows; unswizzled, those writes would all hit the same four banks.  On
-// gfx950 a 128-bit LDS read by four slots of 16 lanes, each slot reading one row, runs at the full
-// rate only while the slots' chunk positions differ in their two low bits at most (measured: XOR of
-// the low two bits 232 B/clk/CU; XOR of all four bits by row 169; the writes reach 62 of at most
-// 72 B/clk/CU with the low two bits), hence kSwz = 3.  Lane byte offsets below 16 NQ and row
-// offsets that are multiples of 16 NQ combine as row_off(r) ^ lane_off, row_off(r) = r * 16 NQ +
-// 16 (r & kSwz): the XOR replaces the address add of an unswizzled row.
-constexpr int kSwz = 3;
-
-template <int VW>
-__device__ __forceinline__ uint32_t tile_row_off(int r) {
-    constexpr int NQ = 4 * VW;
-    return static_cast<uint32_t>(r) * (16u * NQ) + 16u * static_cast<uint32_t>(r & kSwz);
-}
-
-// Buffer resource over an activation of n elements (fp32 or bf16) and a load of one element,
-// widened to fp32: past the end, or at kBufPast, the load returns 0.  Callers keep n * the element
-// size below 2^31.
-template <typename InT>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(const InT *p, int n) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<InT *>(p), static_cast<short>(0),
-                                             n * static_cast<int>(sizeof(InT)), 0x00020000);
-}
-template <typename InT>
-__device__ __forceinline__ float act_ld(__amdgpu_buffer_rsrc_t r, int byte_off);
-template <>
-__device__ __forceinline__ float act_ld<float>(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
-}
-template <>
-__device__ __forceinline__ float act_ld<bf16_t>(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0)) << 16);
-}
-
-// Stages rows [r0, r0 + cn) (feature index) of batch tile bt of a batch-major activation [B][ld]
-// (fp32 or bf16, widened to fp32; ra = act_rsrc over its B * ld elements) into LDS rows 0 .. cn-1
-// in the swizzled layout above; rows cn .. cw (row cw is the zero row) and batch rows >= B are
-// zero (loaded past the buffer).  Item i is chunk q = i / 640 of row c = i % 640 (640 =
-// kTileLdsRows + 1 >= cw + 1, a constant divisor): consecutive threads take consecutive rows of
-// one chunk, so each of a chunk's four batch rows is read in runs of 64 features.
-template <int VW, typename InT>
-__device__ __forceinline__ void tile_stage_rows(float4 *xs4, __amdgpu_buffer_rsrc_t ra, int ld, int bt, int r0,
-                                                int cn, int cw) {
-    constexpr int NQ = 4 * VW, TB = 16 * VW, kStride = kTileLdsRows + 1;
-    constexpr int kEs = static_cast<int>(sizeof(InT));
-    constexpr int kIters = (kStride * NQ + kTileThreads - 1) / kTileThreads;
-    constexpr int kRound = kIters < 5 ? kIters : 5;  // items whose loads are in flight together
-#pragma unroll
-    for (int it0 = 0; it0 < kIters; it0 += kRound) {
-        float4 v[kRound];
-        int at[kRound];
-#pragma unroll
-        for (int u = 0; u < kRound && it0 + u < kIters; ++u) {
-            const int i = (it0 + u) * kTileThreads + static_cast<int>(threadIdx.x);
-            const int q = i / kStride, c = i - q * kStride;
-            at[u] = q < NQ && c <= cw ? c * NQ + (q ^ (c & kSwz)) : -1;
-            const int off = q < NQ && c < cn ? ((TB * bt + 4 * q) * ld + r0 + c) * kEs : kBufPast;
-            const int step = off == kBufPast ? 0 : ld * kEs;
-            v[u] = make_float4(act_ld<InT>(ra, off), act_ld<InT>(ra, off + step), act_ld<InT>(ra, off + 2 * step),
-                               act_ld<InT>(ra, off + 3 * step));
-        }
-#pragma unroll
-        for (int u = 0; u < kRound && it0 + u < kIters; ++u)
-            if (at[u] >= 0) xs4[at[u]] = v[u];
-    }
-}
-
-// The LDS reads of steps T0..T0+3 of one chunk (entry T0+u's staged row, this lane's VW columns;
-// off is the entry's tile_row_off).
-template <int VW, int T0>
-__device__ __forceinline__ void tile_reads4(typename TileVec<VW>::T (&x)[4], uint32_t off, uint32_t lane_off,
-                                            const char *lds) {
-    typedef typename TileVec<VW>::T V;
-    x[0] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 0>(off) ^ lane_off));
-    x[1] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 1>(off) ^ lane_off));
-    x[2] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 2>(off) ^ lane_off));
-    x[3] = *reinterpret_cast<const V *>(lds + (bcast16<T0 + 3>(off) ^ lane_off));
-}
-
-// Lane T of each row of 16 lanes' v, broadcast to the row, in a register of its own (inline asm,
-// so the compiler does not fold the DPP move into the FMAs that use it: a DPP FMA issues at about
-// 0.77 per clock per CU, a plain one at the full rate).  NOP1: the two wait states a VALU write of
-// v needs before a DPP read, on the first step of a chunk; volatile keeps the moves of a chunk in
-// step order, so that one runs first (the compiler adds no wait states for inline asm).
-template <int T, bool NOP1>
-__device__ __forceinline__ float bcast16_reg(float v) {
-    float r;
-    if constexpr (NOP1)
-        asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-                     : "=v"(r) : "v"(v), "n"(T));
-    else
-        asm volatile("v_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-                     : "=v"(r) : "v"(v), "n"(T));
-    return r;
-}
-
-// The FMAs of steps T0..T0+3: acc += (value of entry T0+u) * row.
-template <int VW, int T0>
-__device__ __forceinline__ void tile_fmas4(float (&acc)[VW], float v, const typename TileVec<VW>::T (&x)[4]) {
-    const float v0 = bcast16_reg<T0 + 0, T0 == 0>(v), v1 = bcast16_reg<T0 + 1, false>(v);
-    const float v2 = bcast16_reg<T0 + 2, false>(v), v3 = bcast16_reg<T0 + 3, false>(v);
-#pragma unroll
-    for (int i = 0; i < VW; ++i) {
-        acc[i] = fmaf(v0, vget(x[0], i), acc[i]);
-        acc[i] = fmaf(v1, vget(x[1], i), acc[i]);
-        acc[i] = fmaf(v2, vget(x[2], i), acc[i]);
-        acc[i] = fmaf(v3, vget(x[3], i), acc[i]);
-    }
-}
-
-// One chunk of 16 entries, nst (uniform, 1..16) of them real for the longest slot.  The reads of
-// each group of four steps are issued before the FMAs of the group before it, so a wave has a
-// group's LDS reads in flight while it computes.
-template <int VW>
-__device__ __forceinline__ void tile_chunk(float (&acc)[VW], uint32_t off, float v, int nst, uint32_t lane_off,
-                                           const char *lds) {
-    typedef typename TileVec<VW>::T V;
-    V a[4], b[4];
-    tile_reads4<VW, 0>(a, off, lane_off, lds);
-    if (nst > 4) tile_reads4<VW, 4>(b, off, lane_off, lds);
-    tile_fmas4<VW, 0>(acc, v, a);
-    if (nst > 4) {
-        if (nst > 8) tile_reads4<VW, 8>(a, off, lane_off, lds);
-        tile_fmas4<VW, 4>(acc, v, b);
-        if (nst > 8) {
-            if (nst > 12) tile_reads4<VW, 12>(b, off, lane_off, lds);
-            tile_fmas4<VW, 8>(acc, v, a);
-            if (nst > 12) tile_fmas4<VW, 12>(acc, v, b);
-        }
-    }
-}
-
-// Segment lists: seg[j][p] (int32 x 4) = {key, start, end, 0} for block j (gather indices
-// [j cw, j cw + cw)) and list position p: the key's entries in the block are [start, end).  Within
-// each window of kSegWindow positions [w kSegWindow, w kSegWindow + kSegWindow) the keys are those
-// of the same window, by decreasing end - start, equal lengths by increasing key.  One wave per
-// (block, window): lane l finds key w kSegWindow + l's segment by binary search and its rank by
-// comparing with every other lane's length.
-constexpr int kSegWindow = 32;  // 32 consecutive keys: one 128-byte line of a batch-major row
-
-__device__ __forceinline__ int first_at_or_past(const int32_t *__restrict__ gidx, int lo, int hi, int c) {
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (gidx[mid] < c) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
-}
-
-__global__ __launch_bounds__(kBlock) void tile_segments_kernel(int nkeys, int ncb, int cw,
-                                                               const int32_t *__restrict__ offs,
-                                                               const int32_t *__restrict__ gidx,
-                                                               int4 *__restrict__ seg) {
-    const int nwin = (nkeys + kSegWindow - 1) / kSegWindow;
-    const int64_t wv = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) / kWave;  // uniform per wave
-    if (wv >= static_cast<int64_t>(ncb) * nwin) return;
-    const int j = static_cast<int>(wv / nwin), w = static_cast<int>(wv % nwin);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int key = w * kSegWindow + lane;
-    const bool real = lane < kSegWindow && key < nkeys;
-    int a = 0, e = 0, len = -1;  // lanes without a key rank after every real one
-    if (real) {
-        const int lo = offs[key], hi = offs[key + 1];
-        a = j == 0 ? lo : first_at_or_past(gidx, lo, hi, j * cw);
-        e = j == ncb - 1 ? hi : first_at_or_past(gidx, a, hi, (j + 1) * cw);
-        len = e - a;
-    }
-    int rank = 0;
-    for (int m = 0; m < kSegWindow; ++m) {
-        const int lm = __builtin_amdgcn_readlane(len, m);
-        rank += (lm > len) || (lm == len && m < lane);
-    }
-    if (real) seg[static_cast<int64_t>(j) * nkeys + w * kSegWindow + rank] = make_int4(key, a, e, 0);
-}
-
-// Segment of list position pos of block cb (seg: the int4 records above as int32s, rs its buffer
-// resource; nothing past the tile: pos_ok false gives key 0 and an empty segment).
-__device__ __forceinline__ void seg_load(__amdgpu_buffer_rsrc_t rs, int cb, int nkeys, int pos, bool pos_ok,
-                                         int &key, int &a, int &len) {
-    typedef int v4i __attribute__((ext_vector_type(4)));
-    const v4i r = __builtin_amdgcn_raw_buffer_load_b128(rs, pos_ok ? (cb * nkeys + pos) * 16 : kBufPast, 0, 0);
-    key = r.x;
-    a = r.y;
-    len = r.z - r.y;
-}
-
-// act: the batch-major activation [B][opnd_rows] (fp32 or bf16, B * opnd_rows * its size < 2^31),
-// read in place; batch tile
-// bt = blockIdx.y covers columns [TB bt, TB bt + TB), TB = 16 VW: each lane of a slot holds VW of
-// them, and one staged operand row is TB floats (swizzled, tile_stage_rows).  Logical workgroup
-// L = cb * nrb + rb (XCD-contiguous).
-// VP: the values are read through perm (vals[perm[k]]): the permutation is loaded with the gather
-// indices two groups ahead, the values it points at one group ahead.
-template <int VW, int CH, bool VP, typename InT>
-__global__ __launch_bounds__(kTileThreads) void tile_spmm_kernel(
-    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ segs,
-    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm, int nnz,
-    const InT *__restrict__ act, int opnd_rows, int64_t B, float *__restrict__ part) {
-    constexpr int SL = 4;                      // slots (keys) per wave, 16 lanes each
-    constexpr int TB = 16 * VW;                // batch columns of a tile
-    constexpr uint32_t kRowBytes = 4u * TB;    // one staged operand row
-    // static: its address is known when compiling, so a row chunk's address is one DPP XOR
-    __shared__ float4 xs4[kTileLdsRows * 4 * VW + kTileClaimBytes / 16];
-    const int64_t L = xcd_block();
-    if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
-    const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
-    const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
-    const int bt = blockIdx.y;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int j = lane & 15;                    // entry of a chunk held by this lane
-    const int slot = lane >> 4;                 // the row of 16 lanes is the slot
-    const int ls = lane & 15;                   // lane within the slot: batch columns [ls*VW, ls*VW + VW)
-    const uint32_t lane_off = static_cast<uint32_t>(ls * VW * 4);
-    const uint32_t zoff = tile_row_off<VW>(cw);
-    const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
-    // group G = keys k_lo + SL*G .. +SL-1, slot s taking key k_lo + SL*G + s
-    const int ngroups = (k_hi - k_lo + SL - 1) / SL;
-    unsigned *claims = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(xs4) + (cw + 1) * kRowBytes);
-    // the block's operand rows; rows cn..cw are zero (row cw is the zero row)
-    tile_stage_rows<VW, InT>(xs4, act_rsrc(act, static_cast<int>(B) * opnd_rows), opnd_rows, bt, c0, cn, cw);
-    if (threadIdx.x == 0) *claims = 0u;
-    __syncthreads();
-    const char *lds = reinterpret_cast<const char *>(xs4);
-    float *pout = part + (static_cast<int64_t>(bt) * ncb + cb) * static_cast<int64_t>(nkeys) * TB;
-    // The waves take groups from the workgroup's counter as they go, so they all work until the
-    // tile is done.  A group's segments come from the table when it is claimed (D - 1 groups ahead
-    // of its compute), its chunks of gather indices and values one group later (VP: the permuted
-    // positions, then the values they point at one group before the compute).  Chunk loads go
-    // through buffer resources: lanes past a segment load from past the buffers' end, so nothing
-    // is read for them.
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
-    auto claim = [&]() {
-        unsigned g = 0;
-        if (lane == 0) g = atomicAdd(claims, 1u);
-        return static_cast<int>(__builtin_amdgcn_readfirstlane(g));
-    };
-    auto seg = [&](int G, int &key, int &a, int &len) {  // this slot's segment of group G (none past the tile)
-        const int pos = k_lo + SL * G + slot;
-        seg_load(rs, cb, nkeys, pos, G < ngroups && pos < k_hi, key, a, len);
-    };
-    auto load_chunks = [&](int a, int len, int (&gi)[CH], int (&vv)[CH]) {
-        const int base = (a + j) * 4;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int off = 16 * c + j < len ? base + 64 * c : kBufPast;
-            gi[c] = buf_ld(rg, off);
-            vv[c] = buf_ld(VP ? rp : rv, off);
-        }
-    };
-    auto load_vals = [&](const int (&pm)[CH], int len, int (&vv)[CH]) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) vv[c] = buf_ld(rv, 16 * c + j < len ? pm[c] * 4 : kBufPast);
-    };
-    auto group_len = [&](int len) {
-        return max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
-                   max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
-    };
-    auto compute = [&](int G, int key, int a, int len, const int (&gi)[CH], const int (&vv)[CH]) {
-        const int pos = k_lo + SL * G + slot;
-        const int m = group_len(len);
-        float acc[VW];
-#pragma unroll
-        for (int i = 0; i < VW; ++i) acc[i] = 0.f;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            if (16 * c < m) {
-                const bool ok = 16 * c + j < len;
-                const uint32_t off = ok ? tile_row_off<VW>(gi[c] - c0) : zoff;
-                const float v = ok ? __int_as_float(vv[c]) : 0.f;
-                tile_chunk<VW>(acc, off, v, m - 16 * c, lane_off, lds);
-            }
-        }
-        for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
-            const bool ok = 16 * c + j < len;
-            const int pos = (a + 16 * c + j) * 4;
-            const int gv = buf_ld(rg, pos);
-            const float w = __int_as_float(buf_ld(rv, VP ? (ok ? buf_ld(rp, pos) * 4 : kBufPast) : pos));
-            tile_chunk<VW>(acc, ok ? tile_row_off<VW>(gv - c0) : zoff, ok ? w : 0.f, m - 16 * c, lane_off, lds);
-        }
-        // every chunk register is consumed here, also those a short group skipped: without this
-        // use, refilling them would wait for loads issued after them
-#pragma unroll
-        for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]));
-        if (pos < k_hi) {
-            typedef typename TileVec<VW>::T V;
-            V r;
-            if constexpr (VW == 1) r = acc[0];
-            else if constexpr (VW == 2) r = make_float2(acc[0], acc[1]);
-            else r = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * TB + ls * VW) = r;
-        }
-    };
-    // ring of claimed groups: [0] computed now, [1] next, ..., [D-1] claimed this phase.  Without
-    // a permutation the chunks are loaded one group ahead; with one, the chunks (gather indices and
-    // permuted positions) two groups ahead and the values they point at one ahead.  (Loading the
-    // values two ahead measured slower: those scattered reads are bound by the address unit, not
-    // by their latency.)
-    constexpr int D = VP ? 4 : 3;
-    int Gs[D], Ks[D], As[D], Ls[D];
-#pragma unroll
-    for (int i = 0; i < D - 1; ++i) {
-        Gs[i] = claim();
-        seg(Gs[i], Ks[i], As[i], Ls[i]);
-    }
-    auto advance = [&]() {
-#pragma unroll
-        for (int i = 0; i + 1 < D; ++i) {
-            Gs[i] = Gs[i + 1];
-            Ks[i] = Ks[i + 1];
-            As[i] = As[i + 1];
-            Ls[i] = Ls[i + 1];
-        }
-        return Gs[0] < ngroups;
-    };
-    if constexpr (VP) {
-        // buffer sets 0..2 rotate with the groups: set (t mod 3) holds group t's gather indices g,
-        // permuted positions p and values v
-        int g0[CH], g1[CH], g2[CH], p0[CH], p1[CH], p2[CH], v0[CH], v1[CH], v2[CH];
-        load_chunks(As[0], Ls[0], g0, p0);
-        load_chunks(As[1], Ls[1], g1, p1);
-        load_vals(p0, Ls[0], v0);
-        // one phase: claim group [3], load the chunks of [2] and the values of [1], compute [0]
-        auto phase = [&](int (&gc)[CH], int (&vc)[CH], int (&pv)[CH], int (&vv)[CH], int (&gl)[CH], int (&pl)[CH]) {
-            Gs[D - 1] = claim();
-            seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
-            load_chunks(As[2], Ls[2], gl, pl);
-            load_vals(pv, Ls[1], vv);
-            compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc);
-            return advance();
-        };
-        if (Gs[0] < ngroups) {
-            for (;;) {
-                if (!phase(g0, v0, p1, v1, g2, p2)) break;
-                if (!phase(g1, v1, p2, v2, g0, p0)) break;
-                if (!phase(g2, v2, p0, v0, g1, p1)) break;
-            }
-        }
-    } else {
-        int gA[CH], gB[CH], vA[CH], vB[CH];
-        load_chunks(As[0], Ls[0], gA, vA);
-        // one phase: claim group [2], load the chunks of [1], compute [0]
-        auto phase = [&](int (&gc)[CH], int (&vc)[CH], int (&gn)[CH], int (&vn)[CH]) {
-            Gs[D - 1] = claim();
-            seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
-            load_chunks(As[1], Ls[1], gn, vn);
-            compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc);
-            return advance();
-        };
-        if (Gs[0] < ngroups) {
-            for (;;) {
-                if (!phase(gA, vA, gB, vB)) break;
-                if (!phase(gB, vB, gA, vA)) break;
-            }
-        }
-    }
-}
-
-// Weight gradient on the same tiles: dW[k] = sum_b dY[b, row_k] X[b, col_k] for the entries of the
-// workgroup's (rows x column block) tile, with the block of X^T staged in LDS as above.  Slot s of
-// a group takes row 4g + s; each lane holds its 4 batch columns of that row's dY slice and, per
-// step, the dot product of its 4 columns with the entry's staged X row.  After a chunk of 16 steps
-// a reduce-scatter over the slot's 16 lanes leaves lane j with entry j's sum, stored in triple
-// order (16 consecutive entries per slot).  Each lane holds VW columns of a TB = 16 VW column batch
-// tile (float4 at 64 columns); batch tiles are taken in turn (the block staged again), and tiles
-// after the first add into dW; each entry belongs to one workgroup.
-// Dot products of steps T0..T0+3: p[T0+u] = this lane's VW columns of entry T0+u's staged row
-// times its VW columns of the slot's dY row.
-template <int VW, int T0>
-__device__ __forceinline__ void tile_dots4(float (&p)[16], const typename TileVec<VW>::T (&x)[4],
-                                           const typename TileVec<VW>::T &dy) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        float d = vget(x[u], 0) * vget(dy, 0);
-#pragma unroll
-        for (int i = 1; i < VW; ++i) d = fmaf(vget(x[u], i), vget(dy, i), d);
-        p[T0 + u] = d;
-    }
-}
-
-// The 16 (or nst) dot products of one chunk, four steps at a time (its 16 products and the slot's
-// dY slice leave no room for a second group of reads in flight).
-template <int VW>
-__device__ __forceinline__ void tile_dot_chunk(float (&p)[16], uint32_t off, int nst, uint32_t lane_off,
-                                               const char *lds, const typename TileVec<VW>::T &dy) {
-    typedef typename TileVec<VW>::T V;
-    V a[4];
-    tile_reads4<VW, 0>(a, off, lane_off, lds);
-    tile_dots4<VW, 0>(p, a, dy);
-    if (nst > 4) {
-        tile_reads4<VW, 4>(a, off, lane_off, lds);
-        tile_dots4<VW, 4>(p, a, dy);
-    }
-    if (nst > 8) {
-        tile_reads4<VW, 8>(a, off, lane_off, lds);
-        tile_dots4<VW, 8>(p, a, dy);
-    }
-    if (nst > 12) {
-        tile_reads4<VW, 12>(a, off, lane_off, lds);
-        tile_dots4<VW, 12>(p, a, dy);
-    }
-}
-
-// x: the batch-major X [B][opnd_rows], dy_act: the batch-major dY [B][nkeys] (fp32 or bf16), both
-// read in place: the X block is staged as in tile_spmm_kernel, and each lane loads its VW batch
-// columns of its slot's dY row (zero past the batch).  B * max(opnd_rows, nkeys) * the element
-// size < 2^31 (32-bit buffer offsets).
-template <int VW, int CH, typename InT>
-__global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
-    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, int nbt, const int32_t *__restrict__ segs,
-    const int32_t *__restrict__ gidx, int nnz, const InT *__restrict__ x, int opnd_rows,
-    const InT *__restrict__ dy_act, int64_t B, float *__restrict__ dw) {
-    constexpr int SL = 4;
-    constexpr int TB = 16 * VW;
-    constexpr uint32_t kRowBytes = 4u * TB;
-    typedef typename TileVec<VW>::T V;
-    // static: its address is known when compiling, so a row chunk's address is one DPP XOR
-    __shared__ float4 xs4[kTileLdsRows * 4 * VW + kTileClaimBytes / 16];
-    const int64_t L = xcd_block();
-    if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
-    const int cb = static_cast<int>(L / nrb), rb = static_cast<int>(L % nrb);
-    const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int j = lane & 15;
-    const int slot = lane >> 4;
-    const uint32_t lane_off = static_cast<uint32_t>(j * VW * 4);
-    const uint32_t zoff = tile_row_off<VW>(cw);
-    const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
-    // group G = rows k_lo + SL*G .. +SL-1, taken from the workgroup's counter as in tile_spmm_kernel
-    const int ngroups = (k_hi - k_lo + SL - 1) / SL;
-    unsigned *claims = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(xs4) + (cw + 1) * kRowBytes);
-    const char *lds = reinterpret_cast<const char *>(xs4);
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
-    const __amdgpu_buffer_rsrc_t rx = act_rsrc(x, static_cast<int>(B) * opnd_rows);
-    const __amdgpu_buffer_rsrc_t rdy = act_rsrc(dy_act, static_cast<int>(B) * nkeys);
-    auto claim = [&]() {
-        unsigned g = 0;
-        if (lane == 0) g = atomicAdd(claims, 1u);
-        return static_cast<int>(__builtin_amdgcn_readfirstlane(g));
-    };
-    auto seg = [&](int G, int &key, int &a, int &len) {  // this slot's segment of group G (none past the tile)
-        const int pos = k_lo + SL * G + slot;
-        seg_load(rs, cb, nkeys, pos, G < ngroups && pos < k_hi, key, a, len);
-    };
-    for (int bt = 0; bt < nbt; ++bt) {
-        if (bt > 0) __syncthreads();  // the previous batch tile's reads of the block (and claims) are done
-        tile_stage_rows<VW, InT>(xs4, rx, opnd_rows, bt, c0, cn, cw);
-        if (threadIdx.x == 0) *claims = 0u;
-        __syncthreads();
-        // a group's chunks of gather indices and its rows' dY slices, one group after its claim
-        auto load_group = [&](int key, int a, int len, int (&gi)[CH], V &dy) {
-            const int base = (a + j) * 4;
-#pragma unroll
-            for (int c = 0; c < CH; ++c) gi[c] = buf_ld(rg, 16 * c + j < len ? base + 64 * c : kBufPast);
-            float d[VW];  // batch rows >= B: past the buffer, 0
-            const int off = ((TB * bt + VW * j) * nkeys + key) * static_cast<int>(sizeof(InT));
-#pragma unroll
-            for (int i = 0; i < VW; ++i) d[i] = act_ld<InT>(rdy, off + i * nkeys * static_cast<int>(sizeof(InT)));
-            if constexpr (VW == 1) dy = d[0];
-            else if constexpr (VW == 2) dy = make_float2(d[0], d[1]);
-            else dy = make_float4(d[0], d[1], d[2], d[3]);
-        };
-        auto chunk = [&](int a, int len, int m, int c, uint32_t off, const V &dy) {
-            float p[16];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) p[t] = 0.f;
-            tile_dot_chunk<VW>(p, off, m - 16 * c, lane_off, lds, dy);
-            const float r = group_reduce_scatter<16, 16>(p, j);
-            if (16 * c + j < len) {
-                float *d = dw + a + 16 * c + j;
-                *d = bt == 0 ? r : *d + r;
-            }
-        };
-        auto compute = [&](int a, int len, const int (&gi)[CH], const V &dy) {
-            int m = max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
-                        max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
-#pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                if (16 * c < m) {
-                    const bool ok = 16 * c + j < len;
-                    chunk(a, len, m, c, ok ? tile_row_off<VW>(gi[c] - c0) : zoff, dy);
-                }
-            }
-            for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
-                const bool ok = 16 * c + j < len;
-                const int gv = buf_ld(rg, (a + 16 * c + j) * 4);
-                chunk(a, len, m, c, ok ? tile_row_off<VW>(gv - c0) : zoff, dy);
-            }
-#pragma unroll
-            for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]));
-#pragma unroll
-            for (int i = 0; i < VW; ++i) asm volatile("" ::"v"(vget(dy, i)));
-        };
-        // ring of claimed groups: [0] computed now, [1] its loads in flight, [2] claimed this phase
-        int Gs[3], Ks[3], As[3], Ls[3];
-        Gs[0] = claim();
-        seg(Gs[0], Ks[0], As[0], Ls[0]);
-        Gs[1] = claim();
-        seg(Gs[1], Ks[1], As[1], Ls[1]);
-        int gA[CH], gB[CH], gC[CH];
-        V dA, dB, dC;
-        load_group(Ks[0], As[0], Ls[0], gA, dA);
-        auto phase = [&](int (&gc)[CH], V &dc, int (&gn)[CH], V &dn) {
-            Gs[2] = claim();
-            seg(Gs[2], Ks[2], As[2], Ls[2]);
-            load_group(Ks[1], As[1], Ls[1], gn, dn);
-            compute(As[0], Ls[0], gc, dc);
-            Gs[0] = Gs[1], Ks[0] = Ks[1], As[0] = As[1], Ls[0] = Ls[1];
-            Gs[1] = Gs[2], Ks[1] = Ks[2], As[1] = As[2], Ls[1] = Ls[2];
-            return Gs[0] < ngroups;
-        };
-        if (Gs[0] < ngroups) {
-            for (;;) {
-                if (!phase(gA, dA, gB, dB)) break;
-                if (!phase(gB, dB, gC, dC)) break;
-                if (!phase(gC, dC, gA, dA)) break;
-            }
-        }
-    }
-}
-
-// Both gradients in one tiled pass over the column view (one batch tile of TB = 16 VW columns).
-// The workgroup stages a block of cw rows of dY (features of the output, read in place from the
-// batch-major dY and swizzled as in tile_spmm_kernel); slot s of a group walks the segment of one
-// column of W (the key) and holds that column's X slice: its VW batch columns of X, read in place.
-// Each step reads an entry's staged dY row once and uses it twice: dX partials += v * dY row (as
-// tile_spmm_kernel), and the dot product with the X slice, which a reduce-scatter over the slot's
-// 16 lanes turns into dW of 16 entries per chunk.  dW goes to the walk position, or (VP: values in
-// row order) to perm of it, the same permuted position the value was read from.  The block
-// partials of dX are summed by tile_sum_kernel.
-template <int VW, int T0>
-__device__ __forceinline__ void tile_bwd_steps4(float (&acc)[VW], float (&p)[16], uint32_t off, float v,
-                                                uint32_t lane_off, const char *lds,
-                                                const typename TileVec<VW>::T &xs) {
-    typedef typename TileVec<VW>::T V;
-    V y[4];
-    tile_reads4<VW, T0>(y, off, lane_off, lds);
-    const float v0 = bcast16_reg<T0 + 0, T0 == 0>(v), v1 = bcast16_reg<T0 + 1, false>(v);
-    const float v2 = bcast16_reg<T0 + 2, false>(v), v3 = bcast16_reg<T0 + 3, false>(v);
-#pragma unroll
-    for (int i = 0; i < VW; ++i) {
-        acc[i] = fmaf(v0, vget(y[0], i), acc[i]);
-        acc[i] = fmaf(v1, vget(y[1], i), acc[i]);
-        acc[i] = fmaf(v2, vget(y[2], i), acc[i]);
-        acc[i] = fmaf(v3, vget(y[3], i), acc[i]);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        float d = vget(y[u], 0) * vget(xs, 0);
-#pragma unroll
-        for (int i = 1; i < VW; ++i) d = fmaf(vget(y[u], i), vget(xs, i), d);
-        p[T0 + u] = d;
-    }
-}
-
-// dy: the batch-major dY [B][opnd_rows], x: the batch-major X [B][nkeys] (fp32 or bf16; B times
-// max(opnd_rows, nkeys) times the element size < 2^31), B <= TB.  Groups are claimed from the
-// workgroup's counter as in tile_spmm_kernel; a group's X slices are loaded with its chunks.
-template <int VW, int CH, bool VP, typename InT>
-__global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
-    int nkeys, int ncb, int nrb, int cw, int keys_per_rb, const int32_t *__restrict__ segs,
-    const int32_t *__restrict__ gidx, const float *__restrict__ vals, const int32_t *__restrict__ perm, int nnz,
-    const InT *__restrict__ dy, int opnd_rows, const InT *__restrict__ x, int64_t B, float *__restrict__ part,
-    float *__restrict__ dw) {
-    constexpr int SL = 4;
-    constexpr int TB = 16 * VW;
-    constexpr uint32_t kRowBytes = 4u * TB;
-    constexpr int kEs = static_cast<int>(sizeof(InT));
-    typedef typename TileVec<VW>::T V;
-    // static: its address is known when compiling, so a row chunk's address is one DPP XOR
-    __shared__ float4 xs4[kTileLdsRows * 4 * VW + kTileClaimBytes / 16];
-    const int64_t L = xcd_block();
-    if (L >= static_cast<int64_t>(ncb) * nrb) return;  // whole workgroup, before any barrier
-    // logical workgroup L = rb * ncb + cb: the column blocks of a key range sit together on one XCD,
-    // which reads that range's X slices into its L2 once (the forward's L = cb * nrb + rb stages
-    // each block on fewer XCDs instead).  Measured at 10k x 10k / 95 % / B = 64 with the caches
-    // flushed by a read stream: 69.0 against 70.7 us with the tile sums; warm, the same.
-    const int rb = static_cast<int>(L / ncb), cb = static_cast<int>(L % ncb);
-    const int c0 = cb * cw, cn = min(cw, opnd_rows - c0);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int j = lane & 15;
-    const int slot = lane >> 4;
-    const uint32_t lane_off = static_cast<uint32_t>(j * VW * 4);
-    const uint32_t zoff = tile_row_off<VW>(cw);
-    const int k_lo = rb * keys_per_rb, k_hi = min(nkeys, k_lo + keys_per_rb);
-    const int ngroups = (k_hi - k_lo + SL - 1) / SL;
-    unsigned *claims = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(xs4) + (cw + 1) * kRowBytes);
-    // the block's rows of dY; rows cn..cw are zero (row cw is the zero row)
-    tile_stage_rows<VW, InT>(xs4, act_rsrc(dy, static_cast<int>(B) * opnd_rows), opnd_rows, 0, c0, cn, cw);
-    if (threadIdx.x == 0) *claims = 0u;
-    __syncthreads();
-    const char *lds = reinterpret_cast<const char *>(xs4);
-    float *pout = part + static_cast<int64_t>(cb) * nkeys * TB;
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
-    const __amdgpu_buffer_rsrc_t rx = act_rsrc(x, static_cast<int>(B) * nkeys);
-    auto claim = [&]() {
-        unsigned g = 0;
-        if (lane == 0) g = atomicAdd(claims, 1u);
-        return static_cast<int>(__builtin_amdgcn_readfirstlane(g));
-    };
-    auto seg = [&](int G, int &key, int &a, int &len) {  // this slot's segment of group G (none past the tile)
-        const int pos = k_lo + SL * G + slot;
-        seg_load(rs, cb, nkeys, pos, G < ngroups && pos < k_hi, key, a, len);
-    };
-    // a group's chunks (gather indices, and values or permuted positions) and the X slice of each
-    // slot's key (batch rows VW j .. VW j + VW - 1; none for an empty segment, rows >= B read as 0)
-    auto load_chunks = [&](int key, int a, int len, int (&gi)[CH], int (&vv)[CH], V &xsl) {
-        const int base = (a + j) * 4;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {  // lanes past the segment read nothing
-            const int off = 16 * c + j < len ? base + 64 * c : kBufPast;
-            gi[c] = buf_ld(rg, off);
-            vv[c] = buf_ld(VP ? rp : rv, off);
-        }
-        const int xo = len > 0 ? (VW * j * nkeys + key) * kEs : kBufPast;
-        const int step = len > 0 ? nkeys * kEs : 0;
-        float d[VW];
-#pragma unroll
-        for (int i = 0; i < VW; ++i) d[i] = act_ld<InT>(rx, xo + i * step);
-        if constexpr (VW == 1) xsl = d[0];
-        else if constexpr (VW == 2) xsl = make_float2(d[0], d[1]);
-        else xsl = make_float4(d[0], d[1], d[2], d[3]);
-    };
-    auto load_vals = [&](const int (&pm)[CH], int len, int (&vv)[CH]) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) vv[c] = buf_ld(rv, 16 * c + j < len ? pm[c] * 4 : kBufPast);
-    };
-    auto group_len = [&](int len) {
-        return max(max(__builtin_amdgcn_readlane(len, 0), __builtin_amdgcn_readlane(len, 16)),
-                   max(__builtin_amdgcn_readlane(len, 32), __builtin_amdgcn_readlane(len, 48)));
-    };
-    auto chunk = [&](float (&acc)[VW], int len, int m, int c, uint32_t off, float v, int wpos, const V &xsl) {
-        float p[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) p[t] = 0.f;
-        const int nst = m - 16 * c;
-        tile_bwd_steps4<VW, 0>(acc, p, off, v, lane_off, lds, xsl);
-        if (nst > 4) tile_bwd_steps4<VW, 4>(acc, p, off, v, lane_off, lds, xsl);
-        if (nst > 8) tile_bwd_steps4<VW, 8>(acc, p, off, v, lane_off, lds, xsl);
-        if (nst > 12) tile_bwd_steps4<VW, 12>(acc, p, off, v, lane_off, lds, xsl);
-        const float r = group_reduce_scatter<16, 16>(p, j);
-        if (16 * c + j < len) dw[wpos] = r;
-    };
-    auto compute = [&](int G, int key, int a, int len, const int (&gi)[CH], const int (&vv)[CH],
-                       const int (&pm)[CH], const V &xsl) {
-        const int pos = k_lo + SL * G + slot;
-        const int m = group_len(len);
-        float acc[VW];
-#pragma unroll
-        for (int i = 0; i < VW; ++i) acc[i] = 0.f;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            if (16 * c < m) {
-                const bool ok = 16 * c + j < len;
-                const uint32_t off = ok ? tile_row_off<VW>(gi[c] - c0) : zoff;
-                const float v = ok ? __int_as_float(vv[c]) : 0.f;
-                chunk(acc, len, m, c, off, v, VP ? pm[c] : a + 16 * c + j, xsl);
-            }
-        }
-        for (int c = CH; 16 * c < m; ++c) {  // segments longer than the prefetched chunks
-            const bool ok = 16 * c + j < len;
-            const int at = (a + 16 * c + j) * 4;
-            const int gv = buf_ld(rg, at);
-            const int pv = VP ? buf_ld(rp, at) : a + 16 * c + j;
-            const float w = __int_as_float(buf_ld(rv, ok ? pv * 4 : kBufPast));
-            chunk(acc, len, m, c, ok ? tile_row_off<VW>(gv - c0) : zoff, ok ? w : 0.f, pv, xsl);
-        }
-        // every chunk register is consumed here, also those a short group skipped: without this
-        // use, refilling them would wait for loads issued after them
-#pragma unroll
-        for (int c = 0; c < CH; ++c) asm volatile("" ::"v"(gi[c]), "v"(vv[c]), "v"(pm[c]));
-#pragma unroll
-        for (int i = 0; i < VW; ++i) asm volatile("" ::"v"(vget(xsl, i)));
-        if (pos < k_hi) {
-            V r;
-            if constexpr (VW == 1) r = acc[0];
-            else if constexpr (VW == 2) r = make_float2(acc[0], acc[1]);
-            else r = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            *reinterpret_cast<V *>(pout + static_cast<int64_t>(key) * TB + j * VW) = r;
-        }
-    };
-    // ring of claimed groups as in tile_spmm_kernel: without a permutation the chunks and X slices
-    // are loaded one group ahead; with one, two groups ahead, and the values one ahead
-    constexpr int D = VP ? 4 : 3;
-    int Gs[D], Ks[D], As[D], Ls[D];
-#pragma unroll
-    for (int i = 0; i < D - 1; ++i) {
-        Gs[i] = claim();
-        seg(Gs[i], Ks[i], As[i], Ls[i]);
-    }
-    auto advance = [&]() {
-#pragma unroll
-        for (int i = 0; i + 1 < D; ++i) {
-            Gs[i] = Gs[i + 1];
-            Ks[i] = Ks[i + 1];
-            As[i] = As[i + 1];
-            Ls[i] = Ls[i + 1];
-        }
-        return Gs[0] < ngroups;
-    };
-    if constexpr (VP) {
-        // buffer sets 0..2 rotate with the groups: set (t mod 3) holds group t's gather indices g,
-        // permuted positions p, values v and X slices x
-        int g0[CH], g1[CH], g2[CH], p0[CH], p1[CH], p2[CH], v0[CH], v1[CH], v2[CH];
-        V x0, x1, x2;
-        load_chunks(Ks[0], As[0], Ls[0], g0, p0, x0);
-        load_chunks(Ks[1], As[1], Ls[1], g1, p1, x1);
-        load_vals(p0, Ls[0], v0);
-        // one phase: claim group [3], load the chunks of [2] and the values of [1], compute [0]
-        auto phase = [&](int (&gc)[CH], int (&pc)[CH], int (&vc)[CH], const V &xc, int (&pv)[CH], int (&vv)[CH],
-                         int (&gl)[CH], int (&pl)[CH], V &xl) {
-            Gs[D - 1] = claim();
-            seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
-            load_chunks(Ks[2], As[2], Ls[2], gl, pl, xl);
-            load_vals(pv, Ls[1], vv);
-            compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc, pc, xc);
-            return advance();
-        };
-        if (Gs[0] < ngroups) {
-            for (;;) {
-                if (!phase(g0, p0, v0, x0, p1, v1, g2, p2, x2)) break;
-                if (!phase(g1, p1, v1, x1, p2, v2, g0, p0, x0)) break;
-                if (!phase(g2, p2, v2, x2, p0, v0, g1, p1, x1)) break;
-            }
-        }
-    } else {
-        int gA[CH], gB[CH], vA[CH], vB[CH];
-        V xA, xB;
-        load_chunks(Ks[0], As[0], Ls[0], gA, vA, xA);
-        // one phase: claim group [2], load the chunks of [1], compute [0]
-        auto phase = [&](int (&gc)[CH], int (&vc)[CH], const V &xc, int (&gn)[CH], int (&vn)[CH], V &xn) {
-            Gs[D - 1] = claim();
-            seg(Gs[D - 1], Ks[D - 1], As[D - 1], Ls[D - 1]);
-            load_chunks(Ks[1], As[1], Ls[1], gn, vn, xn);
-            compute(Gs[0], Ks[0], As[0], Ls[0], gc, vc, gc, xc);
-            return advance();
-        };
-        if (Gs[0] < ngroups) {
-            for (;;) {
-                if (!phase(gA, vA, xA, gB, vB, xB)) break;
-                if (!phase(gB, vB, xB, gA, vA, xA)) break;
-            }
-        }
-    }
-}
-
-// out[b][key] = bias[key] + sum over blocks cb (in order) of part[bt][cb][key][b - TB bt], b < nbo.
-// A workgroup adds 1024/TB keys x TB batch columns of one batch tile (one float4 per thread and
-// block, up to 16 blocks' loads in flight) and writes them transposed.
-template <typename OutT, int TB>
-__global__ __launch_bounds__(kBlock) void tile_sum_kernel(const float *__restrict__ part, int nkeys, int ncb,
-                                                          int64_t nbo, const float *__restrict__ bias,
-                                                          OutT *__restrict__ out, int64_t out_ld) {
-    constexpr int KW = 4 * kBlock / TB;  // keys per workgroup
-    constexpr int R4 = TB / 4;           // float4s per key and block
-    __shared__ float tr[KW][TB + 1];
-    const int k0 = blockIdx.x * KW, bt = blockIdx.y;
-    const int t = threadIdx.x;
-    {
-        const int kk = t / R4, qq = t % R4;  // key k0 + kk, batch columns [4 qq, 4 qq + 4)
-        float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (k0 + kk < nkeys) {
-            const float4 *p = reinterpret_cast<const float4 *>(
-                part + ((static_cast<int64_t>(bt) * ncb) * nkeys + k0 + kk) * TB + 4 * qq);
-            const int64_t stride4 = static_cast<int64_t>(nkeys) * R4;
-            for (int cb0 = 0; cb0 < ncb; cb0 += 16) {
-                float4 u[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    u[i] = cb0 + i < ncb ? p[(cb0 + i) * stride4] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (cb0 + i < ncb) {
-                        s0.x += u[i].x;
-                        s0.y += u[i].y;
-                        s0.z += u[i].z;
-                        s0.w += u[i].w;
-                    }
-                }
-            }
-        }
-        float *row = &tr[kk][4 * qq];
-        row[0] = s0.x;
-        row[1] = s0.y;
-        row[2] = s0.z;
-        row[3] = s0.w;
-    }
-    __syncthreads();
-    const int b = t / (KW / 4), kq = (t % (KW / 4)) * 4;  // batch row TB bt + b, keys [k0 + kq, +4)
-    const int64_t bb = static_cast<int64_t>(bt) * TB + b;
-    if (bb < nbo) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = k0 + kq + i;
-            if (key < nkeys) store_act(out, bb * out_ld + key, tr[kq + i][b] + (bias ? bias[key] : 0.f));
-        }
-    }
-}
-
-// ---------------------------------------------------------------- half-precision weights on MFMA
-// The stored fp32 values are rounded to bf16 (nearest even) as they are read, and the products run
-// on gfx950's v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation) over tiles of W made
-// dense in LDS from the stored entries; W is never dense in HBM.  The pages name Tensor-Core
-// SNACK-COO for fp16/bf16 as future work (Conclusion, Limitations, and Future Work).
-//
-// Gather-reduce over a view (the forward over the row order, the input gradient over the column
-// view): out[b][key] = bias[key] + sum over the key's entries e of bf16(v_e) * act[b][gidx_e], as a
-// product of the dense tile W_view[keys][gather indices] (MFMA operand A, rows = keys) with the
-// activations (operand B, columns = batch).  A workgroup owns 64 keys x 64 batch columns (2 x 2
-// MFMA blocks of 32 x 32) and a run of the segment lists' blocks (a K group); it walks each block
-// in two halves of 336 gather indices (from the block's 8-aligned start): it writes the half's
-// entries of its keys into a zeroed LDS slab [64 keys][336] as bf16, its 4 waves take the half's
-// 16-index MFMA steps in contiguous runs (wave w steps 6w .. 6w + 5), and the written cells are
-// zeroed again.  Each wave reads its steps' activation operands (8 consecutive bf16 of one batch
-// row per lane) straight from the batch-major activations before the half's entries are written;
-// contiguous steps make each wave read whole 128-byte lines of a batch row (interleaved steps had
-// four waves fetch every line, each using a quarter, and the L1 fill rate bound the kernel).  The
-// 44 KB slab lets three workgroups share a CU.  At the end the waves' partial tiles are added in
-// wave order through LDS: with one K group the sum plus the bias is the output, else it goes to
-// part[bt][group][key][64] and tile_sum_kernel adds the groups in order.  The result does not
-// depend on timing.
-// A zero of the slab times a non-finite activation gives NaN: a NaN or infinite activation
-// reaches every key of its tile, as in a dense product with a masked weight.
-typedef __bf16 hw_bf8 __attribute__((ext_vector_type(8)));
-typedef float hw_f16 __attribute__((ext_vector_type(16)));
-
-constexpr int kHwThreads = 256;
-constexpr int kHwKeys = 64;                          // keys per workgroup: two MFMA row blocks of 32
-constexpr int kHwTb = 64;                            // batch columns per workgroup: two MFMA column blocks
-constexpr int kHwCols = 336;                         // slab columns: half of a block's <= 645 from an 8-aligned start
-constexpr int kHwSteps = kHwCols / 16;               // MFMA steps of 16 gather indices per half
-constexpr int kHwWaveSteps = (kHwSteps + 3) / 4;     // steps per wave and half
-constexpr int kHwRowBytes = 2 * kHwCols + 16;        // padded: consecutive slab rows start 4 banks apart
-constexpr int kHwCombineLd = kHwKeys + 1;            // floats per row of the combine buffer (bank spread)
-constexpr int kHwWgTarget = 768;                     // K groups make about this many workgroups (3 per CU)
-static_assert(2 * kHwCols >= 638 + 7, "two halves cover a block from its 8-aligned start");
-static_assert(kHwKeys * kHwRowBytes >= 4 * 32 * kHwCombineLd * 4, "combine buffer (one column block) fits the slab");
-
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN
-__device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
-    const uint32_t u = __float_as_uint(v);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-// segs: the view's segment lists ({key, start, end, 0} per block and list position, keys of a
-// 32-key window together); act: bf16 [B][ngather], B * ngather * 2 + 2048 < 2^31, ngather a
-// multiple of 8 and act 16-byte aligned (each operand load is 16 aligned bytes).  Blocks
-// [bpg * z, bpg * z + bpg) for blockIdx.z = z; part: NULL (one K group: out written here) or the
-// fp32 partials [gridDim.y][gridDim.z][nkeys][64].
-template <bool VP, typename OutT>
-__global__ __launch_bounds__(kHwThreads, 3) void hw_spmm_kernel(int nkeys, int ngather, int ncb, int cw, int bpg,
-                                                               const int32_t *__restrict__ segs,
-                                                               const int32_t *__restrict__ gidx,
-                                                               const float *__restrict__ vals,
-                                                               const int32_t *__restrict__ perm, int nnz,
-                                                               const bf16_t *__restrict__ act, int64_t B,
-                                                               const float *__restrict__ bias, OutT *__restrict__ out,
-                                                               float *__restrict__ part) {
-    __shared__ __attribute__((aligned(16))) unsigned char slab[kHwKeys * kHwRowBytes];
-    typedef int v4i __attribute__((ext_vector_type(4)));
-    const int k0 = blockIdx.x * kHwKeys;
-    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kHwTb;
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    for (int i = t; i < kHwKeys * kHwRowBytes / 16; i += kHwThreads)
-        reinterpret_cast<uint4 *>(slab)[i] = make_uint4(0u, 0u, 0u, 0u);
-    // entry writers: 4 threads per list position of the tile
-    const int pos = k0 + t / 4, sub = t % 4;
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
-    // activation operands: lane (n = lane % 32, half = lane / 32) reads batch row b0 + 32 nb + n,
-    // gather indices [base + 8 half, base + 8 half + 8) of each of its steps
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(act), static_cast<short>(0), static_cast<int>(B * ngather * 2), 0x00020000);
-    const int half = lane / 32, n = lane % 32;
-    int arow[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int64_t b = b0 + 32 * nb + n;
-        arow[nb] = b < B ? static_cast<int>(b * ngather * 2) : kBufPast;  // rows past the batch read 0
-    }
-    hw_f16 acc[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
-    __syncthreads();
-    const int cb_lo = static_cast<int>(blockIdx.z) * bpg, cb_hi = min(ncb, cb_lo + bpg);
-    for (int cb = cb_lo; cb < cb_hi; ++cb) {
-        const int g_lo = cb * cw, g0 = g_lo & ~7;
-        const int g_hi = min(g_lo + cw, ngather);
-        const v4i rec = __builtin_amdgcn_raw_buffer_load_b128(
-            rs, pos < nkeys ? (cb * nkeys + pos) * 16 : kBufPast, 0, 0);
-        const int e_end = pos < nkeys ? rec.z : 0;
-        int ecur = rec.y + sub;  // this thread's next entry of the block (every 4th of its key's run)
-#pragma unroll 1
-        for (int h = 0; h < 2; ++h) {
-            const int hs = g0 + kHwCols * h;  // the half's first gather index
-            if (hs >= g_hi) break;            // uniform: depends on the block only
-            const int he = min(hs + kHwCols, g_hi);
-            const int nsteps = (he - hs + 15) / 16;
-            const int row_off = (rec.x - k0) * kHwRowBytes - 2 * hs;
-            // this wave's activation operands for the half (issued first, used after the writes)
-            hw_bf8 bq[kHwWaveSteps][2];
-#pragma unroll
-            for (int q = 0; q < kHwWaveSteps; ++q) {
-                const int s = kHwWaveSteps * w + q;
-                const int col = (hs + 16 * s + 8 * half) * 2;
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int off = s < nsteps && arow[nb] != kBufPast ? arow[nb] + col : kBufPast;
-                    bq[q][nb] = __builtin_bit_cast(hw_bf8, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-                }
-            }
-            // the half's entries of this thread: a prefix of the rest of its run (sorted by index)
-            const int e_first = ecur;
-            for (;;) {
-                int g[4], v[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = ecur + 4 * u;
-                    const int off = e < e_end ? e * 4 : kBufPast;
-                    g[u] = e < e_end ? buf_ld(rg, off) : 0x7FFFFFFF;
-                    v[u] = buf_ld(rv, VP ? (e < e_end ? buf_ld(rp, off) * 4 : kBufPast) : off);
-                }
-                int n_in = 0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    if (g[u] < he) {
-                        *reinterpret_cast<uint16_t *>(slab + row_off + 2 * g[u]) = bf16_bits_rne(__int_as_float(v[u]));
-                        ++n_in;
-                    }
-                }
-                ecur += 4 * n_in;
-                if (n_in < 4) break;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int q = 0; q < kHwWaveSteps; ++q) {
-                const int s = kHwWaveSteps * w + q;
-                if (s < nsteps) {
-#pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) {
-                        const hw_bf8 a = *reinterpret_cast<const hw_bf8 *>(
-                            slab + (32 * mb + n) * kHwRowBytes + 2 * (16 * s + 8 * half));
-#pragma unroll
-                        for (int nb = 0; nb < 2; ++nb)
-                            acc[mb][nb] =
-                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[q][nb], acc[mb][nb], 0, 0, 0);
-                    }
-                }
-            }
-            __syncthreads();
-            // zero the cells written above (their gather indices read again)
-            for (int e0 = e_first; e0 < ecur; e0 += 16) {
-                int g[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) g[u] = buf_ld(rg, e0 + 4 * u < ecur ? (e0 + 4 * u) * 4 : kBufPast);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (e0 + 4 * u < ecur) *reinterpret_cast<uint16_t *>(slab + row_off + 2 * g[u]) = 0;
-            }
-            __syncthreads();
-        }
-    }
-    // the waves' partial tiles, added in wave order, one column block (32 batch columns) at a
-    // time: accumulator r of lane (n, half) in block (mb, nb) is key 32 mb + 8 (r / 4) + 4 half +
-    // r % 4, batch column 32 nb + n
-    float *cbuf = reinterpret_cast<float *>(slab);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                cbuf[(w * 32 + n) * kHwCombineLd + 32 * mb + 8 * (r / 4) + 4 * half + r % 4] = acc[mb][nb][r];
-        __syncthreads();
-        if (!part) {
-            const int key = t % kHwKeys;
-            const float bv = bias && k0 + key < nkeys ? bias[k0 + key] : 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int bc = t / kHwKeys + 4 * j;
-                float s = cbuf[bc * kHwCombineLd + key];
-#pragma unroll
-                for (int ww = 1; ww < 4; ++ww) s += cbuf[(ww * 32 + bc) * kHwCombineLd + key];
-                const int64_t b = b0 + 32 * nb + bc;
-                if (k0 + key < nkeys && b < B) store_act(out, b * nkeys + k0 + key, s + bv);
-            }
-        } else {
-            const int bc = t % 32;
-            float *pp = part + (static_cast<int64_t>(blockIdx.y) * gridDim.z + blockIdx.z) * nkeys * kHwTb;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int key = t / 32 + 8 * j;
-                float s = cbuf[bc * kHwCombineLd + key];
-#pragma unroll
-                for (int ww = 1; ww < 4; ++ww) s += cbuf[(ww * 32 + bc) * kHwCombineLd + key];
-                if (k0 + key < nkeys) pp[static_cast<int64_t>(k0 + key) * kHwTb + 32 * nb + bc] = s;
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// Wide batches: the same gather-reduce with the densified slab shared by kHwWaves batch tiles.
-// A workgroup owns 64 keys x 256 batch columns; the slab of a half block is written once by all
-// threads, and wave w multiplies it by batch tile w (columns b0 + 64 w ..) over all of the half's
-// steps, so the entry loads and slab writes are shared by four batch tiles and each wave keeps
-// its own 64 x 64 output tile (no combine across waves).  Operand B loads run six steps ahead.
-constexpr int kHwWideTb = 4 * kHwTb;                 // batch columns per workgroup
-constexpr int kHwAhead = 10;                         // activation operand steps in flight per wave
-constexpr int64_t kHwWideMinPerKey = 64;             // entries per key from which the wide kernel runs
-
-template <bool VP, typename OutT>
-__global__ __launch_bounds__(kHwThreads, 2) void hw_spmm_wide_kernel(int nkeys, int ngather, int ncb, int cw,
-                                                                    int bpg, const int32_t *__restrict__ segs,
-                                                                    const int32_t *__restrict__ gidx,
-                                                                    const float *__restrict__ vals,
-                                                                    const int32_t *__restrict__ perm, int nnz,
-                                                                    const bf16_t *__restrict__ act, int64_t B,
-                                                                    const float *__restrict__ bias,
-                                                                    OutT *__restrict__ out, float *__restrict__ part) {
-    __shared__ __attribute__((aligned(16))) unsigned char slab[kHwKeys * kHwRowBytes];
-    typedef int v4i __attribute__((ext_vector_type(4)));
-    const int k0 = blockIdx.x * kHwKeys;
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const int64_t b0 = static_cast<int64_t>(blockIdx.y) * kHwWideTb + kHwTb * w;  // this wave's batch tile
-    const bool active = b0 < B;                                                     // uniform per wave
-    for (int i = t; i < kHwKeys * kHwRowBytes / 16; i += kHwThreads)
-        reinterpret_cast<uint4 *>(slab)[i] = make_uint4(0u, 0u, 0u, 0u);
-    const int pos = k0 + t / 4, sub = t % 4;
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz), rv = buf_rsrc(vals, nnz), rp = buf_rsrc(perm, nnz);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(act), static_cast<short>(0), static_cast<int>(B * ngather * 2), 0x00020000);
-    const int half = lane / 32, n = lane % 32;
-    int arow[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int64_t b = b0 + 32 * nb + n;
-        arow[nb] = b < B ? static_cast<int>(b * ngather * 2) : kBufPast;
-    }
-    hw_f16 acc[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
-    __syncthreads();
-    const int cb_lo = static_cast<int>(blockIdx.z) * bpg, cb_hi = min(ncb, cb_lo + bpg);
-    for (int cb = cb_lo; cb < cb_hi; ++cb) {
-        const int g_lo = cb * cw, g0 = g_lo & ~7;
-        const int g_hi = min(g_lo + cw, ngather);
-        const v4i rec = __builtin_amdgcn_raw_buffer_load_b128(
-            rs, pos < nkeys ? (cb * nkeys + pos) * 16 : kBufPast, 0, 0);
-        const int e_end = pos < nkeys ? rec.z : 0;
-        int ecur = rec.y + sub;
-#pragma unroll 1
-        for (int h = 0; h < 2; ++h) {
-            const int hs = g0 + kHwCols * h;
-            if (hs >= g_hi) break;  // uniform: depends on the block only
-            const int he = min(hs + kHwCols, g_hi);
-            const int nsteps = (he - hs + 15) / 16;
-            const int row_off = (rec.x - k0) * kHwRowBytes - 2 * hs;
-            auto bload = [&](int s, int nb) {
-                const int off = active && s < nsteps && arow[nb] != kBufPast ? arow[nb] + (hs + 16 * s + 8 * half) * 2
-                                                                              : kBufPast;
-                return __builtin_bit_cast(hw_bf8, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-            };
-            hw_bf8 bq[kHwSteps][2];
-#pragma unroll
-            for (int s = 0; s < kHwAhead; ++s)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) bq[s][nb] = bload(s, nb);
-            const int e_first = ecur;
-            for (;;) {
-                int g[4], v[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = ecur + 4 * u;
-                    const int off = e < e_end ? e * 4 : kBufPast;
-                    g[u] = e < e_end ? buf_ld(rg, off) : 0x7FFFFFFF;
-                    v[u] = buf_ld(rv, VP ? (e < e_end ? buf_ld(rp, off) * 4 : kBufPast) : off);
-                }
-                int n_in = 0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    if (g[u] < he) {
-                        *reinterpret_cast<uint16_t *>(slab + row_off + 2 * g[u]) = bf16_bits_rne(__int_as_float(v[u]));
-                        ++n_in;
-                    }
-                }
-                ecur += 4 * n_in;
-                if (n_in < 4) break;
-            }
-            __syncthreads();
-            if (active) {
-#pragma unroll
-                for (int s = 0; s < kHwSteps; ++s) {
-                    if (s + kHwAhead < kHwSteps) {
-#pragma unroll
-                        for (int nb = 0; nb < 2; ++nb) bq[s + kHwAhead][nb] = bload(s + kHwAhead, nb);
-                    }
-                    if (s < nsteps) {
-#pragma unroll
-                        for (int mb = 0; mb < 2; ++mb) {
-                            const hw_bf8 a = *reinterpret_cast<const hw_bf8 *>(
-                                slab + (32 * mb + n) * kHwRowBytes + 2 * (16 * s + 8 * half));
-#pragma unroll
-                            for (int nb = 0; nb < 2; ++nb)
-                                acc[mb][nb] =
-                                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s][nb], acc[mb][nb], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-            for (int e0 = e_first; e0 < ecur; e0 += 16) {
-                int g[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) g[u] = buf_ld(rg, e0 + 4 * u < ecur ? (e0 + 4 * u) * 4 : kBufPast);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (e0 + 4 * u < ecur) *reinterpret_cast<uint16_t *>(slab + row_off + 2 * g[u]) = 0;
-            }
-            __syncthreads();
-        }
-    }
-    // each wave's 64 x 64 tile through its quarter of the slab as fp32 [64 batch columns][65]:
-    // accumulator r of lane (n, half) in block (mb, nb) is key 32 mb + 8 (r / 4) + 4 half + r % 4,
-    // batch column 32 nb + n
-    static_assert(kHwKeys * kHwRowBytes >= kHwThreads / kWave * kHwTb * kHwCombineLd * 4 / 2,
-                  "two waves' tiles fit the slab at a time");
-    float *cbuf = reinterpret_cast<float *>(slab) + (w % 2) * kHwTb * kHwCombineLd;
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {  // waves 0 and 1, then 2 and 3
-        if (w / 2 == pass && active) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        cbuf[(32 * nb + n) * kHwCombineLd + 32 * mb + 8 * (r / 4) + 4 * half + r % 4] = acc[mb][nb][r];
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            if (!part) {
-                const int key = k0 + lane;  // lane = key within the tile (64 keys)
-                const float bv = bias && key < nkeys ? bias[key] : 0.f;
-                for (int bc = 0; bc < kHwTb; ++bc) {
-                    const int64_t b = b0 + bc;
-                    if (key < nkeys && b < B) store_act(out, b * nkeys + key, cbuf[bc * kHwCombineLd + lane] + bv);
-                }
-            } else {
-                const int bt = static_cast<int>(b0 / kHwTb);
-                float *pp = part + (static_cast<int64_t>(bt) * gridDim.z + blockIdx.z) * nkeys * kHwTb;
-                for (int r = 0; r < kHwKeys; ++r)
-                    if (k0 + r < nkeys) pp[static_cast<int64_t>(k0 + r) * kHwTb + lane] = cbuf[lane * kHwCombineLd + r];
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// Weight gradient with bf16 activations on the matrix cores (batches of 256 and more).  Each
-// product of two bf16 values is exact in fp32, so this is the bf16 weight gradient (fp32
-// accumulation, in another order) whether or not the weights are half precision.  X and dY are
-// first copied feature-major as bf16 ([features][Bp], Bp the batch rounded up to 16, zero beyond
-// the batch), so that the batch, the product's reduction, is contiguous per lane.  Over the view
-// whose order the values are stored in (the row order: keys = rows, gather = columns; the column
-// view the reverse), a workgroup owns 64 keys (two MFMA row blocks of 32) x 256 gather indices
-// (a third of a segment-list block from its 8-aligned start; wave w takes column blocks 2w and
-// 2w + 1) and computes the dense 64 x 256 product over the batch with
-// v_mfma_f32_32x32x16_bf16, stages it in LDS as fp32, and writes dW for the stored entries of its
-// keys in those 256 indices (each entry belongs to one workgroup: no partial sums).
-constexpr int kHwDwKeys = 64;
-constexpr int kHwDwCols = 256;                      // a third of a block's <= 645 from an 8-aligned start
-constexpr int kHwDwLd = kHwDwCols + 1;              // floats per row of the staged product
-constexpr int kHwDwUnroll = 4;                      // MFMA steps whose operand loads are issued together
-static_assert(3 * kHwDwCols >= 638 + 7, "three thirds cover a block from its 8-aligned start");
-
-// in [B][F] bf16 -> out [F][Bp] bf16, zero for batch rows >= B; tiles of 64 features x 64 rows.
-__global__ __launch_bounds__(kBlock) void bf16_feature_major_kernel(const bf16_t *__restrict__ in, int64_t B,
-                                                                    int64_t F, int64_t Bp, bf16_t *__restrict__ out) {
-    __shared__ uint16_t tile[64][65];
-    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 64, b0 = static_cast<int64_t>(blockIdx.y) * 64;
-    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int64_t b = b0 + ty + 4 * i, f = f0 + tx;
-        tile[ty + 4 * i][tx] = (b < B && f < F) ? in[b * F + f] : static_cast<uint16_t>(0);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int64_t f = f0 + ty + 4 * i, b = b0 + tx;
-        if (f < F && b < Bp) out[f * Bp + b] = tile[tx][ty + 4 * i];
-    }
-}
-
-// segs: the view's segment lists; actK [nkeys][Bp], actG [ngather][Bp] (feature-major bf16,
-// (max(nkeys, ngather) + 320) * Bp * 2 < 2^31, Bp a multiple of 16); dW[e] for the view's entry e.
-__global__ __launch_bounds__(kHwThreads) void hw_sddmm_kernel(int nkeys, int ngather, int ncb, int cw, int Bp,
-                                                             const int32_t *__restrict__ segs,
-                                                             const int32_t *__restrict__ gidx, int nnz,
-                                                             const bf16_t *__restrict__ actK,
-                                                             const bf16_t *__restrict__ actG, float *__restrict__ dW) {
-    __shared__ float cbuf[kHwDwKeys * kHwDwLd];
-    typedef int v4i __attribute__((ext_vector_type(4)));
-    const int cb = static_cast<int>(blockIdx.y) / 3, third = static_cast<int>(blockIdx.y) % 3;
-    const int g_lo = cb * cw, g0 = g_lo & ~7, g_hi = min(g_lo + cw, ngather);
-    const int ts = g0 + kHwDwCols * third;
-    if (ts >= g_hi) return;  // whole workgroup, before any barrier
-    const int te = min(ts + kHwDwCols, g_hi);
-    const int k0 = blockIdx.x * kHwDwKeys;
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const int half = lane / 32, n = lane % 32;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(actK), static_cast<short>(0), static_cast<int>(static_cast<int64_t>(nkeys) * Bp * 2),
-        0x00020000);
-    const __amdgpu_buffer_rsrc_t rgt = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(actG), static_cast<short>(0), static_cast<int>(static_cast<int64_t>(ngather) * Bp * 2),
-        0x00020000);
-    // operand rows: keys k0 + 32 mb + n (A), gather indices ts + 64 w + 32 nb + n (B); rows past the
-    // copies' ends read 0, rows of the next third or block give products that are never read
-    int ka[2], gb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        ka[i] = (k0 + 32 * i + n) * Bp * 2;
-        gb[i] = (ts + 64 * w + 32 * i + n) * Bp * 2;
-    }
-    hw_f16 acc[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
-    const int nsteps = Bp / 16;
-    for (int s0 = 0; s0 < nsteps; s0 += kHwDwUnroll) {
-        hw_bf8 a[kHwDwUnroll][2], b[kHwDwUnroll][2];
-#pragma unroll
-        for (int u = 0; u < kHwDwUnroll; ++u) {
-            const int col = (16 * (s0 + u) + 8 * half) * 2;
-            const bool ok = s0 + u < nsteps;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                a[u][i] = __builtin_bit_cast(hw_bf8, __builtin_amdgcn_raw_buffer_load_b128(rk, ok ? ka[i] + col : kBufPast, 0, 0));
-                b[u][i] = __builtin_bit_cast(hw_bf8, __builtin_amdgcn_raw_buffer_load_b128(rgt, ok ? gb[i] + col : kBufPast, 0, 0));
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kHwDwUnroll; ++u)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][mb], b[u][nb], acc[mb][nb], 0, 0, 0);
-    }
-    // the product through LDS: accumulator r of lane (n, half) in block (mb, nb) is key
-    // 32 mb + 8 (r / 4) + 4 half + r % 4, gather index ts + 64 w + 32 nb + n
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                cbuf[(32 * mb + 8 * (r / 4) + 4 * half + r % 4) * kHwDwLd + 64 * w + 32 * nb + n] = acc[mb][nb][r];
-    __syncthreads();
-    // the tile's entries: 4 threads per list position, every 4th entry of its run with a gather
-    // index in [ts, te) (a contiguous part of the run, which is sorted by index)
-    const int pos = k0 + t / 4, sub = t % 4;
-    if (pos >= nkeys) return;
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(segs, nkeys * ncb * 4);
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gidx, nnz);
-    const v4i rec = __builtin_amdgcn_raw_buffer_load_b128(rs, (cb * nkeys + pos) * 16, 0, 0);
-    const float *crow = cbuf + (rec.x - k0) * kHwDwLd - ts;
-    for (int e0 = rec.y + sub; e0 < rec.z; e0 += 16) {
-        int g[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) g[u] = e0 + 4 * u < rec.z ? buf_ld(rg, (e0 + 4 * u) * 4) : 0x7FFFFFFF;
-        bool past = false;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (g[u] >= ts && g[u] < te) dW[e0 + 4 * u] = crow[g[u]];
-            past = past || g[u] >= te;
-        }
-        if (past) break;
-    }
-}
-
-// ---------------------------------------------------------------- weight gradient
-// xt [I][B], dyt [O][B] feature-major fp32.  A group of BT lanes per entry; lane
-// t covers batch columns t*VW + m*BT*VW (+0..VW-1).  Four steps of G entries are
-// loaded before any is reduced, so each lane has several gathers in flight.
-template <int BT, int VW>
-__global__ __launch_bounds__(kBlock) void sddmm_kernel(int64_t nnz, int64_t steps,
-                                                       const int32_t *__restrict__ rows,
-                                                       const int32_t *__restrict__ cols,
-                                                       const float *__restrict__ xt,
-                                                       const float *__restrict__ dyt, int64_t B,
-                                                       float *__restrict__ dW) {
-    constexpr int G = kWave / BT;
-    constexpr int U = 4;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int g = lane / BT, t = lane % BT;
-    const int64_t w = xcd_block() * kWavesPerBlock + threadIdx.x / kWave;
-    const int64_t kbase = w * steps * G;
-    for (int64_t s = 0; s < steps; s += U) {
-        if (kbase + s * G >= nnz) break;  // uniform per wave
-        int64_t k[U];
-        bool valid[U];
-        const float *xr[U];
-        const float *yr[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            k[u] = kbase + (s + u) * G + g;
-            valid[u] = (s + u < steps) && k[u] < nnz;
-            xr[u] = xt + (valid[u] ? static_cast<int64_t>(cols[k[u]]) * B : 0);
-            yr[u] = dyt + (valid[u] ? static_cast<int64_t>(rows[k[u]]) * B : 0);
-        }
-        float acc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] = 0.f;
-        if constexpr (VW == 4) {
-            for (int64_t bb = 4 * t; bb < B; bb += 4 * BT) {
-                float4 x[U], y[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    x[u] = valid[u] ? *reinterpret_cast<const float4 *>(xr[u] + bb) : make_float4(0.f, 0.f, 0.f, 0.f);
-                    y[u] = valid[u] ? *reinterpret_cast<const float4 *>(yr[u] + bb) : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    acc[u] += x[u].x * y[u].x;
-                    acc[u] += x[u].y * y[u].y;
-                    acc[u] += x[u].z * y[u].z;
-                    acc[u] += x[u].w * y[u].w;
-                }
-            }
-        } else {
-            for (int64_t bb = t; bb < B; bb += BT) {
-                float x[U], y[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    x[u] = valid[u] ? xr[u][bb] : 0.f;
-                    y[u] = valid[u] ? yr[u][bb] : 0.f;
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc[u] += x[u] * y[u];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int d = BT / 2; d >= 1; d >>= 1) acc[u] += __shfl_xor(acc[u], d, kWave);
-            if (valid[u] && t == 0) dW[k[u]] = acc[u];
-        }
-    }
-}
-
-// Largest r in [0, O) with offs[r] <= e, for 0 <= e < offs[O]: the row holding entry e.
-// Wave-parallel: each round samples the interval at 64 points.
-__device__ int csr_row_of(const int32_t *__restrict__ offs, int O, int e, int lane) {
-    int lo = 0, hi = O;  // offs[lo] <= e < offs[hi]
-    while (hi - lo > kWave) {
-        const int len = hi - lo;
-        const int q = lo + static_cast<int>((static_cast<int64_t>(lane) * len) >> 6);
-        const int c = __popcll(__ballot(offs[q] <= e));  // a prefix of the lanes, c >= 1
-        const int qa = lo + static_cast<int>((static_cast<int64_t>(c - 1) * len) >> 6);
-        hi = c == kWave ? hi : lo + static_cast<int>((static_cast<int64_t>(c) * len) >> 6);
-        lo = qa;
-    }
-    const int r = lo + lane;
-    const bool le = r < hi && offs[min(r, O)] <= e;
-    return lo + __popcll(__ballot(le)) - 1;
-}
-
-// As csr_row_of, trying first the 64 rows around the row that entry e would be in if
-// all rows had the average length (one round of loads for near-uniform layers).
-__device__ int csr_row_of_guess(const int32_t *__restrict__ offs, int O, int nnz, int e, int lane) {
-    // a guess only: float arithmetic (a 64-bit integer division costs ~100 scalar instructions)
-    const int g = static_cast<int>(static_cast<float>(e) * (static_cast<float>(O) *
-                                                            __builtin_amdgcn_rcpf(static_cast<float>(nnz))));
-    const int lo = max(0, min(g - kWave / 2, O - 1));
-    const int v = offs[min(lo + lane, O)];  // offs[O] = nnz > e
-    const int c = __popcll(__ballot(v <= e));
-    if (c >= 1 && c < kWave) return lo + c - 1;  // offs[lo + c - 1] <= e < offs[lo + c]
-    return csr_row_of(offs, O, e, lane);
-}
-
-// First index j in [lo, hi) with a[j] >= target (a ascending on [lo, hi)), or hi.
-// The wave first tries the 64 entries around `guess`, then narrows the interval
-// 64-fold per round of loads.  Every argument is uniform across the wave.
-__device__ int wave_lower_bound(const int32_t *__restrict__ a, int lo, int hi, int target, int guess, int lane) {
-    // invariant: the answer lies in [lo, hi]
-    if (hi - lo > kWave) {
-        const int w = min(max(guess - kWave / 2, lo), hi - kWave);
-        const int c = __popcll(__ballot(a[w + lane] < target));  // a prefix of the lanes
-        if (c > 0 && c < kWave) return w + c;
-        if (c == 0)
-            hi = w;
-        else
-            lo = w + kWave;
-    }
-    while (hi - lo > kWave) {
-        const int stride = (hi - lo + kWave - 1) / kWave;
-        const int j = lo + lane * stride;
-        const int c = __popcll(__ballot(j < hi && a[min(j, hi - 1)] < target));
-        if (c == 0) return lo;
-        const int nlo = lo + (c - 1) * stride + 1;
-        hi = min(hi, lo + c * stride);
-        lo = nlo;
-    }
-    if (hi <= lo) return lo;
-    const int j = lo + lane;
-    return lo + __popcll(__ballot(j < hi && a[min(j, hi - 1)] < target));
-}
-
-// Both gradients in one pass over the column view (batch 4*BT*Q, Q in 1..4).
-// A wave owns one input column i (with NB > 1: the column's entries whose rows lie in one
-// band of rows).  The column's X slice is held in registers (lane t: float4s t, t+BT, ..
-// of the feature-major X row i); each stored entry k gathers its dY row once and uses it
-// twice: dX[., i] += vals[k] * dY[., row k] (accumulated as in rowwave_kernel) and
-// dW[k] = <X[., i], dY[., row k]> (summed over the slot's BT lanes by DPP, written at the
-// entry's row-order position).  The window holds, per entry, the dY row as a 32-bit
-// float4 offset, the value and that position; lanes past the range point at dY's zero row.
-//
-// NB == 1: a workgroup owns 4 consecutive columns and writes dX directly.  COLV (values kept in
-// column-view order): the value and dW position of column-view entry j are j itself, so both
-// are read and written coalesced and col_perm is not read.
-// NB == kXcds: the rows are cut into 8 bands of about nnz/8 entries each, and workgroup g
-// takes band g % 8 of columns 4*(g/8) .. +3.  Under round-robin dispatch band b then runs
-// on XCD b alone, walking the columns in order: the dY rows, vals and dW positions that
-// XCD touches are one eighth of each, and the dW lines of a row fill within a short span
-// of columns, so they are completed in L2 instead of being written back piecemeal.  Each
-// wave writes its band's share of dX[., i] as a feature-major row of part[b]; a second
-// kernel adds the bands in order.
-template <int BT, int Q, int NB, typename OutT, bool COLV = false>
-__global__ __launch_bounds__(kBlock) void colbwd_kernel(
-    int64_t I, const int32_t *__restrict__ coffs, const int32_t *__restrict__ crows,
-    const int32_t *__restrict__ cperm, const float *__restrict__ vals, const float *__restrict__ xt,
-    const float *__restrict__ dyt, int zero_row, int64_t B, OutT *__restrict__ dX, float *__restrict__ dW,
-    const int32_t *__restrict__ offs, int nnz, float *__restrict__ part, int64_t nbo) {
-    constexpr int S = kWave / BT;
-    constexpr int UQ = 8 / Q;                                   // gathers in flight: U*Q float4s
-    constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;       // S*U divides 64
-    static_assert(U <= BT, "one storing lane per entry of a slot");
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    const int e = lane / BT, t = lane % BT;
-    int64_t col;
-    int band = 0;
-    if constexpr (NB == 1) {
-        col = xcd_block() * kWavesPerBlock + wave;
-    } else {
-        band = blockIdx.x % NB;
-        col = static_cast<int64_t>(blockIdx.x / NB) * kWavesPerBlock + wave;
-    }
-    const bool cok = col < I;  // uniform per wave
-    const int B4 = static_cast<int>(B / 4);
-    const char *__restrict__ yb = reinterpret_cast<const char *>(dyt);  // uniform base, 32-bit offsets
-    const uint32_t toff = 16u * static_cast<uint32_t>(t);
-    float4 acc[Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (cok) {
-        float4 xv[Q];
-        const float4 *__restrict__ x4 = reinterpret_cast<const float4 *>(xt) + col * B4 + t;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) xv[q] = x4[q * BT];
-        const int zoff = zero_row * B4;
-        int first = coffs[col], end = coffs[col + 1];
-        if constexpr (NB > 1) {
-            // rows [r0, r1) of this band: r_b = the row holding entry b*nnz/NB (r_0 = 0, r_NB = O).
-            // Both boundaries, and then both ends of the column's range, are found with loads
-            // issued together; a window that misses falls back to the full search.
-            const int O = zero_row;
-            const int e0 = static_cast<int>(static_cast<int64_t>(band) * nnz / NB);
-            const int e1 = min(nnz - 1, static_cast<int>(static_cast<int64_t>(band + 1) * nnz / NB));
-            const float rows_per_entry = static_cast<float>(O) * __builtin_amdgcn_rcpf(static_cast<float>(nnz));
-            const int q0 = max(0, min(static_cast<int>(e0 * rows_per_entry) - kWave / 2, O - 1));
-            const int q1 = max(0, min(static_cast<int>(e1 * rows_per_entry) - kWave / 2, O - 1));
-            const int o0 = offs[min(q0 + lane, O)], o1 = offs[min(q1 + lane, O)];  // offs[O] = nnz
-            const int c0 = __popcll(__ballot(o0 <= e0)), c1 = __popcll(__ballot(o1 <= e1));
-            int r0 = c0 >= 1 && c0 < kWave ? q0 + c0 - 1 : csr_row_of(offs, O, e0, lane);
-            int r1 = c1 >= 1 && c1 < kWave ? q1 + c1 - 1 : csr_row_of(offs, O, e1, lane);
-            if (band == 0) r0 = 0;
-            if (band == NB - 1) r1 = O;
-            const int s0 = first, len = end - first;
-            if (len > 0 && len <= kWave) {
-                const bool in = s0 + lane < end;
-                const int v = crows[min(s0 + lane, end - 1)];
-                first = s0 + __popcll(__ballot(in && v < r0));
-                end = s0 + __popcll(__ballot(in && v < r1));
-            } else if (len > kWave) {
-                // guesses: where the band's rows would start and end if the column's rows were uniform
-                const float per_row = static_cast<float>(len) * __builtin_amdgcn_rcpf(static_cast<float>(O));
-                const int g0 = s0 + static_cast<int>(per_row * r0), g1 = s0 + static_cast<int>(per_row * r1);
-                const int w0 = min(max(g0 - kWave / 2, s0), end - kWave);
-                const int w1 = min(max(g1 - kWave / 2, s0), end - kWave);
-                const int v0 = crows[w0 + lane], v1 = crows[w1 + lane];
-                const int n0 = __popcll(__ballot(v0 < r0)), n1 = __popcll(__ballot(v1 < r1));
-                const bool ok0 = (n0 > 0 || w0 == s0) && (n0 < kWave || w0 + kWave == end);
-                const bool ok1 = (n1 > 0 || w1 == s0) && (n1 < kWave || w1 + kWave == end);
-                const int j0 = ok0 ? w0 + n0 : wave_lower_bound(crows, s0, end, r0, g0, lane);
-                const int j1 = ok1 ? w1 + n1 : wave_lower_bound(crows, s0, end, r1, g1, lane);
-                first = j0;
-                end = j1;
-            }
-        }
-        int mo = zoff, mp = 0;
-        float mv = 0.f;
-        if (first + lane < end) {
-            mp = COLV ? first + lane : cperm[first + lane];
-            mo = crows[first + lane] * B4;
-            mv = vals[mp];
-        }
-        for (int base = first; base < end; base += kWave) {
-            const int co = mo, cp = mp;
-            const float cv = mv;
-            const int n = min(kWave, end - base);
-            const int nb = base + kWave;
-            if (nb < end) {  // prefetch this wave's next chunk
-                mo = zoff;
-                mp = 0;
-                mv = 0.f;
-                if (nb + lane < end) {
-                    mp = COLV ? nb + lane : cperm[nb + lane];
-                    mo = crows[nb + lane] * B4;
-                    mv = vals[mp];
-                }
-            }
-            for (int h = 0; h < n; h += S * U) {
-                const int sa = (h + e) << 2;
-                float4 y[U][Q];
-                float v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t o =
-                        16u * static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co)) + toff;
-                    v[u] = __int_as_float(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, __float_as_int(cv)));
-#pragma unroll
-                    for (int q = 0; q < Q; ++q)
-                        y[u][q] = *reinterpret_cast<const float4 *>(yb + (o + 16u * static_cast<uint32_t>(q * BT)));
-                }
-                // dW: the U dot products of a slot are reduce-scattered over its BT lanes; lane t
-                // with t % (BT/U) == 0 then holds entry h + e + S*(t / (BT/U)) and stores it.  The
-                // stores come after the step's last gather is used (loads and stores share one
-                // completion counter, so a store issued between the gathers would make each later
-                // wait also wait for that store).
-                float dv[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float d = 0.f;
-#pragma unroll
-                    for (int q = 0; q < Q; ++q) {
-                        acc[q].x = fmaf(v[u], y[u][q].x, acc[q].x);
-                        acc[q].y = fmaf(v[u], y[u][q].y, acc[q].y);
-                        acc[q].z = fmaf(v[u], y[u][q].z, acc[q].z);
-                        acc[q].w = fmaf(v[u], y[u][q].w, acc[q].w);
-                        d = fmaf(xv[q].x, y[u][q].x, d);
-                        d = fmaf(xv[q].y, y[u][q].y, d);
-                        d = fmaf(xv[q].z, y[u][q].z, d);
-                        d = fmaf(xv[q].w, y[u][q].w, d);
-                    }
-                    dv[u] = d;
-                }
-                {
-                    constexpr int R = BT / U;
-                    const float dsum = group_reduce_scatter<BT, U>(dv, t);
-                    const int us = t / R;
-                    const int k = __builtin_amdgcn_ds_bpermute(sa + 4 * S * us, cp);
-                    if (t % R == 0 && h + us * S + e < n)
-                        *reinterpret_cast<float *>(reinterpret_cast<char *>(dW) + 4u * static_cast<uint32_t>(k)) =
-                            dsum;
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-#pragma unroll
-        for (int d = BT; d < kWave; d <<= 1) {
-            acc[q].x += __shfl_xor(acc[q].x, d, kWave);
-            acc[q].y += __shfl_xor(acc[q].y, d, kWave);
-            acc[q].z += __shfl_xor(acc[q].z, d, kWave);
-            acc[q].w += __shfl_xor(acc[q].w, d, kWave);
-        }
-    }
-    if (cok && e == 0) {
-        if constexpr (NB == 1) {
-#pragma unroll
-            for (int q = 0; q < Q; ++q) {  // nbo of the B (padded) batch columns are stored
-                const int64_t b0 = 4 * static_cast<int64_t>(t + q * BT);
-                if (b0 + 0 < nbo) store_act(dX, (b0 + 0) * I + col, acc[q].x);
-                if (b0 + 1 < nbo) store_act(dX, (b0 + 1) * I + col, acc[q].y);
-                if (b0 + 2 < nbo) store_act(dX, (b0 + 2) * I + col, acc[q].z);
-                if (b0 + 3 < nbo) store_act(dX, (b0 + 3) * I + col, acc[q].w);
-            }
-        } else {
-            float4 *__restrict__ p4 = reinterpret_cast<float4 *>(part) + (band * I + col) * B4 + t;
-#pragma unroll
-            for (int q = 0; q < Q; ++q) p4[q * BT] = acc[q];
-        }
-    }
-}
-
-// dX[b][i] = sum over the NB bands, in band order, of part[band][i][b] (feature-major
-// fp32 partial sums, Bp columns per row) -> batch-major OutT for b < B.  A workgroup adds and transposes a tile of 32
-// columns x 64 batch rows through LDS; its stores are runs of 32 consecutive columns.
-template <int NB, typename OutT>
-__global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restrict__ part, int64_t I, int64_t Bp,
-                                                          int64_t B, OutT *__restrict__ dX) {
-    __shared__ float tile[kTb][kTf + 1];
-    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTf, b0 = static_cast<int64_t>(blockIdx.y) * kTb;
-    const int tid = threadIdx.x;
-    const int bq = tid % 16, cr = tid / 16;  // float4 bq of the tile's batch range, column cr and cr + 16
-    const int64_t B4 = Bp / 4;
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int64_t c = c0 + cr + 16 * rr;
-        const int64_t b4 = b0 / 4 + bq;
-        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c < I && b4 < B4) {
-            float4 v[NB];
-#pragma unroll
-            for (int k = 0; k < NB; ++k) v[k] = reinterpret_cast<const float4 *>(part)[(k * I + c) * B4 + b4];
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                s.x += v[k].x;
-                s.y += v[k].y;
-                s.z += v[k].z;
-                s.w += v[k].w;
-            }
-        }
-        tile[4 * bq + 0][cr + 16 * rr] = s.x;
-        tile[4 * bq + 1][cr + 16 * rr] = s.y;
-        tile[4 * bq + 2][cr + 16 * rr] = s.z;
-        tile[4 * bq + 3][cr + 16 * rr] = s.w;
-    }
-    __syncthreads();
-    const int c = tid % kTf;
-#pragma unroll
-    for (int k = 0; k < kTb / (kBlock / kTf); ++k) {
-        const int bb = tid / kTf + (kBlock / kTf) * k;
-        if (c0 + c < I && b0 + bb < B) store_act(dX, (b0 + bb) * I + c0 + c, tile[bb][c]);
-    }
-}
-
-// Weight gradient for batches 4*BT*Q with Q in 1..4: the rowwave mapping
-// for sampled products.  A workgroup owns 4/WPR rows of W, each split over WPR
-// waves; a wave keeps the row's dY slice in registers (lane t: float4s t,
-// t+BT, .. of the feature-major dY row, Q of them) for the whole row, takes
-// the row's entries 64 at a time with their X rows as 32-bit float4 offsets
-// (the next 64 prefetched; lanes past the row's end point at X's zero row),
-// gathers U entries per slot in flight and reduce-scatters each slot's U dot products over its
-// BT lanes by DPP.
-// ld: row stride (floats) of the feature-major copies; a batch wider than 4*BT*Q is taken in
-// slices of 4*BT*Q columns (xt and dyt offset by the slice), each adding into dW (ACC) after
-// the first.  ACC reads the U old dW values of a step before its gathers: loads and stores
-// complete in issue order on one counter, so a read issued after the gathers would make the
-// step wait for all of them before its first add.  UQ: entries per slot in flight (at most
-// 64/S); the slices measured fastest with 2 (5000 x 5000 at 90 %, batch 4096: 2.07 ms with 8,
-// 1.87 with 2), a single pass with 8.
-template <int BT, int WPR, int Q, int UQ, bool ACC>
-__global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32_t *__restrict__ offs,
-                                                          const int32_t *__restrict__ cols,
-                                                          const float *__restrict__ xt, int zero_row,
-                                                          const float *__restrict__ dyt, int64_t ld,
-                                                          float *__restrict__ dW) {
-    constexpr int S = kWave / BT;
-    constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;  // S*U divides 64
-    constexpr int KPB = kWavesPerBlock / WPR;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    const int e = lane / BT, t = lane % BT;
-    const int64_t r = xcd_block() * KPB + wave / WPR;
-    const int wsub = wave % WPR;
-    if (r >= O) return;  // uniform per wave; no barrier follows
-    const int B4 = static_cast<int>(ld / 4);
-    const char *__restrict__ xb = reinterpret_cast<const char *>(xt) + 16u * static_cast<uint32_t>(t);
-    const float4 *__restrict__ y4 = reinterpret_cast<const float4 *>(dyt) + r * B4 + t;
-    float4 dyv[Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) dyv[q] = y4[q * BT];
-    const int zoff = zero_row * B4;
-    const int s = offs[r], end = offs[r + 1];
-    const int first = s + wsub * kWave;
-    int mo = zoff;
-    if (first + lane < end) mo = cols[first + lane] * B4;
-    for (int base = first; base < end; base += WPR * kWave) {
-        const int co = mo;
-        const int n = min(kWave, end - base);
-        const int nb = base + WPR * kWave;
-        if (nb < end) {  // prefetch this wave's next chunk
-            mo = zoff;
-            if (nb + lane < end) mo = cols[nb + lane] * B4;
-        }
-        for (int h = 0; h < n; h += S * U) {
-            const int sa = (h + e) << 2;
-            // the slot's U dot products are reduce-scattered over its BT lanes: lane t with
-            // t % R == 0 ends with entry h + e + S*(t / R), and the wave's stores are contiguous
-            constexpr int R = BT / U;
-            const int src = h + (t / R) * S + e;
-            float old = 0.f;
-            if constexpr (ACC) old = dW[base + min(src, n - 1)];
-            float4 x[U][Q];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t o = 16u * static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co));
-#pragma unroll
-                for (int q = 0; q < Q; ++q)
-                    x[u][q] = *reinterpret_cast<const float4 *>(xb + (o + 16u * static_cast<uint32_t>(q * BT)));
-            }
-            float dv[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float d = 0.f;
-#pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    d = fmaf(x[u][q].x, dyv[q].x, d);
-                    d = fmaf(x[u][q].y, dyv[q].y, d);
-                    d = fmaf(x[u][q].z, dyv[q].z, d);
-                    d = fmaf(x[u][q].w, dyv[q].w, d);
-                }
-                dv[u] = d;
-            }
-            const float dsum = group_reduce_scatter<BT, U>(dv, t);
-            if (t % R == 0 && src < n) dW[base + src] = ACC ? old + dsum : dsum;
-        }
-    }
-}
-
-// Weight gradient for batches that are multiples of 4 (and >= 16).  A wave owns
-// a range of stored entries, read 64 at a time with the next 64 prefetched;
-// lanes are (slot e, lane t) with S = 64/BT slots, one entry each per step;
-// lane t covers batch float4s t, t+BT, ... of the entry's feature-major X row
-// (gathered, U steps in flight) and of its dY row, which is kept in registers
-// while consecutive entries stay in the same row (Q = B/(4*BT) float4s per
-// lane; Q == 0 means "too many to cache": reload per entry).  Each slot's BT
-// lanes are summed by xor shuffles.  Row offsets are 32-bit (the
-// feature-major copies are < 8 GB).
-template <int BT, int Q>
-__global__ __launch_bounds__(kBlock) void sddmm_wide_kernel(int64_t nnz, int64_t per_wave,
-                                                            const int32_t *__restrict__ rows,
-                                                            const int32_t *__restrict__ cols,
-                                                            const float *__restrict__ xt,
-                                                            const float *__restrict__ dyt, int64_t B,
-                                                            float *__restrict__ dW) {
-    constexpr int S = kWave / BT;
-    constexpr int U = 4;
-    constexpr int QC = Q > 0 ? Q : 1;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int e = lane / BT, t = lane % BT;
-    const int64_t wv = xcd_block() * kWavesPerBlock + threadIdx.x / kWave;
-    const int64_t k0 = wv * per_wave;
-    if (k0 >= nnz) return;  // uniform per wave
-    const int64_t k1 = min(k0 + per_wave, nnz);
-    const int B4 = static_cast<int>(B / 4);
-    const float4 *__restrict__ x4 = reinterpret_cast<const float4 *>(xt);
-    const float4 *__restrict__ y4 = reinterpret_cast<const float4 *>(dyt);
-    int crow = -1;          // row whose dY slice is cached
-    float4 dyc[QC];
-    int mr = 0, mc = 0;
-    if (k0 + lane < k1) {
-        mr = rows[k0 + lane];
-        mc = cols[k0 + lane];
-    }
-    for (int64_t base = k0; base < k1; base += kWave) {
-        const int cr = mr, cc = mc;
-        const int n = static_cast<int>(min<int64_t>(kWave, k1 - base));
-        const int64_t nb = base + kWave;
-        if (nb < k1) {
-            mr = 0;
-            mc = 0;
-            if (nb + lane < k1) {
-                mr = rows[nb + lane];
-                mc = cols[nb + lane];
-            }
-        }
-        for (int h = 0; h < n; h += S * U) {
-            int ro[U];
-            float p[U];
-            if constexpr (Q > 0) {
-                float4 xv[U][QC];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int src = h + u * S + e;  // < 64 because S*U divides 64
-                    const int xo = __shfl(cc, src, kWave) * B4 + t;
-                    ro[u] = __shfl(cr, src, kWave);
-#pragma unroll
-                    for (int q = 0; q < Q; ++q) xv[u][q] = x4[xo + q * BT];
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (ro[u] != crow) {  // row changed: refresh the cached dY slice
-                        crow = ro[u];
-#pragma unroll
-                        for (int q = 0; q < Q; ++q) dyc[q] = y4[crow * B4 + t + q * BT];
-                    }
-                    p[u] = 0.f;
-#pragma unroll
-                    for (int q = 0; q < Q; ++q) {
-                        p[u] += xv[u][q].x * dyc[q].x;
-                        p[u] += xv[u][q].y * dyc[q].y;
-                        p[u] += xv[u][q].z * dyc[q].z;
-                        p[u] += xv[u][q].w * dyc[q].w;
-                    }
-                }
-            } else {
-                int xo[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int src = h + u * S + e;
-                    xo[u] = __shfl(cc, src, kWave) * B4;
-                    ro[u] = __shfl(cr, src, kWave) * B4;
-                    p[u] = 0.f;
-                }
-                for (int q = t; q < B4; q += BT) {
-                    float4 xv[U], yv[U];
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        xv[u] = x4[xo[u] + q];
-                        yv[u] = y4[ro[u] + q];
-                    }
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        p[u] += xv[u].x * yv[u].x;
-                        p[u] += xv[u].y * yv[u].y;
-                        p[u] += xv[u].z * yv[u].z;
-                        p[u] += xv[u].w * yv[u].w;
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                p[u] = group_sum<BT>(p[u]);
-                const int src = h + u * S + e;
-                if (t == 0 && src < n) dW[base + src] = p[u];
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------- small-batch input gradient
-// For small B*I: each workgroup owns a contiguous range of stored entries in
-// row order (coalesced reads of rows, cols, vals), scatters vals[k]*dY[b,rows[k]]
-// into a private LDS copy of dX ([B][I]) with LDS atomic adds, and writes the
-// copy to partial[w].  dx_reduce_kernel sums the partials in workgroup order.
-// Summation order inside a workgroup follows the LDS atomics, so results are
-// equal to rounding but not bit-reproducible run to run.
-constexpr int kScatterThreads = 1024;
-
-template <typename InT>
-__global__ __launch_bounds__(kScatterThreads) void dx_scatter_kernel(int64_t nnz, int64_t per_wg, int64_t O,
-                                                                     int64_t I, int64_t B,
-                                                                     const int32_t *__restrict__ rows,
-                                                                     const int32_t *__restrict__ cols,
-                                                                     const float *__restrict__ vals,
-                                                                     const InT *__restrict__ dY,
-                                                                     float *__restrict__ partial) {
-    extern __shared__ float dxs[];
-    const int64_t n = B * I;
-    for (int64_t i = threadIdx.x; i < n; i += kScatterThreads) dxs[i] = 0.f;
-    __syncthreads();
-    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * per_wg;
-    const int64_t k1 = min(k0 + per_wg, nnz);
-    constexpr int U = 4;
-    for (int64_t k = k0 + threadIdx.x; k < k1; k += U * kScatterThreads) {
-        int r[U], c[U];
-        float v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t kk = k + u * kScatterThreads;
-            const bool ok = kk < k1;
-            r[u] = ok ? rows[kk] : 0;
-            c[u] = ok ? cols[kk] : 0;
-            v[u] = ok ? vals[kk] : 0.f;
-        }
-        for (int64_t b = 0; b < B; ++b) {
-            float d[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) d[u] = load_act(dY, b * O + r[u]);
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (k + u * kScatterThreads < k1) atomicAdd(&dxs[b * I + c[u]], v[u] * d[u]);
-        }
-    }
-    __syncthreads();
-    float *__restrict__ mine = partial + static_cast<int64_t>(blockIdx.x) * n;
-    for (int64_t i = threadIdx.x; i < n; i += kScatterThreads) mine[i] = dxs[i];
-}
-
-// out[i] = sum over w of partial[w][i], w ascending within each of 16 interleaved
-// slices, then the slices in order: a fixed summation order.  A workgroup covers
-// 64 outputs; its 16 waves take the slices and keep 8 loads in flight each.
-constexpr int kReduceThreads = 1024;
-template <typename OutT>
-__global__ __launch_bounds__(kReduceThreads) void dx_reduce_kernel(int64_t n, int64_t nparts,
-                                                                   const float *__restrict__ partial,
-                                                                   OutT *__restrict__ out) {
-    constexpr int kW = kReduceThreads / kWave;  // waves per workgroup, each over every kW-th part
-    __shared__ float slice_sum[kW][kWave];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kWave + lane;
-    float s = 0.f;
-    if (i < n) {
-        constexpr int U = 8;
-        int64_t w = wave;
-        for (; w + (U - 1) * kW < nparts; w += U * kW) {
-            float v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = partial[(w + u * kW) * n + i];
-#pragma unroll
-            for (int u = 0; u < U; ++u) s += v[u];
-        }
-        for (; w < nparts; w += kW) s += partial[w * n + i];
-    }
-    slice_sum[wave][lane] = s;
-    __syncthreads();
-    if (wave == 0 && i < n) {
-        float tot = slice_sum[0][lane];
-#pragma unroll
-        for (int q = 1; q < kW; ++q) tot += slice_sum[q][lane];
-        store_act(out, i, tot);
-    }
-}
-
-// ---------------------------------------------------------------- batch-1 CSR stream mapping
-// Batch 1: the activations are vectors, so an entry's work is one multiply
-// and the path is bound by streaming the triple.  A wave owns the entries
-// [e0, e1) of a fixed-size chunk of the row-sorted triple and reads only cols
-// and vals (8 bytes per entry): the row of each entry is recovered from
-// row_offsets, read 64 rows at a time into a window that also holds those
-// rows' bias (forward) or dY values (gradients).  Eight 64-entry steps of loads
-// are in flight.  A step lies inside one row unless a row ends in it; only
-// then are lanes told apart by row.
-
-__device__ __forceinline__ float readlane_f(float v, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Sum over the 64 lanes, the same value in every lane (fixed order).
-__device__ __forceinline__ float wave_sum(float v) {
-    v = group_sum<16>(v);
-    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
-}
-
-// 64 rows from rb: lane l holds the end offset of row rb + l and that row's value from rv
-// (bias or dY; 0 when rv is null).  Rows past O read row O - 1 / offset nnz (never used).
-template <typename ValT>
-__device__ __forceinline__ void csr_window(const int32_t *__restrict__ offs, int O, int rb, int lane,
-                                           const ValT *__restrict__ rv, int &wend, float &wval) {
-    wend = offs[min(rb + 1 + lane, O)];
-    wval = rv ? load_act(rv, min(rb + lane, O - 1)) : 0.f;
-}
-
-// x staged in LDS by 1024-thread workgroups (I <= kStageMaxI): a 4-byte gather from L2
-// moves a whole 64-byte line, so reading x once per workgroup saves ~16x the L2 traffic.
-constexpr int kStageThreads = 1024;
-constexpr int64_t kStageMaxI = 16384;
-
-// Copies x (I <= kStageMaxI elements) into LDS as fp32; every thread of the workgroup
-// takes part, issuing all of its loads before its stores (one round of latency).
-template <int THREADS, typename ActT>
-__device__ __forceinline__ void stage_vector(const ActT *__restrict__ x, int I, float *xs) {
-    constexpr int K = static_cast<int>(kStageMaxI / THREADS);
-    float v[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int i = threadIdx.x + k * THREADS;
-        v[k] = i < I ? load_act(x, i) : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int i = threadIdx.x + k * THREADS;
-        if (i < I) xs[i] = v[k];
-    }
-    __syncthreads();
-}
-
-// Forward, batch 1: y[r] = bias[r] + sum of the row's vals * x[cols].  Rows cut by a
-// chunk edge leave their partial sum in head[w] (the chunk's first row) or tail[w] (its
-// last row); fixup_kernel finishes them and the empty rows, as for segscan_kernel.
-// THREADS == kStageThreads: x is read from an LDS copy (I elements).
-template <typename ActT, typename OutT, int THREADS, bool VPERM = false>
-__global__ __launch_bounds__(THREADS) void csr1_fwd_kernel(int O, int I, int nnz, int chunk, int nchunks,
-                                                           const int32_t *__restrict__ offs,
-                                                           const int32_t *__restrict__ cols,
-                                                           const float *__restrict__ vals,
-                                                           const int32_t *__restrict__ vperm,
-                                                           const ActT *__restrict__ x,
-                                                           const float *__restrict__ bias, OutT *__restrict__ y,
-                                                           float *__restrict__ head, float *__restrict__ tail) {
-    constexpr int U = 8;
-    constexpr bool kStaged = THREADS == kStageThreads;
-    extern __shared__ float xs[];
-    if constexpr (kStaged) stage_vector<THREADS>(x, I, xs);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = static_cast<int>(xcd_block()) * (THREADS / kWave) +
-                  __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    if (w >= nchunks) return;  // uniform per wave, after the only barrier
-    const int e0 = w * chunk, e1 = min(e0 + chunk, nnz);
-    int r = csr_row_of_guess(offs, O, nnz, e0, lane);
-    const int rfirst = r;
-    int rs = __builtin_amdgcn_readfirstlane(offs[r]);  // start of row r
-    int rb = r, wend;
-    float wbias;
-    csr_window(offs, O, rb, lane, bias, wend, wbias);
-    int E = __builtin_amdgcn_readlane(wend, 0);  // end of row r
-    float acc = 0.f;
-    for (int s0 = e0; s0 < e1; s0 += U * kWave) {
-        float p[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = s0 + u * kWave + lane;
-            const int kk = min(k, e1 - 1);
-            const float v = vals[VPERM ? vperm[kk] : kk];
-            const int c = cols[kk];
-            const float xv = kStaged ? xs[c] : load_act(x, c);
-            p[u] = k < e1 ? v * xv : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = s0 + u * kWave;
-            if (s >= e1) break;
-            int from = 0;  // lanes below `from` belong to rows finished in this step
-            while (E < s + kWave && E < e1) {  // row r ends inside this step
-                const int cut = E - s;
-                const float tot = wave_sum(acc + ((lane >= from && lane < cut) ? p[u] : 0.f));
-                const float bv = readlane_f(wbias, r - rb);
-                acc = 0.f;
-                if (E > rs && lane == 0) {  // non-empty; empty rows are left to the fix-up
-                    if (rs >= e0)
-                        store_act(y, r, tot + bv);
-                    else
-                        head[w] = tot;
-                }
-                from = cut;
-                rs = E;
-                ++r;
-                if (r - rb >= kWave) {
-                    rb = r;
-                    csr_window(offs, O, rb, lane, bias, wend, wbias);
-                }
-                E = __builtin_amdgcn_readlane(wend, r - rb);
-            }
-            acc += lane >= from ? p[u] : 0.f;
-        }
-    }
-    // row r holds entry e1 - 1: complete if it started in this chunk and ends at e1
-    const float tot = wave_sum(acc);
-    const float bv = readlane_f(wbias, r - rb);
-    if (lane == 0) {
-        if (rs >= e0 && E == e1)
-            store_act(y, r, tot + bv);
-        else if (r == rfirst)
-            head[w] = tot;
-        else
-            tail[w] = tot;
-    }
-}
-
-// Walk of one 64-entry step for the gradients: every lane gets the dY value of its
-// entry's row.  Advances (r, E, window) past the rows that end inside the step.
-template <typename ActT>
-__device__ __forceinline__ float csr_step_rowval(int s, int e1, int lane, int O, const int32_t *__restrict__ offs,
-                                                 const ActT *__restrict__ dy, int &r, int &E, int &rb, int &wend,
-                                                 float &wdy) {
-    float dl = readlane_f(wdy, r - rb);
-    while (E < s + kWave && E < e1) {  // row r ends inside this step
-        const int cut = E - s;
-        ++r;
-        if (r - rb >= kWave) {
-            rb = r;
-            csr_window(offs, O, rb, lane, dy, wend, wdy);
-        }
-        E = __builtin_amdgcn_readlane(wend, r - rb);
-        const float d = readlane_f(wdy, r - rb);
-        dl = lane >= cut ? d : dl;
-    }
-    return dl;
-}
-
-// Weight gradient, batch 1: dW[k] = dY[row k] * X[cols[k]], streamed in row order.
-// THREADS == kStageThreads: x is read from an LDS copy (I elements).
-template <typename ActT, int THREADS>
-__global__ __launch_bounds__(THREADS) void csr1_dw_kernel(int O, int I, int nnz, int chunk, int nchunks,
-                                                          const int32_t *__restrict__ offs,
-                                                          const int32_t *__restrict__ cols,
-                                                          const ActT *__restrict__ x, const ActT *__restrict__ dy,
-                                                          float *__restrict__ dW) {
-    constexpr int U = 8;
-    constexpr bool kStaged = THREADS == kStageThreads;
-    extern __shared__ float xs[];
-    if constexpr (kStaged) stage_vector<THREADS>(x, I, xs);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = static_cast<int>(xcd_block()) * (THREADS / kWave) +
-                  __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    if (w >= nchunks) return;  // uniform per wave, after the only barrier
-    const int e0 = w * chunk, e1 = min(e0 + chunk, nnz);
-    int r = csr_row_of_guess(offs, O, nnz, e0, lane);
-    int rb = r, wend;
-    float wdy;
-    csr_window(offs, O, rb, lane, dy, wend, wdy);
-    int E = __builtin_amdgcn_readlane(wend, 0);
-    for (int s0 = e0; s0 < e1; s0 += U * kWave) {
-        float xv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = cols[min(s0 + u * kWave + lane, e1 - 1)];
-            xv[u] = kStaged ? xs[c] : load_act(x, c);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = s0 + u * kWave;
-            if (s >= e1) break;
-            const float dl = csr_step_rowval(s, e1, lane, O, offs, dy, r, E, rb, wend, wdy);
-            if (s + lane < e1) dW[s + lane] = dl * xv[u];
-        }
-    }
-}
-
-// Input gradient, batch 1, I <= 10240, without atomics: each of a workgroup's
-// 4 waves owns a private LDS copy of dX and the rows whose first entry lies in
-// its chunk.  A lane takes 4 consecutive entries per step (16-byte loads of cols
-// and vals), so a step covers 256 entries; two batches of kDxSteps steps are in
-// flight (a CU holds only 4 of these waves, so bytes in flight per wave set the
-// rate).  A step inside one row adds vals[k] * dY[row] into the copy with plain
-// reads and writes: a row's columns are distinct and a wave's LDS operations
-// complete in order.  A step that crosses row ends is taken row by row.  The
-// copies are then added in wave order into partial[blockIdx.x], and
-// dx_reduce_kernel adds the workgroups in order: the result is deterministic.
-// cols and vals must be 16-byte aligned (the plan checks).
-constexpr int kPrivWaves = 4;
-constexpr int64_t kPrivMaxI = 10240;  // 4 copies of dX in 160 KB of LDS
-constexpr int kDxSteps = 8;           // steps of 256 entries per batch of loads
-
-// 4 entries per lane from entry s + 4*lane, clamped to the 16-byte group at kmax (the wave's
-// last group below nnz & ~3).  Every path issues the same two loads, so the compiler's
-// completion counting stays exact, and loads past the wave's entries hit that one cached group
-// instead of fetching the next wave's; the entries [nnz & ~3, nnz) are taken separately.
-__device__ __forceinline__ void dxq_load(const int32_t *__restrict__ cols, const float *__restrict__ vals, int kmax,
-                                         int s, int lane, int4 &c, float4 &v) {
-    const int k = min(s + 4 * lane, kmax);
-    c = *reinterpret_cast<const int4 *>(cols + k);
-    v = *reinterpret_cast<const float4 *>(vals + k);
-}
-
-// Row r's entries in the step of 256 from s (lanes hold entries k0 .. k0 + 3), then the
-// following rows while they start inside the step, up to entry `lim`; the row state (r, its
-// start Es, end E and dY value d, and the 64-row window from rb) advances with them.
-template <typename ActT>
-__device__ __forceinline__ void dxq_rows(float *my, int s, int k0, const int4 &c, const float4 &v, int lim, int &r,
-                                         int &rb, int &Es, int &E, float &d, int &wend, float &wdy,
-                                         const int32_t *__restrict__ offs, int O, const ActT *__restrict__ dy,
-                                         int lane) {
-    while (true) {
-        const int lo = max(Es, s), hi = min(E, lim);
-        const bool p0 = k0 >= lo && k0 < hi, p1 = k0 + 1 >= lo && k0 + 1 < hi;
-        const bool p2 = k0 + 2 >= lo && k0 + 2 < hi, p3 = k0 + 3 >= lo && k0 + 3 < hi;
-        float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f;
-        if (p0) t0 = my[c.x];
-        if (p1) t1 = my[c.y];
-        if (p2) t2 = my[c.z];
-        if (p3) t3 = my[c.w];
-        if (p0) my[c.x] = fmaf(v.x, d, t0);
-        if (p1) my[c.y] = fmaf(v.y, d, t1);
-        if (p2) my[c.z] = fmaf(v.z, d, t2);
-        if (p3) my[c.w] = fmaf(v.w, d, t3);
-        if (E >= s + 4 * kWave || E >= lim) break;
-        Es = E;
-        ++r;
-        if (r - rb >= kWave) {
-            rb = r;
-            csr_window(offs, O, rb, lane, dy, wend, wdy);
-        }
-        E = __builtin_amdgcn_readlane(wend, r - rb);
-        d = readlane_f(wdy, r - rb);
-    }
-}
-
-template <typename ActT>
-__global__ __launch_bounds__(kPrivWaves *kWave) void csr1_dxpriv_kernel(int O, int I, int nnz, int chunk, int nwaves,
-                                                                       const int32_t *__restrict__ offs,
-                                                                       const int32_t *__restrict__ cols,
-                                                                       const float *__restrict__ vals,
-                                                                       const ActT *__restrict__ dy,
-                                                                       float *__restrict__ partial) {
-    extern __shared__ float cp[];  // [kPrivWaves][I]
-    constexpr int kThreads = kPrivWaves * kWave;
-    constexpr int kStep = 4 * kWave;
-    constexpr int kBatch = kDxSteps * kStep;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    const int w = blockIdx.x * kPrivWaves + wave;
-    const int a = w * chunk, b = min(a + chunk, nnz);
-    const int nnz4 = nnz & ~3;
-    // The first batch is loaded from the chunk's start before anything else (the row-aligned
-    // start E0 >= a is found while it is in flight; entries before E0 are not used).
-    const int s00 = a & ~3;
-    int4 ca[kDxSteps], cb[kDxSteps];
-    float4 va[kDxSteps], vb[kDxSteps];
-#pragma unroll
-    for (int u = 0; u < kDxSteps; ++u) dxq_load(cols, vals, nnz4 - 4, s00 + u * kStep, lane, ca[u], va[u]);
-    for (int i = threadIdx.x; i < kPrivWaves * I / 4; i += kThreads)  // 4*I floats: whole float4s
-        reinterpret_cast<float4 *>(cp)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    __syncthreads();
-    float *my = cp + wave * I;
-    if (w < nwaves) {  // uniform per wave; every wave reaches the barrier below
-        // entries [E0, E1): from the first row start >= a to the first row start >= b.  Both
-        // ends, and the row starting at E0, come from one 64-row window of row_offsets each
-        // (loaded together) when the rows near a and b are where uniform rows would put them.
-        const float rows_per_entry = static_cast<float>(O) * __builtin_amdgcn_rcpf(static_cast<float>(nnz));
-        const int la = max(0, min(static_cast<int>(a * rows_per_entry) - kWave / 2, O - 1));
-        const int lb = max(0, min(static_cast<int>(b * rows_per_entry) - kWave / 2, O - 1));
-        const int wa = offs[min(la + lane, O)], wb = offs[min(lb + lane, O)];  // offs[O] = nnz
-        const int na = __popcll(__ballot(wa <= a)), nb = __popcll(__ballot(wb <= b));
-        int E0, E1 = nnz;
-        const bool hit_a = na >= 1 && na < kWave;  // offs[la + na - 1] <= a < offs[la + na]
-        if (hit_a) {
-            const int oa = __builtin_amdgcn_readlane(wa, na - 1);
-            E0 = oa == a ? a : __builtin_amdgcn_readlane(wa, na);
-        } else {
-            const int ra = csr_row_of(offs, O, a, lane);
-            const int oa = __builtin_amdgcn_readfirstlane(offs[ra]);
-            E0 = oa == a ? a : __builtin_amdgcn_readfirstlane(offs[ra + 1]);
-        }
-        if (b < nnz) {
-            if (nb >= 1 && nb < kWave) {
-                const int ob = __builtin_amdgcn_readlane(wb, nb - 1);
-                E1 = ob == b ? b : __builtin_amdgcn_readlane(wb, nb);
-            } else {
-                const int rb1 = csr_row_of(offs, O, b, lane);
-                const int ob = __builtin_amdgcn_readfirstlane(offs[rb1]);
-                E1 = ob == b ? b : __builtin_amdgcn_readfirstlane(offs[rb1 + 1]);
-            }
-        }
-        if (E0 < E1) {
-            // r: the row starting at E0 (the last of several that start there), from the same
-            // window when it reaches past E0
-            const int cr = __popcll(__ballot(wa <= E0));
-            int r = hit_a && cr < kWave ? la + cr - 1 : csr_row_of(offs, O, E0, lane);
-            int rb = r, wend;
-            float wdy;
-            csr_window(offs, O, rb, lane, dy, wend, wdy);
-            int Es = E0;  // start of row r
-            int E = __builtin_amdgcn_readlane(wend, 0);
-            float d = readlane_f(wdy, 0);
-            const int E1m = min(E1, nnz4);  // the 16-byte loads cover [.., nnz4)
-            const int kmax = min(nnz4, (E1 + 3) & ~3) - 4;
-            // batch of kDxSteps steps from s0 in (c, v): the whole step in row r takes the fast path
-            auto run = [&](int s0, const int4 *c, const float4 *v) {
-#pragma unroll
-                for (int u = 0; u < kDxSteps; ++u) {
-                    const int s = s0 + u * kStep;
-                    if (s < E1m) {
-                        if (s >= Es && E >= s + kStep && E1m >= s + kStep) {  // the whole step is row r's
-                            const float t0 = my[c[u].x], t1 = my[c[u].y], t2 = my[c[u].z], t3 = my[c[u].w];
-                            my[c[u].x] = fmaf(v[u].x, d, t0);
-                            my[c[u].y] = fmaf(v[u].y, d, t1);
-                            my[c[u].z] = fmaf(v[u].z, d, t2);
-                            my[c[u].w] = fmaf(v[u].w, d, t3);
-                        } else {
-                            dxq_rows(my, s, s + 4 * lane, c[u], v[u], E1m, r, rb, Es, E, d, wend, wdy, offs, O, dy,
-                                     lane);
-                        }
-                    }
-                }
-                // every load of the batch is complete here on every path (a skipped step included),
-                // so the next batch's loads into these registers never wait for them
-#pragma unroll
-                for (int u = 0; u < kDxSteps; ++u) asm volatile("" ::"v"(c[u].x), "v"(v[u].x));
-            };
-            // two register sets used in turn (no copies, so no wait for the batch in flight)
-            for (int s0 = s00; s0 < E1m; s0 += 2 * kBatch) {
-#pragma unroll
-                for (int u = 0; u < kDxSteps; ++u)  // the next batch, unconditionally (clamped)
-                    dxq_load(cols, vals, kmax, s0 + kBatch + u * kStep, lane, cb[u], vb[u]);
-                run(s0, ca, va);
-                if (s0 + kBatch >= E1m) break;
-#pragma unroll
-                for (int u = 0; u < kDxSteps; ++u)
-                    dxq_load(cols, vals, kmax, s0 + 2 * kBatch + u * kStep, lane, ca[u], va[u]);
-                run(s0 + kBatch, cb, vb);
-            }
-            if (E1 > E1m) {  // entries [max(E0, nnz4), E1) at the end of the arrays: at most 3
-                const int s = nnz4, k0 = s + 4 * lane, last = nnz - 1;
-                const int4 ct = make_int4(cols[min(k0, last)], cols[min(k0 + 1, last)], cols[min(k0 + 2, last)],
-                                          cols[min(k0 + 3, last)]);
-                const float4 vt = make_float4(vals[min(k0, last)], vals[min(k0 + 1, last)], vals[min(k0 + 2, last)],
-                                              vals[min(k0 + 3, last)]);
-                dxq_rows(my, s, k0, ct, vt, E1, r, rb, Es, E, d, wend, wdy, offs, O, dy, lane);
-            }
-        }
-    }
-    __syncthreads();
-    float *__restrict__ mine = partial + static_cast<int64_t>(blockIdx.x) * I;
-    if (I % 4 == 0) {  // the copies and this partial are float4-aligned
-        const float4 *c4 = reinterpret_cast<const float4 *>(cp);
-        const int I4 = I / 4;
-        for (int i = threadIdx.x; i < I4; i += kThreads) {
-            float4 t = c4[i];
-#pragma unroll
-            for (int q = 1; q < kPrivWaves; ++q) {
-                const float4 o = c4[q * I4 + i];
-                t.x += o.x;
-                t.y += o.y;
-                t.z += o.z;
-                t.w += o.w;
-            }
-            reinterpret_cast<float4 *>(mine)[i] = t;
-        }
-    } else {
-        for (int i = threadIdx.x; i < I; i += kThreads) {
-            float t = cp[i];
-#pragma unroll
-            for (int q = 1; q < kPrivWaves; ++q) t += cp[q * I + i];
-            mine[i] = t;
-        }
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void zero_kernel(float *__restrict__ p, int64_t n) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (i < n) p[i] = 0.f;
-}
-
-// ---------------------------------------------------------------- bias gradient
-template <typename InT>
-__global__ __launch_bounds__(kBlock) void bias_grad_kernel(int64_t O, int64_t B, const InT *__restrict__ dY,
-                                                           float *__restrict__ db) {
-    const int64_t o = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (o >= O) return;
-    float s = 0.f;
-    for (int64_t b = 0; b < B; ++b) s += load_act(dY, b * O + o);
-    db[o] = s;
-}
 
 // ================================================================ host side
 using snack::fail;
