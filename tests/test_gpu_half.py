@@ -16,7 +16,9 @@ and columns (segments of a whole block), empty rows, key counts that leave a par
 wide kernel's groups of four tiles with a partial last group), values in row order
 and in column order (each kernel both with and without the value permutation), the 10000 x 10000
 layer at 95 % and batch 64 in full, reruns equal bit for bit, the allocation-free forward equal to
-the forward, and the shape and alignment errors of the path.
+the forward, and the shape and alignment errors of the path; and a seeded random sweep of 24 layers (feature
+counts multiples of 8, six structures, batches 1 to 513, both value orders) through the forward,
+the input gradient, the backward call and the matrix-core weight gradient.
 """
 import math
 
@@ -333,3 +335,50 @@ def test_bf16_weight_gradient_on_matrix_cores(layers, name, B, order, half_weigh
         ref = ref[built["col_perm"].astype(np.int64)]
     check_close(dW.cpu().numpy(), ref, B, f"bf16 dW {name} B={B} ({order})")
     check_close(dW2.cpu().numpy(), ref, B, f"bf16 bwd dW {name} B={B} ({order})")
+
+
+def _half_random_cases(n=24, seed=8888):
+    """Random layers whose feature counts are multiples of 8 (what the path requires), random
+    densities and structures, batches from 1 to 513 (one partial tile, several tiles, the wide
+    kernel's groups of four), values in either order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = ["uniform", "empty_rows", "dense_lines", "skewed_rows", "one_row", "one_col"]
+    batches = [1, 3, 16, 33, 64, 65, 128, 255, 256, 300, 513]
+    out = []
+    for i in range(n):
+        O = 8 * int(rng.integers(1, 400))
+        I = 8 * int(rng.integers(1, 400))
+        dens = float(10 ** rng.uniform(-3.0, -0.5))
+        B = batches[int(rng.integers(0, len(batches)))]
+        nnz = max(1, min(O * I, int(dens * O * I), 300_000_000 // B))
+        shape = shapes[int(rng.integers(0, len(shapes)))]
+        order = "col" if rng.random() < 0.5 else "row"
+        out.append((9600 + i, shape, O, I, nnz, B, order))
+    return out
+
+
+@pytest.mark.parametrize("case", _half_random_cases(),
+                         ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-n{c[4]}-B{c[5]}-{c[6]}")
+def test_half_random_sweep(case):
+    """Forward and input gradient with half weights against the oracle on the rounded weights
+    (check_half), and the weight gradient of the same bf16 activations with the matrix-core form
+    forced on at batches of 256 and more (fp32 tolerance), else the library's choice (bf16
+    tolerance)."""
+    seed, shape, O, I, nnz, B, order = case
+    say(f"half random {shape} {O}x{I} nnz={nnz} B={B} values in {order} order")
+    L = synth.random_small_layer(seed, O, I, nnz, shape)
+    if L["nnz"] == 0:
+        pytest.skip("the shape left no entries")
+    W, X, dY, b, Y, dX, built, x64, dy64 = _run(L, B, seed, order)
+    ref = oracle.grad_weight(O, I, built["rows"], built["cols"], x64, dy64, nthreads=NTHREADS)
+    if order == "col":
+        ref = ref[built["col_perm"].astype(np.int64)]
+    if B >= 256:
+        with snk.option(snk.OPT_BF16_DW_MFMA, 1):
+            dW = snk.snack_coo_grad_weight(W, X, dY, half_weights=True)
+            torch.cuda.synchronize()
+        check_close(dW.cpu().numpy(), ref, B, f"half random dW (matrix cores) B={B}")
+    dX2, dW2 = snk.snack_coo_bwd(W, X, dY, half_weights=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dX2, dX)
+    check_close(dW2.cpu().numpy(), ref, B, f"half random bwd dW B={B}", True)
