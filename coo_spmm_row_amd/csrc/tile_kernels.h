@@ -10,8 +10,9 @@ namespace {
 // The same gather-reduce as rowwave (out[key][:] = sum over the key's entries of
 // vals * opnd[gidx][:]), with the operand rows served from LDS instead of L2.  W is cut into
 // tiles of (a range of keys) x (a block of cw operand rows); a 1024-thread workgroup stages its
-// block of the feature-major operand (cw rows of 64 batch columns, 256 B each, plus one zero
-// row: up to 160 KB, gfx950's LDS) once, then walks its keys' segments inside the block.  The
+// block of the operand, read in place from the batch-major activations (cw rows of 64 batch
+// columns, 256 B each, plus one zero row: up to 160 KB, gfx950's LDS) once, then walks its keys'
+// segments inside the block.  The
 // segments come from a per-block segment list (tile_segments_kernel; the triple is sorted by key,
 // then by gather index, so each segment is a contiguous run of the key's entries), whose keys are
 // ordered by segment length within windows of kSegWindow keys: the four keys a wave walks together
@@ -22,7 +23,8 @@ namespace {
 // Lanes: 4 slots of 16 lanes; slot s walks key 4*g + s of the wave's group g, and each lane holds
 // VW batch columns (VW floats) of a TB = 16*VW column batch tile (64 for batches padded to a
 // multiple of 64, else 32 or 16).  A group's entries are loaded 16 per chunk register (each row
-// of 16 lanes holds entries j = 0..15 of its slot's chunk), two groups ahead of the compute.
+// of 16 lanes holds entries j = 0..15 of its slot's chunk), one group ahead of the compute (two
+// when the values are read through a permutation, the values themselves one ahead).
 // Step t of a chunk hands entry t to every lane of its row with DPP row_newbcast:t: folded into
 // the row address (an XOR), and moved once into a register for the value, so one step costs one
 // LDS read of VW floats per lane, an address XOR, a value move and VW plain FMAs.  Entries past a
