@@ -539,7 +539,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_sddmm_kernel(
 #pragma unroll
             for (int t = 0; t < 16; ++t) p[t] = 0.f;
             tile_dot_chunk<VW>(p, off, m - 16 * c, lane_off, lds, dy);
-            const float r = group_reduce_scatter<16, 16>(p, j);
+            const float r = chunk_reduce_scatter(p, m - 16 * c, j);
             if (16 * c + j < len) {
                 float *d = dw + a + 16 * c + j;
                 *d = bt == 0 ? r : *d + r;
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_bwd_kernel(
         if (nst > 4) tile_bwd_steps4<VW, 4>(acc, p, off, v, lane_off, lds, xsl);
         if (nst > 8) tile_bwd_steps4<VW, 8>(acc, p, off, v, lane_off, lds, xsl);
         if (nst > 12) tile_bwd_steps4<VW, 12>(acc, p, off, v, lane_off, lds, xsl);
-        const float r = group_reduce_scatter<16, 16>(p, j);
+        const float r = chunk_reduce_scatter(p, nst, j);
         if (16 * c + j < len) dw[wpos] = r;
     };
     auto compute = [&](int G, int key, int a, int len, const int (&gi)[CH], const int (&vv)[CH],
