@@ -123,22 +123,34 @@ __global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B,
 // consumed, and keeps U*Q float4 gathers in flight.  Lanes of a chunk past the
 // key's end point at the operand's zero row with value 0, so no step needs a
 // mask.  Slot partial sums are combined by xor shuffles, the WPR waves of a
-// key through LDS.  The operand including its zero row is below 4 GB.  B is the operand's batch
-// columns (a multiple of 4; zero columns pad a batch of nbo columns), nbo the columns stored.
+// key through LDS.  A workgroup of 16 waves owns 16 / WPR consecutive keys; their results are
+// staged in LDS and written with consecutive threads on consecutive keys of one batch row, so each
+// row of the batch-major output gets one run of 16 / WPR keys per workgroup instead of one
+// scattered 2- or 4-byte store per key (written per key, those stores cost about as much as the
+// rest of the kernel at batch 1024).  The operand including its zero row is below 4 GB.  B is the
+// operand's batch columns (a multiple of 4; zero columns pad a batch of nbo columns), nbo the
+// columns stored.
+constexpr int kRwThreads = 1024;
+constexpr int kRwWaves = kRwThreads / kWave;
+
 template <int BT, int WPR, int Q, typename OutT>
-__global__ __launch_bounds__(kBlock) void rowwave_kernel(
+__global__ __launch_bounds__(kRwThreads) void rowwave_kernel(
     int64_t nkeys, const int32_t *__restrict__ offs, const int32_t *__restrict__ gidx,
     const float *__restrict__ vals, const int32_t *__restrict__ perm, const float *__restrict__ opnd, int zero_row,
     int64_t B, const float *__restrict__ bias, OutT *__restrict__ out, int64_t out_ld, int64_t nbo) {
     constexpr int S = kWave / BT;
     constexpr int UQ = 8 / Q;
     constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;  // S*U divides 64
-    constexpr int KPB = kWavesPerBlock / WPR;             // keys per workgroup
-    __shared__ float4 part[kWavesPerBlock][Q][BT];
+    constexpr int KPB = kRwWaves / WPR;                   // keys per workgroup
+    constexpr int TBC = 4 * BT * Q;                       // batch columns of the tile
+    constexpr int OLD = TBC + 4;                          // floats per staged output row
+    __shared__ float4 part[WPR > 1 ? kRwWaves : 1][Q][BT];
+    __shared__ __align__(16) float ost[KPB][OLD];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int e = lane / BT, t = lane % BT;
-    const int64_t r = xcd_block() * KPB + wave / WPR;
+    const int64_t k0 = xcd_block() * KPB;
+    const int64_t r = k0 + wave / WPR;
     const int wsub = wave % WPR;
     const bool rok = r < nkeys;  // uniform per wave
     const int64_t b0 = static_cast<int64_t>(blockIdx.y) * (4 * BT * Q) + 4 * t;
@@ -231,20 +243,18 @@ __global__ __launch_bounds__(kBlock) void rowwave_kernel(
     }
     if (rok && wsub == 0 && e == 0 && bok) {
         const float bv = bias ? bias[r] : 0.f;
+        float *row = ost[wave / WPR];
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int64_t c = b0 + 4 * q * BT;
-            if (c + 3 < nbo) {
-                store_act(out, (c + 0) * out_ld + r, acc[q].x + bv);
-                store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
-                store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
-                store_act(out, (c + 3) * out_ld + r, acc[q].w + bv);
-            } else {  // the last, padded float4 of the batch
-                if (c + 0 < nbo) store_act(out, (c + 0) * out_ld + r, acc[q].x + bv);
-                if (c + 1 < nbo) store_act(out, (c + 1) * out_ld + r, acc[q].y + bv);
-                if (c + 2 < nbo) store_act(out, (c + 2) * out_ld + r, acc[q].z + bv);
-            }
-        }
+        for (int q = 0; q < Q; ++q)
+            *reinterpret_cast<float4 *>(row + 4 * t + 4 * q * BT) =
+                make_float4(acc[q].x + bv, acc[q].y + bv, acc[q].z + bv, acc[q].w + bv);
+    }
+    __syncthreads();
+    // columns past the batch (never staged) and keys past the layer are not written
+    const int64_t c0 = static_cast<int64_t>(blockIdx.y) * TBC;
+    for (int i = threadIdx.x; i < KPB * TBC; i += kRwThreads) {
+        const int k = i % KPB, c = i / KPB;
+        if (k0 + k < nkeys && c0 + c < nbo) store_act(out, (c0 + c) * out_ld + k0 + k, ost[k][c]);
     }
 }
 

@@ -749,14 +749,14 @@ void launch_rowwave_bt(int64_t nkeys, int64_t nnz, const int32_t *offs, const in
     // values are read through the column permutation: one wave per key keeps co-resident
     // waves walking rows in step, so those reads share L2 lines
     const bool split = !perm && nnz >= 256 * nkeys;
-    const int64_t keys_per_block = split ? 1 : kWavesPerBlock;
+    const int64_t keys_per_block = split ? kRwWaves / 4 : kRwWaves;
     const int64_t blocks = round_up8(ceil_div(nkeys, keys_per_block));
     const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(ceil_div(B, 4 * BT * Q)));
     if (split)
-        hipLaunchKernelGGL((rowwave_kernel<BT, 4, Q, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
+        hipLaunchKernelGGL((rowwave_kernel<BT, 4, Q, OutT>), grid, dim3(kRwThreads), 0, st, nkeys, offs, gidx, vals,
                            perm, opnd, zero_row, B, bias, out, out_ld, nbo);
     else
-        hipLaunchKernelGGL((rowwave_kernel<BT, 1, Q, OutT>), grid, dim3(kBlock), 0, st, nkeys, offs, gidx, vals,
+        hipLaunchKernelGGL((rowwave_kernel<BT, 1, Q, OutT>), grid, dim3(kRwThreads), 0, st, nkeys, offs, gidx, vals,
                            perm, opnd, zero_row, B, bias, out, out_ld, nbo);
 }
 
