@@ -367,27 +367,29 @@ __global__ __launch_bounds__(kBlock) void band_sum_kernel(const float *__restric
 // Weight gradient for batches 4*BT*Q with Q in 1..4: the rowwave mapping
 // for sampled products.  A workgroup owns 4/WPR rows of W, each split over WPR
 // waves; a wave keeps the row's dY slice in registers (lane t: float4s t,
-// t+BT, .. of the feature-major dY row, Q of them) for the whole row, takes
-// the row's entries 64 at a time with their X rows as 32-bit float4 offsets
-// (the next 64 prefetched; lanes past the row's end point at X's zero row),
-// gathers U entries per slot in flight and reduce-scatters each slot's U dot products over its
-// BT lanes by DPP.
-// ld: row stride (floats) of the feature-major copies; a batch wider than 4*BT*Q is taken in
-// slices of 4*BT*Q columns (xt and dyt offset by the slice), each adding into dW (ACC) after
-// the first.  ACC reads the U old dW values of a step before its gathers: loads and stores
-// complete in issue order on one counter, so a read issued after the gathers would make the
-// step wait for all of them before its first add.  UQ: entries per slot in flight (at most
-// 64/S); the slices measured fastest with 2 (5000 x 5000 at 90 %, batch 4096: 2.07 ms with 8,
-// 1.87 with 2), a single pass with 8.
-template <int BT, int WPR, int Q, int UQ, bool ACC>
+// t+BT, .. of the feature-major dY row, Q of them), takes the row's entries 64
+// at a time with their X rows as 32-bit float4 offsets (the next 64 prefetched;
+// lanes past the row's end point at X's zero row), gathers U entries per slot
+// in flight and reduce-scatters each slot's U dot products over its BT lanes by DPP.
+// ld: row stride (floats) of the feature-major copies.  A batch wider than 4*BT*Q is taken in
+// nslices slices of 4*BT*Q columns within each chunk of 64 entries: the slice's dY registers are
+// loaded once per chunk, and each step's partial dot products are added in slice order in
+// registers (NSTEP of them per lane), so dW is written once.  UQ: entries per slot in flight (at
+// most 64/S); the sliced form measured fastest with 2, a single slice with 8.
+template <int BT, int WPR, int Q, int UQ>
 __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32_t *__restrict__ offs,
                                                           const int32_t *__restrict__ cols,
                                                           const float *__restrict__ xt, int zero_row,
-                                                          const float *__restrict__ dyt, int64_t ld,
+                                                          const float *__restrict__ dyt, int64_t ld, int nslices,
                                                           float *__restrict__ dW) {
     constexpr int S = kWave / BT;
     constexpr int U = (S * UQ <= kWave) ? UQ : kWave / S;  // S*U divides 64
     constexpr int KPB = kWavesPerBlock / WPR;
+    constexpr int TBC = 4 * BT * Q;                        // batch columns per slice
+    constexpr int NSTEP = kWave / (S * U);                 // steps per chunk of 64 entries
+    // the slot's U dot products are reduce-scattered over its BT lanes: lane t with t % R == 0
+    // ends with entry h + e + S*(t / R) of step h, and the wave's stores are contiguous
+    constexpr int R = BT / U;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int e = lane / BT, t = lane % BT;
@@ -398,8 +400,11 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
     const char *__restrict__ xb = reinterpret_cast<const char *>(xt) + 16u * static_cast<uint32_t>(t);
     const float4 *__restrict__ y4 = reinterpret_cast<const float4 *>(dyt) + r * B4 + t;
     float4 dyv[Q];
+    auto load_dy = [&](int k) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) dyv[q] = y4[q * BT];
+        for (int q = 0; q < Q; ++q) dyv[q] = y4[k * (TBC / 4) + q * BT];
+    };
+    if (nslices == 1) load_dy(0);
     const int zoff = zero_row * B4;
     const int s = offs[r], end = offs[r + 1];
     const int first = s + wsub * kWave;
@@ -413,37 +418,48 @@ __global__ __launch_bounds__(kBlock) void rowsddmm_kernel(int64_t O, const int32
             mo = zoff;
             if (nb + lane < end) mo = cols[nb + lane] * B4;
         }
-        for (int h = 0; h < n; h += S * U) {
-            const int sa = (h + e) << 2;
-            // the slot's U dot products are reduce-scattered over its BT lanes: lane t with
-            // t % R == 0 ends with entry h + e + S*(t / R), and the wave's stores are contiguous
-            constexpr int R = BT / U;
-            const int src = h + (t / R) * S + e;
-            float old = 0.f;
-            if constexpr (ACC) old = dW[base + min(src, n - 1)];
-            float4 x[U][Q];
+        float acc[NSTEP];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t o = 16u * static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co));
+        for (int j = 0; j < NSTEP; ++j) acc[j] = 0.f;
+        for (int k = 0; k < nslices; ++k) {
+            if (nslices > 1) load_dy(k);
+            const uint32_t xs = 16u * static_cast<uint32_t>(k * (TBC / 4));  // slice k's byte offset
 #pragma unroll
-                for (int q = 0; q < Q; ++q)
-                    x[u][q] = *reinterpret_cast<const float4 *>(xb + (o + 16u * static_cast<uint32_t>(q * BT)));
-            }
-            float dv[U];
+            for (int j = 0; j < NSTEP; ++j) {
+                const int h = j * S * U;
+                if (h < n) {
+                    const int sa = (h + e) << 2;
+                    float4 x[U][Q];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float d = 0.f;
+                    for (int u = 0; u < U; ++u) {
+                        const uint32_t o =
+                            16u * static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(sa + 4 * S * u, co)) + xs;
 #pragma unroll
-                for (int q = 0; q < Q; ++q) {
-                    d = fmaf(x[u][q].x, dyv[q].x, d);
-                    d = fmaf(x[u][q].y, dyv[q].y, d);
-                    d = fmaf(x[u][q].z, dyv[q].z, d);
-                    d = fmaf(x[u][q].w, dyv[q].w, d);
+                        for (int q = 0; q < Q; ++q)
+                            x[u][q] = *reinterpret_cast<const float4 *>(xb + (o + 16u * static_cast<uint32_t>(q * BT)));
+                    }
+                    float dv[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        float d = 0.f;
+#pragma unroll
+                        for (int q = 0; q < Q; ++q) {
+                            d = fmaf(x[u][q].x, dyv[q].x, d);
+                            d = fmaf(x[u][q].y, dyv[q].y, d);
+                            d = fmaf(x[u][q].z, dyv[q].z, d);
+                            d = fmaf(x[u][q].w, dyv[q].w, d);
+                        }
+                        dv[u] = d;
+                    }
+                    const float dsum = group_reduce_scatter<BT, U>(dv, t);
+                    acc[j] = k == 0 ? dsum : acc[j] + dsum;
                 }
-                dv[u] = d;
             }
-            const float dsum = group_reduce_scatter<BT, U>(dv, t);
-            if (t % R == 0 && src < n) dW[base + src] = ACC ? old + dsum : dsum;
+        }
+#pragma unroll
+        for (int j = 0; j < NSTEP; ++j) {
+            const int src = j * S * U + (t / R) * S + e;
+            if (t % R == 0 && src < n) dW[base + src] = acc[j];
         }
     }
 }

@@ -1480,8 +1480,8 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
             const dim3 rgrid(static_cast<unsigned>(round_up8(ceil_div(O, split ? 1 : kWavesPerBlock))));
             const int zero_row = static_cast<int>(I);
 #define SNACK_ROWSD(BTV, WPRV, QV)                                                                           \
-    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV, 8, false>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, \
-                       W->cols, xt, zero_row, dyt, p.bpad, dW)
+    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV, 8>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, \
+                       W->cols, xt, zero_row, dyt, p.bpad, 1, dW)
 #define SNACK_ROWSD_Q(BTV, WPRV)                         \
     do {                                                 \
         if (p.rowq == 1) SNACK_ROWSD(BTV, WPRV, 1);      \
@@ -1493,20 +1493,14 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
     if (split) SNACK_ROWSD_Q(BTV, 4);       \
     else SNACK_ROWSD_Q(BTV, 1);
             if (p.slices > 1) {
-                // slice k: columns [256k, 256k + 256) of the copies (one launch per slice, in order)
-                for (int64_t k = 0; k < p.slices; ++k) {
-#define SNACK_ROWSD_SLICE(WPRV, ACCV)                                                                          \
-    hipLaunchKernelGGL((rowsddmm_kernel<16, WPRV, 4, 2, ACCV>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, W->cols, \
-                       xt + 256 * k, zero_row, dyt + 256 * k, p.bpad, dW)
-                    if (split) {
-                        if (k > 0) SNACK_ROWSD_SLICE(4, true);
-                        else SNACK_ROWSD_SLICE(4, false);
-                    } else {
-                        if (k > 0) SNACK_ROWSD_SLICE(1, true);
-                        else SNACK_ROWSD_SLICE(1, false);
-                    }
-#undef SNACK_ROWSD_SLICE
-                }
+                // slices of 256 columns of the copies, added in order inside one launch
+                const int ns = static_cast<int>(p.slices);
+                if (split)
+                    hipLaunchKernelGGL((rowsddmm_kernel<16, 4, 4, 2>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets,
+                                       W->cols, xt, zero_row, dyt, p.bpad, ns, dW);
+                else
+                    hipLaunchKernelGGL((rowsddmm_kernel<16, 1, 4, 2>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets,
+                                       W->cols, xt, zero_row, dyt, p.bpad, ns, dW);
             } else if (p.bt == 16) {
                 SNACK_ROWSD_BT(16)
             } else if (p.bt == 8) {
