@@ -387,10 +387,11 @@ SddmmPlan plan_sddmm(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bo
                 break;
             }
         }
-        // wide batch, large layer or rows averaging < 16 entries:
-        if (p.rowq == 0 && Bp % 256 == 0 && (nnz >= kLargeBatchMinNnz || nnz < 16 * O)) {
-            // slices of 256 columns (each gathers its part of the X rows once per entry; the
-            // per-entry kernel re-reads the whole dY row per entry)
+        // wider batches in multiples of 256: slices of 256 columns in one launch (each gathers
+        // its part of the X rows once per entry; the per-entry kernel re-reads the whole dY row
+        // per entry).  Against the per-entry kernel: GPT-2 3072->768 weight gradient at batch 512
+        // 11.8 against 19.5 us, 5000 x 5000 at 99 % at batch 1024 97 against 115 us.
+        if (p.rowq == 0 && Bp % 256 == 0) {
             p.bt = 16;
             p.rowq = 4;
             p.slices = Bp / 256;
