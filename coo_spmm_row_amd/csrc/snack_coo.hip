@@ -562,7 +562,11 @@ struct BwdPlan {
     // starts at off_spmm, the weight gradient's segment table at off_sddmm.
     // tiled: both gradients in one tiled pass over the column view (tile_bwd_kernel), its segment
     // table and dX partials in the workspace at off_spmm (laid out by sp)
-    bool split, tiled;
+    // shared: the input gradient over the column view and the weight gradient both by the
+    // row-wave kernels, which read feature-major copies of dY (and X): one copy of each made once,
+    // in the weight gradient's workspace at off_sddmm (laid out by sd); the input gradient's
+    // workspace at off_spmm
+    bool split, tiled, shared;
     SpmmPlan sp;
     SddmmPlan sd;
     size_t off_spmm, off_sddmm;
@@ -656,8 +660,20 @@ BwdPlan plan_bwd(int64_t nnz, int64_t O, int64_t I, int64_t B, int dtype, bool a
     } else {
         // the separate calls; the weight gradient's segment lists counted as if the descriptor had none
         const HwDwPlan hp = plan_hw_dw(nnz, O, I, B, dtype, colvals, nullptr);
-        p.total = std::max(plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals).total,
-                           hp.use ? hp.total : plan_sddmm(nnz, O, I, B, dtype, colvals).total);
+        const SpmmPlan sp = plan_spmm(nnz, O, I, B, dtype, true, aligned16, colvals);
+        const SddmmPlan sd = plan_sddmm(nnz, O, I, B, dtype, colvals);
+        p.total = std::max(sp.total, hp.use ? hp.total : sd.total);
+        // both by the row-wave kernels on copies of the same padding: the copies made once
+        // (GPT-2 768->3072 at batch 1024: the step's second 12.6 MB copy of dY and its launch)
+        if (nnz > 0 && B > 0 && I > 0 && O > 0 && !hp.use && sp.mapping == kRowwave && !sp.direct &&
+            sd.rowq > 0 && !sd.csr1 && !sd.tile && !sd.x_direct && !sd.dy_direct && sp.bpad == sd.bpad) {
+            p.shared = true;
+            p.sp = sp;
+            p.sd = sd;
+            p.off_sddmm = 0;
+            p.off_spmm = align_up(sd.total);
+            p.total = align_up(p.off_spmm + sp.total);
+        }
     }
     return p;
 }
@@ -1380,6 +1396,58 @@ extern "C" int snack_coo_bwd_input(const snack_coo_desc *W, const void *dY, int6
     }
 }
 
+namespace {
+
+// The row-wise weight gradient (rowsddmm_kernel, SddmmPlan.rowq > 0) over the feature-major
+// copies xt [I+1][bpad] and dyt [O+1][bpad], written to dW in row order.
+int launch_rowsddmm(const SddmmPlan &p, const snack_coo_desc *W, const float *xt, const float *dyt, float *dW,
+                    hipStream_t st) {
+    const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+    // rows averaging >= 256 entries are split over the 4 waves of a workgroup
+    const bool split = nnz >= 256 * O;
+    const dim3 rgrid(static_cast<unsigned>(round_up8(ceil_div(O, split ? 1 : kWavesPerBlock))));
+    const int zero_row = static_cast<int>(I);
+#define SNACK_ROWSD(BTV, WPRV, QV)                                                                           \
+    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV, 8>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, \
+               W->cols, xt, zero_row, dyt, p.bpad, 1, dW)
+#define SNACK_ROWSD_Q(BTV, WPRV)                         \
+    do {                                                 \
+if (p.rowq == 1) SNACK_ROWSD(BTV, WPRV, 1);      \
+else if (p.rowq == 2) SNACK_ROWSD(BTV, WPRV, 2); \
+else if (p.rowq == 3) SNACK_ROWSD(BTV, WPRV, 3); \
+else SNACK_ROWSD(BTV, WPRV, 4);                  \
+    } while (0)
+#define SNACK_ROWSD_BT(BTV)                 \
+    if (split) SNACK_ROWSD_Q(BTV, 4);       \
+    else SNACK_ROWSD_Q(BTV, 1);
+    if (p.slices > 1) {
+        // slices of 256 columns of the copies, added in order inside one launch
+        const int ns = static_cast<int>(p.slices);
+        if (split)
+            hipLaunchKernelGGL((rowsddmm_kernel<16, 4, 4, 2>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets,
+                               W->cols, xt, zero_row, dyt, p.bpad, ns, dW);
+        else
+            hipLaunchKernelGGL((rowsddmm_kernel<16, 1, 4, 2>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets,
+                               W->cols, xt, zero_row, dyt, p.bpad, ns, dW);
+    } else if (p.bt == 16) {
+        SNACK_ROWSD_BT(16)
+    } else if (p.bt == 8) {
+        SNACK_ROWSD_BT(8)
+    } else if (p.bt == 4) {
+        SNACK_ROWSD_BT(4)
+    } else if (p.bt == 2) {
+        SNACK_ROWSD_BT(2)
+    } else {
+        SNACK_ROWSD_BT(1)
+    }
+#undef SNACK_ROWSD_BT
+#undef SNACK_ROWSD_Q
+#undef SNACK_ROWSD
+    return check_hip("rowsddmm_kernel");
+}
+
+}  // namespace
+
 extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, const void *dY, int64_t batch,
                                      int act_dtype, float *dW_out, void *workspace, size_t workspace_bytes,
                                      void *hip_stream) {
@@ -1476,46 +1544,7 @@ extern "C" int snack_coo_grad_weight(const snack_coo_desc *W, const void *X, con
         const dim3 grid(static_cast<unsigned>(blocks));
         probe(true, st);
         if (p.rowq > 0) {
-            // rows averaging >= 256 entries are split over the 4 waves of a workgroup
-            const bool split = nnz >= 256 * O;
-            const dim3 rgrid(static_cast<unsigned>(round_up8(ceil_div(O, split ? 1 : kWavesPerBlock))));
-            const int zero_row = static_cast<int>(I);
-#define SNACK_ROWSD(BTV, WPRV, QV)                                                                           \
-    hipLaunchKernelGGL((rowsddmm_kernel<BTV, WPRV, QV, 8>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets, \
-                       W->cols, xt, zero_row, dyt, p.bpad, 1, dW)
-#define SNACK_ROWSD_Q(BTV, WPRV)                         \
-    do {                                                 \
-        if (p.rowq == 1) SNACK_ROWSD(BTV, WPRV, 1);      \
-        else if (p.rowq == 2) SNACK_ROWSD(BTV, WPRV, 2); \
-        else if (p.rowq == 3) SNACK_ROWSD(BTV, WPRV, 3); \
-        else SNACK_ROWSD(BTV, WPRV, 4);                  \
-    } while (0)
-#define SNACK_ROWSD_BT(BTV)                 \
-    if (split) SNACK_ROWSD_Q(BTV, 4);       \
-    else SNACK_ROWSD_Q(BTV, 1);
-            if (p.slices > 1) {
-                // slices of 256 columns of the copies, added in order inside one launch
-                const int ns = static_cast<int>(p.slices);
-                if (split)
-                    hipLaunchKernelGGL((rowsddmm_kernel<16, 4, 4, 2>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets,
-                                       W->cols, xt, zero_row, dyt, p.bpad, ns, dW);
-                else
-                    hipLaunchKernelGGL((rowsddmm_kernel<16, 1, 4, 2>), rgrid, dim3(kBlock), 0, st, O, W->row_offsets,
-                                       W->cols, xt, zero_row, dyt, p.bpad, ns, dW);
-            } else if (p.bt == 16) {
-                SNACK_ROWSD_BT(16)
-            } else if (p.bt == 8) {
-                SNACK_ROWSD_BT(8)
-            } else if (p.bt == 4) {
-                SNACK_ROWSD_BT(4)
-            } else if (p.bt == 2) {
-                SNACK_ROWSD_BT(2)
-            } else {
-                SNACK_ROWSD_BT(1)
-            }
-#undef SNACK_ROWSD_BT
-#undef SNACK_ROWSD_Q
-#undef SNACK_ROWSD
+            if (int s = launch_rowsddmm(p, W, xt, dyt, dW, st)) return s;
         } else if (p.wide) {
             const int64_t q = batch / (4 * p.bt);  // float4s per lane (exact when it is cached)
             const bool exact = batch % (4 * p.bt) == 0;
@@ -1635,6 +1664,47 @@ static int run_split_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *
     --g_probe_mute;
     if (s) return s;
     probe(false, st);
+    return snack::ok();
+}
+
+// Both gradients by the row-wave kernels (BwdPlan.shared): db; X and dY copied feature-major
+// once (one launch for both); the input gradient over the column view reading the dY copy; the
+// weight gradient over the row view reading both copies (in row order, then through col_perm when
+// the values are in column order).  The timing probe brackets both gradients' kernels.
+static int run_shared_bwd(const BwdPlan &p, const snack_coo_desc *W, const void *X, const void *dY, int64_t batch,
+                          int act_dtype, void *dX, float *db, float *dW, char *ws, hipStream_t st) {
+    const int64_t O = W->out_features, I = W->in_features, nnz = W->nnz;
+    const bool colvals = W->row_to_col != nullptr;
+    if (db) {
+        const dim3 grid(static_cast<unsigned>(ceil_div(O, kBlock)));
+        if (act_dtype == SNACK_F32)
+            hipLaunchKernelGGL(bias_grad_kernel<float>, grid, dim3(kBlock), 0, st, O, batch,
+                               static_cast<const float *>(dY), db);
+        else
+            hipLaunchKernelGGL(bias_grad_kernel<bf16_t>, grid, dim3(kBlock), 0, st, O, batch,
+                               static_cast<const bf16_t *>(dY), db);
+        if (int s = check_hip("bias_grad_kernel")) return s;
+    }
+    char *wsd = ws + p.off_sddmm;
+    float *xt = reinterpret_cast<float *>(wsd + p.sd.off_x);
+    float *dyt = reinterpret_cast<float *>(wsd + p.sd.off_dy);
+    if (int s = launch_to_feature_major(X, act_dtype, batch, I, xt, st, dY, O, dyt, p.sd.bpad)) return s;
+    probe(true, st);
+    ++g_probe_mute;
+    const int32_t *vperm = colvals ? nullptr : W->col_perm;
+    int s = act_dtype == SNACK_F32
+                ? run_spmm<float>(p.sp, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, vperm, dyt, O,
+                                  batch, nullptr, static_cast<float *>(dX), ws + p.off_spmm, st, W->col_blocks)
+                : run_spmm<bf16_t>(p.sp, I, nnz, W->col_cols, W->col_offsets, W->col_rows, W->vals, vperm, dyt, O,
+                                   batch, nullptr, static_cast<bf16_t *>(dX), ws + p.off_spmm, st, W->col_blocks);
+    float *dwr = colvals ? reinterpret_cast<float *>(wsd + p.sd.off_dw) : dW;
+    if (!s) s = launch_rowsddmm(p.sd, W, xt, dyt, dwr, st);
+    --g_probe_mute;
+    if (s) return s;
+    probe(false, st);
+    if (colvals) {
+        if (int e = launch_gather(W->col_perm, dwr, nnz, dW, st)) return e;
+    }
     return snack::ok();
 }
 
@@ -1764,6 +1834,17 @@ extern "C" int snack_coo_bwd(const snack_coo_desc *W, const void *X, const void 
             if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
             return run_split_bwd(p, W, X, dY, batch, act_dtype, dX, db, dW, static_cast<char *>(workspace),
                                  static_cast<hipStream_t>(hip_stream));
+        }
+        if (p.shared) {
+            if (int s = check_act(X, act_dtype, "X", who)) return s;
+            if (int s = check_act(dY, act_dtype, "dY", who)) return s;
+            if (int s = check_act(dX, act_dtype, "dX", who)) return s;
+            if (!dW) return fail(SNACK_ERR_NULL, "%s: dW is NULL", who);
+            if (reinterpret_cast<uintptr_t>(dW) % 4) return fail(SNACK_ERR_ALIGN, "%s: dW misaligned", who);
+            if (db && reinterpret_cast<uintptr_t>(db) % 4) return fail(SNACK_ERR_ALIGN, "%s: db misaligned", who);
+            if (int s = check_workspace(workspace, workspace_bytes, p.total, who)) return s;
+            return run_shared_bwd(p, W, X, dY, batch, act_dtype, dX, db, dW, static_cast<char *>(workspace),
+                                  static_cast<hipStream_t>(hip_stream));
         }
         if (!p.fused) {
             if (int s = snack_coo_bwd_input(W, dY, batch, act_dtype, dX, db, workspace, workspace_bytes, hip_stream))
