@@ -246,6 +246,25 @@ def test_backward_form_rules():
             assert fused(64) == want, (opt, val)
 
 
+def test_backward_shared_copies_workspace():
+    """On an untiled layer at a wide batch where both gradients take the row-wave kernels (a
+    GPT-2-shaped 768 -> 3072 layer at batch 1024), snack_coo_bwd makes the feature-major copies of
+    X and dY once, in the weight gradient's workspace, beside the input gradient's own: its
+    workspace is at least the two separate calls' together, and holds both copies."""
+    lib = snk._lib
+    d = snk._Desc()
+    d.out_features, d.in_features, d.nnz = 3072, 768, 23593
+    d.row_offsets = d.rows = d.cols = d.vals = 0x1000  # host-side sizing only: never dereferenced
+    d.col_perm = d.col_rows = d.col_cols = d.col_offsets = 0x1000
+    for B in (512, 1024):
+        assert lib.snack_coo_bwd_is_fused(ctypes.byref(d), B, 0) == 0
+        bwd = lib.snack_coo_workspace_bytes(3, ctypes.byref(d), B, 0)
+        dx = lib.snack_coo_workspace_bytes(1, ctypes.byref(d), B, 0)
+        dw = lib.snack_coo_workspace_bytes(2, ctypes.byref(d), B, 0)
+        assert dw >= 4 * B * ((768 + 1) + (3072 + 1))  # X and dY feature-major, zero rows included
+        assert bwd >= dx + dw
+
+
 def test_half_precision_host_checks_and_workspace():
     """SNACK_BF16_HW (2): accepted by every device call and the workspace query, checked before any
     launch (gathered feature count a multiple of 8, activations 16-byte aligned), never the fused

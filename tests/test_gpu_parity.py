@@ -456,3 +456,37 @@ def test_random_sweep(case):
     if L["nnz"] == 0:
         pytest.skip("the shape left no entries")
     run_all(L, B, seed, bf16=bf16)
+
+
+@pytest.mark.parametrize("B", [512, 1024])
+@pytest.mark.parametrize("order", ["row", "col"])
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+def test_backward_shared_copies_equal_separate_calls(bf16, order, B):
+    """snack_coo_bwd on an untiled layer at a wide batch, where both gradients take the row-wave
+    kernels and the feature-major copies of X and dY are made once for both (a GPT-2-shaped
+    768 -> 3072 layer at 1 % density), equals snack_coo_bwd_input and snack_coo_grad_weight
+    called separately, bit for bit (the same kernels on the same copies), and the oracle; values
+    in row order and in column order."""
+    say(f"shared-copy backward B={B} bf16={bf16} values in {order} order")
+    L = synth.random_small_layer(231, 3072, 768, 23593, "uniform")
+    O, I, nnz = L["out_features"], L["in_features"], L["nnz"]
+    built, W = device_layer(L, DEV)
+    if order == "col":
+        W = W.to_column_order()
+    assert snk.snack_coo_bwd_is_fused(W, B, snk.SNACK_BF16 if bf16 else snk.SNACK_F32) == 0
+    x_in, x64 = acts(2300 + B, B, I, bf16)
+    dy_in, dy64 = acts(2301 + B, B, O, bf16)
+    X, dY = to_device(x_in, DEV, bf16), to_device(dy_in, DEV, bf16)
+    db = torch.empty(O, dtype=torch.float32, device=DEV)
+    dX, dW = snk.snack_coo_bwd(W, X, dY, db=db)
+    dXs = snk.snack_coo_bwd_input(W, dY)
+    dWs = snk.snack_coo_grad_weight(W, X, dY)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, dXs) and torch.equal(dW, dWs)
+    r, c, v = built["rows"], built["cols"], built["vals"]
+    check_close(from_device(dX), oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS), nnz / I, "dX", bf16)
+    dWr = oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS)
+    if order == "col":
+        dWr = dWr[built["col_perm"].astype(np.int64)]
+    check_close(dW.cpu().numpy(), dWr, B, "dW")
+    check_close(db.cpu().numpy(), oracle.grad_bias(dy64), B, "db")
