@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B,
 }
 
 // ---------------------------------------------------------------- rowwave mapping
-// For batches that are multiples of 4.  A workgroup of 4 waves owns 4/WPR
+// For batches that are multiples of 4.  A workgroup of 16 waves owns 16/WPR
 // output keys (rows), each split over WPR waves.  Lanes are (slot e, lane t):
 // S = 64/BT slots each take one stored entry per step, lane t holds batch
 // columns b0+4t .. b0+4t+3 and, with Q > 1, the float4s t+BT, .., t+(Q-1)BT
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kBlock) void fixup_kernel(int64_t nkeys, int64_t B,
 // consumed, and keeps U*Q float4 gathers in flight.  Lanes of a chunk past the
 // key's end point at the operand's zero row with value 0, so no step needs a
 // mask.  Slot partial sums are combined by xor shuffles, the WPR waves of a
-// key through LDS.  A workgroup of 16 waves owns 16 / WPR consecutive keys; their results are
+// key through LDS.  The workgroup's keys are consecutive; their results are
 // staged in LDS and written with consecutive threads on consecutive keys of one batch row, so each
 // row of the batch-major output gets one run of 16 / WPR keys per workgroup instead of one
 // scattered 2- or 4-byte store per key (written per key, those stores cost about as much as the
