@@ -4,16 +4,18 @@ same weight with values in row order (needs a GPU).
 With the values in column order every product is the same; vals and every dW are stored in
 column-view order (dW[j] belongs to triple entry col_perm[j]).  The forward walks the same rows in
 the same order and the weight-gradient kernels compute the same per-entry sums, so Y and dW must
-equal the row-order results bit for bit (dW permuted); dX is checked against the oracle (the
-column walk may split long columns over four waves when no permutation is read, and the fused
-pass drops its row bands, both of which change the summation order only).
+equal the row-order results bit for bit (dW permuted) -- Y except on untiled layers whose rows
+average 256 entries or more at batches of 4 and more, where the row-order walk splits each row over
+four waves; dX is checked against the oracle (the column walk may split long columns over four
+waves when no permutation is read, and the fused pass drops its row bands, both of which change
+the summation order only).
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_util import NTHREADS, acts, check_close, device_layer, from_device, say, to_device
+from gpu_util import NTHREADS, acts, check_close, col_counts, device_layer, from_device, row_counts, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -49,15 +51,18 @@ def _run(L, B, seed, bf16=False):
     dXr = oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS)
     dWr = oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS)
     R, C = out["row"], out["col"]
-    # Y and dW: bit for bit the row-order results (dW in column order)
-    assert torch.equal(R["Y"], C["Y"]), "Y differs"
+    # Y and dW: bit for bit the row-order results (dW in column order); Y only where both walks sum
+    # each row in one order: the untiled row-order forward splits rows averaging 256 entries or more
+    # over four waves, the column-order one (values through row_to_col) does not
+    if nnz < 256 * O or nnz >= (1 << 20) or B < 4:
+        assert torch.equal(R["Y"], C["Y"]), "Y differs"
     assert np.array_equal(C["dW"].cpu().numpy().view(np.uint32), R["dW"].cpu().numpy()[cp].view(np.uint32))
     assert np.array_equal(C["bdW"].cpu().numpy().view(np.uint32), R["bdW"].cpu().numpy()[cp].view(np.uint32))
     # against the oracle
-    check_close(from_device(C["Y"]), oracle.fwd(O, I, r, c, v, x64, L["bias"], nthreads=NTHREADS), nnz / max(O, 1),
-                "col Y", bf16)
-    check_close(from_device(C["dX"]), dXr, nnz / max(I, 1), "col dX", bf16)
-    check_close(from_device(C["bdX"]), dXr, nnz / max(I, 1), "col bwd dX", bf16)
+    check_close(from_device(C["Y"]), oracle.fwd(O, I, r, c, v, x64, L["bias"], nthreads=NTHREADS),
+                row_counts(built), "col Y", bf16)
+    check_close(from_device(C["dX"]), dXr, col_counts(built), "col dX", bf16)
+    check_close(from_device(C["bdX"]), dXr, col_counts(built), "col bwd dX", bf16)
     check_close(C["dW"].cpu().numpy(), dWr[cp], B, "col dW")
     check_close(C["bdW"].cpu().numpy(), dWr[cp], B, "col bwd dW")
     for k in ("db", "bdb"):
@@ -123,3 +128,33 @@ def test_conversions_and_topology_refusal():
     Wc.vals.mul_(2.0)
     X = torch.randn(8, 900, device=DEV)
     assert torch.equal(snk.snack_coo_fwd(Wc, X), snk.snack_coo_fwd(W, X * 2.0))
+
+
+def _random_cases(n=24, seed=7373):
+    """Random shapes, densities, structures and batches (1 to 1024: one-pass, two-pass and shared-copy
+    backward forms, batch slices of the weight gradient), a quarter in bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = ["uniform", "empty_rows", "dense_lines", "skewed_rows", "one_row", "one_col"]
+    batches = [1, 3, 4, 12, 16, 32, 48, 64, 65, 128, 256, 512, 1024]
+    out = []
+    for i in range(n):
+        O = int(rng.integers(1, 3000))
+        I = int(rng.integers(1, 3000))
+        dens = float(10 ** rng.uniform(-3.0, -0.7))
+        B = batches[int(rng.integers(0, len(batches)))]
+        nnz = max(1, min(O * I, int(dens * O * I), 300_000_000 // B))
+        shape = shapes[int(rng.integers(0, len(shapes)))]
+        bf16 = bool(rng.random() < 0.25)
+        out.append((7400 + i, shape, O, I, nnz, B, bf16))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-n{c[4]}-B{c[5]}"
+                         + ("-bf16" if c[6] else ""))
+def test_column_order_random_sweep(case):
+    seed, shape, O, I, nnz, B, bf16 = case
+    say(f"column order random {shape} {O}x{I} nnz={nnz} B={B} bf16={bf16}")
+    L = synth.random_small_layer(seed, O, I, nnz, shape)
+    if L["nnz"] == 0:
+        pytest.skip("the shape left no entries")
+    _run(L, B, seed, bf16)
