@@ -19,7 +19,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import NTHREADS, acts, check_close, device_layer, from_device, named_layer, say, to_device
+from gpu_util import (NTHREADS, acts, check_close, col_counts, device_layer, from_device, named_layer, row_counts,
+                      say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -400,3 +401,62 @@ def test_tiled_backward_in_graph(layers, order):
         for t, r in zip((Y, dX, dW, db), ref):
             assert torch.equal(t, r)
         _ = X.sum()
+
+
+def _tiled_random_cases(n=12, seed=5151):
+    """Random layers of at least 2^20 entries (the tiled walks' threshold, which take them where
+    their segments average 8 entries or more): shapes from a single
+    column block to 15, four structures, padded and unpadded batches from 16 to 300 (one to five
+    batch tiles of 64 columns, or tiles of 16 and 32), values in either order, a quarter bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = ["uniform", "empty_rows", "dense_lines", "skewed_rows"]
+    batches = [16, 17, 32, 48, 64, 96, 100, 128, 192, 256, 300]
+    out = []
+    for i in range(n):
+        O = int(rng.integers(600, 9000))
+        I = int(rng.integers(600, 9000))
+        B = batches[int(rng.integers(0, len(batches)))]
+        nnz = int(min(O * I // 3, max(1 << 20, int(rng.uniform(1.05e6, 3.0e6))), 400_000_000 // B))
+        shape = shapes[int(rng.integers(0, len(shapes)))]
+        order = "col" if rng.random() < 0.5 else "row"
+        bf16 = bool(rng.random() < 0.25)
+        out.append((5200 + i, shape, O, I, nnz, B, order, bf16))
+    return out
+
+
+@pytest.mark.parametrize("case", _tiled_random_cases(),
+                         ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-n{c[4]}-B{c[5]}-{c[6]}" + ("-bf16" if c[7] else ""))
+def test_tiled_random_sweep(case):
+    """Forward, input gradient, weight gradient and the backward call on random tiled layers
+    against the oracle (per-feature reduction lengths in the bound); a second backward call gives
+    the same bits."""
+    seed, shape, O, I, nnz, B, order, bf16 = case
+    say(f"tiled random {shape} {O}x{I} nnz={nnz} B={B} values in {order} order bf16={bf16}")
+    L = synth.random_small_layer(seed, O, I, nnz, shape)
+    assert L["nnz"] >= (1 << 20) or shape != "uniform"
+    built, W = device_layer(L, DEV)
+    if order == "col":
+        W = W.to_column_order()
+    nz = L["nnz"]
+    x_in, x64 = acts(seed, B, I, bf16)
+    dy_in, dy64 = acts(seed + 1, B, O, bf16)
+    X, dY = to_device(x_in, DEV, bf16), to_device(dy_in, DEV, bf16)
+    b = torch.from_numpy(L["bias"]).to(DEV)
+    Y = snk.snack_coo_fwd(W, X, b)
+    dX = snk.snack_coo_bwd_input(W, dY)
+    dW = snk.snack_coo_grad_weight(W, X, dY)
+    dX2, dW2 = snk.snack_coo_bwd(W, X, dY)
+    dX3, dW3 = snk.snack_coo_bwd(W, X, dY)
+    torch.cuda.synchronize()
+    assert torch.equal(dX2, dX3) and torch.equal(dW2, dW3)
+    r, c, v = built["rows"], built["cols"], built["vals"]
+    check_close(from_device(Y), oracle.fwd(O, I, r, c, v, x64, L["bias"], nthreads=NTHREADS), row_counts(built),
+                "fwd", bf16)
+    dXr = oracle.bwd_input(O, I, r, c, v, dy64, nthreads=NTHREADS)
+    check_close(from_device(dX), dXr, col_counts(built), "dX", bf16)
+    check_close(from_device(dX2), dXr, col_counts(built), "bwd dX", bf16)
+    dWr = oracle.grad_weight(O, I, r, c, x64, dy64, nthreads=NTHREADS)
+    if order == "col":
+        dWr = dWr[built["col_perm"].astype(np.int64)]
+    check_close(dW.cpu().numpy(), dWr, B, "dW")
+    check_close(dW2.cpu().numpy(), dWr, B, "bwd dW")
